@@ -1,0 +1,205 @@
+"""Seeded synthetic inputs for the gated delta rule workloads.
+
+This module holds input recipes only (shapes, distributions, layouts, seeds) and none
+of the method's arithmetic; both the HIP path's tests/benchmark and the fp64 oracle
+draw their inputs from here.
+
+Every array is produced per (tensor, sequence, head) slice from its own PCG64 stream,
+seeded with ``SeedSequence([seed, tensor_id, s, head])``, so any slice can be
+regenerated alone (sampled parity checks at full size) and the result does not depend
+on how much of the problem is materialised.  Draws are float64, cast to float32.
+
+Recipe (distributions follow the workload descriptions):
+  q, k      N(0, 1), then L2-normalised per (token, head) in float64
+  v         N(0, 1)
+  g         log-gate, U(g_lo, 0): one value per (token, head) for the scalar gate, S_k
+            values for the per-key-channel gate
+  beta      U(0, 1)
+  state0    N(0, 0.1^2)
+  gy        N(0, 1)           (output cotangent)
+  dstate_out N(0, 1)          (final-state cotangent)
+Tokens t >= len_s of a sequence are filled with ``pad_value`` (0 by default; NaN in the
+tests that prove padded tokens are never read).
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import numpy as np
+
+TENSORS = ("q", "k", "v", "g", "beta", "state0", "gy", "dstate_out")
+_TID = {n: i for i, n in enumerate(TENSORS)}
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    """Shape and recipe of one problem."""
+    name: str
+    n_seqs: int
+    T: int
+    H_k: int
+    H_v: int
+    S: int
+    kda: bool
+    C: int                      # checkpoint interval (0: ceil(sqrt(T)))
+    g_lo: float                 # log-gate ~ U(g_lo, 0)
+    seq_lens: tuple | None = None   # None: all T
+    packed: bool = False        # q/k/v are row views of one [n_seqs, T, W] buffer
+    seed: int = 1000
+
+    @property
+    def S_k(self):
+        return self.S
+
+    @property
+    def S_v(self):
+        return self.S
+
+    @property
+    def scale(self):
+        return float(np.float32(1.0 / math.sqrt(self.S)))
+
+    @property
+    def G(self):
+        return self.S if self.kda else 1
+
+    @property
+    def lens(self):
+        return tuple(self.seq_lens) if self.seq_lens is not None else (self.T,) * self.n_seqs
+
+    @property
+    def tokens_heads(self):
+        return sum(self.lens) * self.H_v
+
+    @property
+    def packed_width(self):
+        return 2 * self.H_k * self.S + self.H_v * self.S
+
+    def shape_dict(self, **over):
+        d = dict(n_seqs=self.n_seqs, T=self.T, H_k=self.H_k, H_v=self.H_v, S_k=self.S,
+                 S_v=self.S, kda=self.kda, C=self.C, scale=self.scale,
+                 seq_lens=list(self.lens))
+        d.update(over)
+        return d
+
+    def replace(self, **kw):
+        return dataclasses.replace(self, **kw)
+
+
+# The five workloads (sizes and distributions as the workload descriptions give them).
+WORKLOADS = {
+    # tiny scalar gate, 1 seq, 1 q/k head, 1 v head, S=32, T=16, C=4
+    "tiny_scalar_s32": Workload("tiny_scalar_s32", 1, 16, 1, 1, 32, False, 4, -1.0, seed=1000),
+    # per-key-channel gate, 2 seqs (64 and a ragged 61), 4/4 heads, S=64, C=8
+    "kda_ragged_s64": Workload("kda_ragged_s64", 2, 64, 4, 4, 64, True, 8, -0.5,
+                               seq_lens=(64, 61), seed=1001),
+    # GQA v_repeat 2 with q/k/v as row views of a packed [T, 1024] buffer, S=32, T=256
+    "gqa_strided_s32": Workload("gqa_strided_s32", 2, 256, 8, 16, 32, False, 0, -1.0,
+                                packed=True, seed=1002),
+    # hybrid delta-net layer shape: 4 seqs x 4096, 16 q/k heads, 48 v heads, S=128, C=64,
+    # packed [T, 10240] qkv buffer, per-key-channel gate
+    "layer_kda_s128": Workload("layer_kda_s128", 4, 4096, 16, 48, 128, True, 64, -0.3,
+                               packed=True, seed=1003),
+    # long context: 1 seq x 65536, 16/48 heads, S=128, C=256, scalar gate (slow decay)
+    "long_scalar_s128": Workload("long_scalar_s128", 1, 65536, 16, 48, 128, False, 256, -0.05,
+                                 seed=1004),
+}
+WORKLOAD_ORDER = list(WORKLOADS)
+HEADLINE = "layer_kda_s128"
+
+
+def _rng(seed, tensor, s, head):
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, _TID[tensor], s, head])))
+
+
+def _slice(w: Workload, tensor: str, s: int, head: int) -> np.ndarray:
+    """One (sequence, head) slice of a tensor, float64, before padding."""
+    r = _rng(w.seed, tensor, s, head)
+    T, S = w.T, w.S
+    if tensor in ("q", "k"):
+        x = r.standard_normal((T, S))
+        n = np.sqrt(np.sum(x * x, axis=1, keepdims=True))
+        return x / n
+    if tensor in ("v", "gy"):
+        return r.standard_normal((T, S))
+    if tensor == "g":
+        return w.g_lo + (0.0 - w.g_lo) * r.random((T, w.G))
+    if tensor == "beta":
+        return r.random(T)
+    if tensor == "state0":
+        return 0.1 * r.standard_normal((S, S))
+    if tensor == "dstate_out":
+        return r.standard_normal((S, S))
+    raise KeyError(tensor)
+
+
+def _heads(w: Workload, tensor: str) -> int:
+    return w.H_k if tensor in ("q", "k") else w.H_v
+
+
+def make_tensor(w: Workload, tensor: str, seqs=None, heads=None, pad_value=0.0) -> np.ndarray:
+    """float32 array in the logical layout, restricted to the given sequences / heads.
+
+    Logical layouts: q, k [n][T][H_k][S]; v, gy [n][T][H_v][S]; g [n][T][H_v][G];
+    beta [n][T][H_v]; state0, dstate_out [n][H_v][S][S].
+    """
+    seqs = list(range(w.n_seqs)) if seqs is None else list(seqs)
+    heads = list(range(_heads(w, tensor))) if heads is None else list(heads)
+    lens = w.lens
+    if tensor in ("state0", "dstate_out"):
+        out = np.empty((len(seqs), len(heads), w.S, w.S), np.float32)
+        for a, s in enumerate(seqs):
+            for b, h in enumerate(heads):
+                out[a, b] = _slice(w, tensor, s, h)
+        return out
+    if tensor == "beta":
+        out = np.empty((len(seqs), w.T, len(heads)), np.float32)
+    elif tensor == "g":
+        out = np.empty((len(seqs), w.T, len(heads), w.G), np.float32)
+    else:
+        out = np.empty((len(seqs), w.T, len(heads), w.S), np.float32)
+    for a, s in enumerate(seqs):
+        for b, h in enumerate(heads):
+            x = _slice(w, tensor, s, h).astype(np.float32)
+            if tensor == "beta":
+                out[a, :, b] = x
+            else:
+                out[a, :, b] = x.reshape(w.T, -1)
+        if lens[s] < w.T:
+            out[a, lens[s]:] = pad_value
+    return out
+
+
+def make_all(w: Workload, seqs=None, key_heads=None, pad_value=0.0, with_cotangents=True):
+    """All inputs for the given sequences and key heads (value heads h with h mod H_k in
+    key_heads, increasing).  Returns (dict of float32 arrays, value-head list)."""
+    kh = list(range(w.H_k)) if key_heads is None else list(key_heads)
+    vh = [h for h in range(w.H_v) if (h % w.H_k) in kh]
+    names = TENSORS if with_cotangents else TENSORS[:6]
+    out = {}
+    for n in names:
+        heads = kh if n in ("q", "k") else vh
+        out[n] = make_tensor(w, n, seqs=seqs, heads=heads, pad_value=pad_value)
+    return out, vh
+
+
+def sub_workload(w: Workload, seqs, key_heads) -> Workload:
+    """The workload restricted to some sequences and key heads, as a problem of its own:
+    the kept value heads keep their key head under the modulo map (h -> h mod H_k)."""
+    lens = [w.lens[s] for s in seqs]
+    r = w.H_v // w.H_k
+    return w.replace(name=w.name + "_sub", n_seqs=len(seqs), H_k=len(key_heads),
+                     H_v=len(key_heads) * r, seq_lens=tuple(lens))
+
+
+def pack_qkv(w: Workload, q, k, v) -> np.ndarray:
+    """Place q, k, v as row views of one [n, T, W] buffer: q at columns [0, H_k S),
+    k at [H_k S, 2 H_k S), v at [2 H_k S, W); head h at offset h S within its block."""
+    n, T = q.shape[0], q.shape[1]
+    HkS = w.H_k * w.S
+    buf = np.zeros((n, T, w.packed_width), np.float32)
+    buf[:, :, :HkS] = q.reshape(n, T, -1)
+    buf[:, :, HkS:2 * HkS] = k.reshape(n, T, -1)
+    buf[:, :, 2 * HkS:] = v.reshape(n, T, -1)
+    return buf
