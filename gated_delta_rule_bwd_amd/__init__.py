@@ -6,8 +6,8 @@ the library; the first use of ``fwd``, ``bwd``, ``workspace_size`` or ``Problem`
 raises if the library has not been built (there is no fallback path).
 """
 
-_BINDING_NAMES = ("Problem", "workspace_size", "grad_layout", "fwd", "bwd", "lib",
-                  "GdnError", "STATUS")
+_BINDING_NAMES = ("Problem", "workspace_size", "grad_layout", "unpack_grads", "fwd", "bwd",
+                  "lib", "GdnError", "STATUS", "EXPORTS", "BWD_REUSE_SNAPSHOTS")
 
 
 def __getattr__(name):

@@ -1,0 +1,182 @@
+"""ctypes binding of the C ABI in include/gdn.h (argument marshalling only).
+
+Every step of the computation runs in the HIP kernels of ``libgdn.so``; this module only
+turns torch tensors into raw device pointers, strides and a stream handle.  Loading fails
+loudly when the library has not been built: there is no other implementation to fall
+back to.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgdn.so")
+if not os.path.exists(_LIB_PATH):
+    raise ImportError(
+        f"{_LIB_PATH} is missing: build it with `python -m gated_delta_rule_bwd_amd.build` "
+        "(or __graft_entry__.build())")
+lib = ctypes.CDLL(_LIB_PATH)
+
+STATUS = {0: "GDN_OK", -1: "GDN_ERR_ARG", -2: "GDN_ERR_UNSUPPORTED",
+          -3: "GDN_ERR_WORKSPACE", -4: "GDN_ERR_DEVICE"}
+GATE_SCALAR, GATE_KDA = 0, 1
+BWD_REUSE_SNAPSHOTS = 1
+EXPORTS = ("gdn_workspace_size", "gdn_grad_packed_floats", "gdn_fwd", "gdn_bwd",
+           "gdn_status_string")
+
+
+class GdnError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        super().__init__(f"{what}: {STATUS.get(code, code)} "
+                         f"({lib.gdn_status_string(code).decode()})")
+        self.code = code
+
+
+class _Strides(ctypes.Structure):
+    _fields_ = [("seq", ctypes.c_int64), ("tok", ctypes.c_int64), ("head", ctypes.c_int64)]
+
+
+class _Problem(ctypes.Structure):
+    _fields_ = [("n_seqs", ctypes.c_int32), ("T", ctypes.c_int32), ("H_k", ctypes.c_int32),
+                ("H_v", ctypes.c_int32), ("S_k", ctypes.c_int32), ("S_v", ctypes.c_int32),
+                ("gate", ctypes.c_int32), ("C", ctypes.c_int32), ("scale", ctypes.c_float),
+                ("seq_lens", ctypes.POINTER(ctypes.c_int32))] + \
+               [(n, _Strides) for n in ("q", "k", "v", "g", "beta", "gy", "y")]
+
+
+_VP = ctypes.c_void_p
+lib.gdn_workspace_size.argtypes = [ctypes.POINTER(_Problem)]
+lib.gdn_workspace_size.restype = ctypes.c_size_t
+lib.gdn_grad_packed_floats.argtypes = [ctypes.POINTER(_Problem), ctypes.POINTER(ctypes.c_size_t)]
+lib.gdn_grad_packed_floats.restype = ctypes.c_size_t
+lib.gdn_fwd.argtypes = [ctypes.POINTER(_Problem)] + [_VP] * 9 + [ctypes.c_size_t, _VP]
+lib.gdn_fwd.restype = ctypes.c_int
+lib.gdn_bwd.argtypes = [ctypes.POINTER(_Problem)] + [_VP] * 10 + [ctypes.c_size_t,
+                                                                 ctypes.c_uint, _VP]
+lib.gdn_bwd.restype = ctypes.c_int
+lib.gdn_status_string.argtypes = [ctypes.c_int]
+lib.gdn_status_string.restype = ctypes.c_char_p
+
+
+def _tok_strides(t, name):
+    """(seq, tok, head) strides of a [n, T, H, W] (or [n, T, H]) tensor; innermost must be 1."""
+    if t is None:
+        return (0, 0, 0)
+    if t.dim() == 4:
+        if t.shape[3] > 1 and t.stride(3) != 1:
+            raise ValueError(f"{name}: innermost stride must be 1")
+        return tuple(int(x) for x in t.stride()[:3])
+    if t.dim() == 3:
+        return tuple(int(x) for x in t.stride())
+    raise ValueError(f"{name}: expected 3 or 4 dims, got {tuple(t.shape)}")
+
+
+class Problem:
+    """A gdn_problem: sizes, gate kind, interval, scale, lengths and the strides of the
+    per-token tensors.  Use ``Problem.from_tensors``."""
+
+    def __init__(self, n_seqs, T, H_k, H_v, S, kda, C, scale, seq_lens=None, strides=None):
+        self.n_seqs, self.T, self.H_k, self.H_v, self.S = n_seqs, T, H_k, H_v, S
+        self.kda, self.C, self.scale = bool(kda), int(C), float(scale)
+        self.seq_lens = None if seq_lens is None else [int(x) for x in seq_lens]
+        self._lens = None
+        self.strides = dict(strides or {})
+        self._c = _Problem()
+        self._fill()
+
+    @classmethod
+    def from_tensors(cls, q, k, v, g, beta, C=0, scale=None, seq_lens=None, gy=None, y=None):
+        n, T, H_k, S = q.shape
+        H_v = v.shape[2]
+        kda = g.dim() == 4 and g.shape[3] == S and S > 1
+        strides = {"q": _tok_strides(q, "q"), "k": _tok_strides(k, "k"),
+                   "v": _tok_strides(v, "v"), "g": _tok_strides(g, "g"),
+                   "beta": _tok_strides(beta, "beta"), "gy": _tok_strides(gy, "gy"),
+                   "y": _tok_strides(y, "y")}
+        if scale is None:
+            scale = S ** -0.5
+        return cls(n, T, H_k, H_v, S, kda, C, scale, seq_lens, strides)
+
+    def set_strides(self, **kw):
+        for name, t in kw.items():
+            self.strides[name] = _tok_strides(t, name) if isinstance(t, torch.Tensor) else tuple(t)
+        self._fill()
+        return self
+
+    def _fill(self):
+        c = self._c
+        c.n_seqs, c.T, c.H_k, c.H_v = self.n_seqs, self.T, self.H_k, self.H_v
+        c.S_k = c.S_v = self.S
+        c.gate = GATE_KDA if self.kda else GATE_SCALAR
+        c.C = self.C
+        c.scale = self.scale
+        if self.seq_lens is not None:
+            self._lens = (ctypes.c_int32 * max(1, len(self.seq_lens)))(*self.seq_lens)
+            c.seq_lens = ctypes.cast(self._lens, ctypes.POINTER(ctypes.c_int32))
+        else:
+            self._lens = None
+            c.seq_lens = None
+        for name in ("q", "k", "v", "g", "beta", "gy", "y"):
+            st = self.strides.get(name, (0, 0, 0))
+            setattr(c, name, _Strides(*st))
+
+    @property
+    def c(self):
+        return ctypes.byref(self._c)
+
+
+def workspace_size(p: Problem) -> int:
+    return int(lib.gdn_workspace_size(p.c))
+
+
+def grad_layout(p: Problem):
+    """(total floats, {region: (offset, shape)}) of the packed gradient buffer."""
+    off = (ctypes.c_size_t * 6)()
+    total = int(lib.gdn_grad_packed_floats(p.c, off))
+    n, T, Hk, Hv, S = p.n_seqs, p.T, p.H_k, p.H_v, p.S
+    G = S if p.kda else 1
+    shapes = {"dq": (n, T, Hk, S), "dk": (n, T, Hk, S), "dv": (n, T, Hv, S),
+              "dg": (n, T, Hv, G), "dbeta": (n, T, Hv), "dstate": (n, Hv, S, S)}
+    return total, {name: (int(off[i]), shp) for i, (name, shp) in enumerate(shapes.items())}
+
+
+def unpack_grads(p: Problem, grad_packed: torch.Tensor):
+    _, lay = grad_layout(p)
+    out = {}
+    for name, (o, shp) in lay.items():
+        cnt = 1
+        for x in shp:
+            cnt *= x
+        out[name] = grad_packed[o:o + cnt].view(shp)
+    return out
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def fwd(p: Problem, q, k, v, g, beta, state0, y, state_out, ws, stream=None):
+    """gdn_fwd on device tensors (y must have the strides recorded in p for "y")."""
+    rc = lib.gdn_fwd(p.c, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state0),
+                     _ptr(y), _ptr(state_out), _ptr(ws), ws.numel() * ws.element_size(),
+                     _stream(stream))
+    if rc != 0:
+        raise GdnError(rc, "gdn_fwd")
+
+
+def bwd(p: Problem, q, k, v, g, beta, state0, gy, dstate_out, grad_packed, ws, flags=0,
+        stream=None):
+    """gdn_bwd on device tensors (gy must have the strides recorded in p for "gy")."""
+    rc = lib.gdn_bwd(p.c, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state0),
+                     _ptr(gy), _ptr(dstate_out), _ptr(grad_packed), _ptr(ws),
+                     ws.numel() * ws.element_size(), int(flags), _stream(stream))
+    if rc != 0:
+        raise GdnError(rc, "gdn_bwd")

@@ -1,0 +1,307 @@
+// gdn_api.hip -- host side of the C ABI declared in include/gdn.h: argument validation,
+// workspace sizing and kernel launches.  Nothing here allocates device memory.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "gdn.h"
+#include "gdn_internal.h"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+int ceil_sqrt(int64_t T) {
+    if (T <= 1) return 1;
+    int64_t c = (int64_t)std::ceil(std::sqrt((double)T));
+    while (c > 1 && (c - 1) * (c - 1) >= T) --c;
+    while (c * c < T) ++c;
+    return (int)c;
+}
+
+struct Plan {
+    int C = 1;         // effective checkpoint interval
+    int n_ck_max = 1;  // snapshots per unit
+    int G = 1;         // gate width
+    int64_t units = 0;
+    bool parts = false;  // dq/dk go through per-value-head partials
+    size_t off_snap = 0, off_seg = 0, off_e = 0, off_pq = 0, off_pk = 0, total = 0;
+};
+
+bool strides_ok(const gdn_strides &s) { return s.seq >= 0 && s.tok >= 0 && s.head >= 0; }
+
+int validate(const gdn_problem *p) {
+    if (!p) return GDN_ERR_ARG;
+    if (p->n_seqs < 0 || p->T < 0 || p->H_k <= 0 || p->H_v <= 0 || p->S_k <= 0 ||
+        p->S_v <= 0 || p->C < 0)
+        return GDN_ERR_ARG;
+    if (p->gate != GDN_GATE_SCALAR && p->gate != GDN_GATE_KDA) return GDN_ERR_ARG;
+    if (!std::isfinite(p->scale)) return GDN_ERR_ARG;
+    if (p->seq_lens)
+        for (int s = 0; s < p->n_seqs; ++s)
+            if (p->seq_lens[s] < 0 || p->seq_lens[s] > p->T) return GDN_ERR_ARG;
+    if (p->H_v % p->H_k != 0) return GDN_ERR_UNSUPPORTED;
+    if (p->S_k != p->S_v) return GDN_ERR_UNSUPPORTED;
+    if (p->S_k != 32 && p->S_k != 64 && p->S_k != 128) return GDN_ERR_UNSUPPORTED;
+    const gdn_strides *all[] = {&p->q, &p->k, &p->v, &p->g, &p->beta, &p->gy, &p->y};
+    for (auto *s : all)
+        if (!strides_ok(*s)) return GDN_ERR_UNSUPPORTED;
+    return GDN_OK;
+}
+
+Plan make_plan(const gdn_problem *p) {
+    Plan pl;
+    const int64_t S = p->S_v;
+    pl.C = p->C > 0 ? std::min(p->C, std::max(p->T, 1)) : ceil_sqrt(p->T);
+    pl.n_ck_max = std::max(1, (p->T + pl.C - 1) / pl.C);
+    pl.G = p->gate == GDN_GATE_KDA ? p->S_k : 1;
+    pl.units = (int64_t)p->n_seqs * p->H_v;
+    pl.parts = p->H_v != p->H_k;
+    size_t off = 0;
+    pl.off_snap = off;
+    off = align_up(off + (size_t)pl.units * pl.n_ck_max * S * S * sizeof(float));
+    pl.off_seg = off;
+    off = align_up(off + (size_t)pl.units * pl.C * S * S * sizeof(float));
+    pl.off_e = off;
+    off = align_up(off + (size_t)pl.units * pl.C * S * sizeof(float));
+    if (pl.parts) {
+        const size_t part = (size_t)p->n_seqs * p->T * p->H_v * S * sizeof(float);
+        pl.off_pq = off;
+        off = align_up(off + part);
+        pl.off_pk = off;
+        off = align_up(off + part);
+    }
+    pl.total = off;
+    return pl;
+}
+
+// Byte range [lo, hi) covered by a strided per-token tensor (empty when any extent is 0).
+struct Range {
+    uintptr_t lo = 0, hi = 0;
+};
+
+Range span_tok(const void *base, const gdn_strides &s, int64_t n, int64_t T, int64_t H,
+               int64_t W) {
+    Range r;
+    if (!base || n <= 0 || T <= 0 || H <= 0 || W <= 0) return r;
+    const int64_t last = (n - 1) * s.seq + (T - 1) * s.tok + (H - 1) * s.head + W;
+    r.lo = (uintptr_t)base;
+    r.hi = r.lo + (uintptr_t)last * sizeof(float);
+    return r;
+}
+
+Range span_flat(const void *base, int64_t count_floats) {
+    Range r;
+    if (!base || count_floats <= 0) return r;
+    r.lo = (uintptr_t)base;
+    r.hi = r.lo + (uintptr_t)count_floats * sizeof(float);
+    return r;
+}
+
+Range span_bytes(const void *base, size_t bytes) {
+    Range r;
+    if (!base || bytes == 0) return r;
+    r.lo = (uintptr_t)base;
+    r.hi = r.lo + bytes;
+    return r;
+}
+
+bool overlap(const Range &a, const Range &b) {
+    if (a.lo == a.hi || b.lo == b.hi) return false;
+    return a.lo < b.hi && b.lo < a.hi;
+}
+
+// A written strided view must not map two elements onto one address: sort the dimensions
+// by stride and require each stride to exceed the span of the dimensions inside it.
+bool non_self_overlapping(const gdn_strides &s, int64_t n, int64_t T, int64_t H, int64_t W) {
+    struct Dim {
+        int64_t stride, extent;
+    } d[3] = {{s.seq, n}, {s.tok, T}, {s.head, H}};
+    std::sort(d, d + 3, [](const Dim &x, const Dim &y) { return x.stride < y.stride; });
+    int64_t span = W;  // innermost: W contiguous floats
+    for (auto &x : d) {
+        if (x.extent <= 1) continue;
+        if (x.stride < span) return false;
+        span = x.stride * (x.extent - 1) + span;
+    }
+    return true;
+}
+
+bool aligned4(const void *p) { return ((uintptr_t)p & 3u) == 0; }
+
+void fill_lens(const gdn_problem *p, int s0, int count, int32_t *dst) {
+    for (int i = 0; i < count; ++i) dst[i] = p->seq_lens ? p->seq_lens[s0 + i] : p->T;
+}
+
+int device_status(hipError_t e) { return e == hipSuccess ? GDN_OK : GDN_ERR_DEVICE; }
+
+}  // namespace
+
+extern "C" {
+
+const char *gdn_status_string(int status) {
+    switch (status) {
+        case GDN_OK: return "ok";
+        case GDN_ERR_ARG: return "invalid argument";
+        case GDN_ERR_UNSUPPORTED: return "unsupported problem";
+        case GDN_ERR_WORKSPACE: return "workspace too small";
+        case GDN_ERR_DEVICE: return "device launch failed";
+    }
+    return "unknown status";
+}
+
+size_t gdn_workspace_size(const gdn_problem *p) {
+    if (validate(p) != GDN_OK) return 0;
+    return make_plan(p).total;
+}
+
+size_t gdn_grad_packed_floats(const gdn_problem *p, size_t offsets[6]) {
+    if (validate(p) != GDN_OK) return 0;
+    const size_t n = p->n_seqs, T = p->T, Hk = p->H_k, Hv = p->H_v, Sk = p->S_k, Sv = p->S_v;
+    const size_t G = p->gate == GDN_GATE_KDA ? Sk : 1;
+    const size_t sizes[6] = {n * T * Hk * Sk, n * T * Hk * Sk, n * T * Hv * Sv,
+                             n * T * Hv * G,  n * T * Hv,      n * Hv * Sv * Sk};
+    size_t off = 0;
+    for (int i = 0; i < 6; ++i) {
+        if (offsets) offsets[i] = off;
+        off += sizes[i];
+    }
+    return off;
+}
+
+int gdn_fwd(const gdn_problem *p, const float *q, const float *k, const float *v,
+            const float *g, const float *beta, const float *state0, float *y,
+            float *state_out, void *ws, size_t ws_bytes, gdn_stream_t stream) {
+    int rc = validate(p);
+    if (rc != GDN_OK) return rc;
+    const Plan pl = make_plan(p);
+    const int64_t n = p->n_seqs, T = p->T, Hk = p->H_k, Hv = p->H_v, S = p->S_v;
+    if (!q || !k || !v || !g || !beta || !state0 || !y || !state_out) return GDN_ERR_ARG;
+    const void *ptrs[] = {q, k, v, g, beta, state0, y, state_out};
+    for (auto *x : ptrs)
+        if (!aligned4(x)) return GDN_ERR_UNSUPPORTED;
+    if (ws_bytes < pl.total) return GDN_ERR_WORKSPACE;
+    if (!ws || ((uintptr_t)ws % 16) != 0) return GDN_ERR_ARG;
+    if (!non_self_overlapping(p->y, n, T, Hv, S)) return GDN_ERR_ARG;
+
+    const Range in[] = {span_tok(q, p->q, n, T, Hk, S), span_tok(k, p->k, n, T, Hk, S),
+                        span_tok(v, p->v, n, T, Hv, S), span_tok(g, p->g, n, T, Hv, pl.G),
+                        span_tok(beta, p->beta, n, T, Hv, 1), span_flat(state0, n * Hv * S * S)};
+    const Range out[] = {span_tok(y, p->y, n, T, Hv, S), span_flat(state_out, n * Hv * S * S),
+                         span_bytes(ws, pl.total)};
+    for (auto &o : out)
+        for (auto &i : in)
+            if (overlap(o, i)) return GDN_ERR_ARG;
+    for (int i = 0; i < 3; ++i)
+        for (int j = i + 1; j < 3; ++j)
+            if (overlap(out[i], out[j])) return GDN_ERR_ARG;
+
+    gdn::FwdArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.state0 = state0;
+    a.y = y; a.state_out = state_out;
+    a.snap = (float *)((char *)ws + pl.off_snap);
+    a.sq = p->q; a.sk = p->k; a.sv = p->v; a.sg = p->g; a.sb = p->beta; a.sy = p->y;
+    a.T = p->T; a.H_k = p->H_k; a.H_v = p->H_v; a.C = pl.C; a.n_ck_max = pl.n_ck_max;
+    a.scale = p->scale;
+    for (int s0 = 0; s0 < p->n_seqs; s0 += gdn::kMaxSeqsPerLaunch) {
+        const int cnt = std::min(gdn::kMaxSeqsPerLaunch, p->n_seqs - s0);
+        a.s_base = s0;
+        fill_lens(p, s0, cnt, a.lens);
+        rc = device_status(gdn::launch_fwd(a, (int)S, p->gate == GDN_GATE_KDA, cnt,
+                                           (hipStream_t)stream));
+        if (rc != GDN_OK) return rc;
+    }
+    return GDN_OK;
+}
+
+int gdn_bwd(const gdn_problem *p, const float *q, const float *k, const float *v,
+            const float *g, const float *beta, const float *state0, const float *gy,
+            const float *dstate_out, float *grad_packed, void *ws, size_t ws_bytes,
+            unsigned flags, gdn_stream_t stream) {
+    int rc = validate(p);
+    if (rc != GDN_OK) return rc;
+    if (flags & ~GDN_BWD_REUSE_SNAPSHOTS) return GDN_ERR_ARG;
+    const Plan pl = make_plan(p);
+    const int64_t n = p->n_seqs, T = p->T, Hk = p->H_k, Hv = p->H_v, S = p->S_v;
+    if (!q || !k || !v || !g || !beta || !state0 || !gy || !grad_packed) return GDN_ERR_ARG;
+    const void *ptrs[] = {q, k, v, g, beta, state0, gy, dstate_out, grad_packed};
+    for (auto *x : ptrs)
+        if (x && !aligned4(x)) return GDN_ERR_UNSUPPORTED;
+    if (ws_bytes < pl.total) return GDN_ERR_WORKSPACE;
+    if (!ws || ((uintptr_t)ws % 16) != 0) return GDN_ERR_ARG;
+
+    size_t off[6];
+    const size_t total = gdn_grad_packed_floats(p, off);
+    const Range in[] = {span_tok(q, p->q, n, T, Hk, S),      span_tok(k, p->k, n, T, Hk, S),
+                        span_tok(v, p->v, n, T, Hv, S),      span_tok(g, p->g, n, T, Hv, pl.G),
+                        span_tok(beta, p->beta, n, T, Hv, 1), span_flat(state0, n * Hv * S * S),
+                        span_tok(gy, p->gy, n, T, Hv, S),    span_flat(dstate_out, n * Hv * S * S)};
+    const Range outg = span_flat(grad_packed, (int64_t)total);
+    const Range wsr = span_bytes(ws, pl.total);
+    for (auto &i : in)
+        if (overlap(outg, i) || overlap(wsr, i)) return GDN_ERR_ARG;
+    if (overlap(outg, wsr)) return GDN_ERR_ARG;
+
+    float *dq = grad_packed + off[0], *dk = grad_packed + off[1], *dv = grad_packed + off[2];
+    float *dg = grad_packed + off[3], *dbeta = grad_packed + off[4], *dstate = grad_packed + off[5];
+    float *snap = (float *)((char *)ws + pl.off_snap);
+    const bool kda = p->gate == GDN_GATE_KDA;
+
+    for (int s0 = 0; s0 < p->n_seqs; s0 += gdn::kMaxSeqsPerLaunch) {
+        const int cnt = std::min(gdn::kMaxSeqsPerLaunch, p->n_seqs - s0);
+        if (!(flags & GDN_BWD_REUSE_SNAPSHOTS)) {
+            gdn::FwdArgs f;
+            std::memset(&f, 0, sizeof(f));
+            f.q = q; f.k = k; f.v = v; f.g = g; f.beta = beta; f.state0 = state0;
+            f.snap = snap;
+            f.sq = p->q; f.sk = p->k; f.sv = p->v; f.sg = p->g; f.sb = p->beta; f.sy = p->y;
+            f.s_base = s0;
+            f.T = p->T; f.H_k = p->H_k; f.H_v = p->H_v; f.C = pl.C; f.n_ck_max = pl.n_ck_max;
+            f.scale = p->scale;
+            fill_lens(p, s0, cnt, f.lens);
+            rc = device_status(gdn::launch_fwd(f, (int)S, kda, cnt, (hipStream_t)stream));
+            if (rc != GDN_OK) return rc;
+        }
+        gdn::BwdArgs b;
+        std::memset(&b, 0, sizeof(b));
+        b.q = q; b.k = k; b.v = v; b.g = g; b.beta = beta; b.gy = gy; b.dstate_out = dstate_out;
+        b.snap = snap;
+        b.segbuf = (float *)((char *)ws + pl.off_seg);
+        b.ebuf = (float *)((char *)ws + pl.off_e);
+        if (pl.parts) {
+            b.dq = (float *)((char *)ws + pl.off_pq);
+            b.dk = (float *)((char *)ws + pl.off_pk);
+            b.dqk_head = p->H_v;
+        } else {
+            b.dq = dq;
+            b.dk = dk;
+            b.dqk_head = p->H_k;
+        }
+        b.dv = dv; b.dg = dg; b.dbeta = dbeta; b.dstate = dstate;
+        b.sq = p->q; b.sk = p->k; b.sv = p->v; b.sg = p->g; b.sb = p->beta; b.sgy = p->gy;
+        b.s_base = s0;
+        b.T = p->T; b.H_k = p->H_k; b.H_v = p->H_v; b.C = pl.C; b.n_ck_max = pl.n_ck_max;
+        b.scale = p->scale;
+        fill_lens(p, s0, cnt, b.lens);
+        rc = device_status(gdn::launch_bwd(b, (int)S, kda, cnt, (hipStream_t)stream));
+        if (rc != GDN_OK) return rc;
+    }
+    if (pl.parts) {
+        gdn::CombineArgs c;
+        c.dq_part = (const float *)((char *)ws + pl.off_pq);
+        c.dk_part = (const float *)((char *)ws + pl.off_pk);
+        c.dq = dq; c.dk = dk;
+        c.n_seqs = p->n_seqs; c.T = p->T; c.H_k = p->H_k; c.H_v = p->H_v; c.S = (int)S;
+        rc = device_status(gdn::launch_combine(c, (hipStream_t)stream));
+        if (rc != GDN_OK) return rc;
+    }
+    return GDN_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,55 @@
+// gdn_internal.h -- argument blocks shared by the host side of the C ABI and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gdn.h"
+
+namespace gdn {
+
+// Sequences handled by one launch; their lengths travel in the kernel argument block.
+constexpr int kMaxSeqsPerLaunch = 256;
+
+// Arguments of the forward scan (also used, with y == nullptr, as the checkpoint pass
+// of the backward).
+struct FwdArgs {
+    const float *q, *k, *v, *g, *beta, *state0;
+    float *y;          // nullptr: do not write y
+    float *state_out;  // nullptr: do not write the final state
+    float *snap;       // [unit][n_ck_max][S][S] snapshots (state before tokens 0, C, 2C, ...)
+    gdn_strides sq, sk, sv, sg, sb, sy;
+    int32_t s_base;    // first sequence of this launch
+    int32_t T, H_k, H_v, C, n_ck_max;
+    float scale;
+    int32_t lens[kMaxSeqsPerLaunch];
+};
+
+// Arguments of the backward walk.
+struct BwdArgs {
+    const float *q, *k, *v, *g, *beta, *gy, *dstate_out;
+    const float *snap;  // [unit][n_ck_max][S][S]
+    float *segbuf;      // [unit][C][S][S] decayed previous state Mp of each segment token
+    float *ebuf;        // [unit][C][S] prediction errors v - u of the current segment
+    float *dq, *dk;     // direct outputs (H_v == H_k) or per-value-head partials
+    int64_t dqk_head;   // head count of the dq/dk arrays (H_k direct, H_v for partials)
+    float *dv, *dg, *dbeta, *dstate;
+    gdn_strides sq, sk, sv, sg, sb, sgy;
+    int32_t s_base;
+    int32_t T, H_k, H_v, C, n_ck_max;
+    float scale;
+    int32_t lens[kMaxSeqsPerLaunch];
+};
+
+// Sum of the value heads of each key head (fixed increasing order) for dq and dk.
+struct CombineArgs {
+    const float *dq_part, *dk_part;  // [n_seqs][T][H_v][S]
+    float *dq, *dk;                  // [n_seqs][T][H_k][S]
+    int32_t n_seqs, T, H_k, H_v, S;
+};
+
+hipError_t launch_fwd(const FwdArgs &a, int S, bool kda, int n_seqs_launch, hipStream_t st);
+hipError_t launch_bwd(const BwdArgs &a, int S, bool kda, int n_seqs_launch, hipStream_t st);
+hipError_t launch_combine(const CombineArgs &a, hipStream_t st);
+
+}  // namespace gdn

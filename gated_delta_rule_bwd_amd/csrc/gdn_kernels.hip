@@ -1,0 +1,478 @@
+// gdn_kernels.hip -- HIP kernels (gfx950) of the gated delta rule forward scan and its
+// checkpointed backward.
+//
+// Work decomposition.  One workgroup owns one (sequence, value head) unit and its S x S
+// fp32 state M = S^T (row j = value index, column i = key index).  Rows of M evolve
+// independently in both directions of the recurrence ("metal: GATED_DELTA_NET_BACK",
+// approval review: thread j owns row j), so the state is spread over the workgroup by rows:
+// a row lives on LPR = 16 lanes (one DPP row), each lane holding NC = S/16 of its columns
+// (interleaved, column c = lane%16 + 16 n, so that a token vector load is coalesced), and
+// each lane holds R = 4 rows.  A wave therefore holds 4 row groups x 4 rows = 16 rows and
+// a unit needs S/16 waves.
+//   - Row reductions (u = Mp k, y = M q, dd = dM k) stay inside one DPP row: four DPP adds.
+//   - Column reductions (dq, dk, per-channel dg), which sum over rows, go in-lane over the
+//     4 rows, across the 4 row groups with permlane16/permlane32 swaps, and across waves
+//     through LDS, in a fixed order: no atomics, bitwise reproducible.
+// The state and its gradient stay in VGPRs for the whole walk.
+//
+// Backward schedule (checkpointed recompute, C ~ sqrt(T), PR description of the same page):
+// the forward leaves a snapshot of M before tokens 0, C, 2C, ... in the workspace; for each
+// segment, last first, the backward replays the segment from its snapshot, keeping the
+// decayed previous state Mp = M_{t-1} .* a of every token and the prediction error
+// e = v - u of every row, and then walks the segment in reverse (the state after the token
+// is rebuilt as Mp + delta k^T, the same fma the forward executed).
+#include <hip/hip_runtime.h>
+
+#include "gdn_internal.h"
+
+namespace gdn {
+namespace {
+
+template <int S, int R>
+struct Layout {
+    static constexpr int LPR = 16;         // lanes per row
+    static constexpr int NC = S / LPR;     // columns per lane
+    static constexpr int RG = 64 / LPR;    // row groups per wave
+    static constexpr int RPW = RG * R;     // rows per wave
+    static constexpr int NW = S / RPW;     // waves per unit
+    static constexpr int THREADS = NW * 64;
+    static_assert(S % RPW == 0 && NC >= 1, "unsupported head size");
+};
+
+__device__ __forceinline__ float as_f(int x) { return __builtin_bit_cast(float, x); }
+__device__ __forceinline__ int as_i(float x) { return __builtin_bit_cast(int, x); }
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return as_f(__builtin_amdgcn_mov_dpp(as_i(v), CTRL, 0xF, 0xF, true));
+}
+
+// Sum over the 16 lanes of a DPP row; every lane receives the sum.
+__device__ __forceinline__ float row16_sum(float v) {
+    v += dpp<0xB1>(v);   // quad_perm [1,0,3,2]
+    v += dpp<0x4E>(v);   // quad_perm [2,3,0,1]
+    v += dpp<0x141>(v);  // row_half_mirror: pairs the two quads of each half row
+    v += dpp<0x140>(v);  // row_mirror: pairs the two halves of the row
+    return v;
+}
+
+// Sum over lanes l, l^16, l^32, l^48 (the 4 row groups of a wave); every lane receives it.
+__device__ __forceinline__ float groups4_sum(float v) {
+    auto p = __builtin_amdgcn_permlane16_swap(as_i(v), as_i(v), false, false);
+    v = as_f(p[0]) + as_f(p[1]);
+    auto q = __builtin_amdgcn_permlane32_swap(as_i(v), as_i(v), false, false);
+    return as_f(q[0]) + as_f(q[1]);
+}
+
+// ------------------------------------------------------------------ forward scan
+
+template <int S, int R, bool KDA>
+__global__ void __launch_bounds__((Layout<S, R>::THREADS))
+fwd_kernel(const FwdArgs a) {
+    using Lo = Layout<S, R>;
+    constexpr int NC = Lo::NC, LPR = Lo::LPR;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lc = lane % LPR, rg = lane / LPR;
+    const int sl = blockIdx.x / a.H_v, h = blockIdx.x % a.H_v;
+    const int64_t s = a.s_base + sl;
+    const int hk = h % a.H_k;
+    const int L = a.lens[sl];
+    const int row0 = wave * Lo::RPW + rg * R;
+    const int64_t unit = s * a.H_v + h;
+
+    const float *qp = a.q + s * a.sq.seq + hk * a.sq.head + lc;
+    const float *kp = a.k + s * a.sk.seq + hk * a.sk.head + lc;
+    const float *vp = a.v + s * a.sv.seq + h * a.sv.head + row0;
+    const float *gp = a.g + s * a.sg.seq + h * a.sg.head + (KDA ? lc : 0);
+    const float *bp = a.beta + s * a.sb.seq + h * a.sb.head;
+
+    float M[R][NC];
+    const float *st0 = a.state0 + unit * S * S + (int64_t)row0 * S + lc;
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int n = 0; n < NC; ++n) M[r][n] = st0[r * S + n * LPR];
+
+    float *snap = a.snap + unit * a.n_ck_max * S * S + (int64_t)row0 * S + lc;
+    int until_snap = 0;
+    for (int t = 0; t < L; ++t) {
+        if (until_snap == 0) {
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+#pragma unroll
+                for (int n = 0; n < NC; ++n) snap[r * S + n * LPR] = M[r][n];
+            snap += (int64_t)S * S;
+            until_snap = a.C;
+        }
+        --until_snap;
+        float qv[NC], kv[NC], av[NC], vv[R];
+#pragma unroll
+        for (int n = 0; n < NC; ++n) {
+            qv[n] = qp[t * a.sq.tok + n * LPR];
+            kv[n] = kp[t * a.sk.tok + n * LPR];
+        }
+        if constexpr (KDA) {
+#pragma unroll
+            for (int n = 0; n < NC; ++n) av[n] = expf(gp[t * a.sg.tok + n * LPR]);
+        } else {
+            const float a0 = expf(gp[t * a.sg.tok]);
+#pragma unroll
+            for (int n = 0; n < NC; ++n) av[n] = a0;
+        }
+#pragma unroll
+        for (int r = 0; r < R; ++r) vv[r] = vp[t * a.sv.tok + r];
+        const float beta = bp[t * a.sb.tok];
+
+        float ak[NC];
+#pragma unroll
+        for (int n = 0; n < NC; ++n) ak[n] = av[n] * kv[n];
+        float yr[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            float u = 0.f;
+#pragma unroll
+            for (int n = 0; n < NC; ++n) u = fmaf(M[r][n], ak[n], u);
+            u = row16_sum(u);
+            const float delta = beta * (vv[r] - u);
+            float y = 0.f;
+#pragma unroll
+            for (int n = 0; n < NC; ++n) {
+                M[r][n] = fmaf(delta, kv[n], M[r][n] * av[n]);
+                y = fmaf(M[r][n], qv[n], y);
+            }
+            yr[r] = y;
+        }
+        if (a.y) {
+#pragma unroll
+            for (int r = 0; r < R; ++r) yr[r] = row16_sum(yr[r]);
+            if (lc == 0) {
+                float *yp = a.y + s * a.sy.seq + (int64_t)t * a.sy.tok + h * a.sy.head + row0;
+#pragma unroll
+                for (int r = 0; r < R; ++r) yp[r] = a.scale * yr[r];
+            }
+        }
+    }
+    if (a.y) {
+        for (int64_t t = L; t < a.T; ++t) {
+            if (lc == 0) {
+                float *yp = a.y + s * a.sy.seq + t * a.sy.tok + h * a.sy.head + row0;
+#pragma unroll
+                for (int r = 0; r < R; ++r) yp[r] = 0.f;
+            }
+        }
+    }
+    if (a.state_out) {
+        float *so = a.state_out + unit * S * S + (int64_t)row0 * S + lc;
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int n = 0; n < NC; ++n) so[r * S + n * LPR] = M[r][n];
+    }
+}
+
+// ------------------------------------------------------------------ backward walk
+
+template <int S, int R, bool KDA>
+__global__ void __launch_bounds__((Layout<S, R>::THREADS))
+bwd_kernel(const BwdArgs a) {
+    using Lo = Layout<S, R>;
+    constexpr int NC = Lo::NC, LPR = Lo::LPR, NW = Lo::NW, RG = Lo::RG;
+    constexpr int G = KDA ? S : 1;
+    // column partial sums per wave: [parity][wave][dq | dk | dg][column]
+    __shared__ float red[2][NW][3][S];
+    __shared__ float redb[2][NW * RG];   // dbeta partials per row group
+    __shared__ float redg[2][NW];        // scalar-gate dg partials per wave
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int lc = lane % LPR, rg = lane / LPR;
+    const int sl = blockIdx.x / a.H_v, h = blockIdx.x % a.H_v;
+    const int64_t s = a.s_base + sl;
+    const int hk = h % a.H_k;
+    const int L = a.lens[sl];
+    const int row0 = wave * Lo::RPW + rg * R;
+    const int64_t unit = s * a.H_v + h;
+    const int C = a.C;
+
+    const float *qp = a.q + s * a.sq.seq + hk * a.sq.head + lc;
+    const float *kp = a.k + s * a.sk.seq + hk * a.sk.head + lc;
+    const float *vp = a.v + s * a.sv.seq + h * a.sv.head + row0;
+    const float *gp = a.g + s * a.sg.seq + h * a.sg.head + (KDA ? lc : 0);
+    const float *bp = a.beta + s * a.sb.seq + h * a.sb.head;
+    const float *gyp = a.gy + s * a.sgy.seq + h * a.sgy.head + row0;
+
+    float dM[R][NC];
+    if (a.dstate_out) {
+        const float *d0 = a.dstate_out + unit * S * S + (int64_t)row0 * S + lc;
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int n = 0; n < NC; ++n) dM[r][n] = d0[r * S + n * LPR];
+    } else {
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int n = 0; n < NC; ++n) dM[r][n] = 0.f;
+    }
+
+    float *seg = a.segbuf + unit * C * S * S + (int64_t)row0 * S + lc;
+    float *eb = a.ebuf + unit * C * S + row0;
+    const int n_ck = (L + C - 1) / C;
+    int parity = 0;
+
+    for (int sg = n_ck - 1; sg >= 0; --sg) {
+        const int t0 = sg * C, t1 = min(t0 + C, L);
+        // ---- replay the segment from its snapshot
+        {
+            float M[R][NC];
+            const float *sp = a.snap + (unit * a.n_ck_max + sg) * S * S + (int64_t)row0 * S + lc;
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+#pragma unroll
+                for (int n = 0; n < NC; ++n) M[r][n] = sp[r * S + n * LPR];
+            for (int t = t0; t < t1; ++t) {
+                float kv[NC], av[NC], vv[R];
+#pragma unroll
+                for (int n = 0; n < NC; ++n) kv[n] = kp[t * a.sk.tok + n * LPR];
+                if constexpr (KDA) {
+#pragma unroll
+                    for (int n = 0; n < NC; ++n) av[n] = expf(gp[t * a.sg.tok + n * LPR]);
+                } else {
+                    const float a0 = expf(gp[t * a.sg.tok]);
+#pragma unroll
+                    for (int n = 0; n < NC; ++n) av[n] = a0;
+                }
+#pragma unroll
+                for (int r = 0; r < R; ++r) vv[r] = vp[t * a.sv.tok + r];
+                const float beta = bp[t * a.sb.tok];
+                float ak[NC];
+#pragma unroll
+                for (int n = 0; n < NC; ++n) ak[n] = av[n] * kv[n];
+                float *dst = seg + (int64_t)(t - t0) * S * S;
+                float *edst = eb + (t - t0) * S;
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    float u = 0.f;
+#pragma unroll
+                    for (int n = 0; n < NC; ++n) u = fmaf(M[r][n], ak[n], u);
+                    u = row16_sum(u);
+                    const float e = vv[r] - u;
+                    const float delta = beta * e;
+#pragma unroll
+                    for (int n = 0; n < NC; ++n) {
+                        const float mp = M[r][n] * av[n];
+                        M[r][n] = fmaf(delta, kv[n], mp);
+                        dst[r * S + n * LPR] = mp;  // keep the decayed previous state
+                    }
+                    if (lc == 0) edst[r] = e;
+                }
+            }
+        }
+        __threadfence_block();
+        __syncthreads();
+
+        // ---- reverse walk over the segment
+        for (int t = t1 - 1; t >= t0; --t) {
+            float qv[NC], kv[NC], av[NC], gyv[R], ev[R], Mp[R][NC];
+#pragma unroll
+            for (int n = 0; n < NC; ++n) {
+                qv[n] = qp[t * a.sq.tok + n * LPR];
+                kv[n] = kp[t * a.sk.tok + n * LPR];
+            }
+            if constexpr (KDA) {
+#pragma unroll
+                for (int n = 0; n < NC; ++n) av[n] = expf(gp[t * a.sg.tok + n * LPR]);
+            } else {
+                const float a0 = expf(gp[t * a.sg.tok]);
+#pragma unroll
+                for (int n = 0; n < NC; ++n) av[n] = a0;
+            }
+            const float beta = bp[t * a.sb.tok];
+            const float *src = seg + (int64_t)(t - t0) * S * S;
+            const float *esrc = eb + (t - t0) * S;
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                gyv[r] = a.scale * gyp[t * a.sgy.tok + r];
+                ev[r] = esrc[r];
+#pragma unroll
+                for (int n = 0; n < NC; ++n) Mp[r][n] = src[r * S + n * LPR];
+            }
+
+            float pq[NC], pk[NC], pg[NC], dd[R];
+#pragma unroll
+            for (int n = 0; n < NC; ++n) pq[n] = pk[n] = pg[n] = 0.f;
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const float delta = beta * ev[r];
+                float d = 0.f;
+#pragma unroll
+                for (int n = 0; n < NC; ++n) {
+                    const float mt = fmaf(delta, kv[n], Mp[r][n]);  // M_t = Mp + delta k^T
+                    dM[r][n] = fmaf(gyv[r], qv[n], dM[r][n]);     // dM += scale gy q^T
+                    pq[n] = fmaf(mt, gyv[r], pq[n]);              // dq += M_t^T (scale gy)
+                    d = fmaf(dM[r][n], kv[n], d);                 // dd = dM k
+                }
+                dd[r] = row16_sum(d);
+            }
+            float pb = 0.f;
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const float delta = beta * ev[r];
+                const float du = -beta * dd[r];
+                pb = fmaf(dd[r], ev[r], pb);                      // dbeta = dd . (v - u)
+#pragma unroll
+                for (int n = 0; n < NC; ++n) {
+                    pk[n] = fmaf(dM[r][n], delta, pk[n]);         // dk += dM^T delta
+                    pk[n] = fmaf(Mp[r][n], du, pk[n]);            //     + Mp^T du
+                    dM[r][n] = fmaf(du, kv[n], dM[r][n]);         // dM += du k^T
+                    pg[n] = fmaf(dM[r][n], Mp[r][n], pg[n]);      // dg = sum dM .* Mp
+                    dM[r][n] *= av[n];                            // dM = dM .* a
+                }
+            }
+            if (lc == 0) {
+                float *dvp = a.dv + ((s * a.T + t) * a.H_v + h) * S + row0;
+#pragma unroll
+                for (int r = 0; r < R; ++r) dvp[r] = beta * dd[r];
+                redb[parity][wave * RG + rg] = pb;
+            }
+#pragma unroll
+            for (int n = 0; n < NC; ++n) {
+                pq[n] = groups4_sum(pq[n]);
+                pk[n] = groups4_sum(pk[n]);
+            }
+            if constexpr (KDA) {
+#pragma unroll
+                for (int n = 0; n < NC; ++n) pg[n] = groups4_sum(pg[n]);
+            } else {
+                float gs = 0.f;
+#pragma unroll
+                for (int n = 0; n < NC; ++n) gs += pg[n];
+                gs = groups4_sum(row16_sum(gs));
+                if (lane == 0) redg[parity][wave] = gs;
+            }
+            if (rg == 0) {
+#pragma unroll
+                for (int n = 0; n < NC; ++n) {
+                    red[parity][wave][0][lc + n * LPR] = pq[n];
+                    red[parity][wave][1][lc + n * LPR] = pk[n];
+                    if constexpr (KDA) red[parity][wave][2][lc + n * LPR] = pg[n];
+                }
+            }
+            __syncthreads();
+            const int64_t row_tok = s * a.T + t;
+            for (int idx = tid; idx < (KDA ? 3 : 2) * S; idx += Lo::THREADS) {
+                const int which = idx / S, i = idx % S;
+                float acc = 0.f;
+#pragma unroll
+                for (int w = 0; w < NW; ++w) acc += red[parity][w][which][i];
+                if (which == 0)
+                    a.dq[(row_tok * a.dqk_head + h) * S + i] = acc;
+                else if (which == 1)
+                    a.dk[(row_tok * a.dqk_head + h) * S + i] = acc;
+                else
+                    a.dg[(row_tok * a.H_v + h) * G + i] = acc;
+            }
+            if (tid == Lo::THREADS - 1) {
+                float acc = 0.f;
+#pragma unroll
+                for (int w = 0; w < NW * RG; ++w) acc += redb[parity][w];
+                a.dbeta[row_tok * a.H_v + h] = acc;
+                if constexpr (!KDA) {
+                    float g = 0.f;
+#pragma unroll
+                    for (int w = 0; w < NW; ++w) g += redg[parity][w];
+                    a.dg[row_tok * a.H_v + h] = g;
+                }
+            }
+            parity ^= 1;
+        }
+    }
+
+    {
+        float *ds = a.dstate + unit * S * S + (int64_t)row0 * S + lc;
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int n = 0; n < NC; ++n) ds[r * S + n * LPR] = dM[r][n];
+    }
+    // padded tokens: every per-token output row of this unit is written zero
+    for (int64_t t = L; t < a.T; ++t) {
+        const int64_t row_tok = s * a.T + t;
+        for (int i = tid; i < S; i += Lo::THREADS) {
+            a.dq[(row_tok * a.dqk_head + h) * S + i] = 0.f;
+            a.dk[(row_tok * a.dqk_head + h) * S + i] = 0.f;
+            a.dv[(row_tok * a.H_v + h) * S + i] = 0.f;
+        }
+        for (int i = tid; i < G; i += Lo::THREADS) a.dg[(row_tok * a.H_v + h) * G + i] = 0.f;
+        if (tid == 0) a.dbeta[row_tok * a.H_v + h] = 0.f;
+    }
+}
+
+// ------------------------------------------------------------------ grouped-head sum
+
+__global__ void __launch_bounds__(256) combine_kernel(const CombineArgs a) {
+    const int64_t total = (int64_t)a.n_seqs * a.T * a.H_k * a.S;
+    for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+         idx += (int64_t)gridDim.x * blockDim.x) {
+        const int i = (int)(idx % a.S);
+        const int64_t rest = idx / a.S;
+        const int hk = (int)(rest % a.H_k);
+        const int64_t st = rest / a.H_k;
+        float q = 0.f, k = 0.f;
+        for (int h = hk; h < a.H_v; h += a.H_k) {  // increasing value head
+            const int64_t src = (st * a.H_v + h) * a.S + i;
+            q += a.dq_part[src];
+            k += a.dk_part[src];
+        }
+        a.dq[idx] = q;
+        a.dk[idx] = k;
+    }
+}
+
+template <typename Args>
+hipError_t launch(const void *fn, const Args &args, int blocks, int threads, hipStream_t st) {
+    if (blocks <= 0) return hipSuccess;
+    void *params[] = {const_cast<Args *>(&args)};
+    return hipLaunchKernel(fn, dim3(blocks), dim3(threads), params, 0, st);
+}
+
+template <int S, int R>
+constexpr int kThreads = Layout<S, R>::THREADS;
+
+}  // namespace
+
+hipError_t launch_fwd(const FwdArgs &a, int S, bool kda, int n_seqs_launch, hipStream_t st) {
+    const int blocks = n_seqs_launch * a.H_v;
+    switch (S * 2 + (kda ? 1 : 0)) {
+        case 64: return launch((const void *)fwd_kernel<32, 4, false>, a, blocks, kThreads<32, 4>, st);
+        case 65: return launch((const void *)fwd_kernel<32, 4, true>, a, blocks, kThreads<32, 4>, st);
+        case 128: return launch((const void *)fwd_kernel<64, 4, false>, a, blocks, kThreads<64, 4>, st);
+        case 129: return launch((const void *)fwd_kernel<64, 4, true>, a, blocks, kThreads<64, 4>, st);
+        case 256: return launch((const void *)fwd_kernel<128, 4, false>, a, blocks, kThreads<128, 4>, st);
+        case 257: return launch((const void *)fwd_kernel<128, 4, true>, a, blocks, kThreads<128, 4>, st);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_bwd(const BwdArgs &a, int S, bool kda, int n_seqs_launch, hipStream_t st) {
+    const int blocks = n_seqs_launch * a.H_v;
+    switch (S * 2 + (kda ? 1 : 0)) {
+        case 64: return launch((const void *)bwd_kernel<32, 4, false>, a, blocks, kThreads<32, 4>, st);
+        case 65: return launch((const void *)bwd_kernel<32, 4, true>, a, blocks, kThreads<32, 4>, st);
+        case 128: return launch((const void *)bwd_kernel<64, 4, false>, a, blocks, kThreads<64, 4>, st);
+        case 129: return launch((const void *)bwd_kernel<64, 4, true>, a, blocks, kThreads<64, 4>, st);
+        case 256: return launch((const void *)bwd_kernel<128, 4, false>, a, blocks, kThreads<128, 4>, st);
+        case 257: return launch((const void *)bwd_kernel<128, 4, true>, a, blocks, kThreads<128, 4>, st);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_combine(const CombineArgs &a, hipStream_t st) {
+    const int64_t total = (int64_t)a.n_seqs * a.T * a.H_k * a.S;
+    if (total <= 0) return hipSuccess;
+    int64_t blocks = (total + 255) / 256;
+    if (blocks > 8192) blocks = 8192;
+    return launch((const void *)combine_kernel, a, (int)blocks, 256, st);
+}
+
+}  // namespace gdn

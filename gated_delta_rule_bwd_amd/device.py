@@ -1,0 +1,75 @@
+"""Device placement of a workload: torch supplies the memory, the binding the calls.
+
+``DeviceCase`` puts seeded inputs (``inputs.py``) on the GPU in the workload's layout
+(contiguous, or q/k/v as row views of one packed buffer), allocates the outputs, the
+packed gradient buffer and the workspace once, and runs the forward and backward through
+the C ABI.  No arithmetic of the method happens here.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import binding as B
+from .inputs import Workload, pack_qkv
+
+
+class DeviceCase:
+    def __init__(self, w: Workload, arrays: dict, device="cuda", C=None, strided_gy=False,
+                 packed=None):
+        self.w = w
+        n, T, Hk, Hv, S, G = w.n_seqs, w.T, w.H_k, w.H_v, w.S, w.G
+        dev = torch.device(device)
+        packed = w.packed if packed is None else packed
+
+        def put(a):
+            return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+        if packed:
+            self.qkv = put(pack_qkv(w, arrays["q"], arrays["k"], arrays["v"]))
+            W = w.packed_width
+            HkS = Hk * S
+            self.q = self.qkv[:, :, :HkS].unflatten(2, (Hk, S))
+            self.k = self.qkv[:, :, HkS:2 * HkS].unflatten(2, (Hk, S))
+            self.v = self.qkv[:, :, 2 * HkS:].unflatten(2, (Hv, S))
+            assert self.q.stride() == (T * W, W, S, 1)
+        else:
+            self.qkv = None
+            self.q, self.k, self.v = put(arrays["q"]), put(arrays["k"]), put(arrays["v"])
+        self.g = put(arrays["g"].reshape(n, T, Hv, G))
+        self.beta = put(arrays["beta"])
+        self.state0 = put(arrays["state0"])
+        if strided_gy:
+            # gy as a view with head-major order and a padded token stride
+            base = torch.zeros((n, Hv, T, S + 8), dtype=torch.float32, device=dev)
+            self.gy = base[..., :S].permute(0, 2, 1, 3)
+            self.gy.copy_(put(arrays["gy"]))
+        else:
+            self.gy = put(arrays["gy"])
+        self.dstate_out = put(arrays["dstate_out"]) if arrays.get("dstate_out") is not None else None
+        self.y = torch.empty((n, T, Hv, S), dtype=torch.float32, device=dev)
+        self.state_out = torch.empty((n, Hv, S, S), dtype=torch.float32, device=dev)
+        self.p = B.Problem.from_tensors(self.q, self.k, self.v, self.g, self.beta,
+                                        C=w.C if C is None else C, scale=w.scale,
+                                        seq_lens=list(w.lens), gy=self.gy, y=self.y)
+        self.ws = torch.empty(max(B.workspace_size(self.p), 256), dtype=torch.uint8, device=dev)
+        total, _ = B.grad_layout(self.p)
+        self.grad = torch.empty(max(total, 1), dtype=torch.float32, device=dev)
+
+    def fwd(self, stream=None):
+        B.fwd(self.p, self.q, self.k, self.v, self.g, self.beta, self.state0, self.y,
+              self.state_out, self.ws, stream)
+
+    def bwd(self, reuse=True, stream=None):
+        B.bwd(self.p, self.q, self.k, self.v, self.g, self.beta, self.state0, self.gy,
+              self.dstate_out, self.grad, self.ws,
+              B.BWD_REUSE_SNAPSHOTS if reuse else 0, stream)
+
+    def grads(self):
+        return B.unpack_grads(self.p, self.grad)
+
+    def results_numpy(self):
+        """Everything the two calls produced, as float32 numpy arrays."""
+        out = {"y": self.y, "state_out": self.state_out}
+        out.update(self.grads())
+        return {k: v.detach().cpu().numpy() for k, v in out.items()}

@@ -1,0 +1,145 @@
+/*
+ * gdn.h -- C ABI of the gated delta rule (forward scan and checkpointed backward) on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation (per sequence s and value head h; key head hk = h mod H_k, the head map
+ * "iv1 % neq1" of the first review of "metal: GATED_DELTA_NET_BACK"; the state is kept as
+ * M = S^T, S_v rows j by S_k columns i, as in that page's approval review):
+ *
+ *   forward, per token t (decay before correction; meTile "Training kernels and gradients",
+ *   section "Recurrent delta attention"):
+ *       a = exp(g_t)  (per key channel, or one scalar)      Mp = M .* a  (column scaling)
+ *       u = Mp k_t,   delta = beta_t (v_t - u),   M = Mp + delta k_t^T,   y_t = scale M q_t
+ *   backward (the term-by-term math of the same PR's first review): seeded with
+ *   dM = dstate_out at t = len, walking t downwards:
+ *       dM += scale gy_t q_t^T;   dq_t += scale M_t^T gy_t;   dd = dM k_t;   dv_t = beta dd;
+ *       du = -beta dd;   dbeta_t = dd . (v_t - u);   dk_t += dM^T delta + Mp^T du (dM before
+ *       the next update);   dM += du k_t^T;   dg_t = sum_j dM .* Mp (per column, or in total
+ *       for the scalar gate);   dM = dM .* a;     and dstate = dM after token 0.
+ *   The backward recomputes states from snapshots taken every C tokens (C ~ sqrt(T), the
+ *   PR description); the snapshot interval changes memory and time, not the result.
+ *
+ * All floating point data is fp32.  Index arithmetic is 64-bit.
+ *
+ * Ownership and concurrency
+ *   - The caller owns every buffer.  The library allocates nothing and keeps no state
+ *     between calls.
+ *   - Calls are asynchronous on the given HIP stream (NULL = the legacy default stream);
+ *     results are valid once the stream has passed the call.  Faults surface at the
+ *     caller's synchronisation.
+ *   - The workspace belongs to one call at a time; it may be reused once the stream has
+ *     passed the call.  A workspace written by gdn_fwd holds that call's state snapshots
+ *     (see GDN_BWD_REUSE_SNAPSHOTS).
+ *   - Outputs (y, state_out, grad_packed) must not overlap any input, the workspace or each
+ *     other; the host checks the address ranges and returns GDN_ERR_ARG on overlap.
+ *     Inputs and cotangents are never written.
+ *   - Inputs must be finite for the results to be meaningful (no NaN checks).  Values at
+ *     padded tokens (t >= len_s) are never read.
+ *
+ * Errors are synchronous return codes, checked before anything is enqueued: a non-zero
+ * return means no work was enqueued.
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define GDN_OK 0
+#define GDN_ERR_ARG (-1)         /* a NULL required pointer, a bad size, an overlap       */
+#define GDN_ERR_UNSUPPORTED (-2) /* outside the verified envelope (see gdn_problem)      */
+#define GDN_ERR_WORKSPACE (-3)   /* ws_bytes below gdn_workspace_size()                 */
+#define GDN_ERR_DEVICE (-4)      /* the HIP runtime refused a launch                     */
+
+/* Gate kinds (meTile "Recurrent delta attention": a scalar log-decay per token and head is
+ * Gated DeltaNet, a per-key-channel log-decay is the Kimi Delta Attention core). */
+#define GDN_GATE_SCALAR 0
+#define GDN_GATE_KDA 1
+
+/* gdn_bwd flags. */
+#define GDN_BWD_REUSE_SNAPSHOTS 1u /* ws holds the snapshots written by gdn_fwd on the same
+                                      problem and inputs: skip the checkpoint pass */
+
+/* HIP stream handle (hipStream_t); declared here so that this header needs no HIP header. */
+typedef struct ihipStream_t *gdn_stream_t;
+
+/* Strides of a per-token tensor, in elements (floats).  The innermost (feature) stride is
+ * always 1.  Element (s, t, head, i) lives at base + s*seq + t*tok + head*head_ + i.
+ * Strides must be non-negative.  This admits row views into a packed buffer, as when q and
+ * k are views of one mixed projection ("metal: GATED_DELTA_NET_BACK", first review). */
+typedef struct gdn_strides {
+    int64_t seq, tok, head;
+} gdn_strides;
+
+/* Problem description.
+ *   n_seqs      number of sequences (>= 0); lengths are padded to T
+ *   T           padded sequence length (>= 0)
+ *   H_k, H_v    key and value head counts; H_v must be a multiple of H_k (grouped heads:
+ *               value head h reads key head h mod H_k)
+ *   S_k, S_v    key and value head sizes; supported: S_k == S_v in {32, 64, 128}
+ *   gate        GDN_GATE_SCALAR (g is [.., H_v], one value per token and head) or
+ *               GDN_GATE_KDA (g is [.., H_v, S_k])
+ *   C           checkpoint interval in tokens; 0 selects ceil(sqrt(T)); values above T
+ *               act as T (one segment)
+ *   scale       output scale (commonly 1/sqrt(S_k))
+ *   seq_lens    HOST pointer to n_seqs lengths in [0, T], or NULL for all T
+ *   q, k        strides of q, k   (head counts H_k, width S_k)
+ *   v           strides of v      (H_v, S_v)
+ *   g           strides of g      (H_v, width S_k or 1)
+ *   beta        strides of beta   (H_v, width 1)
+ *   gy          strides of the output cotangent (H_v, S_v); used by gdn_bwd only
+ *   y           strides of the output y (H_v, S_v); used by gdn_fwd only
+ * State tensors (state0, state_out, dstate_out, dstate) are contiguous
+ * [n_seqs][H_v][S_v][S_k] in the M = S^T orientation (row = value index). */
+typedef struct gdn_problem {
+    int32_t n_seqs, T, H_k, H_v, S_k, S_v, gate, C;
+    float scale;
+    const int32_t *seq_lens;
+    gdn_strides q, k, v, g, beta, gy, y;
+} gdn_problem;
+
+/* Bytes of device workspace that gdn_fwd and gdn_bwd need for this problem (0 on an
+ * invalid problem).  The same workspace serves both calls. */
+size_t gdn_workspace_size(const gdn_problem *p);
+
+/* Layout of the packed gradient buffer (PR description of "metal: GATED_DELTA_NET_BACK":
+ * one output holding [dq|dk|dv|dg|dbeta|dstate]).  Writes the float offset of each region
+ * into offsets[6] (may be NULL) and returns the total number of floats (0 on an invalid
+ * problem).  Regions, contiguous, in this order:
+ *   dq     [n_seqs][T][H_k][S_k]     dk  [n_seqs][T][H_k][S_k]
+ *   dv     [n_seqs][T][H_v][S_v]     dg  [n_seqs][T][H_v][G]  (G = S_k or 1)
+ *   dbeta  [n_seqs][T][H_v]          dstate [n_seqs][H_v][S_v][S_k]
+ * Rows with t >= len_s are written as zeros. */
+size_t gdn_grad_packed_floats(const gdn_problem *p, size_t offsets[6]);
+
+/* Forward scan: writes y (strided as p->y) and state_out, and the state snapshots into the
+ * workspace.  All pointers are device pointers, 4-byte aligned.
+ * Returns GDN_OK or an error code (nothing enqueued on error). */
+int gdn_fwd(const gdn_problem *p, const float *q, const float *k, const float *v,
+            const float *g, const float *beta, const float *state0, float *y,
+            float *state_out, void *ws, size_t ws_bytes, gdn_stream_t stream);
+
+/* Backward: given the forward's inputs, the output cotangent gy (strided as p->gy) and
+ * the final-state cotangent dstate_out (NULL means zero), writes the six input gradients
+ * into grad_packed (layout: gdn_grad_packed_floats).  With GDN_BWD_REUSE_SNAPSHOTS the
+ * snapshots already in ws from gdn_fwd are used; otherwise they are recomputed first.
+ * dq and dk of one key head sum its value heads in increasing h, so results are bitwise
+ * reproducible run to run. */
+int gdn_bwd(const gdn_problem *p, const float *q, const float *k, const float *v,
+            const float *g, const float *beta, const float *state0, const float *gy,
+            const float *dstate_out, float *grad_packed, void *ws, size_t ws_bytes,
+            unsigned flags, gdn_stream_t stream);
+
+/* Human-readable name of a status code. */
+const char *gdn_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H */

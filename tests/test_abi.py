@@ -1,0 +1,171 @@
+"""The C-ABI library on the host: it loads, exports every declared entry point, sizes the
+workspace and the packed gradients, and rejects bad arguments before any launch.
+No test here enqueues GPU work (every call below fails validation first)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn.h")
+
+
+@pytest.fixture(scope="module")
+def B():
+    from gated_delta_rule_bwd_amd import binding
+    return binding
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(B):
+    names = declared_functions()
+    assert set(names) == set(B.EXPORTS), names
+    for n in names:
+        assert hasattr(B.lib, n), n
+
+
+def problem(B, strides=None, **kw):
+    d = dict(n_seqs=2, T=64, H_k=4, H_v=8, S=64, kda=True, C=8, scale=0.125,
+             seq_lens=[64, 61])
+    d.update(kw)
+    override = strides or {}
+    strides = {"q": (64 * 4 * 64, 4 * 64, 64), "k": (64 * 4 * 64, 4 * 64, 64),
+               "v": (64 * 8 * 64, 8 * 64, 64), "g": (64 * 8 * 64, 8 * 64, 64),
+               "beta": (64 * 8, 8, 1), "gy": (64 * 8 * 64, 8 * 64, 64),
+               "y": (64 * 8 * 64, 8 * 64, 64)}
+    strides.update(override)
+    return B.Problem(d["n_seqs"], d["T"], d["H_k"], d["H_v"], d["S"], d["kda"], d["C"],
+                     d["scale"], d["seq_lens"], strides)
+
+
+def expected_ws(n, T, Hk, Hv, S, C):
+    al = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    units = n * Hv
+    n_ck = max(1, -(-T // C))
+    tot = al(units * n_ck * S * S * 4)
+    tot = al(tot + units * C * S * S * 4)
+    tot = al(tot + units * C * S * 4)
+    if Hv != Hk:
+        part = n * T * Hv * S * 4
+        tot = al(tot + part)
+        tot = al(tot + part)
+    return tot
+
+
+def test_workspace_size(B):
+    p = problem(B)
+    assert B.workspace_size(p) == expected_ws(2, 64, 4, 8, 64, 8)
+    # C = 0 selects ceil(sqrt(T)) = 8 here
+    assert B.workspace_size(problem(B, C=0)) == expected_ws(2, 64, 4, 8, 64, 8)
+    # no grouped heads: no partial buffers
+    assert B.workspace_size(problem(B, H_v=4)) == expected_ws(2, 64, 4, 4, 64, 8)
+    # layer shape, 4 x 4096 tokens, 48 value heads, S = 128, C = 64
+    big = problem(B, n_seqs=4, T=4096, H_k=16, H_v=48, S=128, C=64, seq_lens=None)
+    assert B.workspace_size(big) == expected_ws(4, 4096, 16, 48, 128, 64)
+
+
+def test_grad_layout(B):
+    p = problem(B)
+    total, lay = B.grad_layout(p)
+    n, T, Hk, Hv, S = 2, 64, 4, 8, 64
+    sizes = [n * T * Hk * S, n * T * Hk * S, n * T * Hv * S, n * T * Hv * S, n * T * Hv,
+             n * Hv * S * S]
+    offs = [0]
+    for x in sizes[:-1]:
+        offs.append(offs[-1] + x)
+    assert [lay[k][0] for k in ("dq", "dk", "dv", "dg", "dbeta", "dstate")] == offs
+    assert total == sum(sizes)
+    total_s, lay_s = B.grad_layout(problem(B, kda=False))
+    assert lay_s["dg"][1] == (n, T, Hv, 1)
+    assert total_s == total - n * T * Hv * (S - 1)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(S=48), -2), (dict(S=16), -2), (dict(H_k=3), -2), (dict(n_seqs=-1), -1),
+    (dict(T=-1), -1), (dict(C=-1), -1), (dict(seq_lens=[65, 3]), -1),
+    (dict(seq_lens=[-1, 3]), -1), (dict(scale=float("nan")), -1), (dict(H_k=0), -1),
+])
+def test_invalid_problems(B, kw, code):
+    p = problem(B, **kw)
+    assert B.workspace_size(p) == 0
+    assert B.lib.gdn_grad_packed_floats(p.c, None) == 0
+    fake = ctypes.c_void_p(1 << 20)
+    rc = B.lib.gdn_fwd(p.c, *([fake] * 8), fake, 1 << 40, None)
+    assert rc == code
+
+
+def _fwd(B, p, ptrs, ws_bytes):
+    return B.lib.gdn_fwd(p.c, *[ctypes.c_void_p(x) if x else None for x in ptrs],
+                         ws_bytes, None)
+
+
+def _bwd(B, p, ptrs, ws_bytes, flags=0):
+    return B.lib.gdn_bwd(p.c, *[ctypes.c_void_p(x) if x else None for x in ptrs],
+                         ws_bytes, flags, None)
+
+
+def layout_ptrs(p, B):
+    """Disjoint fake device addresses for every argument of gdn_fwd / gdn_bwd."""
+    base = 1 << 32
+    step = 1 << 30
+    names = ["q", "k", "v", "g", "beta", "state0", "y", "state_out", "ws", "gy", "dso", "grad"]
+    return {n: base + i * step for i, n in enumerate(names)}
+
+
+def test_fwd_argument_errors(B):
+    p = problem(B)
+    ws = B.workspace_size(p)
+    a = layout_ptrs(p, B)
+    good = [a[n] for n in ("q", "k", "v", "g", "beta", "state0", "y", "state_out", "ws")]
+    for i in range(9):                       # each required pointer NULL
+        bad = list(good)
+        bad[i] = 0
+        assert _fwd(B, p, bad, ws) == -1
+    assert _fwd(B, p, good, ws - 1) == -3    # workspace too small
+    mis = list(good)
+    mis[0] += 2                              # q not 4-byte aligned
+    assert _fwd(B, p, mis, ws) == -2
+    ov = list(good)
+    ov[6] = good[2] + 64                     # y overlapping v
+    assert _fwd(B, p, ov, ws) == -1
+    ov = list(good)
+    ov[8] = good[7] + 256                    # workspace overlapping state_out
+    assert _fwd(B, p, ov, ws) == -1
+    # y as a self-overlapping view
+    pbad = problem(B, strides={"y": (0, 8 * 64, 32)})
+    assert _fwd(B, pbad, good, ws) == -1
+    # negative stride
+    pneg = problem(B, strides={"q": (-1, 256, 64)})
+    assert _fwd(B, pneg, good, ws) == -2
+
+
+def test_bwd_argument_errors(B):
+    p = problem(B)
+    ws = B.workspace_size(p)
+    a = layout_ptrs(p, B)
+    good = [a[n] for n in ("q", "k", "v", "g", "beta", "state0", "gy", "dso", "grad", "ws")]
+    for i in range(10):
+        if i == 7:
+            continue                          # dstate_out may be NULL
+        bad = list(good)
+        bad[i] = 0
+        assert _bwd(B, p, bad, ws) == -1, i
+    assert _bwd(B, p, good, ws, flags=2) == -1
+    assert _bwd(B, p, good, ws - 256) == -3
+    ov = list(good)
+    ov[8] = good[6] + 128                     # packed grads overlapping gy
+    assert _bwd(B, p, ov, ws) == -1
+    ov = list(good)
+    ov[9] = good[0]                           # workspace overlapping q
+    assert _bwd(B, p, ov, ws) == -1
+
+
+def test_status_strings(B):
+    for c in (0, -1, -2, -3, -4):
+        assert B.lib.gdn_status_string(c)

@@ -1,0 +1,134 @@
+"""HIP path (through the C ABI) against the fp64 oracle, on the GPU."""
+import os
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+from gated_delta_rule_bwd_amd import inputs as I  # noqa: E402
+from compare import check  # noqa: E402
+from gpu_cases import (REGIONS_BWD, REGIONS_FWD, gpu_subset, log, oracle_results,  # noqa: E402
+                       oracle_sampled)
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from gated_delta_rule_bwd_amd.device import DeviceCase  # loads libgdn.so
+    return DeviceCase
+
+
+def run_case(DeviceCase, w, arrays, reuse=True, **kw):
+    dc = DeviceCase(w, arrays, **kw)
+    dc.fwd()
+    dc.bwd(reuse=reuse)
+    torch.cuda.synchronize()
+    return dc, dc.results_numpy()
+
+
+SMALL = ["tiny_scalar_s32", "kda_ragged_s64", "gqa_strided_s32"]
+
+
+@pytest.mark.parametrize("name", SMALL)
+@pytest.mark.parametrize("reuse", [True, False])
+def test_parity_full(dev, name, reuse):
+    w = I.WORKLOADS[name]
+    log(f"[parity] {name} reuse={reuse} lens={w.lens}")
+    arrays, _ = I.make_all(w)
+    _, got = run_case(dev, w, arrays, reuse=reuse)
+    ref = oracle_results(w, arrays)
+    rep = check(got, ref, REGIONS_FWD + REGIONS_BWD)
+    log(f"[parity] {name}: " + ", ".join(f"{k} {v:.1e}" for k, v in rep.items()))
+
+
+def test_parity_layer_shape_sampled(dev):
+    """Full-size layer shape in the benchmark's launch configuration; the oracle checks
+    two (sequence, key head) groups, each with its three value heads."""
+    w = I.WORKLOADS["layer_kda_s128"]
+    log(f"[parity] {w.name} full size, sampled")
+    arrays, _ = I.make_all(w)
+    _, got = run_case(dev, w, arrays, reuse=True)
+    del arrays
+    for seqs, khs in (([0], [0]), ([3], [15])):
+        ref, vh = oracle_sampled(w, seqs, khs)
+        sub = gpu_subset(got, w, seqs, khs, vh)
+        rep = check(sub, ref, REGIONS_FWD + REGIONS_BWD)
+        log(f"[parity] {w.name} seq {seqs} key heads {khs}: " +
+            ", ".join(f"{k} {v:.1e}" for k, v in rep.items()))
+
+
+def test_single_ragged_sequence(dev):
+    """A standalone 61-token sequence with an 8-token interval: partial last segment."""
+    w = I.WORKLOADS["kda_ragged_s64"].replace(name="kda_t61", n_seqs=1, T=61, seq_lens=None)
+    arrays, _ = I.make_all(w)
+    _, got = run_case(dev, w, arrays)
+    check(got, oracle_results(w, arrays))
+
+
+def test_one_token_and_empty_sequences(dev):
+    w = I.Workload("edge", 3, 5, 2, 4, 64, True, 2, -0.5, seq_lens=(1, 0, 5), seed=77)
+    arrays, _ = I.make_all(w)
+    _, got = run_case(dev, w, arrays)
+    ref = oracle_results(w, arrays)
+    check(got, ref)
+    # the empty sequence passes state and cotangent through bit for bit
+    assert np.array_equal(got["state_out"][1], arrays["state0"][1])
+    assert np.array_equal(got["dstate"][1], arrays["dstate_out"][1])
+
+
+def test_t1_zero_state(dev):
+    w = I.Workload("t1", 1, 1, 1, 1, 128, False, 0, -1.0, seed=78)
+    arrays, _ = I.make_all(w)
+    arrays["state0"][:] = 0
+    _, got = run_case(dev, w, arrays)
+    check(got, oracle_results(w, arrays))
+
+
+def test_padded_tokens_are_never_read(dev):
+    """NaN in every padded token of every per-token input changes no bit of any output."""
+    w = I.WORKLOADS["kda_ragged_s64"]
+    arrays, _ = I.make_all(w)
+    nan_arrays, _ = I.make_all(w, pad_value=np.nan)
+    _, a = run_case(dev, w, arrays)
+    _, b = run_case(dev, w, nan_arrays)
+    for n in a:
+        assert np.array_equal(a[n], b[n]), n
+    for s, L in enumerate(w.lens):
+        for n in ("y", "dq", "dk", "dv", "dg", "dbeta"):
+            assert not np.any(b[n][s, L:]), n
+
+
+def test_null_final_state_cotangent(dev):
+    w = I.WORKLOADS["tiny_scalar_s32"]
+    arrays, _ = I.make_all(w)
+    arrays["dstate_out"] = None
+    _, got = run_case(dev, w, arrays)
+    ref_arrays = dict(arrays, dstate_out=np.zeros((1, 1, 32, 32), np.float32))
+    check(got, oracle_results(w, ref_arrays))
+
+
+def test_bitwise_run_to_run_and_interval(dev):
+    """Run-to-run bitwise reproducibility; checkpoint interval C = T versus sqrt(T) and the
+    recomputed versus the forward's snapshots change no bit."""
+    w = I.WORKLOADS["gqa_strided_s32"]
+    arrays, _ = I.make_all(w)
+    _, a = run_case(dev, w, arrays, reuse=True)
+    _, b = run_case(dev, w, arrays, reuse=True)
+    _, c = run_case(dev, w, arrays, reuse=False, C=w.T)
+    _, d = run_case(dev, w, arrays, reuse=False, C=5)
+    for n in a:
+        assert np.array_equal(a[n], b[n]), ("run-to-run", n)
+        assert np.array_equal(a[n], c[n]), ("C=T", n)
+        assert np.array_equal(a[n], d[n]), ("C=5", n)
+
+
+def test_strided_views_equal_contiguous_bitwise(dev):
+    w = I.WORKLOADS["gqa_strided_s32"]
+    arrays, _ = I.make_all(w)
+    _, a = run_case(dev, w, arrays, packed=True, strided_gy=True)
+    _, b = run_case(dev, w, arrays, packed=False, strided_gy=False)
+    for n in a:
+        assert np.array_equal(a[n], b[n]), n
