@@ -29,8 +29,12 @@ struct Plan {
     int n_ck_max = 1;  // snapshots per unit
     int G = 1;         // gate width
     int64_t units = 0;
-    bool parts = false;  // dq/dk go through per-value-head partials
-    size_t off_snap = 0, off_seg = 0, off_e = 0, off_pq = 0, off_pk = 0, total = 0;
+    bool s128 = false;   // head size 128: row-quarter kernels
+    bool parts = false;  // S < 128: dq/dk go through per-value-head partials
+    int nvs_max = 1;     // S = 128: 64-token stretches per segment
+    size_t off_snap = 0, off_seg = 0, off_e = 0, off_pq = 0, off_pk = 0;
+    size_t off_a = 0, off_vs = 0, off_part = 0, off_pb = 0, off_pg = 0;
+    size_t total = 0;
 };
 
 bool strides_ok(const gdn_strides &s) { return s.seq >= 0 && s.tok >= 0 && s.head >= 0; }
@@ -61,10 +65,30 @@ Plan make_plan(const gdn_problem *p) {
     pl.n_ck_max = std::max(1, (p->T + pl.C - 1) / pl.C);
     pl.G = p->gate == GDN_GATE_KDA ? p->S_k : 1;
     pl.units = (int64_t)p->n_seqs * p->H_v;
-    pl.parts = p->H_v != p->H_k;
+    pl.s128 = S == 128;
     size_t off = 0;
     pl.off_snap = off;
     off = align_up(off + (size_t)pl.units * pl.n_ck_max * S * S * sizeof(float));
+    if (pl.s128) {
+        const size_t tok_rows = (size_t)p->n_seqs * p->T * p->H_v;
+        constexpr int NQ = 4;
+        pl.nvs_max = std::max(1, (pl.C + 63) / 64);
+        pl.off_a = off;
+        off = align_up(off + tok_rows * pl.G * sizeof(float));
+        pl.off_e = off;
+        off = align_up(off + tok_rows * S * sizeof(float));
+        pl.off_vs = off;
+        if (pl.nvs_max > 1) off = align_up(off + (size_t)pl.units * NQ * pl.nvs_max * 32 * S * sizeof(float));
+        pl.off_part = off;
+        off = align_up(off + tok_rows * NQ * (pl.G == 1 ? 2 : 3) * S * sizeof(float));
+        pl.off_pb = off;
+        off = align_up(off + tok_rows * NQ * sizeof(float));
+        pl.off_pg = off;
+        off = align_up(off + tok_rows * NQ * sizeof(float));
+        pl.total = off;
+        return pl;
+    }
+    pl.parts = p->H_v != p->H_k;
     pl.off_seg = off;
     off = align_up(off + (size_t)pl.units * pl.C * S * S * sizeof(float));
     pl.off_e = off;
@@ -206,6 +230,8 @@ int gdn_fwd(const gdn_problem *p, const float *q, const float *k, const float *v
     a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.state0 = state0;
     a.y = y; a.state_out = state_out;
     a.snap = (float *)((char *)ws + pl.off_snap);
+    a.abuf = (float *)((char *)ws + pl.off_a);
+    a.ebuf = (float *)((char *)ws + pl.off_e);
     a.sq = p->q; a.sk = p->k; a.sv = p->v; a.sg = p->g; a.sb = p->beta; a.sy = p->y;
     a.T = p->T; a.H_k = p->H_k; a.H_v = p->H_v; a.C = pl.C; a.n_ck_max = pl.n_ck_max;
     a.scale = p->scale;
@@ -213,8 +239,9 @@ int gdn_fwd(const gdn_problem *p, const float *q, const float *k, const float *v
         const int cnt = std::min(gdn::kMaxSeqsPerLaunch, p->n_seqs - s0);
         a.s_base = s0;
         fill_lens(p, s0, cnt, a.lens);
-        rc = device_status(gdn::launch_fwd(a, (int)S, p->gate == GDN_GATE_KDA, cnt,
-                                           (hipStream_t)stream));
+        const bool kda = p->gate == GDN_GATE_KDA;
+        rc = device_status(pl.s128 ? gdn::launch_fwd128(a, kda, cnt, (hipStream_t)stream)
+                                   : gdn::launch_fwd(a, (int)S, kda, cnt, (hipStream_t)stream));
         if (rc != GDN_OK) return rc;
     }
     return GDN_OK;
@@ -260,20 +287,33 @@ int gdn_bwd(const gdn_problem *p, const float *q, const float *k, const float *v
             std::memset(&f, 0, sizeof(f));
             f.q = q; f.k = k; f.v = v; f.g = g; f.beta = beta; f.state0 = state0;
             f.snap = snap;
+            f.abuf = (float *)((char *)ws + pl.off_a);
+            f.ebuf = (float *)((char *)ws + pl.off_e);
             f.sq = p->q; f.sk = p->k; f.sv = p->v; f.sg = p->g; f.sb = p->beta; f.sy = p->y;
             f.s_base = s0;
             f.T = p->T; f.H_k = p->H_k; f.H_v = p->H_v; f.C = pl.C; f.n_ck_max = pl.n_ck_max;
             f.scale = p->scale;
             fill_lens(p, s0, cnt, f.lens);
-            rc = device_status(gdn::launch_fwd(f, (int)S, kda, cnt, (hipStream_t)stream));
+            rc = device_status(pl.s128 ? gdn::launch_fwd128(f, kda, cnt, (hipStream_t)stream)
+                                       : gdn::launch_fwd(f, (int)S, kda, cnt, (hipStream_t)stream));
             if (rc != GDN_OK) return rc;
         }
         gdn::BwdArgs b;
         std::memset(&b, 0, sizeof(b));
         b.q = q; b.k = k; b.v = v; b.g = g; b.beta = beta; b.gy = gy; b.dstate_out = dstate_out;
         b.snap = snap;
-        b.segbuf = (float *)((char *)ws + pl.off_seg);
-        b.ebuf = (float *)((char *)ws + pl.off_e);
+        if (pl.s128) {
+            b.abuf = (const float *)((char *)ws + pl.off_a);
+            b.ebuf = (const float *)((char *)ws + pl.off_e);
+            b.vsbuf = (float *)((char *)ws + pl.off_vs);
+            b.part = (float *)((char *)ws + pl.off_part);
+            b.pbuf = (float *)((char *)ws + pl.off_pb);
+            b.pgbuf = (float *)((char *)ws + pl.off_pg);
+            b.nvs_max = pl.nvs_max;
+        } else {
+            b.segbuf = (float *)((char *)ws + pl.off_seg);
+            b.ebuf_seg = (float *)((char *)ws + pl.off_e);
+        }
         if (pl.parts) {
             b.dq = (float *)((char *)ws + pl.off_pq);
             b.dk = (float *)((char *)ws + pl.off_pk);
@@ -289,7 +329,20 @@ int gdn_bwd(const gdn_problem *p, const float *q, const float *k, const float *v
         b.T = p->T; b.H_k = p->H_k; b.H_v = p->H_v; b.C = pl.C; b.n_ck_max = pl.n_ck_max;
         b.scale = p->scale;
         fill_lens(p, s0, cnt, b.lens);
-        rc = device_status(gdn::launch_bwd(b, (int)S, kda, cnt, (hipStream_t)stream));
+        if (pl.s128) {
+            rc = device_status(gdn::launch_bwd128(b, kda, cnt, (hipStream_t)stream));
+            if (rc != GDN_OK) return rc;
+            gdn::Combine128Args c;
+            std::memset(&c, 0, sizeof(c));
+            c.part = b.part; c.pbuf = b.pbuf; c.pgbuf = b.pgbuf;
+            c.dq = dq; c.dk = dk; c.dg = dg; c.dbeta = dbeta;
+            c.s_base = s0; c.n_seqs_launch = cnt; c.T = p->T; c.H_k = p->H_k; c.H_v = p->H_v;
+            c.kda = kda ? 1 : 0;
+            fill_lens(p, s0, cnt, c.lens);
+            rc = device_status(gdn::launch_combine128(c, (hipStream_t)stream));
+        } else {
+            rc = device_status(gdn::launch_bwd(b, (int)S, kda, cnt, (hipStream_t)stream));
+        }
         if (rc != GDN_OK) return rc;
     }
     if (pl.parts) {

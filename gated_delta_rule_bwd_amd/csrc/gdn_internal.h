@@ -18,6 +18,8 @@ struct FwdArgs {
     float *y;          // nullptr: do not write y
     float *state_out;  // nullptr: do not write the final state
     float *snap;       // [unit][n_ck_max][S][S] snapshots (state before tokens 0, C, 2C, ...)
+    float *abuf;       // S = 128 path: gates a = exp(g), [n_seqs][T][H_v][G]
+    float *ebuf;       // S = 128 path: prediction errors e = v - u, [n_seqs][T][H_v][S]
     gdn_strides sq, sk, sv, sg, sb, sy;
     int32_t s_base;    // first sequence of this launch
     int32_t T, H_k, H_v, C, n_ck_max;
@@ -29,15 +31,30 @@ struct FwdArgs {
 struct BwdArgs {
     const float *q, *k, *v, *g, *beta, *gy, *dstate_out;
     const float *snap;  // [unit][n_ck_max][S][S]
-    float *segbuf;      // [unit][C][S][S] decayed previous state Mp of each segment token
-    float *ebuf;        // [unit][C][S] prediction errors v - u of the current segment
+    float *segbuf;      // S < 128: [unit][C][S][S] decayed previous state Mp of each segment token
+    float *ebuf_seg;    // S < 128: [unit][C][S] prediction errors v - u of the current segment
     float *dq, *dk;     // direct outputs (H_v == H_k) or per-value-head partials
     int64_t dqk_head;   // head count of the dq/dk arrays (H_k direct, H_v for partials)
     float *dv, *dg, *dbeta, *dstate;
+    // S = 128 path
+    const float *abuf, *ebuf;  // written by the forward (see FwdArgs)
+    float *vsbuf;              // [unit][4][nvs_max][32 x S] states at 64-token boundaries
+    float *part;               // [n_seqs][T][H_v][4][3][S] column sums of each row quarter
+    float *pbuf, *pgbuf;       // [n_seqs][T][H_v][4] dbeta and scalar-gate dg per quarter
+    int32_t nvs_max;
     gdn_strides sq, sk, sv, sg, sb, sgy;
     int32_t s_base;
     int32_t T, H_k, H_v, C, n_ck_max;
     float scale;
+    int32_t lens[kMaxSeqsPerLaunch];
+};
+
+// Sum of the row-quarter partials (and, for dq/dk, of the value heads of each key head) on
+// the S = 128 path; writes dq, dk, dg, dbeta including the zero rows of padded tokens.
+struct Combine128Args {
+    const float *part, *pbuf, *pgbuf;
+    float *dq, *dk, *dg, *dbeta;
+    int32_t s_base, n_seqs_launch, T, H_k, H_v, kda;
     int32_t lens[kMaxSeqsPerLaunch];
 };
 
@@ -51,5 +68,8 @@ struct CombineArgs {
 hipError_t launch_fwd(const FwdArgs &a, int S, bool kda, int n_seqs_launch, hipStream_t st);
 hipError_t launch_bwd(const BwdArgs &a, int S, bool kda, int n_seqs_launch, hipStream_t st);
 hipError_t launch_combine(const CombineArgs &a, hipStream_t st);
+hipError_t launch_fwd128(const FwdArgs &a, bool kda, int n_seqs_launch, hipStream_t st);
+hipError_t launch_bwd128(const BwdArgs &a, bool kda, int n_seqs_launch, hipStream_t st);
+hipError_t launch_combine128(const Combine128Args &a, hipStream_t st);
 
 }  // namespace gdn

@@ -216,7 +216,7 @@ bwd_kernel(const BwdArgs a) {
     }
 
     float *seg = a.segbuf + unit * C * S * S + (int64_t)row0 * S + lc;
-    float *eb = a.ebuf + unit * C * S + row0;
+    float *eb = a.ebuf_seg + unit * C * S + row0;
     const int n_ck = (L + C - 1) / C;
     int parity = 0;
 

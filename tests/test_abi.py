@@ -44,11 +44,22 @@ def problem(B, strides=None, **kw):
                      d["scale"], d["seq_lens"], strides)
 
 
-def expected_ws(n, T, Hk, Hv, S, C):
+def expected_ws(n, T, Hk, Hv, S, C, kda=True):
     al = lambda x: (x + 255) // 256 * 256  # noqa: E731
     units = n * Hv
     n_ck = max(1, -(-T // C))
     tot = al(units * n_ck * S * S * 4)
+    if S == 128:                    # row-quarter path
+        rows = n * T * Hv
+        nvs = max(1, -(-C // 64))
+        tot = al(tot + rows * (S if kda else 1) * 4)       # gates
+        tot = al(tot + rows * S * 4)                       # prediction errors
+        if nvs > 1:
+            tot = al(tot + units * 4 * nvs * 32 * S * 4)   # stretch starts
+        tot = al(tot + rows * 4 * (3 if kda else 2) * S * 4)   # column partials
+        tot = al(tot + rows * 4 * 4)                       # dbeta partials
+        tot = al(tot + rows * 4 * 4)                       # scalar-gate dg partials
+        return tot
     tot = al(tot + units * C * S * S * 4)
     tot = al(tot + units * C * S * 4)
     if Hv != Hk:
@@ -68,6 +79,9 @@ def test_workspace_size(B):
     # layer shape, 4 x 4096 tokens, 48 value heads, S = 128, C = 64
     big = problem(B, n_seqs=4, T=4096, H_k=16, H_v=48, S=128, C=64, seq_lens=None)
     assert B.workspace_size(big) == expected_ws(4, 4096, 16, 48, 128, 64)
+    long = problem(B, n_seqs=1, T=65536, H_k=16, H_v=48, S=128, C=256, kda=False,
+                   seq_lens=None)
+    assert B.workspace_size(long) == expected_ws(1, 65536, 16, 48, 128, 256, kda=False)
 
 
 def test_grad_layout(B):

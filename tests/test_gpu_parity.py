@@ -132,3 +132,48 @@ def test_strided_views_equal_contiguous_bitwise(dev):
     _, b = run_case(dev, w, arrays, packed=False, strided_gy=False)
     for n in a:
         assert np.array_equal(a[n], b[n]), n
+
+
+# Head size 128: row-quarter kernels with three storage levels (snapshots every C tokens,
+# register states every 8 tokens of a 64-token stretch, LDS states of the walked 8 tokens).
+S128_CASES = {
+    # three segments (64, 64, 22 tokens), ragged second sequence, grouped heads
+    "kda_c64": I.Workload("s128_kda_c64", 2, 150, 2, 4, 128, True, 64, -0.3,
+                          seq_lens=(150, 77), seed=501),
+    # interval above the 64-token stretch: stretches saved to the workspace
+    "scalar_c200": I.Workload("s128_scalar_c200", 2, 300, 1, 3, 128, False, 200, -0.05,
+                              seq_lens=(300, 133), seed=502),
+    # default interval ceil(sqrt(T)) = 10: partial sub-segments everywhere
+    "kda_default": I.Workload("s128_kda_default", 1, 100, 1, 2, 128, True, 0, -0.5, seed=503),
+    # every token its own segment
+    "kda_c1": I.Workload("s128_kda_c1", 1, 19, 1, 1, 128, True, 1, -0.5, seed=504),
+    # one segment longer than a stretch
+    "scalar_cT": I.Workload("s128_scalar_cT", 1, 129, 1, 1, 128, False, 129, -1.0, seed=505),
+}
+
+
+@pytest.mark.parametrize("name", list(S128_CASES))
+def test_parity_s128(dev, name):
+    w = S128_CASES[name]
+    log(f"[parity] {w.name} lens={w.lens} C={w.C}")
+    arrays, _ = I.make_all(w)
+    _, got = run_case(dev, w, arrays, reuse=True)
+    rep = check(got, oracle_results(w, arrays))
+    log(f"[parity] {w.name}: " + ", ".join(f"{k} {v:.1e}" for k, v in rep.items()))
+
+
+def test_s128_bitwise_interval_reuse_and_strides(dev):
+    """S = 128: checkpoint interval, snapshot reuse and strided views change no bit."""
+    w = I.Workload("s128_bits", 2, 140, 2, 4, 128, True, 64, -0.3, seq_lens=(140, 70),
+                   packed=True, seed=506)
+    arrays, _ = I.make_all(w)
+    _, a = run_case(dev, w, arrays, reuse=True)
+    _, b = run_case(dev, w, arrays, reuse=True)
+    _, c = run_case(dev, w, arrays, reuse=False, C=w.T)
+    _, d = run_case(dev, w, arrays, reuse=False, C=8)
+    _, e = run_case(dev, w, arrays, reuse=True, C=100, packed=False, strided_gy=True)
+    for n in a:
+        assert np.array_equal(a[n], b[n]), ("run-to-run", n)
+        assert np.array_equal(a[n], c[n]), ("C=T", n)
+        assert np.array_equal(a[n], d[n]), ("C=8", n)
+        assert np.array_equal(a[n], e[n]), ("C=100, contiguous, strided gy", n)
