@@ -33,7 +33,22 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-heads", type=int, default=0,
                     help="key heads of sequence 0 in the oracle sample (0: auto)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB (for scaling "
+                         "the FETCH_SIZE / WRITE_SIZE counters) and exit")
     return ap.parse_args()
+
+
+def copy_calibration(mib):
+    """A plain copy of known size: reads and writes mib MiB once per launch (3 launches)."""
+    import torch
+    n = mib * 2**20 // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n * 4, "launches": 3}), flush=True)
 
 
 def cpu_baseline(w, n_key_heads):
@@ -61,6 +76,9 @@ def cpu_baseline(w, n_key_heads):
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); every (sequence, "
               "head) unit is independent, so more GPUs would shard units without exchange "
