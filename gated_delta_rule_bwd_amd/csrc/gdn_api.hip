@@ -62,10 +62,13 @@ Plan make_plan(const gdn_problem *p) {
     Plan pl;
     const int64_t S = p->S_v;
     pl.C = p->C > 0 ? std::min(p->C, std::max(p->T, 1)) : ceil_sqrt(p->T);
+    pl.s128 = S == 128;
+    // head size 128: checkpoints fall on the 8-token grid of the column-scaled windows, so
+    // the interval is rounded up to a multiple of 8 and every interval gives the same bits
+    if (pl.s128) pl.C = (pl.C + 7) / 8 * 8;
     pl.n_ck_max = std::max(1, (p->T + pl.C - 1) / pl.C);
     pl.G = p->gate == GDN_GATE_KDA ? p->S_k : 1;
     pl.units = (int64_t)p->n_seqs * p->H_v;
-    pl.s128 = S == 128;
     size_t off = 0;
     pl.off_snap = off;
     off = align_up(off + (size_t)pl.units * pl.n_ck_max * S * S * sizeof(float));
@@ -84,7 +87,7 @@ Plan make_plan(const gdn_problem *p) {
         pl.off_pb = off;
         off = align_up(off + tok_rows * NQ * sizeof(float));
         pl.off_pg = off;
-        off = align_up(off + tok_rows * NQ * sizeof(float));
+        off = align_up(off + tok_rows * NQ * 2 * sizeof(float));
         pl.total = off;
         return pl;
     }
@@ -164,6 +167,19 @@ void fill_lens(const gdn_problem *p, int s0, int count, int32_t *dst) {
 
 int device_status(hipError_t e) { return e == hipSuccess ? GDN_OK : GDN_ERR_DEVICE; }
 
+// a = exp(g) into the workspace for sequences s0 .. s0 + cnt - 1 (head size 128)
+hipError_t launch_gates(const gdn_problem *p, const Plan &pl, const float *g, void *ws, int s0,
+                        int cnt, hipStream_t st) {
+    gdn::GateArgs ga;
+    std::memset(&ga, 0, sizeof(ga));
+    ga.g = g;
+    ga.abuf = (float *)((char *)ws + pl.off_a);
+    ga.sg = p->g;
+    ga.s_base = s0; ga.n_seqs_launch = cnt; ga.T = p->T; ga.H_v = p->H_v; ga.G = pl.G;
+    fill_lens(p, s0, cnt, ga.lens);
+    return gdn::launch_gate128(ga, st);
+}
+
 }  // namespace
 
 extern "C" {
@@ -240,6 +256,10 @@ int gdn_fwd(const gdn_problem *p, const float *q, const float *k, const float *v
         a.s_base = s0;
         fill_lens(p, s0, cnt, a.lens);
         const bool kda = p->gate == GDN_GATE_KDA;
+        if (pl.s128) {
+            rc = device_status(launch_gates(p, pl, g, ws, s0, cnt, (hipStream_t)stream));
+            if (rc != GDN_OK) return rc;
+        }
         rc = device_status(pl.s128 ? gdn::launch_fwd128(a, kda, cnt, (hipStream_t)stream)
                                    : gdn::launch_fwd(a, (int)S, kda, cnt, (hipStream_t)stream));
         if (rc != GDN_OK) return rc;
@@ -294,6 +314,10 @@ int gdn_bwd(const gdn_problem *p, const float *q, const float *k, const float *v
             f.T = p->T; f.H_k = p->H_k; f.H_v = p->H_v; f.C = pl.C; f.n_ck_max = pl.n_ck_max;
             f.scale = p->scale;
             fill_lens(p, s0, cnt, f.lens);
+            if (pl.s128) {
+                rc = device_status(launch_gates(p, pl, g, ws, s0, cnt, (hipStream_t)stream));
+                if (rc != GDN_OK) return rc;
+            }
             rc = device_status(pl.s128 ? gdn::launch_fwd128(f, kda, cnt, (hipStream_t)stream)
                                        : gdn::launch_fwd(f, (int)S, kda, cnt, (hipStream_t)stream));
             if (rc != GDN_OK) return rc;

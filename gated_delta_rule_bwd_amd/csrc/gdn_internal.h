@@ -18,7 +18,7 @@ struct FwdArgs {
     float *y;          // nullptr: do not write y
     float *state_out;  // nullptr: do not write the final state
     float *snap;       // [unit][n_ck_max][S][S] snapshots (state before tokens 0, C, 2C, ...)
-    float *abuf;       // S = 128 path: gates a = exp(g), [n_seqs][T][H_v][G]
+    const float *abuf; // S = 128 path: gates a = exp(g), [n_seqs][T][H_v][G] (gate kernel)
     float *ebuf;       // S = 128 path: prediction errors e = v - u, [n_seqs][T][H_v][S]
     gdn_strides sq, sk, sv, sg, sb, sy;
     int32_t s_base;    // first sequence of this launch
@@ -40,12 +40,22 @@ struct BwdArgs {
     const float *abuf, *ebuf;  // written by the forward (see FwdArgs)
     float *vsbuf;              // [unit][4][nvs_max][32 x S] states at 64-token boundaries
     float *part;               // [n_seqs][T][H_v][4][3][S] column sums of each row quarter
-    float *pbuf, *pgbuf;       // [n_seqs][T][H_v][4] dbeta and scalar-gate dg per quarter
+    float *pbuf;               // [n_seqs][T][H_v][4] dbeta per quarter
+    float *pgbuf;              // [n_seqs][T][H_v][4][2] scalar-gate dg per quarter and column half
     int32_t nvs_max;
     gdn_strides sq, sk, sv, sg, sb, sgy;
     int32_t s_base;
     int32_t T, H_k, H_v, C, n_ck_max;
     float scale;
+    int32_t lens[kMaxSeqsPerLaunch];
+};
+
+// Gates a = exp(g) of every token t < len of the launch's sequences (S = 128 path).
+struct GateArgs {
+    const float *g;
+    float *abuf;       // [n_seqs][T][H_v][G]
+    gdn_strides sg;
+    int32_t s_base, n_seqs_launch, T, H_v, G;
     int32_t lens[kMaxSeqsPerLaunch];
 };
 
@@ -68,6 +78,7 @@ struct CombineArgs {
 hipError_t launch_fwd(const FwdArgs &a, int S, bool kda, int n_seqs_launch, hipStream_t st);
 hipError_t launch_bwd(const BwdArgs &a, int S, bool kda, int n_seqs_launch, hipStream_t st);
 hipError_t launch_combine(const CombineArgs &a, hipStream_t st);
+hipError_t launch_gate128(const GateArgs &a, hipStream_t st);
 hipError_t launch_fwd128(const FwdArgs &a, bool kda, int n_seqs_launch, hipStream_t st);
 hipError_t launch_bwd128(const BwdArgs &a, bool kda, int n_seqs_launch, hipStream_t st);
 hipError_t launch_combine128(const Combine128Args &a, hipStream_t st);

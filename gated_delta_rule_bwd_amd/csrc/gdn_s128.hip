@@ -3,33 +3,37 @@
 // Work decomposition.  A (sequence, value head) unit owns a 128 x 128 fp32 state M = S^T
 // (row j = value index, column i = key index).  Rows evolve independently in both
 // directions of the recurrence ("metal: GATED_DELTA_NET_BACK", approval review: thread j
-// owns row j of M), so each unit is split into four row quarters of 32 rows and every
-// quarter is one workgroup of four waves (eight rows per wave).  At the layer shape
-// (192 units) that is 768 workgroups: three per compute unit, so all 256 CUs carry equal
-// work.  The only coupling between quarters is the set of column sums of the backward
-// (dq, dk and the per-channel dg sum over rows, dbeta over rows); each quarter writes its
+// owns row j of M), so each unit is split into four row quarters of 32 rows, one workgroup
+// each.  At the layer shape (192 units) that is 768 workgroups, three per compute unit, so
+// all 256 CUs carry equal work.  The quarters are coupled only through column sums of the
+// backward (dq, dk, the per-channel dg) and the row sum dbeta; each quarter writes its
 // partial sums and a fixed-order kernel adds the four quarters (and, for dq/dk, the value
 // heads of each key head in increasing order), so results are bitwise reproducible.
 //
-// Forward (fwd128_kernel): lanes are laid out as 8 lanes per row with 16 contiguous columns
-// per lane and one row per lane, so the two row reductions per token (u = Mp k and
-// y = M q) are three DPP adds each.  Token vectors are staged through LDS in
-// chunks of 8 tokens.  Besides y, the final state and the snapshots every C tokens, the
-// forward saves two per-token vectors to the workspace: the gates a = exp(g) and the
-// prediction errors e = v - u of every row.  With e saved, replaying a token is just
-// Mp = M .* a, M = Mp + (beta e) k^T, bit-identical to the forward's own arithmetic.
+// Column-scaled state.  The gate only scales columns: M_t = M_{t-1} diag(a_t) + delta_t k_t^T.
+// Inside a window of tokens starting at t0 the state is carried as M_t = Mh_t diag(c_t) with
+// c_t = a_t0 * ... * a_t (running product per column), which turns the update into a single
+// fma per element, Mh_t = Mh_{t-1} + delta_t (k_t / c_t)^T, while the readouts use the vectors
+// c_t .* k_t and c_t .* q_t.  At the end of a window the product is folded back into the
+// state (one multiply per element).  The backward carries dM the same way, with the suffix
+// product d_t = a_{t+1} * ... * a_end of the window, so its two rank-one updates and the
+// decay become two fmas per element.  Windows are the 8-token blocks of the sequence
+// (checkpoints fall on them), so both directions use the same windows and the backward's
+// replay reproduces the forward's states bit for bit.  A window whose running product would
+// leave [2^-60, 1] (a gate above one, or a decay below 2^-60 over the window) is processed
+// unscaled instead, with the decay applied per token; both directions take that decision
+// from the same values.
 //
-// Backward (bwd128_kernel): lanes are laid out as 64 lanes per row with two columns per
-// lane (columns lane and lane + 64) and eight rows per lane, so every column sum is in-lane
-// and the only row reduction per token (dd = dM k) is a permlane/DPP reduce-scatter followed
-// by v_readlane broadcasts.  The checkpointed schedule has three storage levels:
-//   - snapshots every C tokens in HBM (from the forward),
-//   - states every 8 tokens inside a 64-token stretch, in registers (a 64-token stretch
-//     longer segments are cut into starts from a state saved to the workspace),
-//   - the decayed previous states Mp of the 8 tokens being walked, in LDS (128 KiB).
-// A replay pass over each 64-token stretch records the 8-token states, then each 8-token
-// sub-segment, last first, is replayed into LDS and walked in reverse.
+// Kernels: gate128_kernel writes a = exp(g) once (both directions read it); fwd128_kernel
+// (four waves, 8 lanes per row with 16 columns each, so the row sums u = Mp k and y = M q
+// are three DPP adds) writes y, the final state, the snapshots every C tokens and the
+// prediction errors e = v - u; bwd128_kernel (eight waves, 64 lanes per row with columns
+// lane and lane + 64 and four rows per lane, so column sums are in-lane and the row sum
+// dd = dM k is a permlane/DPP reduce-scatter) replays and walks; combine128_kernel adds
+// the partial sums.
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
 
 #include "gdn_internal.h"
 
@@ -39,11 +43,10 @@ namespace {
 constexpr int S = 128;
 constexpr int QR = 32;         // rows per workgroup (one row quarter)
 constexpr int NQ = S / QR;     // quarters per unit
-constexpr int THREADS = 256;   // four waves
-constexpr int TC = 8;          // tokens per staged chunk in the forward
-constexpr int C2 = 8;          // tokens per sub-segment walked from LDS
-constexpr int VS = 64;         // tokens per stretch with register-resident sub-snapshots
-constexpr int NSUB = VS / C2;  // sub-snapshots per stretch
+constexpr int WIN = 8;         // tokens per window
+constexpr int VS = 64;         // tokens per stretch in the backward
+constexpr int NWS = VS / WIN;  // windows per stretch
+constexpr float kScaleMin = 0x1p-60f;
 
 __device__ __forceinline__ float as_f(int x) { return __builtin_bit_cast(float, x); }
 __device__ __forceinline__ int as_i(float x) { return __builtin_bit_cast(int, x); }
@@ -62,14 +65,21 @@ __device__ __forceinline__ float row16_sum(float v) {
     return v;
 }
 
-// Sum over all 64 lanes; every lane receives the sum.
-__device__ __forceinline__ float wave_sum(float v) {
+// Sum over each 32-lane half of the wave; every lane receives its half's sum.
+__device__ __forceinline__ float half_sum(float v) {
     v = row16_sum(v);
     auto p = __builtin_amdgcn_permlane16_swap(as_i(v), as_i(v), false, false);
-    v = as_f(p[0]) + as_f(p[1]);
+    return as_f(p[0]) + as_f(p[1]);
+}
+
+// Sum over all 64 lanes; every lane receives the sum.
+__device__ __forceinline__ float wave_sum(float v) {
+    v = half_sum(v);
     auto q = __builtin_amdgcn_permlane32_swap(as_i(v), as_i(v), false, false);
     return as_f(q[0]) + as_f(q[1]);
 }
+
+__device__ __forceinline__ float rcp(float x) { return __builtin_amdgcn_rcpf(x); }
 
 // Block index -> (unit within the launch, row quarter).  The four quarters of a unit read
 // the same token vectors, so they are placed on the same XCD (blocks are dispatched to the
@@ -81,175 +91,243 @@ __device__ __forceinline__ void map_block(int b, int nb, int &unit, int &qb) {
     qb = lin % NQ;
 }
 
+// A window is processed column-scaled when every gate in it is at most one and the product
+// over the window stays at or above 2^-60; then every prefix and suffix product of the
+// window lies in [2^-60, 1].  (NaN gates fail both tests.)
+__device__ __forceinline__ bool gate_ok(float a) { return a <= 1.f; }
+__device__ __forceinline__ bool prod_ok(float c) { return c >= kScaleMin; }
+
+// ------------------------------------------------------------------ gates
+
+// a = exp(g) for every token t < len of every (sequence, value head): rows of G values.
+__global__ void __launch_bounds__(256) gate128_kernel(const GateArgs a) {
+    const int64_t rows = (int64_t)a.n_seqs_launch * a.T * a.H_v;
+    if (a.G == 1) {
+        for (int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; r < rows;
+             r += (int64_t)gridDim.x * blockDim.x) {
+            const int h = (int)(r % a.H_v);
+            const int64_t st = r / a.H_v;
+            const int t = (int)(st % a.T), sl = (int)(st / a.T);
+            if (t >= a.lens[sl]) continue;
+            const int64_t s = a.s_base + sl;
+            a.abuf[(s * a.T + t) * a.H_v + h] = expf(a.g[s * a.sg.seq + t * a.sg.tok + h * a.sg.head]);
+        }
+        return;
+    }
+    const int lane = threadIdx.x & 63;
+    const int64_t wave0 = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+    const int64_t nwaves = (int64_t)gridDim.x * (blockDim.x >> 6);
+    for (int64_t r = wave0; r < rows; r += nwaves) {
+        const int h = (int)(r % a.H_v);
+        const int64_t st = r / a.H_v;
+        const int t = (int)(st % a.T), sl = (int)(st / a.T);
+        if (t >= a.lens[sl]) continue;
+        const int64_t s = a.s_base + sl;
+        const float *gp = a.g + s * a.sg.seq + t * a.sg.tok + h * a.sg.head;
+        float *ap = a.abuf + ((s * a.T + t) * a.H_v + h) * S;
+        ap[lane] = expf(gp[lane]);
+        ap[lane + 64] = expf(gp[lane + 64]);
+    }
+}
+
 // ------------------------------------------------------------------ forward scan
 
-// Token vectors in the forward's LDS: the 16-column block of lane lc starts at word 20 lc,
-// so the eight lanes of a row read disjoint bank groups.
-constexpr int SP = S + S / 4;
+constexpr int FT = 256;            // forward threads: four waves of eight rows
+constexpr int SP = S + S / 4;      // padded vector: the 16-column block b starts at word 20 b
 __device__ __forceinline__ int padc(int c) { return c + (c >> 4) * 4; }
 
 template <bool KDA>
-__global__ void __launch_bounds__(THREADS)
-fwd128_kernel(const FwdArgs a) {
-    constexpr int GW = KDA ? SP : 1;
-    __shared__ float qs[2][TC][SP], ks[2][TC][SP], gs[2][TC][GW];
-    __shared__ float vs[2][TC][QR], bs[2][TC];
-    __shared__ float ys[TC][QR], es[TC][QR];
+struct alignas(16) FwdLds {
+    static constexpr int GW = KDA ? SP : 1;
+    float kc[WIN][SP], kr[WIN][SP], qc[WIN][SP];         // c.*k, k./c, c.*q (scaled window)
+    float kraw[WIN][SP], qraw[WIN][SP], araw[WIN][GW];   // unscaled window
+    float cend[GW];                                      // product over the window
+    float vq[WIN][QR];                                   // v of this quarter's rows
+    float bt[WIN];                                       // beta
+    float ys[WIN][QR], es[WIN][QR];                      // outputs of the window
+};
 
+template <bool KDA>
+__global__ void __launch_bounds__(FT)
+fwd128_kernel(const FwdArgs a) {
+    constexpr int GW = KDA ? S : 1;
+    __shared__ FwdLds<KDA> sm;
     int ul, qb;
     map_block(blockIdx.x, gridDim.x, ul, qb);
     const int sl = ul / a.H_v, h = ul % a.H_v;
     const int64_t s = a.s_base + sl;
     const int hk = h % a.H_k;
     const int L = a.lens[sl];
+    const int C = a.C;
     const int64_t unit = s * a.H_v + h;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int lc = lane & 7, rg = lane >> 3;  // 8 lanes per row, 16 columns per lane
-    const int lr0 = w * 8 + rg;               // local row of this lane
-    const int row0 = qb * QR + lr0;           // global row
+    const int lc = lane & 7;                  // 16-column block of this lane
+    const int lrow = w * 8 + (lane >> 3);     // row within the quarter
+    const int row = qb * QR + lrow;           // row of the state
     const bool write_y = a.y != nullptr;
 
-    const float *qp = a.q + s * a.sq.seq + hk * a.sq.head;
-    const float *kp = a.k + s * a.sk.seq + hk * a.sk.head;
-    const float *gp = a.g + s * a.sg.seq + h * a.sg.head;
-    const float *vp = a.v + s * a.sv.seq + h * a.sv.head + qb * QR;
+    // staging roles: threads 0..127 hold the k and gate values of column ci for the window's
+    // tokens, threads 128..255 the q and gate values; thread tid also holds v of row srow of
+    // token stt, threads 0..7 beta
+    const int ci = tid & (S - 1), pci = padc(ci);
+    const bool kside = tid < S;
+    const int stt = tid >> 5, srow = tid & 31;
+    const float *xp = kside ? a.k + s * a.sk.seq + hk * a.sk.head + ci
+                            : a.q + s * a.sq.seq + hk * a.sq.head + ci;
+    const int64_t xtok = kside ? a.sk.tok : a.sq.tok;
+    const float *vp = a.v + s * a.sv.seq + h * a.sv.head + qb * QR + srow;
     const float *bp = a.beta + s * a.sb.seq + h * a.sb.head;
-    const int64_t tok_ae = (int64_t)a.H_v;   // token stride of abuf / ebuf rows, in rows
-    float *abase = a.abuf + (s * a.T * a.H_v + h) * (KDA ? S : 1);
+    const int64_t tok_ae = a.H_v;   // token stride of abuf / ebuf rows, in rows
+    const float *ap = a.abuf + (s * a.T * a.H_v + h) * GW + (KDA ? ci : 0);
     float *ebase = a.ebuf + (s * a.T * a.H_v + h) * S + qb * QR;
 
     float M[16];
     {
-        const float *st0 = a.state0 + unit * S * S + (int64_t)row0 * S + lc * 16;
+        const float *st0 = a.state0 + unit * S * S + (int64_t)row * S + lc * 16;
 #pragma unroll
         for (int n = 0; n < 16; ++n) M[n] = st0[n];
     }
 
-    // staging: thread -> (token tt of the chunk, four consecutive columns cc)
-    const int stt = tid >> 5, scc = (tid & 31) * 4, srow = tid & 31;
-    float rq[4], rk[4], rg4[4], rv = 0.f, rb = 0.f;
-    auto load_chunk = [&](int c) {
-        const int t = c * TC + stt;
-        const bool ok = t < L;
+    float av[WIN], xv[WIN], rv = 0.f, rb = 0.f;
+    auto load_window = [&](int t0, int cnt) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            rq[i] = ok ? qp[t * a.sq.tok + scc + i] : 0.f;
-            rk[i] = ok ? kp[t * a.sk.tok + scc + i] : 0.f;
-            if constexpr (KDA) rg4[i] = ok ? gp[t * a.sg.tok + scc + i] : 0.f;
+        for (int tt = 0; tt < WIN; ++tt) {
+            const int64_t t = t0 + tt;
+            av[tt] = tt < cnt ? ap[t * tok_ae * GW] : 1.f;
+            xv[tt] = tt < cnt ? xp[t * xtok] : 0.f;
         }
-        rv = ok ? vp[t * a.sv.tok + srow] : 0.f;
-        if (tid < TC) {
-            const int tb = c * TC + tid;
-            rb = tb < L ? bp[tb * a.sb.tok] : 0.f;
-        } else if (!KDA && tid < 2 * TC) {
-            const int tb = c * TC + tid - TC;
-            rb = tb < L ? gp[tb * a.sg.tok] : 0.f;
-        }
-    };
-    auto store_chunk = [&](int c, int buf) {
-        const int t = c * TC + stt;
-        const bool ok = t < L;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            qs[buf][stt][padc(scc + i)] = rq[i];
-            ks[buf][stt][padc(scc + i)] = rk[i];
-        }
-        if constexpr (KDA) {
-            float av[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) av[i] = expf(rg4[i]);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) gs[buf][stt][padc(scc + i)] = av[i];
-            if (qb == 0 && ok) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) abase[t * tok_ae * S + scc + i] = av[i];
-            }
-        }
-        vs[buf][stt][srow] = rv;
-        if (tid < TC) {
-            bs[buf][tid] = rb;
-        } else if (!KDA && tid < 2 * TC) {
-            const float av = expf(rb);
-            gs[buf][tid - TC][0] = av;
-            const int tb = c * TC + tid - TC;
-            if (qb == 0 && tb < L) abase[tb * tok_ae] = av;
-        }
+        if (stt < cnt) rv = vp[(int64_t)(t0 + stt) * a.sv.tok];
+        if (tid < cnt) rb = bp[(int64_t)(t0 + tid) * a.sb.tok];
     };
 
-    const int nchunks = (L + TC - 1) / TC;
-    float *snap = a.snap + unit * a.n_ck_max * S * S + (int64_t)row0 * S + lc * 16;
-    int next_snap = 0;
-    if (nchunks > 0) {
-        load_chunk(0);
-        store_chunk(0, 0);
-    }
-    __syncthreads();
-    for (int c = 0; c < nchunks; ++c) {
-        const int buf = c & 1;
-        if (c + 1 < nchunks) load_chunk(c + 1);
-        const int cnt = min(TC, L - c * TC);
-        for (int tt = 0; tt < cnt; ++tt) {
-            const int t = c * TC + tt;
-            if (t == next_snap) {
+    float *snap = a.snap + unit * a.n_ck_max * S * S + (int64_t)row * S + lc * 16;
+    int ta = 0, prev_ta = 0, prev_cnt = 0;
+    int cnt = min(WIN, L);
+    if (cnt > 0) load_window(0, cnt);
+    while (cnt > 0) {
+        __syncthreads();   // the previous window's vectors and outputs are no longer read
+        if (stt < prev_cnt) {
+            const int64_t t = prev_ta + stt;
+            if (write_y) a.y[s * a.sy.seq + t * a.sy.tok + h * a.sy.head + qb * QR + srow] = sm.ys[stt][srow];
+            ebase[t * tok_ae * S + srow] = sm.es[stt][srow];
+        }
+        // window vectors from the registers: running product c, its reciprocal, flag
+        bool ok = true;
+        {
+            float c = 1.f;
 #pragma unroll
-                for (int n = 0; n < 16; ++n) snap[n] = M[n];
-                snap += (int64_t)S * S;
-                next_snap += a.C;
+            for (int tt = 0; tt < WIN; ++tt) {
+                ok = ok && gate_ok(av[tt]);
+                c *= av[tt];
+                if (kside) {
+                    sm.kc[tt][pci] = xv[tt] * c;
+                    sm.kr[tt][pci] = xv[tt] * rcp(c);
+                    sm.kraw[tt][pci] = xv[tt];
+                    if (KDA || ci == 0) sm.araw[tt][KDA ? pci : 0] = av[tt];
+                } else {
+                    sm.qc[tt][pci] = xv[tt] * c;
+                    sm.qraw[tt][pci] = xv[tt];
+                }
             }
-            float qv[16], kv[16], av[16];
+            ok = ok && prod_ok(c);   // the padding gates are 1
+            if (kside && (KDA || ci == 0)) sm.cend[KDA ? pci : 0] = c;
+        }
+        if (stt < cnt) sm.vq[stt][srow] = rv;
+        if (tid < cnt) sm.bt[tid] = rb;
+        const bool direct = __syncthreads_or(!ok) != 0;
+        const int next = ta + cnt;
+        const int ncnt = min(WIN, L - next);
+        if (ncnt > 0) load_window(next, ncnt);
+
+        if (ta % C == 0) {   // checkpoint: the state before token ta
 #pragma unroll
-            for (int n = 0; n < 16; ++n) {
-                qv[n] = qs[buf][tt][lc * 20 + n];
-                kv[n] = ks[buf][tt][lc * 20 + n];
-                av[n] = gs[buf][tt][KDA ? lc * 20 + n : 0];
-            }
-            const float beta = bs[buf][tt];
-            const float vr = vs[buf][tt][lr0];
-            float mp[16], u4[4] = {0.f, 0.f, 0.f, 0.f};
+            for (int n = 0; n < 16; ++n) snap[(int64_t)(ta / C) * S * S + n] = M[n];
+        }
+        const int cb = lc * 20;   // padded offset of this lane's 16 columns (16-byte aligned)
+        auto ld16 = [&](const float *base, float (&x)[16]) {
 #pragma unroll
-            for (int n = 0; n < 16; ++n) {
-                mp[n] = M[n] * av[n];
-                u4[n & 3] = fmaf(mp[n], kv[n], u4[n & 3]);
+            for (int j = 0; j < 4; ++j) {
+                const float4 v = *reinterpret_cast<const float4 *>(base + 4 * j);
+                x[4 * j] = v.x; x[4 * j + 1] = v.y; x[4 * j + 2] = v.z; x[4 * j + 3] = v.w;
             }
-            float u = (u4[0] + u4[1]) + (u4[2] + u4[3]);
-            u += dpp<0xB1>(u);   // quad_perm [1,0,3,2]
-            u += dpp<0x4E>(u);   // quad_perm [2,3,0,1]
-            u += dpp<0x141>(u);  // row_half_mirror: the two quads of each 8-lane row
-            const float e = vr - u;
-            const float de = beta * e;
-            float y4[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int n = 0; n < 16; ++n) {
-                M[n] = fmaf(de, kv[n], mp[n]);
-                y4[n & 3] = fmaf(M[n], qv[n], y4[n & 3]);
-            }
-            float y = (y4[0] + y4[1]) + (y4[2] + y4[3]);
+        };
+        auto finish = [&](int tt, float y, float e) {
             y += dpp<0xB1>(y);
             y += dpp<0x4E>(y);
             y += dpp<0x141>(y);
             if (lc == 0) {
-                ys[tt][lr0] = a.scale * y;
-                es[tt][lr0] = e;
+                sm.ys[tt][lrow] = a.scale * y;
+                sm.es[tt][lrow] = e;
+            }
+        };
+        if (!direct) {
+            for (int tt = 0; tt < cnt; ++tt) {
+                float kc[16], kr[16], qc[16];
+                ld16(&sm.kc[tt][cb], kc);
+                ld16(&sm.kr[tt][cb], kr);
+                ld16(&sm.qc[tt][cb], qc);
+                float u = 0.f, y = 0.f;
+#pragma unroll
+                for (int n = 0; n < 16; ++n) u = fmaf(M[n], kc[n], u);
+                u += dpp<0xB1>(u);   // quad_perm [1,0,3,2]
+                u += dpp<0x4E>(u);   // quad_perm [2,3,0,1]
+                u += dpp<0x141>(u);  // row_half_mirror: the two quads of each 8-lane row
+                const float e = sm.vq[tt][lrow] - u;
+                const float de = sm.bt[tt] * e;
+#pragma unroll
+                for (int n = 0; n < 16; ++n) M[n] = fmaf(de, kr[n], M[n]);
+#pragma unroll
+                for (int n = 0; n < 16; ++n) y = fmaf(M[n], qc[n], y);
+                finish(tt, y, e);
+            }
+#pragma unroll
+            for (int n = 0; n < 16; ++n) M[n] *= sm.cend[KDA ? cb + n : 0];
+        } else {
+            for (int tt = 0; tt < cnt; ++tt) {
+                float kv[16], qv[16], gv[16];
+                ld16(&sm.kraw[tt][cb], kv);
+                ld16(&sm.qraw[tt][cb], qv);
+                if constexpr (KDA) {
+                    ld16(&sm.araw[tt][cb], gv);
+                } else {
+#pragma unroll
+                    for (int n = 0; n < 16; ++n) gv[n] = sm.araw[tt][0];
+                }
+                float u = 0.f, y = 0.f;
+#pragma unroll
+                for (int n = 0; n < 16; ++n) u = fmaf(M[n], gv[n] * kv[n], u);
+                u += dpp<0xB1>(u);
+                u += dpp<0x4E>(u);
+                u += dpp<0x141>(u);
+                const float e = sm.vq[tt][lrow] - u;
+                const float de = sm.bt[tt] * e;
+#pragma unroll
+                for (int n = 0; n < 16; ++n) M[n] = fmaf(M[n], gv[n], de * kv[n]);
+#pragma unroll
+                for (int n = 0; n < 16; ++n) y = fmaf(M[n], qv[n], y);
+                finish(tt, y, e);
             }
         }
-        __syncthreads();
-        if (stt < cnt) {
-            const int64_t t = c * TC + stt;
-            if (write_y)
-                a.y[s * a.sy.seq + t * a.sy.tok + h * a.sy.head + qb * QR + srow] = ys[stt][srow];
-            ebase[t * tok_ae * S + srow] = es[stt][srow];
-        }
-        if (c + 1 < nchunks) store_chunk(c + 1, buf ^ 1);
-        __syncthreads();
+
+        prev_ta = ta;
+        prev_cnt = cnt;
+        ta = next;
+        cnt = ncnt;
+    }
+    __syncthreads();
+    if (stt < prev_cnt) {
+        const int64_t t = prev_ta + stt;
+        if (write_y) a.y[s * a.sy.seq + t * a.sy.tok + h * a.sy.head + qb * QR + srow] = sm.ys[stt][srow];
+        ebase[t * tok_ae * S + srow] = sm.es[stt][srow];
     }
     if (write_y) {
-        for (int64_t idx = tid; idx < (int64_t)(a.T - L) * QR; idx += THREADS) {
+        for (int64_t idx = tid; idx < (int64_t)(a.T - L) * QR; idx += FT) {
             const int64_t t = L + idx / QR;
             a.y[s * a.sy.seq + t * a.sy.tok + h * a.sy.head + qb * QR + idx % QR] = 0.f;
         }
     }
     if (a.state_out) {
-        float *so = a.state_out + unit * S * S + (int64_t)row0 * S + lc * 16;
+        float *so = a.state_out + unit * S * S + (int64_t)row * S + lc * 16;
 #pragma unroll
         for (int n = 0; n < 16; ++n) so[n] = M[n];
     }
@@ -257,47 +335,50 @@ fwd128_kernel(const FwdArgs a) {
 
 // ------------------------------------------------------------------ backward walk
 
-// Token data of one chunk of C2 tokens, staged in LDS for the waves of a workgroup.
-template <int GW>
-struct TokStage {
-    float q[C2][S];
-    float k[C2][S];
-    float a[C2][GW];
-    float e[C2][QR];     // prediction errors of this quarter's rows
-    float de[C2][QR];    // beta * e (the forward's rounding)
-    float gy[C2][QR];    // output cotangent of this quarter's rows
-    float beta[C2];
+constexpr int RW = 4;              // rows per wave
+constexpr int NW = QR / RW;        // waves per workgroup (two per SIMD)
+constexpr int BT = 64 * NW;        // backward threads
+constexpr int CT = BT / S;         // threads per column in the stretch staging
+static_assert(RW == 4 && NW == WIN && WIN * QR <= BT, "backward layout");
+
+template <bool KDA>
+struct alignas(16) BwdLds {
+    union {
+        // state before each token of the window, thread-private: st[tt][g][tid] holds rows
+        // 2g, 2g + 1 of the thread's rows at columns (lane, lane + 64).  Once a token is
+        // walked, its slot holds the thread's column sums of that token:
+        // st[tt][0] = (dq lo, dq hi, dk lo, dk hi), st[tt][1] = (dk' lo, dk' hi, dg lo, dg hi)
+        float4 st[WIN][2][BT];
+        // stretch data of the window-start pass: k./c for columns (lane, lane + 64), beta e
+        // of the quarter's rows, window products
+        struct {
+            float2 kt[VS][64];
+            float4 det[VS][QR / 4];
+            float2 cend[NWS][64];
+        } sa;
+    };
+    int wflag[NWS];            // unscaled windows of the stretch
+    // window data for columns (lane, lane + 64): (d.*k, scale q./d), -beta k./d, k./c for the
+    // replay (raw k in an unscaled window), (c, d) and k for the column sums, the window
+    // product; rows: beta e, gy, e; per token: beta, sum over the quarter's rows of
+    // (beta e) gy, and the dbeta of each wave's rows
+    float4 wv[WIN][64];
+    float2 wh[WIN][64];
+    float2 kt8[WIN][64];
+    float4 de8[WIN][QR / 4], gy8[WIN][QR / 4], e8[WIN][QR / 4];
+    float4 pcd[WIN][64];
+    float2 pk[WIN][64];
+    float bt[WIN], s1[WIN];
+    float2 pP[64];
+    float dbw[WIN][NW];
 };
 
-// LDS of the backward: the small arrays come first so that their addresses fit the 16-bit
-// immediate offsets of ds instructions; the per-thread states follow.
-template <int GW, int RW>
-struct BwdLds {
-    static constexpr int NT = 64 * (QR / RW);
-    static constexpr int NV = 2 * RW;   // floats per thread per token state
-    TokStage<GW> ts;
-    float redb[C2][QR / RW], redg[C2][QR / RW];
-    // decayed previous states of a sub-segment, thread-private and component-major:
-    // value k of thread tid for chunk position tt sits at st[tt][k][tid], so a wave's
-    // accesses are consecutive words (no bank conflicts).  After a token is walked its
-    // slot holds the thread's column sums of that token (k = 0..5: dq, dk, dg for its
-    // two columns) until the sub-segment's reduction.
-    float st[C2][NV][NT];
-};
-
-// RW rows per wave, 32 / RW waves per workgroup; each lane holds columns lane and lane + 64
-// of its wave's rows, so column sums are in-lane and the row sum dd = dM k is rows_sum.
-template <bool KDA, int RW>
-__global__ void __launch_bounds__(64 * (QR / RW), 1)
+template <bool KDA>
+__global__ void __launch_bounds__(BT, 1)
 bwd128_kernel(const BwdArgs a) {
     constexpr int GW = KDA ? S : 1;
     constexpr int NP = KDA ? 3 : 2;     // partial slots per quarter: dq | dk (| dg)
-    constexpr int NW = QR / RW;         // waves
-    constexpr int NT = 64 * NW;         // threads
-    constexpr int NV = 2 * RW;          // floats per thread per token state
-    static_assert(NV >= 6, "the column-sum stash needs six words per thread");
-    __shared__ BwdLds<GW, RW> sm;
-    auto &ts = sm.ts;
+    __shared__ BwdLds<KDA> sm;
 
     int ul, qb;
     map_block(blockIdx.x, gridDim.x, ul, qb);
@@ -305,81 +386,29 @@ bwd128_kernel(const BwdArgs a) {
     const int64_t s = a.s_base + sl;
     const int hk = h % a.H_k;
     const int L = a.lens[sl];
+    const int C = a.C;
     const int64_t unit = s * a.H_v + h;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int wr0 = w * RW;             // first row of this wave within the quarter
-    const int row0 = qb * QR + wr0;     // first global row of this wave
-    const int C = a.C;
-    // after rows_sum, lane 16 i of a 4-row group holds row 4p + {0, 2, 1, 3}[i]
-    const int dv_row = ((lane >> 4) & 1) * 2 + (lane >> 5);
+    const int row0 = qb * QR + wr0;     // first state row of this wave
+    const float scale = a.scale;
+    // after the dd reduce-scatter, lane 16 m of the wave holds row {0, 2, 1, 3}[m]
+    const int dd_row = ((lane >> 4) & 1) * 2 + (lane >> 5);
+    const int ci = tid & (S - 1), cr = tid >> 7;   // stretch staging: column, column thread
 
+    const int64_t tok_ae = a.H_v;
     const float *snapu = a.snap + unit * a.n_ck_max * S * S + (int64_t)row0 * S + lane;
     float4 *vsb = reinterpret_cast<float4 *>(a.vsbuf) +
-                  ((unit * NQ + qb) * (int64_t)a.nvs_max) * (RW / 2 * NT) + tid;
-
-    // ---- staging of token data (register prefetch of the next chunk, then LDS).  Thread tid
-    // stages column sc = tid % S of tokens stt + m * (NT / S) of the q, k, a vectors, and
-    // row rrow = tid % QR of token rtt = tid / QR of the e and gy vectors.
-    constexpr int TG = NT / S;          // tokens covered by one pass over the threads
-    constexpr int PV = C2 / TG;         // vector elements per thread per chunk
-    static_assert(C2 % TG == 0 && C2 * QR <= NT, "staging layout");
-    const int64_t tok_ae = a.H_v;
-    const int sc = tid % S, stt = tid / S;
-    const int rtt = tid / QR, rrow = tid % QR;
-    const float *kp0 = a.k + s * a.sk.seq + hk * a.sk.head + sc + stt * a.sk.tok;
-    const float *qp0 = a.q + s * a.sq.seq + hk * a.sq.head + sc + stt * a.sq.tok;
-    const float *ap0 = a.abuf + (s * a.T * a.H_v + h) * GW + (KDA ? sc + stt * tok_ae * GW : 0);
-    const float *ep0 = a.ebuf + (s * a.T * a.H_v + h) * S + qb * QR + rrow + rtt * tok_ae * S;
-    const float *gyp0 = a.gy + s * a.sgy.seq + h * a.sgy.head + qb * QR + rrow + rtt * a.sgy.tok;
+                  ((unit * NQ + qb) * (int64_t)a.nvs_max) * (RW / 2 * BT) + tid;
+    const float *kp = a.k + s * a.sk.seq + hk * a.sk.head;
+    const float *qp = a.q + s * a.sq.seq + hk * a.sq.head;
+    const float *ab = a.abuf + (s * a.T * a.H_v + h) * GW;           // gates, token stride tok_ae*GW
+    const float *eb = a.ebuf + (s * a.T * a.H_v + h) * S + qb * QR;  // errors, token stride tok_ae*S
+    const float *gyp = a.gy + s * a.sgy.seq + h * a.sgy.head + qb * QR;
     const float *bp = a.beta + s * a.sb.seq + h * a.sb.head;
-    const float *as0 = a.abuf + (s * a.T * a.H_v + h) * GW;   // scalar gate values
-    float pq[PV], pk[PV], pa[PV], pe = 0.f, pgy = 0.f, pb1 = 0.f, pbe = 0.f;
-    int pcnt = 0;
-    auto load_chunk = [&](int tstart, int cnt, bool walk) {
-        pcnt = cnt;
-#pragma unroll
-        for (int m = 0; m < PV; ++m) {
-            if (stt + m * TG < cnt) {
-                const int64_t t = tstart + m * TG;
-                pk[m] = kp0[t * a.sk.tok];
-                if (walk) pq[m] = qp0[t * a.sq.tok];
-                if constexpr (KDA) pa[m] = ap0[t * tok_ae * GW];
-            }
-        }
-        if (tid < C2 * QR && rtt < cnt) {
-            pe = ep0[(int64_t)tstart * tok_ae * S];
-            pbe = bp[(tstart + rtt) * a.sb.tok];
-            if (walk) pgy = gyp0[(int64_t)tstart * a.sgy.tok];
-        }
-        if (tid < cnt) {
-            pb1 = bp[(tstart + tid) * a.sb.tok];
-        } else if (!KDA && tid >= C2 && tid < C2 + cnt) {
-            pb1 = as0[(tstart + tid - C2) * tok_ae];
-        }
-    };
-    auto store_chunk = [&](bool walk) {
-#pragma unroll
-        for (int m = 0; m < PV; ++m) {
-            const int tt = stt + m * TG;
-            if (tt < pcnt) {
-                ts.k[tt][sc] = pk[m];
-                if (walk) ts.q[tt][sc] = pq[m];
-                if constexpr (KDA) ts.a[tt][sc] = pa[m];
-            }
-        }
-        if (tid < C2 * QR && rtt < pcnt) {
-            ts.e[rtt][rrow] = pe;
-            ts.de[rtt][rrow] = pbe * pe;
-            if (walk) ts.gy[rtt][rrow] = pgy;
-        }
-        if (tid < pcnt) {
-            ts.beta[tid] = pb1;
-        } else if (!KDA && tid >= C2 && tid < C2 + pcnt) {
-            ts.a[tid - C2][0] = pb1;
-        }
-    };
+    float *dvw = a.dv + (s * a.T * a.H_v + h) * S + qb * QR + wr0;    // this wave's rows
 
-    float X[RW][2];
+    float X[RW][2];   // the walked gradient dM (scaled by d inside a window)
     if (a.dstate_out) {
         const float *d0 = a.dstate_out + unit * S * S + (int64_t)row0 * S + lane;
 #pragma unroll
@@ -390,166 +419,328 @@ bwd128_kernel(const BwdArgs a) {
 #pragma unroll
         for (int r = 0; r < RW; ++r) X[r][0] = X[r][1] = 0.f;
     }
+    auto rows4 = [](const float4 &v, float (&x)[RW]) { x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w; };
 
-    auto put4 = [&](float4 *dst, const float (&M)[RW][2]) {
+    // ---- stretch staging: k./c per token (the forward's arithmetic, so the replay is bit
+    // exact), beta e, the product over each window and the unscaled-window flags
+    auto stage_stretch = [&](int va, int vb) {
+        constexpr int NTASK = NWS / CT;   // windows per thread
+        float kv[NTASK][WIN], cv[NTASK][WIN];
+        int cn[NTASK];
 #pragma unroll
-        for (int c = 0; c < RW / 2; ++c)
-            dst[c * NT] = make_float4(M[2 * c][0], M[2 * c][1], M[2 * c + 1][0], M[2 * c + 1][1]);
-    };
-    auto get4 = [&](const float4 *src, float (&M)[RW][2]) {
+        for (int x = 0; x < NTASK; ++x) {
+            const int t0 = va + (cr + CT * x) * WIN;
+            cn[x] = t0 < vb ? min(WIN, vb - t0) : 0;
 #pragma unroll
-        for (int c = 0; c < RW / 2; ++c) {
-            const float4 x = src[c * NT];
-            M[2 * c][0] = x.x; M[2 * c][1] = x.y; M[2 * c + 1][0] = x.z; M[2 * c + 1][1] = x.w;
-        }
-    };
-
-    // one replayed token from the staged chunk: Mp = M .* a; M = Mp + (beta e) k^T
-    auto replay = [&](int tt, float (&M)[RW][2], bool keep) {
-        float kv[2], av[2], de[RW];
-#pragma unroll
-        for (int n = 0; n < 2; ++n) {
-            kv[n] = ts.k[tt][lane + 64 * n];
-            av[n] = ts.a[tt][KDA ? lane + 64 * n : 0];
-        }
-#pragma unroll
-        for (int r = 0; r < RW; ++r) de[r] = ts.de[tt][wr0 + r];
-#pragma unroll
-        for (int r = 0; r < RW; ++r)
-#pragma unroll
-            for (int n = 0; n < 2; ++n) {
-                const float mp = M[r][n] * av[n];
-                if (keep) sm.st[tt][2 * r + n][tid] = mp;
-                M[r][n] = fmaf(de[r], kv[n], mp);
-            }
-    };
-
-    // one token of the reverse walk (token t, chunk position tt).  Once a thread has read its
-    // LDS state of token tt it owns that slot again and leaves its column sums there.
-    auto walk = [&](int t, int tt) {
-        float Mp[RW][2];
-#pragma unroll
-        for (int r = 0; r < RW; ++r)
-#pragma unroll
-            for (int n = 0; n < 2; ++n) Mp[r][n] = sm.st[tt][2 * r + n][tid];
-        float qs[2], kv[2], kn[2], av[2], gy[RW], ev[RW], de[RW];
-        const float beta = ts.beta[tt];
-#pragma unroll
-        for (int n = 0; n < 2; ++n) {
-            qs[n] = a.scale * ts.q[tt][lane + 64 * n];
-            kv[n] = ts.k[tt][lane + 64 * n];
-            kn[n] = -beta * kv[n];
-            av[n] = ts.a[tt][KDA ? lane + 64 * n : 0];
-        }
-#pragma unroll
-        for (int r = 0; r < RW; ++r) {
-            gy[r] = ts.gy[tt][wr0 + r];
-            ev[r] = ts.e[tt][wr0 + r];
-            de[r] = ts.de[tt][wr0 + r];
-        }
-        float pq[2] = {0.f, 0.f}, pe2[2] = {0.f, 0.f}, pm[2] = {0.f, 0.f}, pg[2] = {0.f, 0.f};
-        float dpart[RW];
-#pragma unroll
-        for (int r = 0; r < RW; ++r) {
-            dpart[r] = 0.f;
-#pragma unroll
-            for (int n = 0; n < 2; ++n) {
-                const float mt = fmaf(de[r], kv[n], Mp[r][n]);  // state after token t
-                X[r][n] = fmaf(gy[r], qs[n], X[r][n]);         // dM += scale gy q^T
-                pq[n] = fmaf(mt, gy[r], pq[n]);                // dq  (x scale below)
-                pe2[n] = fmaf(X[r][n], de[r], pe2[n]);         // dk: dM^T delta
-                dpart[r] = fmaf(X[r][n], kv[n], dpart[r]);     // dd = dM k
+            for (int tt = 0; tt < WIN; ++tt) {
+                const int64_t t = t0 + tt;
+                kv[x][tt] = tt < cn[x] ? kp[t * a.sk.tok + ci] : 0.f;
+                cv[x][tt] = tt < cn[x] ? ab[t * tok_ae * GW + (KDA ? ci : 0)] : 1.f;
             }
         }
-        // dd = dM k over the 64 lanes; lane 16 i of each 16-lane row holds one row's total
-        float hh[RW / 2];
+        constexpr int NDE = VS * QR / BT;
+        float ev[NDE], bv[NDE];
 #pragma unroll
-        for (int p = 0; p < RW / 2; ++p) {
-            auto sw = __builtin_amdgcn_permlane32_swap(as_i(dpart[2 * p]), as_i(dpart[2 * p + 1]),
-                                                       false, false);
-            hh[p] = as_f(sw[0]) + as_f(sw[1]);
+        for (int x = 0; x < NDE; ++x) {
+            const int tr = (tid >> 5) + (BT / QR) * x;   // token within the stretch
+            const int64_t t = va + tr;
+            ev[x] = va + tr < vb ? eb[t * tok_ae * S + (tid & 31)] : 0.f;
+            bv[x] = va + tr < vb ? bp[t * a.sb.tok] : 0.f;
         }
-        float dd[RW];
+        __syncthreads();   // the previous users of the slot area are done
+        if (tid < NWS) sm.wflag[tid] = 0;
 #pragma unroll
-        for (int p = 0; p < RW / 4; ++p) {
-            auto sw = __builtin_amdgcn_permlane16_swap(as_i(hh[2 * p]), as_i(hh[2 * p + 1]), false,
-                                                       false);
-            const float g = row16_sum(as_f(sw[0]) + as_f(sw[1]));
-            dd[4 * p + 0] = as_f(__builtin_amdgcn_readlane(as_i(g), 0));
-            dd[4 * p + 2] = as_f(__builtin_amdgcn_readlane(as_i(g), 16));
-            dd[4 * p + 1] = as_f(__builtin_amdgcn_readlane(as_i(g), 32));
-            dd[4 * p + 3] = as_f(__builtin_amdgcn_readlane(as_i(g), 48));
-            if ((lane & 15) == 0)                              // dv = beta dd
-                a.dv[((s * a.T + t) * a.H_v + h) * S + row0 + 4 * p + dv_row] = beta * g;
-        }
-        float pb = 0.f;
+        for (int x = 0; x < NDE; ++x)
+            reinterpret_cast<float *>(sm.sa.det[(tid >> 5) + (BT / QR) * x])[tid & 31] = bv[x] * ev[x];
+        __syncthreads();
 #pragma unroll
-        for (int r = 0; r < RW; ++r) {
-            pb = fmaf(dd[r], ev[r], pb);                       // dbeta = dd . (v - u)
+        for (int x = 0; x < NTASK; ++x) {
+            const int m = cr + CT * x;
+            float c = 1.f;
+            bool g = true;
 #pragma unroll
-            for (int n = 0; n < 2; ++n) {
-                pm[n] = fmaf(Mp[r][n], dd[r], pm[n]);          // Mp^T dd (du = -beta dd)
-                X[r][n] = fmaf(dd[r], kn[n], X[r][n]);         // dM += du k^T
-                pg[n] = fmaf(X[r][n], Mp[r][n], pg[n]);        // dg = sum dM .* Mp
-                X[r][n] *= av[n];                              // dM = dM .* a
+            for (int tt = 0; tt < WIN; ++tt) {
+                g = g && gate_ok(cv[x][tt]);
+                c *= cv[x][tt];
+                reinterpret_cast<float *>(&sm.sa.kt[m * WIN + tt][ci & 63])[ci >> 6] = kv[x][tt] * rcp(c);
             }
+            if (KDA || ci < 64) {
+                if (KDA) reinterpret_cast<float *>(&sm.sa.cend[m][ci & 63])[ci >> 6] = c;
+                else sm.sa.cend[m][ci] = make_float2(c, c);
+            }
+            if (cn[x] > 0 && !(g && prod_ok(c))) atomicOr(&sm.wflag[m], 1);
         }
-#pragma unroll
-        for (int n = 0; n < 2; ++n) {
-            sm.st[tt][n][tid] = a.scale * pq[n];
-            sm.st[tt][2 + n][tid] = fmaf(-beta, pm[n], pe2[n]);
-            if constexpr (KDA) sm.st[tt][4 + n][tid] = pg[n];
-        }
-        if constexpr (!KDA) {
-            const float gs = wave_sum(pg[0] + pg[1]);
-            if (lane == 0) sm.redg[tt][w] = gs;
-        }
-        if (lane == 0) sm.redb[tt][w] = pb;
+        __syncthreads();
     };
 
-    // the column sums of the cnt walked tokens starting at token ta, summed over the waves
-    // in a fixed order and written to the quarter's partial buffers.  Thread tid reduces
-    // column sc of tokens stt + m * TG.
-    const int64_t part_tok = (int64_t)a.H_v * NQ * NP * S;   // floats per token
+    // ---- replay of window m of the stretch from M (its start state) to its end
+    auto replay_window = [&](float (&M)[RW][2], int va, int vb, int m) {
+        const int t0 = va + m * WIN;
+        const int cnt = min(WIN, vb - t0);
+        if (sm.wflag[m] == 0) {
+            for (int tt = 0; tt < cnt; ++tt) {
+                const int tr = m * WIN + tt;
+                const float2 kv = sm.sa.kt[tr][lane];
+                float dv[RW];
+                rows4(sm.sa.det[tr][w], dv);
+#pragma unroll
+                for (int r = 0; r < RW; ++r) {
+                    M[r][0] = fmaf(dv[r], kv.x, M[r][0]);
+                    M[r][1] = fmaf(dv[r], kv.y, M[r][1]);
+                }
+            }
+            const float2 ce = sm.sa.cend[m][lane];
+#pragma unroll
+            for (int r = 0; r < RW; ++r) M[r][0] *= ce.x, M[r][1] *= ce.y;
+        } else {
+            // unscaled window: keys and gates come from memory directly (rare path)
+            for (int tt = 0; tt < cnt; ++tt) {
+                const int tr = m * WIN + tt;
+                const int64_t t = t0 + tt;
+                const float kv[2] = {kp[t * a.sk.tok + lane], kp[t * a.sk.tok + lane + 64]};
+                const float av[2] = {ab[t * tok_ae * GW + (KDA ? lane : 0)],
+                                     ab[t * tok_ae * GW + (KDA ? lane + 64 : 0)]};
+                float dv[RW];
+                rows4(sm.sa.det[tr][w], dv);
+#pragma unroll
+                for (int r = 0; r < RW; ++r)
+#pragma unroll
+                    for (int n = 0; n < 2; ++n) M[r][n] = fmaf(M[r][n], av[n], dv[r] * kv[n]);
+            }
+        }
+    };
+
+    // ---- window data, prefetched into registers one window ahead: thread (tok = w, lane)
+    // holds the gates of columns (lane, lane + 64) for all tokens, and k, q, beta of token
+    // tok; thread tid < WIN * QR holds gy, e and beta of row tid & 31 of token tid >> 5
+    float wa[WIN][2], wk[2], wq[2], wbt = 0.f, rgy = 0.f, re = 0.f, rb = 0.f;
+    auto load_window = [&](int t0, int cnt) {
+#pragma unroll
+        for (int u = 0; u < WIN; ++u)
+#pragma unroll
+            for (int n = 0; n < 2; ++n)
+                wa[u][n] = u < cnt ? ab[(int64_t)(t0 + u) * tok_ae * GW + (KDA ? lane + 64 * n : 0)] : 1.f;
+        const int64_t t = t0 + w;
+#pragma unroll
+        for (int n = 0; n < 2; ++n) {
+            wk[n] = w < cnt ? kp[t * a.sk.tok + lane + 64 * n] : 0.f;
+            wq[n] = w < cnt ? qp[t * a.sq.tok + lane + 64 * n] : 0.f;
+        }
+        wbt = w < cnt ? bp[t * a.sb.tok] : 0.f;
+        if (tid < WIN * QR && (tid >> 5) < cnt) {
+            const int64_t tr = t0 + (tid >> 5);
+            rgy = gyp[tr * a.sgy.tok + (tid & 31)];
+            re = eb[tr * tok_ae * S + (tid & 31)];
+            rb = bp[tr * a.sb.tok];
+        }
+    };
+    // store the window's data and its derived vectors (cnt tokens; unscaled when direct)
+    auto stage_window = [&](int cnt, bool direct) {
+        const int tt = w;
+        float c[2] = {1.f, 1.f}, d[2] = {1.f, 1.f};
+#pragma unroll
+        for (int n = 0; n < 2; ++n) {
+            if (!direct) {
+#pragma unroll
+                for (int u = 0; u < WIN; ++u) {   // prefix in token order, as the forward
+                    if (u <= tt) c[n] *= wa[u][n];
+                    else d[n] *= wa[u][n];
+                }
+            } else {
+#pragma unroll
+                for (int u = 0; u < WIN; ++u)
+                    if (u == tt) c[n] = wa[u][n];
+            }
+        }
+        const float rd[2] = {direct ? 1.f : rcp(d[0]), direct ? 1.f : rcp(d[1])};
+        sm.wv[tt][lane] = make_float4(wk[0] * d[0], wk[1] * d[1], scale * wq[0] * rd[0], scale * wq[1] * rd[1]);
+        sm.wh[tt][lane] = make_float2(-wbt * wk[0] * rd[0], -wbt * wk[1] * rd[1]);
+        sm.kt8[tt][lane] = direct ? make_float2(wk[0], wk[1])
+                                  : make_float2(wk[0] * rcp(c[0]), wk[1] * rcp(c[1]));
+        sm.pcd[tt][lane] = make_float4(c[0], c[1], d[0], d[1]);
+        sm.pk[tt][lane] = make_float2(wk[0], wk[1]);
+        if (tt == 0) sm.pP[lane] = direct ? make_float2(1.f, 1.f) : make_float2(c[0] * d[0], c[1] * d[1]);
+        if (lane == 0) sm.bt[tt] = wbt;
+        if (tid < WIN * QR) {   // rows: beta e, gy, e, and the sum of (beta e) gy per token
+            const int rt = tid >> 5, r = tid & 31;
+            const float de = rb * re;
+            reinterpret_cast<float *>(sm.de8[rt])[r] = de;
+            reinterpret_cast<float *>(sm.gy8[rt])[r] = rgy;
+            reinterpret_cast<float *>(sm.e8[rt])[r] = re;
+            const float p = half_sum(rt < cnt ? de * rgy : 0.f);
+            if (r == 0) sm.s1[rt] = p;
+        }
+    };
+
+    // ---- column sums of the cnt walked tokens of the window at ta: fixed-order sum over the
+    // waves, scaling, and the quarter's partial outputs; dbeta from the per-wave sums.
+    // Wave w handles token w, lane the columns (lane, lane + 64).
     auto reduce_columns = [&](int ta, int cnt) {
-        __syncthreads();   // every wave has left its column sums in the LDS slots
-        float *pp = a.part + (((s * a.T + ta) * a.H_v + h) * NQ + qb) * NP * S + sc;
+        const int tt = w;
+        if (tt < cnt) {   // uniform over the wave
+            float4 A = sm.st[tt][0][lane], B = sm.st[tt][1][lane];
 #pragma unroll
-        for (int m = 0; m < PV; ++m) {
-            const int tt = stt + m * TG;
-            if (tt < cnt) {
+            for (int ww = 1; ww < NW; ++ww) {
+                const float4 x = sm.st[tt][0][ww * 64 + lane], y = sm.st[tt][1][ww * 64 + lane];
+                A.x += x.x; A.y += x.y; A.z += x.z; A.w += x.w;
+                B.x += y.x; B.y += y.y; B.z += y.z; B.w += y.w;
+            }
+            const float4 cd = sm.pcd[tt][lane];
+            const float2 kk = sm.pk[tt][lane];
+            const float beta = sm.bt[tt], s1 = sm.s1[tt];
+            const float cq[2] = {A.x, A.y}, ce[2] = {A.z, A.w}, cm[2] = {B.x, B.y}, cg[2] = {B.z, B.w};
+            const float c[2] = {cd.x, cd.y}, d[2] = {cd.z, cd.w}, kv[2] = {kk.x, kk.y};
+            float dq[2], dk[2], dg[2];
 #pragma unroll
-                for (int which = 0; which < NP; ++which) {
-                    // value (which, column sc) of wave w: thread w*64 + sc%64, word 2*which + sc/64
-                    const float *base = &sm.st[tt][2 * which + (sc >> 6)][sc & 63];
-                    float acc = base[0];
-#pragma unroll
-                    for (int ww = 1; ww < NW; ++ww) acc += base[ww * 64];
-                    pp[tt * part_tok + which * S] = acc;
+            for (int n = 0; n < 2; ++n) {
+                dq[n] = scale * fmaf(c[n], cq[n], kv[n] * s1);
+                dk[n] = fmaf(-beta * c[n], cm[n], d[n] * ce[n]);
+                dg[n] = c[n] * fmaf(-beta * kv[n], cm[n], d[n] * cg[n]);
+            }
+            const int64_t rq = ((s * a.T + ta + tt) * a.H_v + h) * NQ + qb;
+            float *pp = a.part + rq * NP * S + lane;
+            pp[0] = dq[0]; pp[64] = dq[1];
+            pp[S] = dk[0]; pp[S + 64] = dk[1];
+            if constexpr (KDA) {
+                pp[2 * S] = dg[0]; pp[2 * S + 64] = dg[1];
+            } else {
+                const float gsum = wave_sum(dg[0] + dg[1]);
+                if (lane == 0) {
+                    a.pgbuf[rq << 1] = gsum;
+                    a.pgbuf[(rq << 1) + 1] = 0.f;
                 }
             }
         }
         if (tid < cnt) {
-            const int64_t rt = ((s * a.T + ta + tid) * a.H_v + h) * NQ + qb;
-            float b = sm.redb[tid][0];
+            float b = sm.dbw[tid][0];
 #pragma unroll
-            for (int ww = 1; ww < NW; ++ww) b += sm.redb[tid][ww];
-            a.pbuf[rt] = b;
-            if constexpr (!KDA) {
-                float g = sm.redg[tid][0];
-#pragma unroll
-                for (int ww = 1; ww < NW; ++ww) g += sm.redg[tid][ww];
-                a.pgbuf[rt] = g;
-            }
+            for (int ww = 1; ww < NW; ++ww) b += sm.dbw[tid][ww];
+            a.pbuf[((s * a.T + ta + tid) * a.H_v + h) * NQ + qb] = b;
         }
-        __syncthreads();   // LDS slots free for the next sub-segment
     };
 
-    auto load_state = [&](const float *src, float (&M)[RW][2]) {
+    // replay of the window into the state slots: the state before token tt goes to st[tt]
+    auto replay_slots = [&](const float (&M0)[RW][2], int ta, auto cnt_, auto direct_tag) {
+        constexpr bool direct = decltype(direct_tag)::value;
+        const int cnt = cnt_;
+        float M[RW][2];
+#pragma unroll
+        for (int r = 0; r < RW; ++r) M[r][0] = M0[r][0], M[r][1] = M0[r][1];
+        for (int tt = 0; tt < cnt; ++tt) {
+            sm.st[tt][0][tid] = make_float4(M[0][0], M[0][1], M[1][0], M[1][1]);
+            sm.st[tt][1][tid] = make_float4(M[2][0], M[2][1], M[3][0], M[3][1]);
+            if (tt + 1 < cnt) {
+                const float2 kv = sm.kt8[tt][lane];
+                float dv[RW];
+                rows4(sm.de8[tt][w], dv);
+                if constexpr (!direct) {
+#pragma unroll
+                    for (int r = 0; r < RW; ++r) {
+                        M[r][0] = fmaf(dv[r], kv.x, M[r][0]);
+                        M[r][1] = fmaf(dv[r], kv.y, M[r][1]);
+                    }
+                } else {
+                    const int64_t t = ta + tt;
+                    const float av[2] = {ab[t * tok_ae * GW + (KDA ? lane : 0)],
+                                         ab[t * tok_ae * GW + (KDA ? lane + 64 : 0)]};
+#pragma unroll
+                    for (int r = 0; r < RW; ++r) {
+                        M[r][0] = fmaf(M[r][0], av[0], dv[r] * kv.x);
+                        M[r][1] = fmaf(M[r][1], av[1], dv[r] * kv.y);
+                    }
+                }
+            }
+        }
+    };
+
+    // one token of the reverse walk (window position tt of the window at ta): reads the
+    // replayed state from the thread's slot and leaves its column sums there
+    auto walk_token = [&](int ta, int tt, auto direct_tag) {
+        constexpr bool direct = decltype(direct_tag)::value;
+        float Mt[RW][2];
+        {
+            const float4 s0 = sm.st[tt][0][tid], s1v = sm.st[tt][1][tid];
+            Mt[0][0] = s0.x; Mt[0][1] = s0.y; Mt[1][0] = s0.z; Mt[1][1] = s0.w;
+            Mt[2][0] = s1v.x; Mt[2][1] = s1v.y; Mt[3][0] = s1v.z; Mt[3][1] = s1v.w;
+        }
+        const float4 v4 = sm.wv[tt][lane];
+        const float2 h2 = sm.wh[tt][lane];
+        const float kd[2] = {v4.x, v4.y}, qh[2] = {v4.z, v4.w};
+        const float kh[2] = {h2.x, h2.y};
+        float gy[RW], de[RW];
+        rows4(sm.gy8[tt][w], gy);
+        rows4(sm.de8[tt][w], de);
+        // dM += scale gy q^T (q./d carries the scale and the column factor)
 #pragma unroll
         for (int r = 0; r < RW; ++r)
 #pragma unroll
-            for (int n = 0; n < 2; ++n) M[r][n] = src[r * S + n * 64];
+            for (int n = 0; n < 2; ++n) X[r][n] = fmaf(gy[r], qh[n], X[r][n]);
+        float dpart[RW];
+#pragma unroll
+        for (int r = 0; r < RW; ++r) dpart[r] = fmaf(X[r][1], kd[1], X[r][0] * kd[0]);
+        // column sums that do not need dd
+        float cq[2], ce[2], cg[2];
+#pragma unroll
+        for (int n = 0; n < 2; ++n) {
+            cq[n] = Mt[0][n] * gy[0];
+            ce[n] = X[0][n] * de[0];
+            cg[n] = X[0][n] * Mt[0][n];
+#pragma unroll
+            for (int r = 1; r < RW; ++r) {
+                cq[n] = fmaf(Mt[r][n], gy[r], cq[n]);
+                ce[n] = fmaf(X[r][n], de[r], ce[n]);
+                cg[n] = fmaf(X[r][n], Mt[r][n], cg[n]);
+            }
+        }
+        // dd = dM k: reduce-scatter over the 64 lanes, then broadcast
+        float hsum[2];
+#pragma unroll
+        for (int pr = 0; pr < 2; ++pr) {
+            auto sw = __builtin_amdgcn_permlane32_swap(as_i(dpart[2 * pr]), as_i(dpart[2 * pr + 1]),
+                                                       false, false);
+            hsum[pr] = as_f(sw[0]) + as_f(sw[1]);
+        }
+        auto sw16 = __builtin_amdgcn_permlane16_swap(as_i(hsum[0]), as_i(hsum[1]), false, false);
+        const float gsum = row16_sum(as_f(sw16[0]) + as_f(sw16[1]));
+        float dd[RW];
+        dd[0] = as_f(__builtin_amdgcn_readlane(as_i(gsum), 0));
+        dd[2] = as_f(__builtin_amdgcn_readlane(as_i(gsum), 16));
+        dd[1] = as_f(__builtin_amdgcn_readlane(as_i(gsum), 32));
+        dd[3] = as_f(__builtin_amdgcn_readlane(as_i(gsum), 48));
+        const float beta = sm.bt[tt];
+        if ((lane & 15) == 0) {   // dv = beta dd for the row this lane holds
+            float *dvt = dvw + (int64_t)(ta + tt) * tok_ae * S;   // uniform base
+            dvt[dd_row] = beta * gsum;
+        }
+        {   // dbeta of the wave's rows: sum of dd (v - u)
+            float ev[RW];
+            rows4(sm.e8[tt][w], ev);
+            const float pb = fmaf(dd[3], ev[3], fmaf(dd[2], ev[2], fmaf(dd[1], ev[1], dd[0] * ev[0])));
+            if (lane == 0) sm.dbw[tt][w] = pb;
+        }
+        float cm[2];
+#pragma unroll
+        for (int n = 0; n < 2; ++n) {
+            cm[n] = Mt[0][n] * dd[0];
+#pragma unroll
+            for (int r = 1; r < RW; ++r) cm[n] = fmaf(Mt[r][n], dd[r], cm[n]);
+        }
+        // dM += du k^T with du = -beta dd (k./d carries -beta)
+#pragma unroll
+        for (int r = 0; r < RW; ++r)
+#pragma unroll
+            for (int n = 0; n < 2; ++n) X[r][n] = fmaf(dd[r], kh[n], X[r][n]);
+        if constexpr (direct) {   // unscaled window: dM .* a now
+            const int64_t t = ta + tt;
+            const float av[2] = {ab[t * tok_ae * GW + (KDA ? lane : 0)],
+                                 ab[t * tok_ae * GW + (KDA ? lane + 64 : 0)]};
+#pragma unroll
+            for (int r = 0; r < RW; ++r)
+#pragma unroll
+                for (int n = 0; n < 2; ++n) X[r][n] *= av[n];
+        }
+        sm.st[tt][0][tid] = make_float4(cq[0], cq[1], ce[0], ce[1]);
+        sm.st[tt][1][tid] = make_float4(cm[0], cm[1], cg[0], cg[1]);
     };
 
     const int n_ck = (L + C - 1) / C;
@@ -557,70 +748,87 @@ bwd128_kernel(const BwdArgs a) {
         const int t0 = sg * C, t1 = min(t0 + C, L);
         const int nvs = (t1 - t0 + VS - 1) / VS;
         float M[RW][2];
-        load_state(snapu + (int64_t)sg * S * S, M);
-        // stretch starts beyond the first: replay once and keep them in the workspace
-        if (nvs > 1) {
-            const int tend = t0 + VS * (nvs - 1);
-            load_chunk(t0, C2, false);
-            __syncthreads();
-            store_chunk(false);
-            __syncthreads();
-            for (int tc = t0; tc < tend; tc += C2) {
-                if (tc > t0 && (tc - t0) % VS == 0)
-                    put4(vsb + (int64_t)((tc - t0) / VS) * (RW / 2 * NT), M);
-                if (tc + C2 < tend) load_chunk(tc + C2, C2, false);
-                for (int tt = 0; tt < C2; ++tt) replay(tt, M, false);
-                __syncthreads();
-                if (tc + C2 < tend) store_chunk(false);
-                __syncthreads();
+        auto load_snapshot = [&]() {
+#pragma unroll
+            for (int r = 0; r < RW; ++r)
+#pragma unroll
+                for (int n = 0; n < 2; ++n) M[r][n] = snapu[(int64_t)sg * S * S + r * S + n * 64];
+        };
+        if (nvs > 1) {   // stretch starts beyond the first, kept in the workspace
+            load_snapshot();
+            for (int v = 0; v < nvs - 1; ++v) {
+                const int va = t0 + v * VS, vb = va + VS;
+                stage_stretch(va, vb);
+                for (int m = 0; m < NWS; ++m) replay_window(M, va, vb, m);
+#pragma unroll
+                for (int c = 0; c < RW / 2; ++c)
+                    vsb[(int64_t)(v + 1) * (RW / 2 * BT) + c * BT] =
+                        make_float4(M[2 * c][0], M[2 * c][1], M[2 * c + 1][0], M[2 * c + 1][1]);
             }
         }
         for (int v = nvs - 1; v >= 0; --v) {
             const int va = t0 + v * VS, vb = min(va + VS, t1);
-            const int nsub = (vb - va + C2 - 1) / C2;
-            if (v < nvs - 1) {
-                if (v == 0)
-                    load_state(snapu + (int64_t)sg * S * S, M);
-                else
-                    get4(vsb + (int64_t)v * (RW / 2 * NT), M);
-            }
-            auto cnt_of = [&](int j) { return min(C2, vb - (va + j * C2)); };
-            // first chunk of the stretch: replay chunk 0, or the walk of the only sub-segment
-            load_chunk(va, nsub > 1 ? C2 : cnt_of(0), nsub == 1);
-            __syncthreads();
-            store_chunk(nsub == 1);
-            __syncthreads();
-            // replay the stretch, keeping the state every C2 tokens in registers
-            float SS[NSUB][RW][2];
+            const int nwin = (vb - va + WIN - 1) / WIN;
+            if (v == 0) {
+                load_snapshot();
+            } else {
 #pragma unroll
-            for (int r = 0; r < RW; ++r) SS[0][r][0] = M[r][0], SS[0][r][1] = M[r][1];
-#pragma unroll
-            for (int j = 0; j < NSUB - 1; ++j) {
-                if (j < nsub - 1) {
-                    const bool next_walk = j + 1 == nsub - 1;
-                    load_chunk(va + (j + 1) * C2, next_walk ? cnt_of(j + 1) : C2, next_walk);
-                    for (int tt = 0; tt < C2; ++tt) replay(tt, M, false);
-#pragma unroll
-                    for (int r = 0; r < RW; ++r) SS[j + 1][r][0] = M[r][0], SS[j + 1][r][1] = M[r][1];
-                    __syncthreads();
-                    store_chunk(next_walk);
-                    __syncthreads();
+                for (int c = 0; c < RW / 2; ++c) {
+                    const float4 x = vsb[(int64_t)v * (RW / 2 * BT) + c * BT];
+                    M[2 * c][0] = x.x; M[2 * c][1] = x.y; M[2 * c + 1][0] = x.z; M[2 * c + 1][1] = x.w;
                 }
             }
-            // sub-segments last first: replay into LDS, then walk in reverse
+            stage_stretch(va, vb);
+            // states at every window start of the stretch
+            float SS[NWS][RW][2];
+            int flags = 0;
 #pragma unroll
-            for (int j = NSUB - 1; j >= 0; --j) {
-                if (j < nsub) {
-                    if (j > 0) load_chunk(va + (j - 1) * C2, C2, true);
+            for (int m = 0; m < NWS; ++m) {
+                if (m < nwin) {
 #pragma unroll
-                    for (int r = 0; r < RW; ++r) M[r][0] = SS[j][r][0], M[r][1] = SS[j][r][1];
-                    const int ta = va + j * C2, cnt = cnt_of(j);
-                    for (int tt = 0; tt < cnt; ++tt) replay(tt, M, true);
-                    for (int tt = cnt - 1; tt >= 0; --tt) walk(ta + tt, tt);
-                    reduce_columns(ta, cnt);
-                    if (j > 0) store_chunk(true);
-                    __syncthreads();
+                    for (int r = 0; r < RW; ++r) SS[m][r][0] = M[r][0], SS[m][r][1] = M[r][1];
+                    if (m + 1 < nwin) replay_window(M, va, vb, m);
+                    flags |= (sm.wflag[m] != 0) << m;
                 }
+            }
+            load_window(va + (nwin - 1) * WIN, vb - (va + (nwin - 1) * WIN));
+            for (int m = nwin - 1; m >= 0; --m) {
+                const int ta = va + m * WIN;
+                const int cnt = min(WIN, vb - ta);
+                const bool direct = (flags >> m) & 1;
+                __syncthreads();   // the previous window (or the stretch pass) is done
+                stage_window(cnt, direct);
+                __syncthreads();
+                if (m > 0) load_window(ta - WIN, WIN);
+                float M0[RW][2];   // state at the window start
+                switch (m) {
+#define GDN_PICK(k)                                                                    \
+    case k:                                                                            \
+        for (int r = 0; r < RW; ++r) M0[r][0] = SS[k][r][0], M0[r][1] = SS[k][r][1];   \
+        break;
+                    GDN_PICK(0) GDN_PICK(1) GDN_PICK(2) GDN_PICK(3)
+                    GDN_PICK(4) GDN_PICK(5) GDN_PICK(6) GDN_PICK(7)
+#undef GDN_PICK
+                }
+                if (cnt == WIN && !direct) {
+                    // full column-scaled window: unrolled, so every LDS offset is constant
+                    replay_slots(M0, ta, std::integral_constant<int, WIN>{}, std::false_type{});
+#pragma unroll
+                    for (int tt = WIN - 1; tt >= 0; --tt) walk_token(ta, tt, std::false_type{});
+                } else if (!direct) {
+                    replay_slots(M0, ta, cnt, std::false_type{});
+                    for (int tt = cnt - 1; tt >= 0; --tt) walk_token(ta, tt, std::false_type{});
+                } else {
+                    replay_slots(M0, ta, cnt, std::true_type{});
+                    for (int tt = cnt - 1; tt >= 0; --tt) walk_token(ta, tt, std::true_type{});
+                }
+                if (!direct) {   // fold the window's decay into the walked gradient
+                    const float2 P = sm.pP[lane];
+#pragma unroll
+                    for (int r = 0; r < RW; ++r) X[r][0] *= P.x, X[r][1] *= P.y;
+                }
+                __syncthreads();
+                reduce_columns(ta, cnt);
             }
         }
     }
@@ -632,7 +840,7 @@ bwd128_kernel(const BwdArgs a) {
 #pragma unroll
             for (int n = 0; n < 2; ++n) ds[r * S + n * 64] = X[r][n];
     }
-    for (int64_t idx = tid; idx < (int64_t)(a.T - L) * QR; idx += NT) {
+    for (int64_t idx = tid; idx < (int64_t)(a.T - L) * QR; idx += BT) {
         const int64_t t = L + idx / QR;
         a.dv[((s * a.T + t) * a.H_v + h) * S + qb * QR + idx % QR] = 0.f;
     }
@@ -683,9 +891,13 @@ __global__ void __launch_bounds__(256) combine128_kernel(const Combine128Args a)
             float g = 0.f;
             if (t < a.lens[sl]) {
                 const int64_t rt = (((seq0 + sl) * T + t) * Hv + h) * NQ;
+                if (a.kda) {
 #pragma unroll
-                for (int qb = 0; qb < NQ; ++qb)
-                    g += a.kda ? a.part[((rt + qb) * NP + 2) * S + i] : a.pgbuf[rt + qb];
+                    for (int qb = 0; qb < NQ; ++qb) g += a.part[((rt + qb) * NP + 2) * S + i];
+                } else {
+#pragma unroll
+                    for (int x = 0; x < 2 * NQ; ++x) g += a.pgbuf[rt * 2 + x];
+                }
             }
             a.dg[(((seq0 + sl) * T + t) * Hv + h) * G + i] = g;
         } else {
@@ -714,19 +926,24 @@ hipError_t launch(const void *fn, const Args &args, int blocks, int threads, hip
 
 }  // namespace
 
-hipError_t launch_fwd128(const FwdArgs &a, bool kda, int n_seqs_launch, hipStream_t st) {
-    const int blocks = n_seqs_launch * a.H_v * NQ;
-    return kda ? launch((const void *)fwd128_kernel<true>, a, blocks, THREADS, st)
-               : launch((const void *)fwd128_kernel<false>, a, blocks, THREADS, st);
+hipError_t launch_gate128(const GateArgs &a, hipStream_t st) {
+    const int64_t rows = (int64_t)a.n_seqs_launch * a.T * a.H_v;
+    if (rows <= 0) return hipSuccess;
+    int64_t blocks = a.G == 1 ? (rows + 255) / 256 : (rows + 3) / 4;
+    if (blocks > 8192) blocks = 8192;
+    return launch((const void *)gate128_kernel, a, (int)blocks, 256, st);
 }
 
-constexpr int kBwdRW = 4;   // rows per wave of the backward (8 waves per quarter)
+hipError_t launch_fwd128(const FwdArgs &a, bool kda, int n_seqs_launch, hipStream_t st) {
+    const int blocks = n_seqs_launch * a.H_v * NQ;
+    return kda ? launch((const void *)fwd128_kernel<true>, a, blocks, FT, st)
+               : launch((const void *)fwd128_kernel<false>, a, blocks, FT, st);
+}
 
 hipError_t launch_bwd128(const BwdArgs &a, bool kda, int n_seqs_launch, hipStream_t st) {
     const int blocks = n_seqs_launch * a.H_v * NQ;
-    constexpr int nt = 64 * (QR / kBwdRW);
-    return kda ? launch((const void *)bwd128_kernel<true, kBwdRW>, a, blocks, nt, st)
-               : launch((const void *)bwd128_kernel<false, kBwdRW>, a, blocks, nt, st);
+    return kda ? launch((const void *)bwd128_kernel<true>, a, blocks, BT, st)
+               : launch((const void *)bwd128_kernel<false>, a, blocks, BT, st);
 }
 
 hipError_t launch_combine128(const Combine128Args &a, hipStream_t st) {

@@ -85,7 +85,10 @@ typedef struct gdn_strides {
  *   gate        GDN_GATE_SCALAR (g is [.., H_v], one value per token and head) or
  *               GDN_GATE_KDA (g is [.., H_v, S_k])
  *   C           checkpoint interval in tokens; 0 selects ceil(sqrt(T)); values above T
- *               act as T (one segment)
+ *               act as T (one segment).  For S = 128 the interval is rounded up to a
+ *               multiple of 8 (the kernels carry the state column-scaled over 8-token
+ *               windows that checkpoints must not split); results are then bitwise the
+ *               same for every interval
  *   scale       output scale (commonly 1/sqrt(S_k))
  *   seq_lens    HOST pointer to n_seqs lengths in [0, T], or NULL for all T
  *   q, k        strides of q, k   (head counts H_k, width S_k)

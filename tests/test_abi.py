@@ -47,6 +47,8 @@ def problem(B, strides=None, **kw):
 def expected_ws(n, T, Hk, Hv, S, C, kda=True):
     al = lambda x: (x + 255) // 256 * 256  # noqa: E731
     units = n * Hv
+    if S == 128:                    # checkpoints on the 8-token window grid
+        C = -(-C // 8) * 8
     n_ck = max(1, -(-T // C))
     tot = al(units * n_ck * S * S * 4)
     if S == 128:                    # row-quarter path
@@ -58,7 +60,7 @@ def expected_ws(n, T, Hk, Hv, S, C, kda=True):
             tot = al(tot + units * 4 * nvs * 32 * S * 4)   # stretch starts
         tot = al(tot + rows * 4 * (3 if kda else 2) * S * 4)   # column partials
         tot = al(tot + rows * 4 * 4)                       # dbeta partials
-        tot = al(tot + rows * 4 * 4)                       # scalar-gate dg partials
+        tot = al(tot + rows * 4 * 2 * 4)                   # scalar-gate dg partials
         return tot
     tot = al(tot + units * C * S * S * 4)
     tot = al(tot + units * C * S * 4)
