@@ -36,7 +36,81 @@ def parse():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (for scaling "
                          "the FETCH_SIZE / WRITE_SIZE counters) and exit")
+    ap.add_argument("--pmc-summary", default=None, metavar="DIR",
+                    help="summarise rocprofv3 counter runs under DIR (fetch/, write/, cfetch/, "
+                         "cwrite/ with run_counter_collection.csv) into the traffic file under "
+                         "profiles/ and exit")
     return ap.parse_args()
+
+
+# Kernel sources whose hash stamps a traffic measurement: a measurement is reported only
+# while the kernels are unchanged.
+KERNEL_SOURCES = ["gated_delta_rule_bwd_amd/csrc/gdn_s128.hip", "gated_delta_rule_bwd_amd/csrc/gdn_api.hip",
+                  "gated_delta_rule_bwd_amd/csrc/gdn_internal.h"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_layer_kda_s128.json")
+BWD_KERNELS = ("bwd128_kernel", "combine128_kernel")   # the kernels of one gdn_bwd call
+
+
+def sources_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def pmc_summary(d):
+    """Per-dispatch HBM bytes of every kernel from FETCH_SIZE / WRITE_SIZE runs, each scaled
+    by what the same counter reads for the plain copy of --copy-calibration."""
+    import csv
+    import re
+
+    def load(sub):
+        out, disp = {}, {}
+        with open(os.path.join(d, sub, "run_counter_collection.csv")) as f:
+            for r in csv.DictReader(f):
+                m = re.search(r"(\w+_kernel)", r["Kernel_Name"])
+                k = m.group(1) if m else r["Kernel_Name"][:48]
+                out[(k, r["Counter_Name"])] = out.get((k, r["Counter_Name"]), 0.0) + float(r["Counter_Value"])
+                disp.setdefault(k, set()).add(r["Dispatch_Id"])
+        return out, {k: len(v) for k, v in disp.items()}
+
+    fe, nfe = load("fetch")
+    wr, nwr = load("write")
+    cf, ncf = load("cfetch")
+    cw, ncw = load("cwrite")
+    copy = [k for k in ncf if "copyBuffer" in k]
+    with open(os.path.join(d, "cfetch.log")) as f:
+        cal = json.loads([l for l in f if "copy_calibration_bytes" in l][-1])
+    n_copy = sum(ncf[k] for k in copy)
+    fetch_scale = n_copy * cal["copy_calibration_bytes"] / (1024 * sum(cf[(k, "FETCH_SIZE")] for k in copy))
+    write_scale = n_copy * cal["copy_calibration_bytes"] / (1024 * sum(cw[(k, "WRITE_SIZE")] for k in copy))
+    kernels = {}
+    for k in nfe:
+        if k not in nwr:
+            continue
+        kernels[k] = {"fetch_bytes": fe[(k, "FETCH_SIZE")] * 1024 * fetch_scale / nfe[k],
+                      "write_bytes": wr[(k, "WRITE_SIZE")] * 1024 * write_scale / nwr[k]}
+    return {"workload": "layer_kda_s128", "source_sha256": sources_hash(),
+            "counter_scale": {"fetch": fetch_scale, "write": write_scale},
+            "kernels": kernels}
+
+
+def traffic_bytes():
+    """HBM bytes of one gdn_bwd call from the committed counter summary, or None when the
+    summary is missing or the kernels changed since it was taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except OSError:
+        return None
+    if t.get("source_sha256") != sources_hash():
+        return None
+    ks = t["kernels"]
+    if not all(k in ks for k in BWD_KERNELS):
+        return None
+    return sum(ks[k]["fetch_bytes"] + ks[k]["write_bytes"] for k in BWD_KERNELS)
 
 
 def copy_calibration(mib):
@@ -76,6 +150,12 @@ def cpu_baseline(w, n_key_heads):
 
 def main():
     args = parse()
+    if args.pmc_summary:
+        summ = pmc_summary(args.pmc_summary)
+        with open(TRAFFIC_FILE, "w") as f:
+            json.dump(summ, f, indent=1)
+        print(json.dumps(summ, indent=1))
+        return
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
         return
@@ -144,9 +224,10 @@ def main():
         "pct_fp32_valu_peak": 100.0 * credited / (ms / 1e3) / PEAK_FP32_VALU,
         "fwd_ms": fwd_ms,
         "bwd_ms": bwd_ms,
-        "roofline": {"bound": "alu", "kernel": "gdn_bwd (bwd_kernel + grouped-head combine)",
+        "roofline": {"bound": "alu", "kernel": "gdn_bwd (bwd128_kernel + combine128_kernel)",
                      "achieved": achieved / 1e12, "peak": PEAK_FP32_VALU / 1e12,
-                     "unit": "TFLOP/s", "frac": achieved / PEAK_FP32_VALU, "traffic": None},
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_FP32_VALU,
+                     "traffic": traffic_bytes() if w.name == "layer_kda_s128" else None},
     }
     if not args.no_cpu_baseline:
         cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else 8

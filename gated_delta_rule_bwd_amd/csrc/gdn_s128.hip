@@ -133,8 +133,10 @@ __global__ void __launch_bounds__(256) gate128_kernel(const GateArgs a) {
 // ------------------------------------------------------------------ forward scan
 
 constexpr int FT = 256;            // forward threads: four waves of eight rows
-constexpr int SP = S + S / 4;      // padded vector: the 16-column block b starts at word 20 b
-__device__ __forceinline__ int padc(int c) { return c + (c >> 4) * 4; }
+constexpr int FR = 2;              // rows per lane in the forward
+constexpr int FC = 8;              // columns per lane in the forward (16 lanes per row)
+constexpr int SP = S + 8;          // padded vector: column c at word c + 4 (c / 64)
+__device__ __forceinline__ int padc(int c) { return c + 4 * (c >> 6); }
 
 template <bool KDA>
 struct alignas(16) FwdLds {
@@ -161,9 +163,10 @@ fwd128_kernel(const FwdArgs a) {
     const int C = a.C;
     const int64_t unit = s * a.H_v + h;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int lc = lane & 7;                  // 16-column block of this lane
-    const int lrow = w * 8 + (lane >> 3);     // row within the quarter
-    const int row = qb * QR + lrow;           // row of the state
+    const int lc = lane & 15;                     // 8-column block of this lane
+    const int lrow = w * 8 + (lane >> 4) * FR;    // first of the lane's two rows (quarter)
+    const int row = qb * QR + lrow;               // first of the lane's rows (state)
+    const int cb = padc(lc * FC);                 // padded offset of the lane's columns
     const bool write_y = a.y != nullptr;
 
     // staging roles: threads 0..127 hold the k and gate values of column ci for the window's
@@ -181,11 +184,25 @@ fwd128_kernel(const FwdArgs a) {
     const float *ap = a.abuf + (s * a.T * a.H_v + h) * GW + (KDA ? ci : 0);
     float *ebase = a.ebuf + (s * a.T * a.H_v + h) * S + qb * QR;
 
-    float M[16];
-    {
-        const float *st0 = a.state0 + unit * S * S + (int64_t)row * S + lc * 16;
+    float M[FR][FC];
+    auto rw_state = [&](float *base, bool store) {   // the lane's 2 x 8 block of a state
 #pragma unroll
-        for (int n = 0; n < 16; ++n) M[n] = st0[n];
+        for (int r = 0; r < FR; ++r)
+#pragma unroll
+            for (int j = 0; j < FC; j += 4) {
+                float4 *p4 = reinterpret_cast<float4 *>(base + (int64_t)(row + r) * S + lc * FC + j);
+                if (store) *p4 = make_float4(M[r][j], M[r][j + 1], M[r][j + 2], M[r][j + 3]);
+                else { const float4 v = *p4; M[r][j] = v.x; M[r][j + 1] = v.y; M[r][j + 2] = v.z; M[r][j + 3] = v.w; }
+            }
+    };
+    const bool st_vec = ((uintptr_t)a.state0 & 15) == 0;
+    if (st_vec) {
+        rw_state(const_cast<float *>(a.state0) + unit * S * S, false);
+    } else {
+#pragma unroll
+        for (int r = 0; r < FR; ++r)
+#pragma unroll
+            for (int n = 0; n < FC; ++n) M[r][n] = a.state0[unit * S * S + (int64_t)(row + r) * S + lc * FC + n];
     }
 
     float av[WIN], xv[WIN], rv = 0.f, rb = 0.f;
@@ -200,10 +217,25 @@ fwd128_kernel(const FwdArgs a) {
         if (tid < cnt) rb = bp[(int64_t)(t0 + tid) * a.sb.tok];
     };
 
-    float *snap = a.snap + unit * a.n_ck_max * S * S + (int64_t)row * S + lc * 16;
+    float *snap = a.snap + unit * a.n_ck_max * S * S;
     int ta = 0, prev_ta = 0, prev_cnt = 0;
     int cnt = min(WIN, L);
     if (cnt > 0) load_window(0, cnt);
+    // reads of the lane's 8 columns of a padded vector
+    auto ld8 = [&](const float *base, float (&x)[FC]) {
+        const float4 v0 = *reinterpret_cast<const float4 *>(base);
+        const float4 v1 = *reinterpret_cast<const float4 *>(base + 4);
+        x[0] = v0.x; x[1] = v0.y; x[2] = v0.z; x[3] = v0.w;
+        x[4] = v1.x; x[5] = v1.y; x[6] = v1.z; x[7] = v1.w;
+    };
+    auto finish = [&](int tt, float (&y)[FR], const float (&e)[FR]) {
+#pragma unroll
+        for (int r = 0; r < FR; ++r) y[r] = row16_sum(y[r]);
+        if (lc == 0) {
+            *reinterpret_cast<float2 *>(&sm.ys[tt][lrow]) = make_float2(a.scale * y[0], a.scale * y[1]);
+            *reinterpret_cast<float2 *>(&sm.es[tt][lrow]) = make_float2(e[0], e[1]);
+        }
+    };
     while (cnt > 0) {
         __syncthreads();   // the previous window's vectors and outputs are no longer read
         if (stt < prev_cnt) {
@@ -239,76 +271,82 @@ fwd128_kernel(const FwdArgs a) {
         const int ncnt = min(WIN, L - next);
         if (ncnt > 0) load_window(next, ncnt);
 
-        if (ta % C == 0) {   // checkpoint: the state before token ta
-#pragma unroll
-            for (int n = 0; n < 16; ++n) snap[(int64_t)(ta / C) * S * S + n] = M[n];
-        }
-        const int cb = lc * 20;   // padded offset of this lane's 16 columns (16-byte aligned)
-        auto ld16 = [&](const float *base, float (&x)[16]) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const float4 v = *reinterpret_cast<const float4 *>(base + 4 * j);
-                x[4 * j] = v.x; x[4 * j + 1] = v.y; x[4 * j + 2] = v.z; x[4 * j + 3] = v.w;
-            }
-        };
-        auto finish = [&](int tt, float y, float e) {
-            y += dpp<0xB1>(y);
-            y += dpp<0x4E>(y);
-            y += dpp<0x141>(y);
-            if (lc == 0) {
-                sm.ys[tt][lrow] = a.scale * y;
-                sm.es[tt][lrow] = e;
-            }
-        };
+        if (ta % C == 0) rw_state(snap + (int64_t)(ta / C) * S * S, true);   // checkpoint
         if (!direct) {
             for (int tt = 0; tt < cnt; ++tt) {
-                float kc[16], kr[16], qc[16];
-                ld16(&sm.kc[tt][cb], kc);
-                ld16(&sm.kr[tt][cb], kr);
-                ld16(&sm.qc[tt][cb], qc);
-                float u = 0.f, y = 0.f;
+                float kc[FC], kr[FC], qc[FC];
+                ld8(&sm.kc[tt][cb], kc);
+                ld8(&sm.kr[tt][cb], kr);
+                ld8(&sm.qc[tt][cb], qc);
+                const float2 vr = *reinterpret_cast<const float2 *>(&sm.vq[tt][lrow]);
+                const float beta = sm.bt[tt];
+                float u[FR], e[FR], y[FR];
 #pragma unroll
-                for (int n = 0; n < 16; ++n) u = fmaf(M[n], kc[n], u);
-                u += dpp<0xB1>(u);   // quad_perm [1,0,3,2]
-                u += dpp<0x4E>(u);   // quad_perm [2,3,0,1]
-                u += dpp<0x141>(u);  // row_half_mirror: the two quads of each 8-lane row
-                const float e = sm.vq[tt][lrow] - u;
-                const float de = sm.bt[tt] * e;
+                for (int r = 0; r < FR; ++r) {
+                    u[r] = M[r][0] * kc[0];
 #pragma unroll
-                for (int n = 0; n < 16; ++n) M[n] = fmaf(de, kr[n], M[n]);
+                    for (int n = 1; n < FC; ++n) u[r] = fmaf(M[r][n], kc[n], u[r]);
+                    u[r] = row16_sum(u[r]);
+                }
+                e[0] = vr.x - u[0];
+                e[1] = vr.y - u[1];
 #pragma unroll
-                for (int n = 0; n < 16; ++n) y = fmaf(M[n], qc[n], y);
+                for (int r = 0; r < FR; ++r) {
+                    const float de = beta * e[r];
+#pragma unroll
+                    for (int n = 0; n < FC; ++n) M[r][n] = fmaf(de, kr[n], M[r][n]);
+                    y[r] = M[r][0] * qc[0];
+#pragma unroll
+                    for (int n = 1; n < FC; ++n) y[r] = fmaf(M[r][n], qc[n], y[r]);
+                }
                 finish(tt, y, e);
             }
+            float ce[FC];
+            if constexpr (KDA) {
+                ld8(&sm.cend[cb], ce);
+            } else {
 #pragma unroll
-            for (int n = 0; n < 16; ++n) M[n] *= sm.cend[KDA ? cb + n : 0];
+                for (int n = 0; n < FC; ++n) ce[n] = sm.cend[0];
+            }
+#pragma unroll
+            for (int r = 0; r < FR; ++r)
+#pragma unroll
+                for (int n = 0; n < FC; ++n) M[r][n] *= ce[n];
         } else {
             for (int tt = 0; tt < cnt; ++tt) {
-                float kv[16], qv[16], gv[16];
-                ld16(&sm.kraw[tt][cb], kv);
-                ld16(&sm.qraw[tt][cb], qv);
+                float kv[FC], qv[FC], gv[FC];
+                ld8(&sm.kraw[tt][cb], kv);
+                ld8(&sm.qraw[tt][cb], qv);
                 if constexpr (KDA) {
-                    ld16(&sm.araw[tt][cb], gv);
+                    ld8(&sm.araw[tt][cb], gv);
                 } else {
 #pragma unroll
-                    for (int n = 0; n < 16; ++n) gv[n] = sm.araw[tt][0];
+                    for (int n = 0; n < FC; ++n) gv[n] = sm.araw[tt][0];
                 }
-                float u = 0.f, y = 0.f;
+                const float2 vr = *reinterpret_cast<const float2 *>(&sm.vq[tt][lrow]);
+                const float beta = sm.bt[tt];
+                float u[FR], e[FR], y[FR];
 #pragma unroll
-                for (int n = 0; n < 16; ++n) u = fmaf(M[n], gv[n] * kv[n], u);
-                u += dpp<0xB1>(u);
-                u += dpp<0x4E>(u);
-                u += dpp<0x141>(u);
-                const float e = sm.vq[tt][lrow] - u;
-                const float de = sm.bt[tt] * e;
+                for (int r = 0; r < FR; ++r) {
+                    u[r] = 0.f;
 #pragma unroll
-                for (int n = 0; n < 16; ++n) M[n] = fmaf(M[n], gv[n], de * kv[n]);
+                    for (int n = 0; n < FC; ++n) u[r] = fmaf(M[r][n], gv[n] * kv[n], u[r]);
+                    u[r] = row16_sum(u[r]);
+                }
+                e[0] = vr.x - u[0];
+                e[1] = vr.y - u[1];
 #pragma unroll
-                for (int n = 0; n < 16; ++n) y = fmaf(M[n], qv[n], y);
+                for (int r = 0; r < FR; ++r) {
+                    const float de = beta * e[r];
+#pragma unroll
+                    for (int n = 0; n < FC; ++n) M[r][n] = fmaf(M[r][n], gv[n], de * kv[n]);
+                    y[r] = 0.f;
+#pragma unroll
+                    for (int n = 0; n < FC; ++n) y[r] = fmaf(M[r][n], qv[n], y[r]);
+                }
                 finish(tt, y, e);
             }
         }
-
         prev_ta = ta;
         prev_cnt = cnt;
         ta = next;
@@ -327,9 +365,14 @@ fwd128_kernel(const FwdArgs a) {
         }
     }
     if (a.state_out) {
-        float *so = a.state_out + unit * S * S + (int64_t)row * S + lc * 16;
+        if (((uintptr_t)a.state_out & 15) == 0) {
+            rw_state(a.state_out + unit * S * S, true);
+        } else {
 #pragma unroll
-        for (int n = 0; n < 16; ++n) so[n] = M[n];
+            for (int r = 0; r < FR; ++r)
+#pragma unroll
+                for (int n = 0; n < FC; ++n) a.state_out[unit * S * S + (int64_t)(row + r) * S + lc * FC + n] = M[r][n];
+        }
     }
 }
 
