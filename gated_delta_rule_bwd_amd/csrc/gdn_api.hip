@@ -33,7 +33,7 @@ struct Plan {
     bool parts = false;  // S < 128: dq/dk go through per-value-head partials
     int nvs_max = 1;     // S = 128: 64-token stretches per segment
     size_t off_snap = 0, off_seg = 0, off_e = 0, off_pq = 0, off_pk = 0;
-    size_t off_a = 0, off_vs = 0, off_part = 0, off_pb = 0, off_pg = 0;
+    size_t off_a = 0, gate_floats = 0, off_wf = 0, off_vs = 0, off_part = 0, off_pb = 0, off_pg = 0;
     size_t total = 0;
 };
 
@@ -76,8 +76,11 @@ Plan make_plan(const gdn_problem *p) {
         const size_t tok_rows = (size_t)p->n_seqs * p->T * p->H_v;
         constexpr int NQ = 4;
         pl.nvs_max = std::max(1, (pl.C + 63) / 64);
-        pl.off_a = off;
-        off = align_up(off + tok_rows * pl.G * sizeof(float));
+        pl.off_a = off;   // a, c, d
+        pl.gate_floats = tok_rows * pl.G;
+        off = align_up(off + 3 * pl.gate_floats * sizeof(float));
+        pl.off_wf = off;  // window flags
+        off = align_up(off + (size_t)p->n_seqs * ((p->T + 7) / 8) * p->H_v * sizeof(int32_t));
         pl.off_e = off;
         off = align_up(off + tok_rows * S * sizeof(float));
         pl.off_vs = off;
@@ -174,6 +177,9 @@ hipError_t launch_gates(const gdn_problem *p, const Plan &pl, const float *g, vo
     std::memset(&ga, 0, sizeof(ga));
     ga.g = g;
     ga.abuf = (float *)((char *)ws + pl.off_a);
+    ga.cbuf = ga.abuf + pl.gate_floats;
+    ga.dbuf = ga.cbuf + pl.gate_floats;
+    ga.wflag = (int32_t *)((char *)ws + pl.off_wf);
     ga.sg = p->g;
     ga.s_base = s0; ga.n_seqs_launch = cnt; ga.T = p->T; ga.H_v = p->H_v; ga.G = pl.G;
     fill_lens(p, s0, cnt, ga.lens);
@@ -247,6 +253,9 @@ int gdn_fwd(const gdn_problem *p, const float *q, const float *k, const float *v
     a.y = y; a.state_out = state_out;
     a.snap = (float *)((char *)ws + pl.off_snap);
     a.abuf = (float *)((char *)ws + pl.off_a);
+    a.cbuf = a.abuf + pl.gate_floats;
+    a.dbuf = a.cbuf + pl.gate_floats;
+    a.wflag = (const int32_t *)((char *)ws + pl.off_wf);
     a.ebuf = (float *)((char *)ws + pl.off_e);
     a.sq = p->q; a.sk = p->k; a.sv = p->v; a.sg = p->g; a.sb = p->beta; a.sy = p->y;
     a.T = p->T; a.H_k = p->H_k; a.H_v = p->H_v; a.C = pl.C; a.n_ck_max = pl.n_ck_max;
@@ -308,6 +317,9 @@ int gdn_bwd(const gdn_problem *p, const float *q, const float *k, const float *v
             f.q = q; f.k = k; f.v = v; f.g = g; f.beta = beta; f.state0 = state0;
             f.snap = snap;
             f.abuf = (float *)((char *)ws + pl.off_a);
+            f.cbuf = f.abuf + pl.gate_floats;
+            f.dbuf = f.cbuf + pl.gate_floats;
+            f.wflag = (const int32_t *)((char *)ws + pl.off_wf);
             f.ebuf = (float *)((char *)ws + pl.off_e);
             f.sq = p->q; f.sk = p->k; f.sv = p->v; f.sg = p->g; f.sb = p->beta; f.sy = p->y;
             f.s_base = s0;
@@ -328,6 +340,9 @@ int gdn_bwd(const gdn_problem *p, const float *q, const float *k, const float *v
         b.snap = snap;
         if (pl.s128) {
             b.abuf = (const float *)((char *)ws + pl.off_a);
+            b.cbuf = b.abuf + pl.gate_floats;
+            b.dbuf = b.cbuf + pl.gate_floats;
+            b.wflag = (const int32_t *)((char *)ws + pl.off_wf);
             b.ebuf = (const float *)((char *)ws + pl.off_e);
             b.vsbuf = (float *)((char *)ws + pl.off_vs);
             b.part = (float *)((char *)ws + pl.off_part);

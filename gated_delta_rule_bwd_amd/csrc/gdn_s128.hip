@@ -81,6 +81,21 @@ __device__ __forceinline__ float wave_sum(float v) {
 
 __device__ __forceinline__ float rcp(float x) { return __builtin_amdgcn_rcpf(x); }
 
+// Global accesses as a wave-uniform base plus a 32-bit element offset, so the address is a
+// scalar base and one vector offset register instead of a per-lane 64-bit pointer.
+template <typename T>
+__device__ __forceinline__ T ldg(const T *base, uint32_t i) {
+    return *reinterpret_cast<const T *>(reinterpret_cast<const char *>(base) + i * (uint32_t)sizeof(T));
+}
+template <typename T>
+__device__ __forceinline__ void stg(T *base, uint32_t i, T v) {
+    *reinterpret_cast<T *>(reinterpret_cast<char *>(base) + i * (uint32_t)sizeof(T)) = v;
+}
+__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+// Compiler-only memory barrier: bounds how far the compiler hoists LDS loads (and so how many
+// registers they hold); it emits no instruction.
+__device__ __forceinline__ void hoist_fence() { asm volatile("" ::: "memory"); }
+
 // Block index -> (unit within the launch, row quarter).  The four quarters of a unit read
 // the same token vectors, so they are placed on the same XCD (blocks are dispatched to the
 // eight XCDs round robin) when the grid allows it.
@@ -99,34 +114,67 @@ __device__ __forceinline__ bool prod_ok(float c) { return c >= kScaleMin; }
 
 // ------------------------------------------------------------------ gates
 
-// a = exp(g) for every token t < len of every (sequence, value head): rows of G values.
+// For every 8-token window of every (sequence, value head): a = exp(g) per token, the
+// running product c_t = a_t0 * ... * a_t from the window's first token t0 (taken in token
+// order, so every kernel that scales by it uses the same bits), the product d_t of the
+// window's gates after t, and the flag of a window that must be processed unscaled.  One
+// wave per window for the per-channel gate (lane: columns lane, lane + 64), one thread per
+// window for the scalar gate.
 __global__ void __launch_bounds__(256) gate128_kernel(const GateArgs a) {
-    const int64_t rows = (int64_t)a.n_seqs_launch * a.T * a.H_v;
-    if (a.G == 1) {
-        for (int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; r < rows;
-             r += (int64_t)gridDim.x * blockDim.x) {
-            const int h = (int)(r % a.H_v);
-            const int64_t st = r / a.H_v;
-            const int t = (int)(st % a.T), sl = (int)(st / a.T);
-            if (t >= a.lens[sl]) continue;
-            const int64_t s = a.s_base + sl;
-            a.abuf[(s * a.T + t) * a.H_v + h] = expf(a.g[s * a.sg.seq + t * a.sg.tok + h * a.sg.head]);
-        }
-        return;
-    }
+    const int nwin = (a.T + WIN - 1) / WIN;
+    const int64_t items = (int64_t)a.n_seqs_launch * nwin * a.H_v;
+    const bool kda = a.G != 1;
     const int lane = threadIdx.x & 63;
-    const int64_t wave0 = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
-    const int64_t nwaves = (int64_t)gridDim.x * (blockDim.x >> 6);
-    for (int64_t r = wave0; r < rows; r += nwaves) {
-        const int h = (int)(r % a.H_v);
-        const int64_t st = r / a.H_v;
-        const int t = (int)(st % a.T), sl = (int)(st / a.T);
-        if (t >= a.lens[sl]) continue;
+    const int64_t first = kda ? (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6)
+                              : (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t step = kda ? (int64_t)gridDim.x * (blockDim.x >> 6) : (int64_t)gridDim.x * blockDim.x;
+    for (int64_t it = first; it < items; it += step) {
+        const int h = (int)(it % a.H_v);
+        const int64_t rest = it / a.H_v;
+        const int m = (int)(rest % nwin), sl = (int)(rest / nwin);
+        const int t0 = m * WIN;
+        const int cnt = min(WIN, a.lens[sl] - t0);
+        if (cnt <= 0) continue;
         const int64_t s = a.s_base + sl;
-        const float *gp = a.g + s * a.sg.seq + t * a.sg.tok + h * a.sg.head;
-        float *ap = a.abuf + ((s * a.T + t) * a.H_v + h) * S;
-        ap[lane] = expf(gp[lane]);
-        ap[lane + 64] = expf(gp[lane + 64]);
+        const int NC = kda ? 2 : 1;
+        float av[WIN][2];
+        bool ok = true;
+#pragma unroll
+        for (int tt = 0; tt < WIN; ++tt)
+#pragma unroll
+            for (int n = 0; n < 2; ++n) {
+                av[tt][n] = 1.f;
+                if (tt < cnt && n < NC) {
+                    const float *gp = a.g + s * a.sg.seq + (int64_t)(t0 + tt) * a.sg.tok + h * a.sg.head;
+                    av[tt][n] = expf(gp[kda ? lane + 64 * n : 0]);
+                }
+            }
+        float c[2] = {1.f, 1.f}, d[2] = {1.f, 1.f};
+#pragma unroll
+        for (int tt = 0; tt < WIN; ++tt)
+#pragma unroll
+            for (int n = 0; n < 2; ++n) {
+                ok = ok && gate_ok(av[tt][n]);
+                c[n] *= av[tt][n];
+                if (tt < cnt && n < NC) {
+                    const int64_t o = ((s * a.T + t0 + tt) * a.H_v + h) * a.G + (kda ? lane + 64 * n : 0);
+                    a.abuf[o] = av[tt][n];
+                    a.cbuf[o] = c[n];
+                }
+            }
+        ok = ok && prod_ok(c[0]) && prod_ok(c[1]);   // the padding gates are 1
+#pragma unroll
+        for (int tt = WIN - 1; tt >= 0; --tt)
+#pragma unroll
+            for (int n = 0; n < 2; ++n) {
+                if (tt < cnt && n < NC) {
+                    const int64_t o = ((s * a.T + t0 + tt) * a.H_v + h) * a.G + (kda ? lane + 64 * n : 0);
+                    a.dbuf[o] = d[n];
+                }
+                d[n] *= av[tt][n];
+            }
+        const bool direct = kda ? __ballot(!ok) != 0 : !ok;
+        if (!kda || lane == 0) a.wflag[(s * nwin + m) * a.H_v + h] = direct ? 1 : 0;
     }
 }
 
@@ -180,8 +228,11 @@ fwd128_kernel(const FwdArgs a) {
     const int64_t xtok = kside ? a.sk.tok : a.sq.tok;
     const float *vp = a.v + s * a.sv.seq + h * a.sv.head + qb * QR + srow;
     const float *bp = a.beta + s * a.sb.seq + h * a.sb.head;
-    const int64_t tok_ae = a.H_v;   // token stride of abuf / ebuf rows, in rows
+    const int64_t tok_ae = a.H_v;   // token stride of abuf / cbuf / ebuf rows, in rows
     const float *ap = a.abuf + (s * a.T * a.H_v + h) * GW + (KDA ? ci : 0);
+    const float *cp = a.cbuf + (s * a.T * a.H_v + h) * GW + (KDA ? ci : 0);
+    const int nwin_T = (a.T + WIN - 1) / WIN;
+    const int32_t *wfl = a.wflag + s * nwin_T * a.H_v + h;   // window stride H_v
     float *ebase = a.ebuf + (s * a.T * a.H_v + h) * S + qb * QR;
 
     float M[FR][FC];
@@ -205,12 +256,17 @@ fwd128_kernel(const FwdArgs a) {
             for (int n = 0; n < FC; ++n) M[r][n] = a.state0[unit * S * S + (int64_t)(row + r) * S + lc * FC + n];
     }
 
+    // per token of the window: the running product c (a column-scaled window) or the gate a
+    // (an unscaled one), the k or q value, v and beta
     float av[WIN], xv[WIN], rv = 0.f, rb = 0.f;
+    int wdir = 0;
     auto load_window = [&](int t0, int cnt) {
+        wdir = wfl[(int64_t)(t0 / WIN) * a.H_v];
+        const float *gsrc = wdir ? ap : cp;
 #pragma unroll
         for (int tt = 0; tt < WIN; ++tt) {
             const int64_t t = t0 + tt;
-            av[tt] = tt < cnt ? ap[t * tok_ae * GW] : 1.f;
+            av[tt] = tt < cnt ? gsrc[t * tok_ae * GW] : 1.f;
             xv[tt] = tt < cnt ? xp[t * xtok] : 0.f;
         }
         if (stt < cnt) rv = vp[(int64_t)(t0 + stt) * a.sv.tok];
@@ -243,30 +299,35 @@ fwd128_kernel(const FwdArgs a) {
             if (write_y) a.y[s * a.sy.seq + t * a.sy.tok + h * a.sy.head + qb * QR + srow] = sm.ys[stt][srow];
             ebase[t * tok_ae * S + srow] = sm.es[stt][srow];
         }
-        // window vectors from the registers: running product c, its reciprocal, flag
-        bool ok = true;
-        {
-            float c = 1.f;
+        // window vectors from the registers
+        const bool direct = wdir != 0;
+        if (!direct) {
+            float ce = av[0];   // product over the window: c at its last token
 #pragma unroll
             for (int tt = 0; tt < WIN; ++tt) {
-                ok = ok && gate_ok(av[tt]);
-                c *= av[tt];
+                if (tt < cnt) ce = av[tt];
                 if (kside) {
-                    sm.kc[tt][pci] = xv[tt] * c;
-                    sm.kr[tt][pci] = xv[tt] * rcp(c);
+                    sm.kc[tt][pci] = xv[tt] * av[tt];
+                    sm.kr[tt][pci] = xv[tt] * rcp(av[tt]);
+                } else {
+                    sm.qc[tt][pci] = xv[tt] * av[tt];
+                }
+            }
+            if (kside && (KDA || ci == 0)) sm.cend[KDA ? pci : 0] = ce;
+        } else {
+#pragma unroll
+            for (int tt = 0; tt < WIN; ++tt) {
+                if (kside) {
                     sm.kraw[tt][pci] = xv[tt];
                     if (KDA || ci == 0) sm.araw[tt][KDA ? pci : 0] = av[tt];
                 } else {
-                    sm.qc[tt][pci] = xv[tt] * c;
                     sm.qraw[tt][pci] = xv[tt];
                 }
             }
-            ok = ok && prod_ok(c);   // the padding gates are 1
-            if (kside && (KDA || ci == 0)) sm.cend[KDA ? pci : 0] = c;
         }
         if (stt < cnt) sm.vq[stt][srow] = rv;
         if (tid < cnt) sm.bt[tid] = rb;
-        const bool direct = __syncthreads_or(!ok) != 0;
+        __syncthreads();
         const int next = ta + cnt;
         const int ncnt = min(WIN, L - next);
         if (ncnt > 0) load_window(next, ncnt);
@@ -446,6 +507,10 @@ bwd128_kernel(const BwdArgs a) {
     const float *kp = a.k + s * a.sk.seq + hk * a.sk.head;
     const float *qp = a.q + s * a.sq.seq + hk * a.sq.head;
     const float *ab = a.abuf + (s * a.T * a.H_v + h) * GW;           // gates, token stride tok_ae*GW
+    const float *cb = a.cbuf + (s * a.T * a.H_v + h) * GW;           // window prefix products
+    const float *db = a.dbuf + (s * a.T * a.H_v + h) * GW;           // window suffix products
+    const int nwin_T = (a.T + WIN - 1) / WIN;
+    const int32_t *wfl = a.wflag + s * nwin_T * a.H_v + h;            // window stride H_v
     const float *eb = a.ebuf + (s * a.T * a.H_v + h) * S + qb * QR;  // errors, token stride tok_ae*S
     const float *gyp = a.gy + s * a.sgy.seq + h * a.sgy.head + qb * QR;
     const float *bp = a.beta + s * a.sb.seq + h * a.sb.head;
@@ -554,18 +619,18 @@ bwd128_kernel(const BwdArgs a) {
     };
 
     // ---- window data, prefetched into registers one window ahead: thread (tok = w, lane)
-    // holds the gates of columns (lane, lane + 64) for all tokens, and k, q, beta of token
-    // tok; thread tid < WIN * QR holds gy, e and beta of row tid & 31 of token tid >> 5
-    float wa[WIN][2], wk[2], wq[2], wbt = 0.f, rgy = 0.f, re = 0.f, rb = 0.f;
-    auto load_window = [&](int t0, int cnt) {
-#pragma unroll
-        for (int u = 0; u < WIN; ++u)
-#pragma unroll
-            for (int n = 0; n < 2; ++n)
-                wa[u][n] = u < cnt ? ab[(int64_t)(t0 + u) * tok_ae * GW + (KDA ? lane + 64 * n : 0)] : 1.f;
+    // holds, for columns (lane, lane + 64) of token tok, the window's running product c and
+    // the product d of its later gates (an unscaled window: the gate a, and 1), k, q, and
+    // beta; thread tid < WIN * QR holds gy, e and beta of row tid & 31 of token tid >> 5
+    float wc[2], wd[2], wk[2], wq[2], wbt = 0.f, rgy = 0.f, re = 0.f, rb = 0.f;
+    int wlast = 0;   // the window's last token
+    auto load_window = [&](int t0, int cnt, bool dir) {
         const int64_t t = t0 + w;
+        wlast = cnt - 1;
 #pragma unroll
         for (int n = 0; n < 2; ++n) {
+            wc[n] = w < cnt ? (dir ? ab : cb)[t * tok_ae * GW + (KDA ? lane + 64 * n : 0)] : 1.f;
+            wd[n] = w < cnt && !dir ? db[t * tok_ae * GW + (KDA ? lane + 64 * n : 0)] : 1.f;
             wk[n] = w < cnt ? kp[t * a.sk.tok + lane + 64 * n] : 0.f;
             wq[n] = w < cnt ? qp[t * a.sq.tok + lane + 64 * n] : 0.f;
         }
@@ -580,21 +645,7 @@ bwd128_kernel(const BwdArgs a) {
     // store the window's data and its derived vectors (cnt tokens; unscaled when direct)
     auto stage_window = [&](int cnt, bool direct) {
         const int tt = w;
-        float c[2] = {1.f, 1.f}, d[2] = {1.f, 1.f};
-#pragma unroll
-        for (int n = 0; n < 2; ++n) {
-            if (!direct) {
-#pragma unroll
-                for (int u = 0; u < WIN; ++u) {   // prefix in token order, as the forward
-                    if (u <= tt) c[n] *= wa[u][n];
-                    else d[n] *= wa[u][n];
-                }
-            } else {
-#pragma unroll
-                for (int u = 0; u < WIN; ++u)
-                    if (u == tt) c[n] = wa[u][n];
-            }
-        }
+        const float c[2] = {wc[0], wc[1]}, d[2] = {wd[0], wd[1]};   // unscaled: the gate, 1
         const float rd[2] = {direct ? 1.f : rcp(d[0]), direct ? 1.f : rcp(d[1])};
         sm.wv[tt][lane] = make_float4(wk[0] * d[0], wk[1] * d[1], scale * wq[0] * rd[0], scale * wq[1] * rd[1]);
         sm.wh[tt][lane] = make_float2(-wbt * wk[0] * rd[0], -wbt * wk[1] * rd[1]);
@@ -602,7 +653,7 @@ bwd128_kernel(const BwdArgs a) {
                                   : make_float2(wk[0] * rcp(c[0]), wk[1] * rcp(c[1]));
         sm.pcd[tt][lane] = make_float4(c[0], c[1], d[0], d[1]);
         sm.pk[tt][lane] = make_float2(wk[0], wk[1]);
-        if (tt == 0) sm.pP[lane] = direct ? make_float2(1.f, 1.f) : make_float2(c[0] * d[0], c[1] * d[1]);
+        if (tt == wlast) sm.pP[lane] = direct ? make_float2(1.f, 1.f) : make_float2(c[0], c[1]);   // window product
         if (lane == 0) sm.bt[tt] = wbt;
         if (tid < WIN * QR) {   // rows: beta e, gy, e, and the sum of (beta e) gy per token
             const int rt = tid >> 5, r = tid & 31;
@@ -834,7 +885,7 @@ bwd128_kernel(const BwdArgs a) {
                     flags |= (sm.wflag[m] != 0) << m;
                 }
             }
-            load_window(va + (nwin - 1) * WIN, vb - (va + (nwin - 1) * WIN));
+            load_window(va + (nwin - 1) * WIN, vb - (va + (nwin - 1) * WIN), (flags >> (nwin - 1)) & 1);
             for (int m = nwin - 1; m >= 0; --m) {
                 const int ta = va + m * WIN;
                 const int cnt = min(WIN, vb - ta);
@@ -842,7 +893,7 @@ bwd128_kernel(const BwdArgs a) {
                 __syncthreads();   // the previous window (or the stretch pass) is done
                 stage_window(cnt, direct);
                 __syncthreads();
-                if (m > 0) load_window(ta - WIN, WIN);
+                if (m > 0) load_window(ta - WIN, WIN, (flags >> (m - 1)) & 1);
                 float M0[RW][2];   // state at the window start
                 switch (m) {
 #define GDN_PICK(k)                                                                    \
@@ -970,9 +1021,9 @@ hipError_t launch(const void *fn, const Args &args, int blocks, int threads, hip
 }  // namespace
 
 hipError_t launch_gate128(const GateArgs &a, hipStream_t st) {
-    const int64_t rows = (int64_t)a.n_seqs_launch * a.T * a.H_v;
-    if (rows <= 0) return hipSuccess;
-    int64_t blocks = a.G == 1 ? (rows + 255) / 256 : (rows + 3) / 4;
+    const int64_t items = (int64_t)a.n_seqs_launch * ((a.T + WIN - 1) / WIN) * a.H_v;
+    if (items <= 0) return hipSuccess;
+    int64_t blocks = a.G == 1 ? (items + 255) / 256 : (items + 3) / 4;
     if (blocks > 8192) blocks = 8192;
     return launch((const void *)gate128_kernel, a, (int)blocks, 256, st);
 }

@@ -54,7 +54,8 @@ def expected_ws(n, T, Hk, Hv, S, C, kda=True):
     if S == 128:                    # row-quarter path
         rows = n * T * Hv
         nvs = max(1, -(-C // 64))
-        tot = al(tot + rows * (S if kda else 1) * 4)       # gates
+        tot = al(tot + 3 * rows * (S if kda else 1) * 4)   # gates, window products
+        tot = al(tot + n * (-(-T // 8)) * Hv * 4)          # window flags
         tot = al(tot + rows * S * 4)                       # prediction errors
         if nvs > 1:
             tot = al(tot + units * 4 * nvs * 32 * S * 4)   # stretch starts
