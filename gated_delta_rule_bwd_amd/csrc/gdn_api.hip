@@ -33,7 +33,8 @@ struct Plan {
     bool parts = false;  // S < 128: dq/dk go through per-value-head partials
     int nvs_max = 1;     // S = 128: 64-token stretches per segment
     size_t off_snap = 0, off_seg = 0, off_e = 0, off_pq = 0, off_pk = 0;
-    size_t off_a = 0, gate_floats = 0, off_wf = 0, off_vs = 0, off_part = 0, off_pb = 0, off_pg = 0;
+    size_t off_a = 0, gate_floats = 0, off_wf = 0, off_vs = 0, off_part = 0, off_pb = 0, off_pg = 0,
+           off_hf = 0;
     size_t total = 0;
 };
 
@@ -91,6 +92,8 @@ Plan make_plan(const gdn_problem *p) {
         off = align_up(off + tok_rows * NQ * sizeof(float));
         pl.off_pg = off;
         off = align_up(off + tok_rows * NQ * 2 * sizeof(float));
+        pl.off_hf = off;
+        off = align_up(off + (size_t)pl.units * NQ * pl.G * sizeof(float));
         pl.total = off;
         return pl;
     }
@@ -348,6 +351,7 @@ int gdn_bwd(const gdn_problem *p, const float *q, const float *k, const float *v
             b.part = (float *)((char *)ws + pl.off_part);
             b.pbuf = (float *)((char *)ws + pl.off_pb);
             b.pgbuf = (float *)((char *)ws + pl.off_pg);
+            b.hfin = (float *)((char *)ws + pl.off_hf);
             b.nvs_max = pl.nvs_max;
         } else {
             b.segbuf = (float *)((char *)ws + pl.off_seg);
@@ -373,7 +377,7 @@ int gdn_bwd(const gdn_problem *p, const float *q, const float *k, const float *v
             if (rc != GDN_OK) return rc;
             gdn::Combine128Args c;
             std::memset(&c, 0, sizeof(c));
-            c.part = b.part; c.pbuf = b.pbuf; c.pgbuf = b.pgbuf;
+            c.part = b.part; c.pbuf = b.pbuf; c.pgbuf = b.pgbuf; c.hfin = b.hfin;
             c.dq = dq; c.dk = dk; c.dg = dg; c.dbeta = dbeta;
             c.s_base = s0; c.n_seqs_launch = cnt; c.T = p->T; c.H_k = p->H_k; c.H_v = p->H_v;
             c.kda = kda ? 1 : 0;

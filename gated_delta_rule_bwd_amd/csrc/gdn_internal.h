@@ -48,6 +48,7 @@ struct BwdArgs {
     float *part;               // [n_seqs][T][H_v][4][3][S] column sums of each row quarter
     float *pbuf;               // [n_seqs][T][H_v][4] dbeta per quarter
     float *pgbuf;              // [n_seqs][T][H_v][4][2] scalar-gate dg per quarter and column half
+    float *hfin;               // [n_seqs][H_v][4][G] column sums of dstate_out .* M_final per quarter
     int32_t nvs_max;
     gdn_strides sq, sk, sv, sg, sb, sgy;
     int32_t s_base;
@@ -70,7 +71,7 @@ struct GateArgs {
 // Sum of the row-quarter partials (and, for dq/dk, of the value heads of each key head) on
 // the S = 128 path; writes dq, dk, dg, dbeta including the zero rows of padded tokens.
 struct Combine128Args {
-    const float *part, *pbuf, *pgbuf;
+    const float *part, *pbuf, *pgbuf, *hfin;
     float *dq, *dk, *dg, *dbeta;
     int32_t s_base, n_seqs_launch, T, H_k, H_v, kda;
     int32_t lens[kMaxSeqsPerLaunch];

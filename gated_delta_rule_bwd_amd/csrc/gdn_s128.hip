@@ -462,6 +462,7 @@ struct alignas(16) BwdLds {
         } sa;
     };
     int wflag[NWS];            // unscaled windows of the stretch
+    float hsc[NW];             // scalar gate: per-wave window-start dg
     // window data for columns (lane, lane + 64): (d.*k, scale q./d), -beta k./d, k./c for the
     // replay (raw k in an unscaled window), (c, d) and k for the column sums, the window
     // product; rows: beta e, gy, e; per token: beta, sum over the quarter's rows of
@@ -471,10 +472,9 @@ struct alignas(16) BwdLds {
     float2 kt8[WIN][64];
     float4 de8[WIN][QR / 4], gy8[WIN][QR / 4], e8[WIN][QR / 4];
     float4 pcd[WIN][64];
-    float2 pk[WIN][64];
     float bt[WIN], s1[WIN];
     float2 pP[64];
-    float dbw[WIN][NW];
+    float dd8[WIN][QR];        // dd of the quarter's rows per token
 };
 
 template <bool KDA>
@@ -514,7 +514,6 @@ bwd128_kernel(const BwdArgs a) {
     const float *eb = a.ebuf + (s * a.T * a.H_v + h) * S + qb * QR;  // errors, token stride tok_ae*S
     const float *gyp = a.gy + s * a.sgy.seq + h * a.sgy.head + qb * QR;
     const float *bp = a.beta + s * a.sb.seq + h * a.sb.head;
-    float *dvw = a.dv + (s * a.T * a.H_v + h) * S + qb * QR + wr0;    // this wave's rows
 
     float X[RW][2];   // the walked gradient dM (scaled by d inside a window)
     if (a.dstate_out) {
@@ -652,7 +651,6 @@ bwd128_kernel(const BwdArgs a) {
         sm.kt8[tt][lane] = direct ? make_float2(wk[0], wk[1])
                                   : make_float2(wk[0] * rcp(c[0]), wk[1] * rcp(c[1]));
         sm.pcd[tt][lane] = make_float4(c[0], c[1], d[0], d[1]);
-        sm.pk[tt][lane] = make_float2(wk[0], wk[1]);
         if (tt == wlast) sm.pP[lane] = direct ? make_float2(1.f, 1.f) : make_float2(c[0], c[1]);   // window product
         if (lane == 0) sm.bt[tt] = wbt;
         if (tid < WIN * QR) {   // rows: beta e, gy, e, and the sum of (beta e) gy per token
@@ -666,51 +664,139 @@ bwd128_kernel(const BwdArgs a) {
         }
     };
 
+    // ---- dg.  Each token's dg is colsum(dMp .* Mp).  At the first token t0 of a window it
+    // equals colsum(dM_out .* M0), with dM_out the walked gradient before the window and M0
+    // the state at its start; inside the window dg_t = dg_{t+1} + q.*dq_t
+    // - k.*(dM_t^T delta_t - Mp_t^T du_t), from the next window's dg_t0 down (after the
+    // sequence's last token: the column sums of dstate_out .* M_final).  The quarter writes,
+    // per token, the increment (at t0: dg_t0 itself) and, per sequence, the final column
+    // sums; the partial-sum kernel runs the recursion over each window.
+    // column sums over the wave's rows of dM .* M (per column; the scalar gate: per wave)
+    auto colsum_xm = [&](const float (&M)[RW][2], float (&hp)[2]) {
+#pragma unroll
+        for (int n = 0; n < 2; ++n) {
+            hp[n] = X[0][n] * M[0][n];
+#pragma unroll
+            for (int r = 1; r < RW; ++r) hp[n] = fmaf(X[r][n], M[r][n], hp[n]);
+        }
+    };
+    // the recursion's start: column sums over the quarter's rows of dstate_out .* M_final
+    auto start_dg = [&](const float (&Mf)[RW][2]) {
+        float hp[2];
+        colsum_xm(Mf, hp);
+        __syncthreads();   // the stretch data (sharing the slot area) is no longer read
+        if constexpr (KDA) {
+            *reinterpret_cast<float2 *>(&sm.st[0][0][tid]) = make_float2(hp[0], hp[1]);
+        } else {
+            const float hs = wave_sum(hp[0] + hp[1]);
+            if (lane == 0) sm.hsc[w] = hs;
+        }
+        __syncthreads();
+        float *hf = a.hfin + (unit * NQ + qb) * GW;
+        if constexpr (KDA) {
+            if (tid < S) {
+                float g = 0.f;
+#pragma unroll
+                for (int ww = 0; ww < NW; ++ww) g += reinterpret_cast<const float *>(&sm.st[0][0][ww * 64 + (tid & 63)])[tid >> 6];
+                hf[tid] = g;
+            }
+        } else {
+            if (tid == 0) {
+                float g = 0.f;
+#pragma unroll
+                for (int ww = 0; ww < NW; ++ww) g += sm.hsc[ww];
+                hf[0] = g;
+            }
+        }
+    };
+
     // ---- column sums of the cnt walked tokens of the window at ta: fixed-order sum over the
     // waves, scaling, and the quarter's partial outputs; dbeta from the per-wave sums.
     // Wave w handles token w, lane the columns (lane, lane + 64).
+    // outputs of a reduced window, stored once the next window is staged: global stores
+    // issued after the prefetch loads would otherwise be waited for together with them
+    float o_dq[2] = {0.f, 0.f}, o_dk[2] = {0.f, 0.f}, o_dg[2] = {0.f, 0.f}, o_dv = 0.f, o_db = 0.f;
+    int o_ta = 0, o_cnt = 0;
+    auto flush_outputs = [&]() {
+        const int tt = w;
+        if (tt < o_cnt) {
+            const int64_t rq = ((s * a.T + o_ta + tt) * a.H_v + h) * NQ + qb;
+            float *pp = a.part + rq * NP * S + lane;
+            pp[0] = o_dq[0]; pp[64] = o_dq[1];
+            pp[S] = o_dk[0]; pp[S + 64] = o_dk[1];
+            if constexpr (KDA) {
+                pp[2 * S] = o_dg[0]; pp[2 * S + 64] = o_dg[1];
+            } else if (lane == 0) {
+                a.pgbuf[rq << 1] = o_dg[0];
+                a.pgbuf[(rq << 1) + 1] = 0.f;
+            }
+            if (lane < QR) a.dv[((s * a.T + o_ta + tt) * a.H_v + h) * S + qb * QR + lane] = o_dv;
+            if (lane == 0) a.pbuf[rq] = o_db;
+        }
+        o_cnt = 0;
+    };
+
+    // ---- column sums of the cnt walked tokens of the window at ta: fixed-order sum over the
+    // waves, scaling, and the quarter's partial outputs; dv and dbeta from the rows' dd.
+    // Wave w handles token w, lane the columns (lane, lane + 64) and row lane (< 32).
     auto reduce_columns = [&](int ta, int cnt) {
         const int tt = w;
         if (tt < cnt) {   // uniform over the wave
-            float4 A = sm.st[tt][0][lane], B = sm.st[tt][1][lane];
+            float4 A = sm.st[tt][0][lane];
+            float2 B = *reinterpret_cast<const float2 *>(&sm.st[tt][1][lane]);
 #pragma unroll
             for (int ww = 1; ww < NW; ++ww) {
-                const float4 x = sm.st[tt][0][ww * 64 + lane], y = sm.st[tt][1][ww * 64 + lane];
+                const float4 x = sm.st[tt][0][ww * 64 + lane];
+                const float2 y = *reinterpret_cast<const float2 *>(&sm.st[tt][1][ww * 64 + lane]);
                 A.x += x.x; A.y += x.y; A.z += x.z; A.w += x.w;
-                B.x += y.x; B.y += y.y; B.z += y.z; B.w += y.w;
+                B.x += y.x; B.y += y.y;
             }
             const float4 cd = sm.pcd[tt][lane];
-            const float2 kk = sm.pk[tt][lane];
+            const float4 v4 = sm.wv[tt][lane];
             const float beta = sm.bt[tt], s1 = sm.s1[tt];
-            const float cq[2] = {A.x, A.y}, ce[2] = {A.z, A.w}, cm[2] = {B.x, B.y}, cg[2] = {B.z, B.w};
-            const float c[2] = {cd.x, cd.y}, d[2] = {cd.z, cd.w}, kv[2] = {kk.x, kk.y};
-            float dq[2], dk[2], dg[2];
+            const float cq[2] = {A.x, A.y}, ce[2] = {A.z, A.w}, cm[2] = {B.x, B.y};
+            const float c[2] = {cd.x, cd.y}, d[2] = {cd.z, cd.w};
+            // k = (k.*d)./d (d is 1 in an unscaled window), scale q = (scale q./d).*d
+            const float kv[2] = {v4.x * rcp(d[0]), v4.y * rcp(d[1])}, sq[2] = {v4.z * d[0], v4.w * d[1]};
+            float inc[2];
 #pragma unroll
             for (int n = 0; n < 2; ++n) {
-                dq[n] = scale * fmaf(c[n], cq[n], kv[n] * s1);
-                dk[n] = fmaf(-beta * c[n], cm[n], d[n] * ce[n]);
-                dg[n] = c[n] * fmaf(-beta * kv[n], cm[n], d[n] * cg[n]);
+                const float qs = fmaf(c[n], cq[n], kv[n] * s1);   // dq / scale
+                o_dq[n] = scale * qs;
+                const float e1 = d[n] * ce[n], e2 = beta * c[n] * cm[n];   // dM^T delta, -Mp^T du
+                o_dk[n] = e1 - e2;
+                // dg increment: q.*dq - k.*(dM^T delta - Mp^T du)
+                inc[n] = fmaf(sq[n], qs, -kv[n] * (e1 + e2));
             }
-            const int64_t rq = ((s * a.T + ta + tt) * a.H_v + h) * NQ + qb;
-            float *pp = a.part + rq * NP * S + lane;
-            pp[0] = dq[0]; pp[64] = dq[1];
-            pp[S] = dk[0]; pp[S + 64] = dk[1];
-            if constexpr (KDA) {
-                pp[2 * S] = dg[0]; pp[2 * S + 64] = dg[1];
-            } else {
-                const float gsum = wave_sum(dg[0] + dg[1]);
-                if (lane == 0) {
-                    a.pgbuf[rq << 1] = gsum;
-                    a.pgbuf[(rq << 1) + 1] = 0.f;
+            if (tt == 0 && KDA) {   // the window's first token: dg itself, from the window-start partials
+                inc[0] = inc[1] = 0.f;
+#pragma unroll
+                for (int ww = 0; ww < NW; ++ww) {
+                    const float2 v = reinterpret_cast<const float2 *>(&sm.st[(ww + 1) & 7][1][ww * 64 + lane])[1];
+                    inc[0] += v.x;
+                    inc[1] += v.y;
                 }
             }
-        }
-        if (tid < cnt) {
-            float b = sm.dbw[tid][0];
+            if constexpr (KDA) {
+                o_dg[0] = inc[0];
+                o_dg[1] = inc[1];
+            } else {
+                float gsum = wave_sum(inc[0] + inc[1]);
+                if (tt == 0) {
+                    gsum = sm.hsc[0];
 #pragma unroll
-            for (int ww = 1; ww < NW; ++ww) b += sm.dbw[tid][ww];
-            a.pbuf[((s * a.T + ta + tid) * a.H_v + h) * NQ + qb] = b;
+                    for (int ww = 1; ww < NW; ++ww) gsum += sm.hsc[ww];
+                }
+                o_dg[0] = gsum;
+            }
+            // dv = beta dd and dbeta = sum over rows of dd (v - u), row lane of the quarter
+            const float ddr = lane < QR ? sm.dd8[tt][lane] : 0.f;
+            const float er = lane < QR ? reinterpret_cast<const float *>(sm.e8[tt])[lane] : 0.f;
+            o_dv = beta * ddr;
+            o_db = half_sum(ddr * er);
         }
+        o_ta = ta;
+        o_cnt = cnt;
     };
 
     // replay of the window into the state slots: the state before token tt goes to st[tt]
@@ -773,17 +859,15 @@ bwd128_kernel(const BwdArgs a) {
 #pragma unroll
         for (int r = 0; r < RW; ++r) dpart[r] = fmaf(X[r][1], kd[1], X[r][0] * kd[0]);
         // column sums that do not need dd
-        float cq[2], ce[2], cg[2];
+        float cq[2], ce[2];
 #pragma unroll
         for (int n = 0; n < 2; ++n) {
             cq[n] = Mt[0][n] * gy[0];
             ce[n] = X[0][n] * de[0];
-            cg[n] = X[0][n] * Mt[0][n];
 #pragma unroll
             for (int r = 1; r < RW; ++r) {
                 cq[n] = fmaf(Mt[r][n], gy[r], cq[n]);
                 ce[n] = fmaf(X[r][n], de[r], ce[n]);
-                cg[n] = fmaf(X[r][n], Mt[r][n], cg[n]);
             }
         }
         // dd = dM k: reduce-scatter over the 64 lanes, then broadcast
@@ -802,16 +886,7 @@ bwd128_kernel(const BwdArgs a) {
         dd[1] = as_f(__builtin_amdgcn_readlane(as_i(gsum), 32));
         dd[3] = as_f(__builtin_amdgcn_readlane(as_i(gsum), 48));
         const float beta = sm.bt[tt];
-        if ((lane & 15) == 0) {   // dv = beta dd for the row this lane holds
-            float *dvt = dvw + (int64_t)(ta + tt) * tok_ae * S;   // uniform base
-            dvt[dd_row] = beta * gsum;
-        }
-        {   // dbeta of the wave's rows: sum of dd (v - u)
-            float ev[RW];
-            rows4(sm.e8[tt][w], ev);
-            const float pb = fmaf(dd[3], ev[3], fmaf(dd[2], ev[2], fmaf(dd[1], ev[1], dd[0] * ev[0])));
-            if (lane == 0) sm.dbw[tt][w] = pb;
-        }
+        if ((lane & 15) == 0) sm.dd8[tt][wr0 + dd_row] = gsum;   // dv and dbeta come later
         float cm[2];
 #pragma unroll
         for (int n = 0; n < 2; ++n) {
@@ -834,10 +909,11 @@ bwd128_kernel(const BwdArgs a) {
                 for (int n = 0; n < 2; ++n) X[r][n] *= av[n];
         }
         sm.st[tt][0][tid] = make_float4(cq[0], cq[1], ce[0], ce[1]);
-        sm.st[tt][1][tid] = make_float4(cm[0], cm[1], cg[0], cg[1]);
+        *reinterpret_cast<float2 *>(&sm.st[tt][1][tid]) = make_float2(cm[0], cm[1]);
     };
 
     const int n_ck = (L + C - 1) / C;
+    bool first = true;
     for (int sg = n_ck - 1; sg >= 0; --sg) {
         const int t0 = sg * C, t1 = min(t0 + C, L);
         const int nvs = (t1 - t0 + VS - 1) / VS;
@@ -885,6 +961,11 @@ bwd128_kernel(const BwdArgs a) {
                     flags |= (sm.wflag[m] != 0) << m;
                 }
             }
+            if (first) {   // the final state, for the start of the dg recursion
+                replay_window(M, va, vb, nwin - 1);
+                start_dg(M);
+                first = false;
+            }
             load_window(va + (nwin - 1) * WIN, vb - (va + (nwin - 1) * WIN), (flags >> (nwin - 1)) & 1);
             for (int m = nwin - 1; m >= 0; --m) {
                 const int ta = va + m * WIN;
@@ -893,6 +974,7 @@ bwd128_kernel(const BwdArgs a) {
                 __syncthreads();   // the previous window (or the stretch pass) is done
                 stage_window(cnt, direct);
                 __syncthreads();
+                flush_outputs();   // the previous window's results, before the prefetch
                 if (m > 0) load_window(ta - WIN, WIN, (flags >> (m - 1)) & 1);
                 float M0[RW][2];   // state at the window start
                 switch (m) {
@@ -921,12 +1003,23 @@ bwd128_kernel(const BwdArgs a) {
 #pragma unroll
                     for (int r = 0; r < RW; ++r) X[r][0] *= P.x, X[r][1] *= P.y;
                 }
+                {   // window-start dg partials, into a free half slot of this thread
+                    float hp[2];
+                    colsum_xm(M0, hp);
+                    if constexpr (KDA) {
+                        reinterpret_cast<float2 *>(&sm.st[(w + 1) & 7][1][tid])[1] = make_float2(hp[0], hp[1]);
+                    } else {
+                        const float hs = wave_sum(hp[0] + hp[1]);
+                        if (lane == 0) sm.hsc[w] = hs;
+                    }
+                }
                 __syncthreads();
                 reduce_columns(ta, cnt);
             }
         }
     }
 
+    flush_outputs();
     {
         float *ds = a.dstate + unit * S * S + (int64_t)row0 * S + lane;
 #pragma unroll
@@ -942,11 +1035,16 @@ bwd128_kernel(const BwdArgs a) {
 
 // ------------------------------------------------------------------ quarter / head sums
 
+// dq and dk: sums over the four quarters and the value heads of each key head (increasing
+// order); dbeta: sum over the quarters; dg: per 8-token window, the quarters' window-start
+// value at its first token and, from its last token down, the next window's first-token value
+// (after the sequence's last token, the final-state column sums) plus the quarters' increments.
 __global__ void __launch_bounds__(256) combine128_kernel(const Combine128Args a) {
     const int64_t T = a.T, n = a.n_seqs_launch, Hk = a.H_k, Hv = a.H_v;
     const int64_t G = a.kda ? S : 1;
+    const int64_t nwin = (T + WIN - 1) / WIN;
     const int64_t n_qk = n * T * Hk * S;   // dq and dk elements (each)
-    const int64_t n_g = n * T * Hv * G;    // dg elements
+    const int64_t n_g = n * nwin * Hv * G; // dg (window, column) chains
     const int64_t n_b = n * T * Hv;        // dbeta elements
     const int64_t NP = a.kda ? 3 : 2;
     const int64_t total = n_qk + n_g + n_b;
@@ -980,11 +1078,14 @@ __global__ void __launch_bounds__(256) combine128_kernel(const Combine128Args a)
             int64_t rest = j / G;
             const int h = (int)(rest % Hv);
             rest /= Hv;
-            const int t = (int)(rest % T);
-            const int sl = (int)(rest / T);
-            float g = 0.f;
-            if (t < a.lens[sl]) {
+            const int m = (int)(rest % nwin);
+            const int sl = (int)(rest / nwin);
+            const int t0 = m * WIN, L = a.lens[sl];
+            const int cnt = max(0, min(WIN, L - t0));
+            // sum over the quarters of the dg partial of token t
+            auto part_sum = [&](int t) {
                 const int64_t rt = (((seq0 + sl) * T + t) * Hv + h) * NQ;
+                float g = 0.f;
                 if (a.kda) {
 #pragma unroll
                     for (int qb = 0; qb < NQ; ++qb) g += a.part[((rt + qb) * NP + 2) * S + i];
@@ -992,8 +1093,33 @@ __global__ void __launch_bounds__(256) combine128_kernel(const Combine128Args a)
 #pragma unroll
                     for (int x = 0; x < 2 * NQ; ++x) g += a.pgbuf[rt * 2 + x];
                 }
+                return g;
+            };
+            float carry = 0.f;
+            if (cnt > 0) {
+                if (t0 + WIN < L) {
+                    carry = part_sum(t0 + WIN);
+                } else {
+                    const float *hf = a.hfin + ((seq0 + sl) * Hv + h) * NQ * G + i;
+#pragma unroll
+                    for (int qb = 0; qb < NQ; ++qb) carry += hf[qb * G];
+                }
             }
-            a.dg[(((seq0 + sl) * T + t) * Hv + h) * G + i] = g;
+            for (int tt = WIN - 1; tt >= 0; --tt) {
+                const int t = t0 + tt;
+                if (t >= T) continue;
+                float g = 0.f;
+                if (tt < cnt) {
+                    const float p = part_sum(t);
+                    if (tt == 0) {
+                        g = p;
+                    } else {
+                        carry += p;
+                        g = carry;
+                    }
+                }
+                a.dg[(((seq0 + sl) * T + t) * Hv + h) * G + i] = g;
+            }
         } else {
             const int64_t j = idx - n_qk - n_g;
             const int h = (int)(j % Hv);
@@ -1042,7 +1168,8 @@ hipError_t launch_bwd128(const BwdArgs &a, bool kda, int n_seqs_launch, hipStrea
 
 hipError_t launch_combine128(const Combine128Args &a, hipStream_t st) {
     const int64_t G = a.kda ? S : 1;
-    const int64_t total = (int64_t)a.n_seqs_launch * a.T * (a.H_k * S + a.H_v * G + a.H_v);
+    const int64_t total = (int64_t)a.n_seqs_launch *
+                          (a.T * (a.H_k * S + a.H_v) + (int64_t)((a.T + WIN - 1) / WIN) * a.H_v * G);
     if (total <= 0) return hipSuccess;
     int64_t blocks = (total + 255) / 256;
     if (blocks > 16384) blocks = 16384;

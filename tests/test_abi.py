@@ -62,6 +62,7 @@ def expected_ws(n, T, Hk, Hv, S, C, kda=True):
         tot = al(tot + rows * 4 * (3 if kda else 2) * S * 4)   # column partials
         tot = al(tot + rows * 4 * 4)                       # dbeta partials
         tot = al(tot + rows * 4 * 2 * 4)                   # scalar-gate dg partials
+        tot = al(tot + units * 4 * (S if kda else 1) * 4)  # final-state dg column sums
         return tot
     tot = al(tot + units * C * S * S * 4)
     tot = al(tot + units * C * S * 4)
