@@ -475,6 +475,8 @@ struct alignas(16) BwdLds {
     float bt[WIN], s1[WIN];
     float2 pP[64];
     float dd8[WIN][QR];        // dd of the quarter's rows per token
+    float D1[WIN][WIN];        // [s][t]: delta_s . gy_t over the quarter's rows
+    float D2w[NW][WIN][WIN];   // [wave][t][s]: delta_s . dd_t over the wave's rows
 };
 
 template <bool KDA>
@@ -739,7 +741,7 @@ bwd128_kernel(const BwdArgs a) {
     // ---- column sums of the cnt walked tokens of the window at ta: fixed-order sum over the
     // waves, scaling, and the quarter's partial outputs; dv and dbeta from the rows' dd.
     // Wave w handles token w, lane the columns (lane, lane + 64) and row lane (< 32).
-    auto reduce_columns = [&](int ta, int cnt) {
+    auto reduce_columns = [&](int ta, int cnt, bool direct) {
         const int tt = w;
         if (tt < cnt) {   // uniform over the wave
             float4 A = sm.st[tt][0][lane];
@@ -750,6 +752,20 @@ bwd128_kernel(const BwdArgs a) {
                 const float2 y = *reinterpret_cast<const float2 *>(&sm.st[tt][1][ww * 64 + lane]);
                 A.x += x.x; A.y += x.y; A.z += x.z; A.w += x.w;
                 B.x += y.x; B.y += y.y;
+            }
+            if (!direct && tt > 0) {   // from the window-start state to the state before token tt
+                float d2 = 0.f;        // lane s: delta_s . dd_tt over the quarter
+                if (lane < WIN) {
+#pragma unroll
+                    for (int ww = 0; ww < NW; ++ww) d2 += sm.D2w[ww][tt][lane];
+                }
+                for (int sx = 0; sx < tt; ++sx) {
+                    const float2 kc = sm.kt8[sx][lane];
+                    const float d1v = sm.D1[sx][tt];
+                    const float d2v = as_f(__builtin_amdgcn_readlane(as_i(d2), sx));
+                    A.x = fmaf(kc.x, d1v, A.x); A.y = fmaf(kc.y, d1v, A.y);
+                    B.x = fmaf(kc.x, d2v, B.x); B.y = fmaf(kc.y, d2v, B.y);
+                }
             }
             const float4 cd = sm.pcd[tt][lane];
             const float4 v4 = sm.wv[tt][lane];
@@ -835,13 +851,20 @@ bwd128_kernel(const BwdArgs a) {
 
     // one token of the reverse walk (window position tt of the window at ta): reads the
     // replayed state from the thread's slot and leaves its column sums there
-    auto walk_token = [&](int ta, int tt, auto direct_tag) {
+    // In a column-scaled window the column sums are taken against the window-start state Mh;
+    // the state before token t differs from it by sum_{s<t} delta_s (k_s./c_s)^T, whose
+    // contribution the column-sum phase adds from the row products delta_s . gy_t and
+    // delta_s . dd_t.  An unscaled window walks the replayed per-token states in the slots.
+    auto walk_token = [&](int ta, int tt, const float (&Mh)[RW][2], auto direct_tag) {
         constexpr bool direct = decltype(direct_tag)::value;
         float Mt[RW][2];
-        {
+        if constexpr (direct) {
             const float4 s0 = sm.st[tt][0][tid], s1v = sm.st[tt][1][tid];
             Mt[0][0] = s0.x; Mt[0][1] = s0.y; Mt[1][0] = s0.z; Mt[1][1] = s0.w;
             Mt[2][0] = s1v.x; Mt[2][1] = s1v.y; Mt[3][0] = s1v.z; Mt[3][1] = s1v.w;
+        } else {
+#pragma unroll
+            for (int r = 0; r < RW; ++r) Mt[r][0] = Mh[r][0], Mt[r][1] = Mh[r][1];
         }
         const float4 v4 = sm.wv[tt][lane];
         const float2 h2 = sm.wh[tt][lane];
@@ -887,6 +910,12 @@ bwd128_kernel(const BwdArgs a) {
         dd[3] = as_f(__builtin_amdgcn_readlane(as_i(gsum), 48));
         const float beta = sm.bt[tt];
         if ((lane & 15) == 0) sm.dd8[tt][wr0 + dd_row] = gsum;   // dv and dbeta come later
+        if constexpr (!direct) {   // delta_s . dd_t over the wave's rows, lane s
+            if (lane < WIN) {
+                const float4 x = sm.de8[lane][w];
+                sm.D2w[w][tt][lane] = fmaf(x.w, dd[3], fmaf(x.z, dd[2], fmaf(x.y, dd[1], x.x * dd[0])));
+            }
+        }
         float cm[2];
 #pragma unroll
         for (int n = 0; n < 2; ++n) {
@@ -974,6 +1003,17 @@ bwd128_kernel(const BwdArgs a) {
                 __syncthreads();   // the previous window (or the stretch pass) is done
                 stage_window(cnt, direct);
                 __syncthreads();
+                {   // delta_s . gy_t over the quarter's rows for s = w (lane: t = lane & 7, rows 4 (lane >> 3)..)
+                    const int t = lane & 7, c4 = lane >> 3;
+                    const float4 x = sm.de8[w][c4], y = sm.gy8[t][c4];
+                    float p = fmaf(x.w, y.w, fmaf(x.z, y.z, fmaf(x.y, y.y, x.x * y.x)));
+                    p += dpp<0x128>(p);   // row_ror 8
+                    auto p16 = __builtin_amdgcn_permlane16_swap(as_i(p), as_i(p), false, false);
+                    p = as_f(p16[0]) + as_f(p16[1]);
+                    auto p32 = __builtin_amdgcn_permlane32_swap(as_i(p), as_i(p), false, false);
+                    p = as_f(p32[0]) + as_f(p32[1]);
+                    if (lane < WIN) sm.D1[w][lane] = p;
+                }
                 flush_outputs();   // the previous window's results, before the prefetch
                 if (m > 0) load_window(ta - WIN, WIN, (flags >> (m - 1)) & 1);
                 float M0[RW][2];   // state at the window start
@@ -988,15 +1028,13 @@ bwd128_kernel(const BwdArgs a) {
                 }
                 if (cnt == WIN && !direct) {
                     // full column-scaled window: unrolled, so every LDS offset is constant
-                    replay_slots(M0, ta, std::integral_constant<int, WIN>{}, std::false_type{});
 #pragma unroll
-                    for (int tt = WIN - 1; tt >= 0; --tt) walk_token(ta, tt, std::false_type{});
+                    for (int tt = WIN - 1; tt >= 0; --tt) walk_token(ta, tt, M0, std::false_type{});
                 } else if (!direct) {
-                    replay_slots(M0, ta, cnt, std::false_type{});
-                    for (int tt = cnt - 1; tt >= 0; --tt) walk_token(ta, tt, std::false_type{});
+                    for (int tt = cnt - 1; tt >= 0; --tt) walk_token(ta, tt, M0, std::false_type{});
                 } else {
                     replay_slots(M0, ta, cnt, std::true_type{});
-                    for (int tt = cnt - 1; tt >= 0; --tt) walk_token(ta, tt, std::true_type{});
+                    for (int tt = cnt - 1; tt >= 0; --tt) walk_token(ta, tt, M0, std::true_type{});
                 }
                 if (!direct) {   // fold the window's decay into the walked gradient
                     const float2 P = sm.pP[lane];
@@ -1014,7 +1052,7 @@ bwd128_kernel(const BwdArgs a) {
                     }
                 }
                 __syncthreads();
-                reduce_columns(ta, cnt);
+                reduce_columns(ta, cnt, direct);
             }
         }
     }
