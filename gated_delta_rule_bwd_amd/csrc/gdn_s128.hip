@@ -745,11 +745,11 @@ bwd128_kernel(const BwdArgs a) {
         const int tt = w;
         if (tt < cnt) {   // uniform over the wave
             float4 A = sm.st[tt][0][lane];
-            float2 B = *reinterpret_cast<const float2 *>(&sm.st[tt][1][lane]);
+            float2 B = reinterpret_cast<const float2 *>(&sm.st[tt][1][0])[lane];
 #pragma unroll
             for (int ww = 1; ww < NW; ++ww) {
                 const float4 x = sm.st[tt][0][ww * 64 + lane];
-                const float2 y = *reinterpret_cast<const float2 *>(&sm.st[tt][1][ww * 64 + lane]);
+                const float2 y = reinterpret_cast<const float2 *>(&sm.st[tt][1][ww * 64])[lane];
                 A.x += x.x; A.y += x.y; A.z += x.z; A.w += x.w;
                 B.x += y.x; B.y += y.y;
             }
@@ -788,7 +788,7 @@ bwd128_kernel(const BwdArgs a) {
                 inc[0] = inc[1] = 0.f;
 #pragma unroll
                 for (int ww = 0; ww < NW; ++ww) {
-                    const float2 v = reinterpret_cast<const float2 *>(&sm.st[(ww + 1) & 7][1][ww * 64 + lane])[1];
+                    const float2 v = reinterpret_cast<const float2 *>(&sm.st[(ww + 1) & 7][1][ww * 64 + 32])[lane];
                     inc[0] += v.x;
                     inc[1] += v.y;
                 }
@@ -938,7 +938,9 @@ bwd128_kernel(const BwdArgs a) {
                 for (int n = 0; n < 2; ++n) X[r][n] *= av[n];
         }
         sm.st[tt][0][tid] = make_float4(cq[0], cq[1], ce[0], ce[1]);
-        *reinterpret_cast<float2 *>(&sm.st[tt][1][tid]) = make_float2(cm[0], cm[1]);
+        // Mt^T dd packed in the first half of the wave's slots of the second kind: consecutive
+        // lanes at consecutive 8 bytes (no bank conflicts); those slots' states are read above
+        reinterpret_cast<float2 *>(&sm.st[tt][1][w * 64])[lane] = make_float2(cm[0], cm[1]);
     };
 
     const int n_ck = (L + C - 1) / C;
@@ -1041,11 +1043,11 @@ bwd128_kernel(const BwdArgs a) {
 #pragma unroll
                     for (int r = 0; r < RW; ++r) X[r][0] *= P.x, X[r][1] *= P.y;
                 }
-                {   // window-start dg partials, into a free half slot of this thread
+                {   // window-start dg partials, packed in the second half of the wave's slots of token w + 1
                     float hp[2];
                     colsum_xm(M0, hp);
                     if constexpr (KDA) {
-                        reinterpret_cast<float2 *>(&sm.st[(w + 1) & 7][1][tid])[1] = make_float2(hp[0], hp[1]);
+                        reinterpret_cast<float2 *>(&sm.st[(w + 1) & 7][1][w * 64 + 32])[lane] = make_float2(hp[0], hp[1]);
                     } else {
                         const float hs = wave_sum(hp[0] + hp[1]);
                         if (lane == 0) sm.hsc[w] = hs;
