@@ -77,9 +77,9 @@ Plan make_plan(const gdn_problem *p) {
         const size_t tok_rows = (size_t)p->n_seqs * p->T * p->H_v;
         constexpr int NQ = 4;
         pl.nvs_max = std::max(1, (pl.C + 63) / 64);
-        pl.off_a = off;   // a, c, d
+        pl.off_a = off;   // window gate factors c (or a) and d
         pl.gate_floats = tok_rows * pl.G;
-        off = align_up(off + 3 * pl.gate_floats * sizeof(float));
+        off = align_up(off + 2 * pl.gate_floats * sizeof(float));
         pl.off_wf = off;  // window flags
         off = align_up(off + (size_t)p->n_seqs * ((p->T + 7) / 8) * p->H_v * sizeof(int32_t));
         pl.off_e = off;
@@ -173,14 +173,14 @@ void fill_lens(const gdn_problem *p, int s0, int count, int32_t *dst) {
 
 int device_status(hipError_t e) { return e == hipSuccess ? GDN_OK : GDN_ERR_DEVICE; }
 
-// a = exp(g) into the workspace for sequences s0 .. s0 + cnt - 1 (head size 128)
+// per-window gate factors and flags into the workspace for sequences s0 .. s0 + cnt - 1
+// (head size 128)
 hipError_t launch_gates(const gdn_problem *p, const Plan &pl, const float *g, void *ws, int s0,
                         int cnt, hipStream_t st) {
     gdn::GateArgs ga;
     std::memset(&ga, 0, sizeof(ga));
     ga.g = g;
-    ga.abuf = (float *)((char *)ws + pl.off_a);
-    ga.cbuf = ga.abuf + pl.gate_floats;
+    ga.cbuf = (float *)((char *)ws + pl.off_a);
     ga.dbuf = ga.cbuf + pl.gate_floats;
     ga.wflag = (int32_t *)((char *)ws + pl.off_wf);
     ga.sg = p->g;
@@ -255,8 +255,7 @@ int gdn_fwd(const gdn_problem *p, const float *q, const float *k, const float *v
     a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.state0 = state0;
     a.y = y; a.state_out = state_out;
     a.snap = (float *)((char *)ws + pl.off_snap);
-    a.abuf = (float *)((char *)ws + pl.off_a);
-    a.cbuf = a.abuf + pl.gate_floats;
+    a.cbuf = (float *)((char *)ws + pl.off_a);
     a.dbuf = a.cbuf + pl.gate_floats;
     a.wflag = (const int32_t *)((char *)ws + pl.off_wf);
     a.ebuf = (float *)((char *)ws + pl.off_e);
@@ -319,8 +318,7 @@ int gdn_bwd(const gdn_problem *p, const float *q, const float *k, const float *v
             std::memset(&f, 0, sizeof(f));
             f.q = q; f.k = k; f.v = v; f.g = g; f.beta = beta; f.state0 = state0;
             f.snap = snap;
-            f.abuf = (float *)((char *)ws + pl.off_a);
-            f.cbuf = f.abuf + pl.gate_floats;
+            f.cbuf = (float *)((char *)ws + pl.off_a);
             f.dbuf = f.cbuf + pl.gate_floats;
             f.wflag = (const int32_t *)((char *)ws + pl.off_wf);
             f.ebuf = (float *)((char *)ws + pl.off_e);
@@ -342,8 +340,7 @@ int gdn_bwd(const gdn_problem *p, const float *q, const float *k, const float *v
         b.q = q; b.k = k; b.v = v; b.g = g; b.beta = beta; b.gy = gy; b.dstate_out = dstate_out;
         b.snap = snap;
         if (pl.s128) {
-            b.abuf = (const float *)((char *)ws + pl.off_a);
-            b.cbuf = b.abuf + pl.gate_floats;
+            b.cbuf = (const float *)((char *)ws + pl.off_a);
             b.dbuf = b.cbuf + pl.gate_floats;
             b.wflag = (const int32_t *)((char *)ws + pl.off_wf);
             b.ebuf = (const float *)((char *)ws + pl.off_e);

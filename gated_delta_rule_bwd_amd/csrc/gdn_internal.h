@@ -18,11 +18,12 @@ struct FwdArgs {
     float *y;          // nullptr: do not write y
     float *state_out;  // nullptr: do not write the final state
     float *snap;       // [unit][n_ck_max][S][S] snapshots (state before tokens 0, C, 2C, ...)
-    // S = 128 path, written by the gate kernel, each [n_seqs][T][H_v][G]: gates a = exp(g),
-    // their running product c within the token's 8-token window (inclusive) and the
-    // product d of the window's later gates; wflag [n_seqs][ceil(T / 8)][H_v] is nonzero
-    // for a window processed unscaled
-    const float *abuf, *cbuf, *dbuf;
+    // S = 128 path, written by the gate kernel, each [n_seqs][T][H_v][G]: in a window
+    // processed column-scaled, cbuf holds the running product c of the gates a = exp(g)
+    // within the token's 8-token window (inclusive) and dbuf the product d of the window's
+    // later gates; in a window processed unscaled, cbuf holds a itself and dbuf 1.  wflag
+    // [n_seqs][ceil(T / 8)][H_v] is nonzero for a window processed unscaled
+    const float *cbuf, *dbuf;
     const int32_t *wflag;
     float *ebuf;       // S = 128 path: prediction errors e = v - u, [n_seqs][T][H_v][S]
     gdn_strides sq, sk, sv, sg, sb, sy;
@@ -42,7 +43,7 @@ struct BwdArgs {
     int64_t dqk_head;   // head count of the dq/dk arrays (H_k direct, H_v for partials)
     float *dv, *dg, *dbeta, *dstate;
     // S = 128 path
-    const float *abuf, *cbuf, *dbuf, *ebuf;  // gate kernel and forward outputs (see FwdArgs)
+    const float *cbuf, *dbuf, *ebuf;  // gate kernel and forward outputs (see FwdArgs)
     const int32_t *wflag;
     float *vsbuf;              // [unit][4][nvs_max][32 x S] states at 64-token boundaries
     float *part;               // [n_seqs][T][H_v][4][3][S] column sums of each row quarter
@@ -57,11 +58,11 @@ struct BwdArgs {
     int32_t lens[kMaxSeqsPerLaunch];
 };
 
-// Gates a = exp(g) of every token t < len of the launch's sequences, with the per-window
-// products and flags described in FwdArgs (S = 128 path).
+// Per-window gate factors and flags of every token t < len of the launch's sequences, as
+// described in FwdArgs (S = 128 path).
 struct GateArgs {
     const float *g;
-    float *abuf, *cbuf, *dbuf;   // [n_seqs][T][H_v][G]
+    float *cbuf, *dbuf;          // [n_seqs][T][H_v][G]
     int32_t *wflag;              // [n_seqs][ceil(T / 8)][H_v]
     gdn_strides sg;
     int32_t s_base, n_seqs_launch, T, H_v, G;

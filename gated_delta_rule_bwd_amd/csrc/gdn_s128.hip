@@ -24,7 +24,8 @@
 // unscaled instead, with the decay applied per token; both directions take that decision
 // from the same values.
 //
-// Kernels: gate128_kernel writes a = exp(g) once (both directions read it); fwd128_kernel
+// Kernels: gate128_kernel writes each window's gate factors once (both directions read
+// them); fwd128_kernel
 // (four waves, 8 lanes per row with 16 columns each, so the row sums u = Mp k and y = M q
 // are three DPP adds) writes y, the final state, the snapshots every C tokens and the
 // prediction errors e = v - u; bwd128_kernel (eight waves, 64 lanes per row with columns
@@ -114,12 +115,14 @@ __device__ __forceinline__ bool prod_ok(float c) { return c >= kScaleMin; }
 
 // ------------------------------------------------------------------ gates
 
-// For every 8-token window of every (sequence, value head): a = exp(g) per token, the
-// running product c_t = a_t0 * ... * a_t from the window's first token t0 (taken in token
-// order, so every kernel that scales by it uses the same bits), the product d_t of the
-// window's gates after t, and the flag of a window that must be processed unscaled.  One
-// wave per window for the per-channel gate (lane: columns lane, lane + 64), one thread per
-// window for the scalar gate.
+// For every 8-token window of every (sequence, value head): the gates a = exp(g) of its
+// tokens, the running product c_t = a_t0 * ... * a_t from the window's first token t0 (taken
+// in token order, so every kernel that scales by it uses the same bits), the product d_t of
+// the window's gates after t, and the flag of a window that must be processed unscaled.  A
+// column-scaled window stores (c, d) per token, an unscaled one (a, 1), so the kernels load
+// the same array in both cases and need the flag only when they use the values.  One wave
+// per window for the per-channel gate (lane: columns lane, lane + 64), one thread per window
+// for the scalar gate.
 __global__ void __launch_bounds__(256) gate128_kernel(const GateArgs a) {
     const int nwin = (a.T + WIN - 1) / WIN;
     const int64_t items = (int64_t)a.n_seqs_launch * nwin * a.H_v;
@@ -137,7 +140,7 @@ __global__ void __launch_bounds__(256) gate128_kernel(const GateArgs a) {
         if (cnt <= 0) continue;
         const int64_t s = a.s_base + sl;
         const int NC = kda ? 2 : 1;
-        float av[WIN][2];
+        float av[WIN][2], cv[WIN][2];
         bool ok = true;
 #pragma unroll
         for (int tt = 0; tt < WIN; ++tt)
@@ -149,31 +152,29 @@ __global__ void __launch_bounds__(256) gate128_kernel(const GateArgs a) {
                     av[tt][n] = expf(gp[kda ? lane + 64 * n : 0]);
                 }
             }
-        float c[2] = {1.f, 1.f}, d[2] = {1.f, 1.f};
+        float c[2] = {1.f, 1.f};
 #pragma unroll
         for (int tt = 0; tt < WIN; ++tt)
 #pragma unroll
             for (int n = 0; n < 2; ++n) {
                 ok = ok && gate_ok(av[tt][n]);
                 c[n] *= av[tt][n];
-                if (tt < cnt && n < NC) {
-                    const int64_t o = ((s * a.T + t0 + tt) * a.H_v + h) * a.G + (kda ? lane + 64 * n : 0);
-                    a.abuf[o] = av[tt][n];
-                    a.cbuf[o] = c[n];
-                }
+                cv[tt][n] = c[n];
             }
         ok = ok && prod_ok(c[0]) && prod_ok(c[1]);   // the padding gates are 1
+        const bool direct = kda ? __ballot(!ok) != 0 : !ok;
+        float d[2] = {1.f, 1.f};
 #pragma unroll
         for (int tt = WIN - 1; tt >= 0; --tt)
 #pragma unroll
             for (int n = 0; n < 2; ++n) {
                 if (tt < cnt && n < NC) {
                     const int64_t o = ((s * a.T + t0 + tt) * a.H_v + h) * a.G + (kda ? lane + 64 * n : 0);
-                    a.dbuf[o] = d[n];
+                    a.cbuf[o] = direct ? av[tt][n] : cv[tt][n];
+                    a.dbuf[o] = direct ? 1.f : d[n];
                 }
                 d[n] *= av[tt][n];
             }
-        const bool direct = kda ? __ballot(!ok) != 0 : !ok;
         if (!kda || lane == 0) a.wflag[(s * nwin + m) * a.H_v + h] = direct ? 1 : 0;
     }
 }
@@ -194,7 +195,7 @@ struct alignas(16) FwdLds {
     float cend[GW];                                      // product over the window
     float vq[WIN][QR];                                   // v of this quarter's rows
     float bt[WIN];                                       // beta
-    float ys[WIN][QR], es[WIN][QR];                      // outputs of the window
+    float ys[2][WIN][QR], es[2][WIN][QR];                // outputs of the last two windows
 };
 
 template <bool KDA>
@@ -228,8 +229,7 @@ fwd128_kernel(const FwdArgs a) {
     const int64_t xtok = kside ? a.sk.tok : a.sq.tok;
     const float *vp = a.v + s * a.sv.seq + h * a.sv.head + qb * QR + srow;
     const float *bp = a.beta + s * a.sb.seq + h * a.sb.head;
-    const int64_t tok_ae = a.H_v;   // token stride of abuf / cbuf / ebuf rows, in rows
-    const float *ap = a.abuf + (s * a.T * a.H_v + h) * GW + (KDA ? ci : 0);
+    const int64_t tok_ae = a.H_v;   // token stride of cbuf / ebuf rows, in rows
     const float *cp = a.cbuf + (s * a.T * a.H_v + h) * GW + (KDA ? ci : 0);
     const int nwin_T = (a.T + WIN - 1) / WIN;
     const int32_t *wfl = a.wflag + s * nwin_T * a.H_v + h;   // window stride H_v
@@ -255,26 +255,38 @@ fwd128_kernel(const FwdArgs a) {
 #pragma unroll
             for (int n = 0; n < FC; ++n) M[r][n] = a.state0[unit * S * S + (int64_t)(row + r) * S + lc * FC + n];
     }
+    // the state has arrived before the scan starts, so no wait inside the scan is charged to it
+    __builtin_amdgcn_s_waitcnt(0);
 
-    // per token of the window: the running product c (a column-scaled window) or the gate a
-    // (an unscaled one), the k or q value, v and beta
+    // per token of the window: the gate factor (the running product c in a column-scaled
+    // window, the gate a in an unscaled one), the k or q value, v and beta; the window's flag
+    // is used only at its staging, one window later
     float av[WIN], xv[WIN], rv = 0.f, rb = 0.f;
     int wdir = 0;
     auto load_window = [&](int t0, int cnt) {
         wdir = wfl[(int64_t)(t0 / WIN) * a.H_v];
-        const float *gsrc = wdir ? ap : cp;
 #pragma unroll
-        for (int tt = 0; tt < WIN; ++tt) {
-            const int64_t t = t0 + tt;
-            av[tt] = tt < cnt ? gsrc[t * tok_ae * GW] : 1.f;
-            xv[tt] = tt < cnt ? xp[t * xtok] : 0.f;
+        for (int tt = 0; tt < WIN; ++tt) {   // clamped loads: no branch per token
+            const int64_t t = t0 + min(tt, cnt - 1);
+            const float g = cp[t * tok_ae * GW], x = xp[t * xtok];
+            av[tt] = tt < cnt ? g : 1.f;
+            xv[tt] = tt < cnt ? x : 0.f;
         }
-        if (stt < cnt) rv = vp[(int64_t)(t0 + stt) * a.sv.tok];
-        if (tid < cnt) rb = bp[(int64_t)(t0 + tid) * a.sb.tok];
+        const int64_t tv = t0 + min(stt, cnt - 1), tb = t0 + min(tid & (WIN - 1), cnt - 1);
+        rv = vp[tv * a.sv.tok];
+        rb = bp[tb * a.sb.tok];
+    };
+    // outputs of the window at t (cnt tokens) from output buffer ob
+    auto flush = [&](int t, int cnt, int ob) {
+        if (stt < cnt) {
+            const int64_t tt = t + stt;
+            if (write_y) a.y[s * a.sy.seq + tt * a.sy.tok + h * a.sy.head + qb * QR + srow] = sm.ys[ob][stt][srow];
+            ebase[tt * tok_ae * S + srow] = sm.es[ob][stt][srow];
+        }
     };
 
     float *snap = a.snap + unit * a.n_ck_max * S * S;
-    int ta = 0, prev_ta = 0, prev_cnt = 0;
+    int ta = 0, prev_ta = 0, prev_cnt = 0, ob = 0;
     int cnt = min(WIN, L);
     if (cnt > 0) load_window(0, cnt);
     // reads of the lane's 8 columns of a padded vector
@@ -288,18 +300,15 @@ fwd128_kernel(const FwdArgs a) {
 #pragma unroll
         for (int r = 0; r < FR; ++r) y[r] = row16_sum(y[r]);
         if (lc == 0) {
-            *reinterpret_cast<float2 *>(&sm.ys[tt][lrow]) = make_float2(a.scale * y[0], a.scale * y[1]);
-            *reinterpret_cast<float2 *>(&sm.es[tt][lrow]) = make_float2(e[0], e[1]);
+            *reinterpret_cast<float2 *>(&sm.ys[ob][tt][lrow]) = make_float2(a.scale * y[0], a.scale * y[1]);
+            *reinterpret_cast<float2 *>(&sm.es[ob][tt][lrow]) = make_float2(e[0], e[1]);
         }
     };
+    // Per window: stage its vectors from the registers; store the previous window's outputs
+    // and the checkpoint; prefetch the next window; scan.  The stores go out before the
+    // prefetch loads, so the next staging's wait for those loads does not wait for them too.
     while (cnt > 0) {
-        __syncthreads();   // the previous window's vectors and outputs are no longer read
-        if (stt < prev_cnt) {
-            const int64_t t = prev_ta + stt;
-            if (write_y) a.y[s * a.sy.seq + t * a.sy.tok + h * a.sy.head + qb * QR + srow] = sm.ys[stt][srow];
-            ebase[t * tok_ae * S + srow] = sm.es[stt][srow];
-        }
-        // window vectors from the registers
+        __syncthreads();   // the previous window's vectors are no longer read
         const bool direct = wdir != 0;
         if (!direct) {
             float ce = av[0];   // product over the window: c at its last token
@@ -328,11 +337,12 @@ fwd128_kernel(const FwdArgs a) {
         if (stt < cnt) sm.vq[stt][srow] = rv;
         if (tid < cnt) sm.bt[tid] = rb;
         __syncthreads();
+        flush(prev_ta, prev_cnt, ob ^ 1);
+        if (ta % C == 0) rw_state(snap + (int64_t)(ta / C) * S * S, true);   // checkpoint
         const int next = ta + cnt;
         const int ncnt = min(WIN, L - next);
         if (ncnt > 0) load_window(next, ncnt);
 
-        if (ta % C == 0) rw_state(snap + (int64_t)(ta / C) * S * S, true);   // checkpoint
         if (!direct) {
             for (int tt = 0; tt < cnt; ++tt) {
                 float kc[FC], kr[FC], qc[FC];
@@ -412,13 +422,10 @@ fwd128_kernel(const FwdArgs a) {
         prev_cnt = cnt;
         ta = next;
         cnt = ncnt;
+        ob ^= 1;
     }
     __syncthreads();
-    if (stt < prev_cnt) {
-        const int64_t t = prev_ta + stt;
-        if (write_y) a.y[s * a.sy.seq + t * a.sy.tok + h * a.sy.head + qb * QR + srow] = sm.ys[stt][srow];
-        ebase[t * tok_ae * S + srow] = sm.es[stt][srow];
-    }
+    flush(prev_ta, prev_cnt, ob ^ 1);
     if (write_y) {
         for (int64_t idx = tid; idx < (int64_t)(a.T - L) * QR; idx += FT) {
             const int64_t t = L + idx / QR;
@@ -508,9 +515,10 @@ bwd128_kernel(const BwdArgs a) {
                   ((unit * NQ + qb) * (int64_t)a.nvs_max) * (RW / 2 * BT) + tid;
     const float *kp = a.k + s * a.sk.seq + hk * a.sk.head;
     const float *qp = a.q + s * a.sq.seq + hk * a.sq.head;
-    const float *ab = a.abuf + (s * a.T * a.H_v + h) * GW;           // gates, token stride tok_ae*GW
-    const float *cb = a.cbuf + (s * a.T * a.H_v + h) * GW;           // window prefix products
-    const float *db = a.dbuf + (s * a.T * a.H_v + h) * GW;           // window suffix products
+    // window gate factors, token stride tok_ae * GW: running products c and suffix products d
+    // (an unscaled window: the gates a, and 1)
+    const float *cb = a.cbuf + (s * a.T * a.H_v + h) * GW;
+    const float *db = a.dbuf + (s * a.T * a.H_v + h) * GW;
     const int nwin_T = (a.T + WIN - 1) / WIN;
     const int32_t *wfl = a.wflag + s * nwin_T * a.H_v + h;            // window stride H_v
     const float *eb = a.ebuf + (s * a.T * a.H_v + h) * S + qb * QR;  // errors, token stride tok_ae*S
@@ -541,12 +549,15 @@ bwd128_kernel(const BwdArgs a) {
             const int t0 = va + (cr + CT * x) * WIN;
             cn[x] = t0 < vb ? min(WIN, vb - t0) : 0;
 #pragma unroll
-            for (int tt = 0; tt < WIN; ++tt) {
-                const int64_t t = t0 + tt;
-                kv[x][tt] = tt < cn[x] ? kp[t * a.sk.tok + ci] : 0.f;
-                cv[x][tt] = tt < cn[x] ? ab[t * tok_ae * GW + (KDA ? ci : 0)] : 1.f;
+            for (int tt = 0; tt < WIN; ++tt) {   // clamped loads (no branch per token)
+                const int64_t t = min(t0 + tt, vb - 1);
+                const float k = kp[t * a.sk.tok + ci], c = cb[t * tok_ae * GW + (KDA ? ci : 0)];
+                kv[x][tt] = tt < cn[x] ? k : 0.f;
+                cv[x][tt] = tt < cn[x] ? c : 1.f;
             }
         }
+        int fl = 0;
+        if (tid < NWS && va + tid * WIN < vb) fl = wfl[(int64_t)((va + tid * WIN) / WIN) * a.H_v];
         constexpr int NDE = VS * QR / BT;
         float ev[NDE], bv[NDE];
 #pragma unroll
@@ -557,7 +568,7 @@ bwd128_kernel(const BwdArgs a) {
             bv[x] = va + tr < vb ? bp[t * a.sb.tok] : 0.f;
         }
         __syncthreads();   // the previous users of the slot area are done
-        if (tid < NWS) sm.wflag[tid] = 0;
+        if (tid < NWS) sm.wflag[tid] = fl;
 #pragma unroll
         for (int x = 0; x < NDE; ++x)
             reinterpret_cast<float *>(sm.sa.det[(tid >> 5) + (BT / QR) * x])[tid & 31] = bv[x] * ev[x];
@@ -565,19 +576,16 @@ bwd128_kernel(const BwdArgs a) {
 #pragma unroll
         for (int x = 0; x < NTASK; ++x) {
             const int m = cr + CT * x;
-            float c = 1.f;
-            bool g = true;
+            float c = 1.f;   // window product: c at the last token
 #pragma unroll
             for (int tt = 0; tt < WIN; ++tt) {
-                g = g && gate_ok(cv[x][tt]);
-                c *= cv[x][tt];
-                reinterpret_cast<float *>(&sm.sa.kt[m * WIN + tt][ci & 63])[ci >> 6] = kv[x][tt] * rcp(c);
+                if (tt < cn[x]) c = cv[x][tt];
+                reinterpret_cast<float *>(&sm.sa.kt[m * WIN + tt][ci & 63])[ci >> 6] = kv[x][tt] * rcp(cv[x][tt]);
             }
             if (KDA || ci < 64) {
                 if (KDA) reinterpret_cast<float *>(&sm.sa.cend[m][ci & 63])[ci >> 6] = c;
                 else sm.sa.cend[m][ci] = make_float2(c, c);
             }
-            if (cn[x] > 0 && !(g && prod_ok(c))) atomicOr(&sm.wflag[m], 1);
         }
         __syncthreads();
     };
@@ -607,8 +615,8 @@ bwd128_kernel(const BwdArgs a) {
                 const int tr = m * WIN + tt;
                 const int64_t t = t0 + tt;
                 const float kv[2] = {kp[t * a.sk.tok + lane], kp[t * a.sk.tok + lane + 64]};
-                const float av[2] = {ab[t * tok_ae * GW + (KDA ? lane : 0)],
-                                     ab[t * tok_ae * GW + (KDA ? lane + 64 : 0)]};
+                const float av[2] = {cb[t * tok_ae * GW + (KDA ? lane : 0)],
+                                     cb[t * tok_ae * GW + (KDA ? lane + 64 : 0)]};
                 float dv[RW];
                 rows4(sm.sa.det[tr][w], dv);
 #pragma unroll
@@ -625,13 +633,13 @@ bwd128_kernel(const BwdArgs a) {
     // beta; thread tid < WIN * QR holds gy, e and beta of row tid & 31 of token tid >> 5
     float wc[2], wd[2], wk[2], wq[2], wbt = 0.f, rgy = 0.f, re = 0.f, rb = 0.f;
     int wlast = 0;   // the window's last token
-    auto load_window = [&](int t0, int cnt, bool dir) {
+    auto load_window = [&](int t0, int cnt) {
         const int64_t t = t0 + w;
         wlast = cnt - 1;
 #pragma unroll
         for (int n = 0; n < 2; ++n) {
-            wc[n] = w < cnt ? (dir ? ab : cb)[t * tok_ae * GW + (KDA ? lane + 64 * n : 0)] : 1.f;
-            wd[n] = w < cnt && !dir ? db[t * tok_ae * GW + (KDA ? lane + 64 * n : 0)] : 1.f;
+            wc[n] = w < cnt ? cb[t * tok_ae * GW + (KDA ? lane + 64 * n : 0)] : 1.f;
+            wd[n] = w < cnt ? db[t * tok_ae * GW + (KDA ? lane + 64 * n : 0)] : 1.f;
             wk[n] = w < cnt ? kp[t * a.sk.tok + lane + 64 * n] : 0.f;
             wq[n] = w < cnt ? qp[t * a.sq.tok + lane + 64 * n] : 0.f;
         }
@@ -837,8 +845,8 @@ bwd128_kernel(const BwdArgs a) {
                     }
                 } else {
                     const int64_t t = ta + tt;
-                    const float av[2] = {ab[t * tok_ae * GW + (KDA ? lane : 0)],
-                                         ab[t * tok_ae * GW + (KDA ? lane + 64 : 0)]};
+                    const float av[2] = {cb[t * tok_ae * GW + (KDA ? lane : 0)],
+                                         cb[t * tok_ae * GW + (KDA ? lane + 64 : 0)]};
 #pragma unroll
                     for (int r = 0; r < RW; ++r) {
                         M[r][0] = fmaf(M[r][0], av[0], dv[r] * kv.x);
@@ -930,8 +938,8 @@ bwd128_kernel(const BwdArgs a) {
             for (int n = 0; n < 2; ++n) X[r][n] = fmaf(dd[r], kh[n], X[r][n]);
         if constexpr (direct) {   // unscaled window: dM .* a now
             const int64_t t = ta + tt;
-            const float av[2] = {ab[t * tok_ae * GW + (KDA ? lane : 0)],
-                                 ab[t * tok_ae * GW + (KDA ? lane + 64 : 0)]};
+            const float av[2] = {cb[t * tok_ae * GW + (KDA ? lane : 0)],
+                                 cb[t * tok_ae * GW + (KDA ? lane + 64 : 0)]};
 #pragma unroll
             for (int r = 0; r < RW; ++r)
 #pragma unroll
@@ -997,7 +1005,7 @@ bwd128_kernel(const BwdArgs a) {
                 start_dg(M);
                 first = false;
             }
-            load_window(va + (nwin - 1) * WIN, vb - (va + (nwin - 1) * WIN), (flags >> (nwin - 1)) & 1);
+            load_window(va + (nwin - 1) * WIN, vb - (va + (nwin - 1) * WIN));
             for (int m = nwin - 1; m >= 0; --m) {
                 const int ta = va + m * WIN;
                 const int cnt = min(WIN, vb - ta);
@@ -1017,7 +1025,7 @@ bwd128_kernel(const BwdArgs a) {
                     if (lane < WIN) sm.D1[w][lane] = p;
                 }
                 flush_outputs();   // the previous window's results, before the prefetch
-                if (m > 0) load_window(ta - WIN, WIN, (flags >> (m - 1)) & 1);
+                if (m > 0) load_window(ta - WIN, WIN);
                 float M0[RW][2];   // state at the window start
                 switch (m) {
 #define GDN_PICK(k)                                                                    \

@@ -54,7 +54,7 @@ def expected_ws(n, T, Hk, Hv, S, C, kda=True):
     if S == 128:                    # row-quarter path
         rows = n * T * Hv
         nvs = max(1, -(-C // 64))
-        tot = al(tot + 3 * rows * (S if kda else 1) * 4)   # gates, window products
+        tot = al(tot + 2 * rows * (S if kda else 1) * 4)   # window gate factors c (or a), d
         tot = al(tot + n * (-(-T // 8)) * Hv * 4)          # window flags
         tot = al(tot + rows * S * 4)                       # prediction errors
         if nvs > 1:
