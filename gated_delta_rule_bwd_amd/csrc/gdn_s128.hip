@@ -595,7 +595,7 @@ bwd128_kernel(const BwdArgs a) {
         const int t0 = va + m * WIN;
         const int cnt = min(WIN, vb - t0);
         if (sm.wflag[m] == 0) {
-            for (int tt = 0; tt < cnt; ++tt) {
+            auto step = [&](int tt) {
                 const int tr = m * WIN + tt;
                 const float2 kv = sm.sa.kt[tr][lane];
                 float dv[RW];
@@ -605,6 +605,12 @@ bwd128_kernel(const BwdArgs a) {
                     M[r][0] = fmaf(dv[r], kv.x, M[r][0]);
                     M[r][1] = fmaf(dv[r], kv.y, M[r][1]);
                 }
+            };
+            if (cnt == WIN) {   // full window: unrolled, so all its LDS reads go out together
+#pragma unroll
+                for (int tt = 0; tt < WIN; ++tt) step(tt);
+            } else {
+                for (int tt = 0; tt < cnt; ++tt) step(tt);
             }
             const float2 ce = sm.sa.cend[m][lane];
 #pragma unroll
@@ -720,11 +726,8 @@ bwd128_kernel(const BwdArgs a) {
         }
     };
 
-    // ---- column sums of the cnt walked tokens of the window at ta: fixed-order sum over the
-    // waves, scaling, and the quarter's partial outputs; dbeta from the per-wave sums.
-    // Wave w handles token w, lane the columns (lane, lane + 64).
-    // outputs of a reduced window, stored once the next window is staged: global stores
-    // issued after the prefetch loads would otherwise be waited for together with them
+    // outputs of a reduced window, stored after the next window is staged and its successor's
+    // loads are issued, so no wait for loads ever stands behind them
     float o_dq[2] = {0.f, 0.f}, o_dk[2] = {0.f, 0.f}, o_dg[2] = {0.f, 0.f}, o_dv = 0.f, o_db = 0.f;
     int o_ta = 0, o_cnt = 0;
     auto flush_outputs = [&]() {
@@ -767,10 +770,11 @@ bwd128_kernel(const BwdArgs a) {
 #pragma unroll
                     for (int ww = 0; ww < NW; ++ww) d2 += sm.D2w[ww][tt][lane];
                 }
-                for (int sx = 0; sx < tt; ++sx) {
+#pragma unroll
+                for (int sx = 0; sx < WIN - 1; ++sx) {   // all reads issued together; tokens sx >= tt add zero
                     const float2 kc = sm.kt8[sx][lane];
-                    const float d1v = sm.D1[sx][tt];
-                    const float d2v = as_f(__builtin_amdgcn_readlane(as_i(d2), sx));
+                    const float d1v = sx < tt ? sm.D1[sx][tt] : 0.f;
+                    const float d2v = sx < tt ? as_f(__builtin_amdgcn_readlane(as_i(d2), sx)) : 0.f;
                     A.x = fmaf(kc.x, d1v, A.x); A.y = fmaf(kc.y, d1v, A.y);
                     B.x = fmaf(kc.x, d2v, B.x); B.y = fmaf(kc.y, d2v, B.y);
                 }
@@ -1012,6 +1016,7 @@ bwd128_kernel(const BwdArgs a) {
                 const bool direct = (flags >> m) & 1;
                 __syncthreads();   // the previous window (or the stretch pass) is done
                 stage_window(cnt, direct);
+                if (m > 0) load_window(ta - WIN, WIN);   // prefetch: the registers are free now
                 __syncthreads();
                 {   // delta_s . gy_t over the quarter's rows for s = w (lane: t = lane & 7, rows 4 (lane >> 3)..)
                     const int t = lane & 7, c4 = lane >> 3;
@@ -1024,8 +1029,7 @@ bwd128_kernel(const BwdArgs a) {
                     p = as_f(p32[0]) + as_f(p32[1]);
                     if (lane < WIN) sm.D1[w][lane] = p;
                 }
-                flush_outputs();   // the previous window's results, before the prefetch
-                if (m > 0) load_window(ta - WIN, WIN);
+                flush_outputs();   // the previous window's results
                 float M0[RW][2];   // state at the window start
                 switch (m) {
 #define GDN_PICK(k)                                                                    \
