@@ -1091,86 +1091,131 @@ bwd128_kernel(const BwdArgs a) {
 // order); dbeta: sum over the quarters; dg: per 8-token window, the quarters' window-start
 // value at its first token and, from its last token down, the next window's first-token value
 // (after the sequence's last token, the final-state column sums) plus the quarters' increments.
+// V columns per thread (4 when every buffer allows 16-byte accesses, else 1).
+template <int V>
+__device__ __forceinline__ void ldv(const float *p, float (&x)[V]) {
+    if constexpr (V == 4) {
+        const float4 t = *reinterpret_cast<const float4 *>(p);
+        x[0] = t.x; x[1] = t.y; x[2] = t.z; x[3] = t.w;
+    } else {
+        x[0] = *p;
+    }
+}
+template <int V>
+__device__ __forceinline__ void stv(float *p, const float (&x)[V]) {
+    if constexpr (V == 4) *reinterpret_cast<float4 *>(p) = make_float4(x[0], x[1], x[2], x[3]);
+    else *p = x[0];
+}
+
+template <int V>
 __global__ void __launch_bounds__(256) combine128_kernel(const Combine128Args a) {
     const int64_t T = a.T, n = a.n_seqs_launch, Hk = a.H_k, Hv = a.H_v;
     const int64_t G = a.kda ? S : 1;
+    const int64_t VG = a.kda ? V : 1;          // columns per dg chain item
     const int64_t nwin = (T + WIN - 1) / WIN;
-    const int64_t n_qk = n * T * Hk * S;   // dq and dk elements (each)
-    const int64_t n_g = n * nwin * Hv * G; // dg (window, column) chains
-    const int64_t n_b = n * T * Hv;        // dbeta elements
+    const int64_t n_qk = n * T * Hk * (S / V);     // dq and dk items (V columns each)
+    const int64_t n_g = n * nwin * Hv * (G / VG);   // dg (window, column group) chains
+    const int64_t n_b = n * T * Hv;                 // dbeta elements
     const int64_t NP = a.kda ? 3 : 2;
     const int64_t total = n_qk + n_g + n_b;
     const int64_t seq0 = (int64_t)a.s_base;
     for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
          idx += (int64_t)gridDim.x * blockDim.x) {
         if (idx < n_qk) {
-            const int i = (int)(idx % S);
-            int64_t rest = idx / S;
+            const int i = (int)(idx % (S / V)) * V;
+            int64_t rest = idx / (S / V);
             const int kh = (int)(rest % Hk);
             rest /= Hk;
             const int t = (int)(rest % T);
             const int sl = (int)(rest / T);
-            float q = 0.f, k = 0.f;
+            float q[V], k[V];
+#pragma unroll
+            for (int c = 0; c < V; ++c) q[c] = k[c] = 0.f;
             if (t < a.lens[sl]) {
                 for (int h = kh; h < Hv; h += (int)Hk) {   // value heads in increasing order
                     const float *pp = a.part + ((((seq0 + sl) * T + t) * Hv + h) * NQ) * NP * S + i;
 #pragma unroll
                     for (int qb = 0; qb < NQ; ++qb) {
-                        q += pp[(qb * NP + 0) * S];
-                        k += pp[(qb * NP + 1) * S];
+                        float x[V], y[V];
+                        ldv<V>(pp + (qb * NP + 0) * S, x);
+                        ldv<V>(pp + (qb * NP + 1) * S, y);
+#pragma unroll
+                        for (int c = 0; c < V; ++c) q[c] += x[c], k[c] += y[c];
                     }
                 }
             }
             const int64_t o = (((seq0 + sl) * T + t) * Hk + kh) * S + i;
-            a.dq[o] = q;
-            a.dk[o] = k;
+            stv<V>(a.dq + o, q);
+            stv<V>(a.dk + o, k);
         } else if (idx < n_qk + n_g) {
             const int64_t j = idx - n_qk;
-            const int i = (int)(j % G);
-            int64_t rest = j / G;
+            const int i = (int)(j % (G / VG)) * (int)VG;
+            int64_t rest = j / (G / VG);
             const int h = (int)(rest % Hv);
             rest /= Hv;
             const int m = (int)(rest % nwin);
             const int sl = (int)(rest / nwin);
             const int t0 = m * WIN, L = a.lens[sl];
             const int cnt = max(0, min(WIN, L - t0));
-            // sum over the quarters of the dg partial of token t
-            auto part_sum = [&](int t) {
+            // sum over the quarters of the dg partial of token t (columns i .. i + V - 1; the
+            // scalar gate: one value)
+            auto part_sum = [&](int t, float (&g)[V]) {
                 const int64_t rt = (((seq0 + sl) * T + t) * Hv + h) * NQ;
-                float g = 0.f;
+#pragma unroll
+                for (int c = 0; c < V; ++c) g[c] = 0.f;
                 if (a.kda) {
 #pragma unroll
-                    for (int qb = 0; qb < NQ; ++qb) g += a.part[((rt + qb) * NP + 2) * S + i];
+                    for (int qb = 0; qb < NQ; ++qb) {
+                        float x[V];
+                        ldv<V>(a.part + ((rt + qb) * NP + 2) * S + i, x);
+#pragma unroll
+                        for (int c = 0; c < V; ++c) g[c] += x[c];
+                    }
                 } else {
 #pragma unroll
-                    for (int x = 0; x < 2 * NQ; ++x) g += a.pgbuf[rt * 2 + x];
+                    for (int x = 0; x < 2 * NQ; ++x) g[0] += a.pgbuf[rt * 2 + x];
                 }
-                return g;
             };
-            float carry = 0.f;
+            float carry[V];
+#pragma unroll
+            for (int c = 0; c < V; ++c) carry[c] = 0.f;
             if (cnt > 0) {
                 if (t0 + WIN < L) {
-                    carry = part_sum(t0 + WIN);
+                    part_sum(t0 + WIN, carry);
                 } else {
                     const float *hf = a.hfin + ((seq0 + sl) * Hv + h) * NQ * G + i;
 #pragma unroll
-                    for (int qb = 0; qb < NQ; ++qb) carry += hf[qb * G];
+                    for (int qb = 0; qb < NQ; ++qb) {
+                        float x[V] = {};
+                        if (a.kda) ldv<V>(hf + qb * G, x);
+                        else x[0] = hf[qb * G];
+#pragma unroll
+                        for (int c = 0; c < V; ++c) carry[c] += x[c];
+                    }
                 }
             }
             for (int tt = WIN - 1; tt >= 0; --tt) {
                 const int t = t0 + tt;
                 if (t >= T) continue;
-                float g = 0.f;
+                float g[V];
+#pragma unroll
+                for (int c = 0; c < V; ++c) g[c] = 0.f;
                 if (tt < cnt) {
-                    const float p = part_sum(t);
-                    if (tt == 0) {
-                        g = p;
-                    } else {
-                        carry += p;
-                        g = carry;
+                    float p[V];
+                    part_sum(t, p);
+#pragma unroll
+                    for (int c = 0; c < V; ++c) {
+                        if (tt == 0) {
+                            g[c] = p[c];
+                        } else {
+                            carry[c] += p[c];
+                            g[c] = carry[c];
+                        }
                     }
                 }
-                a.dg[(((seq0 + sl) * T + t) * Hv + h) * G + i] = g;
+                float *dst = a.dg + (((seq0 + sl) * T + t) * Hv + h) * G + i;
+                if (a.kda) stv<V>(dst, g);
+                else dst[0] = g[0];
             }
         } else {
             const int64_t j = idx - n_qk - n_g;
@@ -1219,13 +1264,17 @@ hipError_t launch_bwd128(const BwdArgs &a, bool kda, int n_seqs_launch, hipStrea
 }
 
 hipError_t launch_combine128(const Combine128Args &a, hipStream_t st) {
+    auto a16 = [](const void *p) { return p == nullptr || ((uintptr_t)p & 15) == 0; };
+    const bool vec = a16(a.part) && a16(a.hfin) && a16(a.dq) && a16(a.dk) && a16(a.dg);
+    const int64_t V = vec ? 4 : 1, VG = a.kda ? V : 1;
     const int64_t G = a.kda ? S : 1;
     const int64_t total = (int64_t)a.n_seqs_launch *
-                          (a.T * (a.H_k * S + a.H_v) + (int64_t)((a.T + WIN - 1) / WIN) * a.H_v * G);
+                          (a.T * (a.H_k * (S / V) + a.H_v) + (int64_t)((a.T + WIN - 1) / WIN) * a.H_v * (G / VG));
     if (total <= 0) return hipSuccess;
     int64_t blocks = (total + 255) / 256;
     if (blocks > 16384) blocks = 16384;
-    return launch((const void *)combine128_kernel, a, (int)blocks, 256, st);
+    return vec ? launch((const void *)combine128_kernel<4>, a, (int)blocks, 256, st)
+               : launch((const void *)combine128_kernel<1>, a, (int)blocks, 256, st);
 }
 
 }  // namespace gdn

@@ -16,7 +16,7 @@ from .inputs import Workload, pack_qkv
 
 class DeviceCase:
     def __init__(self, w: Workload, arrays: dict, device="cuda", C=None, strided_gy=False,
-                 packed=None):
+                 packed=None, grad_offset=0):
         self.w = w
         n, T, Hk, Hv, S, G = w.n_seqs, w.T, w.H_k, w.H_v, w.S, w.G
         dev = torch.device(device)
@@ -54,7 +54,9 @@ class DeviceCase:
                                         seq_lens=list(w.lens), gy=self.gy, y=self.y)
         self.ws = torch.empty(max(B.workspace_size(self.p), 256), dtype=torch.uint8, device=dev)
         total, _ = B.grad_layout(self.p)
-        self.grad = torch.empty(max(total, 1), dtype=torch.float32, device=dev)
+        # grad_offset floats in: a packed gradient buffer that is only 4-byte aligned
+        self.grad_all = torch.empty(max(total, 1) + grad_offset, dtype=torch.float32, device=dev)
+        self.grad = self.grad_all[grad_offset:]
 
     def fwd(self, stream=None):
         B.fwd(self.p, self.q, self.k, self.v, self.g, self.beta, self.state0, self.y,

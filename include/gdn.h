@@ -121,8 +121,8 @@ size_t gdn_workspace_size(const gdn_problem *p);
 size_t gdn_grad_packed_floats(const gdn_problem *p, size_t offsets[6]);
 
 /* Forward scan: writes y (strided as p->y) and state_out, and the state snapshots into the
- * workspace.  All pointers are device pointers, 4-byte aligned.
- * Returns GDN_OK or an error code (nothing enqueued on error). */
+ * workspace.  All pointers are device pointers, 4-byte aligned; ws 16-byte aligned
+ * (GDN_ERR_ARG otherwise).  Returns GDN_OK or an error code (nothing enqueued on error). */
 int gdn_fwd(const gdn_problem *p, const float *q, const float *k, const float *v,
             const float *g, const float *beta, const float *state0, float *y,
             float *state_out, void *ws, size_t ws_bytes, gdn_stream_t stream);
@@ -132,7 +132,8 @@ int gdn_fwd(const gdn_problem *p, const float *q, const float *k, const float *v
  * into grad_packed (layout: gdn_grad_packed_floats).  With GDN_BWD_REUSE_SNAPSHOTS the
  * snapshots already in ws from gdn_fwd are used; otherwise they are recomputed first.
  * dq and dk of one key head sum its value heads in increasing h, so results are bitwise
- * reproducible run to run. */
+ * reproducible run to run.  Pointer alignment as for gdn_fwd; results do not depend on the
+ * alignment of grad_packed. */
 int gdn_bwd(const gdn_problem *p, const float *q, const float *k, const float *v,
             const float *g, const float *beta, const float *state0, const float *gy,
             const float *dstate_out, float *grad_packed, void *ws, size_t ws_bytes,

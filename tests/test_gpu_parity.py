@@ -172,8 +172,11 @@ def test_s128_bitwise_interval_reuse_and_strides(dev):
     _, c = run_case(dev, w, arrays, reuse=False, C=w.T)
     _, d = run_case(dev, w, arrays, reuse=False, C=8)
     _, e = run_case(dev, w, arrays, reuse=True, C=100, packed=False, strided_gy=True)
+    # a gradient buffer 4 bytes off a 16-byte boundary takes the one-column partial sums
+    _, f = run_case(dev, w, arrays, reuse=True, grad_offset=1)
     for n in a:
         assert np.array_equal(a[n], b[n]), ("run-to-run", n)
         assert np.array_equal(a[n], c[n]), ("C=T", n)
         assert np.array_equal(a[n], d[n]), ("C=8", n)
         assert np.array_equal(a[n], e[n]), ("C=100, contiguous, strided gy", n)
+        assert np.array_equal(a[n], f[n]), ("unaligned gradient buffer", n)
