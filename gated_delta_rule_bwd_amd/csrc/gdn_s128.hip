@@ -221,16 +221,16 @@ fwd128_kernel(const FwdArgs a) {
     // staging roles: threads 0..127 hold the k and gate values of column ci for the window's
     // tokens, threads 128..255 the q and gate values; thread tid also holds v of row srow of
     // token stt, threads 0..7 beta
+    // Global addresses are a uniform base (scalar arithmetic) plus a 32-bit per-thread offset.
     const int ci = tid & (S - 1), pci = padc(ci);
-    const bool kside = tid < S;
+    const bool kside = uni(tid) < S;   // uniform: waves 0 and 1
     const int stt = tid >> 5, srow = tid & 31;
-    const float *xp = kside ? a.k + s * a.sk.seq + hk * a.sk.head + ci
-                            : a.q + s * a.sq.seq + hk * a.sq.head + ci;
+    const float *xp = kside ? a.k + s * a.sk.seq + hk * a.sk.head : a.q + s * a.sq.seq + hk * a.sq.head;
     const int64_t xtok = kside ? a.sk.tok : a.sq.tok;
-    const float *vp = a.v + s * a.sv.seq + h * a.sv.head + qb * QR + srow;
+    const float *vp = a.v + s * a.sv.seq + h * a.sv.head + qb * QR;
     const float *bp = a.beta + s * a.sb.seq + h * a.sb.head;
     const int64_t tok_ae = a.H_v;   // token stride of cbuf / ebuf rows, in rows
-    const float *cp = a.cbuf + (s * a.T * a.H_v + h) * GW + (KDA ? ci : 0);
+    const float *cp = a.cbuf + (s * a.T * a.H_v + h) * GW;
     const int nwin_T = (a.T + WIN - 1) / WIN;
     const int32_t *wfl = a.wflag + s * nwin_T * a.H_v + h;   // window stride H_v
     float *ebase = a.ebuf + (s * a.T * a.H_v + h) * S + qb * QR;
@@ -268,20 +268,22 @@ fwd128_kernel(const FwdArgs a) {
 #pragma unroll
         for (int tt = 0; tt < WIN; ++tt) {   // clamped loads: no branch per token
             const int64_t t = t0 + min(tt, cnt - 1);
-            const float g = cp[t * tok_ae * GW], x = xp[t * xtok];
+            const float g = ldg(cp + t * tok_ae * GW, (uint32_t)(KDA ? ci : 0));
+            const float x = ldg(xp + t * xtok, (uint32_t)ci);
             av[tt] = tt < cnt ? g : 1.f;
             xv[tt] = tt < cnt ? x : 0.f;
         }
-        const int64_t tv = t0 + min(stt, cnt - 1), tb = t0 + min(tid & (WIN - 1), cnt - 1);
-        rv = vp[tv * a.sv.tok];
-        rb = bp[tb * a.sb.tok];
+        const int tv = min(stt, cnt - 1), tb = min(tid & (WIN - 1), cnt - 1);
+        rv = ldg(vp + (int64_t)t0 * a.sv.tok, (uint32_t)(tv * a.sv.tok + srow));
+        rb = ldg(bp + (int64_t)t0 * a.sb.tok, (uint32_t)(tb * a.sb.tok));
     };
     // outputs of the window at t (cnt tokens) from output buffer ob
     auto flush = [&](int t, int cnt, int ob) {
         if (stt < cnt) {
-            const int64_t tt = t + stt;
-            if (write_y) a.y[s * a.sy.seq + tt * a.sy.tok + h * a.sy.head + qb * QR + srow] = sm.ys[ob][stt][srow];
-            ebase[tt * tok_ae * S + srow] = sm.es[ob][stt][srow];
+            if (write_y)
+                stg(a.y + s * a.sy.seq + (int64_t)t * a.sy.tok + h * a.sy.head + qb * QR,
+                    (uint32_t)(stt * a.sy.tok + srow), sm.ys[ob][stt][srow]);
+            stg(ebase + (int64_t)t * tok_ae * S, (uint32_t)(stt * tok_ae * S + srow), sm.es[ob][stt][srow]);
         }
     };
 
