@@ -258,24 +258,27 @@ fwd128_kernel(const FwdArgs a) {
     // the state has arrived before the scan starts, so no wait inside the scan is charged to it
     __builtin_amdgcn_s_waitcnt(0);
 
-    // per token of the window: the gate factor (the running product c in a column-scaled
-    // window, the gate a in an unscaled one), the k or q value, v and beta; the window's flag
-    // is used only at its staging, one window later
-    float av[WIN], xv[WIN], rv = 0.f, rb = 0.f;
-    int wdir = 0;
-    auto load_window = [&](int t0, int cnt) {
-        wdir = wfl[(int64_t)(t0 / WIN) * a.H_v];
+    // Per token of a window: the gate factor (the running product c in a column-scaled window,
+    // the gate a in an unscaled one), the k or q value, v and beta, and the window's flag.  Two
+    // register sets take turns, so each window's loads are issued two windows before its
+    // staging uses them.
+    struct WinRegs {
+        float av[WIN], xv[WIN], rv, rb;
+        int wdir;
+    };
+    auto load_window = [&](WinRegs &W, int t0, int cnt) __attribute__((always_inline)) {
+        W.wdir = wfl[(int64_t)(t0 / WIN) * a.H_v];
 #pragma unroll
         for (int tt = 0; tt < WIN; ++tt) {   // clamped loads: no branch per token
             const int64_t t = t0 + min(tt, cnt - 1);
             const float g = ldg(cp + t * tok_ae * GW, (uint32_t)(KDA ? ci : 0));
             const float x = ldg(xp + t * xtok, (uint32_t)ci);
-            av[tt] = tt < cnt ? g : 1.f;
-            xv[tt] = tt < cnt ? x : 0.f;
+            W.av[tt] = tt < cnt ? g : 1.f;
+            W.xv[tt] = tt < cnt ? x : 0.f;
         }
         const int tv = min(stt, cnt - 1), tb = min(tid & (WIN - 1), cnt - 1);
-        rv = ldg(vp + (int64_t)t0 * a.sv.tok, (uint32_t)(tv * a.sv.tok + srow));
-        rb = ldg(bp + (int64_t)t0 * a.sb.tok, (uint32_t)(tb * a.sb.tok));
+        W.rv = ldg(vp + (int64_t)t0 * a.sv.tok, (uint32_t)(tv * a.sv.tok + srow));
+        W.rb = ldg(bp + (int64_t)t0 * a.sb.tok, (uint32_t)(tb * a.sb.tok));
     };
     // outputs of the window at t (cnt tokens) from output buffer ob
     auto flush = [&](int t, int cnt, int ob) {
@@ -288,9 +291,11 @@ fwd128_kernel(const FwdArgs a) {
     };
 
     float *snap = a.snap + unit * a.n_ck_max * S * S;
-    int ta = 0, prev_ta = 0, prev_cnt = 0, ob = 0;
+    int ta = 0, prev_ta = 0, prev_cnt = 0;
     int cnt = min(WIN, L);
-    if (cnt > 0) load_window(0, cnt);
+    WinRegs R0, R1;
+    if (cnt > 0) load_window(R0, 0, cnt);
+    if (min(WIN, L - cnt) > 0) load_window(R1, cnt, min(WIN, L - cnt));
     // reads of the lane's 8 columns of a padded vector
     auto ld8 = [&](const float *base, float (&x)[FC]) {
         const float4 v0 = *reinterpret_cast<const float4 *>(base);
@@ -298,7 +303,7 @@ fwd128_kernel(const FwdArgs a) {
         x[0] = v0.x; x[1] = v0.y; x[2] = v0.z; x[3] = v0.w;
         x[4] = v1.x; x[5] = v1.y; x[6] = v1.z; x[7] = v1.w;
     };
-    auto finish = [&](int tt, float (&y)[FR], const float (&e)[FR]) {
+    auto finish = [&](int tt, int ob, float (&y)[FR], const float (&e)[FR]) {
 #pragma unroll
         for (int r = 0; r < FR; ++r) y[r] = row16_sum(y[r]);
         if (lc == 0) {
@@ -306,45 +311,40 @@ fwd128_kernel(const FwdArgs a) {
             *reinterpret_cast<float2 *>(&sm.es[ob][tt][lrow]) = make_float2(e[0], e[1]);
         }
     };
-    // Per window: stage its vectors from the registers; store the previous window's outputs
-    // and the checkpoint; prefetch the next window; scan.  The stores go out before the
-    // prefetch loads, so the next staging's wait for those loads does not wait for them too.
-    while (cnt > 0) {
+    // One window from register set W: stage its vectors; store the previous window's outputs
+    // and the checkpoint; prefetch the window after the next into W; scan.  The stores go out
+    // before the prefetch loads, so a staging's wait for loads never waits for them too.
+    auto window = [&](WinRegs &W, auto par) __attribute__((always_inline)) {
+        constexpr int ob = decltype(par)::value;   // output buffer: the window's parity
         __syncthreads();   // the previous window's vectors are no longer read
-        const bool direct = wdir != 0;
+        const bool direct = W.wdir != 0;
+        // (one store target per wave, chosen up front: k rows for waves 0 and 1, q rows else)
         if (!direct) {
-            float ce = av[0];   // product over the window: c at its last token
+            float ce = W.av[0];   // product over the window: c at its last token
+            float *xc = kside ? &sm.kc[0][0] : &sm.qc[0][0];
 #pragma unroll
             for (int tt = 0; tt < WIN; ++tt) {
-                if (tt < cnt) ce = av[tt];
-                if (kside) {
-                    sm.kc[tt][pci] = xv[tt] * av[tt];
-                    sm.kr[tt][pci] = xv[tt] * rcp(av[tt]);
-                } else {
-                    sm.qc[tt][pci] = xv[tt] * av[tt];
-                }
+                if (tt < cnt) ce = W.av[tt];
+                xc[tt * SP + pci] = W.xv[tt] * W.av[tt];
+                if (kside) sm.kr[tt][pci] = W.xv[tt] * rcp(W.av[tt]);
             }
             if (kside && (KDA || ci == 0)) sm.cend[KDA ? pci : 0] = ce;
         } else {
+            float *xr = kside ? &sm.kraw[0][0] : &sm.qraw[0][0];
 #pragma unroll
             for (int tt = 0; tt < WIN; ++tt) {
-                if (kside) {
-                    sm.kraw[tt][pci] = xv[tt];
-                    if (KDA || ci == 0) sm.araw[tt][KDA ? pci : 0] = av[tt];
-                } else {
-                    sm.qraw[tt][pci] = xv[tt];
-                }
+                xr[tt * SP + pci] = W.xv[tt];
+                if (kside && (KDA || ci == 0)) sm.araw[tt][KDA ? pci : 0] = W.av[tt];
             }
         }
-        if (stt < cnt) sm.vq[stt][srow] = rv;
-        if (tid < cnt) sm.bt[tid] = rb;
+        if (stt < cnt) sm.vq[stt][srow] = W.rv;
+        if (tid < cnt) sm.bt[tid] = W.rb;
         __syncthreads();
         flush(prev_ta, prev_cnt, ob ^ 1);
         if (ta % C == 0) rw_state(snap + (int64_t)(ta / C) * S * S, true);   // checkpoint
         const int next = ta + cnt;
         const int ncnt = min(WIN, L - next);
-        if (ncnt > 0) load_window(next, ncnt);
-
+        if (ncnt > 0 && min(WIN, L - next - ncnt) > 0) load_window(W, next + ncnt, min(WIN, L - next - ncnt));
         if (!direct) {
             for (int tt = 0; tt < cnt; ++tt) {
                 float kc[FC], kr[FC], qc[FC];
@@ -372,7 +372,7 @@ fwd128_kernel(const FwdArgs a) {
 #pragma unroll
                     for (int n = 1; n < FC; ++n) y[r] = fmaf(M[r][n], qc[n], y[r]);
                 }
-                finish(tt, y, e);
+                finish(tt, ob, y, e);
             }
             float ce[FC];
             if constexpr (KDA) {
@@ -417,17 +417,21 @@ fwd128_kernel(const FwdArgs a) {
 #pragma unroll
                     for (int n = 0; n < FC; ++n) y[r] = fmaf(M[r][n], qv[n], y[r]);
                 }
-                finish(tt, y, e);
+                finish(tt, ob, y, e);
             }
         }
         prev_ta = ta;
         prev_cnt = cnt;
         ta = next;
         cnt = ncnt;
-        ob ^= 1;
+    };
+    while (cnt > 0) {
+        window(R0, std::integral_constant<int, 0>{});
+        if (cnt <= 0) break;
+        window(R1, std::integral_constant<int, 1>{});
     }
     __syncthreads();
-    flush(prev_ta, prev_cnt, ob ^ 1);
+    flush(prev_ta, prev_cnt, (L + WIN - 1) / WIN % 2 ^ 1);   // the last window's buffer
     if (write_y) {
         for (int64_t idx = tid; idx < (int64_t)(a.T - L) * QR; idx += FT) {
             const int64_t t = L + idx / QR;
