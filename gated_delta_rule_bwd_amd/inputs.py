@@ -12,8 +12,9 @@ on how much of the problem is materialised.  Draws are float64, cast to float32.
 Recipe (distributions follow the workload descriptions):
   q, k      N(0, 1), then L2-normalised per (token, head) in float64
   v         N(0, 1)
-  g         log-gate, U(g_lo, 0): one value per (token, head) for the scalar gate, S_k
-            values for the per-key-channel gate
+  g         log-gate, U(g_lo, g_hi) with g_hi = 0 (gates at most one) unless a workload
+            says otherwise: one value per (token, head) for the scalar gate, S_k values for
+            the per-key-channel gate
   beta      U(0, 1)
   state0    N(0, 0.1^2)
   gy        N(0, 1)           (output cotangent)
@@ -43,10 +44,11 @@ class Workload:
     S: int
     kda: bool
     C: int                      # checkpoint interval (0: ceil(sqrt(T)))
-    g_lo: float                 # log-gate ~ U(g_lo, 0)
+    g_lo: float                 # log-gate ~ U(g_lo, g_hi)
     seq_lens: tuple | None = None   # None: all T
     packed: bool = False        # q/k/v are row views of one [n_seqs, T, W] buffer
     seed: int = 1000
+    g_hi: float = 0.0           # upper end of the log-gate range (above 0: some gates exceed one)
 
     @property
     def S_k(self):
@@ -124,7 +126,7 @@ def _slice(w: Workload, tensor: str, s: int, head: int) -> np.ndarray:
     if tensor in ("v", "gy"):
         return r.standard_normal((T, S))
     if tensor == "g":
-        return w.g_lo + (0.0 - w.g_lo) * r.random((T, w.G))
+        return w.g_lo + (w.g_hi - w.g_lo) * r.random((T, w.G))
     if tensor == "beta":
         return r.random(T)
     if tensor == "state0":

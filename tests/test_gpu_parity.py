@@ -149,7 +149,33 @@ S128_CASES = {
     "kda_c1": I.Workload("s128_kda_c1", 1, 19, 1, 1, 128, True, 1, -0.5, seed=504),
     # one segment longer than a stretch
     "scalar_cT": I.Workload("s128_scalar_cT", 1, 129, 1, 1, 128, False, 129, -1.0, seed=505),
+    # windows processed unscaled, mixed with column-scaled ones: some gates above one ...
+    "kda_gate_above_one": I.Workload("s128_kda_up", 1, 150, 1, 2, 128, True, 64, -0.5,
+                                     seed=507, g_hi=0.00035),
+    "scalar_gate_above_one": I.Workload("s128_scalar_up", 1, 150, 1, 2, 128, False, 64, -1.0,
+                                        seed=508, g_hi=0.09),
+    # ... and window products below 2^-60
+    "kda_tiny_products": I.Workload("s128_kda_tiny", 1, 150, 1, 2, 128, True, 64, -7.0, seed=509),
+    "scalar_tiny_products": I.Workload("s128_scalar_tiny", 1, 150, 1, 2, 128, False, 200, -11.0,
+                                       seed=510),
 }
+UNSCALED = ("kda_gate_above_one", "scalar_gate_above_one", "kda_tiny_products",
+            "scalar_tiny_products")
+
+
+def unscaled_fraction(w, arrays):
+    """Share of the 8-token windows of each (sequence, value head) that hold a gate above
+    one or whose gate product falls below 2^-60 in some channel (float32, as the kernels)."""
+    a = np.exp(arrays["g"].astype(np.float32)).reshape(w.n_seqs, w.T, w.H_v, w.G)
+    hits = tot = 0
+    for s, L in enumerate(w.lens):
+        for t0 in range(0, L, 8):
+            win = a[s, t0:min(t0 + 8, L)]                      # [tokens, H_v, G]
+            prod = np.prod(win, axis=0, dtype=np.float32)      # [H_v, G]
+            bad = (win > 1).any(axis=(0, 2)) | (prod < np.float32(2.0 ** -60)).any(axis=1)
+            hits += int(bad.sum())
+            tot += bad.size
+    return hits / tot
 
 
 @pytest.mark.parametrize("name", list(S128_CASES))
@@ -157,6 +183,10 @@ def test_parity_s128(dev, name):
     w = S128_CASES[name]
     log(f"[parity] {w.name} lens={w.lens} C={w.C}")
     arrays, _ = I.make_all(w)
+    if name in UNSCALED:   # the case must mix both kinds of window
+        f = unscaled_fraction(w, arrays)
+        log(f"[parity] {w.name}: unscaled windows {f:.2f}")
+        assert 0.1 < f < 0.9, f
     _, got = run_case(dev, w, arrays, reuse=True)
     rep = check(got, oracle_results(w, arrays))
     log(f"[parity] {w.name}: " + ", ".join(f"{k} {v:.1e}" for k, v in rep.items()))
