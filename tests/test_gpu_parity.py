@@ -60,6 +60,21 @@ def test_parity_layer_shape_sampled(dev):
             ", ".join(f"{k} {v:.1e}" for k, v in rep.items()))
 
 
+def test_parity_long_context_sampled(dev):
+    """Full-size long-context workload (one 65536-token sequence, 48 value heads, interval
+    256, scalar gate); the oracle checks one key head with its three value heads over the
+    whole sequence."""
+    w = I.WORKLOADS["long_scalar_s128"]
+    log(f"[parity] {w.name} full size, sampled")
+    arrays, _ = I.make_all(w)
+    _, got = run_case(dev, w, arrays, reuse=True)
+    del arrays
+    ref, vh = oracle_sampled(w, [0], [5])
+    sub = gpu_subset(got, w, [0], [5], vh)
+    rep = check(sub, ref, REGIONS_FWD + REGIONS_BWD)
+    log(f"[parity] {w.name} seq [0] key head [5]: " + ", ".join(f"{k} {v:.1e}" for k, v in rep.items()))
+
+
 def test_single_ragged_sequence(dev):
     """A standalone 61-token sequence with an 8-token interval: partial last segment."""
     w = I.WORKLOADS["kda_ragged_s64"].replace(name="kda_t61", n_seqs=1, T=61, seq_lens=None)
