@@ -461,11 +461,14 @@ static_assert(RW == 4 && NW == WIN && WIN * QR <= BT, "backward layout");
 template <bool KDA>
 struct alignas(16) BwdLds {
     union {
-        // state before each token of the window, thread-private: st[tt][g][tid] holds rows
-        // 2g, 2g + 1 of the thread's rows at columns (lane, lane + 64).  Once a token is
-        // walked, its slot holds the thread's column sums of that token:
-        // st[tt][0] = (dq lo, dq hi, dk lo, dk hi), st[tt][1] = (dk' lo, dk' hi, dg lo, dg hi)
-        float4 st[WIN][2][BT];
+        // the thread's column sums over its rows at columns (lane, lane + 64), per walked
+        // token: cqce = (Mt^T gy lo, hi, dM^T delta lo, hi), cm = Mt^T dd; hx: the window-start
+        // dg partials (dM_out .* M0)
+        struct {
+            float4 cqce[WIN][BT];
+            float2 cm[WIN][BT];
+            float2 hx[BT];
+        } sl;
         // stretch data of the window-start pass: k./c for columns (lane, lane + 64), beta e
         // of the quarter's rows, window products
         struct {
@@ -708,7 +711,7 @@ bwd128_kernel(const BwdArgs a) {
         colsum_xm(Mf, hp);
         __syncthreads();   // the stretch data (sharing the slot area) is no longer read
         if constexpr (KDA) {
-            *reinterpret_cast<float2 *>(&sm.st[0][0][tid]) = make_float2(hp[0], hp[1]);
+            sm.sl.hx[tid] = make_float2(hp[0], hp[1]);
         } else {
             const float hs = wave_sum(hp[0] + hp[1]);
             if (lane == 0) sm.hsc[w] = hs;
@@ -719,7 +722,7 @@ bwd128_kernel(const BwdArgs a) {
             if (tid < S) {
                 float g = 0.f;
 #pragma unroll
-                for (int ww = 0; ww < NW; ++ww) g += reinterpret_cast<const float *>(&sm.st[0][0][ww * 64 + (tid & 63)])[tid >> 6];
+                for (int ww = 0; ww < NW; ++ww) g += reinterpret_cast<const float *>(&sm.sl.hx[ww * 64 + (tid & 63)])[tid >> 6];
                 hf[tid] = g;
             }
         } else {
@@ -761,12 +764,12 @@ bwd128_kernel(const BwdArgs a) {
     auto reduce_columns = [&](int ta, int cnt, bool direct) {
         const int tt = w;
         if (tt < cnt) {   // uniform over the wave
-            float4 A = sm.st[tt][0][lane];
-            float2 B = reinterpret_cast<const float2 *>(&sm.st[tt][1][0])[lane];
+            float4 A = sm.sl.cqce[tt][lane];
+            float2 B = sm.sl.cm[tt][lane];
 #pragma unroll
             for (int ww = 1; ww < NW; ++ww) {
-                const float4 x = sm.st[tt][0][ww * 64 + lane];
-                const float2 y = reinterpret_cast<const float2 *>(&sm.st[tt][1][ww * 64])[lane];
+                const float4 x = sm.sl.cqce[tt][ww * 64 + lane];
+                const float2 y = sm.sl.cm[tt][ww * 64 + lane];
                 A.x += x.x; A.y += x.y; A.z += x.z; A.w += x.w;
                 B.x += y.x; B.y += y.y;
             }
@@ -806,7 +809,7 @@ bwd128_kernel(const BwdArgs a) {
                 inc[0] = inc[1] = 0.f;
 #pragma unroll
                 for (int ww = 0; ww < NW; ++ww) {
-                    const float2 v = reinterpret_cast<const float2 *>(&sm.st[(ww + 1) & 7][1][ww * 64 + 32])[lane];
+                    const float2 v = sm.sl.hx[ww * 64 + lane];
                     inc[0] += v.x;
                     inc[1] += v.y;
                 }
@@ -833,56 +836,30 @@ bwd128_kernel(const BwdArgs a) {
         o_cnt = cnt;
     };
 
-    // replay of the window into the state slots: the state before token tt goes to st[tt]
-    auto replay_slots = [&](const float (&M0)[RW][2], int ta, auto cnt_, auto direct_tag) {
-        constexpr bool direct = decltype(direct_tag)::value;
-        const int cnt = cnt_;
-        float M[RW][2];
-#pragma unroll
-        for (int r = 0; r < RW; ++r) M[r][0] = M0[r][0], M[r][1] = M0[r][1];
-        for (int tt = 0; tt < cnt; ++tt) {
-            sm.st[tt][0][tid] = make_float4(M[0][0], M[0][1], M[1][0], M[1][1]);
-            sm.st[tt][1][tid] = make_float4(M[2][0], M[2][1], M[3][0], M[3][1]);
-            if (tt + 1 < cnt) {
-                const float2 kv = sm.kt8[tt][lane];
-                float dv[RW];
-                rows4(sm.de8[tt][w], dv);
-                if constexpr (!direct) {
-#pragma unroll
-                    for (int r = 0; r < RW; ++r) {
-                        M[r][0] = fmaf(dv[r], kv.x, M[r][0]);
-                        M[r][1] = fmaf(dv[r], kv.y, M[r][1]);
-                    }
-                } else {
-                    const int64_t t = ta + tt;
-                    const float av[2] = {cb[t * tok_ae * GW + (KDA ? lane : 0)],
-                                         cb[t * tok_ae * GW + (KDA ? lane + 64 : 0)]};
-#pragma unroll
-                    for (int r = 0; r < RW; ++r) {
-                        M[r][0] = fmaf(M[r][0], av[0], dv[r] * kv.x);
-                        M[r][1] = fmaf(M[r][1], av[1], dv[r] * kv.y);
-                    }
-                }
-            }
-        }
-    };
-
-    // one token of the reverse walk (window position tt of the window at ta): reads the
-    // replayed state from the thread's slot and leaves its column sums there
+    // one token of the reverse walk (window position tt of the window at ta); leaves the
+    // thread's column sums of the token in its slots.
     // In a column-scaled window the column sums are taken against the window-start state Mh;
     // the state before token t differs from it by sum_{s<t} delta_s (k_s./c_s)^T, whose
     // contribution the column-sum phase adds from the row products delta_s . gy_t and
-    // delta_s . dd_t.  An unscaled window walks the replayed per-token states in the slots.
+    // delta_s . dd_t.  An unscaled window (rare) replays the state before token tt from the
+    // window start, with the forward's arithmetic: M <- M .* a_s + delta_s k_s^T.
     auto walk_token = [&](int ta, int tt, const float (&Mh)[RW][2], auto direct_tag) {
         constexpr bool direct = decltype(direct_tag)::value;
         float Mt[RW][2];
-        if constexpr (direct) {
-            const float4 s0 = sm.st[tt][0][tid], s1v = sm.st[tt][1][tid];
-            Mt[0][0] = s0.x; Mt[0][1] = s0.y; Mt[1][0] = s0.z; Mt[1][1] = s0.w;
-            Mt[2][0] = s1v.x; Mt[2][1] = s1v.y; Mt[3][0] = s1v.z; Mt[3][1] = s1v.w;
-        } else {
 #pragma unroll
-            for (int r = 0; r < RW; ++r) Mt[r][0] = Mh[r][0], Mt[r][1] = Mh[r][1];
+        for (int r = 0; r < RW; ++r) Mt[r][0] = Mh[r][0], Mt[r][1] = Mh[r][1];
+        if constexpr (direct) {
+            for (int sx = 0; sx < tt; ++sx) {
+                const float4 cd = sm.pcd[sx][lane];   // the gates (unscaled window)
+                const float2 kv = sm.kt8[sx][lane];   // raw k (unscaled window)
+                float dv[RW];
+                rows4(sm.de8[sx][w], dv);
+#pragma unroll
+                for (int r = 0; r < RW; ++r) {
+                    Mt[r][0] = fmaf(Mt[r][0], cd.x, dv[r] * kv.x);
+                    Mt[r][1] = fmaf(Mt[r][1], cd.y, dv[r] * kv.y);
+                }
+            }
         }
         const float4 v4 = sm.wv[tt][lane];
         const float2 h2 = sm.wh[tt][lane];
@@ -947,18 +924,12 @@ bwd128_kernel(const BwdArgs a) {
 #pragma unroll
             for (int n = 0; n < 2; ++n) X[r][n] = fmaf(dd[r], kh[n], X[r][n]);
         if constexpr (direct) {   // unscaled window: dM .* a now
-            const int64_t t = ta + tt;
-            const float av[2] = {cb[t * tok_ae * GW + (KDA ? lane : 0)],
-                                 cb[t * tok_ae * GW + (KDA ? lane + 64 : 0)]};
+            const float4 cd = sm.pcd[tt][lane];
 #pragma unroll
-            for (int r = 0; r < RW; ++r)
-#pragma unroll
-                for (int n = 0; n < 2; ++n) X[r][n] *= av[n];
+            for (int r = 0; r < RW; ++r) X[r][0] *= cd.x, X[r][1] *= cd.y;
         }
-        sm.st[tt][0][tid] = make_float4(cq[0], cq[1], ce[0], ce[1]);
-        // Mt^T dd packed in the first half of the wave's slots of the second kind: consecutive
-        // lanes at consecutive 8 bytes (no bank conflicts); those slots' states are read above
-        reinterpret_cast<float2 *>(&sm.st[tt][1][w * 64])[lane] = make_float2(cm[0], cm[1]);
+        sm.sl.cqce[tt][tid] = make_float4(cq[0], cq[1], ce[0], ce[1]);
+        sm.sl.cm[tt][tid] = make_float2(cm[0], cm[1]);
     };
 
     const int n_ck = (L + C - 1) / C;
@@ -1053,7 +1024,6 @@ bwd128_kernel(const BwdArgs a) {
                 } else if (!direct) {
                     for (int tt = cnt - 1; tt >= 0; --tt) walk_token(ta, tt, M0, std::false_type{});
                 } else {
-                    replay_slots(M0, ta, cnt, std::true_type{});
                     for (int tt = cnt - 1; tt >= 0; --tt) walk_token(ta, tt, M0, std::true_type{});
                 }
                 if (!direct) {   // fold the window's decay into the walked gradient
@@ -1061,11 +1031,11 @@ bwd128_kernel(const BwdArgs a) {
 #pragma unroll
                     for (int r = 0; r < RW; ++r) X[r][0] *= P.x, X[r][1] *= P.y;
                 }
-                {   // window-start dg partials, packed in the second half of the wave's slots of token w + 1
+                {   // window-start dg partials
                     float hp[2];
                     colsum_xm(M0, hp);
                     if constexpr (KDA) {
-                        reinterpret_cast<float2 *>(&sm.st[(w + 1) & 7][1][w * 64 + 32])[lane] = make_float2(hp[0], hp[1]);
+                        sm.sl.hx[tid] = make_float2(hp[0], hp[1]);
                     } else {
                         const float hs = wave_sum(hp[0] + hp[1]);
                         if (lane == 0) sm.hsc[w] = hs;
