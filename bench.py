@@ -168,7 +168,8 @@ def main():
     from gated_delta_rule_bwd_amd import inputs as I
     from gated_delta_rule_bwd_amd.device import DeviceCase
 
-    w = I.WORKLOADS[args.workload or I.HEADLINE]
+    name = args.workload or I.HEADLINE
+    w = I.WORKLOADS[name] if name in I.WORKLOADS else I.EXTRA_WORKLOADS[name]
     arrays, _ = I.make_all(w)
     dc = DeviceCase(w, arrays, device="cuda:0")
     del arrays
@@ -224,7 +225,9 @@ def main():
         "pct_fp32_valu_peak": 100.0 * credited / (ms / 1e3) / PEAK_FP32_VALU,
         "fwd_ms": fwd_ms,
         "bwd_ms": bwd_ms,
-        "roofline": {"bound": "alu", "kernel": "gdn_bwd (bwd128_kernel + combine128_kernel)",
+        "roofline": {"bound": "alu",
+                     "kernel": "gdn_bwd (bwd128_kernel + combine128_kernel)" if S == 128 else
+                     "gdn_bwd (bwd_kernel" + (" + combine_kernel)" if w.H_v != w.H_k else ")"),
                      "achieved": achieved / 1e12, "peak": PEAK_FP32_VALU / 1e12,
                      "unit": "TFLOP/s", "frac": achieved / PEAK_FP32_VALU,
                      "traffic": traffic_bytes() if w.name == "layer_kda_s128" else None},

@@ -52,7 +52,7 @@ int validate(const gdn_problem *p) {
             if (p->seq_lens[s] < 0 || p->seq_lens[s] > p->T) return GDN_ERR_ARG;
     if (p->H_v % p->H_k != 0) return GDN_ERR_UNSUPPORTED;
     if (p->S_k != p->S_v) return GDN_ERR_UNSUPPORTED;
-    if (p->S_k != 32 && p->S_k != 64 && p->S_k != 128) return GDN_ERR_UNSUPPORTED;
+    if (p->S_k != 16 && p->S_k != 32 && p->S_k != 64 && p->S_k != 128) return GDN_ERR_UNSUPPORTED;
     const gdn_strides *all[] = {&p->q, &p->k, &p->v, &p->g, &p->beta, &p->gy, &p->y};
     for (auto *s : all)
         if (!strides_ok(*s)) return GDN_ERR_UNSUPPORTED;

@@ -444,6 +444,8 @@ constexpr int kThreads = Layout<S, R>::THREADS;
 hipError_t launch_fwd(const FwdArgs &a, int S, bool kda, int n_seqs_launch, hipStream_t st) {
     const int blocks = n_seqs_launch * a.H_v;
     switch (S * 2 + (kda ? 1 : 0)) {
+        case 32: return launch((const void *)fwd_kernel<16, 4, false>, a, blocks, kThreads<16, 4>, st);
+        case 33: return launch((const void *)fwd_kernel<16, 4, true>, a, blocks, kThreads<16, 4>, st);
         case 64: return launch((const void *)fwd_kernel<32, 4, false>, a, blocks, kThreads<32, 4>, st);
         case 65: return launch((const void *)fwd_kernel<32, 4, true>, a, blocks, kThreads<32, 4>, st);
         case 128: return launch((const void *)fwd_kernel<64, 4, false>, a, blocks, kThreads<64, 4>, st);
@@ -457,6 +459,8 @@ hipError_t launch_fwd(const FwdArgs &a, int S, bool kda, int n_seqs_launch, hipS
 hipError_t launch_bwd(const BwdArgs &a, int S, bool kda, int n_seqs_launch, hipStream_t st) {
     const int blocks = n_seqs_launch * a.H_v;
     switch (S * 2 + (kda ? 1 : 0)) {
+        case 32: return launch((const void *)bwd_kernel<16, 4, false>, a, blocks, kThreads<16, 4>, st);
+        case 33: return launch((const void *)bwd_kernel<16, 4, true>, a, blocks, kThreads<16, 4>, st);
         case 64: return launch((const void *)bwd_kernel<32, 4, false>, a, blocks, kThreads<32, 4>, st);
         case 65: return launch((const void *)bwd_kernel<32, 4, true>, a, blocks, kThreads<32, 4>, st);
         case 128: return launch((const void *)bwd_kernel<64, 4, false>, a, blocks, kThreads<64, 4>, st);

@@ -110,6 +110,12 @@ WORKLOADS = {
 WORKLOAD_ORDER = list(WORKLOADS)
 HEADLINE = "layer_kda_s128"
 
+# Beyond the five: head size 16 (the layer shape with 16-wide heads; packed [T, 1280] qkv).
+EXTRA_WORKLOADS = {
+    "layer_kda_s16": Workload("layer_kda_s16", 4, 4096, 16, 48, 16, True, 64, -0.3,
+                              packed=True, seed=1005),
+}
+
 
 def _rng(seed, tensor, s, head):
     return np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, _TID[tensor], s, head])))

@@ -105,7 +105,7 @@ def test_grad_layout(B):
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(S=48), -2), (dict(S=16), -2), (dict(H_k=3), -2), (dict(n_seqs=-1), -1),
+    (dict(S=48), -2), (dict(S=8), -2), (dict(H_k=3), -2), (dict(n_seqs=-1), -1),
     (dict(T=-1), -1), (dict(C=-1), -1), (dict(seq_lens=[65, 3]), -1),
     (dict(seq_lens=[-1, 3]), -1), (dict(scale=float("nan")), -1), (dict(H_k=0), -1),
 ])

@@ -75,6 +75,39 @@ def test_parity_long_context_sampled(dev):
     log(f"[parity] {w.name} seq [0] key head [5]: " + ", ".join(f"{k} {v:.1e}" for k, v in rep.items()))
 
 
+# Head size 16: one wave per unit (16 rows, one column per lane).
+S16_CASES = {
+    "kda_ragged": I.Workload("s16_kda_ragged", 2, 64, 2, 4, 16, True, 8, -0.5,
+                             seq_lens=(64, 37), seed=601),
+    "scalar_gqa_packed": I.Workload("s16_scalar_gqa", 2, 100, 2, 6, 16, False, 0, -1.0,
+                                    packed=True, seed=602),
+}
+
+
+@pytest.mark.parametrize("name", list(S16_CASES))
+@pytest.mark.parametrize("reuse", [True, False])
+def test_parity_s16(dev, name, reuse):
+    w = S16_CASES[name]
+    log(f"[parity] {w.name} reuse={reuse} lens={w.lens}")
+    arrays, _ = I.make_all(w)
+    _, got = run_case(dev, w, arrays, reuse=reuse)
+    rep = check(got, oracle_results(w, arrays), REGIONS_FWD + REGIONS_BWD)
+    log(f"[parity] {w.name}: " + ", ".join(f"{k} {v:.1e}" for k, v in rep.items()))
+
+
+def test_parity_s16_layer_sampled(dev):
+    """The layer shape with head size 16 at full size; the oracle checks two groups."""
+    w = I.EXTRA_WORKLOADS["layer_kda_s16"]
+    arrays, _ = I.make_all(w)
+    _, got = run_case(dev, w, arrays, reuse=True)
+    del arrays
+    for seqs, khs in (([1], [3]), ([2], [12])):
+        ref, vh = oracle_sampled(w, seqs, khs)
+        rep = check(gpu_subset(got, w, seqs, khs, vh), ref, REGIONS_FWD + REGIONS_BWD)
+        log(f"[parity] {w.name} seq {seqs} key heads {khs}: " +
+            ", ".join(f"{k} {v:.1e}" for k, v in rep.items()))
+
+
 def test_single_ragged_sequence(dev):
     """A standalone 61-token sequence with an 8-token interval: partial last segment."""
     w = I.WORKLOADS["kda_ragged_s64"].replace(name="kda_t61", n_seqs=1, T=61, seq_lens=None)
