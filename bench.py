@@ -3,7 +3,8 @@
 One step = gdn_fwd then gdn_bwd (reusing the forward's snapshots) over the whole workload,
 inputs already resident in HBM.  Prints one JSON line.
 
-  python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+  python bench.py [--steps K] [--warmup W] [--workload NAME] [--input-dtype f32|f16|bf16]
+                  [--no-cpu-baseline]
 
 Metric: tokens x value-heads per second, fwd+bwd, and the fraction of the FP32 vector peak
 (157.3 TFLOP/s) that the credited work reaches.  Credited work per token x head is
@@ -31,6 +32,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--input-dtype", choices=("f32", "f16", "bf16"), default="f32",
+                    help="element type of q, k, v, g, beta, gy (state and gradients stay fp32)")
     ap.add_argument("--cpu-sample-heads", type=int, default=0,
                     help="key heads of sequence 0 in the oracle sample (0: auto)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -171,7 +174,11 @@ def main():
     name = args.workload or I.HEADLINE
     w = I.WORKLOADS[name] if name in I.WORKLOADS else I.EXTRA_WORKLOADS[name]
     arrays, _ = I.make_all(w)
-    dc = DeviceCase(w, arrays, device="cuda:0")
+    in_dtype = torch.float32
+    if args.input_dtype != "f32":
+        arrays = I.round_inputs(arrays, args.input_dtype)
+        in_dtype = torch.float16 if args.input_dtype == "f16" else torch.bfloat16
+    dc = DeviceCase(w, arrays, device="cuda:0", in_dtype=in_dtype)
     del arrays
     stream = torch.cuda.current_stream()
 
@@ -217,6 +224,7 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
+        "input_dtype": args.input_dtype,
         "data": "synthetic",
         "config": {"workload": w.name, "n_seqs": w.n_seqs, "T": w.T, "H_k": w.H_k,
                    "H_v": w.H_v, "S_k": S, "S_v": S, "gate": "kda" if w.kda else "scalar",

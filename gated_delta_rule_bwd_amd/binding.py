@@ -22,6 +22,8 @@ lib = ctypes.CDLL(_LIB_PATH)
 STATUS = {0: "GDN_OK", -1: "GDN_ERR_ARG", -2: "GDN_ERR_UNSUPPORTED",
           -3: "GDN_ERR_WORKSPACE", -4: "GDN_ERR_DEVICE"}
 GATE_SCALAR, GATE_KDA = 0, 1
+DTYPE_F32, DTYPE_F16, DTYPE_BF16 = 0, 1, 2
+_DTYPES = {torch.float32: DTYPE_F32, torch.float16: DTYPE_F16, torch.bfloat16: DTYPE_BF16}
 BWD_REUSE_SNAPSHOTS = 1
 EXPORTS = ("gdn_workspace_size", "gdn_grad_packed_floats", "gdn_fwd", "gdn_bwd",
            "gdn_status_string")
@@ -43,7 +45,8 @@ class _Problem(ctypes.Structure):
                 ("H_v", ctypes.c_int32), ("S_k", ctypes.c_int32), ("S_v", ctypes.c_int32),
                 ("gate", ctypes.c_int32), ("C", ctypes.c_int32), ("scale", ctypes.c_float),
                 ("seq_lens", ctypes.POINTER(ctypes.c_int32))] + \
-               [(n, _Strides) for n in ("q", "k", "v", "g", "beta", "gy", "y")]
+               [(n, _Strides) for n in ("q", "k", "v", "g", "beta", "gy", "y")] + \
+               [("dtype", ctypes.c_int32)]
 
 
 _VP = ctypes.c_void_p
@@ -77,8 +80,10 @@ class Problem:
     """A gdn_problem: sizes, gate kind, interval, scale, lengths and the strides of the
     per-token tensors.  Use ``Problem.from_tensors``."""
 
-    def __init__(self, n_seqs, T, H_k, H_v, S, kda, C, scale, seq_lens=None, strides=None):
+    def __init__(self, n_seqs, T, H_k, H_v, S, kda, C, scale, seq_lens=None, strides=None,
+                 dtype=DTYPE_F32):
         self.n_seqs, self.T, self.H_k, self.H_v, self.S = n_seqs, T, H_k, H_v, S
+        self.dtype = int(dtype)
         self.kda, self.C, self.scale = bool(kda), int(C), float(scale)
         self.seq_lens = None if seq_lens is None else [int(x) for x in seq_lens]
         self._lens = None
@@ -97,7 +102,11 @@ class Problem:
                    "y": _tok_strides(y, "y")}
         if scale is None:
             scale = S ** -0.5
-        return cls(n, T, H_k, H_v, S, kda, C, scale, seq_lens, strides)
+        dts = {t.dtype for t in (q, k, v, g, beta, gy) if t is not None}
+        if len(dts) != 1 or next(iter(dts)) not in _DTYPES:
+            raise ValueError(f"q, k, v, g, beta, gy must share one of {list(_DTYPES)}: {dts}")
+        return cls(n, T, H_k, H_v, S, kda, C, scale, seq_lens, strides,
+                   _DTYPES[next(iter(dts))])
 
     def set_strides(self, **kw):
         for name, t in kw.items():
@@ -112,6 +121,7 @@ class Problem:
         c.gate = GATE_KDA if self.kda else GATE_SCALAR
         c.C = self.C
         c.scale = self.scale
+        c.dtype = self.dtype
         if self.seq_lens is not None:
             self._lens = (ctypes.c_int32 * max(1, len(self.seq_lens)))(*self.seq_lens)
             c.seq_lens = ctypes.cast(self._lens, ctypes.POINTER(ctypes.c_int32))

@@ -35,6 +35,8 @@ struct Plan {
     size_t off_snap = 0, off_seg = 0, off_e = 0, off_pq = 0, off_pk = 0;
     size_t off_a = 0, gate_floats = 0, off_wf = 0, off_vs = 0, off_part = 0, off_pb = 0, off_pg = 0,
            off_hf = 0;
+    // half-precision inputs: their fp32 copies, contiguous [n_seqs][T][heads][width] each
+    size_t off_in = 0, in_q = 0, in_k = 0, in_v = 0, in_g = 0, in_b = 0, in_gy = 0;
     size_t total = 0;
 };
 
@@ -46,6 +48,8 @@ int validate(const gdn_problem *p) {
         p->S_v <= 0 || p->C < 0)
         return GDN_ERR_ARG;
     if (p->gate != GDN_GATE_SCALAR && p->gate != GDN_GATE_KDA) return GDN_ERR_ARG;
+    if (p->dtype != GDN_DTYPE_F32 && p->dtype != GDN_DTYPE_F16 && p->dtype != GDN_DTYPE_BF16)
+        return GDN_ERR_ARG;
     if (!std::isfinite(p->scale)) return GDN_ERR_ARG;
     if (p->seq_lens)
         for (int s = 0; s < p->n_seqs; ++s)
@@ -71,6 +75,17 @@ Plan make_plan(const gdn_problem *p) {
     pl.G = p->gate == GDN_GATE_KDA ? p->S_k : 1;
     pl.units = (int64_t)p->n_seqs * p->H_v;
     size_t off = 0;
+    if (p->dtype != GDN_DTYPE_F32) {   // widened inputs (offsets in floats from off_in)
+        const size_t nt = (size_t)p->n_seqs * p->T;
+        pl.off_in = off;
+        pl.in_q = 0;
+        pl.in_k = pl.in_q + nt * p->H_k * S;
+        pl.in_v = pl.in_k + nt * p->H_k * S;
+        pl.in_g = pl.in_v + nt * p->H_v * S;
+        pl.in_b = pl.in_g + nt * p->H_v * pl.G;
+        pl.in_gy = pl.in_b + nt * p->H_v;
+        off = align_up(off + (pl.in_gy + nt * p->H_v * S) * sizeof(float));
+    }
     pl.off_snap = off;
     off = align_up(off + (size_t)pl.units * pl.n_ck_max * S * S * sizeof(float));
     if (pl.s128) {
@@ -119,12 +134,12 @@ struct Range {
 };
 
 Range span_tok(const void *base, const gdn_strides &s, int64_t n, int64_t T, int64_t H,
-               int64_t W) {
+               int64_t W, int64_t esize = sizeof(float)) {
     Range r;
     if (!base || n <= 0 || T <= 0 || H <= 0 || W <= 0) return r;
     const int64_t last = (n - 1) * s.seq + (T - 1) * s.tok + (H - 1) * s.head + W;
     r.lo = (uintptr_t)base;
-    r.hi = r.lo + (uintptr_t)last * sizeof(float);
+    r.hi = r.lo + (uintptr_t)(last * esize);
     return r;
 }
 
@@ -166,6 +181,11 @@ bool non_self_overlapping(const gdn_strides &s, int64_t n, int64_t T, int64_t H,
 }
 
 bool aligned4(const void *p) { return ((uintptr_t)p & 3u) == 0; }
+int64_t in_esize(const gdn_problem *p) { return p->dtype == GDN_DTYPE_F32 ? 4 : 2; }
+bool aligned_in(const gdn_problem *p, const void *x) {
+    return ((uintptr_t)x & (uintptr_t)(in_esize(p) - 1)) == 0;
+}
+gdn_strides contiguous(int64_t T, int64_t H, int64_t W) { return gdn_strides{T * H * W, H * W, W}; }
 
 void fill_lens(const gdn_problem *p, int s0, int count, int32_t *dst) {
     for (int i = 0; i < count; ++i) dst[i] = p->seq_lens ? p->seq_lens[s0 + i] : p->T;
@@ -187,6 +207,47 @@ hipError_t launch_gates(const gdn_problem *p, const Plan &pl, const float *g, vo
     ga.s_base = s0; ga.n_seqs_launch = cnt; ga.T = p->T; ga.H_v = p->H_v; ga.G = pl.G;
     fill_lens(p, s0, cnt, ga.lens);
     return gdn::launch_gate128(ga, st);
+}
+
+// Widen the given half-precision inputs into the workspace (a null source is skipped but
+// still redirected: its copy is already there) and describe the copies in pc: contiguous
+// fp32 tensors, dtype fp32.
+int widen_inputs(const gdn_problem *p, const Plan &pl, void *ws, const void *q, const void *k,
+                 const void *v, const void *g, const void *beta, const void *gy, hipStream_t st,
+                 gdn_problem &pc, const float *&qf, const float *&kf, const float *&vf,
+                 const float *&gf, const float *&bf, const float **gyf) {
+    float *base = (float *)((char *)ws + pl.off_in);
+    const int64_t n = p->n_seqs, T = p->T, S = p->S_v;
+    struct Job {
+        const void *src;
+        const gdn_strides *st;
+        size_t off;
+        int64_t H, W;
+        gdn_strides *dst_st;
+        const float **dst;
+    } jobs[] = {{q, &p->q, pl.in_q, p->H_k, S, &pc.q, &qf},
+                {k, &p->k, pl.in_k, p->H_k, S, &pc.k, &kf},
+                {v, &p->v, pl.in_v, p->H_v, S, &pc.v, &vf},
+                {g, &p->g, pl.in_g, p->H_v, pl.G, &pc.g, &gf},
+                {beta, &p->beta, pl.in_b, p->H_v, 1, &pc.beta, &bf},
+                {gy, &p->gy, pl.in_gy, p->H_v, S, &pc.gy, gyf}};
+    for (auto &j : jobs) {
+        if (!j.dst) continue;   // gy of the forward
+        if (j.src) {
+            gdn::WidenArgs w;
+            w.src = (const uint16_t *)j.src;
+            w.st = *j.st;
+            w.dst = base + j.off;
+            w.n = n; w.T = T; w.H = j.H; w.W = j.W;
+            w.bf16 = p->dtype == GDN_DTYPE_BF16;
+            const int rc = device_status(gdn::launch_widen(w, st));
+            if (rc != GDN_OK) return rc;
+        }
+        *j.dst_st = contiguous(T, j.H, j.W);
+        *j.dst = base + j.off;
+    }
+    pc.dtype = GDN_DTYPE_F32;
+    return GDN_OK;
 }
 
 }  // namespace
@@ -223,24 +284,28 @@ size_t gdn_grad_packed_floats(const gdn_problem *p, size_t offsets[6]) {
     return off;
 }
 
-int gdn_fwd(const gdn_problem *p, const float *q, const float *k, const float *v,
-            const float *g, const float *beta, const float *state0, float *y,
+int gdn_fwd(const gdn_problem *p, const void *q_in, const void *k_in, const void *v_in,
+            const void *g_in, const void *beta_in, const float *state0, float *y,
             float *state_out, void *ws, size_t ws_bytes, gdn_stream_t stream) {
     int rc = validate(p);
     if (rc != GDN_OK) return rc;
     const Plan pl = make_plan(p);
     const int64_t n = p->n_seqs, T = p->T, Hk = p->H_k, Hv = p->H_v, S = p->S_v;
-    if (!q || !k || !v || !g || !beta || !state0 || !y || !state_out) return GDN_ERR_ARG;
-    const void *ptrs[] = {q, k, v, g, beta, state0, y, state_out};
+    if (!q_in || !k_in || !v_in || !g_in || !beta_in || !state0 || !y || !state_out) return GDN_ERR_ARG;
+    const void *ins[] = {q_in, k_in, v_in, g_in, beta_in};
+    for (auto *x : ins)
+        if (!aligned_in(p, x)) return GDN_ERR_UNSUPPORTED;
+    const void *ptrs[] = {state0, y, state_out};
     for (auto *x : ptrs)
         if (!aligned4(x)) return GDN_ERR_UNSUPPORTED;
     if (ws_bytes < pl.total) return GDN_ERR_WORKSPACE;
     if (!ws || ((uintptr_t)ws % 16) != 0) return GDN_ERR_ARG;
     if (!non_self_overlapping(p->y, n, T, Hv, S)) return GDN_ERR_ARG;
 
-    const Range in[] = {span_tok(q, p->q, n, T, Hk, S), span_tok(k, p->k, n, T, Hk, S),
-                        span_tok(v, p->v, n, T, Hv, S), span_tok(g, p->g, n, T, Hv, pl.G),
-                        span_tok(beta, p->beta, n, T, Hv, 1), span_flat(state0, n * Hv * S * S)};
+    const int64_t es = in_esize(p);
+    const Range in[] = {span_tok(q_in, p->q, n, T, Hk, S, es), span_tok(k_in, p->k, n, T, Hk, S, es),
+                        span_tok(v_in, p->v, n, T, Hv, S, es), span_tok(g_in, p->g, n, T, Hv, pl.G, es),
+                        span_tok(beta_in, p->beta, n, T, Hv, 1, es), span_flat(state0, n * Hv * S * S)};
     const Range out[] = {span_tok(y, p->y, n, T, Hv, S), span_flat(state_out, n * Hv * S * S),
                          span_bytes(ws, pl.total)};
     for (auto &o : out)
@@ -249,6 +314,17 @@ int gdn_fwd(const gdn_problem *p, const float *q, const float *k, const float *v
     for (int i = 0; i < 3; ++i)
         for (int j = i + 1; j < 3; ++j)
             if (overlap(out[i], out[j])) return GDN_ERR_ARG;
+
+    // half-precision inputs: widened into the workspace, then the fp32 path on the copies
+    gdn_problem pc = *p;
+    const float *q = (const float *)q_in, *k = (const float *)k_in, *v = (const float *)v_in;
+    const float *g = (const float *)g_in, *beta = (const float *)beta_in;
+    if (p->dtype != GDN_DTYPE_F32) {
+        rc = widen_inputs(p, pl, ws, q_in, k_in, v_in, g_in, beta_in, nullptr, (hipStream_t)stream, pc,
+                          q, k, v, g, beta, nullptr);
+        if (rc != GDN_OK) return rc;
+    }
+    p = &pc;
 
     gdn::FwdArgs a;
     std::memset(&a, 0, sizeof(a));
@@ -278,8 +354,8 @@ int gdn_fwd(const gdn_problem *p, const float *q, const float *k, const float *v
     return GDN_OK;
 }
 
-int gdn_bwd(const gdn_problem *p, const float *q, const float *k, const float *v,
-            const float *g, const float *beta, const float *state0, const float *gy,
+int gdn_bwd(const gdn_problem *p, const void *q_in, const void *k_in, const void *v_in,
+            const void *g_in, const void *beta_in, const float *state0, const void *gy_in,
             const float *dstate_out, float *grad_packed, void *ws, size_t ws_bytes,
             unsigned flags, gdn_stream_t stream) {
     int rc = validate(p);
@@ -287,8 +363,12 @@ int gdn_bwd(const gdn_problem *p, const float *q, const float *k, const float *v
     if (flags & ~GDN_BWD_REUSE_SNAPSHOTS) return GDN_ERR_ARG;
     const Plan pl = make_plan(p);
     const int64_t n = p->n_seqs, T = p->T, Hk = p->H_k, Hv = p->H_v, S = p->S_v;
-    if (!q || !k || !v || !g || !beta || !state0 || !gy || !grad_packed) return GDN_ERR_ARG;
-    const void *ptrs[] = {q, k, v, g, beta, state0, gy, dstate_out, grad_packed};
+    if (!q_in || !k_in || !v_in || !g_in || !beta_in || !state0 || !gy_in || !grad_packed)
+        return GDN_ERR_ARG;
+    const void *ins[] = {q_in, k_in, v_in, g_in, beta_in, gy_in};
+    for (auto *x : ins)
+        if (!aligned_in(p, x)) return GDN_ERR_UNSUPPORTED;
+    const void *ptrs[] = {state0, dstate_out, grad_packed};
     for (auto *x : ptrs)
         if (x && !aligned4(x)) return GDN_ERR_UNSUPPORTED;
     if (ws_bytes < pl.total) return GDN_ERR_WORKSPACE;
@@ -296,15 +376,30 @@ int gdn_bwd(const gdn_problem *p, const float *q, const float *k, const float *v
 
     size_t off[6];
     const size_t total = gdn_grad_packed_floats(p, off);
-    const Range in[] = {span_tok(q, p->q, n, T, Hk, S),      span_tok(k, p->k, n, T, Hk, S),
-                        span_tok(v, p->v, n, T, Hv, S),      span_tok(g, p->g, n, T, Hv, pl.G),
-                        span_tok(beta, p->beta, n, T, Hv, 1), span_flat(state0, n * Hv * S * S),
-                        span_tok(gy, p->gy, n, T, Hv, S),    span_flat(dstate_out, n * Hv * S * S)};
+    const int64_t es = in_esize(p);
+    const Range in[] = {span_tok(q_in, p->q, n, T, Hk, S, es),      span_tok(k_in, p->k, n, T, Hk, S, es),
+                        span_tok(v_in, p->v, n, T, Hv, S, es),      span_tok(g_in, p->g, n, T, Hv, pl.G, es),
+                        span_tok(beta_in, p->beta, n, T, Hv, 1, es), span_flat(state0, n * Hv * S * S),
+                        span_tok(gy_in, p->gy, n, T, Hv, S, es),    span_flat(dstate_out, n * Hv * S * S)};
     const Range outg = span_flat(grad_packed, (int64_t)total);
     const Range wsr = span_bytes(ws, pl.total);
     for (auto &i : in)
         if (overlap(outg, i) || overlap(wsr, i)) return GDN_ERR_ARG;
     if (overlap(outg, wsr)) return GDN_ERR_ARG;
+
+    // half-precision inputs: gy widened into the workspace, and q, k, v, g, beta too unless the
+    // forward on the same inputs left their copies there (GDN_BWD_REUSE_SNAPSHOTS)
+    gdn_problem pc = *p;
+    const float *q = (const float *)q_in, *k = (const float *)k_in, *v = (const float *)v_in;
+    const float *g = (const float *)g_in, *beta = (const float *)beta_in, *gy = (const float *)gy_in;
+    if (p->dtype != GDN_DTYPE_F32) {
+        const bool reuse = flags & GDN_BWD_REUSE_SNAPSHOTS;
+        rc = widen_inputs(p, pl, ws, reuse ? nullptr : q_in, reuse ? nullptr : k_in,
+                          reuse ? nullptr : v_in, reuse ? nullptr : g_in, reuse ? nullptr : beta_in,
+                          gy_in, (hipStream_t)stream, pc, q, k, v, g, beta, &gy);
+        if (rc != GDN_OK) return rc;
+    }
+    p = &pc;
 
     float *dq = grad_packed + off[0], *dk = grad_packed + off[1], *dv = grad_packed + off[2];
     float *dg = grad_packed + off[3], *dbeta = grad_packed + off[4], *dstate = grad_packed + off[5];

@@ -85,6 +85,17 @@ struct CombineArgs {
     int32_t n_seqs, T, H_k, H_v, S;
 };
 
+// Exact widening of a strided half-precision per-token tensor [n][T][H][W] (IEEE binary16,
+// or bfloat16 when bf16 != 0) into a contiguous fp32 copy.
+struct WidenArgs {
+    const uint16_t *src;
+    gdn_strides st;
+    float *dst;
+    int64_t n, T, H, W;
+    int32_t bf16;
+};
+
+hipError_t launch_widen(const WidenArgs &a, hipStream_t st);
 hipError_t launch_fwd(const FwdArgs &a, int S, bool kda, int n_seqs_launch, hipStream_t st);
 hipError_t launch_bwd(const BwdArgs &a, int S, bool kda, int n_seqs_launch, hipStream_t st);
 hipError_t launch_combine(const CombineArgs &a, hipStream_t st);

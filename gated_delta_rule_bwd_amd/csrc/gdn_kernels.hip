@@ -429,6 +429,45 @@ __global__ void __launch_bounds__(256) combine_kernel(const CombineArgs a) {
     }
 }
 
+// ------------------------------------------------------------------ half-precision inputs
+
+// dst[s][t][h][i] = src(s, t, h, i) widened to fp32 (exact for both half formats).  A thread
+// handles 8 consecutive elements of one row: one 16-byte load and two 16-byte stores when
+// VEC (the host checked that every row start is 16-byte aligned and W is a multiple of 8).
+__device__ __forceinline__ float widen1(uint16_t b, bool bf16) {
+    return bf16 ? __builtin_bit_cast(float, (uint32_t)b << 16) : (float)__builtin_bit_cast(_Float16, b);
+}
+
+template <bool VEC>
+__global__ void __launch_bounds__(256) widen_kernel(const WidenArgs a) {
+    const int64_t chunks = (a.W + 7) / 8;
+    const int64_t total = a.n * a.T * a.H * chunks;
+    const bool bf16 = a.bf16 != 0;
+    for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+         idx += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t c = idx % chunks, row = idx / chunks;
+        const int64_t h = row % a.H, st = row / a.H;
+        const int64_t t = st % a.T, s = st / a.T;
+        const uint16_t *src = a.src + s * a.st.seq + t * a.st.tok + h * a.st.head + c * 8;
+        float *dst = a.dst + row * a.W + c * 8;
+        if constexpr (VEC) {
+            const uint4 v = *reinterpret_cast<const uint4 *>(src);
+            const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+            float f[8];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                f[2 * j] = widen1((uint16_t)(w4[j] & 0xFFFFu), bf16);
+                f[2 * j + 1] = widen1((uint16_t)(w4[j] >> 16), bf16);
+            }
+            reinterpret_cast<float4 *>(dst)[0] = make_float4(f[0], f[1], f[2], f[3]);
+            reinterpret_cast<float4 *>(dst)[1] = make_float4(f[4], f[5], f[6], f[7]);
+        } else {
+            const int m = (int)min<int64_t>(8, a.W - c * 8);
+            for (int j = 0; j < m; ++j) dst[j] = widen1(src[j], bf16);
+        }
+    }
+}
+
 template <typename Args>
 hipError_t launch(const void *fn, const Args &args, int blocks, int threads, hipStream_t st) {
     if (blocks <= 0) return hipSuccess;
@@ -469,6 +508,18 @@ hipError_t launch_bwd(const BwdArgs &a, int S, bool kda, int n_seqs_launch, hipS
         case 257: return launch((const void *)bwd_kernel<128, 4, true>, a, blocks, kThreads<128, 4>, st);
     }
     return hipErrorInvalidValue;
+}
+
+hipError_t launch_widen(const WidenArgs &a, hipStream_t st) {
+    const int64_t total = a.n * a.T * a.H * ((a.W + 7) / 8);
+    if (total <= 0) return hipSuccess;
+    int64_t blocks = (total + 255) / 256;
+    if (blocks > 16384) blocks = 16384;
+    // 16-byte vectors when every row start is 16-byte aligned (the fp32 rows then are too)
+    const bool vec = a.W % 8 == 0 && ((uintptr_t)a.src & 15) == 0 && a.st.seq % 8 == 0 &&
+                     a.st.tok % 8 == 0 && a.st.head % 8 == 0 && ((uintptr_t)a.dst & 15) == 0;
+    return vec ? launch((const void *)widen_kernel<true>, a, (int)blocks, 256, st)
+               : launch((const void *)widen_kernel<false>, a, (int)blocks, 256, st);
 }
 
 hipError_t launch_combine(const CombineArgs &a, hipStream_t st) {

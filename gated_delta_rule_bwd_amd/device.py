@@ -16,7 +16,7 @@ from .inputs import Workload, pack_qkv
 
 class DeviceCase:
     def __init__(self, w: Workload, arrays: dict, device="cuda", C=None, strided_gy=False,
-                 packed=None, grad_offset=0):
+                 packed=None, grad_offset=0, in_dtype=torch.float32):
         self.w = w
         n, T, Hk, Hv, S, G = w.n_seqs, w.T, w.H_k, w.H_v, w.S, w.G
         dev = torch.device(device)
@@ -25,8 +25,11 @@ class DeviceCase:
         def put(a):
             return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
+        def put_in(a):   # q, k, v, g, beta, gy in the input element type (values must fit it)
+            return put(a).to(in_dtype)
+
         if packed:
-            self.qkv = put(pack_qkv(w, arrays["q"], arrays["k"], arrays["v"]))
+            self.qkv = put_in(pack_qkv(w, arrays["q"], arrays["k"], arrays["v"]))
             W = w.packed_width
             HkS = Hk * S
             self.q = self.qkv[:, :, :HkS].unflatten(2, (Hk, S))
@@ -35,17 +38,17 @@ class DeviceCase:
             assert self.q.stride() == (T * W, W, S, 1)
         else:
             self.qkv = None
-            self.q, self.k, self.v = put(arrays["q"]), put(arrays["k"]), put(arrays["v"])
-        self.g = put(arrays["g"].reshape(n, T, Hv, G))
-        self.beta = put(arrays["beta"])
+            self.q, self.k, self.v = put_in(arrays["q"]), put_in(arrays["k"]), put_in(arrays["v"])
+        self.g = put_in(arrays["g"].reshape(n, T, Hv, G))
+        self.beta = put_in(arrays["beta"])
         self.state0 = put(arrays["state0"])
         if strided_gy:
             # gy as a view with head-major order and a padded token stride
-            base = torch.zeros((n, Hv, T, S + 8), dtype=torch.float32, device=dev)
+            base = torch.zeros((n, Hv, T, S + 8), dtype=in_dtype, device=dev)
             self.gy = base[..., :S].permute(0, 2, 1, 3)
-            self.gy.copy_(put(arrays["gy"]))
+            self.gy.copy_(put_in(arrays["gy"]))
         else:
-            self.gy = put(arrays["gy"])
+            self.gy = put_in(arrays["gy"])
         self.dstate_out = put(arrays["dstate_out"]) if arrays.get("dstate_out") is not None else None
         self.y = torch.empty((n, T, Hv, S), dtype=torch.float32, device=dev)
         self.state_out = torch.empty((n, Hv, S, S), dtype=torch.float32, device=dev)

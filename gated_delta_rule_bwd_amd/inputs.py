@@ -201,6 +201,27 @@ def sub_workload(w: Workload, seqs, key_heads) -> Workload:
                      H_v=len(key_heads) * r, seq_lens=tuple(lens))
 
 
+HALF_INPUTS = ("q", "k", "v", "g", "beta", "gy")
+
+
+def round_inputs(arrays: dict, kind: str) -> dict:
+    """The arrays with q, k, v, g, beta, gy rounded to the nearest "f16" or "bf16" value
+    (ties to even), still stored as float32: the values a half-precision run receives, so the
+    oracle and the device see the same numbers."""
+    out = dict(arrays)
+    for n in HALF_INPUTS:
+        x = np.ascontiguousarray(arrays[n], dtype=np.float32)
+        if kind == "f16":
+            out[n] = x.astype(np.float16).astype(np.float32)
+        elif kind == "bf16":
+            u = x.view(np.uint32).astype(np.uint64)
+            u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
+            out[n] = u.astype(np.uint32).view(np.float32)
+        else:
+            raise ValueError(kind)
+    return out
+
+
 def pack_qkv(w: Workload, q, k, v) -> np.ndarray:
     """Place q, k, v as row views of one [n, T, W] buffer: q at columns [0, H_k S),
     k at [H_k S, 2 H_k S), v at [2 H_k S, W); head h at offset h S within its block."""

@@ -61,6 +61,15 @@ extern "C" {
 #define GDN_GATE_SCALAR 0
 #define GDN_GATE_KDA 1
 
+/* Element type of the inputs q, k, v, g, beta and gy (gdn_problem.dtype).  The state, y and
+ * every gradient are fp32 (the contract of "Training kernels and gradients", introduction:
+ * half-precision inputs, fp32 gradient storage).  Half-precision inputs are widened exactly
+ * to fp32 in the workspace before the fp32 kernels run, so the results equal those of fp32
+ * inputs holding the same values. */
+#define GDN_DTYPE_F32 0
+#define GDN_DTYPE_F16 1
+#define GDN_DTYPE_BF16 2
+
 /* gdn_bwd flags. */
 #define GDN_BWD_REUSE_SNAPSHOTS 1u /* ws holds the snapshots written by gdn_fwd on the same
                                       problem and inputs: skip the checkpoint pass */
@@ -97,6 +106,8 @@ typedef struct gdn_strides {
  *   beta        strides of beta   (H_v, width 1)
  *   gy          strides of the output cotangent (H_v, S_v); used by gdn_bwd only
  *   y           strides of the output y (H_v, S_v); used by gdn_fwd only
+ *   dtype       GDN_DTYPE_* of q, k, v, g, beta, gy (strides count elements of that type);
+ *               0 (fp32) in a zero-initialised struct
  * State tensors (state0, state_out, dstate_out, dstate) are contiguous
  * [n_seqs][H_v][S_v][S_k] in the M = S^T orientation (row = value index). */
 typedef struct gdn_problem {
@@ -104,6 +115,7 @@ typedef struct gdn_problem {
     float scale;
     const int32_t *seq_lens;
     gdn_strides q, k, v, g, beta, gy, y;
+    int32_t dtype;
 } gdn_problem;
 
 /* Bytes of device workspace that gdn_fwd and gdn_bwd need for this problem (0 on an
@@ -121,10 +133,12 @@ size_t gdn_workspace_size(const gdn_problem *p);
 size_t gdn_grad_packed_floats(const gdn_problem *p, size_t offsets[6]);
 
 /* Forward scan: writes y (strided as p->y) and state_out, and the state snapshots into the
- * workspace.  All pointers are device pointers, 4-byte aligned; ws 16-byte aligned
- * (GDN_ERR_ARG otherwise).  Returns GDN_OK or an error code (nothing enqueued on error). */
-int gdn_fwd(const gdn_problem *p, const float *q, const float *k, const float *v,
-            const float *g, const float *beta, const float *state0, float *y,
+ * workspace.  All pointers are device pointers; q, k, v, g, beta (and gy) hold p->dtype
+ * elements and are aligned to that element size, every other buffer is 4-byte aligned, ws
+ * 16-byte aligned (GDN_ERR_UNSUPPORTED / GDN_ERR_ARG otherwise).  Returns GDN_OK or an error
+ * code (nothing enqueued on error). */
+int gdn_fwd(const gdn_problem *p, const void *q, const void *k, const void *v,
+            const void *g, const void *beta, const float *state0, float *y,
             float *state_out, void *ws, size_t ws_bytes, gdn_stream_t stream);
 
 /* Backward: given the forward's inputs, the output cotangent gy (strided as p->gy) and
@@ -134,8 +148,8 @@ int gdn_fwd(const gdn_problem *p, const float *q, const float *k, const float *v
  * dq and dk of one key head sum its value heads in increasing h, so results are bitwise
  * reproducible run to run.  Pointer alignment as for gdn_fwd; results do not depend on the
  * alignment of grad_packed. */
-int gdn_bwd(const gdn_problem *p, const float *q, const float *k, const float *v,
-            const float *g, const float *beta, const float *state0, const float *gy,
+int gdn_bwd(const gdn_problem *p, const void *q, const void *k, const void *v,
+            const void *g, const void *beta, const float *state0, const void *gy,
             const float *dstate_out, float *grad_packed, void *ws, size_t ws_bytes,
             unsigned flags, gdn_stream_t stream);
 

@@ -32,7 +32,7 @@ def test_exports_every_declared_symbol(B):
 
 def problem(B, strides=None, **kw):
     d = dict(n_seqs=2, T=64, H_k=4, H_v=8, S=64, kda=True, C=8, scale=0.125,
-             seq_lens=[64, 61])
+             seq_lens=[64, 61], dtype=0)
     d.update(kw)
     override = strides or {}
     strides = {"q": (64 * 4 * 64, 4 * 64, 64), "k": (64 * 4 * 64, 4 * 64, 64),
@@ -41,7 +41,7 @@ def problem(B, strides=None, **kw):
                "y": (64 * 8 * 64, 8 * 64, 64)}
     strides.update(override)
     return B.Problem(d["n_seqs"], d["T"], d["H_k"], d["H_v"], d["S"], d["kda"], d["C"],
-                     d["scale"], d["seq_lens"], strides)
+                     d["scale"], d["seq_lens"], strides, d["dtype"])
 
 
 def expected_ws(n, T, Hk, Hv, S, C, kda=True):
@@ -108,6 +108,7 @@ def test_grad_layout(B):
     (dict(S=48), -2), (dict(S=8), -2), (dict(H_k=3), -2), (dict(n_seqs=-1), -1),
     (dict(T=-1), -1), (dict(C=-1), -1), (dict(seq_lens=[65, 3]), -1),
     (dict(seq_lens=[-1, 3]), -1), (dict(scale=float("nan")), -1), (dict(H_k=0), -1),
+    (dict(dtype=3), -1), (dict(dtype=-1), -1),
 ])
 def test_invalid_problems(B, kw, code):
     p = problem(B, **kw)
@@ -182,6 +183,35 @@ def test_bwd_argument_errors(B):
     ov = list(good)
     ov[9] = good[0]                           # workspace overlapping q
     assert _bwd(B, p, ov, ws) == -1
+
+
+def test_half_inputs_workspace_and_alignment(B):
+    """fp16/bf16 inputs: the workspace gains their fp32 copies; input pointers need only
+    2-byte alignment (the other buffers still 4)."""
+    al = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    n, T, Hk, Hv, S = 2, 64, 4, 8, 64
+    for kda in (True, False):
+        for dt in (1, 2):
+            G = S if kda else 1
+            widened = (2 * n * T * Hk * S + 2 * n * T * Hv * S + n * T * Hv * G + n * T * Hv) * 4
+            ph = problem(B, dtype=dt, kda=kda)
+            assert B.workspace_size(ph) == al(widened) + expected_ws(n, T, Hk, Hv, S, 8, kda=kda)
+    ph = problem(B, dtype=2)
+    ws = B.workspace_size(ph)
+    a = layout_ptrs(ph, B)
+    good = [a[x] for x in ("q", "k", "v", "g", "beta", "state0", "y", "state_out", "ws")]
+    odd = list(good)
+    odd[0] += 1                               # q not 2-byte aligned
+    assert _fwd(B, ph, odd, ws) == -2
+    two = list(good)
+    two[0] += 2                               # q 2-byte aligned: accepted, then ws too small
+    assert _fwd(B, ph, two, ws - 1) == -3
+    st = list(good)
+    st[5] += 2                                # state0 stays fp32: 4-byte alignment
+    assert _fwd(B, ph, st, ws) == -2
+    gb = [a[x] for x in ("q", "k", "v", "g", "beta", "state0", "gy", "dso", "grad", "ws")]
+    gb[6] += 1                                # gy not 2-byte aligned
+    assert _bwd(B, ph, gb, ws) == -2
 
 
 def test_status_strings(B):

@@ -108,6 +108,38 @@ def test_parity_s16_layer_sampled(dev):
             ", ".join(f"{k} {v:.1e}" for k, v in rep.items()))
 
 
+# Half-precision inputs (q, k, v, g, beta, gy in fp16 or bf16; state and gradients fp32).
+HALF_CASES = {
+    "bf16_s128_kda": ("bf16", I.Workload("h_s128_kda", 2, 150, 2, 4, 128, True, 64, -0.3,
+                                         seq_lens=(150, 77), packed=True, seed=701)),
+    "f16_s128_scalar": ("f16", I.Workload("h_s128_scalar", 1, 140, 1, 3, 128, False, 0, -0.5,
+                                          seed=702)),
+    "bf16_s32_gqa": ("bf16", I.Workload("h_s32_gqa", 2, 100, 4, 8, 32, False, 0, -1.0,
+                                        packed=True, seed=703)),
+    "f16_s64_kda": ("f16", I.Workload("h_s64_kda", 2, 64, 2, 2, 64, True, 8, -0.5,
+                                      seq_lens=(64, 41), seed=704)),
+}
+TORCH_HALF = {"f16": torch.float16, "bf16": torch.bfloat16}
+
+
+@pytest.mark.parametrize("name", list(HALF_CASES))
+def test_parity_half_inputs(dev, name):
+    """Against the oracle on the rounded values, and bitwise equal to the fp32 run on the
+    same values (the widening is exact), with the snapshots reused and recomputed and with a
+    strided gy."""
+    kind, w = HALF_CASES[name]
+    log(f"[parity] {w.name} {kind} lens={w.lens}")
+    arrays = I.round_inputs(I.make_all(w)[0], kind)
+    _, got = run_case(dev, w, arrays, reuse=True, in_dtype=TORCH_HALF[kind])
+    rep = check(got, oracle_results(w, arrays), REGIONS_FWD + REGIONS_BWD)
+    log(f"[parity] {w.name} {kind}: " + ", ".join(f"{k} {v:.1e}" for k, v in rep.items()))
+    _, f32 = run_case(dev, w, arrays, reuse=True)
+    _, rec = run_case(dev, w, arrays, reuse=False, in_dtype=TORCH_HALF[kind], strided_gy=True)
+    for n in got:
+        assert np.array_equal(got[n], f32[n]), ("half vs fp32 inputs", n)
+        assert np.array_equal(got[n], rec[n]), ("recomputed, strided gy", n)
+
+
 def test_single_ragged_sequence(dev):
     """A standalone 61-token sequence with an 8-token interval: partial last segment."""
     w = I.WORKLOADS["kda_ragged_s64"].replace(name="kda_t61", n_seqs=1, T=61, seq_lens=None)
