@@ -207,10 +207,11 @@ def main():
     ms = total_ms / args.steps
 
     S = w.S
+    S2 = w.S_k * w.S_v                 # state elements (S^2 for square heads)
     th = w.tokens_heads
     value = th / (ms / 1e3)
-    credited = 28 * S * S * th
-    bwd_flops = 21 * S * S * th        # segment replay 5 S^2 + reverse walk 16 S^2
+    credited = 28 * S2 * th
+    bwd_flops = 21 * S2 * th           # segment replay 5 S^2 + reverse walk 16 S^2
     achieved = bwd_flops / (bwd_ms / 1e3)
     out = {
         "metric": METRIC,
@@ -227,14 +228,14 @@ def main():
         "input_dtype": args.input_dtype,
         "data": "synthetic",
         "config": {"workload": w.name, "n_seqs": w.n_seqs, "T": w.T, "H_k": w.H_k,
-                   "H_v": w.H_v, "S_k": S, "S_v": S, "gate": "kda" if w.kda else "scalar",
+                   "H_v": w.H_v, "S_k": w.S_k, "S_v": w.S_v, "gate": "kda" if w.kda else "scalar",
                    "C": w.C, "layout": "q/k/v row views of a packed buffer" if w.packed
                    else "contiguous", "tokens_heads": th},
         "pct_fp32_valu_peak": 100.0 * credited / (ms / 1e3) / PEAK_FP32_VALU,
         "fwd_ms": fwd_ms,
         "bwd_ms": bwd_ms,
         "roofline": {"bound": "alu",
-                     "kernel": "gdn_bwd (bwd128_kernel + combine128_kernel)" if S == 128 else
+                     "kernel": "gdn_bwd (bwd128_kernel + combine128_kernel)" if S2 == 128 * 128 else
                      "gdn_bwd (bwd_kernel" + (" + combine_kernel)" if w.H_v != w.H_k else ")"),
                      "achieved": achieved / 1e12, "peak": PEAK_FP32_VALU / 1e12,
                      "unit": "TFLOP/s", "frac": achieved / PEAK_FP32_VALU,

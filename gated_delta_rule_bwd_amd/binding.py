@@ -81,8 +81,9 @@ class Problem:
     per-token tensors.  Use ``Problem.from_tensors``."""
 
     def __init__(self, n_seqs, T, H_k, H_v, S, kda, C, scale, seq_lens=None, strides=None,
-                 dtype=DTYPE_F32):
+                 dtype=DTYPE_F32, S_v=None):
         self.n_seqs, self.T, self.H_k, self.H_v, self.S = n_seqs, T, H_k, H_v, S
+        self.S_k, self.S_v = S, (S if S_v is None else int(S_v))
         self.dtype = int(dtype)
         self.kda, self.C, self.scale = bool(kda), int(C), float(scale)
         self.seq_lens = None if seq_lens is None else [int(x) for x in seq_lens]
@@ -94,7 +95,7 @@ class Problem:
     @classmethod
     def from_tensors(cls, q, k, v, g, beta, C=0, scale=None, seq_lens=None, gy=None, y=None):
         n, T, H_k, S = q.shape
-        H_v = v.shape[2]
+        H_v, S_v = v.shape[2], v.shape[3]
         kda = g.dim() == 4 and g.shape[3] == S and S > 1
         strides = {"q": _tok_strides(q, "q"), "k": _tok_strides(k, "k"),
                    "v": _tok_strides(v, "v"), "g": _tok_strides(g, "g"),
@@ -106,7 +107,7 @@ class Problem:
         if len(dts) != 1 or next(iter(dts)) not in _DTYPES:
             raise ValueError(f"q, k, v, g, beta, gy must share one of {list(_DTYPES)}: {dts}")
         return cls(n, T, H_k, H_v, S, kda, C, scale, seq_lens, strides,
-                   _DTYPES[next(iter(dts))])
+                   _DTYPES[next(iter(dts))], S_v)
 
     def set_strides(self, **kw):
         for name, t in kw.items():
@@ -117,7 +118,7 @@ class Problem:
     def _fill(self):
         c = self._c
         c.n_seqs, c.T, c.H_k, c.H_v = self.n_seqs, self.T, self.H_k, self.H_v
-        c.S_k = c.S_v = self.S
+        c.S_k, c.S_v = self.S_k, self.S_v
         c.gate = GATE_KDA if self.kda else GATE_SCALAR
         c.C = self.C
         c.scale = self.scale
@@ -145,10 +146,10 @@ def grad_layout(p: Problem):
     """(total floats, {region: (offset, shape)}) of the packed gradient buffer."""
     off = (ctypes.c_size_t * 6)()
     total = int(lib.gdn_grad_packed_floats(p.c, off))
-    n, T, Hk, Hv, S = p.n_seqs, p.T, p.H_k, p.H_v, p.S
+    n, T, Hk, Hv, S, Sv = p.n_seqs, p.T, p.H_k, p.H_v, p.S_k, p.S_v
     G = S if p.kda else 1
-    shapes = {"dq": (n, T, Hk, S), "dk": (n, T, Hk, S), "dv": (n, T, Hv, S),
-              "dg": (n, T, Hv, G), "dbeta": (n, T, Hv), "dstate": (n, Hv, S, S)}
+    shapes = {"dq": (n, T, Hk, S), "dk": (n, T, Hk, S), "dv": (n, T, Hv, Sv),
+              "dg": (n, T, Hv, G), "dbeta": (n, T, Hv), "dstate": (n, Hv, Sv, S)}
     return total, {name: (int(off[i]), shp) for i, (name, shp) in enumerate(shapes.items())}
 
 

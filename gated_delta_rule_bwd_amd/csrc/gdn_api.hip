@@ -30,8 +30,8 @@ struct Plan {
     int G = 1;         // gate width
     int64_t units = 0;
     bool s128 = false;   // head size 128: row-quarter kernels
-    bool parts = false;  // S < 128: dq/dk go through per-value-head partials
-    int nvs_max = 1;     // S = 128: 64-token stretches per segment
+    bool parts = false;  // small heads: dq/dk go through per-value-head partials
+    int nvs_max = 1;     // S_k = S_v = 128: 64-token stretches per segment
     size_t off_snap = 0, off_seg = 0, off_e = 0, off_pq = 0, off_pk = 0;
     size_t off_a = 0, gate_floats = 0, off_wf = 0, off_vs = 0, off_part = 0, off_pb = 0, off_pg = 0,
            off_hf = 0;
@@ -55,8 +55,8 @@ int validate(const gdn_problem *p) {
         for (int s = 0; s < p->n_seqs; ++s)
             if (p->seq_lens[s] < 0 || p->seq_lens[s] > p->T) return GDN_ERR_ARG;
     if (p->H_v % p->H_k != 0) return GDN_ERR_UNSUPPORTED;
-    if (p->S_k != p->S_v) return GDN_ERR_UNSUPPORTED;
-    if (p->S_k != 16 && p->S_k != 32 && p->S_k != 64 && p->S_k != 128) return GDN_ERR_UNSUPPORTED;
+    auto size_ok = [](int x) { return x == 16 || x == 32 || x == 64 || x == 128; };
+    if (!size_ok(p->S_k) || !size_ok(p->S_v)) return GDN_ERR_UNSUPPORTED;
     const gdn_strides *all[] = {&p->q, &p->k, &p->v, &p->g, &p->beta, &p->gy, &p->y};
     for (auto *s : all)
         if (!strides_ok(*s)) return GDN_ERR_UNSUPPORTED;
@@ -65,9 +65,9 @@ int validate(const gdn_problem *p) {
 
 Plan make_plan(const gdn_problem *p) {
     Plan pl;
-    const int64_t S = p->S_v;
+    const int64_t S = p->S_v, SK = p->S_k, SV = p->S_v;   // S only where SK == SV == 128
     pl.C = p->C > 0 ? std::min(p->C, std::max(p->T, 1)) : ceil_sqrt(p->T);
-    pl.s128 = S == 128;
+    pl.s128 = SK == 128 && SV == 128;
     // head size 128: checkpoints fall on the 8-token grid of the column-scaled windows, so
     // the interval is rounded up to a multiple of 8 and every interval gives the same bits
     if (pl.s128) pl.C = (pl.C + 7) / 8 * 8;
@@ -79,15 +79,15 @@ Plan make_plan(const gdn_problem *p) {
         const size_t nt = (size_t)p->n_seqs * p->T;
         pl.off_in = off;
         pl.in_q = 0;
-        pl.in_k = pl.in_q + nt * p->H_k * S;
-        pl.in_v = pl.in_k + nt * p->H_k * S;
-        pl.in_g = pl.in_v + nt * p->H_v * S;
+        pl.in_k = pl.in_q + nt * p->H_k * SK;
+        pl.in_v = pl.in_k + nt * p->H_k * SK;
+        pl.in_g = pl.in_v + nt * p->H_v * SV;
         pl.in_b = pl.in_g + nt * p->H_v * pl.G;
         pl.in_gy = pl.in_b + nt * p->H_v;
-        off = align_up(off + (pl.in_gy + nt * p->H_v * S) * sizeof(float));
+        off = align_up(off + (pl.in_gy + nt * p->H_v * SV) * sizeof(float));
     }
     pl.off_snap = off;
-    off = align_up(off + (size_t)pl.units * pl.n_ck_max * S * S * sizeof(float));
+    off = align_up(off + (size_t)pl.units * pl.n_ck_max * SV * SK * sizeof(float));
     if (pl.s128) {
         const size_t tok_rows = (size_t)p->n_seqs * p->T * p->H_v;
         constexpr int NQ = 4;
@@ -114,11 +114,11 @@ Plan make_plan(const gdn_problem *p) {
     }
     pl.parts = p->H_v != p->H_k;
     pl.off_seg = off;
-    off = align_up(off + (size_t)pl.units * pl.C * S * S * sizeof(float));
+    off = align_up(off + (size_t)pl.units * pl.C * SV * SK * sizeof(float));
     pl.off_e = off;
-    off = align_up(off + (size_t)pl.units * pl.C * S * sizeof(float));
+    off = align_up(off + (size_t)pl.units * pl.C * SV * sizeof(float));
     if (pl.parts) {
-        const size_t part = (size_t)p->n_seqs * p->T * p->H_v * S * sizeof(float);
+        const size_t part = (size_t)p->n_seqs * p->T * p->H_v * SK * sizeof(float);
         pl.off_pq = off;
         off = align_up(off + part);
         pl.off_pk = off;
@@ -217,7 +217,7 @@ int widen_inputs(const gdn_problem *p, const Plan &pl, void *ws, const void *q, 
                  gdn_problem &pc, const float *&qf, const float *&kf, const float *&vf,
                  const float *&gf, const float *&bf, const float **gyf) {
     float *base = (float *)((char *)ws + pl.off_in);
-    const int64_t n = p->n_seqs, T = p->T, S = p->S_v;
+    const int64_t n = p->n_seqs, T = p->T, SK = p->S_k, SV = p->S_v;
     struct Job {
         const void *src;
         const gdn_strides *st;
@@ -225,12 +225,12 @@ int widen_inputs(const gdn_problem *p, const Plan &pl, void *ws, const void *q, 
         int64_t H, W;
         gdn_strides *dst_st;
         const float **dst;
-    } jobs[] = {{q, &p->q, pl.in_q, p->H_k, S, &pc.q, &qf},
-                {k, &p->k, pl.in_k, p->H_k, S, &pc.k, &kf},
-                {v, &p->v, pl.in_v, p->H_v, S, &pc.v, &vf},
+    } jobs[] = {{q, &p->q, pl.in_q, p->H_k, SK, &pc.q, &qf},
+                {k, &p->k, pl.in_k, p->H_k, SK, &pc.k, &kf},
+                {v, &p->v, pl.in_v, p->H_v, SV, &pc.v, &vf},
                 {g, &p->g, pl.in_g, p->H_v, pl.G, &pc.g, &gf},
                 {beta, &p->beta, pl.in_b, p->H_v, 1, &pc.beta, &bf},
-                {gy, &p->gy, pl.in_gy, p->H_v, S, &pc.gy, gyf}};
+                {gy, &p->gy, pl.in_gy, p->H_v, SV, &pc.gy, gyf}};
     for (auto &j : jobs) {
         if (!j.dst) continue;   // gy of the forward
         if (j.src) {
@@ -290,7 +290,7 @@ int gdn_fwd(const gdn_problem *p, const void *q_in, const void *k_in, const void
     int rc = validate(p);
     if (rc != GDN_OK) return rc;
     const Plan pl = make_plan(p);
-    const int64_t n = p->n_seqs, T = p->T, Hk = p->H_k, Hv = p->H_v, S = p->S_v;
+    const int64_t n = p->n_seqs, T = p->T, Hk = p->H_k, Hv = p->H_v, SK = p->S_k, SV = p->S_v;
     if (!q_in || !k_in || !v_in || !g_in || !beta_in || !state0 || !y || !state_out) return GDN_ERR_ARG;
     const void *ins[] = {q_in, k_in, v_in, g_in, beta_in};
     for (auto *x : ins)
@@ -300,13 +300,13 @@ int gdn_fwd(const gdn_problem *p, const void *q_in, const void *k_in, const void
         if (!aligned4(x)) return GDN_ERR_UNSUPPORTED;
     if (ws_bytes < pl.total) return GDN_ERR_WORKSPACE;
     if (!ws || ((uintptr_t)ws % 16) != 0) return GDN_ERR_ARG;
-    if (!non_self_overlapping(p->y, n, T, Hv, S)) return GDN_ERR_ARG;
+    if (!non_self_overlapping(p->y, n, T, Hv, SV)) return GDN_ERR_ARG;
 
     const int64_t es = in_esize(p);
-    const Range in[] = {span_tok(q_in, p->q, n, T, Hk, S, es), span_tok(k_in, p->k, n, T, Hk, S, es),
-                        span_tok(v_in, p->v, n, T, Hv, S, es), span_tok(g_in, p->g, n, T, Hv, pl.G, es),
-                        span_tok(beta_in, p->beta, n, T, Hv, 1, es), span_flat(state0, n * Hv * S * S)};
-    const Range out[] = {span_tok(y, p->y, n, T, Hv, S), span_flat(state_out, n * Hv * S * S),
+    const Range in[] = {span_tok(q_in, p->q, n, T, Hk, SK, es), span_tok(k_in, p->k, n, T, Hk, SK, es),
+                        span_tok(v_in, p->v, n, T, Hv, SV, es), span_tok(g_in, p->g, n, T, Hv, pl.G, es),
+                        span_tok(beta_in, p->beta, n, T, Hv, 1, es), span_flat(state0, n * Hv * SV * SK)};
+    const Range out[] = {span_tok(y, p->y, n, T, Hv, SV), span_flat(state_out, n * Hv * SV * SK),
                          span_bytes(ws, pl.total)};
     for (auto &o : out)
         for (auto &i : in)
@@ -348,7 +348,7 @@ int gdn_fwd(const gdn_problem *p, const void *q_in, const void *k_in, const void
             if (rc != GDN_OK) return rc;
         }
         rc = device_status(pl.s128 ? gdn::launch_fwd128(a, kda, cnt, (hipStream_t)stream)
-                                   : gdn::launch_fwd(a, (int)S, kda, cnt, (hipStream_t)stream));
+                                   : gdn::launch_fwd(a, (int)SK, (int)SV, kda, cnt, (hipStream_t)stream));
         if (rc != GDN_OK) return rc;
     }
     return GDN_OK;
@@ -362,7 +362,7 @@ int gdn_bwd(const gdn_problem *p, const void *q_in, const void *k_in, const void
     if (rc != GDN_OK) return rc;
     if (flags & ~GDN_BWD_REUSE_SNAPSHOTS) return GDN_ERR_ARG;
     const Plan pl = make_plan(p);
-    const int64_t n = p->n_seqs, T = p->T, Hk = p->H_k, Hv = p->H_v, S = p->S_v;
+    const int64_t n = p->n_seqs, T = p->T, Hk = p->H_k, Hv = p->H_v, SK = p->S_k, SV = p->S_v;
     if (!q_in || !k_in || !v_in || !g_in || !beta_in || !state0 || !gy_in || !grad_packed)
         return GDN_ERR_ARG;
     const void *ins[] = {q_in, k_in, v_in, g_in, beta_in, gy_in};
@@ -377,10 +377,10 @@ int gdn_bwd(const gdn_problem *p, const void *q_in, const void *k_in, const void
     size_t off[6];
     const size_t total = gdn_grad_packed_floats(p, off);
     const int64_t es = in_esize(p);
-    const Range in[] = {span_tok(q_in, p->q, n, T, Hk, S, es),      span_tok(k_in, p->k, n, T, Hk, S, es),
-                        span_tok(v_in, p->v, n, T, Hv, S, es),      span_tok(g_in, p->g, n, T, Hv, pl.G, es),
-                        span_tok(beta_in, p->beta, n, T, Hv, 1, es), span_flat(state0, n * Hv * S * S),
-                        span_tok(gy_in, p->gy, n, T, Hv, S, es),    span_flat(dstate_out, n * Hv * S * S)};
+    const Range in[] = {span_tok(q_in, p->q, n, T, Hk, SK, es),      span_tok(k_in, p->k, n, T, Hk, SK, es),
+                        span_tok(v_in, p->v, n, T, Hv, SV, es),      span_tok(g_in, p->g, n, T, Hv, pl.G, es),
+                        span_tok(beta_in, p->beta, n, T, Hv, 1, es), span_flat(state0, n * Hv * SV * SK),
+                        span_tok(gy_in, p->gy, n, T, Hv, SV, es),    span_flat(dstate_out, n * Hv * SV * SK)};
     const Range outg = span_flat(grad_packed, (int64_t)total);
     const Range wsr = span_bytes(ws, pl.total);
     for (auto &i : in)
@@ -427,7 +427,7 @@ int gdn_bwd(const gdn_problem *p, const void *q_in, const void *k_in, const void
                 if (rc != GDN_OK) return rc;
             }
             rc = device_status(pl.s128 ? gdn::launch_fwd128(f, kda, cnt, (hipStream_t)stream)
-                                       : gdn::launch_fwd(f, (int)S, kda, cnt, (hipStream_t)stream));
+                                       : gdn::launch_fwd(f, (int)SK, (int)SV, kda, cnt, (hipStream_t)stream));
             if (rc != GDN_OK) return rc;
         }
         gdn::BwdArgs b;
@@ -476,7 +476,7 @@ int gdn_bwd(const gdn_problem *p, const void *q_in, const void *k_in, const void
             fill_lens(p, s0, cnt, c.lens);
             rc = device_status(gdn::launch_combine128(c, (hipStream_t)stream));
         } else {
-            rc = device_status(gdn::launch_bwd(b, (int)S, kda, cnt, (hipStream_t)stream));
+            rc = device_status(gdn::launch_bwd(b, (int)SK, (int)SV, kda, cnt, (hipStream_t)stream));
         }
         if (rc != GDN_OK) return rc;
     }
@@ -485,7 +485,7 @@ int gdn_bwd(const gdn_problem *p, const void *q_in, const void *k_in, const void
         c.dq_part = (const float *)((char *)ws + pl.off_pq);
         c.dk_part = (const float *)((char *)ws + pl.off_pk);
         c.dq = dq; c.dk = dk;
-        c.n_seqs = p->n_seqs; c.T = p->T; c.H_k = p->H_k; c.H_v = p->H_v; c.S = (int)S;
+        c.n_seqs = p->n_seqs; c.T = p->T; c.H_k = p->H_k; c.H_v = p->H_v; c.S = (int)SK;
         rc = device_status(gdn::launch_combine(c, (hipStream_t)stream));
         if (rc != GDN_OK) return rc;
     }

@@ -80,7 +80,7 @@ struct Combine128Args {
 
 // Sum of the value heads of each key head (fixed increasing order) for dq and dk.
 struct CombineArgs {
-    const float *dq_part, *dk_part;  // [n_seqs][T][H_v][S]
+    const float *dq_part, *dk_part;  // [n_seqs][T][H_v][S] (S: the key width)
     float *dq, *dk;                  // [n_seqs][T][H_k][S]
     int32_t n_seqs, T, H_k, H_v, S;
 };
@@ -96,8 +96,9 @@ struct WidenArgs {
 };
 
 hipError_t launch_widen(const WidenArgs &a, hipStream_t st);
-hipError_t launch_fwd(const FwdArgs &a, int S, bool kda, int n_seqs_launch, hipStream_t st);
-hipError_t launch_bwd(const BwdArgs &a, int S, bool kda, int n_seqs_launch, hipStream_t st);
+// head sizes: key width SK and value width SV, each in {16, 32, 64, 128}, not both 128
+hipError_t launch_fwd(const FwdArgs &a, int SK, int SV, bool kda, int n_seqs_launch, hipStream_t st);
+hipError_t launch_bwd(const BwdArgs &a, int SK, int SV, bool kda, int n_seqs_launch, hipStream_t st);
 hipError_t launch_combine(const CombineArgs &a, hipStream_t st);
 hipError_t launch_gate128(const GateArgs &a, hipStream_t st);
 hipError_t launch_fwd128(const FwdArgs &a, bool kda, int n_seqs_launch, hipStream_t st);

@@ -23,20 +23,23 @@
 // is rebuilt as Mp + delta k^T, the same fma the forward executed).
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "gdn_internal.h"
 
 namespace gdn {
 namespace {
 
-template <int S, int R>
+// SK columns (key width), SV rows (value width)
+template <int SK, int SV, int R>
 struct Layout {
     static constexpr int LPR = 16;         // lanes per row
-    static constexpr int NC = S / LPR;     // columns per lane
+    static constexpr int NC = SK / LPR;    // columns per lane
     static constexpr int RG = 64 / LPR;    // row groups per wave
     static constexpr int RPW = RG * R;     // rows per wave
-    static constexpr int NW = S / RPW;     // waves per unit
+    static constexpr int NW = SV / RPW;    // waves per unit
     static constexpr int THREADS = NW * 64;
-    static_assert(S % RPW == 0 && NC >= 1, "unsupported head size");
+    static_assert(SV % RPW == 0 && NC >= 1 && SK % LPR == 0, "unsupported head size");
 };
 
 __device__ __forceinline__ float as_f(int x) { return __builtin_bit_cast(float, x); }
@@ -66,10 +69,10 @@ __device__ __forceinline__ float groups4_sum(float v) {
 
 // ------------------------------------------------------------------ forward scan
 
-template <int S, int R, bool KDA>
-__global__ void __launch_bounds__((Layout<S, R>::THREADS))
+template <int SK, int SV, int R, bool KDA>
+__global__ void __launch_bounds__((Layout<SK, SV, R>::THREADS))
 fwd_kernel(const FwdArgs a) {
-    using Lo = Layout<S, R>;
+    using Lo = Layout<SK, SV, R>;
     constexpr int NC = Lo::NC, LPR = Lo::LPR;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int lc = lane % LPR, rg = lane / LPR;
@@ -87,21 +90,21 @@ fwd_kernel(const FwdArgs a) {
     const float *bp = a.beta + s * a.sb.seq + h * a.sb.head;
 
     float M[R][NC];
-    const float *st0 = a.state0 + unit * S * S + (int64_t)row0 * S + lc;
+    const float *st0 = a.state0 + unit * SV * SK + (int64_t)row0 * SK + lc;
 #pragma unroll
     for (int r = 0; r < R; ++r)
 #pragma unroll
-        for (int n = 0; n < NC; ++n) M[r][n] = st0[r * S + n * LPR];
+        for (int n = 0; n < NC; ++n) M[r][n] = st0[r * SK + n * LPR];
 
-    float *snap = a.snap + unit * a.n_ck_max * S * S + (int64_t)row0 * S + lc;
+    float *snap = a.snap + unit * a.n_ck_max * SV * SK + (int64_t)row0 * SK + lc;
     int until_snap = 0;
     for (int t = 0; t < L; ++t) {
         if (until_snap == 0) {
 #pragma unroll
             for (int r = 0; r < R; ++r)
 #pragma unroll
-                for (int n = 0; n < NC; ++n) snap[r * S + n * LPR] = M[r][n];
-            snap += (int64_t)S * S;
+                for (int n = 0; n < NC; ++n) snap[r * SK + n * LPR] = M[r][n];
+            snap += (int64_t)SV * SK;
             until_snap = a.C;
         }
         --until_snap;
@@ -162,24 +165,24 @@ fwd_kernel(const FwdArgs a) {
         }
     }
     if (a.state_out) {
-        float *so = a.state_out + unit * S * S + (int64_t)row0 * S + lc;
+        float *so = a.state_out + unit * SV * SK + (int64_t)row0 * SK + lc;
 #pragma unroll
         for (int r = 0; r < R; ++r)
 #pragma unroll
-            for (int n = 0; n < NC; ++n) so[r * S + n * LPR] = M[r][n];
+            for (int n = 0; n < NC; ++n) so[r * SK + n * LPR] = M[r][n];
     }
 }
 
 // ------------------------------------------------------------------ backward walk
 
-template <int S, int R, bool KDA>
-__global__ void __launch_bounds__((Layout<S, R>::THREADS))
+template <int SK, int SV, int R, bool KDA>
+__global__ void __launch_bounds__((Layout<SK, SV, R>::THREADS))
 bwd_kernel(const BwdArgs a) {
-    using Lo = Layout<S, R>;
+    using Lo = Layout<SK, SV, R>;
     constexpr int NC = Lo::NC, LPR = Lo::LPR, NW = Lo::NW, RG = Lo::RG;
-    constexpr int G = KDA ? S : 1;
+    constexpr int G = KDA ? SK : 1;
     // column partial sums per wave: [parity][wave][dq | dk | dg][column]
-    __shared__ float red[2][NW][3][S];
+    __shared__ float red[2][NW][3][SK];
     __shared__ float redb[2][NW * RG];   // dbeta partials per row group
     __shared__ float redg[2][NW];        // scalar-gate dg partials per wave
 
@@ -203,11 +206,11 @@ bwd_kernel(const BwdArgs a) {
 
     float dM[R][NC];
     if (a.dstate_out) {
-        const float *d0 = a.dstate_out + unit * S * S + (int64_t)row0 * S + lc;
+        const float *d0 = a.dstate_out + unit * SV * SK + (int64_t)row0 * SK + lc;
 #pragma unroll
         for (int r = 0; r < R; ++r)
 #pragma unroll
-            for (int n = 0; n < NC; ++n) dM[r][n] = d0[r * S + n * LPR];
+            for (int n = 0; n < NC; ++n) dM[r][n] = d0[r * SK + n * LPR];
     } else {
 #pragma unroll
         for (int r = 0; r < R; ++r)
@@ -215,8 +218,8 @@ bwd_kernel(const BwdArgs a) {
             for (int n = 0; n < NC; ++n) dM[r][n] = 0.f;
     }
 
-    float *seg = a.segbuf + unit * C * S * S + (int64_t)row0 * S + lc;
-    float *eb = a.ebuf_seg + unit * C * S + row0;
+    float *seg = a.segbuf + unit * C * SV * SK + (int64_t)row0 * SK + lc;
+    float *eb = a.ebuf_seg + unit * C * SV + row0;
     const int n_ck = (L + C - 1) / C;
     int parity = 0;
 
@@ -225,11 +228,11 @@ bwd_kernel(const BwdArgs a) {
         // ---- replay the segment from its snapshot
         {
             float M[R][NC];
-            const float *sp = a.snap + (unit * a.n_ck_max + sg) * S * S + (int64_t)row0 * S + lc;
+            const float *sp = a.snap + (unit * a.n_ck_max + sg) * SV * SK + (int64_t)row0 * SK + lc;
 #pragma unroll
             for (int r = 0; r < R; ++r)
 #pragma unroll
-                for (int n = 0; n < NC; ++n) M[r][n] = sp[r * S + n * LPR];
+                for (int n = 0; n < NC; ++n) M[r][n] = sp[r * SK + n * LPR];
             for (int t = t0; t < t1; ++t) {
                 float kv[NC], av[NC], vv[R];
 #pragma unroll
@@ -248,8 +251,8 @@ bwd_kernel(const BwdArgs a) {
                 float ak[NC];
 #pragma unroll
                 for (int n = 0; n < NC; ++n) ak[n] = av[n] * kv[n];
-                float *dst = seg + (int64_t)(t - t0) * S * S;
-                float *edst = eb + (t - t0) * S;
+                float *dst = seg + (int64_t)(t - t0) * SV * SK;
+                float *edst = eb + (t - t0) * SV;
 #pragma unroll
                 for (int r = 0; r < R; ++r) {
                     float u = 0.f;
@@ -262,7 +265,7 @@ bwd_kernel(const BwdArgs a) {
                     for (int n = 0; n < NC; ++n) {
                         const float mp = M[r][n] * av[n];
                         M[r][n] = fmaf(delta, kv[n], mp);
-                        dst[r * S + n * LPR] = mp;  // keep the decayed previous state
+                        dst[r * SK + n * LPR] = mp;  // keep the decayed previous state
                     }
                     if (lc == 0) edst[r] = e;
                 }
@@ -288,14 +291,14 @@ bwd_kernel(const BwdArgs a) {
                 for (int n = 0; n < NC; ++n) av[n] = a0;
             }
             const float beta = bp[t * a.sb.tok];
-            const float *src = seg + (int64_t)(t - t0) * S * S;
-            const float *esrc = eb + (t - t0) * S;
+            const float *src = seg + (int64_t)(t - t0) * SV * SK;
+            const float *esrc = eb + (t - t0) * SV;
 #pragma unroll
             for (int r = 0; r < R; ++r) {
                 gyv[r] = a.scale * gyp[t * a.sgy.tok + r];
                 ev[r] = esrc[r];
 #pragma unroll
-                for (int n = 0; n < NC; ++n) Mp[r][n] = src[r * S + n * LPR];
+                for (int n = 0; n < NC; ++n) Mp[r][n] = src[r * SK + n * LPR];
             }
 
             float pq[NC], pk[NC], pg[NC], dd[R];
@@ -330,7 +333,7 @@ bwd_kernel(const BwdArgs a) {
                 }
             }
             if (lc == 0) {
-                float *dvp = a.dv + ((s * a.T + t) * a.H_v + h) * S + row0;
+                float *dvp = a.dv + ((s * a.T + t) * a.H_v + h) * SV + row0;
 #pragma unroll
                 for (int r = 0; r < R; ++r) dvp[r] = beta * dd[r];
                 redb[parity][wave * RG + rg] = pb;
@@ -360,15 +363,15 @@ bwd_kernel(const BwdArgs a) {
             }
             __syncthreads();
             const int64_t row_tok = s * a.T + t;
-            for (int idx = tid; idx < (KDA ? 3 : 2) * S; idx += Lo::THREADS) {
-                const int which = idx / S, i = idx % S;
+            for (int idx = tid; idx < (KDA ? 3 : 2) * SK; idx += Lo::THREADS) {
+                const int which = idx / SK, i = idx % SK;
                 float acc = 0.f;
 #pragma unroll
                 for (int w = 0; w < NW; ++w) acc += red[parity][w][which][i];
                 if (which == 0)
-                    a.dq[(row_tok * a.dqk_head + h) * S + i] = acc;
+                    a.dq[(row_tok * a.dqk_head + h) * SK + i] = acc;
                 else if (which == 1)
-                    a.dk[(row_tok * a.dqk_head + h) * S + i] = acc;
+                    a.dk[(row_tok * a.dqk_head + h) * SK + i] = acc;
                 else
                     a.dg[(row_tok * a.H_v + h) * G + i] = acc;
             }
@@ -389,20 +392,20 @@ bwd_kernel(const BwdArgs a) {
     }
 
     {
-        float *ds = a.dstate + unit * S * S + (int64_t)row0 * S + lc;
+        float *ds = a.dstate + unit * SV * SK + (int64_t)row0 * SK + lc;
 #pragma unroll
         for (int r = 0; r < R; ++r)
 #pragma unroll
-            for (int n = 0; n < NC; ++n) ds[r * S + n * LPR] = dM[r][n];
+            for (int n = 0; n < NC; ++n) ds[r * SK + n * LPR] = dM[r][n];
     }
     // padded tokens: every per-token output row of this unit is written zero
     for (int64_t t = L; t < a.T; ++t) {
         const int64_t row_tok = s * a.T + t;
-        for (int i = tid; i < S; i += Lo::THREADS) {
-            a.dq[(row_tok * a.dqk_head + h) * S + i] = 0.f;
-            a.dk[(row_tok * a.dqk_head + h) * S + i] = 0.f;
-            a.dv[(row_tok * a.H_v + h) * S + i] = 0.f;
+        for (int i = tid; i < SK; i += Lo::THREADS) {
+            a.dq[(row_tok * a.dqk_head + h) * SK + i] = 0.f;
+            a.dk[(row_tok * a.dqk_head + h) * SK + i] = 0.f;
         }
+        for (int i = tid; i < SV; i += Lo::THREADS) a.dv[(row_tok * a.H_v + h) * SV + i] = 0.f;
         for (int i = tid; i < G; i += Lo::THREADS) a.dg[(row_tok * a.H_v + h) * G + i] = 0.f;
         if (tid == 0) a.dbeta[row_tok * a.H_v + h] = 0.f;
     }
@@ -475,39 +478,57 @@ hipError_t launch(const void *fn, const Args &args, int blocks, int threads, hip
     return hipLaunchKernel(fn, dim3(blocks), dim3(threads), params, 0, st);
 }
 
-template <int S, int R>
-constexpr int kThreads = Layout<S, R>::THREADS;
+template <int SK, int SV, int R>
+constexpr int kThreads = Layout<SK, SV, R>::THREADS;
 
-}  // namespace
+// Launch a kernel template over the supported (key width, value width) pairs: every pair of
+// {16, 32, 64, 128} except 128 x 128 (the row-quarter kernels of gdn_s128.hip).
+template <int SK, int SV, typename Args, typename Pick>
+hipError_t launch_pair(const Args &a, bool kda, int blocks, hipStream_t st, Pick pick) {
+    if constexpr (SK == 128 && SV == 128) {
+        return hipErrorInvalidValue;
+    } else {
+        return launch(pick(std::integral_constant<int, SK>{}, std::integral_constant<int, SV>{}, kda), a,
+                      blocks, kThreads<SK, SV, 4>, st);
+    }
+}
 
-hipError_t launch_fwd(const FwdArgs &a, int S, bool kda, int n_seqs_launch, hipStream_t st) {
-    const int blocks = n_seqs_launch * a.H_v;
-    switch (S * 2 + (kda ? 1 : 0)) {
-        case 32: return launch((const void *)fwd_kernel<16, 4, false>, a, blocks, kThreads<16, 4>, st);
-        case 33: return launch((const void *)fwd_kernel<16, 4, true>, a, blocks, kThreads<16, 4>, st);
-        case 64: return launch((const void *)fwd_kernel<32, 4, false>, a, blocks, kThreads<32, 4>, st);
-        case 65: return launch((const void *)fwd_kernel<32, 4, true>, a, blocks, kThreads<32, 4>, st);
-        case 128: return launch((const void *)fwd_kernel<64, 4, false>, a, blocks, kThreads<64, 4>, st);
-        case 129: return launch((const void *)fwd_kernel<64, 4, true>, a, blocks, kThreads<64, 4>, st);
-        case 256: return launch((const void *)fwd_kernel<128, 4, false>, a, blocks, kThreads<128, 4>, st);
-        case 257: return launch((const void *)fwd_kernel<128, 4, true>, a, blocks, kThreads<128, 4>, st);
+template <int SK, typename Args, typename Pick>
+hipError_t launch_sv(const Args &a, int SV, bool kda, int blocks, hipStream_t st, Pick pick) {
+    switch (SV) {
+        case 16: return launch_pair<SK, 16>(a, kda, blocks, st, pick);
+        case 32: return launch_pair<SK, 32>(a, kda, blocks, st, pick);
+        case 64: return launch_pair<SK, 64>(a, kda, blocks, st, pick);
+        case 128: return launch_pair<SK, 128>(a, kda, blocks, st, pick);
     }
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_bwd(const BwdArgs &a, int S, bool kda, int n_seqs_launch, hipStream_t st) {
-    const int blocks = n_seqs_launch * a.H_v;
-    switch (S * 2 + (kda ? 1 : 0)) {
-        case 32: return launch((const void *)bwd_kernel<16, 4, false>, a, blocks, kThreads<16, 4>, st);
-        case 33: return launch((const void *)bwd_kernel<16, 4, true>, a, blocks, kThreads<16, 4>, st);
-        case 64: return launch((const void *)bwd_kernel<32, 4, false>, a, blocks, kThreads<32, 4>, st);
-        case 65: return launch((const void *)bwd_kernel<32, 4, true>, a, blocks, kThreads<32, 4>, st);
-        case 128: return launch((const void *)bwd_kernel<64, 4, false>, a, blocks, kThreads<64, 4>, st);
-        case 129: return launch((const void *)bwd_kernel<64, 4, true>, a, blocks, kThreads<64, 4>, st);
-        case 256: return launch((const void *)bwd_kernel<128, 4, false>, a, blocks, kThreads<128, 4>, st);
-        case 257: return launch((const void *)bwd_kernel<128, 4, true>, a, blocks, kThreads<128, 4>, st);
+template <typename Args, typename Pick>
+hipError_t launch_sizes(const Args &a, int SK, int SV, bool kda, int blocks, hipStream_t st, Pick pick) {
+    switch (SK) {
+        case 16: return launch_sv<16>(a, SV, kda, blocks, st, pick);
+        case 32: return launch_sv<32>(a, SV, kda, blocks, st, pick);
+        case 64: return launch_sv<64>(a, SV, kda, blocks, st, pick);
+        case 128: return launch_sv<128>(a, SV, kda, blocks, st, pick);
     }
     return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_fwd(const FwdArgs &a, int SK, int SV, bool kda, int n_seqs_launch, hipStream_t st) {
+    return launch_sizes(a, SK, SV, kda, n_seqs_launch * a.H_v, st, [](auto sk, auto sv, bool k) {
+        constexpr int K = decltype(sk)::value, V = decltype(sv)::value;
+        return k ? (const void *)fwd_kernel<K, V, 4, true> : (const void *)fwd_kernel<K, V, 4, false>;
+    });
+}
+
+hipError_t launch_bwd(const BwdArgs &a, int SK, int SV, bool kda, int n_seqs_launch, hipStream_t st) {
+    return launch_sizes(a, SK, SV, kda, n_seqs_launch * a.H_v, st, [](auto sk, auto sv, bool k) {
+        constexpr int K = decltype(sk)::value, V = decltype(sv)::value;
+        return k ? (const void *)bwd_kernel<K, V, 4, true> : (const void *)bwd_kernel<K, V, 4, false>;
+    });
 }
 
 hipError_t launch_widen(const WidenArgs &a, hipStream_t st) {

@@ -18,7 +18,7 @@ class DeviceCase:
     def __init__(self, w: Workload, arrays: dict, device="cuda", C=None, strided_gy=False,
                  packed=None, grad_offset=0, in_dtype=torch.float32):
         self.w = w
-        n, T, Hk, Hv, S, G = w.n_seqs, w.T, w.H_k, w.H_v, w.S, w.G
+        n, T, Hk, Hv, S, Sv, G = w.n_seqs, w.T, w.H_k, w.H_v, w.S, w.S_v, w.G
         dev = torch.device(device)
         packed = w.packed if packed is None else packed
 
@@ -34,7 +34,7 @@ class DeviceCase:
             HkS = Hk * S
             self.q = self.qkv[:, :, :HkS].unflatten(2, (Hk, S))
             self.k = self.qkv[:, :, HkS:2 * HkS].unflatten(2, (Hk, S))
-            self.v = self.qkv[:, :, 2 * HkS:].unflatten(2, (Hv, S))
+            self.v = self.qkv[:, :, 2 * HkS:].unflatten(2, (Hv, Sv))
             assert self.q.stride() == (T * W, W, S, 1)
         else:
             self.qkv = None
@@ -44,14 +44,14 @@ class DeviceCase:
         self.state0 = put(arrays["state0"])
         if strided_gy:
             # gy as a view with head-major order and a padded token stride
-            base = torch.zeros((n, Hv, T, S + 8), dtype=in_dtype, device=dev)
-            self.gy = base[..., :S].permute(0, 2, 1, 3)
+            base = torch.zeros((n, Hv, T, Sv + 8), dtype=in_dtype, device=dev)
+            self.gy = base[..., :Sv].permute(0, 2, 1, 3)
             self.gy.copy_(put_in(arrays["gy"]))
         else:
             self.gy = put_in(arrays["gy"])
         self.dstate_out = put(arrays["dstate_out"]) if arrays.get("dstate_out") is not None else None
-        self.y = torch.empty((n, T, Hv, S), dtype=torch.float32, device=dev)
-        self.state_out = torch.empty((n, Hv, S, S), dtype=torch.float32, device=dev)
+        self.y = torch.empty((n, T, Hv, Sv), dtype=torch.float32, device=dev)
+        self.state_out = torch.empty((n, Hv, Sv, S), dtype=torch.float32, device=dev)
         self.p = B.Problem.from_tensors(self.q, self.k, self.v, self.g, self.beta,
                                         C=w.C if C is None else C, scale=w.scale,
                                         seq_lens=list(w.lens), gy=self.gy, y=self.y)

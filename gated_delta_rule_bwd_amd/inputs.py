@@ -49,6 +49,7 @@ class Workload:
     packed: bool = False        # q/k/v are row views of one [n_seqs, T, W] buffer
     seed: int = 1000
     g_hi: float = 0.0           # upper end of the log-gate range (above 0: some gates exceed one)
+    Sv: int = 0                 # value head size when it differs from the key head size S
 
     @property
     def S_k(self):
@@ -56,7 +57,7 @@ class Workload:
 
     @property
     def S_v(self):
-        return self.S
+        return self.Sv or self.S
 
     @property
     def scale(self):
@@ -76,11 +77,11 @@ class Workload:
 
     @property
     def packed_width(self):
-        return 2 * self.H_k * self.S + self.H_v * self.S
+        return 2 * self.H_k * self.S + self.H_v * self.S_v
 
     def shape_dict(self, **over):
         d = dict(n_seqs=self.n_seqs, T=self.T, H_k=self.H_k, H_v=self.H_v, S_k=self.S,
-                 S_v=self.S, kda=self.kda, C=self.C, scale=self.scale,
+                 S_v=self.S_v, kda=self.kda, C=self.C, scale=self.scale,
                  seq_lens=list(self.lens))
         d.update(over)
         return d
@@ -130,15 +131,15 @@ def _slice(w: Workload, tensor: str, s: int, head: int) -> np.ndarray:
         n = np.sqrt(np.sum(x * x, axis=1, keepdims=True))
         return x / n
     if tensor in ("v", "gy"):
-        return r.standard_normal((T, S))
+        return r.standard_normal((T, w.S_v))
     if tensor == "g":
         return w.g_lo + (w.g_hi - w.g_lo) * r.random((T, w.G))
     if tensor == "beta":
         return r.random(T)
     if tensor == "state0":
-        return 0.1 * r.standard_normal((S, S))
+        return 0.1 * r.standard_normal((w.S_v, S))
     if tensor == "dstate_out":
-        return r.standard_normal((S, S))
+        return r.standard_normal((w.S_v, S))
     raise KeyError(tensor)
 
 
@@ -149,14 +150,14 @@ def _heads(w: Workload, tensor: str) -> int:
 def make_tensor(w: Workload, tensor: str, seqs=None, heads=None, pad_value=0.0) -> np.ndarray:
     """float32 array in the logical layout, restricted to the given sequences / heads.
 
-    Logical layouts: q, k [n][T][H_k][S]; v, gy [n][T][H_v][S]; g [n][T][H_v][G];
-    beta [n][T][H_v]; state0, dstate_out [n][H_v][S][S].
+    Logical layouts: q, k [n][T][H_k][S_k]; v, gy [n][T][H_v][S_v]; g [n][T][H_v][G];
+    beta [n][T][H_v]; state0, dstate_out [n][H_v][S_v][S_k].
     """
     seqs = list(range(w.n_seqs)) if seqs is None else list(seqs)
     heads = list(range(_heads(w, tensor))) if heads is None else list(heads)
     lens = w.lens
     if tensor in ("state0", "dstate_out"):
-        out = np.empty((len(seqs), len(heads), w.S, w.S), np.float32)
+        out = np.empty((len(seqs), len(heads), w.S_v, w.S), np.float32)
         for a, s in enumerate(seqs):
             for b, h in enumerate(heads):
                 out[a, b] = _slice(w, tensor, s, h)
@@ -166,7 +167,8 @@ def make_tensor(w: Workload, tensor: str, seqs=None, heads=None, pad_value=0.0) 
     elif tensor == "g":
         out = np.empty((len(seqs), w.T, len(heads), w.G), np.float32)
     else:
-        out = np.empty((len(seqs), w.T, len(heads), w.S), np.float32)
+        width = w.S if tensor in ("q", "k") else w.S_v
+        out = np.empty((len(seqs), w.T, len(heads), width), np.float32)
     for a, s in enumerate(seqs):
         for b, h in enumerate(heads):
             x = _slice(w, tensor, s, h).astype(np.float32)
@@ -224,7 +226,7 @@ def round_inputs(arrays: dict, kind: str) -> dict:
 
 def pack_qkv(w: Workload, q, k, v) -> np.ndarray:
     """Place q, k, v as row views of one [n, T, W] buffer: q at columns [0, H_k S),
-    k at [H_k S, 2 H_k S), v at [2 H_k S, W); head h at offset h S within its block."""
+    k at [H_k S, 2 H_k S), v at [2 H_k S, W); head h at offset h S (h S_v for v) in its block."""
     n, T = q.shape[0], q.shape[1]
     HkS = w.H_k * w.S
     buf = np.zeros((n, T, w.packed_width), np.float32)

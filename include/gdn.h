@@ -90,7 +90,7 @@ typedef struct gdn_strides {
  *   T           padded sequence length (>= 0)
  *   H_k, H_v    key and value head counts; H_v must be a multiple of H_k (grouped heads:
  *               value head h reads key head h mod H_k)
- *   S_k, S_v    key and value head sizes; supported: S_k == S_v in {16, 32, 64, 128}
+ *   S_k, S_v    key and value head sizes, each in {16, 32, 64, 128} (equal or not)
  *   gate        GDN_GATE_SCALAR (g is [.., H_v], one value per token and head) or
  *               GDN_GATE_KDA (g is [.., H_v, S_k])
  *   C           checkpoint interval in tokens; 0 selects ceil(sqrt(T)); values above T

@@ -32,7 +32,7 @@ def test_exports_every_declared_symbol(B):
 
 def problem(B, strides=None, **kw):
     d = dict(n_seqs=2, T=64, H_k=4, H_v=8, S=64, kda=True, C=8, scale=0.125,
-             seq_lens=[64, 61], dtype=0)
+             seq_lens=[64, 61], dtype=0, S_v=None)
     d.update(kw)
     override = strides or {}
     strides = {"q": (64 * 4 * 64, 4 * 64, 64), "k": (64 * 4 * 64, 4 * 64, 64),
@@ -41,7 +41,7 @@ def problem(B, strides=None, **kw):
                "y": (64 * 8 * 64, 8 * 64, 64)}
     strides.update(override)
     return B.Problem(d["n_seqs"], d["T"], d["H_k"], d["H_v"], d["S"], d["kda"], d["C"],
-                     d["scale"], d["seq_lens"], strides, d["dtype"])
+                     d["scale"], d["seq_lens"], strides, d["dtype"], d["S_v"])
 
 
 def expected_ws(n, T, Hk, Hv, S, C, kda=True):
@@ -105,7 +105,8 @@ def test_grad_layout(B):
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(S=48), -2), (dict(S=8), -2), (dict(H_k=3), -2), (dict(n_seqs=-1), -1),
+    (dict(S=48), -2), (dict(S=8), -2), (dict(S_v=8), -2), (dict(S_v=256), -2),
+    (dict(H_k=3), -2), (dict(n_seqs=-1), -1),
     (dict(T=-1), -1), (dict(C=-1), -1), (dict(seq_lens=[65, 3]), -1),
     (dict(seq_lens=[-1, 3]), -1), (dict(scale=float("nan")), -1), (dict(H_k=0), -1),
     (dict(dtype=3), -1), (dict(dtype=-1), -1),
@@ -183,6 +184,27 @@ def test_bwd_argument_errors(B):
     ov = list(good)
     ov[9] = good[0]                           # workspace overlapping q
     assert _bwd(B, p, ov, ws) == -1
+
+
+def test_rectangular_heads_layout(B):
+    """S_k != S_v: workspace (small-head path at every pair but 128 x 128) and the packed
+    gradient regions (dq, dk, dg over S_k; dv over S_v; dstate S_v x S_k)."""
+    al = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    n, T, Hk, Hv, C = 2, 64, 4, 8, 8
+    for Sk, Sv in ((64, 32), (32, 128), (128, 16), (16, 64)):
+        for kda in (True, False):
+            p = problem(B, S=Sk, S_v=Sv, kda=kda)
+            units = n * Hv
+            ws = al(units * -(-T // C) * Sv * Sk * 4)
+            ws = al(ws + units * C * Sv * Sk * 4)
+            ws = al(ws + units * C * Sv * 4)
+            ws = al(al(ws + n * T * Hv * Sk * 4) + n * T * Hv * Sk * 4)
+            assert B.workspace_size(p) == ws, (Sk, Sv, kda)
+            total, lay = B.grad_layout(p)
+            G = Sk if kda else 1
+            assert lay["dq"][1] == (n, T, Hk, Sk) and lay["dv"][1] == (n, T, Hv, Sv)
+            assert lay["dg"][1] == (n, T, Hv, G) and lay["dstate"][1] == (n, Hv, Sv, Sk)
+            assert total == n * T * (2 * Hk * Sk + Hv * Sv + Hv * G + Hv) + n * Hv * Sv * Sk
 
 
 def test_half_inputs_workspace_and_alignment(B):

@@ -108,6 +108,28 @@ def test_parity_s16_layer_sampled(dev):
             ", ".join(f"{k} {v:.1e}" for k, v in rep.items()))
 
 
+# Key and value head sizes that differ: the small-head kernels over S_v rows x S_k columns.
+RECT_CASES = {
+    "k64_v32_kda_ragged": I.Workload("r_k64_v32", 2, 64, 2, 4, 64, True, 8, -0.5,
+                                     seq_lens=(64, 45), seed=801, Sv=32),
+    "k32_v128_scalar_gqa_packed": I.Workload("r_k32_v128", 2, 80, 2, 6, 32, False, 0, -1.0,
+                                             packed=True, seed=802, Sv=128),
+    "k128_v64_kda": I.Workload("r_k128_v64", 1, 72, 1, 2, 128, True, 16, -0.3, seed=803, Sv=64),
+    "k16_v64_scalar": I.Workload("r_k16_v64", 1, 50, 1, 1, 16, False, 0, -1.0, seed=804, Sv=64),
+}
+
+
+@pytest.mark.parametrize("name", list(RECT_CASES))
+@pytest.mark.parametrize("reuse", [True, False])
+def test_parity_rectangular_heads(dev, name, reuse):
+    w = RECT_CASES[name]
+    log(f"[parity] {w.name} S_k={w.S_k} S_v={w.S_v} reuse={reuse} lens={w.lens}")
+    arrays, _ = I.make_all(w)
+    _, got = run_case(dev, w, arrays, reuse=reuse)
+    rep = check(got, oracle_results(w, arrays), REGIONS_FWD + REGIONS_BWD)
+    log(f"[parity] {w.name}: " + ", ".join(f"{k} {v:.1e}" for k, v in rep.items()))
+
+
 # Half-precision inputs (q, k, v, g, beta, gy in fp16 or bf16; state and gradients fp32).
 HALF_CASES = {
     "bf16_s128_kda": ("bf16", I.Workload("h_s128_kda", 2, 150, 2, 4, 128, True, 64, -0.3,
