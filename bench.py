@@ -34,6 +34,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--input-dtype", choices=("f32", "f16", "bf16"), default="f32",
                     help="element type of q, k, v, g, beta, gy (state and gradients stay fp32)")
+    ap.add_argument("--op", choices=("gdn", "ssm_conv"), default="gdn",
+                    help="gdn: the recurrence fwd+bwd (default); ssm_conv: the short "
+                         "convolution fwd+bwd on the layer shape's packed rows")
     ap.add_argument("--cpu-sample-heads", type=int, default=0,
                     help="key heads of sequence 0 in the oracle sample (0: auto)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -151,8 +154,89 @@ def cpu_baseline(w, n_key_heads):
                       f"{w.T} tokens each ({th} tokens·heads), fp64 fwd+bwd, {dt:.1f} s"}
 
 
+PEAK_HBM = 8.0e12              # MI355X HBM3E, bytes/s
+
+
+def bench_conv(args):
+    """The convolution forward + backward (gdn_ssm_conv_fwd then gdn_ssm_conv_bwd) on the
+    layer shape's packed rows.  Algorithmic bytes per launch: forward reads sx and c and
+    writes y; backward reads dy and c and writes d_sx, each once."""
+    import torch
+    from gated_delta_rule_bwd_amd import binding as B
+    from gated_delta_rule_bwd_amd import inputs as I
+    cfg = I.CONV_LAYER
+    n, T, D, K = cfg["n_seqs"], cfg["T"], cfg["d_inner"], cfg["d_conv"]
+    sx, c, dy = I.make_conv(cfg)
+    dev = "cuda:0"
+    gsx, gc, gdy = (torch.from_numpy(a).to(dev) for a in (sx, c, dy))
+    del sx, dy
+    y = torch.empty((n, T, D), device=dev)
+    dsx = torch.empty((n, T + K - 1, D), device=dev)
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        B.ssm_conv_fwd(gsx, gc, y, stream)
+        B.ssm_conv_bwd(gdy, gc, dsx, stream)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for e0, e1, e2 in ev:
+        e0.record(stream)
+        B.ssm_conv_fwd(gsx, gc, y, stream)
+        e1.record(stream)
+        B.ssm_conv_bwd(gdy, gc, dsx, stream)
+        e2.record(stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    fwd_ms = sum(a.elapsed_time(b) for a, b, _ in ev) / args.steps
+    bwd_ms = sum(b.elapsed_time(e) for _, b, e in ev) / args.steps
+    rows_in = n * (T + K - 1) * D * 4
+    rows_out = n * T * D * 4
+    taps = D * K * 4
+    launch_bytes = rows_in + rows_out + taps          # the same for both directions
+    tc = n * T * D
+    out = {
+        "metric": "SSM_CONV fwd+bwd tokens·channels/s; % HBM peak",
+        "value": tc / (ms / 1e3), "unit": "tokens·channels/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": cfg["name"], "n_seqs": n, "T": T, "d_inner": D, "d_conv": K},
+        "fwd_ms": fwd_ms, "bwd_ms": bwd_ms,
+        "roofline": {"bound": "hbm", "kernel": "conv_kernel (backward launch)",
+                     "achieved": launch_bytes / (bwd_ms / 1e3) / 1e9, "peak": PEAK_HBM / 1e9,
+                     "unit": "GB/s", "frac": launch_bytes / (bwd_ms / 1e3) / PEAK_HBM,
+                     "traffic": None},
+        "fwd_GBps": launch_bytes / (fwd_ms / 1e3) / 1e9,
+    }
+    if not args.no_cpu_baseline:
+        import oracle.ssm_conv as OC
+        s_sx, s_c, s_dy = I.make_conv(cfg, seqs=[0])
+        t0 = time.perf_counter()
+        reps = 0
+        while True:
+            OC.conv_fwd(s_sx, s_c)
+            OC.conv_bwd(s_dy, s_c)
+            reps += 1
+            dt = time.perf_counter() - t0
+            if dt > 10.0:
+                break
+        out["cpu_baseline"] = {"value": reps * T * D / dt, "unit": "tokens·channels/s",
+                               "cores": 1, "kind": "oracle",
+                               "sample": f"sequence 0 ({T} tokens x {D} channels), fp64 fwd+bwd, "
+                                         f"{reps} repetitions in {dt:.1f} s"}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
+    if args.op == "ssm_conv" and not (args.pmc_summary or args.copy_calibration):
+        if args.gpus != 1:
+            print("bench.py runs on one GPU only", file=sys.stderr)
+            sys.exit(2)
+        bench_conv(args)
+        return
     if args.pmc_summary:
         summ = pmc_summary(args.pmc_summary)
         with open(TRAFFIC_FILE, "w") as f:

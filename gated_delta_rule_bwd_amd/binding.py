@@ -26,7 +26,7 @@ DTYPE_F32, DTYPE_F16, DTYPE_BF16 = 0, 1, 2
 _DTYPES = {torch.float32: DTYPE_F32, torch.float16: DTYPE_F16, torch.bfloat16: DTYPE_BF16}
 BWD_REUSE_SNAPSHOTS = 1
 EXPORTS = ("gdn_workspace_size", "gdn_grad_packed_floats", "gdn_fwd", "gdn_bwd",
-           "gdn_status_string")
+           "gdn_ssm_conv_fwd", "gdn_ssm_conv_bwd", "gdn_status_string")
 
 
 class GdnError(RuntimeError):
@@ -59,6 +59,16 @@ lib.gdn_fwd.restype = ctypes.c_int
 lib.gdn_bwd.argtypes = [ctypes.POINTER(_Problem)] + [_VP] * 10 + [ctypes.c_size_t,
                                                                  ctypes.c_uint, _VP]
 lib.gdn_bwd.restype = ctypes.c_int
+class _ConvProblem(ctypes.Structure):
+    _fields_ = [("n_seqs", ctypes.c_int32), ("T", ctypes.c_int32), ("d_inner", ctypes.c_int32),
+                ("d_conv", ctypes.c_int32), ("sx_seq", ctypes.c_int64), ("sx_tok", ctypes.c_int64),
+                ("y_seq", ctypes.c_int64), ("y_tok", ctypes.c_int64)]
+
+
+for _f in (lib.gdn_ssm_conv_fwd, lib.gdn_ssm_conv_bwd):
+    _f.argtypes = [ctypes.POINTER(_ConvProblem), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                   ctypes.c_void_p]
+    _f.restype = ctypes.c_int
 lib.gdn_status_string.argtypes = [ctypes.c_int]
 lib.gdn_status_string.restype = ctypes.c_char_p
 
@@ -191,3 +201,41 @@ def bwd(p: Problem, q, k, v, g, beta, state0, gy, dstate_out, grad_packed, ws, f
                      ws.numel() * ws.element_size(), int(flags), _stream(stream))
     if rc != 0:
         raise GdnError(rc, "gdn_bwd")
+
+
+def conv_problem(n_seqs, T, d_inner, d_conv, sx_strides, y_strides) -> _ConvProblem:
+    """A gdn_conv_problem; strides are (seq, row) in floats (the channel stride is 1)."""
+    return _ConvProblem(n_seqs, T, d_inner, d_conv, sx_strides[0], sx_strides[1],
+                        y_strides[0], y_strides[1])
+
+
+def _taps(c):
+    if c.dim() != 2 or not c.is_contiguous():
+        raise ValueError("c: expected a contiguous [d_inner, d_conv] tensor")
+    return _ptr(c)
+
+
+def _rows(t, name):
+    if t.dim() == 3 and t.numel() == 0:
+        return (t.shape[1] * t.shape[2], t.shape[2])   # no element is addressed
+    if t.dim() != 3 or (t.shape[2] > 1 and t.stride(2) != 1):
+        raise ValueError(f"{name}: expected [n_seqs, rows, d_inner] with unit channel stride")
+    return (t.stride(0), t.stride(1))
+
+
+def ssm_conv_fwd(sx, c, y, stream=None):
+    """gdn_ssm_conv_fwd: y [n, T, D] from sx [n, d_conv - 1 + T, D] and taps c [D, d_conv]."""
+    n, D, K = sx.shape[0], sx.shape[2], c.shape[1]
+    p = conv_problem(n, y.shape[1], D, K, _rows(sx, "sx"), _rows(y, "y"))
+    rc = lib.gdn_ssm_conv_fwd(ctypes.byref(p), _ptr(sx), _taps(c), _ptr(y), _stream(stream))
+    if rc != 0:
+        raise GdnError(rc, "gdn_ssm_conv_fwd")
+
+
+def ssm_conv_bwd(dy, c, d_sx, stream=None):
+    """gdn_ssm_conv_bwd: d_sx [n, d_conv - 1 + T, D] from dy [n, T, D] and taps c [D, d_conv]."""
+    n, D, K = dy.shape[0], dy.shape[2], c.shape[1]
+    p = conv_problem(n, dy.shape[1], D, K, _rows(d_sx, "d_sx"), _rows(dy, "dy"))
+    rc = lib.gdn_ssm_conv_bwd(ctypes.byref(p), _ptr(dy), _taps(c), _ptr(d_sx), _stream(stream))
+    if rc != 0:
+        raise GdnError(rc, "gdn_ssm_conv_bwd")

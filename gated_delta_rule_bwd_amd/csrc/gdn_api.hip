@@ -170,6 +170,7 @@ bool non_self_overlapping(const gdn_strides &s, int64_t n, int64_t T, int64_t H,
     struct Dim {
         int64_t stride, extent;
     } d[3] = {{s.seq, n}, {s.tok, T}, {s.head, H}};
+    if (n <= 0 || T <= 0 || H <= 0 || W <= 0) return true;   // no element at all
     std::sort(d, d + 3, [](const Dim &x, const Dim &y) { return x.stride < y.stride; });
     int64_t span = W;  // innermost: W contiguous floats
     for (auto &x : d) {
@@ -490,6 +491,51 @@ int gdn_bwd(const gdn_problem *p, const void *q_in, const void *k_in, const void
         if (rc != GDN_OK) return rc;
     }
     return GDN_OK;
+}
+
+static int conv_check(const gdn_conv_problem *p, const void *in, const void *c, const void *out,
+                      bool bwd) {
+    if (!p) return GDN_ERR_ARG;
+    if (p->n_seqs < 0 || p->T < 0 || p->d_inner <= 0 || p->d_conv <= 0) return GDN_ERR_ARG;
+    if (p->d_conv > 8) return GDN_ERR_UNSUPPORTED;
+    if (p->sx_seq < 0 || p->sx_tok < 0 || p->y_seq < 0 || p->y_tok < 0) return GDN_ERR_UNSUPPORTED;
+    const int64_t n = p->n_seqs, D = p->d_inner, rows_sx = p->T + p->d_conv - 1;
+    // a tensor with no elements may be NULL: sx / d_sx has n rows_sx rows, y / dy n T rows
+    const bool need_in = n * (bwd ? p->T : rows_sx) > 0, need_out = n * (bwd ? rows_sx : p->T) > 0;
+    if ((need_in && !in) || !c || (need_out && !out)) return GDN_ERR_ARG;
+    if (!aligned4(in) || !aligned4(c) || !aligned4(out)) return GDN_ERR_UNSUPPORTED;
+    const gdn_strides ssx{p->sx_seq, p->sx_tok, 0}, sy{p->y_seq, p->y_tok, 0};
+    const Range rsx = span_tok(bwd ? out : in, ssx, n, rows_sx, 1, D);
+    const Range ry = span_tok(bwd ? in : out, sy, n, p->T, 1, D);
+    const Range rc = span_flat(c, D * p->d_conv);
+    const Range &ro = bwd ? rsx : ry, &ri = bwd ? ry : rsx;
+    if (overlap(ro, ri) || overlap(ro, rc)) return GDN_ERR_ARG;
+    if (!non_self_overlapping(bwd ? ssx : sy, n, bwd ? rows_sx : p->T, 1, D)) return GDN_ERR_ARG;
+    return GDN_OK;
+}
+
+int gdn_ssm_conv_fwd(const gdn_conv_problem *p, const float *sx, const float *c, float *y,
+                     gdn_stream_t stream) {
+    const int rc = conv_check(p, sx, c, y, false);
+    if (rc != GDN_OK) return rc;
+    gdn::ConvArgs a;
+    a.in = sx; a.w = c; a.out = y;
+    a.in_seq = p->sx_seq; a.in_tok = p->sx_tok; a.out_seq = p->y_seq; a.out_tok = p->y_tok;
+    a.n_seqs = p->n_seqs; a.rows_in = p->T + p->d_conv - 1; a.rows_out = p->T;
+    a.d_inner = p->d_inner; a.d_conv = p->d_conv;
+    return device_status(gdn::launch_conv(a, false, (hipStream_t)stream));
+}
+
+int gdn_ssm_conv_bwd(const gdn_conv_problem *p, const float *dy, const float *c, float *d_sx,
+                     gdn_stream_t stream) {
+    const int rc = conv_check(p, dy, c, d_sx, true);
+    if (rc != GDN_OK) return rc;
+    gdn::ConvArgs a;
+    a.in = dy; a.w = c; a.out = d_sx;
+    a.in_seq = p->y_seq; a.in_tok = p->y_tok; a.out_seq = p->sx_seq; a.out_tok = p->sx_tok;
+    a.n_seqs = p->n_seqs; a.rows_in = p->T; a.rows_out = p->T + p->d_conv - 1;
+    a.d_inner = p->d_inner; a.d_conv = p->d_conv;
+    return device_status(gdn::launch_conv(a, true, (hipStream_t)stream));
 }
 
 }  // extern "C"

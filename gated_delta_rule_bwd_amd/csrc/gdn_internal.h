@@ -96,6 +96,16 @@ struct WidenArgs {
 };
 
 hipError_t launch_widen(const WidenArgs &a, hipStream_t st);
+
+// Short causal depthwise convolution (forward) or its input gradient (backward), over
+// channel-innermost rows; in/out row counts and strides in floats (see ssm_conv.hip).
+struct ConvArgs {
+    const float *in, *w;   // input rows; taps [d_inner][d_conv]
+    float *out;
+    int64_t in_seq, in_tok, out_seq, out_tok;
+    int32_t n_seqs, rows_in, rows_out, d_inner, d_conv;
+};
+hipError_t launch_conv(const ConvArgs &a, bool bwd, hipStream_t st);
 // head sizes: key width SK and value width SV, each in {16, 32, 64, 128}, not both 128
 hipError_t launch_fwd(const FwdArgs &a, int SK, int SV, bool kda, int n_seqs_launch, hipStream_t st);
 hipError_t launch_bwd(const BwdArgs &a, int SK, int SV, bool kda, int n_seqs_launch, hipStream_t st);

@@ -234,3 +234,26 @@ def pack_qkv(w: Workload, q, k, v) -> np.ndarray:
     buf[:, :, HkS:2 * HkS] = k.reshape(n, T, -1)
     buf[:, :, 2 * HkS:] = v.reshape(n, T, -1)
     return buf
+
+
+# The short convolution feeding the layer shape's packed rows: 4 sequences x 4096 tokens,
+# d_inner = 2 H_k S + H_v S = 10240 channels, 4 taps (3 carried state rows per sequence).
+CONV_LAYER = {"name": "conv_layer_d10240_k4", "n_seqs": 4, "T": 4096, "d_inner": 10240,
+              "d_conv": 4, "seed": 1100}
+
+
+def make_conv(cfg: dict, seqs=None):
+    """Seeded inputs of the convolution, float32: sx [n, d_conv - 1 + T, D] and dy [n, T, D]
+    standard normal (one generator per sequence, so a sample of sequences is reproducible on
+    its own), taps c [D, d_conv] normal with variance 1 / d_conv."""
+    n, T, D, K, seed = cfg["n_seqs"], cfg["T"], cfg["d_inner"], cfg["d_conv"], cfg["seed"]
+    seqs = list(range(n)) if seqs is None else list(seqs)
+    sx = np.empty((len(seqs), T + K - 1, D), np.float32)
+    dy = np.empty((len(seqs), T, D), np.float32)
+    for i, s in enumerate(seqs):
+        r = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 1, s])))
+        sx[i] = r.standard_normal((T + K - 1, D), dtype=np.float32)
+        dy[i] = r.standard_normal((T, D), dtype=np.float32)
+    r = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 0])))
+    c = (r.standard_normal((D, K)) / np.sqrt(K)).astype(np.float32)
+    return sx, c, dy

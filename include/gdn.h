@@ -153,6 +153,31 @@ int gdn_bwd(const gdn_problem *p, const void *q, const void *k, const void *v,
             const float *dstate_out, float *grad_packed, void *ws, size_t ws_bytes,
             unsigned flags, gdn_stream_t stream);
 
+/* Short causal depthwise convolution upstream of the recurrence (the one that produces the
+ * mixed q/k/v rows) and its gradient with respect to the input; the weights are frozen and
+ * take no gradient (page "S1-24: chunked attention -- the kernel-free long-context path",
+ * the commit notes on SSM_CONV_BACK).  Channels are innermost:
+ *   sx, d_sx [n_seqs][d_conv - 1 + T][d_inner]  the d_conv - 1 carried state rows, then T
+ *   c        [d_inner][d_conv] (contiguous)
+ *   y, dy    [n_seqs][T][d_inner]
+ *   y[s][t][i]    = sum_j sx[s][t + j][i] c[i][j]              (j = 0 .. d_conv - 1)
+ *   d_sx[s][u][i] = sum_j dy[s][u - j][i] c[i][j]  over 0 <= u - j < T
+ * (the carried state rows get their gradient too).  Row strides are in floats; the channel
+ * stride is 1.  Supported: 1 <= d_conv <= 8.  Pointers are device pointers, 4-byte aligned;
+ * a tensor with no elements (n_seqs = 0, or no rows) may be NULL.  Outputs must not overlap
+ * inputs.  Results are deterministic (one owner per output, taps
+ * in increasing j).  Returns GDN_OK or an error code (nothing enqueued on error). */
+typedef struct gdn_conv_problem {
+    int32_t n_seqs, T, d_inner, d_conv;
+    int64_t sx_seq, sx_tok;   /* strides of sx and d_sx */
+    int64_t y_seq, y_tok;     /* strides of y and dy */
+} gdn_conv_problem;
+
+int gdn_ssm_conv_fwd(const gdn_conv_problem *p, const float *sx, const float *c, float *y,
+                     gdn_stream_t stream);
+int gdn_ssm_conv_bwd(const gdn_conv_problem *p, const float *dy, const float *c, float *d_sx,
+                     gdn_stream_t stream);
+
 /* Human-readable name of a status code. */
 const char *gdn_status_string(int status);
 

@@ -239,3 +239,43 @@ def test_half_inputs_workspace_and_alignment(B):
 def test_status_strings(B):
     for c in (0, -1, -2, -3, -4):
         assert B.lib.gdn_status_string(c)
+
+
+def _conv(B, fwd, n=2, T=16, D=8, K=4, sx_st=None, y_st=None, ptrs=None):
+    sx_st = sx_st or ((T + K - 1) * D, D)
+    y_st = y_st or (T * D, D)
+    p = B.conv_problem(n, T, D, K, sx_st, y_st)
+    a = ptrs or (1 << 32, 1 << 33, 1 << 34)
+    f = B.lib.gdn_ssm_conv_fwd if fwd else B.lib.gdn_ssm_conv_bwd
+    return f(ctypes.byref(p), *[ctypes.c_void_p(x) if x else None for x in a], None)
+
+
+def test_conv_argument_errors(B):
+    """The convolution entry points reject bad problems and pointers before any launch."""
+    for fwd in (True, False):
+        assert _conv(B, fwd, K=0) == -1
+        assert _conv(B, fwd, K=9) == -2
+        assert _conv(B, fwd, D=0) == -1
+        assert _conv(B, fwd, T=-1) == -1
+        assert _conv(B, fwd, sx_st=(-1, 8)) == -2
+        for i in range(3):
+            bad = [1 << 32, 1 << 33, 1 << 34]
+            bad[i] = 0
+            assert _conv(B, fwd, ptrs=bad) == -1
+            bad = [1 << 32, 1 << 33, 1 << 34]
+            bad[i] += 2
+            assert _conv(B, fwd, ptrs=bad) == -2
+        # the output overlapping the input, or the taps
+        assert _conv(B, fwd, ptrs=(1 << 32, 1 << 33, (1 << 32) + 64)) == -1
+        assert _conv(B, fwd, ptrs=(1 << 32, 1 << 33, (1 << 33) + 16)) == -1
+    # a tensor with no elements may be NULL (and nothing is launched when no output row
+    # exists); one that has elements may not
+    assert _conv(B, True, T=0, ptrs=(1 << 32, 1 << 33, 0)) == 0
+    assert _conv(B, True, n=0, ptrs=(0, 1 << 33, 0)) == 0
+    assert _conv(B, False, n=0, ptrs=(0, 1 << 33, 0)) == 0
+    assert _conv(B, True, T=0, ptrs=(0, 1 << 33, 1 << 34)) == -1     # 3 carried rows to read
+    assert _conv(B, False, T=0, ptrs=(1 << 32, 1 << 33, 0)) == -1    # 3 carried rows to write
+    # an output view whose rows overlap each other (row stride below the channel count):
+    # y in the forward, d_sx in the backward
+    assert _conv(B, True, y_st=(16 * 8, 4)) == -1
+    assert _conv(B, False, sx_st=(19 * 8, 4)) == -1
