@@ -34,9 +34,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--input-dtype", choices=("f32", "f16", "bf16"), default="f32",
                     help="element type of q, k, v, g, beta, gy (state and gradients stay fp32)")
-    ap.add_argument("--op", choices=("gdn", "ssm_conv"), default="gdn",
+    ap.add_argument("--op", choices=("gdn", "ssm_conv", "l2norm"), default="gdn",
                     help="gdn: the recurrence fwd+bwd (default); ssm_conv: the short "
-                         "convolution fwd+bwd on the layer shape's packed rows")
+                         "convolution fwd+bwd on the layer shape's packed rows; l2norm: the "
+                         "q/k row normalisation fwd+bwd on the same rows")
     ap.add_argument("--cpu-sample-heads", type=int, default=0,
                     help="key heads of sequence 0 in the oracle sample (0: auto)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -229,13 +230,83 @@ def bench_conv(args):
     print(json.dumps(out), flush=True)
 
 
+def bench_l2norm(args):
+    """The q/k row normalisation forward + backward (gdn_l2norm_fwd then gdn_l2norm_bwd) on
+    the layer shape: 4 x 4096 tokens, the 32 q and k heads of 128 at the start of each packed
+    [10240]-float token row; the cotangent and the outputs are contiguous.  Algorithmic bytes:
+    the forward reads x and writes y, the backward reads x and dy and writes dx, once each."""
+    import torch
+    from gated_delta_rule_bwd_amd import binding as B
+    n, T, H, W, eps = 4, 4096, 32, 128, 1e-6
+    dev = "cuda:0"
+    g = torch.Generator(device=dev)
+    g.manual_seed(1200)
+    buf = torch.randn((n, T, 10240), device=dev, generator=g)
+    x = buf[:, :, :H * W].unflatten(2, (H, W))
+    dy = torch.randn((n, T, H, W), device=dev, generator=g)
+    y = torch.empty_like(dy)
+    dx = torch.empty_like(dy)
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        B.l2norm_fwd(x, y, eps, stream)
+        B.l2norm_bwd(x, dy, dx, eps, stream)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for e0, e1, e2 in ev:
+        e0.record(stream)
+        B.l2norm_fwd(x, y, eps, stream)
+        e1.record(stream)
+        B.l2norm_bwd(x, dy, dx, eps, stream)
+        e2.record(stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    fwd_ms = sum(a.elapsed_time(b) for a, b, _ in ev) / args.steps
+    bwd_ms = sum(b.elapsed_time(e) for _, b, e in ev) / args.steps
+    tensor = n * T * H * W * 4
+    rows = n * T * H
+    out = {
+        "metric": "L2-norm (q/k rows) fwd+bwd rows/s; % HBM peak",
+        "value": rows / (ms / 1e3), "unit": "rows/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "l2norm_layer_qk_rows", "n_seqs": n, "T": T, "H": H, "W": W},
+        "fwd_ms": fwd_ms, "bwd_ms": bwd_ms,
+        "roofline": {"bound": "hbm", "kernel": "l2norm_kernel (backward launch)",
+                     "achieved": 3 * tensor / (bwd_ms / 1e3) / 1e9, "peak": PEAK_HBM / 1e9,
+                     "unit": "GB/s", "frac": 3 * tensor / (bwd_ms / 1e3) / PEAK_HBM,
+                     "traffic": None},
+        "fwd_GBps": 2 * tensor / (fwd_ms / 1e3) / 1e9,
+    }
+    if not args.no_cpu_baseline:
+        import oracle.l2norm as OL
+        xs = x[0].cpu().numpy()          # sample: sequence 0, all its rows
+        dys = dy[0].cpu().numpy()
+        t0 = time.perf_counter()
+        reps = 0
+        while True:
+            OL.l2norm_fwd(xs, eps)
+            OL.l2norm_bwd(xs, dys, eps)
+            reps += 1
+            dt = time.perf_counter() - t0
+            if dt > 10.0:
+                break
+        out["cpu_baseline"] = {"value": reps * T * H / dt, "unit": "rows/s", "cores": 1,
+                               "kind": "oracle",
+                               "sample": f"sequence 0 ({T} tokens x {H} heads of {W}), fp64 "
+                                         f"fwd+bwd, {reps} repetitions in {dt:.1f} s"}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
-    if args.op == "ssm_conv" and not (args.pmc_summary or args.copy_calibration):
+    if args.op != "gdn" and not (args.pmc_summary or args.copy_calibration):
         if args.gpus != 1:
             print("bench.py runs on one GPU only", file=sys.stderr)
             sys.exit(2)
-        bench_conv(args)
+        (bench_conv if args.op == "ssm_conv" else bench_l2norm)(args)
         return
     if args.pmc_summary:
         summ = pmc_summary(args.pmc_summary)

@@ -26,7 +26,8 @@ DTYPE_F32, DTYPE_F16, DTYPE_BF16 = 0, 1, 2
 _DTYPES = {torch.float32: DTYPE_F32, torch.float16: DTYPE_F16, torch.bfloat16: DTYPE_BF16}
 BWD_REUSE_SNAPSHOTS = 1
 EXPORTS = ("gdn_workspace_size", "gdn_grad_packed_floats", "gdn_fwd", "gdn_bwd",
-           "gdn_ssm_conv_fwd", "gdn_ssm_conv_bwd", "gdn_status_string")
+           "gdn_ssm_conv_fwd", "gdn_ssm_conv_bwd", "gdn_l2norm_fwd", "gdn_l2norm_bwd",
+           "gdn_status_string")
 
 
 class GdnError(RuntimeError):
@@ -69,6 +70,20 @@ for _f in (lib.gdn_ssm_conv_fwd, lib.gdn_ssm_conv_bwd):
     _f.argtypes = [ctypes.POINTER(_ConvProblem), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                    ctypes.c_void_p]
     _f.restype = ctypes.c_int
+
+
+class _L2Problem(ctypes.Structure):
+    _fields_ = [("n_seqs", ctypes.c_int32), ("T", ctypes.c_int32), ("H", ctypes.c_int32),
+                ("W", ctypes.c_int32), ("eps", ctypes.c_float), ("x", _Strides), ("dy", _Strides),
+                ("out", _Strides)]
+
+
+lib.gdn_l2norm_fwd.argtypes = [ctypes.POINTER(_L2Problem), ctypes.c_void_p, ctypes.c_void_p,
+                               ctypes.c_void_p]
+lib.gdn_l2norm_fwd.restype = ctypes.c_int
+lib.gdn_l2norm_bwd.argtypes = [ctypes.POINTER(_L2Problem), ctypes.c_void_p, ctypes.c_void_p,
+                               ctypes.c_void_p, ctypes.c_void_p]
+lib.gdn_l2norm_bwd.restype = ctypes.c_int
 lib.gdn_status_string.argtypes = [ctypes.c_int]
 lib.gdn_status_string.restype = ctypes.c_char_p
 
@@ -239,3 +254,41 @@ def ssm_conv_bwd(dy, c, d_sx, stream=None):
     rc = lib.gdn_ssm_conv_bwd(ctypes.byref(p), _ptr(dy), _taps(c), _ptr(d_sx), _stream(stream))
     if rc != 0:
         raise GdnError(rc, "gdn_ssm_conv_bwd")
+
+
+def _head_rows(t, name):
+    """(seq, tok, head) strides of a [n, T, H, W] tensor with unit innermost stride."""
+    if t.dim() != 4:
+        raise ValueError(f"{name}: expected [n_seqs, T, H, W], got {tuple(t.shape)}")
+    if t.numel() == 0:
+        return (0, 0, 0)
+    if t.shape[3] > 1 and t.stride(3) != 1:
+        raise ValueError(f"{name}: innermost stride must be 1")
+    return tuple(int(x) for x in t.stride()[:3])
+
+
+def l2norm_problem(x, eps, dy=None, out=None) -> _L2Problem:
+    n, T, H, W = (int(v) for v in x.shape)
+    return _L2Problem(n, T, H, W, eps, _Strides(*_head_rows(x, "x")),
+                      _Strides(*(_head_rows(dy, "dy") if dy is not None else (0, 0, 0))),
+                      _Strides(*(_head_rows(out, "out") if out is not None else (0, 0, 0))))
+
+
+def l2norm_fwd(x, y, eps=1e-6, stream=None):
+    """gdn_l2norm_fwd: y = x / sqrt(sum x^2 + eps) per row of [n, T, H, W] views."""
+    if tuple(y.shape) != tuple(x.shape):
+        raise ValueError("y must have the shape of x")
+    p = l2norm_problem(x, eps, out=y)
+    rc = lib.gdn_l2norm_fwd(ctypes.byref(p), _ptr(x), _ptr(y), _stream(stream))
+    if rc != 0:
+        raise GdnError(rc, "gdn_l2norm_fwd")
+
+
+def l2norm_bwd(x, dy, dx, eps=1e-6, stream=None):
+    """gdn_l2norm_bwd: dx = dy / n - x (x . dy) / n^3 per row, n = sqrt(sum x^2 + eps)."""
+    if tuple(dy.shape) != tuple(x.shape) or tuple(dx.shape) != tuple(x.shape):
+        raise ValueError("dy and dx must have the shape of x")
+    p = l2norm_problem(x, eps, dy=dy, out=dx)
+    rc = lib.gdn_l2norm_bwd(ctypes.byref(p), _ptr(x), _ptr(dy), _ptr(dx), _stream(stream))
+    if rc != 0:
+        raise GdnError(rc, "gdn_l2norm_bwd")

@@ -538,4 +538,51 @@ int gdn_ssm_conv_bwd(const gdn_conv_problem *p, const float *dy, const float *c,
     return device_status(gdn::launch_conv(a, true, (hipStream_t)stream));
 }
 
+static bool same_view(const void *a, const gdn_strides &sa, const void *b, const gdn_strides &sb) {
+    return a == b && sa.seq == sb.seq && sa.tok == sb.tok && sa.head == sb.head;
+}
+
+static int l2norm_check(const gdn_l2norm_problem *p, const float *x, const float *dy,
+                        const float *out, bool bwd) {
+    if (!p) return GDN_ERR_ARG;
+    if (p->n_seqs < 0 || p->T < 0 || p->H < 0 || p->W <= 0) return GDN_ERR_ARG;
+    if (p->W > 1024) return GDN_ERR_UNSUPPORTED;
+    if (!(p->eps >= 0.f) || !std::isfinite(p->eps)) return GDN_ERR_ARG;
+    const gdn_strides *ss[3] = {&p->x, &p->dy, &p->out};
+    for (int i = 0; i < 3; ++i) {
+        if (i == 1 && !bwd) continue;
+        if (ss[i]->seq < 0 || ss[i]->tok < 0 || ss[i]->head < 0) return GDN_ERR_UNSUPPORTED;
+    }
+    const int64_t n = p->n_seqs, T = p->T, H = p->H, W = p->W;
+    const bool any = n * T * H > 0;
+    if (any && (!x || !out || (bwd && !dy))) return GDN_ERR_ARG;
+    if (!aligned4(x) || !aligned4(out) || (bwd && !aligned4(dy))) return GDN_ERR_UNSUPPORTED;
+    if (!non_self_overlapping(p->out, n, T, H, W)) return GDN_ERR_ARG;
+    const Range ro = span_tok(out, p->out, n, T, H, W);
+    if (!same_view(out, p->out, x, p->x) && overlap(ro, span_tok(x, p->x, n, T, H, W))) return GDN_ERR_ARG;
+    if (bwd && !same_view(out, p->out, dy, p->dy) && overlap(ro, span_tok(dy, p->dy, n, T, H, W)))
+        return GDN_ERR_ARG;
+    return GDN_OK;
+}
+
+static int l2norm_run(const gdn_l2norm_problem *p, const float *x, const float *dy, float *out,
+                      bool bwd, gdn_stream_t stream) {
+    const int rc = l2norm_check(p, x, dy, out, bwd);
+    if (rc != GDN_OK) return rc;
+    gdn::NormArgs a;
+    a.x = x; a.dy = bwd ? dy : nullptr; a.out = out;
+    a.sx = p->x; a.sdy = bwd ? p->dy : gdn_strides{0, 0, 0}; a.so = p->out;
+    a.n_seqs = p->n_seqs; a.T = p->T; a.H = p->H; a.W = p->W; a.eps = p->eps;
+    return device_status(gdn::launch_l2norm(a, bwd, (hipStream_t)stream));
+}
+
+int gdn_l2norm_fwd(const gdn_l2norm_problem *p, const float *x, float *y, gdn_stream_t stream) {
+    return l2norm_run(p, x, nullptr, y, false, stream);
+}
+
+int gdn_l2norm_bwd(const gdn_l2norm_problem *p, const float *x, const float *dy, float *dx,
+                   gdn_stream_t stream) {
+    return l2norm_run(p, x, dy, dx, true, stream);
+}
+
 }  // extern "C"

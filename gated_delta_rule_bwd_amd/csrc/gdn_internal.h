@@ -106,6 +106,17 @@ struct ConvArgs {
     int32_t n_seqs, rows_in, rows_out, d_inner, d_conv;
 };
 hipError_t launch_conv(const ConvArgs &a, bool bwd, hipStream_t st);
+
+// L2 normalisation of rows [n_seqs][T][H] of W floats (forward: out = x / n) or its backward
+// (out = dy / n - x (x . dy) / n^3), n = sqrt(sum x^2 + eps); 1 <= W <= 1024 (see l2norm.hip).
+struct NormArgs {
+    const float *x, *dy;   // dy: backward only
+    float *out;
+    gdn_strides sx, sdy, so;
+    int32_t n_seqs, T, H, W;
+    float eps;
+};
+hipError_t launch_l2norm(const NormArgs &a, bool bwd, hipStream_t st);
 // head sizes: key width SK and value width SV, each in {16, 32, 64, 128}, not both 128
 hipError_t launch_fwd(const FwdArgs &a, int SK, int SV, bool kda, int n_seqs_launch, hipStream_t st);
 hipError_t launch_bwd(const BwdArgs &a, int SK, int SV, bool kda, int n_seqs_launch, hipStream_t st);

@@ -178,6 +178,31 @@ int gdn_ssm_conv_fwd(const gdn_conv_problem *p, const float *sx, const float *c,
 int gdn_ssm_conv_bwd(const gdn_conv_problem *p, const float *dy, const float *c, float *d_sx,
                      gdn_stream_t stream);
 
+/* L2 normalisation of the q and k rows between the short convolution and the recurrence, and
+ * its backward (meTile, "Training kernels and gradients", section "Recurrent delta attention":
+ * normalisation is a step of its own, outside the recurrence kernel).  Each row of W floats
+ * (one token of one head) maps to
+ *   n = sqrt(sum_i x_i^2 + eps),  y = x / n,
+ * and the backward takes the cotangent dy of y to
+ *   dx = dy / n - x (x . dy) / n^3.
+ * Rows are [n_seqs][T][H]; each tensor has its own (seq, tok, head) strides in floats and unit
+ * innermost stride, so q and k may be row views of the mixed rows and dx may be written into a
+ * view of their gradient.  Supported: 1 <= W <= 1024, eps >= 0 and finite (eps = 0 maps an
+ * all-zero row to non-finite values, as the formula does).  Pointers are device pointers,
+ * 4-byte aligned; a tensor with no rows may be NULL.  The output may be the very same view as
+ * an input (same pointer, same strides: in place) and must not otherwise overlap one, nor
+ * overlap itself.  Deterministic.  Returns GDN_OK or an error code (nothing enqueued on
+ * error). */
+typedef struct gdn_l2norm_problem {
+    int32_t n_seqs, T, H, W;
+    float eps;
+    gdn_strides x, dy, out;   /* dy: backward only */
+} gdn_l2norm_problem;
+
+int gdn_l2norm_fwd(const gdn_l2norm_problem *p, const float *x, float *y, gdn_stream_t stream);
+int gdn_l2norm_bwd(const gdn_l2norm_problem *p, const float *x, const float *dy, float *dx,
+                   gdn_stream_t stream);
+
 /* Human-readable name of a status code. */
 const char *gdn_status_string(int status);
 

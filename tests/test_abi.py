@@ -20,7 +20,7 @@ def B():
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(gdn_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(gdn_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_exports_every_declared_symbol(B):
@@ -279,3 +279,42 @@ def test_conv_argument_errors(B):
     # y in the forward, d_sx in the backward
     assert _conv(B, True, y_st=(16 * 8, 4)) == -1
     assert _conv(B, False, sx_st=(19 * 8, 4)) == -1
+
+
+def _l2(B, bwd, n=2, T=8, H=3, W=16, eps=1e-6, st=None, ptrs=None):
+    """One l2norm call with fake device addresses; st = (x, dy, out) stride triples."""
+    dense = (T * H * W, H * W, W)
+    sx, sdy, so = st or (dense, dense, dense)
+    p = B._L2Problem(n, T, H, W, eps, B._Strides(*sx), B._Strides(*sdy), B._Strides(*so))
+    a = ptrs or (1 << 32, 1 << 33, 1 << 34)
+    args = [ctypes.c_void_p(x) if x else None for x in a]
+    if bwd:
+        return B.lib.gdn_l2norm_bwd(ctypes.byref(p), args[0], args[1], args[2], None)
+    return B.lib.gdn_l2norm_fwd(ctypes.byref(p), args[0], args[2], None)
+
+
+def test_l2norm_argument_errors(B):
+    """The normalisation entry points reject bad problems, pointers and overlaps before any
+    launch; every call here fails validation."""
+    dense = (8 * 3 * 16, 3 * 16, 16)
+    for bwd in (False, True):
+        assert _l2(B, bwd, W=0) == -1
+        assert _l2(B, bwd, W=1025) == -2
+        assert _l2(B, bwd, T=-1) == -1
+        assert _l2(B, bwd, eps=-1.0) == -1
+        assert _l2(B, bwd, eps=float("nan")) == -1
+        assert _l2(B, bwd, eps=float("inf")) == -1
+        assert _l2(B, bwd, st=((-1, 48, 16), dense, dense)) == -2
+        assert _l2(B, bwd, ptrs=(0, 1 << 33, 1 << 34)) == -1            # x missing
+        assert _l2(B, bwd, ptrs=(1 << 32, 1 << 33, 0)) == -1            # out missing
+        assert _l2(B, bwd, ptrs=((1 << 32) + 2, 1 << 33, 1 << 34)) == -2
+        # out overlapping x without being the same view
+        assert _l2(B, bwd, ptrs=(1 << 32, 1 << 33, (1 << 32) + 64)) == -1
+        assert _l2(B, bwd, st=(dense, dense, (48, 16, 16)), ptrs=(1 << 32, 1 << 33, 1 << 32)) == -1
+        # out overlapping itself (head stride below the row width)
+        assert _l2(B, bwd, st=(dense, dense, (8 * 3 * 8, 3 * 8, 8))) == -1
+    assert _l2(B, True, ptrs=(1 << 32, 0, 1 << 34)) == -1               # dy missing
+    assert _l2(B, True, ptrs=(1 << 32, 1 << 33, (1 << 33) + 32)) == -1  # out overlapping dy
+    # no rows: NULL pointers are fine and nothing is launched
+    assert _l2(B, False, T=0, ptrs=(0, 0, 0)) == 0
+    assert _l2(B, True, n=0, ptrs=(0, 0, 0)) == 0
