@@ -14,6 +14,8 @@ from __future__ import annotations
 
 import argparse
 import json
+
+import numpy as np
 import os
 import sys
 import time
@@ -34,10 +36,12 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--input-dtype", choices=("f32", "f16", "bf16"), default="f32",
                     help="element type of q, k, v, g, beta, gy (state and gradients stay fp32)")
-    ap.add_argument("--op", choices=("gdn", "ssm_conv", "l2norm"), default="gdn",
+    ap.add_argument("--op", choices=("gdn", "ssm_conv", "l2norm", "ssm_scan"), default="gdn",
                     help="gdn: the recurrence fwd+bwd (default); ssm_conv: the short "
                          "convolution fwd+bwd on the layer shape's packed rows; l2norm: the "
-                         "q/k row normalisation fwd+bwd on the same rows")
+                         "q/k row normalisation fwd+bwd on the same rows; ssm_scan: the "
+                         "selective scan fwd+bwd (--workload ssm2_layer_h80_p64_n128 or "
+                         "ssm1_layer_d5120_n16)")
     ap.add_argument("--cpu-sample-heads", type=int, default=0,
                     help="key heads of sequence 0 in the oracle sample (0: auto)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -300,13 +304,95 @@ def bench_l2norm(args):
     print(json.dumps(out), flush=True)
 
 
+def bench_ssm(args):
+    """The selective scan forward + backward (gdn_ssm_fwd, then gdn_ssm_bwd reusing its window
+    states) on a layer-sized workload.  Credited work per token x state element: forward 5
+    flops (decay, input, readout), backward 12 (window replay 3, reverse walk 9)."""
+    import torch
+    from gated_delta_rule_bwd_amd import binding as B
+    from gated_delta_rule_bwd_amd import inputs as I
+    name = args.workload or "ssm2_layer_h80_p64_n128"
+    cfg = I.SSM_WORKLOADS[name]
+    arr = I.make_ssm(cfg)
+    dev = "cuda:0"
+    g = {k: torch.from_numpy(np.ascontiguousarray(v)).to(dev) for k, v in arr.items()}
+    del arr
+    p = B.ssm_problem_from(g["x"], g["B"], g["A"], True)
+    ws = torch.empty(max(B.ssm_workspace_size(p), 16) // 4, dtype=torch.float32, device=dev)
+    y = torch.empty_like(g["x"])
+    s_out = torch.empty_like(g["s0"])
+    total, _ = B.ssm_grad_layout(p)
+    gp = torch.empty(total, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def fwd():
+        B.ssm_fwd(p, g["s0"], g["x"], g["dt"], g["A"], g["B"], g["C"], y, s_out, ws, stream)
+
+    def bwd():
+        B.ssm_bwd(p, g["s0"], g["x"], g["dt"], g["A"], g["B"], g["C"], g["gy"], g["gs"], gp, ws,
+                  flags=B.BWD_REUSE_SNAPSHOTS, stream=stream)
+
+    for _ in range(args.warmup):
+        fwd()
+        bwd()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for e0, e1, e2 in ev:
+        e0.record(stream)
+        fwd()
+        e1.record(stream)
+        bwd()
+        e2.record(stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    fwd_ms = sum(a.elapsed_time(b) for a, b, _ in ev) / args.steps
+    bwd_ms = sum(b.elapsed_time(e) for _, b, e in ev) / args.steps
+    n, T, H, P, N = (cfg[k] for k in ("n_seqs", "T", "H", "P", "N"))
+    elems = n * T * H * P * N                     # token x state-element steps
+    bwd_flops = 12 * elems
+    out = {
+        "metric": "SSM_SCAN fwd+bwd token·state-element steps/s; % FP32 VALU peak",
+        "value": elems / (ms / 1e3), "unit": "token·state-elements/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": name, **{k: cfg[k] for k in ("n_seqs", "T", "H", "P", "N", "G",
+                                                             "a_per_state")}},
+        "fwd_ms": fwd_ms, "bwd_ms": bwd_ms,
+        "pct_fp32_valu_peak": 100.0 * 17 * elems / (ms / 1e3) / PEAK_FP32_VALU,
+        "roofline": {"bound": "alu", "kernel": "gdn_ssm_bwd (ssm_bwd_kernel + ssm_combine_kernel)",
+                     "achieved": bwd_flops / (bwd_ms / 1e3) / 1e12, "peak": PEAK_FP32_VALU / 1e12,
+                     "unit": "TFLOP/s", "frac": bwd_flops / (bwd_ms / 1e3) / PEAK_FP32_VALU,
+                     "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        import oracle.ssm_scan as OS
+        a = I.make_ssm(cfg)
+        hs = 1 if cfg["P"] > 1 else 64           # sample: sequence 0, the first hs heads
+        sub = {"s0": a["s0"][:1, :hs], "x": a["x"][:1, :, :hs], "dt": a["dt"][:1, :, :hs],
+               "A": a["A"][:hs], "B": a["B"][:1], "C": a["C"][:1], "gy": a["gy"][:1, :, :hs],
+               "gs": a["gs"][:1, :hs]}
+        t0 = time.perf_counter()
+        OS.ssm_fwd(sub["s0"], sub["x"], sub["dt"], sub["A"], sub["B"], sub["C"])
+        OS.ssm_bwd(sub["s0"], sub["x"], sub["dt"], sub["A"], sub["B"], sub["C"], sub["gy"], sub["gs"])
+        dt_s = time.perf_counter() - t0
+        se = T * hs * P * N
+        out["cpu_baseline"] = {"value": se / dt_s, "unit": "token·state-elements/s", "cores": 1,
+                               "kind": "oracle",
+                               "sample": f"sequence 0, heads 0..{hs - 1} ({T} tokens, {se} "
+                                         f"token·state-elements), fp64 fwd+bwd, {dt_s:.1f} s"}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.op != "gdn" and not (args.pmc_summary or args.copy_calibration):
         if args.gpus != 1:
             print("bench.py runs on one GPU only", file=sys.stderr)
             sys.exit(2)
-        (bench_conv if args.op == "ssm_conv" else bench_l2norm)(args)
+        {"ssm_conv": bench_conv, "l2norm": bench_l2norm, "ssm_scan": bench_ssm}[args.op](args)
         return
     if args.pmc_summary:
         summ = pmc_summary(args.pmc_summary)

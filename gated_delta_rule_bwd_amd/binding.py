@@ -27,6 +27,7 @@ _DTYPES = {torch.float32: DTYPE_F32, torch.float16: DTYPE_F16, torch.bfloat16: D
 BWD_REUSE_SNAPSHOTS = 1
 EXPORTS = ("gdn_workspace_size", "gdn_grad_packed_floats", "gdn_fwd", "gdn_bwd",
            "gdn_ssm_conv_fwd", "gdn_ssm_conv_bwd", "gdn_l2norm_fwd", "gdn_l2norm_bwd",
+           "gdn_ssm_workspace_size", "gdn_ssm_grad_packed_floats", "gdn_ssm_fwd", "gdn_ssm_bwd",
            "gdn_status_string")
 
 
@@ -84,6 +85,23 @@ lib.gdn_l2norm_fwd.restype = ctypes.c_int
 lib.gdn_l2norm_bwd.argtypes = [ctypes.POINTER(_L2Problem), ctypes.c_void_p, ctypes.c_void_p,
                                ctypes.c_void_p, ctypes.c_void_p]
 lib.gdn_l2norm_bwd.restype = ctypes.c_int
+
+
+class _SsmProblem(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("n_seqs", "T", "H", "P", "N", "G", "a_per_state",
+                                               "dt_softplus")]
+
+
+lib.gdn_ssm_workspace_size.argtypes = [ctypes.POINTER(_SsmProblem)]
+lib.gdn_ssm_workspace_size.restype = ctypes.c_size_t
+lib.gdn_ssm_grad_packed_floats.argtypes = [ctypes.POINTER(_SsmProblem), ctypes.POINTER(ctypes.c_size_t)]
+lib.gdn_ssm_grad_packed_floats.restype = ctypes.c_size_t
+lib.gdn_ssm_fwd.argtypes = [ctypes.POINTER(_SsmProblem)] + [ctypes.c_void_p] * 9 + [ctypes.c_size_t,
+                                                                                   ctypes.c_void_p]
+lib.gdn_ssm_fwd.restype = ctypes.c_int
+lib.gdn_ssm_bwd.argtypes = [ctypes.POINTER(_SsmProblem)] + [ctypes.c_void_p] * 10 + [
+    ctypes.c_size_t, ctypes.c_uint, ctypes.c_void_p]
+lib.gdn_ssm_bwd.restype = ctypes.c_int
 lib.gdn_status_string.argtypes = [ctypes.c_int]
 lib.gdn_status_string.restype = ctypes.c_char_p
 
@@ -292,3 +310,54 @@ def l2norm_bwd(x, dy, dx, eps=1e-6, stream=None):
     rc = lib.gdn_l2norm_bwd(ctypes.byref(p), _ptr(x), _ptr(dy), _ptr(dx), _stream(stream))
     if rc != 0:
         raise GdnError(rc, "gdn_l2norm_bwd")
+
+
+def ssm_problem(n_seqs, T, H, P, N, G, a_per_state, dt_softplus=True) -> _SsmProblem:
+    return _SsmProblem(n_seqs, T, H, P, N, G, int(a_per_state), int(dt_softplus))
+
+
+def ssm_problem_from(x, B, A, dt_softplus=True) -> _SsmProblem:
+    """The problem of contiguous x [n, T, H, P], B [n, T, G, N] and A ([H, N] or [H])."""
+    n, T, H, P = (int(v) for v in x.shape)
+    G, N = int(B.shape[2]), int(B.shape[3])
+    return ssm_problem(n, T, H, P, N, G, A.dim() == 2, dt_softplus)
+
+
+def ssm_workspace_size(p: _SsmProblem) -> int:
+    return int(lib.gdn_ssm_workspace_size(ctypes.byref(p)))
+
+
+def ssm_grad_layout(p: _SsmProblem):
+    """(total floats, {name: (offset, shape)}) of [d_s | d_x | d_dt | d_B | d_C]."""
+    off = (ctypes.c_size_t * 5)()
+    total = lib.gdn_ssm_grad_packed_floats(ctypes.byref(p), off)
+    n, T, H, P, N, G = p.n_seqs, p.T, p.H, p.P, p.N, p.G
+    shapes = {"ds": (n, H, P, N), "dx": (n, T, H, P), "ddt": (n, T, H), "dB": (n, T, G, N),
+              "dC": (n, T, G, N)}
+    return int(total), {k: (int(off[i]), shp) for i, (k, shp) in enumerate(shapes.items())}
+
+
+def _contig(*ts):
+    for t in ts:
+        if t is not None and not t.is_contiguous():
+            raise ValueError("the scan takes contiguous tensors")
+
+
+def ssm_fwd(p: _SsmProblem, s0, x, dt, A, B, C, y, s_out, ws, stream=None):
+    _contig(s0, x, dt, A, B, C, y, s_out)
+    rc = lib.gdn_ssm_fwd(ctypes.byref(p), _ptr(s0), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C),
+                         _ptr(y), _ptr(s_out), _ptr(ws), ws.numel() * ws.element_size(),
+                         _stream(stream))
+    if rc != 0:
+        raise GdnError(rc, "gdn_ssm_fwd")
+
+
+def ssm_bwd(p: _SsmProblem, s0, x, dt, A, B, C, gy, gs_final, grad_packed, ws, flags=0,
+            stream=None):
+    _contig(s0, x, dt, A, B, C, gy, gs_final, grad_packed)
+    rc = lib.gdn_ssm_bwd(ctypes.byref(p), _ptr(s0), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C),
+                         _ptr(gy), _ptr(gs_final) if gs_final is not None else None,
+                         _ptr(grad_packed), _ptr(ws), ws.numel() * ws.element_size(), flags,
+                         _stream(stream))
+    if rc != 0:
+        raise GdnError(rc, "gdn_ssm_bwd")

@@ -585,4 +585,147 @@ int gdn_l2norm_bwd(const gdn_l2norm_problem *p, const float *x, const float *dy,
     return l2norm_run(p, x, dy, dx, true, stream);
 }
 
+// ---- selective scan ----------------------------------------------------------------------
+
+struct SsmPlan {
+    size_t off_step, off_ck, off_part, off_dd, total;
+    int64_t rows, nwin;
+};
+
+static int ssm_validate(const gdn_ssm_problem *p) {
+    if (!p) return GDN_ERR_ARG;
+    if (p->n_seqs < 0 || p->T < 0 || p->H < 1 || p->P < 1 || p->N < 1 || p->G < 1) return GDN_ERR_ARG;
+    if (p->H % p->G != 0) return GDN_ERR_ARG;
+    if ((p->a_per_state != 0 && p->a_per_state != 1) || (p->dt_softplus != 0 && p->dt_softplus != 1))
+        return GDN_ERR_ARG;
+    if (p->N != 16 && p->N != 32 && p->N != 64 && p->N != 128) return GDN_ERR_UNSUPPORTED;
+    if ((int64_t)p->P * (p->H / p->G) % 16 != 0) return GDN_ERR_UNSUPPORTED;
+    return GDN_OK;
+}
+
+static SsmPlan ssm_plan(const gdn_ssm_problem *p) {
+    SsmPlan pl;
+    const size_t n = p->n_seqs, T = p->T, H = p->H, P = p->P, N = p->N;
+    pl.rows = (int64_t)(n * H * P);
+    pl.nwin = (p->T + 7) / 8;
+    size_t off = 0;
+    pl.off_step = off; off += align_up(n * T * H * 4);
+    pl.off_ck = off;   off += align_up((size_t)pl.rows * pl.nwin * N * 4);
+    pl.off_part = off; off += align_up((size_t)pl.rows / 16 * T * 2 * N * 4);
+    pl.off_dd = off;   off += align_up(n * T * H * P * 4);
+    pl.total = off;
+    return pl;
+}
+
+static bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+size_t gdn_ssm_workspace_size(const gdn_ssm_problem *p) {
+    if (ssm_validate(p) != GDN_OK) return 0;
+    return ssm_plan(p).total;
+}
+
+size_t gdn_ssm_grad_packed_floats(const gdn_ssm_problem *p, size_t offsets[5]) {
+    if (ssm_validate(p) != GDN_OK) return 0;
+    const size_t n = p->n_seqs, T = p->T, H = p->H, P = p->P, N = p->N, G = p->G;
+    const size_t sizes[5] = {n * H * P * N, n * T * H * P, n * T * H, n * T * G * N, n * T * G * N};
+    size_t off = 0;
+    for (int i = 0; i < 5; ++i) {
+        if (offsets) offsets[i] = off;
+        off += sizes[i];
+    }
+    return off;
+}
+
+// Pointer and overlap checks shared by both directions: ins[] are read, outs[] written.
+static int ssm_check_ptrs(const gdn_ssm_problem *p, const float *s0, const float *x, const float *dt,
+                          const float *A, const float *B, const float *C, const Range *extra_in,
+                          int n_extra_in, const Range *outs, int n_outs) {
+    const int64_t n = p->n_seqs, T = p->T, H = p->H, P = p->P, N = p->N, G = p->G;
+    const bool any_state = n > 0, any_tok = n * T > 0;
+    if ((any_state && !s0) || !A || (any_tok && (!x || !dt || !B || !C))) return GDN_ERR_ARG;
+    if (!aligned16(s0) || !aligned16(A) || !aligned16(B) || !aligned16(C)) return GDN_ERR_UNSUPPORTED;
+    if (!aligned4(x) || !aligned4(dt)) return GDN_ERR_UNSUPPORTED;
+    const Range in[] = {span_flat(s0, n * H * P * N), span_flat(x, n * T * H * P), span_flat(dt, n * T * H),
+                        span_flat(A, p->a_per_state ? H * N : H), span_flat(B, n * T * G * N),
+                        span_flat(C, n * T * G * N)};
+    for (int o = 0; o < n_outs; ++o) {
+        for (auto &i : in)
+            if (overlap(outs[o], i)) return GDN_ERR_ARG;
+        for (int e = 0; e < n_extra_in; ++e)
+            if (overlap(outs[o], extra_in[e])) return GDN_ERR_ARG;
+        for (int q = o + 1; q < n_outs; ++q)
+            if (overlap(outs[o], outs[q])) return GDN_ERR_ARG;
+    }
+    return GDN_OK;
+}
+
+static gdn::SsmArgs ssm_args(const gdn_ssm_problem *p, const SsmPlan &pl, void *ws, const float *s0,
+                             const float *x, const float *dt, const float *A, const float *B,
+                             const float *C) {
+    gdn::SsmArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.s0 = s0; a.x = x; a.dt = dt; a.A = A; a.B = B; a.C = C;
+    char *w = (char *)ws;
+    a.dstep = (float *)(w + pl.off_step);
+    a.ck = (float *)(w + pl.off_ck);
+    a.part = (float *)(w + pl.off_part);
+    a.ddrow = (float *)(w + pl.off_dd);
+    a.n_seqs = p->n_seqs; a.T = p->T; a.H = p->H; a.P = p->P; a.N = p->N; a.G = p->G;
+    a.aps = p->a_per_state; a.softplus = p->dt_softplus;
+    return a;
+}
+
+int gdn_ssm_fwd(const gdn_ssm_problem *p, const float *s0, const float *x, const float *dt,
+                const float *A, const float *B, const float *C, float *y, float *s_out,
+                void *ws, size_t ws_bytes, gdn_stream_t stream) {
+    int rc = ssm_validate(p);
+    if (rc != GDN_OK) return rc;
+    const SsmPlan pl = ssm_plan(p);
+    const int64_t n = p->n_seqs, T = p->T, H = p->H, P = p->P, N = p->N;
+    if ((n * T > 0 && !y) || (n > 0 && !s_out) || (pl.total > 0 && !ws)) return GDN_ERR_ARG;
+    if (!aligned4(y) || !aligned16(s_out) || !aligned16(ws)) return GDN_ERR_UNSUPPORTED;
+    if (ws_bytes < pl.total) return GDN_ERR_WORKSPACE;
+    const Range outs[] = {span_flat(y, n * T * H * P), span_flat(s_out, n * H * P * N), span_bytes(ws, pl.total)};
+    rc = ssm_check_ptrs(p, s0, x, dt, A, B, C, nullptr, 0, outs, 3);
+    if (rc != GDN_OK) return rc;
+    gdn::SsmArgs a = ssm_args(p, pl, ws, s0, x, dt, A, B, C);
+    a.y = y; a.s_out = s_out;
+    hipError_t e = gdn::launch_ssm_step(a, (hipStream_t)stream);
+    if (e == hipSuccess) e = gdn::launch_ssm(a, false, (hipStream_t)stream);
+    return device_status(e);
+}
+
+int gdn_ssm_bwd(const gdn_ssm_problem *p, const float *s0, const float *x, const float *dt,
+                const float *A, const float *B, const float *C, const float *gy,
+                const float *gs_final, float *grad_packed, void *ws, size_t ws_bytes,
+                unsigned flags, gdn_stream_t stream) {
+    int rc = ssm_validate(p);
+    if (rc != GDN_OK) return rc;
+    if (flags & ~GDN_BWD_REUSE_SNAPSHOTS) return GDN_ERR_ARG;
+    const SsmPlan pl = ssm_plan(p);
+    const int64_t n = p->n_seqs, T = p->T, H = p->H, P = p->P, N = p->N;
+    size_t off[5];
+    const size_t total = gdn_ssm_grad_packed_floats(p, off);
+    if ((n * T > 0 && !gy) || (total > 0 && !grad_packed) || (pl.total > 0 && !ws)) return GDN_ERR_ARG;
+    if (!aligned4(gy) || !aligned16(gs_final) || !aligned16(grad_packed) || !aligned16(ws))
+        return GDN_ERR_UNSUPPORTED;
+    if (ws_bytes < pl.total) return GDN_ERR_WORKSPACE;
+    const Range extra[] = {span_flat(gy, n * T * H * P), span_flat(gs_final, n * H * P * N)};
+    const Range outs[] = {span_flat(grad_packed, (int64_t)total), span_bytes(ws, pl.total)};
+    rc = ssm_check_ptrs(p, s0, x, dt, A, B, C, extra, 2, outs, 2);
+    if (rc != GDN_OK) return rc;
+    gdn::SsmArgs a = ssm_args(p, pl, ws, s0, x, dt, A, B, C);
+    a.gy = gy; a.gs = gs_final;
+    a.ds0 = grad_packed + off[0]; a.dx = grad_packed + off[1]; a.ddt = grad_packed + off[2];
+    a.dB = grad_packed + off[3]; a.dC = grad_packed + off[4];
+    hipError_t e = hipSuccess;
+    if (!(flags & GDN_BWD_REUSE_SNAPSHOTS)) {   // steps and window states first (no y, s_out)
+        e = gdn::launch_ssm_step(a, (hipStream_t)stream);
+        if (e == hipSuccess) e = gdn::launch_ssm(a, false, (hipStream_t)stream);
+    }
+    if (e == hipSuccess) e = gdn::launch_ssm(a, true, (hipStream_t)stream);
+    if (e == hipSuccess) e = gdn::launch_ssm_combine(a, (hipStream_t)stream);
+    return device_status(e);
+}
+
 }  // extern "C"

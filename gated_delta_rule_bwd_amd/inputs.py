@@ -257,3 +257,38 @@ def make_conv(cfg: dict, seqs=None):
     r = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 0])))
     c = (r.standard_normal((D, K)) / np.sqrt(K)).astype(np.float32)
     return sx, c, dy
+
+
+# Selective-scan workloads, 4 sequences x 4096 tokens like the recurrence's layer shape:
+# a Mamba-2 layer (80 heads of 64, 128 states, one group, one decay per head) and a Mamba-1
+# layer (5120 channels, 16 states, one decay per state).
+SSM_WORKLOADS = {
+    "ssm2_layer_h80_p64_n128": {"n_seqs": 4, "T": 4096, "H": 80, "P": 64, "N": 128, "G": 1,
+                                "a_per_state": False, "seed": 1400},
+    "ssm1_layer_d5120_n16": {"n_seqs": 4, "T": 4096, "H": 5120, "P": 1, "N": 16, "G": 1,
+                             "a_per_state": True, "seed": 1401},
+}
+
+
+def make_ssm(cfg: dict, seed=None):
+    """Seeded float32 inputs and cotangents of one scan: x, B, C, gy, gs ~ N(0, 1),
+    s0 ~ N(0, 0.1^2), raw steps dt ~ U(-6, -2) (softplus(dt) in about [0.0025, 0.13]),
+    decays A = -exp(U(0, log 16)) per head, or A[h][n] = -(n + 1) per state (all negative)."""
+    n, T, H, P, N, G = (cfg[k] for k in ("n_seqs", "T", "H", "P", "N", "G"))
+    r = np.random.Generator(np.random.PCG64(np.random.SeedSequence(
+        [cfg.get("seed", 0) if seed is None else seed, 7])))
+    f32 = np.float32
+    out = {
+        "s0": (0.1 * r.standard_normal((n, H, P, N), dtype=f32)).astype(f32),
+        "x": r.standard_normal((n, T, H, P), dtype=f32),
+        "dt": r.uniform(-6.0, -2.0, (n, T, H)).astype(f32),
+        "B": r.standard_normal((n, T, G, N), dtype=f32),
+        "C": r.standard_normal((n, T, G, N), dtype=f32),
+        "gy": r.standard_normal((n, T, H, P), dtype=f32),
+        "gs": r.standard_normal((n, H, P, N), dtype=f32),
+    }
+    if cfg["a_per_state"]:
+        out["A"] = np.ascontiguousarray(np.broadcast_to(-(np.arange(N, dtype=f32) + 1), (H, N)))
+    else:
+        out["A"] = (-np.exp(r.uniform(0.0, np.log(16.0), H))).astype(f32)
+    return out

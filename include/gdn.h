@@ -203,6 +203,50 @@ int gdn_l2norm_fwd(const gdn_l2norm_problem *p, const float *x, float *y, gdn_st
 int gdn_l2norm_bwd(const gdn_l2norm_problem *p, const float *x, const float *dy, float *dx,
                    gdn_stream_t stream);
 
+/* Selective state-space scan (Mamba-1 and Mamba-2 branches) and its backward, the reverse
+ * recurrence (page "S1-24: chunked attention": the SSM_SCAN_BACK commit notes and the n_group
+ * fold).  Per sequence, head h, head element i and state n, with step d = softplus(dt) when
+ * dt_softplus is 1 (d = dt when 0) and group g = h / (H / G):
+ *   a = exp(d A[h][n])  (A[h] for every n when a_per_state is 0)
+ *   s[i][n] = a s[i][n] + d x[i] B[g][n],   y[i] = sum_n s[i][n] C[g][n]
+ * Contiguous fp32 tensors (device pointers):
+ *   s0, s_out  [n_seqs][H][P][N]     x, y, gy  [n_seqs][T][H][P]     dt  [n_seqs][T][H]
+ *   A          [H][N] or [H]         B, C      [n_seqs][T][G][N]
+ * Supported: N in {16, 32, 64, 128}; H % G == 0 and P * H / G a multiple of 16 (16-row
+ * blocks of the kernels never straddle a group); s0, s_out, A, B, C, gs_final, grad_packed
+ * and ws 16-byte aligned, the rest 4-byte aligned.  Outputs must not overlap inputs or each
+ * other.  Returns GDN_OK or an error code (nothing enqueued on error). */
+typedef struct gdn_ssm_problem {
+    int32_t n_seqs, T, H, P, N, G;
+    int32_t a_per_state;   /* 1: A is [H][N] (Mamba-1); 0: A is [H] (Mamba-2) */
+    int32_t dt_softplus;   /* 1: step = softplus(dt); 0: step = dt */
+} gdn_ssm_problem;
+
+/* Bytes of device workspace gdn_ssm_fwd and gdn_ssm_bwd need (0 on an invalid problem): the
+ * steps, the state before every 8-token window, per-16-row column partials and per-row ddt
+ * terms.  The same workspace serves both calls. */
+size_t gdn_ssm_workspace_size(const gdn_ssm_problem *p);
+
+/* Layout of the packed gradient (the page's [d_s | d_x | d_dt | d_B | d_C], contiguous, in
+ * that order, shaped like s0, x, dt, B, C).  Writes the float offset of each region into
+ * offsets[5] (may be NULL) and returns the total number of floats (0 on an invalid problem). */
+size_t gdn_ssm_grad_packed_floats(const gdn_ssm_problem *p, size_t offsets[5]);
+
+/* Forward: writes y and s_out, and the steps and window states into ws. */
+int gdn_ssm_fwd(const gdn_ssm_problem *p, const float *s0, const float *x, const float *dt,
+                const float *A, const float *B, const float *C, float *y, float *s_out,
+                void *ws, size_t ws_bytes, gdn_stream_t stream);
+
+/* Backward: the gradients of L = <gy, y> + <gs_final, s_out> (gs_final NULL means zero; the
+ * reverse walk is seeded with it) with respect to s0, x, dt, B and C, into grad_packed.  A takes
+ * no gradient.  With GDN_BWD_REUSE_SNAPSHOTS the steps and window states that gdn_ssm_fwd left
+ * in ws for the same inputs are used; otherwise they are recomputed first.  dB and dC of a
+ * group sum its heads and rows in a fixed order: results are bitwise reproducible. */
+int gdn_ssm_bwd(const gdn_ssm_problem *p, const float *s0, const float *x, const float *dt,
+                const float *A, const float *B, const float *C, const float *gy,
+                const float *gs_final, float *grad_packed, void *ws, size_t ws_bytes,
+                unsigned flags, gdn_stream_t stream);
+
 /* Human-readable name of a status code. */
 const char *gdn_status_string(int status);
 

@@ -318,3 +318,66 @@ def test_l2norm_argument_errors(B):
     # no rows: NULL pointers are fine and nothing is launched
     assert _l2(B, False, T=0, ptrs=(0, 0, 0)) == 0
     assert _l2(B, True, n=0, ptrs=(0, 0, 0)) == 0
+
+
+def _ssm(B, **kw):
+    d = dict(n_seqs=2, T=20, H=4, P=8, N=32, G=2, a_per_state=0, dt_softplus=1)
+    d.update(kw)
+    return B._SsmProblem(*(d[k] for k in ("n_seqs", "T", "H", "P", "N", "G", "a_per_state",
+                                          "dt_softplus")))
+
+
+def test_ssm_sizes_and_layout(B):
+    p = _ssm(B)
+    ws = B.ssm_workspace_size(p)
+    nwin = 3
+    rows = 2 * 4 * 8
+    assert ws >= 4 * (2 * 20 * 4 + rows * nwin * 32 + rows // 16 * 20 * 2 * 32 + 2 * 20 * 4 * 8)
+    total, lay = B.ssm_grad_layout(p)
+    sizes = [2 * 4 * 8 * 32, 2 * 20 * 4 * 8, 2 * 20 * 4, 2 * 20 * 2 * 32, 2 * 20 * 2 * 32]
+    assert total == sum(sizes)
+    assert [lay[k][0] for k in ("ds", "dx", "ddt", "dB", "dC")] == [sum(sizes[:i]) for i in range(5)]
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(H=4, G=3), -1), (dict(N=24), -2), (dict(N=256), -2), (dict(P=3, H=4, G=2), -2),
+    (dict(a_per_state=2), -1), (dict(dt_softplus=-1), -1), (dict(T=-1), -1), (dict(P=0), -1),
+])
+def test_ssm_invalid_problems(B, kw, code):
+    p = _ssm(B, **kw)
+    assert B.lib.gdn_ssm_workspace_size(ctypes.byref(p)) == 0
+    assert B.lib.gdn_ssm_fwd(ctypes.byref(p), *([None] * 8), None, 0, None) == code
+
+
+def test_ssm_argument_errors(B):
+    """Every call fails validation before any launch."""
+    p = _ssm(B)
+    ws = B.ssm_workspace_size(p)
+    base = [1 << 32, 1 << 33, 1 << 34, 1 << 35, 1 << 36, 1 << 37]     # s0 x dt A B C
+    y, s_out, w = 1 << 38, 1 << 39, 1 << 40
+
+    def fwd(ins=base, y=y, s_out=s_out, w=w, wsb=ws):
+        args = [ctypes.c_void_p(v) if v else None for v in list(ins) + [y, s_out, w]]
+        return B.lib.gdn_ssm_fwd(ctypes.byref(p), *args, wsb, None)
+
+    def bwd(ins=base, gy=1 << 41, gs=1 << 42, gp=1 << 43, w=w, wsb=ws, flags=0):
+        args = [ctypes.c_void_p(v) if v else None for v in list(ins) + [gy, gs, gp, w]]
+        return B.lib.gdn_ssm_bwd(ctypes.byref(p), *args, wsb, flags, None)
+
+    for i in range(6):                                   # a required input missing
+        bad = list(base)
+        bad[i] = 0
+        assert fwd(ins=bad) == -1 and bwd(ins=bad) == -1
+    assert fwd(y=0) == -1 and fwd(s_out=0) == -1 and fwd(w=0) == -1
+    assert bwd(gy=0) == -1 and bwd(gp=0) == -1 and bwd(w=0) == -1
+    assert fwd(wsb=ws - 1) == -3 and bwd(wsb=ws - 1) == -3
+    assert bwd(flags=2) == -1
+    mis = list(base)
+    mis[4] += 4                                          # B not 16-byte aligned
+    assert fwd(ins=mis) == -2 and bwd(ins=mis) == -2
+    assert fwd(s_out=s_out + 8) == -2 and bwd(gs=(1 << 42) + 4) == -2 and bwd(gp=(1 << 43) + 8) == -2
+    assert fwd(y=base[1] + 64) == -1                     # y over x
+    assert fwd(w=base[4]) == -1                          # workspace over B
+    assert bwd(gp=base[0] + 16) == -1                    # gradients over s0
+    assert bwd(gp=(1 << 41) + 16) == -1                  # gradients over gy
+    assert bwd(w=(1 << 43) + 64) == -1                   # workspace over the gradients
