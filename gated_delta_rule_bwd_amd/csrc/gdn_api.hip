@@ -588,7 +588,7 @@ int gdn_l2norm_bwd(const gdn_l2norm_problem *p, const float *x, const float *dy,
 // ---- selective scan ----------------------------------------------------------------------
 
 struct SsmPlan {
-    size_t off_step, off_ck, off_part, off_dd, total;
+    size_t off_ck, off_part, off_dd, total;
     int64_t rows, nwin;
 };
 
@@ -609,7 +609,6 @@ static SsmPlan ssm_plan(const gdn_ssm_problem *p) {
     pl.rows = (int64_t)(n * H * P);
     pl.nwin = (p->T + 7) / 8;
     size_t off = 0;
-    pl.off_step = off; off += align_up(n * T * H * 4);
     pl.off_ck = off;   off += align_up((size_t)pl.rows * pl.nwin * N * 4);
     pl.off_part = off; off += align_up((size_t)pl.rows / 16 * T * 2 * N * 4);
     pl.off_dd = off;   off += align_up(n * T * H * P * 4);
@@ -666,7 +665,6 @@ static gdn::SsmArgs ssm_args(const gdn_ssm_problem *p, const SsmPlan &pl, void *
     std::memset(&a, 0, sizeof(a));
     a.s0 = s0; a.x = x; a.dt = dt; a.A = A; a.B = B; a.C = C;
     char *w = (char *)ws;
-    a.dstep = (float *)(w + pl.off_step);
     a.ck = (float *)(w + pl.off_ck);
     a.part = (float *)(w + pl.off_part);
     a.ddrow = (float *)(w + pl.off_dd);
@@ -690,9 +688,7 @@ int gdn_ssm_fwd(const gdn_ssm_problem *p, const float *s0, const float *x, const
     if (rc != GDN_OK) return rc;
     gdn::SsmArgs a = ssm_args(p, pl, ws, s0, x, dt, A, B, C);
     a.y = y; a.s_out = s_out;
-    hipError_t e = gdn::launch_ssm_step(a, (hipStream_t)stream);
-    if (e == hipSuccess) e = gdn::launch_ssm(a, false, (hipStream_t)stream);
-    return device_status(e);
+    return device_status(gdn::launch_ssm(a, false, (hipStream_t)stream));
 }
 
 int gdn_ssm_bwd(const gdn_ssm_problem *p, const float *s0, const float *x, const float *dt,
@@ -719,10 +715,8 @@ int gdn_ssm_bwd(const gdn_ssm_problem *p, const float *s0, const float *x, const
     a.ds0 = grad_packed + off[0]; a.dx = grad_packed + off[1]; a.ddt = grad_packed + off[2];
     a.dB = grad_packed + off[3]; a.dC = grad_packed + off[4];
     hipError_t e = hipSuccess;
-    if (!(flags & GDN_BWD_REUSE_SNAPSHOTS)) {   // steps and window states first (no y, s_out)
-        e = gdn::launch_ssm_step(a, (hipStream_t)stream);
-        if (e == hipSuccess) e = gdn::launch_ssm(a, false, (hipStream_t)stream);
-    }
+    if (!(flags & GDN_BWD_REUSE_SNAPSHOTS))     // window states first (no y, s_out)
+        e = gdn::launch_ssm(a, false, (hipStream_t)stream);
     if (e == hipSuccess) e = gdn::launch_ssm(a, true, (hipStream_t)stream);
     if (e == hipSuccess) e = gdn::launch_ssm_combine(a, (hipStream_t)stream);
     return device_status(e);

@@ -119,16 +119,15 @@ struct NormArgs {
 hipError_t launch_l2norm(const NormArgs &a, bool bwd, hipStream_t st);
 
 // Selective state-space scan and its reverse recurrence (see ssm_scan.hip).  Contiguous
-// tensors: s0/s_out/ds0 [n][H][P][N], x/y/gy/dx/ddrow [n][T][H][P], dt/dstep/ddt [n][T][H],
-// A [H][N] (aps) or [H], B/C/dB/dC [n][T][G][N]; workspace: dstep, ck [rows][ceil(T/8)][N],
+// tensors: s0/s_out/ds0 [n][H][P][N], x/y/gy/dx/ddrow [n][T][H][P], dt/ddt [n][T][H],
+// A [H][N] (aps) or [H], B/C/dB/dC [n][T][G][N]; workspace: ck [rows][ceil(T/8)][N],
 // part [rows/16][T][2][N], ddrow.
 struct SsmArgs {
     const float *s0, *x, *dt, *A, *B, *C, *gy, *gs;
-    float *dstep, *ck, *part, *ddrow;
+    float *ck, *part, *ddrow;
     float *y, *s_out, *ds0, *dx, *ddt, *dB, *dC;
     int32_t n_seqs, T, H, P, N, G, aps, softplus;
 };
-hipError_t launch_ssm_step(const SsmArgs &a, hipStream_t st);
 hipError_t launch_ssm(const SsmArgs &a, bool bwd, hipStream_t st);   // forward or walk
 hipError_t launch_ssm_combine(const SsmArgs &a, hipStream_t st);
 // head sizes: key width SK and value width SV, each in {16, 32, 64, 128}, not both 128

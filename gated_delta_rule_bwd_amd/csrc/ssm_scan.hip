@@ -86,57 +86,152 @@ __device__ __forceinline__ Row row_of(const SsmArgs &a, int64_t r) {
     return o;
 }
 
-// ---- step sizes ------------------------------------------------------------------------
-__global__ void __launch_bounds__(256) ssm_step_kernel(const SsmArgs a) {
-    const int64_t n = (int64_t)a.n_seqs * a.T * a.H;
-    for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < n;
-         idx += (int64_t)gridDim.x * blockDim.x) {
-        const float z = a.dt[idx];
-        a.dstep[idx] = a.softplus ? (z > 20.f ? z : log1pf(expf(z))) : z;
+// The step of a token and head: softplus(dt) = log(1 + e^dt), or the raw dt.  Computed with
+// the hardware exp and log: below dt = -4 (e^dt < 0.019) as the series e - e^2/2 + e^3/3 -
+// e^4/4 (truncation below 2e-8 relative), elsewhere as log(1 + e^dt), whose argument is then
+// at least 1.018 so the rounding of 1 + e^dt costs at most ~3e-6 relative; above 20 it is dt.
+// Both directions use this one function, so the backward's replay gives the forward's bits.
+__device__ __forceinline__ float step_of(float z, int softplus) {
+    if (!softplus) return z;
+    const float e = __expf(z);
+    const float series = e * (1.f - e * (0.5f - e * (1.f / 3.f - e * 0.25f)));
+    const float direct = __logf(1.f + e);
+    return z > 20.f ? z : (z < -4.f ? series : direct);
+}
+
+// ---- window staging --------------------------------------------------------------------
+// The 16 rows of a workgroup share one (sequence, group), so a window's B and C rows are
+// common to all of them; x, the step (and gy) are per row.  Each window is staged in LDS once
+// and the next one is loaded into registers while the current one is computed.
+struct Stage {
+    float B[WIN][128], C[WIN][128];
+    float x[WIN][ROWS], d[WIN][ROWS], gy[WIN][ROWS];
+};
+
+template <int NPL, bool GY>
+struct Loader {
+    static constexpr int NQ = NPL >= 4 ? NPL / 4 : 1;   // float4s of B|C per thread
+    float4 q[NQ];
+    float s0v, s1v;                                     // x or step; gy
+    int tid;
+    int64_t seq, g;
+    int64_t lh, li;                                     // head and element of the loader's row
+
+    __device__ void init(const SsmArgs &a, int64_t r0, int t) {
+        tid = t;
+        const Row lw = row_of(a, r0 + (t & 15));
+        seq = lw.s; g = lw.g; lh = lw.h; li = lw.i;
+    }
+    __device__ void load(const SsmArgs &a, int t0, int cnt) {
+        const int64_t N = a.N, T = a.T, H = a.H, P = a.P, G = a.G;
+#pragma unroll
+        for (int m = 0; m < NQ; ++m) {
+            const int qq = tid + 256 * m;               // of 2 arrays x WIN tokens x N / 4
+            if (qq < 4 * a.N) {
+                const int arr = qq >= 2 * a.N;
+                const int q2 = qq - arr * 2 * a.N;
+                const int tok = q2 / (a.N / 4), c4 = q2 % (a.N / 4);
+                const int64_t t = t0 + min(tok, cnt - 1);
+                q[m] = *reinterpret_cast<const float4 *>((arr ? a.C : a.B) + ((seq * T + t) * G + g) * N + 4 * c4);
+            }
+        }
+        const int tok = (tid & 127) >> 4;
+        const int64_t t = t0 + min(tok, cnt - 1);
+        if (tid < 128) s0v = a.x[((seq * T + t) * H + lh) * P + li];
+        else s0v = a.dt[(seq * T + t) * H + lh];   // raw: the step is taken in put()
+        if constexpr (GY) {
+            if (tid < 128) s1v = a.gy[((seq * T + t) * H + lh) * P + li];
+        }
+    }
+    __device__ void put(const SsmArgs &a, Stage &st) const {
+#pragma unroll
+        for (int m = 0; m < NQ; ++m) {
+            const int qq = tid + 256 * m;
+            if (qq < 4 * a.N) {
+                const int arr = qq >= 2 * a.N;
+                const int q2 = qq - arr * 2 * a.N;
+                const int tok = q2 / (a.N / 4), c4 = q2 % (a.N / 4);
+                *reinterpret_cast<float4 *>(&(arr ? st.C : st.B)[tok][4 * c4]) = q[m];
+            }
+        }
+        const int tok = (tid & 127) >> 4, rr = tid & 15;
+        if (tid < 128) st.x[tok][rr] = s0v;
+        else st.d[tok][rr] = step_of(s0v, a.softplus);
+        if constexpr (GY) {
+            if (tid < 128) st.gy[tok][rr] = s1v;
+        }
+    }
+};
+
+template <int NPL>
+__device__ __forceinline__ void lds_row(const float *p, float (&v)[NPL]) {
+    if constexpr (NPL >= 4) {
+#pragma unroll
+        for (int q = 0; q < NPL / 4; ++q) {
+            const float4 t = reinterpret_cast<const float4 *>(p)[q];
+            v[4 * q] = t.x; v[4 * q + 1] = t.y; v[4 * q + 2] = t.z; v[4 * q + 3] = t.w;
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < NPL; ++j) v[j] = p[j];
     }
 }
 
 // ---- forward -------------------------------------------------------------------------------
 template <int NPL, bool APS>
 __global__ void __launch_bounds__(256) ssm_fwd_kernel(const SsmArgs a) {
-    const int sub = threadIdx.x & 15;
-    const Row w = row_of(a, (int64_t)blockIdx.x * ROWS + (threadIdx.x >> 4));
+    __shared__ Stage stg[2];
+    __shared__ float ys[2][WIN][ROWS];
+    const int tid = threadIdx.x, sub = tid & 15, rho = tid >> 4;
+    const int64_t r0 = (int64_t)blockIdx.x * ROWS;
+    const Row w = row_of(a, r0 + rho);
     const int c0 = sub * NPL;
-    const int64_t N = a.N, T = a.T, H = a.H, G = a.G;
+    const int64_t N = a.N, T = a.T, H = a.H, P = a.P;
     const int nwin = (a.T + WIN - 1) / WIN;
     float st[NPL], Aj[NPL];
     ldv<NPL>(a.s0 + w.r * N + c0, st);
     float Ah = 0.f;
     if constexpr (APS) ldv<NPL>(a.A + w.h * N + c0, Aj);
     else Ah = a.A[w.h];
-    const float *xr = a.x + (w.s * T * H + w.h) * a.P + w.i;      // + t H P
-    const float *dr = a.dstep + w.s * T * H + w.h;                 // + t H
-    const float *br = a.B + (w.s * T * G + w.g) * N + c0;          // + t G N
-    const float *cr = a.C + (w.s * T * G + w.g) * N + c0;
-    float *yr = a.y ? a.y + (w.s * T * H + w.h) * a.P + w.i : nullptr;
+    Loader<NPL, false> ld;
+    ld.init(a, r0, tid);
+    const int wr = tid & 15, wtok = (tid & 127) >> 4;   // y writer: row, token
+    const Row ow = row_of(a, r0 + wr);
+    if (nwin > 0) {
+        ld.load(a, 0, min(WIN, a.T));
+        ld.put(a, stg[0]);
+    }
+    __syncthreads();
     for (int win = 0; win < nwin; ++win) {
-        stv<NPL>(a.ck + (w.r * nwin + win) * N + c0, st);         // state before the window
-        const int t0 = win * WIN;
+        const int cur = win & 1;
+        const int t0 = win * WIN, cnt = min(WIN, a.T - t0);
+        if (win + 1 < nwin) ld.load(a, t0 + WIN, min(WIN, a.T - t0 - WIN));
+        stv<NPL>(a.ck + (w.r * nwin + win) * N + c0, st);          // state before the window
+        const Stage &sg = stg[cur];
 #pragma unroll
         for (int k = 0; k < WIN; ++k) {
-            const int64_t t = t0 + k;
-            if (t >= T) break;                                     // uniform
-            const float d = dr[t * H];
-            const float b = d * xr[t * H * a.P];
-            float Bv[NPL], Cv[NPL];
-            ldv<NPL>(br + t * G * N, Bv);
-            ldv<NPL>(cr + t * G * N, Cv);
-            float yp = 0.f;
-            const float ah = APS ? 0.f : dexp(d * Ah);
+            if (k < cnt) {                                           // uniform
+                const float d = sg.d[k][rho];
+                const float b = d * sg.x[k][rho];
+                float Bv[NPL], Cv[NPL];
+                lds_row<NPL>(&sg.B[k][c0], Bv);
+                lds_row<NPL>(&sg.C[k][c0], Cv);
+                float yp = 0.f;
+                const float ah = APS ? 0.f : dexp(d * Ah);
 #pragma unroll
-            for (int j = 0; j < NPL; ++j) {
-                const float aj = APS ? dexp(d * Aj[j]) : ah;
-                st[j] = fmaf(aj, st[j], b * Bv[j]);
-                yp = fmaf(st[j], Cv[j], yp);
+                for (int j = 0; j < NPL; ++j) {
+                    const float aj = APS ? dexp(d * Aj[j]) : ah;
+                    st[j] = fmaf(aj, st[j], b * Bv[j]);
+                    yp = fmaf(st[j], Cv[j], yp);
+                }
+                yp = row16_sum(yp);
+                if (sub == 0) ys[cur][k][rho] = yp;
             }
-            yp = row16_sum(yp);
-            if (yr && sub == 0) yr[t * H * a.P] = yp;
         }
+        if (win + 1 < nwin) ld.put(a, stg[cur ^ 1]);
+        __syncthreads();
+        if (a.y && tid < 128 && wtok < cnt)
+            a.y[((ow.s * T + t0 + wtok) * H + ow.h) * P + ow.i] = ys[cur][wtok][wr];
     }
     if (a.s_out) stv<NPL>(a.s_out + w.r * N + c0, st);
 }
@@ -144,12 +239,15 @@ __global__ void __launch_bounds__(256) ssm_fwd_kernel(const SsmArgs a) {
 // ---- backward ------------------------------------------------------------------------------
 template <int NPL, bool APS>
 __global__ void __launch_bounds__(256) ssm_bwd_kernel(const SsmArgs a) {
+    __shared__ Stage stg[2];
     __shared__ float red[WIN][4][2][128];          // [token][wave][dC | dB][column]
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int sub = threadIdx.x & 15, rho = lane >> 4;
-    const Row w = row_of(a, (int64_t)blockIdx.x * ROWS + (threadIdx.x >> 4));
+    __shared__ float os[2][WIN][ROWS];             // dx, ddt term per (token, row)
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int sub = tid & 15, rho = tid >> 4, rg = lane >> 4;
+    const int64_t r0 = (int64_t)blockIdx.x * ROWS;
+    const Row w = row_of(a, r0 + rho);
     const int c0 = sub * NPL;
-    const int64_t N = a.N, T = a.T, H = a.H, G = a.G, P = a.P;
+    const int64_t N = a.N, T = a.T, H = a.H, P = a.P;
     const int nwin = (a.T + WIN - 1) / WIN;
     float gs[NPL], Aj[NPL];
     if (a.gs) ldv<NPL>(a.gs + w.r * N + c0, gs);
@@ -160,28 +258,32 @@ __global__ void __launch_bounds__(256) ssm_bwd_kernel(const SsmArgs a) {
     float Ah = 0.f;
     if constexpr (APS) ldv<NPL>(a.A + w.h * N + c0, Aj);
     else Ah = a.A[w.h];
-    const float *xr = a.x + (w.s * T * H + w.h) * P + w.i;
-    const float *gyr = a.gy + (w.s * T * H + w.h) * P + w.i;
-    const float *dr = a.dstep + w.s * T * H + w.h;
-    const float *br = a.B + (w.s * T * G + w.g) * N + c0;
-    const float *cr = a.C + (w.s * T * G + w.g) * N + c0;
-    float *dxr = a.dx + (w.s * T * H + w.h) * P + w.i;
-    float *ddr = a.ddrow + (w.s * T * H + w.h) * P + w.i;
+    Loader<NPL, true> ld;
+    ld.init(a, r0, tid);
+    const int wr = tid & 15, wtok = (tid & 127) >> 4, wq = tid >> 7;   // dx / dd writer
+    const Row ow = row_of(a, r0 + wr);
     float *part = a.part + (int64_t)blockIdx.x * T * 2 * N;
-    for (int win = nwin - 1; win >= 0; --win) {
-        const int t0 = win * WIN;
-        const int cnt = min(WIN, a.T - t0);
+    if (nwin > 0) {
+        const int t0 = (nwin - 1) * WIN;
+        ld.load(a, t0, a.T - t0);
+        ld.put(a, stg[0]);
+    }
+    __syncthreads();
+    for (int it = 0; it < nwin; ++it) {
+        const int win = nwin - 1 - it, cur = it & 1;
+        const int t0 = win * WIN, cnt = min(WIN, a.T - t0);
+        if (win > 0) ld.load(a, t0 - WIN, WIN);
+        const Stage &sg = stg[cur];
         float sp[NPL], S[WIN][NPL];
         ldv<NPL>(a.ck + (w.r * nwin + win) * N + c0, sp);
         // replay the window: S[k] is the state after token t0 + k
 #pragma unroll
         for (int k = 0; k < WIN; ++k) {
             if (k < cnt) {
-                const int64_t t = t0 + k;
-                const float d = dr[t * H];
-                const float b = d * xr[t * H * P];
+                const float d = sg.d[k][rho];
+                const float b = d * sg.x[k][rho];
                 float Bv[NPL];
-                ldv<NPL>(br + t * G * N, Bv);
+                lds_row<NPL>(&sg.B[k][c0], Bv);
                 const float ah = APS ? 0.f : dexp(d * Ah);
 #pragma unroll
                 for (int j = 0; j < NPL; ++j) {
@@ -194,13 +296,12 @@ __global__ void __launch_bounds__(256) ssm_bwd_kernel(const SsmArgs a) {
 #pragma unroll
         for (int k = WIN - 1; k >= 0; --k) {
             if (k < cnt) {
-                const int64_t t = t0 + k;
-                const float d = dr[t * H];
-                const float xv = xr[t * H * P];
-                const float gyv = gyr[t * H * P];
+                const float d = sg.d[k][rho];
+                const float xv = sg.x[k][rho];
+                const float gyv = sg.gy[k][rho];
                 float Bv[NPL], Cv[NPL];
-                ldv<NPL>(br + t * G * N, Bv);
-                ldv<NPL>(cr + t * G * N, Cv);
+                lds_row<NPL>(&sg.B[k][c0], Bv);
+                lds_row<NPL>(&sg.C[k][c0], Cv);
                 const float ah = APS ? 0.f : dexp(d * Ah);
                 const float dxv = d * xv;
                 float v[2 * NPL];             // column partials: dC then dB
@@ -219,33 +320,34 @@ __global__ void __launch_bounds__(256) ssm_bwd_kernel(const SsmArgs a) {
                 gB = row16_sum(gB);
                 dec = row16_sum(dec);
                 if (sub == 0) {
-                    dxr[t * H * P] = d * gB;
-                    ddr[t * H * P] = (APS ? dec : Ah * ah * dec) + xv * gB;
+                    os[0][k][rho] = d * gB;
+                    os[1][k][rho] = (APS ? dec : Ah * ah * dec) + xv * gB;
                 }
                 // reduce-scatter the column partials over the wave's four row groups
                 float u[NPL];
 #pragma unroll
                 for (int m = 0; m < NPL; ++m) {
-                    auto p = __builtin_amdgcn_permlane32_swap(as_i(v[m]), as_i(v[NPL + m]), false, false);
-                    u[m] = as_f(p[0]) + as_f(p[1]);   // rows 0-1: dC, rows 2-3: dB (columns m)
+                    auto pr = __builtin_amdgcn_permlane32_swap(as_i(v[m]), as_i(v[NPL + m]), false, false);
+                    u[m] = as_f(pr[0]) + as_f(pr[1]);   // row groups 0-1: dC, 2-3: dB (columns m)
                 }
                 if constexpr (NPL == 1) {
-                    auto p = __builtin_amdgcn_permlane16_swap(as_i(u[0]), as_i(u[0]), false, false);
-                    const float q = as_f(p[0]) + as_f(p[1]);
-                    if ((rho & 1) == 0) red[k][wave][rho >> 1][c0] = q;
+                    auto pr = __builtin_amdgcn_permlane16_swap(as_i(u[0]), as_i(u[0]), false, false);
+                    const float q = as_f(pr[0]) + as_f(pr[1]);
+                    if ((rg & 1) == 0) red[k][wave][rg >> 1][c0] = q;
                 } else {
 #pragma unroll
                     for (int m = 0; m < NPL / 2; ++m) {
-                        auto p = __builtin_amdgcn_permlane16_swap(as_i(u[m]), as_i(u[NPL / 2 + m]), false, false);
-                        // rows 0, 2: columns m; rows 1, 3: columns NPL / 2 + m
-                        red[k][wave][rho >> 1][c0 + (rho & 1) * (NPL / 2) + m] = as_f(p[0]) + as_f(p[1]);
+                        auto pr = __builtin_amdgcn_permlane16_swap(as_i(u[m]), as_i(u[NPL / 2 + m]), false, false);
+                        // row groups 0, 2: columns m; 1, 3: columns NPL / 2 + m
+                        red[k][wave][rg >> 1][c0 + (rg & 1) * (NPL / 2) + m] = as_f(pr[0]) + as_f(pr[1]);
                     }
                 }
             }
         }
+        if (win > 0) ld.put(a, stg[cur ^ 1]);
         __syncthreads();
         {   // the window's column sums over the four waves: NPL consecutive outputs per thread
-            const int o = threadIdx.x * NPL;                  // of WIN x 2 x N
+            const int o = tid * NPL;                          // of WIN x 2 x N
             const int tok = o / (2 * a.N), qty = (o / a.N) & 1, col = o % a.N;
             if (tok < cnt) {
                 float acc[NPL];
@@ -255,6 +357,10 @@ __global__ void __launch_bounds__(256) ssm_bwd_kernel(const SsmArgs a) {
                              red[tok][3][qty][col + m];
                 stv<NPL>(part + (int64_t)(t0 + tok) * 2 * N + qty * N + col, acc);
             }
+            if (wtok < cnt) {
+                const int64_t at = ((ow.s * T + t0 + wtok) * H + ow.h) * P + ow.i;
+                (wq ? a.ddrow : a.dx)[at] = os[wq][wtok][wr];
+            }
         }
         __syncthreads();
     }
@@ -262,24 +368,45 @@ __global__ void __launch_bounds__(256) ssm_bwd_kernel(const SsmArgs a) {
 }
 
 // ---- combine: dB, dC over the segments of each group; ddt over the rows of each head ------
+// One thread per (sequence, token, group, 4 columns) of dB / dC, summing the group's segments
+// in increasing order with eight loads in flight; one per (sequence, token, head) of ddt.
 __global__ void __launch_bounds__(256) ssm_combine_kernel(const SsmArgs a) {
     const int64_t T = a.T, H = a.H, G = a.G, N = a.N, P = a.P;
-    const int64_t nbc = (int64_t)a.n_seqs * T * G * N;   // dB / dC elements
+    const int64_t N4 = N / 4;
+    const int64_t nbc = (int64_t)a.n_seqs * T * G * N4;    // float4 groups of dB / dC
     const int64_t ndt = (int64_t)a.n_seqs * T * H;
-    const int64_t segs_per_group = P * (H / G) / ROWS;
+    const int64_t K = P * (H / G) / ROWS;                    // segments per group
+    const int64_t kstride = T * 2 * N;                       // floats between segments
     for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < nbc + ndt;
          idx += (int64_t)gridDim.x * blockDim.x) {
         if (idx < nbc) {
-            const int64_t n = idx % N, g = (idx / N) % G, t = (idx / (N * G)) % T, s = idx / (N * G * T);
+            const int64_t n4 = idx % N4, g = (idx / N4) % G, t = (idx / (N4 * G)) % T, s = idx / (N4 * G * T);
             const int64_t seg0 = (s * H * P + g * P * (H / G)) / ROWS;
-            float db = 0.f, dc = 0.f;
-            for (int64_t k = 0; k < segs_per_group; ++k) {
-                const float *pp = a.part + ((seg0 + k) * T + t) * 2 * N;
-                dc += pp[n];
-                db += pp[N + n];
+            const float *pp = a.part + (seg0 * T + t) * 2 * N + 4 * n4;
+            float4 dc = make_float4(0.f, 0.f, 0.f, 0.f), db = dc;
+            int64_t k = 0;
+            for (; k + 8 <= K; k += 8) {
+                float4 c[8], b[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    c[u] = *reinterpret_cast<const float4 *>(pp + (k + u) * kstride);
+                    b[u] = *reinterpret_cast<const float4 *>(pp + (k + u) * kstride + N);
+                }
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    dc.x += c[u].x; dc.y += c[u].y; dc.z += c[u].z; dc.w += c[u].w;
+                    db.x += b[u].x; db.y += b[u].y; db.z += b[u].z; db.w += b[u].w;
+                }
             }
-            a.dB[idx] = db;
-            a.dC[idx] = dc;
+            for (; k < K; ++k) {
+                const float4 c = *reinterpret_cast<const float4 *>(pp + k * kstride);
+                const float4 b = *reinterpret_cast<const float4 *>(pp + k * kstride + N);
+                dc.x += c.x; dc.y += c.y; dc.z += c.z; dc.w += c.w;
+                db.x += b.x; db.y += b.y; db.z += b.z; db.w += b.w;
+            }
+            const int64_t o = idx * 4;   // dB / dC are [n][T][G][N]: the same flat index
+            a.dB[o] = db.x; a.dB[o + 1] = db.y; a.dB[o + 2] = db.z; a.dB[o + 3] = db.w;
+            a.dC[o] = dc.x; a.dC[o + 1] = dc.y; a.dC[o + 2] = dc.z; a.dC[o + 3] = dc.w;
         } else {
             const int64_t j = idx - nbc;                      // (s, t, h)
             const float *rr = a.ddrow + j * P;
@@ -308,13 +435,6 @@ unsigned grid_for(int64_t n) {
 
 }  // namespace
 
-hipError_t launch_ssm_step(const SsmArgs &a, hipStream_t st) {
-    const int64_t n = (int64_t)a.n_seqs * a.T * a.H;
-    if (n <= 0) return hipSuccess;
-    void *params[] = {const_cast<SsmArgs *>(&a)};
-    return hipLaunchKernel((const void *)ssm_step_kernel, dim3(grid_for(n)), dim3(256), params, 0, st);
-}
-
 hipError_t launch_ssm(const SsmArgs &a, bool bwd, hipStream_t st) {
     if ((int64_t)a.n_seqs * a.H * a.P <= 0) return hipSuccess;
     switch (a.N) {
@@ -327,7 +447,7 @@ hipError_t launch_ssm(const SsmArgs &a, bool bwd, hipStream_t st) {
 }
 
 hipError_t launch_ssm_combine(const SsmArgs &a, hipStream_t st) {
-    const int64_t n = (int64_t)a.n_seqs * a.T * ((int64_t)a.G * a.N + a.H);
+    const int64_t n = (int64_t)a.n_seqs * a.T * ((int64_t)a.G * a.N / 4 + a.H);
     if (n <= 0) return hipSuccess;
     void *params[] = {const_cast<SsmArgs *>(&a)};
     return hipLaunchKernel((const void *)ssm_combine_kernel, dim3(grid_for(n)), dim3(256), params, 0, st);

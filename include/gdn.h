@@ -223,8 +223,8 @@ typedef struct gdn_ssm_problem {
 } gdn_ssm_problem;
 
 /* Bytes of device workspace gdn_ssm_fwd and gdn_ssm_bwd need (0 on an invalid problem): the
- * steps, the state before every 8-token window, per-16-row column partials and per-row ddt
- * terms.  The same workspace serves both calls. */
+ * state before every 8-token window, per-16-row column partials and per-row ddt terms.  The
+ * same workspace serves both calls. */
 size_t gdn_ssm_workspace_size(const gdn_ssm_problem *p);
 
 /* Layout of the packed gradient (the page's [d_s | d_x | d_dt | d_B | d_C], contiguous, in
@@ -239,7 +239,7 @@ int gdn_ssm_fwd(const gdn_ssm_problem *p, const float *s0, const float *x, const
 
 /* Backward: the gradients of L = <gy, y> + <gs_final, s_out> (gs_final NULL means zero; the
  * reverse walk is seeded with it) with respect to s0, x, dt, B and C, into grad_packed.  A takes
- * no gradient.  With GDN_BWD_REUSE_SNAPSHOTS the steps and window states that gdn_ssm_fwd left
+ * no gradient.  With GDN_BWD_REUSE_SNAPSHOTS the window states that gdn_ssm_fwd left
  * in ws for the same inputs are used; otherwise they are recomputed first.  dB and dC of a
  * group sum its heads and rows in a fixed order: results are bitwise reproducible. */
 int gdn_ssm_bwd(const gdn_ssm_problem *p, const float *s0, const float *x, const float *dt,

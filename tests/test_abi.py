@@ -332,7 +332,7 @@ def test_ssm_sizes_and_layout(B):
     ws = B.ssm_workspace_size(p)
     nwin = 3
     rows = 2 * 4 * 8
-    assert ws >= 4 * (2 * 20 * 4 + rows * nwin * 32 + rows // 16 * 20 * 2 * 32 + 2 * 20 * 4 * 8)
+    assert ws >= 4 * (rows * nwin * 32 + rows // 16 * 20 * 2 * 32 + 2 * 20 * 4 * 8)
     total, lay = B.ssm_grad_layout(p)
     sizes = [2 * 4 * 8 * 32, 2 * 20 * 4 * 8, 2 * 20 * 4, 2 * 20 * 2 * 32, 2 * 20 * 2 * 32]
     assert total == sum(sizes)
