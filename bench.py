@@ -136,15 +136,17 @@ def copy_calibration(mib):
     print(json.dumps({"copy_calibration_bytes": n * 4, "launches": 3}), flush=True)
 
 
-def cpu_baseline(w, n_key_heads):
-    """The fp64 oracle (as it stands) on a bounded sample of the same workload: sequence 0,
-    the first n_key_heads key heads with all their value heads, full length, fwd+bwd."""
+def cpu_baseline(w, n_key_heads, n_seqs=2):
+    """The fp64 oracle (as it stands) on a bounded sample of the same workload: the first
+    n_seqs sequences, the first n_key_heads key heads with all their value heads, full length,
+    fwd+bwd."""
     import oracle
     from gated_delta_rule_bwd_amd import inputs as I
     cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
     kh = list(range(n_key_heads))
-    arrays, vh = I.make_all(w, seqs=[0], key_heads=kh)
-    sub = I.sub_workload(w, [0], kh)
+    seqs = list(range(min(n_seqs, w.n_seqs)))
+    arrays, vh = I.make_all(w, seqs=seqs, key_heads=kh)
+    sub = I.sub_workload(w, seqs, kh)
     orc = oracle.Oracle(threads=cores)
     shape = sub.shape_dict()
     args = [arrays[n] for n in ("q", "k", "v", "g", "beta", "state0")]
@@ -153,10 +155,11 @@ def cpu_baseline(w, n_key_heads):
     orc.bwd(shape, *args, arrays["gy"], arrays["dstate_out"])
     dt = time.perf_counter() - t0
     th = sub.tokens_heads
-    used = min(cores, len(kh))  # the oracle threads over (sequence, key head) pairs
+    used = min(cores, len(kh) * len(seqs))  # the oracle threads over (sequence, key head) pairs
     return {"value": th / dt, "unit": "tokens·heads/s", "cores": used, "kind": "oracle",
-            "sample": f"sequence 0, key heads 0..{len(kh) - 1} with their {len(vh)} value heads, "
-                      f"{w.T} tokens each ({th} tokens·heads), fp64 fwd+bwd, {dt:.1f} s"}
+            "sample": f"sequences 0..{len(seqs) - 1}, key heads 0..{len(kh) - 1} with their "
+                      f"{len(vh)} value heads, {w.T} tokens each ({th} tokens·heads), fp64 "
+                      f"fwd+bwd, {dt:.1f} s"}
 
 
 PEAK_HBM = 8.0e12              # MI355X HBM3E, bytes/s
