@@ -4,8 +4,8 @@
 // head h (group g = h / (H / G)), head element i and state n, with step d = softplus(dt) (or dt):
 //   a = exp(d A[h, n]),  s[i, n] = a s[i, n] + d x[i] B[g, n],  y[i] = sum_n s[i, n] C[g, n].
 //
-// Layout of the work: a row is one (s, h, i); 16 lanes own a row, each lane NPL = N / 16
-// consecutive state columns; a workgroup is 16 rows (4 per wave), which must lie in one group.
+// Layout of the work: a row is one (s, h, i); 16 lanes own a row, each lane NPL = N / 16 state
+// columns (see col_of); a workgroup is 16 rows (4 per wave), which must lie in one group.
 // The forward keeps the row's state in registers, writes y through a 16-lane DPP sum and saves
 // the state before every 8-token window.  The backward walks the windows in reverse: it
 // replays a window from its saved state into registers, then walks its tokens backwards with
@@ -163,17 +163,36 @@ struct Loader {
     }
 };
 
+// The state columns a lane owns.  With NPL >= 4 they are float4 chunks 64 columns apart
+// (columns 4 sub .. 4 sub + 3, then 64 + 4 sub .., ...), so the 16 lanes of a row read 256
+// contiguous bytes per 16-byte access and LDS rows are read without bank conflicts; with
+// NPL < 4 the NPL columns from sub NPL on.
 template <int NPL>
-__device__ __forceinline__ void lds_row(const float *p, float (&v)[NPL]) {
+__device__ __forceinline__ int col_of(int sub, int j) {
+    if constexpr (NPL >= 4) return (j >> 2) * 64 + 4 * sub + (j & 3);
+    else return sub * NPL + j;
+}
+template <int NPL>
+__device__ __forceinline__ void ld_cols(const float *row, int sub, float (&v)[NPL]) {
     if constexpr (NPL >= 4) {
 #pragma unroll
         for (int q = 0; q < NPL / 4; ++q) {
-            const float4 t = reinterpret_cast<const float4 *>(p)[q];
+            const float4 t = *reinterpret_cast<const float4 *>(row + q * 64 + 4 * sub);
             v[4 * q] = t.x; v[4 * q + 1] = t.y; v[4 * q + 2] = t.z; v[4 * q + 3] = t.w;
         }
     } else {
+        ldv<NPL>(row + sub * NPL, v);
+    }
+}
+template <int NPL>
+__device__ __forceinline__ void st_cols(float *row, int sub, const float (&v)[NPL]) {
+    if constexpr (NPL >= 4) {
 #pragma unroll
-        for (int j = 0; j < NPL; ++j) v[j] = p[j];
+        for (int q = 0; q < NPL / 4; ++q)
+            *reinterpret_cast<float4 *>(row + q * 64 + 4 * sub) =
+                make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+    } else {
+        stv<NPL>(row + sub * NPL, v);
     }
 }
 
@@ -185,13 +204,12 @@ __global__ void __launch_bounds__(256) ssm_fwd_kernel(const SsmArgs a) {
     const int tid = threadIdx.x, sub = tid & 15, rho = tid >> 4;
     const int64_t r0 = (int64_t)blockIdx.x * ROWS;
     const Row w = row_of(a, r0 + rho);
-    const int c0 = sub * NPL;
     const int64_t N = a.N, T = a.T, H = a.H, P = a.P;
     const int nwin = (a.T + WIN - 1) / WIN;
     float st[NPL], Aj[NPL];
-    ldv<NPL>(a.s0 + w.r * N + c0, st);
+    ld_cols<NPL>(a.s0 + w.r * N, sub, st);
     float Ah = 0.f;
-    if constexpr (APS) ldv<NPL>(a.A + w.h * N + c0, Aj);
+    if constexpr (APS) ld_cols<NPL>(a.A + w.h * N, sub, Aj);
     else Ah = a.A[w.h];
     Loader<NPL, false> ld;
     ld.init(a, r0, tid);
@@ -206,7 +224,7 @@ __global__ void __launch_bounds__(256) ssm_fwd_kernel(const SsmArgs a) {
         const int cur = win & 1;
         const int t0 = win * WIN, cnt = min(WIN, a.T - t0);
         if (win + 1 < nwin) ld.load(a, t0 + WIN, min(WIN, a.T - t0 - WIN));
-        stv<NPL>(a.ck + (w.r * nwin + win) * N + c0, st);          // state before the window
+        st_cols<NPL>(a.ck + (w.r * nwin + win) * N, sub, st);     // state before the window
         const Stage &sg = stg[cur];
 #pragma unroll
         for (int k = 0; k < WIN; ++k) {
@@ -214,8 +232,8 @@ __global__ void __launch_bounds__(256) ssm_fwd_kernel(const SsmArgs a) {
                 const float d = sg.d[k][rho];
                 const float b = d * sg.x[k][rho];
                 float Bv[NPL], Cv[NPL];
-                lds_row<NPL>(&sg.B[k][c0], Bv);
-                lds_row<NPL>(&sg.C[k][c0], Cv);
+                ld_cols<NPL>(&sg.B[k][0], sub, Bv);
+                ld_cols<NPL>(&sg.C[k][0], sub, Cv);
                 float yp = 0.f;
                 const float ah = APS ? 0.f : dexp(d * Ah);
 #pragma unroll
@@ -233,7 +251,7 @@ __global__ void __launch_bounds__(256) ssm_fwd_kernel(const SsmArgs a) {
         if (a.y && tid < 128 && wtok < cnt)
             a.y[((ow.s * T + t0 + wtok) * H + ow.h) * P + ow.i] = ys[cur][wtok][wr];
     }
-    if (a.s_out) stv<NPL>(a.s_out + w.r * N + c0, st);
+    if (a.s_out) st_cols<NPL>(a.s_out + w.r * N, sub, st);
 }
 
 // ---- backward ------------------------------------------------------------------------------
@@ -246,17 +264,16 @@ __global__ void __launch_bounds__(256) ssm_bwd_kernel(const SsmArgs a) {
     const int sub = tid & 15, rho = tid >> 4, rg = lane >> 4;
     const int64_t r0 = (int64_t)blockIdx.x * ROWS;
     const Row w = row_of(a, r0 + rho);
-    const int c0 = sub * NPL;
     const int64_t N = a.N, T = a.T, H = a.H, P = a.P;
     const int nwin = (a.T + WIN - 1) / WIN;
     float gs[NPL], Aj[NPL];
-    if (a.gs) ldv<NPL>(a.gs + w.r * N + c0, gs);
+    if (a.gs) ld_cols<NPL>(a.gs + w.r * N, sub, gs);
     else {
 #pragma unroll
         for (int j = 0; j < NPL; ++j) gs[j] = 0.f;
     }
     float Ah = 0.f;
-    if constexpr (APS) ldv<NPL>(a.A + w.h * N + c0, Aj);
+    if constexpr (APS) ld_cols<NPL>(a.A + w.h * N, sub, Aj);
     else Ah = a.A[w.h];
     Loader<NPL, true> ld;
     ld.init(a, r0, tid);
@@ -275,7 +292,7 @@ __global__ void __launch_bounds__(256) ssm_bwd_kernel(const SsmArgs a) {
         if (win > 0) ld.load(a, t0 - WIN, WIN);
         const Stage &sg = stg[cur];
         float sp[NPL], S[WIN][NPL];
-        ldv<NPL>(a.ck + (w.r * nwin + win) * N + c0, sp);
+        ld_cols<NPL>(a.ck + (w.r * nwin + win) * N, sub, sp);
         // replay the window: S[k] is the state after token t0 + k
 #pragma unroll
         for (int k = 0; k < WIN; ++k) {
@@ -283,7 +300,7 @@ __global__ void __launch_bounds__(256) ssm_bwd_kernel(const SsmArgs a) {
                 const float d = sg.d[k][rho];
                 const float b = d * sg.x[k][rho];
                 float Bv[NPL];
-                lds_row<NPL>(&sg.B[k][c0], Bv);
+                ld_cols<NPL>(&sg.B[k][0], sub, Bv);
                 const float ah = APS ? 0.f : dexp(d * Ah);
 #pragma unroll
                 for (int j = 0; j < NPL; ++j) {
@@ -300,8 +317,8 @@ __global__ void __launch_bounds__(256) ssm_bwd_kernel(const SsmArgs a) {
                 const float xv = sg.x[k][rho];
                 const float gyv = sg.gy[k][rho];
                 float Bv[NPL], Cv[NPL];
-                lds_row<NPL>(&sg.B[k][c0], Bv);
-                lds_row<NPL>(&sg.C[k][c0], Cv);
+                ld_cols<NPL>(&sg.B[k][0], sub, Bv);
+                ld_cols<NPL>(&sg.C[k][0], sub, Cv);
                 const float ah = APS ? 0.f : dexp(d * Ah);
                 const float dxv = d * xv;
                 float v[2 * NPL];             // column partials: dC then dB
@@ -333,29 +350,40 @@ __global__ void __launch_bounds__(256) ssm_bwd_kernel(const SsmArgs a) {
                 if constexpr (NPL == 1) {
                     auto pr = __builtin_amdgcn_permlane16_swap(as_i(u[0]), as_i(u[0]), false, false);
                     const float q = as_f(pr[0]) + as_f(pr[1]);
-                    if ((rg & 1) == 0) red[k][wave][rg >> 1][c0] = q;
+                    if ((rg & 1) == 0) red[k][wave][rg >> 1][sub] = q;
                 } else {
+                    // row groups 0, 2: the lane's columns m; 1, 3: its columns NPL / 2 + m, which
+                    // are consecutive, so one vector store per lane (32 lanes: 512 contiguous B)
+                    float q[NPL / 2];
 #pragma unroll
                     for (int m = 0; m < NPL / 2; ++m) {
                         auto pr = __builtin_amdgcn_permlane16_swap(as_i(u[m]), as_i(u[NPL / 2 + m]), false, false);
-                        // row groups 0, 2: columns m; 1, 3: columns NPL / 2 + m
-                        red[k][wave][rg >> 1][c0 + (rg & 1) * (NPL / 2) + m] = as_f(pr[0]) + as_f(pr[1]);
+                        q[m] = as_f(pr[0]) + as_f(pr[1]);
                     }
+                    float *dst = &red[k][wave][rg >> 1][col_of<NPL>(sub, (rg & 1) * (NPL / 2))];
+                    if constexpr (NPL == 8) *reinterpret_cast<float4 *>(dst) = make_float4(q[0], q[1], q[2], q[3]);
+                    else if constexpr (NPL == 4) *reinterpret_cast<float2 *>(dst) = make_float2(q[0], q[1]);
+                    else dst[0] = q[0];
                 }
             }
         }
         if (win > 0) ld.put(a, stg[cur ^ 1]);
         __syncthreads();
-        {   // the window's column sums over the four waves: NPL consecutive outputs per thread
-            const int o = tid * NPL;                          // of WIN x 2 x N
-            const int tok = o / (2 * a.N), qty = (o / a.N) & 1, col = o % a.N;
-            if (tok < cnt) {
-                float acc[NPL];
+        {   // the window's column sums over the four waves (WIN x 2 x N outputs): groups of
+            // V consecutive outputs, consecutive threads on consecutive groups
+            constexpr int V = NPL >= 4 ? 4 : NPL;
 #pragma unroll
-                for (int m = 0; m < NPL; ++m)
-                    acc[m] = ((red[tok][0][qty][col + m] + red[tok][1][qty][col + m]) + red[tok][2][qty][col + m]) +
-                             red[tok][3][qty][col + m];
-                stv<NPL>(part + (int64_t)(t0 + tok) * 2 * N + qty * N + col, acc);
+            for (int u = 0; u < NPL / V; ++u) {
+                const int o = V * tid + 256 * V * u;
+                const int tok = o / (2 * a.N), qty = (o / a.N) & 1, col = o % a.N;
+                if (tok < cnt) {
+                    float acc[V];
+#pragma unroll
+                    for (int m = 0; m < V; ++m)
+                        acc[m] = ((red[tok][0][qty][col + m] + red[tok][1][qty][col + m]) + red[tok][2][qty][col + m]) +
+                                 red[tok][3][qty][col + m];
+                    stv<V>(part + (int64_t)(t0 + tok) * 2 * N + qty * N + col, acc);
+                }
             }
             if (wtok < cnt) {
                 const int64_t at = ((ow.s * T + t0 + wtok) * H + ow.h) * P + ow.i;
@@ -364,7 +392,7 @@ __global__ void __launch_bounds__(256) ssm_bwd_kernel(const SsmArgs a) {
         }
         __syncthreads();
     }
-    stv<NPL>(a.ds0 + w.r * N + c0, gs);
+    st_cols<NPL>(a.ds0 + w.r * N, sub, gs);
 }
 
 // ---- combine: dB, dC over the segments of each group; ddt over the rows of each head ------
