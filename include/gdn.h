@@ -19,7 +19,14 @@
  *   The backward recomputes states from snapshots taken every C tokens (C ~ sqrt(T), the
  *   PR description); the snapshot interval changes memory and time, not the result.
  *
- * All floating point data is fp32.  Index arithmetic is 64-bit.
+ * Declared further down, under the same conventions: the steps around the recurrence in a
+ * hybrid layer -- the short causal convolution that produces the mixed q/k/v rows and its
+ * input gradient (gdn_ssm_conv_fwd / _bwd) and the per-row L2 normalisation of q and k and
+ * its backward (gdn_l2norm_fwd / _bwd) -- and a second reverse recurrence, the selective
+ * state-space scan of the Mamba-1 and Mamba-2 branches with its backward (gdn_ssm_*).
+ *
+ * All floating point data is fp32, apart from the inputs of gdn_fwd / gdn_bwd when
+ * gdn_problem.dtype selects a half type.  Index arithmetic is 64-bit.
  *
  * Ownership and concurrency
  *   - The caller owns every buffer.  The library allocates nothing and keeps no state
@@ -30,8 +37,9 @@
  *   - The workspace belongs to one call at a time; it may be reused once the stream has
  *     passed the call.  A workspace written by gdn_fwd holds that call's state snapshots
  *     (see GDN_BWD_REUSE_SNAPSHOTS).
- *   - Outputs (y, state_out, grad_packed) must not overlap any input, the workspace or each
- *     other; the host checks the address ranges and returns GDN_ERR_ARG on overlap.
+ *   - Outputs (y, state_out, grad_packed, ...) must not overlap any input, the workspace or
+ *     each other (gdn_l2norm_* alone may write exactly over an input view); the host checks
+ *     the address ranges and returns GDN_ERR_ARG on overlap.
  *     Inputs and cotangents are never written.
  *   - Inputs must be finite for the results to be meaningful (no NaN checks).  Values at
  *     padded tokens (t >= len_s) are never read.
