@@ -98,7 +98,34 @@ fwd_kernel(const FwdArgs a) {
 
     float *snap = a.snap + unit * a.n_ck_max * SV * SK + (int64_t)row0 * SK + lc;
     int until_snap = 0;
-    for (int t = 0; t < L; ++t) {
+    // A token's inputs.  Windows of W tokens are loaded one window ahead (two windows per
+    // loop trip, so neither buffer is copied): the loads of a window are in flight while the
+    // previous one is computed.  Loads past the sequence end are clamped to its last token.
+    constexpr int W = NC == 1 ? 8 : (NC == 2 ? 4 : 2);
+    struct Tok {
+        float q[NC], k[NC], g[KDA ? NC : 1], v[R], beta;
+    };
+    auto load = [&](Tok (&b)[W], int t0) __attribute__((always_inline)) {
+#pragma unroll
+        for (int w = 0; w < W; ++w) {
+            const int64_t t = min(t0 + w, L - 1);
+#pragma unroll
+            for (int n = 0; n < NC; ++n) {
+                b[w].q[n] = qp[t * a.sq.tok + n * LPR];
+                b[w].k[n] = kp[t * a.sk.tok + n * LPR];
+            }
+            if constexpr (KDA) {
+#pragma unroll
+                for (int n = 0; n < NC; ++n) b[w].g[n] = gp[t * a.sg.tok + n * LPR];
+            } else {
+                b[w].g[0] = gp[t * a.sg.tok];
+            }
+#pragma unroll
+            for (int r = 0; r < R; ++r) b[w].v[r] = vp[t * a.sv.tok + r];
+            b[w].beta = bp[t * a.sb.tok];
+        }
+    };
+    auto step = [&](const Tok &x, int t) __attribute__((always_inline)) {
         if (until_snap == 0) {
 #pragma unroll
             for (int r = 0; r < R; ++r)
@@ -108,27 +135,18 @@ fwd_kernel(const FwdArgs a) {
             until_snap = a.C;
         }
         --until_snap;
-        float qv[NC], kv[NC], av[NC], vv[R];
-#pragma unroll
-        for (int n = 0; n < NC; ++n) {
-            qv[n] = qp[t * a.sq.tok + n * LPR];
-            kv[n] = kp[t * a.sk.tok + n * LPR];
-        }
+        float av[NC];
         if constexpr (KDA) {
 #pragma unroll
-            for (int n = 0; n < NC; ++n) av[n] = expf(gp[t * a.sg.tok + n * LPR]);
+            for (int n = 0; n < NC; ++n) av[n] = expf(x.g[n]);
         } else {
-            const float a0 = expf(gp[t * a.sg.tok]);
+            const float a0 = expf(x.g[0]);
 #pragma unroll
             for (int n = 0; n < NC; ++n) av[n] = a0;
         }
-#pragma unroll
-        for (int r = 0; r < R; ++r) vv[r] = vp[t * a.sv.tok + r];
-        const float beta = bp[t * a.sb.tok];
-
         float ak[NC];
 #pragma unroll
-        for (int n = 0; n < NC; ++n) ak[n] = av[n] * kv[n];
+        for (int n = 0; n < NC; ++n) ak[n] = av[n] * x.k[n];
         float yr[R];
 #pragma unroll
         for (int r = 0; r < R; ++r) {
@@ -136,12 +154,12 @@ fwd_kernel(const FwdArgs a) {
 #pragma unroll
             for (int n = 0; n < NC; ++n) u = fmaf(M[r][n], ak[n], u);
             u = row16_sum(u);
-            const float delta = beta * (vv[r] - u);
+            const float delta = x.beta * (x.v[r] - u);
             float y = 0.f;
 #pragma unroll
             for (int n = 0; n < NC; ++n) {
-                M[r][n] = fmaf(delta, kv[n], M[r][n] * av[n]);
-                y = fmaf(M[r][n], qv[n], y);
+                M[r][n] = fmaf(delta, x.k[n], M[r][n] * av[n]);
+                y = fmaf(M[r][n], x.q[n], y);
             }
             yr[r] = y;
         }
@@ -154,6 +172,18 @@ fwd_kernel(const FwdArgs a) {
                 for (int r = 0; r < R; ++r) yp[r] = a.scale * yr[r];
             }
         }
+    };
+    Tok bufA[W], bufB[W];
+    if (L > 0) load(bufA, 0);
+    for (int t0 = 0; t0 < L; t0 += 2 * W) {
+        if (t0 + W < L) load(bufB, t0 + W);
+#pragma unroll
+        for (int w = 0; w < W; ++w)
+            if (t0 + w < L) step(bufA[w], t0 + w);
+        if (t0 + 2 * W < L) load(bufA, t0 + 2 * W);
+#pragma unroll
+        for (int w = 0; w < W; ++w)
+            if (t0 + W + w < L) step(bufB[w], t0 + W + w);
     }
     if (a.y) {
         for (int64_t t = L; t < a.T; ++t) {
