@@ -253,6 +253,35 @@ bwd_kernel(const BwdArgs a) {
     const int n_ck = (L + C - 1) / C;
     int parity = 0;
 
+    // Token inputs come in windows loaded one window ahead (two windows per loop trip, so no
+    // buffer is copied); loads past a segment's end are clamped into the segment.
+    constexpr int WR = NC == 1 ? 8 : (NC == 2 ? 4 : 2);    // replay window
+    constexpr int WW = NC == 1 ? 4 : (NC == 2 ? 2 : 1);    // walk window
+    struct RTok {
+        float k[NC], g[KDA ? NC : 1], v[R], beta;
+    };
+    struct WTok {
+        float q[NC], k[NC], g[KDA ? NC : 1], beta, gy[R], e[R], Mp[R][NC];
+    };
+    auto load_gate = [&](float (&g)[KDA ? NC : 1], int64_t t) __attribute__((always_inline)) {
+        if constexpr (KDA) {
+#pragma unroll
+            for (int n = 0; n < NC; ++n) g[n] = gp[t * a.sg.tok + n * LPR];
+        } else {
+            g[0] = gp[t * a.sg.tok];
+        }
+    };
+    auto decay = [&](const float (&g)[KDA ? NC : 1], float (&av)[NC]) __attribute__((always_inline)) {
+        if constexpr (KDA) {
+#pragma unroll
+            for (int n = 0; n < NC; ++n) av[n] = expf(g[n]);
+        } else {
+            const float a0 = expf(g[0]);
+#pragma unroll
+            for (int n = 0; n < NC; ++n) av[n] = a0;
+        }
+    };
+
     for (int sg = n_ck - 1; sg >= 0; --sg) {
         const int t0 = sg * C, t1 = min(t0 + C, L);
         // ---- replay the segment from its snapshot
@@ -263,24 +292,24 @@ bwd_kernel(const BwdArgs a) {
             for (int r = 0; r < R; ++r)
 #pragma unroll
                 for (int n = 0; n < NC; ++n) M[r][n] = sp[r * SK + n * LPR];
-            for (int t = t0; t < t1; ++t) {
-                float kv[NC], av[NC], vv[R];
+            auto rload = [&](RTok (&b)[WR], int tb) __attribute__((always_inline)) {
 #pragma unroll
-                for (int n = 0; n < NC; ++n) kv[n] = kp[t * a.sk.tok + n * LPR];
-                if constexpr (KDA) {
+                for (int w = 0; w < WR; ++w) {
+                    const int64_t t = min(tb + w, t1 - 1);
 #pragma unroll
-                    for (int n = 0; n < NC; ++n) av[n] = expf(gp[t * a.sg.tok + n * LPR]);
-                } else {
-                    const float a0 = expf(gp[t * a.sg.tok]);
+                    for (int n = 0; n < NC; ++n) b[w].k[n] = kp[t * a.sk.tok + n * LPR];
+                    load_gate(b[w].g, t);
 #pragma unroll
-                    for (int n = 0; n < NC; ++n) av[n] = a0;
+                    for (int r = 0; r < R; ++r) b[w].v[r] = vp[t * a.sv.tok + r];
+                    b[w].beta = bp[t * a.sb.tok];
                 }
-#pragma unroll
-                for (int r = 0; r < R; ++r) vv[r] = vp[t * a.sv.tok + r];
-                const float beta = bp[t * a.sb.tok];
+            };
+            auto rstep = [&](const RTok &x, int t) __attribute__((always_inline)) {
+                float av[NC];
+                decay(x.g, av);
                 float ak[NC];
 #pragma unroll
-                for (int n = 0; n < NC; ++n) ak[n] = av[n] * kv[n];
+                for (int n = 0; n < NC; ++n) ak[n] = av[n] * x.k[n];
                 float *dst = seg + (int64_t)(t - t0) * SV * SK;
                 float *edst = eb + (t - t0) * SV;
 #pragma unroll
@@ -289,84 +318,102 @@ bwd_kernel(const BwdArgs a) {
 #pragma unroll
                     for (int n = 0; n < NC; ++n) u = fmaf(M[r][n], ak[n], u);
                     u = row16_sum(u);
-                    const float e = vv[r] - u;
-                    const float delta = beta * e;
+                    const float e = x.v[r] - u;
+                    const float delta = x.beta * e;
 #pragma unroll
                     for (int n = 0; n < NC; ++n) {
                         const float mp = M[r][n] * av[n];
-                        M[r][n] = fmaf(delta, kv[n], mp);
+                        M[r][n] = fmaf(delta, x.k[n], mp);
                         dst[r * SK + n * LPR] = mp;  // keep the decayed previous state
                     }
                     if (lc == 0) edst[r] = e;
                 }
+            };
+            RTok ra[WR], rb[WR];
+            rload(ra, t0);
+            for (int tb = t0; tb < t1; tb += 2 * WR) {
+                if (tb + WR < t1) rload(rb, tb + WR);
+#pragma unroll
+                for (int w = 0; w < WR; ++w)
+                    if (tb + w < t1) rstep(ra[w], tb + w);
+                if (tb + 2 * WR < t1) rload(ra, tb + 2 * WR);
+#pragma unroll
+                for (int w = 0; w < WR; ++w)
+                    if (tb + WR + w < t1) rstep(rb[w], tb + WR + w);
             }
         }
         __threadfence_block();
         __syncthreads();
 
         // ---- reverse walk over the segment
-        for (int t = t1 - 1; t >= t0; --t) {
-            float qv[NC], kv[NC], av[NC], gyv[R], ev[R], Mp[R][NC];
+        auto wload = [&](WTok (&b)[WW], int tb) __attribute__((always_inline)) {
 #pragma unroll
-            for (int n = 0; n < NC; ++n) {
-                qv[n] = qp[t * a.sq.tok + n * LPR];
-                kv[n] = kp[t * a.sk.tok + n * LPR];
+            for (int w = 0; w < WW; ++w) {
+                const int64_t t = max(tb - w, t0);
+#pragma unroll
+                for (int n = 0; n < NC; ++n) {
+                    b[w].q[n] = qp[t * a.sq.tok + n * LPR];
+                    b[w].k[n] = kp[t * a.sk.tok + n * LPR];
+                }
+                load_gate(b[w].g, t);
+                b[w].beta = bp[t * a.sb.tok];
+                const float *src = seg + (int64_t)(t - t0) * SV * SK;
+                const float *esrc = eb + (t - t0) * SV;
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    b[w].gy[r] = gyp[t * a.sgy.tok + r];
+                    b[w].e[r] = esrc[r];
+#pragma unroll
+                    for (int n = 0; n < NC; ++n) b[w].Mp[r][n] = src[r * SK + n * LPR];
+                }
             }
-            if constexpr (KDA) {
+        };
+        auto wstep = [&](const WTok &x, int t) __attribute__((always_inline)) {
+            float av[NC];
+            decay(x.g, av);
+            const float beta = x.beta;
+            float gyv[R];
 #pragma unroll
-                for (int n = 0; n < NC; ++n) av[n] = expf(gp[t * a.sg.tok + n * LPR]);
-            } else {
-                const float a0 = expf(gp[t * a.sg.tok]);
-#pragma unroll
-                for (int n = 0; n < NC; ++n) av[n] = a0;
-            }
-            const float beta = bp[t * a.sb.tok];
-            const float *src = seg + (int64_t)(t - t0) * SV * SK;
-            const float *esrc = eb + (t - t0) * SV;
-#pragma unroll
-            for (int r = 0; r < R; ++r) {
-                gyv[r] = a.scale * gyp[t * a.sgy.tok + r];
-                ev[r] = esrc[r];
-#pragma unroll
-                for (int n = 0; n < NC; ++n) Mp[r][n] = src[r * SK + n * LPR];
-            }
+            for (int r = 0; r < R; ++r) gyv[r] = a.scale * x.gy[r];
 
             float pq[NC], pk[NC], pg[NC], dd[R];
+            float redg_one = 0.f;   // scalar-gate dg of a one-wave unit
+            (void)redg_one;
 #pragma unroll
             for (int n = 0; n < NC; ++n) pq[n] = pk[n] = pg[n] = 0.f;
 #pragma unroll
             for (int r = 0; r < R; ++r) {
-                const float delta = beta * ev[r];
+                const float delta = beta * x.e[r];
                 float d = 0.f;
 #pragma unroll
                 for (int n = 0; n < NC; ++n) {
-                    const float mt = fmaf(delta, kv[n], Mp[r][n]);  // M_t = Mp + delta k^T
-                    dM[r][n] = fmaf(gyv[r], qv[n], dM[r][n]);     // dM += scale gy q^T
-                    pq[n] = fmaf(mt, gyv[r], pq[n]);              // dq += M_t^T (scale gy)
-                    d = fmaf(dM[r][n], kv[n], d);                 // dd = dM k
+                    const float mt = fmaf(delta, x.k[n], x.Mp[r][n]);  // M_t = Mp + delta k^T
+                    dM[r][n] = fmaf(gyv[r], x.q[n], dM[r][n]);       // dM += scale gy q^T
+                    pq[n] = fmaf(mt, gyv[r], pq[n]);                 // dq += M_t^T (scale gy)
+                    d = fmaf(dM[r][n], x.k[n], d);                   // dd = dM k
                 }
                 dd[r] = row16_sum(d);
             }
             float pb = 0.f;
 #pragma unroll
             for (int r = 0; r < R; ++r) {
-                const float delta = beta * ev[r];
+                const float delta = beta * x.e[r];
                 const float du = -beta * dd[r];
-                pb = fmaf(dd[r], ev[r], pb);                      // dbeta = dd . (v - u)
+                pb = fmaf(dd[r], x.e[r], pb);                        // dbeta = dd . (v - u)
 #pragma unroll
                 for (int n = 0; n < NC; ++n) {
-                    pk[n] = fmaf(dM[r][n], delta, pk[n]);         // dk += dM^T delta
-                    pk[n] = fmaf(Mp[r][n], du, pk[n]);            //     + Mp^T du
-                    dM[r][n] = fmaf(du, kv[n], dM[r][n]);         // dM += du k^T
-                    pg[n] = fmaf(dM[r][n], Mp[r][n], pg[n]);      // dg = sum dM .* Mp
-                    dM[r][n] *= av[n];                            // dM = dM .* a
+                    pk[n] = fmaf(dM[r][n], delta, pk[n]);            // dk += dM^T delta
+                    pk[n] = fmaf(x.Mp[r][n], du, pk[n]);             //     + Mp^T du
+                    dM[r][n] = fmaf(du, x.k[n], dM[r][n]);           // dM += du k^T
+                    pg[n] = fmaf(dM[r][n], x.Mp[r][n], pg[n]);       // dg = sum dM .* Mp
+                    dM[r][n] *= av[n];                               // dM = dM .* a
                 }
             }
             if (lc == 0) {
                 float *dvp = a.dv + ((s * a.T + t) * a.H_v + h) * SV + row0;
 #pragma unroll
                 for (int r = 0; r < R; ++r) dvp[r] = beta * dd[r];
-                redb[parity][wave * RG + rg] = pb;
+                if constexpr (NW > 1) redb[parity][wave * RG + rg] = pb;
             }
 #pragma unroll
             for (int n = 0; n < NC; ++n) {
@@ -381,7 +428,29 @@ bwd_kernel(const BwdArgs a) {
 #pragma unroll
                 for (int n = 0; n < NC; ++n) gs += pg[n];
                 gs = groups4_sum(row16_sum(gs));
-                if (lane == 0) redg[parity][wave] = gs;
+                if constexpr (NW == 1) redg_one = 0.f + gs;
+                else if (lane == 0) redg[parity][wave] = gs;
+            }
+            const int64_t row_tok = s * a.T + t;
+            if constexpr (NW == 1) {
+                // one wave holds every row: the column sums above are complete, stored from
+                // registers; dbeta adds the row groups' values in the same order as below
+                if (rg == 0) {
+#pragma unroll
+                    for (int n = 0; n < NC; ++n) {
+                        a.dq[(row_tok * a.dqk_head + h) * SK + lc + n * LPR] = pq[n];
+                        a.dk[(row_tok * a.dqk_head + h) * SK + lc + n * LPR] = pk[n];
+                        if constexpr (KDA) a.dg[(row_tok * a.H_v + h) * G + lc + n * LPR] = pg[n];
+                    }
+                }
+                float pbs = as_f(__builtin_amdgcn_readlane(as_i(pb), 0));
+#pragma unroll
+                for (int q = 1; q < RG; ++q) pbs += as_f(__builtin_amdgcn_readlane(as_i(pb), q * LPR));
+                if (lane == 0) {
+                    a.dbeta[row_tok * a.H_v + h] = pbs;
+                    if constexpr (!KDA) a.dg[row_tok * a.H_v + h] = redg_one;
+                }
+                return;
             }
             if (rg == 0) {
 #pragma unroll
@@ -392,7 +461,6 @@ bwd_kernel(const BwdArgs a) {
                 }
             }
             __syncthreads();
-            const int64_t row_tok = s * a.T + t;
             for (int idx = tid; idx < (KDA ? 3 : 2) * SK; idx += Lo::THREADS) {
                 const int which = idx / SK, i = idx % SK;
                 float acc = 0.f;
@@ -418,6 +486,18 @@ bwd_kernel(const BwdArgs a) {
                 }
             }
             parity ^= 1;
+        };
+        WTok wa[WW], wb[WW];
+        wload(wa, t1 - 1);
+        for (int tb = t1 - 1; tb >= t0; tb -= 2 * WW) {
+            if (tb - WW >= t0) wload(wb, tb - WW);
+#pragma unroll
+            for (int w = 0; w < WW; ++w)
+                if (tb - w >= t0) wstep(wa[w], tb - w);
+            if (tb - 2 * WW >= t0) wload(wa, tb - 2 * WW);
+#pragma unroll
+            for (int w = 0; w < WW; ++w)
+                if (tb - WW - w >= t0) wstep(wb[w], tb - WW - w);
         }
     }
 
