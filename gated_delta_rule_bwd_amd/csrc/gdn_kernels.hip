@@ -591,36 +591,45 @@ hipError_t launch(const void *fn, const Args &args, int blocks, int threads, hip
 template <int SK, int SV, int R>
 constexpr int kThreads = Layout<SK, SV, R>::THREADS;
 
+// Rows per lane.  The forward's rows are independent, so it spreads a unit over more waves
+// (one row per lane group up to 64 rows): the scan is one serial chain per wave, and with a
+// few hundred units on 1024 SIMDs more, shorter waves finish sooner.  The backward keeps four
+// rows per lane (its column sums cross waves through LDS once per token).
+template <bool FWD, int SV>
+constexpr int kRows = FWD ? (SV <= 64 ? 1 : 2) : 4;
+
 // Launch a kernel template over the supported (key width, value width) pairs: every pair of
 // {16, 32, 64, 128} except 128 x 128 (the row-quarter kernels of gdn_s128.hip).
-template <int SK, int SV, typename Args, typename Pick>
+template <bool FWD, int SK, int SV, typename Args, typename Pick>
 hipError_t launch_pair(const Args &a, bool kda, int blocks, hipStream_t st, Pick pick) {
     if constexpr (SK == 128 && SV == 128) {
         return hipErrorInvalidValue;
     } else {
-        return launch(pick(std::integral_constant<int, SK>{}, std::integral_constant<int, SV>{}, kda), a,
-                      blocks, kThreads<SK, SV, 4>, st);
+        constexpr int R = kRows<FWD, SV>;
+        return launch(pick(std::integral_constant<int, SK>{}, std::integral_constant<int, SV>{},
+                           std::integral_constant<int, R>{}, kda),
+                      a, blocks, kThreads<SK, SV, R>, st);
     }
 }
 
-template <int SK, typename Args, typename Pick>
+template <bool FWD, int SK, typename Args, typename Pick>
 hipError_t launch_sv(const Args &a, int SV, bool kda, int blocks, hipStream_t st, Pick pick) {
     switch (SV) {
-        case 16: return launch_pair<SK, 16>(a, kda, blocks, st, pick);
-        case 32: return launch_pair<SK, 32>(a, kda, blocks, st, pick);
-        case 64: return launch_pair<SK, 64>(a, kda, blocks, st, pick);
-        case 128: return launch_pair<SK, 128>(a, kda, blocks, st, pick);
+        case 16: return launch_pair<FWD, SK, 16>(a, kda, blocks, st, pick);
+        case 32: return launch_pair<FWD, SK, 32>(a, kda, blocks, st, pick);
+        case 64: return launch_pair<FWD, SK, 64>(a, kda, blocks, st, pick);
+        case 128: return launch_pair<FWD, SK, 128>(a, kda, blocks, st, pick);
     }
     return hipErrorInvalidValue;
 }
 
-template <typename Args, typename Pick>
+template <bool FWD, typename Args, typename Pick>
 hipError_t launch_sizes(const Args &a, int SK, int SV, bool kda, int blocks, hipStream_t st, Pick pick) {
     switch (SK) {
-        case 16: return launch_sv<16>(a, SV, kda, blocks, st, pick);
-        case 32: return launch_sv<32>(a, SV, kda, blocks, st, pick);
-        case 64: return launch_sv<64>(a, SV, kda, blocks, st, pick);
-        case 128: return launch_sv<128>(a, SV, kda, blocks, st, pick);
+        case 16: return launch_sv<FWD, 16>(a, SV, kda, blocks, st, pick);
+        case 32: return launch_sv<FWD, 32>(a, SV, kda, blocks, st, pick);
+        case 64: return launch_sv<FWD, 64>(a, SV, kda, blocks, st, pick);
+        case 128: return launch_sv<FWD, 128>(a, SV, kda, blocks, st, pick);
     }
     return hipErrorInvalidValue;
 }
@@ -628,16 +637,16 @@ hipError_t launch_sizes(const Args &a, int SK, int SV, bool kda, int blocks, hip
 }  // namespace
 
 hipError_t launch_fwd(const FwdArgs &a, int SK, int SV, bool kda, int n_seqs_launch, hipStream_t st) {
-    return launch_sizes(a, SK, SV, kda, n_seqs_launch * a.H_v, st, [](auto sk, auto sv, bool k) {
-        constexpr int K = decltype(sk)::value, V = decltype(sv)::value;
-        return k ? (const void *)fwd_kernel<K, V, 4, true> : (const void *)fwd_kernel<K, V, 4, false>;
+    return launch_sizes<true>(a, SK, SV, kda, n_seqs_launch * a.H_v, st, [](auto sk, auto sv, auto r, bool k) {
+        constexpr int K = decltype(sk)::value, V = decltype(sv)::value, RR = decltype(r)::value;
+        return k ? (const void *)fwd_kernel<K, V, RR, true> : (const void *)fwd_kernel<K, V, RR, false>;
     });
 }
 
 hipError_t launch_bwd(const BwdArgs &a, int SK, int SV, bool kda, int n_seqs_launch, hipStream_t st) {
-    return launch_sizes(a, SK, SV, kda, n_seqs_launch * a.H_v, st, [](auto sk, auto sv, bool k) {
-        constexpr int K = decltype(sk)::value, V = decltype(sv)::value;
-        return k ? (const void *)bwd_kernel<K, V, 4, true> : (const void *)bwd_kernel<K, V, 4, false>;
+    return launch_sizes<false>(a, SK, SV, kda, n_seqs_launch * a.H_v, st, [](auto sk, auto sv, auto r, bool k) {
+        constexpr int K = decltype(sk)::value, V = decltype(sv)::value, RR = decltype(r)::value;
+        return k ? (const void *)bwd_kernel<K, V, RR, true> : (const void *)bwd_kernel<K, V, RR, false>;
     });
 }
 
