@@ -600,6 +600,8 @@ static int ssm_validate(const gdn_ssm_problem *p) {
         return GDN_ERR_ARG;
     if (p->N != 16 && p->N != 32 && p->N != 64 && p->N != 128) return GDN_ERR_UNSUPPORTED;
     if ((int64_t)p->P * (p->H / p->G) % 16 != 0) return GDN_ERR_UNSUPPORTED;
+    // one workgroup per 16 rows: the grid must fit a launch dimension
+    if ((int64_t)p->n_seqs * p->H * p->P / 16 > INT32_MAX) return GDN_ERR_UNSUPPORTED;
     return GDN_OK;
 }
 

@@ -342,6 +342,7 @@ def test_ssm_sizes_and_layout(B):
 @pytest.mark.parametrize("kw,code", [
     (dict(H=4, G=3), -1), (dict(N=24), -2), (dict(N=256), -2), (dict(P=3, H=4, G=2), -2),
     (dict(a_per_state=2), -1), (dict(dt_softplus=-1), -1), (dict(T=-1), -1), (dict(P=0), -1),
+    (dict(n_seqs=1 << 20, H=1 << 10, P=1 << 7, G=1), -2),    # 2^33 rows: beyond one launch
 ])
 def test_ssm_invalid_problems(B, kw, code):
     p = _ssm(B, **kw)
