@@ -181,8 +181,9 @@ __global__ void __launch_bounds__(256) gate128_kernel(const GateArgs a) {
 
 // ------------------------------------------------------------------ forward scan
 
-constexpr int FT = 256;            // forward threads: four waves of eight rows
-constexpr int FR = 2;              // rows per lane in the forward
+// Forward rows per lane FR: 2 (four waves of eight rows) when the launch has enough
+// workgroups to fill the chip, 1 (eight waves of four rows) when it has few, so that each
+// SIMD runs more, shorter scan chains.  The window staging is done by the first 256 threads.
 constexpr int FC = 8;              // columns per lane in the forward (16 lanes per row)
 constexpr int SP = S + 8;          // padded vector: column c at word c + 4 (c / 64)
 __device__ __forceinline__ int padc(int c) { return c + 4 * (c >> 6); }
@@ -198,10 +199,11 @@ struct alignas(16) FwdLds {
     float ys[2][WIN][QR], es[2][WIN][QR];                // outputs of the last two windows
 };
 
-template <bool KDA>
-__global__ void __launch_bounds__(FT)
+template <bool KDA, int FR>
+__global__ void __launch_bounds__(512 / FR)
 fwd128_kernel(const FwdArgs a) {
     constexpr int GW = KDA ? S : 1;
+    constexpr int FT = 512 / FR;                  // threads
     __shared__ FwdLds<KDA> sm;
     int ul, qb;
     map_block(blockIdx.x, gridDim.x, ul, qb);
@@ -213,7 +215,7 @@ fwd128_kernel(const FwdArgs a) {
     const int64_t unit = s * a.H_v + h;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int lc = lane & 15;                     // 8-column block of this lane
-    const int lrow = w * 8 + (lane >> 4) * FR;    // first of the lane's two rows (quarter)
+    const int lrow = w * (4 * FR) + (lane >> 4) * FR;   // first of the lane's rows (quarter)
     const int row = qb * QR + lrow;               // first of the lane's rows (state)
     const int cb = padc(lc * FC);                 // padded offset of the lane's columns
     const bool write_y = a.y != nullptr;
@@ -224,6 +226,7 @@ fwd128_kernel(const FwdArgs a) {
     // Global addresses are a uniform base (scalar arithmetic) plus a 32-bit per-thread offset.
     const int ci = tid & (S - 1), pci = padc(ci);
     const bool kside = uni(tid) < S;   // uniform: waves 0 and 1
+    const bool stager = uni(tid) < 2 * S;   // uniform: waves 0 to 3 stage the windows
     const int stt = tid >> 5, srow = tid & 31;
     const float *xp = kside ? a.k + s * a.sk.seq + hk * a.sk.head : a.q + s * a.sq.seq + hk * a.sq.head;
     const int64_t xtok = kside ? a.sk.tok : a.sq.tok;
@@ -268,6 +271,7 @@ fwd128_kernel(const FwdArgs a) {
     };
     auto load_window = [&](WinRegs &W, int t0, int cnt) __attribute__((always_inline)) {
         W.wdir = wfl[(int64_t)(t0 / WIN) * a.H_v];
+        if (FR == 2 || stager) {
 #pragma unroll
         for (int tt = 0; tt < WIN; ++tt) {   // clamped loads: no branch per token
             const int64_t t = t0 + min(tt, cnt - 1);
@@ -279,6 +283,7 @@ fwd128_kernel(const FwdArgs a) {
         const int tv = min(stt, cnt - 1), tb = min(tid & (WIN - 1), cnt - 1);
         W.rv = ldg(vp + (int64_t)t0 * a.sv.tok, (uint32_t)(tv * a.sv.tok + srow));
         W.rb = ldg(bp + (int64_t)t0 * a.sb.tok, (uint32_t)(tb * a.sb.tok));
+        }
     };
     // outputs of the window at t (cnt tokens) from output buffer ob
     auto flush = [&](int t, int cnt, int ob) {
@@ -307,8 +312,22 @@ fwd128_kernel(const FwdArgs a) {
 #pragma unroll
         for (int r = 0; r < FR; ++r) y[r] = row16_sum(y[r]);
         if (lc == 0) {
-            *reinterpret_cast<float2 *>(&sm.ys[ob][tt][lrow]) = make_float2(a.scale * y[0], a.scale * y[1]);
-            *reinterpret_cast<float2 *>(&sm.es[ob][tt][lrow]) = make_float2(e[0], e[1]);
+            if constexpr (FR == 2) {
+                *reinterpret_cast<float2 *>(&sm.ys[ob][tt][lrow]) = make_float2(a.scale * y[0], a.scale * y[1]);
+                *reinterpret_cast<float2 *>(&sm.es[ob][tt][lrow]) = make_float2(e[0], e[1]);
+            } else {
+                sm.ys[ob][tt][lrow] = a.scale * y[0];
+                sm.es[ob][tt][lrow] = e[0];
+            }
+        }
+    };
+    auto vrows = [&](int tt, float (&vr)[FR]) __attribute__((always_inline)) {
+        if constexpr (FR == 2) {
+            const float2 v2 = *reinterpret_cast<const float2 *>(&sm.vq[tt][lrow]);
+            vr[0] = v2.x;
+            vr[1] = v2.y;
+        } else {
+            vr[0] = sm.vq[tt][lrow];
         }
     };
     // One window from register set W: stage its vectors; store the previous window's outputs
@@ -319,7 +338,8 @@ fwd128_kernel(const FwdArgs a) {
         __syncthreads();   // the previous window's vectors are no longer read
         const bool direct = W.wdir != 0;
         // (one store target per wave, chosen up front: k rows for waves 0 and 1, q rows else)
-        if (!direct) {
+        if (FR == 1 && !stager) {
+        } else if (!direct) {
             float ce = W.av[0];   // product over the window: c at its last token
             float *xc = kside ? &sm.kc[0][0] : &sm.qc[0][0];
 #pragma unroll
@@ -351,7 +371,8 @@ fwd128_kernel(const FwdArgs a) {
                 ld8(&sm.kc[tt][cb], kc);
                 ld8(&sm.kr[tt][cb], kr);
                 ld8(&sm.qc[tt][cb], qc);
-                const float2 vr = *reinterpret_cast<const float2 *>(&sm.vq[tt][lrow]);
+                float vr[FR];
+                vrows(tt, vr);
                 const float beta = sm.bt[tt];
                 float u[FR], e[FR], y[FR];
 #pragma unroll
@@ -361,8 +382,8 @@ fwd128_kernel(const FwdArgs a) {
                     for (int n = 1; n < FC; ++n) u[r] = fmaf(M[r][n], kc[n], u[r]);
                     u[r] = row16_sum(u[r]);
                 }
-                e[0] = vr.x - u[0];
-                e[1] = vr.y - u[1];
+#pragma unroll
+                for (int r = 0; r < FR; ++r) e[r] = vr[r] - u[r];
 #pragma unroll
                 for (int r = 0; r < FR; ++r) {
                     const float de = beta * e[r];
@@ -396,7 +417,8 @@ fwd128_kernel(const FwdArgs a) {
 #pragma unroll
                     for (int n = 0; n < FC; ++n) gv[n] = sm.araw[tt][0];
                 }
-                const float2 vr = *reinterpret_cast<const float2 *>(&sm.vq[tt][lrow]);
+                float vr[FR];
+                vrows(tt, vr);
                 const float beta = sm.bt[tt];
                 float u[FR], e[FR], y[FR];
 #pragma unroll
@@ -406,8 +428,8 @@ fwd128_kernel(const FwdArgs a) {
                     for (int n = 0; n < FC; ++n) u[r] = fmaf(M[r][n], gv[n] * kv[n], u[r]);
                     u[r] = row16_sum(u[r]);
                 }
-                e[0] = vr.x - u[0];
-                e[1] = vr.y - u[1];
+#pragma unroll
+                for (int r = 0; r < FR; ++r) e[r] = vr[r] - u[r];
 #pragma unroll
                 for (int r = 0; r < FR; ++r) {
                     const float de = beta * e[r];
@@ -1229,8 +1251,11 @@ hipError_t launch_gate128(const GateArgs &a, hipStream_t st) {
 
 hipError_t launch_fwd128(const FwdArgs &a, bool kda, int n_seqs_launch, hipStream_t st) {
     const int blocks = n_seqs_launch * a.H_v * NQ;
-    return kda ? launch((const void *)fwd128_kernel<true>, a, blocks, FT, st)
-               : launch((const void *)fwd128_kernel<false>, a, blocks, FT, st);
+    if (blocks < 512)   // fewer than two workgroups per CU: one row per lane, eight waves
+        return kda ? launch((const void *)fwd128_kernel<true, 1>, a, blocks, 512, st)
+                   : launch((const void *)fwd128_kernel<false, 1>, a, blocks, 512, st);
+    return kda ? launch((const void *)fwd128_kernel<true, 2>, a, blocks, 256, st)
+               : launch((const void *)fwd128_kernel<false, 2>, a, blocks, 256, st);
 }
 
 hipError_t launch_bwd128(const BwdArgs &a, bool kda, int n_seqs_launch, hipStream_t st) {
