@@ -211,19 +211,25 @@ __global__ void __launch_bounds__(256) ssm_fwd_kernel(const SsmArgs a) {
     float Ah = 0.f;
     if constexpr (APS) ld_cols<NPL>(a.A + w.h * N, sub, Aj);
     else Ah = a.A[w.h];
-    Loader<NPL, false> ld;
-    ld.init(a, r0, tid);
+    // window j is loaded into register set j % PD at the start of window j - PD + 1, staged
+    // into LDS at the end of window j - 1: PD - 1 windows of compute cover its load latency
+    constexpr int PD = 3;
+    Loader<NPL, false> ld[PD];
+#pragma unroll
+    for (int q = 0; q < PD; ++q) ld[q].init(a, r0, tid);
     const int wr = tid & 15, wtok = (tid & 127) >> 4;   // y writer: row, token
     const Row ow = row_of(a, r0 + wr);
-    if (nwin > 0) {
-        ld.load(a, 0, min(WIN, a.T));
-        ld.put(a, stg[0]);
-    }
+    auto wcnt = [&](int j) { return min(WIN, a.T - j * WIN); };
+#pragma unroll
+    for (int q = 0; q < PD - 1; ++q)
+        if (q < nwin) ld[q].load(a, q * WIN, wcnt(q));
+    if (nwin > 0) ld[0].put(a, stg[0]);
     __syncthreads();
-    for (int win = 0; win < nwin; ++win) {
+    auto window = [&](int win, auto u) __attribute__((always_inline)) {
+        constexpr int U = decltype(u)::value;            // win % PD
         const int cur = win & 1;
-        const int t0 = win * WIN, cnt = min(WIN, a.T - t0);
-        if (win + 1 < nwin) ld.load(a, t0 + WIN, min(WIN, a.T - t0 - WIN));
+        const int t0 = win * WIN, cnt = wcnt(win);
+        if (win + PD - 1 < nwin) ld[(U + PD - 1) % PD].load(a, (win + PD - 1) * WIN, wcnt(win + PD - 1));
         st_cols<NPL>(a.ck + (w.r * nwin + win) * N, sub, st);     // state before the window
         const Stage &sg = stg[cur];
 #pragma unroll
@@ -246,10 +252,15 @@ __global__ void __launch_bounds__(256) ssm_fwd_kernel(const SsmArgs a) {
                 if (sub == 0) ys[cur][k][rho] = yp;
             }
         }
-        if (win + 1 < nwin) ld.put(a, stg[cur ^ 1]);
+        if (win + 1 < nwin) ld[(U + 1) % PD].put(a, stg[cur ^ 1]);
         __syncthreads();
         if (a.y && tid < 128 && wtok < cnt)
             a.y[((ow.s * T + t0 + wtok) * H + ow.h) * P + ow.i] = ys[cur][wtok][wr];
+    };
+    for (int win = 0; win < nwin; win += PD) {
+        window(win, std::integral_constant<int, 0>{});
+        if (win + 1 < nwin) window(win + 1, std::integral_constant<int, 1>{});
+        if (win + 2 < nwin) window(win + 2, std::integral_constant<int, 2>{});
     }
     if (a.s_out) st_cols<NPL>(a.s_out + w.r * N, sub, st);
 }
