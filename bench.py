@@ -49,40 +49,66 @@ def parse():
                          "the FETCH_SIZE / WRITE_SIZE counters) and exit")
     ap.add_argument("--pmc-summary", default=None, metavar="DIR",
                     help="summarise rocprofv3 counter runs under DIR (fetch/, write/, cfetch/, "
-                         "cwrite/ with run_counter_collection.csv) into the traffic file under "
-                         "profiles/ and exit")
+                         "cwrite/ with run_counter_collection.csv) of --op / --workload into "
+                         "its traffic file under profiles/ and exit")
     return ap.parse_args()
 
 
-# Kernel sources whose hash stamps a traffic measurement: a measurement is reported only
-# while the kernels are unchanged.
-KERNEL_SOURCES = ["gated_delta_rule_bwd_amd/csrc/gdn_s128.hip", "gated_delta_rule_bwd_amd/csrc/gdn_api.hip",
-                  "gated_delta_rule_bwd_amd/csrc/gdn_internal.h"]
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_layer_kda_s128.json")
-BWD_KERNELS = ("bwd128_kernel", "combine128_kernel")   # the kernels of one gdn_bwd call
+# Traffic measurements: per (op, workload), the kernels of the timed call whose HBM bytes make
+# the roofline's `traffic`, the file holding the counter summary, and the sources whose hash
+# stamps it (a summary is reported only while those sources are unchanged).
+_C = "gated_delta_rule_bwd_amd/csrc/"
+TRAFFIC = {
+    ("gdn", "layer_kda_s128"): {
+        "file": "traffic_layer_kda_s128.json",
+        "sources": [_C + "gdn_s128.hip", _C + "gdn_api.hip", _C + "gdn_internal.h"],
+        "kernels": ("bwd128_kernel<true>", "combine128_kernel<4>")},
+    ("ssm_conv", "conv_layer_d10240_k4"): {
+        "file": "traffic_conv_layer_d10240_k4.json",
+        "sources": [_C + "ssm_conv.hip", _C + "gdn_internal.h"],
+        "kernels": ("conv_kernel<4, 4, true>",)},
+    ("l2norm", "l2norm_layer_qk_rows"): {
+        "file": "traffic_l2norm_layer_qk_rows.json",
+        "sources": [_C + "l2norm.hip", _C + "gdn_internal.h"],
+        "kernels": ("l2norm_kernel<4, 16, true>",)},
+    ("ssm_scan", "ssm2_layer_h80_p64_n128"): {
+        "file": "traffic_ssm2_layer_h80_p64_n128.json",
+        "sources": [_C + "ssm_scan.hip", _C + "gdn_api.hip", _C + "gdn_internal.h"],
+        "kernels": ("ssm_bwd_kernel<8, false>", "ssm_combine_kernel")},
+    ("ssm_scan", "ssm1_layer_d5120_n16"): {
+        "file": "traffic_ssm1_layer_d5120_n16.json",
+        "sources": [_C + "ssm_scan.hip", _C + "gdn_api.hip", _C + "gdn_internal.h"],
+        "kernels": ("ssm_bwd_kernel<1, true>", "ssm_combine_kernel")},
+}
 
 
-def sources_hash():
+def sources_hash(sources):
     import hashlib
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in sources:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
 
 
-def pmc_summary(d):
-    """Per-dispatch HBM bytes of every kernel from FETCH_SIZE / WRITE_SIZE runs, each scaled
-    by what the same counter reads for the plain copy of --copy-calibration."""
-    import csv
+def kernel_key(name):
+    """A kernel's name with its template arguments, without namespaces and parameters."""
     import re
+    m = re.search(r"(\w+_kernel(?:<[^()]*>)?)\(", name)
+    return m.group(1) if m else name[:64]
+
+
+def pmc_summary(d, op, workload):
+    """Per-dispatch HBM bytes of every kernel from FETCH_SIZE / WRITE_SIZE runs (d/fetch,
+    d/write), each scaled by what the same counter reads for the plain copy of
+    --copy-calibration (d/cfetch, d/cwrite)."""
+    import csv
 
     def load(sub):
         out, disp = {}, {}
         with open(os.path.join(d, sub, "run_counter_collection.csv")) as f:
             for r in csv.DictReader(f):
-                m = re.search(r"(\w+_kernel)", r["Kernel_Name"])
-                k = m.group(1) if m else r["Kernel_Name"][:48]
+                k = kernel_key(r["Kernel_Name"])
                 out[(k, r["Counter_Name"])] = out.get((k, r["Counter_Name"]), 0.0) + float(r["Counter_Value"])
                 disp.setdefault(k, set()).add(r["Dispatch_Id"])
         return out, {k: len(v) for k, v in disp.items()}
@@ -103,25 +129,29 @@ def pmc_summary(d):
             continue
         kernels[k] = {"fetch_bytes": fe[(k, "FETCH_SIZE")] * 1024 * fetch_scale / nfe[k],
                       "write_bytes": wr[(k, "WRITE_SIZE")] * 1024 * write_scale / nwr[k]}
-    return {"workload": "layer_kda_s128", "source_sha256": sources_hash(),
+    spec = TRAFFIC[(op, workload)]
+    return {"op": op, "workload": workload, "source_sha256": sources_hash(spec["sources"]),
             "counter_scale": {"fetch": fetch_scale, "write": write_scale},
             "kernels": kernels}
 
 
-def traffic_bytes():
-    """HBM bytes of one gdn_bwd call from the committed counter summary, or None when the
-    summary is missing or the kernels changed since it was taken."""
+def traffic_bytes(op, workload):
+    """HBM bytes of one timed call (the roofline kernels) from the committed counter summary,
+    or None when there is none or the kernels changed since it was taken."""
+    spec = TRAFFIC.get((op, workload))
+    if spec is None:
+        return None
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(os.path.join(ROOT, "profiles", spec["file"])) as f:
             t = json.load(f)
     except OSError:
         return None
-    if t.get("source_sha256") != sources_hash():
+    if t.get("source_sha256") != sources_hash(spec["sources"]):
         return None
     ks = t["kernels"]
-    if not all(k in ks for k in BWD_KERNELS):
+    if not all(k in ks for k in spec["kernels"]):
         return None
-    return sum(ks[k]["fetch_bytes"] + ks[k]["write_bytes"] for k in BWD_KERNELS)
+    return sum(ks[k]["fetch_bytes"] + ks[k]["write_bytes"] for k in spec["kernels"])
 
 
 def copy_calibration(mib):
@@ -215,7 +245,7 @@ def bench_conv(args):
         "roofline": {"bound": "hbm", "kernel": "conv_kernel (backward launch)",
                      "achieved": launch_bytes / (bwd_ms / 1e3) / 1e9, "peak": PEAK_HBM / 1e9,
                      "unit": "GB/s", "frac": launch_bytes / (bwd_ms / 1e3) / PEAK_HBM,
-                     "traffic": None},
+                     "traffic": traffic_bytes("ssm_conv", cfg["name"])},
         "fwd_GBps": launch_bytes / (fwd_ms / 1e3) / 1e9,
     }
     if not args.no_cpu_baseline:
@@ -284,7 +314,7 @@ def bench_l2norm(args):
         "roofline": {"bound": "hbm", "kernel": "l2norm_kernel (backward launch)",
                      "achieved": 3 * tensor / (bwd_ms / 1e3) / 1e9, "peak": PEAK_HBM / 1e9,
                      "unit": "GB/s", "frac": 3 * tensor / (bwd_ms / 1e3) / PEAK_HBM,
-                     "traffic": None},
+                     "traffic": traffic_bytes("l2norm", "l2norm_layer_qk_rows")},
         "fwd_GBps": 2 * tensor / (fwd_ms / 1e3) / 1e9,
     }
     if not args.no_cpu_baseline:
@@ -368,7 +398,7 @@ def bench_ssm(args):
         "roofline": {"bound": "alu", "kernel": "gdn_ssm_bwd (ssm_bwd_kernel + ssm_combine_kernel)",
                      "achieved": bwd_flops / (bwd_ms / 1e3) / 1e12, "peak": PEAK_FP32_VALU / 1e12,
                      "unit": "TFLOP/s", "frac": bwd_flops / (bwd_ms / 1e3) / PEAK_FP32_VALU,
-                     "traffic": None},
+                     "traffic": traffic_bytes("ssm_scan", name)},
     }
     if not args.no_cpu_baseline:
         import oracle.ssm_scan as OS
@@ -404,8 +434,12 @@ def main():
         {"ssm_conv": bench_conv, "l2norm": bench_l2norm, "ssm_scan": bench_ssm}[args.op](args)
         return
     if args.pmc_summary:
-        summ = pmc_summary(args.pmc_summary)
-        with open(TRAFFIC_FILE, "w") as f:
+        from gated_delta_rule_bwd_amd import inputs as I
+        wl = args.workload or {"gdn": I.HEADLINE, "ssm_conv": I.CONV_LAYER["name"],
+                               "l2norm": "l2norm_layer_qk_rows",
+                               "ssm_scan": "ssm2_layer_h80_p64_n128"}[args.op]
+        summ = pmc_summary(args.pmc_summary, args.op, wl)
+        with open(os.path.join(ROOT, "profiles", TRAFFIC[(args.op, wl)]["file"]), "w") as f:
             json.dump(summ, f, indent=1)
         print(json.dumps(summ, indent=1))
         return
@@ -489,7 +523,7 @@ def main():
                      "gdn_bwd (bwd_kernel" + (" + combine_kernel)" if w.H_v != w.H_k else ")"),
                      "achieved": achieved / 1e12, "peak": PEAK_FP32_VALU / 1e12,
                      "unit": "TFLOP/s", "frac": achieved / PEAK_FP32_VALU,
-                     "traffic": traffic_bytes() if w.name == "layer_kda_s128" else None},
+                     "traffic": traffic_bytes("gdn", w.name)},
     }
     if not args.no_cpu_baseline:
         cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else 8
