@@ -9,6 +9,13 @@ inputs already resident in HBM.  Prints one JSON line.
 Metric: tokens x value-heads per second, fwd+bwd, and the fraction of the FP32 vector peak
 (157.3 TFLOP/s) that the credited work reaches.  Credited work per token x head is
 28 S^2 flops: forward 7 S^2, segment replay 5 S^2, reverse walk 16 S^2.
+
+The same line, with the roofline of each op's own bound, for the other entry points:
+  --op ssm_conv   the short convolution fwd+bwd on the layer shape's packed rows (HBM)
+  --op l2norm     the q/k row normalisation fwd+bwd on the same rows (HBM)
+  --op ssm_scan   the selective scan fwd+bwd, --workload ssm2_layer_h80_p64_n128 (default) or
+                  ssm1_layer_d5120_n16 (FP32 VALU)
+Helpers for the counter summaries in profiles/: --copy-calibration MIB, --pmc-summary DIR.
 """
 from __future__ import annotations
 
