@@ -75,7 +75,9 @@ Plan make_plan(const gdn_problem *p) {
     pl.G = p->gate == GDN_GATE_KDA ? p->S_k : 1;
     pl.units = (int64_t)p->n_seqs * p->H_v;
     size_t off = 0;
-    if (p->dtype != GDN_DTYPE_F32) {   // widened inputs (offsets in floats from off_in)
+    // half-precision inputs of the small-head kernels are widened into fp32 copies first
+    // (offsets in floats from off_in); the head-128 kernels read them as they are
+    if (p->dtype != GDN_DTYPE_F32 && !pl.s128) {
         const size_t nt = (size_t)p->n_seqs * p->T;
         pl.off_in = off;
         pl.in_q = 0;
@@ -201,6 +203,7 @@ hipError_t launch_gates(const gdn_problem *p, const Plan &pl, const float *g, vo
     gdn::GateArgs ga;
     std::memset(&ga, 0, sizeof(ga));
     ga.g = g;
+    ga.dtype = p->dtype;
     ga.cbuf = (float *)((char *)ws + pl.off_a);
     ga.dbuf = ga.cbuf + pl.gate_floats;
     ga.wflag = (int32_t *)((char *)ws + pl.off_wf);
@@ -320,7 +323,7 @@ int gdn_fwd(const gdn_problem *p, const void *q_in, const void *k_in, const void
     gdn_problem pc = *p;
     const float *q = (const float *)q_in, *k = (const float *)k_in, *v = (const float *)v_in;
     const float *g = (const float *)g_in, *beta = (const float *)beta_in;
-    if (p->dtype != GDN_DTYPE_F32) {
+    if (p->dtype != GDN_DTYPE_F32 && !pl.s128) {
         rc = widen_inputs(p, pl, ws, q_in, k_in, v_in, g_in, beta_in, nullptr, (hipStream_t)stream, pc,
                           q, k, v, g, beta, nullptr);
         if (rc != GDN_OK) return rc;
@@ -339,6 +342,7 @@ int gdn_fwd(const gdn_problem *p, const void *q_in, const void *k_in, const void
     a.sq = p->q; a.sk = p->k; a.sv = p->v; a.sg = p->g; a.sb = p->beta; a.sy = p->y;
     a.T = p->T; a.H_k = p->H_k; a.H_v = p->H_v; a.C = pl.C; a.n_ck_max = pl.n_ck_max;
     a.scale = p->scale;
+    a.dtype = p->dtype;
     for (int s0 = 0; s0 < p->n_seqs; s0 += gdn::kMaxSeqsPerLaunch) {
         const int cnt = std::min(gdn::kMaxSeqsPerLaunch, p->n_seqs - s0);
         a.s_base = s0;
@@ -388,12 +392,13 @@ int gdn_bwd(const gdn_problem *p, const void *q_in, const void *k_in, const void
         if (overlap(outg, i) || overlap(wsr, i)) return GDN_ERR_ARG;
     if (overlap(outg, wsr)) return GDN_ERR_ARG;
 
-    // half-precision inputs: gy widened into the workspace, and q, k, v, g, beta too unless the
-    // forward on the same inputs left their copies there (GDN_BWD_REUSE_SNAPSHOTS)
+    // half-precision inputs of the small-head kernels: gy widened into the workspace, and q, k,
+    // v, g, beta too unless the forward on the same inputs left their copies there
+    // (GDN_BWD_REUSE_SNAPSHOTS); the head-128 kernels read the half values directly
     gdn_problem pc = *p;
     const float *q = (const float *)q_in, *k = (const float *)k_in, *v = (const float *)v_in;
     const float *g = (const float *)g_in, *beta = (const float *)beta_in, *gy = (const float *)gy_in;
-    if (p->dtype != GDN_DTYPE_F32) {
+    if (p->dtype != GDN_DTYPE_F32 && !pl.s128) {
         const bool reuse = flags & GDN_BWD_REUSE_SNAPSHOTS;
         rc = widen_inputs(p, pl, ws, reuse ? nullptr : q_in, reuse ? nullptr : k_in,
                           reuse ? nullptr : v_in, reuse ? nullptr : g_in, reuse ? nullptr : beta_in,
@@ -422,6 +427,7 @@ int gdn_bwd(const gdn_problem *p, const void *q_in, const void *k_in, const void
             f.s_base = s0;
             f.T = p->T; f.H_k = p->H_k; f.H_v = p->H_v; f.C = pl.C; f.n_ck_max = pl.n_ck_max;
             f.scale = p->scale;
+            f.dtype = p->dtype;
             fill_lens(p, s0, cnt, f.lens);
             if (pl.s128) {
                 rc = device_status(launch_gates(p, pl, g, ws, s0, cnt, (hipStream_t)stream));
@@ -464,6 +470,7 @@ int gdn_bwd(const gdn_problem *p, const void *q_in, const void *k_in, const void
         b.s_base = s0;
         b.T = p->T; b.H_k = p->H_k; b.H_v = p->H_v; b.C = pl.C; b.n_ck_max = pl.n_ck_max;
         b.scale = p->scale;
+        b.dtype = p->dtype;
         fill_lens(p, s0, cnt, b.lens);
         if (pl.s128) {
             rc = device_status(gdn::launch_bwd128(b, kda, cnt, (hipStream_t)stream));

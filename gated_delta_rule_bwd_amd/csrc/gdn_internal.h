@@ -30,6 +30,9 @@ struct FwdArgs {
     int32_t s_base;    // first sequence of this launch
     int32_t T, H_k, H_v, C, n_ck_max;
     float scale;
+    // element type (GDN_DTYPE_*) of q, k, v, g, beta, which the S = 128 kernels read as such
+    // (widened exactly at the load); the other kernels always receive fp32
+    int32_t dtype;
     int32_t lens[kMaxSeqsPerLaunch];
 };
 
@@ -55,6 +58,7 @@ struct BwdArgs {
     int32_t s_base;
     int32_t T, H_k, H_v, C, n_ck_max;
     float scale;
+    int32_t dtype;      // element type of q, k, v, g, beta, gy (see FwdArgs)
     int32_t lens[kMaxSeqsPerLaunch];
 };
 
@@ -66,6 +70,7 @@ struct GateArgs {
     int32_t *wflag;              // [n_seqs][ceil(T / 8)][H_v]
     gdn_strides sg;
     int32_t s_base, n_seqs_launch, T, H_v, G;
+    int32_t dtype;               // element type of g (see FwdArgs)
     int32_t lens[kMaxSeqsPerLaunch];
 };
 

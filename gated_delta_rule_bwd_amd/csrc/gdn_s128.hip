@@ -93,6 +93,32 @@ __device__ __forceinline__ void stg(T *base, uint32_t i, T v) {
     *reinterpret_cast<T *>(reinterpret_cast<char *>(base) + i * (uint32_t)sizeof(T)) = v;
 }
 __device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// Element type DT (GDN_DTYPE_*) of the caller's q, k, v, g, beta and gy: fp32, IEEE binary16
+// or bfloat16, read as such and widened to fp32 exactly at the load.
+template <int DT>
+struct InT {
+    using type = float;
+};
+template <>
+struct InT<GDN_DTYPE_F16> {
+    using type = _Float16;
+};
+template <>
+struct InT<GDN_DTYPE_BF16> {
+    using type = uint16_t;
+};
+template <int DT>
+using In = typename InT<DT>::type;
+template <int DT>
+__device__ __forceinline__ float fin(In<DT> x) {
+    if constexpr (DT == GDN_DTYPE_BF16) return __builtin_bit_cast(float, (uint32_t)x << 16);
+    else return (float)x;
+}
+template <int DT>
+__device__ __forceinline__ const In<DT> *inp(const float *p) {
+    return reinterpret_cast<const In<DT> *>(p);
+}
 // Compiler-only memory barrier: bounds how far the compiler hoists LDS loads (and so how many
 // registers they hold); it emits no instruction.
 __device__ __forceinline__ void hoist_fence() { asm volatile("" ::: "memory"); }
@@ -123,6 +149,7 @@ __device__ __forceinline__ bool prod_ok(float c) { return c >= kScaleMin; }
 // the same array in both cases and need the flag only when they use the values.  One wave
 // per window for the per-channel gate (lane: columns lane, lane + 64), one thread per window
 // for the scalar gate.
+template <int DT>
 __global__ void __launch_bounds__(256) gate128_kernel(const GateArgs a) {
     const int nwin = (a.T + WIN - 1) / WIN;
     const int64_t items = (int64_t)a.n_seqs_launch * nwin * a.H_v;
@@ -148,8 +175,8 @@ __global__ void __launch_bounds__(256) gate128_kernel(const GateArgs a) {
             for (int n = 0; n < 2; ++n) {
                 av[tt][n] = 1.f;
                 if (tt < cnt && n < NC) {
-                    const float *gp = a.g + s * a.sg.seq + (int64_t)(t0 + tt) * a.sg.tok + h * a.sg.head;
-                    av[tt][n] = expf(gp[kda ? lane + 64 * n : 0]);
+                    const In<DT> *gp = inp<DT>(a.g) + s * a.sg.seq + (int64_t)(t0 + tt) * a.sg.tok + h * a.sg.head;
+                    av[tt][n] = expf(fin<DT>(gp[kda ? lane + 64 * n : 0]));
                 }
             }
         float c[2] = {1.f, 1.f};
@@ -199,7 +226,7 @@ struct alignas(16) FwdLds {
     float ys[2][WIN][QR], es[2][WIN][QR];                // outputs of the last two windows
 };
 
-template <bool KDA, int FR>
+template <bool KDA, int FR, int DT>
 __global__ void __launch_bounds__(512 / FR)
 fwd128_kernel(const FwdArgs a) {
     constexpr int GW = KDA ? S : 1;
@@ -228,10 +255,11 @@ fwd128_kernel(const FwdArgs a) {
     const bool kside = uni(tid) < S;   // uniform: waves 0 and 1
     const bool stager = uni(tid) < 2 * S;   // uniform: waves 0 to 3 stage the windows
     const int stt = tid >> 5, srow = tid & 31;
-    const float *xp = kside ? a.k + s * a.sk.seq + hk * a.sk.head : a.q + s * a.sq.seq + hk * a.sq.head;
+    const In<DT> *xp = kside ? inp<DT>(a.k) + s * a.sk.seq + hk * a.sk.head
+                             : inp<DT>(a.q) + s * a.sq.seq + hk * a.sq.head;
     const int64_t xtok = kside ? a.sk.tok : a.sq.tok;
-    const float *vp = a.v + s * a.sv.seq + h * a.sv.head + qb * QR;
-    const float *bp = a.beta + s * a.sb.seq + h * a.sb.head;
+    const In<DT> *vp = inp<DT>(a.v) + s * a.sv.seq + h * a.sv.head + qb * QR;
+    const In<DT> *bp = inp<DT>(a.beta) + s * a.sb.seq + h * a.sb.head;
     const int64_t tok_ae = a.H_v;   // token stride of cbuf / ebuf rows, in rows
     const float *cp = a.cbuf + (s * a.T * a.H_v + h) * GW;
     const int nwin_T = (a.T + WIN - 1) / WIN;
@@ -265,8 +293,9 @@ fwd128_kernel(const FwdArgs a) {
     // the gate a in an unscaled one), the k or q value, v and beta, and the window's flag.  Two
     // register sets take turns, so each window's loads are issued two windows before its
     // staging uses them.
-    struct WinRegs {
-        float av[WIN], xv[WIN], rv, rb;
+    struct WinRegs {   // k / q, v and beta kept in the input type until staged
+        float av[WIN];
+        In<DT> xv[WIN], rv, rb;
         int wdir;
     };
     auto load_window = [&](WinRegs &W, int t0, int cnt) __attribute__((always_inline)) {
@@ -276,9 +305,9 @@ fwd128_kernel(const FwdArgs a) {
         for (int tt = 0; tt < WIN; ++tt) {   // clamped loads: no branch per token
             const int64_t t = t0 + min(tt, cnt - 1);
             const float g = ldg(cp + t * tok_ae * GW, (uint32_t)(KDA ? ci : 0));
-            const float x = ldg(xp + t * xtok, (uint32_t)ci);
+            const In<DT> x = ldg(xp + t * xtok, (uint32_t)ci);
             W.av[tt] = tt < cnt ? g : 1.f;
-            W.xv[tt] = tt < cnt ? x : 0.f;
+            W.xv[tt] = tt < cnt ? x : In<DT>(0);
         }
         const int tv = min(stt, cnt - 1), tb = min(tid & (WIN - 1), cnt - 1);
         W.rv = ldg(vp + (int64_t)t0 * a.sv.tok, (uint32_t)(tv * a.sv.tok + srow));
@@ -345,20 +374,21 @@ fwd128_kernel(const FwdArgs a) {
 #pragma unroll
             for (int tt = 0; tt < WIN; ++tt) {
                 if (tt < cnt) ce = W.av[tt];
-                xc[tt * SP + pci] = W.xv[tt] * W.av[tt];
-                if (kside) sm.kr[tt][pci] = W.xv[tt] * rcp(W.av[tt]);
+                const float xv = fin<DT>(W.xv[tt]);
+                xc[tt * SP + pci] = xv * W.av[tt];
+                if (kside) sm.kr[tt][pci] = xv * rcp(W.av[tt]);
             }
             if (kside && (KDA || ci == 0)) sm.cend[KDA ? pci : 0] = ce;
         } else {
             float *xr = kside ? &sm.kraw[0][0] : &sm.qraw[0][0];
 #pragma unroll
             for (int tt = 0; tt < WIN; ++tt) {
-                xr[tt * SP + pci] = W.xv[tt];
+                xr[tt * SP + pci] = fin<DT>(W.xv[tt]);
                 if (kside && (KDA || ci == 0)) sm.araw[tt][KDA ? pci : 0] = W.av[tt];
             }
         }
-        if (stt < cnt) sm.vq[stt][srow] = W.rv;
-        if (tid < cnt) sm.bt[tid] = W.rb;
+        if (stt < cnt) sm.vq[stt][srow] = fin<DT>(W.rv);
+        if (tid < cnt) sm.bt[tid] = fin<DT>(W.rb);
         __syncthreads();
         flush(prev_ta, prev_cnt, ob ^ 1);
         if (ta % C == 0) rw_state(snap + (int64_t)(ta / C) * S * S, true);   // checkpoint
@@ -517,7 +547,7 @@ struct alignas(16) BwdLds {
     float D2w[NW][WIN][WIN];   // [wave][t][s]: delta_s . dd_t over the wave's rows
 };
 
-template <bool KDA>
+template <bool KDA, int DT>
 __global__ void __launch_bounds__(BT, 1)
 bwd128_kernel(const BwdArgs a) {
     constexpr int GW = KDA ? S : 1;
@@ -544,8 +574,8 @@ bwd128_kernel(const BwdArgs a) {
     const float *snapu = a.snap + unit * a.n_ck_max * S * S + (int64_t)row0 * S + lane;
     float4 *vsb = reinterpret_cast<float4 *>(a.vsbuf) +
                   ((unit * NQ + qb) * (int64_t)a.nvs_max) * (RW / 2 * BT) + tid;
-    const float *kp = a.k + s * a.sk.seq + hk * a.sk.head;
-    const float *qp = a.q + s * a.sq.seq + hk * a.sq.head;
+    const In<DT> *kp = inp<DT>(a.k) + s * a.sk.seq + hk * a.sk.head;
+    const In<DT> *qp = inp<DT>(a.q) + s * a.sq.seq + hk * a.sq.head;
     // window gate factors, token stride tok_ae * GW: running products c and suffix products d
     // (an unscaled window: the gates a, and 1)
     const float *cb = a.cbuf + (s * a.T * a.H_v + h) * GW;
@@ -553,8 +583,8 @@ bwd128_kernel(const BwdArgs a) {
     const int nwin_T = (a.T + WIN - 1) / WIN;
     const int32_t *wfl = a.wflag + s * nwin_T * a.H_v + h;            // window stride H_v
     const float *eb = a.ebuf + (s * a.T * a.H_v + h) * S + qb * QR;  // errors, token stride tok_ae*S
-    const float *gyp = a.gy + s * a.sgy.seq + h * a.sgy.head + qb * QR;
-    const float *bp = a.beta + s * a.sb.seq + h * a.sb.head;
+    const In<DT> *gyp = inp<DT>(a.gy) + s * a.sgy.seq + h * a.sgy.head + qb * QR;
+    const In<DT> *bp = inp<DT>(a.beta) + s * a.sb.seq + h * a.sb.head;
 
     float X[RW][2];   // the walked gradient dM (scaled by d inside a window)
     if (a.dstate_out) {
@@ -573,7 +603,8 @@ bwd128_kernel(const BwdArgs a) {
     // exact), beta e, the product over each window and the unscaled-window flags
     auto stage_stretch = [&](int va, int vb) {
         constexpr int NTASK = NWS / CT;   // windows per thread
-        float kv[NTASK][WIN], cv[NTASK][WIN];
+        In<DT> kv[NTASK][WIN];            // in the input type until used
+        float cv[NTASK][WIN];
         int cn[NTASK];
 #pragma unroll
         for (int x = 0; x < NTASK; ++x) {
@@ -582,27 +613,29 @@ bwd128_kernel(const BwdArgs a) {
 #pragma unroll
             for (int tt = 0; tt < WIN; ++tt) {   // clamped loads (no branch per token)
                 const int64_t t = min(t0 + tt, vb - 1);
-                const float k = kp[t * a.sk.tok + ci], c = cb[t * tok_ae * GW + (KDA ? ci : 0)];
-                kv[x][tt] = tt < cn[x] ? k : 0.f;
+                const In<DT> k = kp[t * a.sk.tok + ci];
+                const float c = cb[t * tok_ae * GW + (KDA ? ci : 0)];
+                kv[x][tt] = tt < cn[x] ? k : In<DT>(0);
                 cv[x][tt] = tt < cn[x] ? c : 1.f;
             }
         }
         int fl = 0;
         if (tid < NWS && va + tid * WIN < vb) fl = wfl[(int64_t)((va + tid * WIN) / WIN) * a.H_v];
         constexpr int NDE = VS * QR / BT;
-        float ev[NDE], bv[NDE];
+        float ev[NDE];
+        In<DT> bv[NDE];
 #pragma unroll
         for (int x = 0; x < NDE; ++x) {
             const int tr = (tid >> 5) + (BT / QR) * x;   // token within the stretch
             const int64_t t = va + tr;
             ev[x] = va + tr < vb ? eb[t * tok_ae * S + (tid & 31)] : 0.f;
-            bv[x] = va + tr < vb ? bp[t * a.sb.tok] : 0.f;
+            bv[x] = va + tr < vb ? bp[t * a.sb.tok] : In<DT>(0);
         }
         __syncthreads();   // the previous users of the slot area are done
         if (tid < NWS) sm.wflag[tid] = fl;
 #pragma unroll
         for (int x = 0; x < NDE; ++x)
-            reinterpret_cast<float *>(sm.sa.det[(tid >> 5) + (BT / QR) * x])[tid & 31] = bv[x] * ev[x];
+            reinterpret_cast<float *>(sm.sa.det[(tid >> 5) + (BT / QR) * x])[tid & 31] = fin<DT>(bv[x]) * ev[x];
         __syncthreads();
 #pragma unroll
         for (int x = 0; x < NTASK; ++x) {
@@ -611,7 +644,7 @@ bwd128_kernel(const BwdArgs a) {
 #pragma unroll
             for (int tt = 0; tt < WIN; ++tt) {
                 if (tt < cn[x]) c = cv[x][tt];
-                reinterpret_cast<float *>(&sm.sa.kt[m * WIN + tt][ci & 63])[ci >> 6] = kv[x][tt] * rcp(cv[x][tt]);
+                reinterpret_cast<float *>(&sm.sa.kt[m * WIN + tt][ci & 63])[ci >> 6] = fin<DT>(kv[x][tt]) * rcp(cv[x][tt]);
             }
             if (KDA || ci < 64) {
                 if (KDA) reinterpret_cast<float *>(&sm.sa.cend[m][ci & 63])[ci >> 6] = c;
@@ -651,7 +684,7 @@ bwd128_kernel(const BwdArgs a) {
             for (int tt = 0; tt < cnt; ++tt) {
                 const int tr = m * WIN + tt;
                 const int64_t t = t0 + tt;
-                const float kv[2] = {kp[t * a.sk.tok + lane], kp[t * a.sk.tok + lane + 64]};
+                const float kv[2] = {fin<DT>(kp[t * a.sk.tok + lane]), fin<DT>(kp[t * a.sk.tok + lane + 64])};
                 const float av[2] = {cb[t * tok_ae * GW + (KDA ? lane : 0)],
                                      cb[t * tok_ae * GW + (KDA ? lane + 64 : 0)]};
                 float dv[RW];
@@ -668,7 +701,9 @@ bwd128_kernel(const BwdArgs a) {
     // holds, for columns (lane, lane + 64) of token tok, the window's running product c and
     // the product d of its later gates (an unscaled window: the gate a, and 1), k, q, and
     // beta; thread tid < WIN * QR holds gy, e and beta of row tid & 31 of token tid >> 5
-    float wc[2], wd[2], wk[2], wq[2], wbt = 0.f, rgy = 0.f, re = 0.f, rb = 0.f;
+    // (k, q, beta and gy kept in the input type until staged)
+    float wc[2], wd[2], re = 0.f;
+    In<DT> wk[2], wq[2], wbt = In<DT>(0), rgy = In<DT>(0), rb = In<DT>(0);
     int wlast = 0;   // the window's last token
     auto load_window = [&](int t0, int cnt) {
         const int64_t t = t0 + w;
@@ -677,10 +712,10 @@ bwd128_kernel(const BwdArgs a) {
         for (int n = 0; n < 2; ++n) {
             wc[n] = w < cnt ? cb[t * tok_ae * GW + (KDA ? lane + 64 * n : 0)] : 1.f;
             wd[n] = w < cnt ? db[t * tok_ae * GW + (KDA ? lane + 64 * n : 0)] : 1.f;
-            wk[n] = w < cnt ? kp[t * a.sk.tok + lane + 64 * n] : 0.f;
-            wq[n] = w < cnt ? qp[t * a.sq.tok + lane + 64 * n] : 0.f;
+            wk[n] = w < cnt ? kp[t * a.sk.tok + lane + 64 * n] : In<DT>(0);
+            wq[n] = w < cnt ? qp[t * a.sq.tok + lane + 64 * n] : In<DT>(0);
         }
-        wbt = w < cnt ? bp[t * a.sb.tok] : 0.f;
+        wbt = w < cnt ? bp[t * a.sb.tok] : In<DT>(0);
         if (tid < WIN * QR && (tid >> 5) < cnt) {
             const int64_t tr = t0 + (tid >> 5);
             rgy = gyp[tr * a.sgy.tok + (tid & 31)];
@@ -693,23 +728,27 @@ bwd128_kernel(const BwdArgs a) {
         const int tt = w;
         const float c[2] = {wc[0], wc[1]}, d[2] = {wd[0], wd[1]};   // unscaled: the gate, 1
         const float rd[2] = {direct ? 1.f : rcp(d[0]), direct ? 1.f : rcp(d[1])};
-        sm.wv[tt][lane] = make_float4(wk[0] * d[0], wk[1] * d[1], scale * wq[0] * rd[0], scale * wq[1] * rd[1]);
-        sm.wh[tt][lane] = make_float2(-wbt * wk[0] * rd[0], -wbt * wk[1] * rd[1]);
-        sm.kt8[tt][lane] = direct ? make_float2(wk[0], wk[1])
-                                  : make_float2(wk[0] * rcp(c[0]), wk[1] * rcp(c[1]));
+        const float kk[2] = {fin<DT>(wk[0]), fin<DT>(wk[1])}, qq[2] = {fin<DT>(wq[0]), fin<DT>(wq[1])};
+        const float bt = fin<DT>(wbt);
+        sm.wv[tt][lane] = make_float4(kk[0] * d[0], kk[1] * d[1], scale * qq[0] * rd[0], scale * qq[1] * rd[1]);
+        sm.wh[tt][lane] = make_float2(-bt * kk[0] * rd[0], -bt * kk[1] * rd[1]);
+        sm.kt8[tt][lane] = direct ? make_float2(kk[0], kk[1])
+                                  : make_float2(kk[0] * rcp(c[0]), kk[1] * rcp(c[1]));
         sm.pcd[tt][lane] = make_float4(c[0], c[1], d[0], d[1]);
         if (tt == wlast) sm.pP[lane] = direct ? make_float2(1.f, 1.f) : make_float2(c[0], c[1]);   // window product
-        if (lane == 0) sm.bt[tt] = wbt;
+        if (lane == 0) sm.bt[tt] = bt;
         if (tid < WIN * QR) {   // rows: beta e, gy, e, and the sum of (beta e) gy per token
             const int rt = tid >> 5, r = tid & 31;
-            const float de = rb * re;
+            const float gyv = fin<DT>(rgy);
+            const float de = fin<DT>(rb) * re;
             reinterpret_cast<float *>(sm.de8[rt])[r] = de;
-            reinterpret_cast<float *>(sm.gy8[rt])[r] = rgy;
+            reinterpret_cast<float *>(sm.gy8[rt])[r] = gyv;
             reinterpret_cast<float *>(sm.e8[rt])[r] = re;
-            const float p = half_sum(rt < cnt ? de * rgy : 0.f);
+            const float p = half_sum(rt < cnt ? de * gyv : 0.f);
             if (r == 0) sm.s1[rt] = p;
         }
     };
+
 
     // ---- dg.  Each token's dg is colsum(dMp .* Mp).  At the first token t0 of a window it
     // equals colsum(dM_out .* M0), with dM_out the walked gradient before the window and M0
@@ -1246,22 +1285,38 @@ hipError_t launch_gate128(const GateArgs &a, hipStream_t st) {
     if (items <= 0) return hipSuccess;
     int64_t blocks = a.G == 1 ? (items + 255) / 256 : (items + 3) / 4;
     if (blocks > 8192) blocks = 8192;
-    return launch((const void *)gate128_kernel, a, (int)blocks, 256, st);
+    const void *fn = a.dtype == GDN_DTYPE_BF16  ? (const void *)gate128_kernel<GDN_DTYPE_BF16>
+                     : a.dtype == GDN_DTYPE_F16 ? (const void *)gate128_kernel<GDN_DTYPE_F16>
+                                                : (const void *)gate128_kernel<GDN_DTYPE_F32>;
+    return launch(fn, a, (int)blocks, 256, st);
 }
 
 hipError_t launch_fwd128(const FwdArgs &a, bool kda, int n_seqs_launch, hipStream_t st) {
     const int blocks = n_seqs_launch * a.H_v * NQ;
-    if (blocks < 512)   // fewer than two workgroups per CU: one row per lane, eight waves
-        return kda ? launch((const void *)fwd128_kernel<true, 1>, a, blocks, 512, st)
-                   : launch((const void *)fwd128_kernel<false, 1>, a, blocks, 512, st);
-    return kda ? launch((const void *)fwd128_kernel<true, 2>, a, blocks, 256, st)
-               : launch((const void *)fwd128_kernel<false, 2>, a, blocks, 256, st);
+    const bool few = blocks < 512;   // fewer than two workgroups per CU: one row per lane, eight waves
+    const void *fn = nullptr;
+#define GDN_F128(DT)                                                                                  \
+    fn = few ? (kda ? (const void *)fwd128_kernel<true, 1, DT> : (const void *)fwd128_kernel<false, 1, DT>) \
+             : (kda ? (const void *)fwd128_kernel<true, 2, DT> : (const void *)fwd128_kernel<false, 2, DT>);
+    if (a.dtype == GDN_DTYPE_BF16) {
+        GDN_F128(GDN_DTYPE_BF16)
+    } else if (a.dtype == GDN_DTYPE_F16) {
+        GDN_F128(GDN_DTYPE_F16)
+    } else {
+        GDN_F128(GDN_DTYPE_F32)
+    }
+#undef GDN_F128
+    return launch(fn, a, blocks, few ? 512 : 256, st);
 }
 
 hipError_t launch_bwd128(const BwdArgs &a, bool kda, int n_seqs_launch, hipStream_t st) {
     const int blocks = n_seqs_launch * a.H_v * NQ;
-    return kda ? launch((const void *)bwd128_kernel<true>, a, blocks, BT, st)
-               : launch((const void *)bwd128_kernel<false>, a, blocks, BT, st);
+    const void *fn = a.dtype == GDN_DTYPE_BF16
+                         ? (kda ? (const void *)bwd128_kernel<true, GDN_DTYPE_BF16> : (const void *)bwd128_kernel<false, GDN_DTYPE_BF16>)
+                     : a.dtype == GDN_DTYPE_F16
+                         ? (kda ? (const void *)bwd128_kernel<true, GDN_DTYPE_F16> : (const void *)bwd128_kernel<false, GDN_DTYPE_F16>)
+                         : (kda ? (const void *)bwd128_kernel<true, GDN_DTYPE_F32> : (const void *)bwd128_kernel<false, GDN_DTYPE_F32>);
+    return launch(fn, a, blocks, BT, st);
 }
 
 hipError_t launch_combine128(const Combine128Args &a, hipStream_t st) {

@@ -72,8 +72,8 @@ extern "C" {
 /* Element type of the inputs q, k, v, g, beta and gy (gdn_problem.dtype).  The state, y and
  * every gradient are fp32 (the contract of "Training kernels and gradients", introduction:
  * half-precision inputs, fp32 gradient storage).  Half-precision inputs are widened exactly
- * to fp32 in the workspace before the fp32 kernels run, so the results equal those of fp32
- * inputs holding the same values. */
+ * to fp32 (at the load for head size 128; into workspace copies for the other head sizes), so
+ * the results equal those of fp32 inputs holding the same values. */
 #define GDN_DTYPE_F32 0
 #define GDN_DTYPE_F16 1
 #define GDN_DTYPE_BF16 2

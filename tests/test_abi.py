@@ -218,6 +218,10 @@ def test_half_inputs_workspace_and_alignment(B):
             widened = (2 * n * T * Hk * S + 2 * n * T * Hv * S + n * T * Hv * G + n * T * Hv) * 4
             ph = problem(B, dtype=dt, kda=kda)
             assert B.workspace_size(ph) == al(widened) + expected_ws(n, T, Hk, Hv, S, 8, kda=kda)
+    # head size 128 reads half inputs directly: no copies, the fp32 workspace
+    for dt in (1, 2):
+        assert B.workspace_size(problem(B, dtype=dt, S=128, C=16)) == \
+            B.workspace_size(problem(B, dtype=0, S=128, C=16))
     ph = problem(B, dtype=2)
     ws = B.workspace_size(ph)
     a = layout_ptrs(ph, B)
