@@ -69,7 +69,7 @@ TRAFFIC = {
     ("gdn", "layer_kda_s128"): {
         "file": "traffic_layer_kda_s128.json",
         "sources": [_C + "gdn_s128.hip", _C + "gdn_api.hip", _C + "gdn_internal.h"],
-        "kernels": ("bwd128_kernel<true>", "combine128_kernel<4>")},
+        "kernels": ("bwd128_kernel<true, 0>", "combine128_kernel<4>")},
     ("ssm_conv", "conv_layer_d10240_k4"): {
         "file": "traffic_conv_layer_d10240_k4.json",
         "sources": [_C + "ssm_conv.hip", _C + "gdn_internal.h"],
