@@ -60,6 +60,27 @@ def test_parity_layer_shape_sampled(dev):
             ", ".join(f"{k} {v:.1e}" for k, v in rep.items()))
 
 
+def test_layer_shape_bf16_inputs_bitwise(dev):
+    """Full-size layer shape with bf16 inputs, as the benchmark's bf16 mode launches it: every
+    output is bitwise equal to the fp32-input run on the same (rounded) values, which holds at
+    any size because the kernels widen each input exactly at the load; the fp32 kernels' own
+    parity at this shape is sampled against the oracle above."""
+    w = I.WORKLOADS["layer_kda_s128"]
+    log(f"[parity] {w.name} full size, bf16 inputs against fp32 inputs holding the same values")
+    arrays = I.round_inputs(I.make_all(w)[0], "bf16")
+    outs = []
+    for dt in (torch.bfloat16, torch.float32):
+        dc = dev(w, arrays, in_dtype=dt)
+        dc.fwd()
+        dc.bwd(reuse=True)
+        torch.cuda.synchronize()
+        outs.append((dc.y.clone(), dc.state_out.clone(), dc.grad.clone()))
+        del dc
+    for name, a, b in zip(("y", "state_out", "grad"), *outs):
+        assert torch.equal(a, b), name
+    assert bool(torch.isfinite(outs[0][2]).all())
+
+
 def test_parity_long_context_sampled(dev):
     """Full-size long-context workload (one 65536-token sequence, 48 value heads, interval
     256, scalar gate); the oracle checks one key head with its three value heads over the
