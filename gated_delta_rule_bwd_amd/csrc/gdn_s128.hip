@@ -338,12 +338,24 @@ fwd128_kernel(const FwdArgs a) {
         x[4] = v1.x; x[5] = v1.y; x[6] = v1.z; x[7] = v1.w;
     };
     auto finish = [&](int tt, int ob, float (&y)[FR], const float (&e)[FR]) {
+        if constexpr (FR == 2) {
+            // The two row sums only need to reach one lane each: the half-rows swap the
+            // partials of the row they do not keep (lanes 0-7 keep row 0, 8-15 row 1), then
+            // each half sums its eight lanes (6 operations instead of two 16-lane sums' 8).
+            const bool hi = (lc & 8) != 0;
+            float keep = hi ? y[1] : y[0];
+            keep += dpp<0x128>(hi ? y[0] : y[1]);   // row_ror:8, lane i <- lane i ^ 8
+            keep += dpp<0xB1>(keep);                // quad_perm [1,0,3,2]
+            keep += dpp<0x4E>(keep);                // quad_perm [2,3,0,1]
+            keep += dpp<0x141>(keep);               // row_half_mirror
+            if ((lc & 7) == 0) sm.ys[ob][tt][lrow + (hi ? 1 : 0)] = a.scale * keep;
+            if (lc == 0) *reinterpret_cast<float2 *>(&sm.es[ob][tt][lrow]) = make_float2(e[0], e[1]);
+            return;
+        }
 #pragma unroll
         for (int r = 0; r < FR; ++r) y[r] = row16_sum(y[r]);
         if (lc == 0) {
             if constexpr (FR == 2) {
-                *reinterpret_cast<float2 *>(&sm.ys[ob][tt][lrow]) = make_float2(a.scale * y[0], a.scale * y[1]);
-                *reinterpret_cast<float2 *>(&sm.es[ob][tt][lrow]) = make_float2(e[0], e[1]);
             } else {
                 sm.ys[ob][tt][lrow] = a.scale * y[0];
                 sm.es[ob][tt][lrow] = e[0];
