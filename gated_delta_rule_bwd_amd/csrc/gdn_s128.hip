@@ -244,6 +244,10 @@ fwd128_kernel(const FwdArgs a) {
     const int lc = lane & 15;                     // 8-column block of this lane
     const int lrow = w * (4 * FR) + (lane >> 4) * FR;   // first of the lane's rows (quarter)
     const int row = qb * QR + lrow;               // first of the lane's rows (state)
+    // With two rows per lane, lanes 8-15 of each 16-lane row group hold them in swapped order
+    // (register r holds row lrow + (r ^ hsw)): lanes i and i ^ 8 then hold the same row in
+    // registers 0 and 1, so both rows' sums are one reduce-scatter without selects.
+    const int hsw = (FR == 2 && (lc & 8)) ? 1 : 0;
     const int cb = padc(lc * FC);                 // padded offset of the lane's columns
     const bool write_y = a.y != nullptr;
 
@@ -272,7 +276,7 @@ fwd128_kernel(const FwdArgs a) {
         for (int r = 0; r < FR; ++r)
 #pragma unroll
             for (int j = 0; j < FC; j += 4) {
-                float4 *p4 = reinterpret_cast<float4 *>(base + (int64_t)(row + r) * S + lc * FC + j);
+                float4 *p4 = reinterpret_cast<float4 *>(base + (int64_t)(row + (r ^ hsw)) * S + lc * FC + j);
                 if (store) *p4 = make_float4(M[r][j], M[r][j + 1], M[r][j + 2], M[r][j + 3]);
                 else { const float4 v = *p4; M[r][j] = v.x; M[r][j + 1] = v.y; M[r][j + 2] = v.z; M[r][j + 3] = v.w; }
             }
@@ -284,7 +288,7 @@ fwd128_kernel(const FwdArgs a) {
 #pragma unroll
         for (int r = 0; r < FR; ++r)
 #pragma unroll
-            for (int n = 0; n < FC; ++n) M[r][n] = a.state0[unit * S * S + (int64_t)(row + r) * S + lc * FC + n];
+            for (int n = 0; n < FC; ++n) M[r][n] = a.state0[unit * S * S + (int64_t)(row + (r ^ hsw)) * S + lc * FC + n];
     }
     // the state has arrived before the scan starts, so no wait inside the scan is charged to it
     __builtin_amdgcn_s_waitcnt(0);
@@ -337,18 +341,32 @@ fwd128_kernel(const FwdArgs a) {
         x[0] = v0.x; x[1] = v0.y; x[2] = v0.z; x[3] = v0.w;
         x[4] = v1.x; x[5] = v1.y; x[6] = v1.z; x[7] = v1.w;
     };
+    // Two rows per lane: the row of register 0 summed over the eight lanes of each half of the
+    // 16-lane group (lanes i and i ^ 8 first pair register 0 with the partner's register 1,
+    // which holds the same row); every lane of a half receives its half's sum.
+    auto pair_reduce = [&](float r0, float r1) __attribute__((always_inline)) {
+        float t = r0 + dpp<0x128>(r1);   // row_ror:8, lane i <- lane i ^ 8
+        t += dpp<0xB1>(t);               // quad_perm [1,0,3,2]
+        t += dpp<0x4E>(t);               // quad_perm [2,3,0,1]
+        t += dpp<0x141>(t);              // row_half_mirror
+        return t;
+    };
+    // the row sums of u on every lane of the row group
+    auto row_sums = [&](float (&u)[FR]) __attribute__((always_inline)) {
+        if constexpr (FR == 2) {
+            const float t = pair_reduce(u[0], u[1]);
+            u[1] = dpp<0x128>(t);        // the other half's sum: this lane's register-1 row
+            u[0] = t;
+        } else {
+            u[0] = row16_sum(u[0]);
+        }
+    };
     auto finish = [&](int tt, int ob, float (&y)[FR], const float (&e)[FR]) {
         if constexpr (FR == 2) {
-            // The two row sums only need to reach one lane each: the half-rows swap the
-            // partials of the row they do not keep (lanes 0-7 keep row 0, 8-15 row 1), then
-            // each half sums its eight lanes (6 operations instead of two 16-lane sums' 8).
-            const bool hi = (lc & 8) != 0;
-            float keep = hi ? y[1] : y[0];
-            keep += dpp<0x128>(hi ? y[0] : y[1]);   // row_ror:8, lane i <- lane i ^ 8
-            keep += dpp<0xB1>(keep);                // quad_perm [1,0,3,2]
-            keep += dpp<0x4E>(keep);                // quad_perm [2,3,0,1]
-            keep += dpp<0x141>(keep);               // row_half_mirror
-            if ((lc & 7) == 0) sm.ys[ob][tt][lrow + (hi ? 1 : 0)] = a.scale * keep;
+            // The two output sums only need to reach one lane each: lanes 0-7 sum register 0's
+            // row, lanes 8-15 register 0's (the other) row.
+            const float keep = pair_reduce(y[0], y[1]);
+            if ((lc & 7) == 0) sm.ys[ob][tt][lrow + hsw] = a.scale * keep;
             if (lc == 0) *reinterpret_cast<float2 *>(&sm.es[ob][tt][lrow]) = make_float2(e[0], e[1]);
             return;
         }
@@ -364,9 +382,8 @@ fwd128_kernel(const FwdArgs a) {
     };
     auto vrows = [&](int tt, float (&vr)[FR]) __attribute__((always_inline)) {
         if constexpr (FR == 2) {
-            const float2 v2 = *reinterpret_cast<const float2 *>(&sm.vq[tt][lrow]);
-            vr[0] = v2.x;
-            vr[1] = v2.y;
+            vr[0] = sm.vq[tt][lrow + hsw];
+            vr[1] = sm.vq[tt][lrow + (hsw ^ 1)];
         } else {
             vr[0] = sm.vq[tt][lrow];
         }
@@ -422,8 +439,8 @@ fwd128_kernel(const FwdArgs a) {
                     u[r] = M[r][0] * kc[0];
 #pragma unroll
                     for (int n = 1; n < FC; ++n) u[r] = fmaf(M[r][n], kc[n], u[r]);
-                    u[r] = row16_sum(u[r]);
                 }
+                row_sums(u);
 #pragma unroll
                 for (int r = 0; r < FR; ++r) e[r] = vr[r] - u[r];
 #pragma unroll
@@ -468,8 +485,8 @@ fwd128_kernel(const FwdArgs a) {
                     u[r] = 0.f;
 #pragma unroll
                     for (int n = 0; n < FC; ++n) u[r] = fmaf(M[r][n], gv[n] * kv[n], u[r]);
-                    u[r] = row16_sum(u[r]);
                 }
+                row_sums(u);
 #pragma unroll
                 for (int r = 0; r < FR; ++r) e[r] = vr[r] - u[r];
 #pragma unroll
@@ -509,7 +526,7 @@ fwd128_kernel(const FwdArgs a) {
 #pragma unroll
             for (int r = 0; r < FR; ++r)
 #pragma unroll
-                for (int n = 0; n < FC; ++n) a.state_out[unit * S * S + (int64_t)(row + r) * S + lc * FC + n] = M[r][n];
+                for (int n = 0; n < FC; ++n) a.state_out[unit * S * S + (int64_t)(row + (r ^ hsw)) * S + lc * FC + n] = M[r][n];
         }
     }
 }
