@@ -13,7 +13,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libgdn.so")
-SOURCES = ["gdn_api.hip", "gdn_kernels.hip", "gdn_s128.hip", "ssm_conv.hip", "l2norm.hip",
+SOURCES = ["gdn_api.hip", "gdn_kernels.hip", "gdn_mf.hip", "ssm_conv.hip", "l2norm.hip",
            "ssm_scan.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

@@ -31,10 +31,9 @@ struct Plan {
     int64_t units = 0;
     bool s128 = false;   // head size 128: row-quarter kernels
     bool parts = false;  // small heads: dq/dk go through per-value-head partials
-    int nvs_max = 1;     // S_k = S_v = 128: 64-token stretches per segment
+    int nvs_max = 1;     // S_k = S_v = 128: replayed stretches per segment
     size_t off_snap = 0, off_seg = 0, off_e = 0, off_pq = 0, off_pk = 0;
-    size_t off_a = 0, gate_floats = 0, off_wf = 0, off_vs = 0, off_part = 0, off_pb = 0, off_pg = 0,
-           off_hf = 0;
+    size_t off_wm = 0, off_wf = 0, off_vs = 0, off_part = 0, off_pb = 0, off_hf = 0;
     // half-precision inputs: their fp32 copies, contiguous [n_seqs][T][heads][width] each
     size_t off_in = 0, in_q = 0, in_k = 0, in_v = 0, in_g = 0, in_b = 0, in_gy = 0;
     size_t total = 0;
@@ -68,9 +67,9 @@ Plan make_plan(const gdn_problem *p) {
     const int64_t S = p->S_v, SK = p->S_k, SV = p->S_v;   // S only where SK == SV == 128
     pl.C = p->C > 0 ? std::min(p->C, std::max(p->T, 1)) : ceil_sqrt(p->T);
     pl.s128 = SK == 128 && SV == 128;
-    // head size 128: checkpoints fall on the 8-token grid of the column-scaled windows, so
-    // the interval is rounded up to a multiple of 8 and every interval gives the same bits
-    if (pl.s128) pl.C = (pl.C + 7) / 8 * 8;
+    // head size 128: checkpoints fall on the 16-token blocks of the matrix-core kernels, so
+    // the interval is rounded up to a multiple of 16 and every interval gives the same bits
+    if (pl.s128) pl.C = (pl.C + 15) / 16 * 16;
     pl.n_ck_max = std::max(1, (p->T + pl.C - 1) / pl.C);
     pl.G = p->gate == GDN_GATE_KDA ? p->S_k : 1;
     pl.units = (int64_t)p->n_seqs * p->H_v;
@@ -92,25 +91,24 @@ Plan make_plan(const gdn_problem *p) {
     off = align_up(off + (size_t)pl.units * pl.n_ck_max * SV * SK * sizeof(float));
     if (pl.s128) {
         const size_t tok_rows = (size_t)p->n_seqs * p->T * p->H_v;
+        const size_t nblk = (size_t)(p->T + 15) / 16;
         constexpr int NQ = 4;
-        pl.nvs_max = std::max(1, (pl.C + 63) / 64);
-        pl.off_a = off;   // window gate factors c (or a) and d
-        pl.gate_floats = tok_rows * pl.G;
-        off = align_up(off + 2 * pl.gate_floats * sizeof(float));
-        pl.off_wf = off;  // window flags
-        off = align_up(off + (size_t)p->n_seqs * ((p->T + 7) / 8) * p->H_v * sizeof(int32_t));
+        const int vs = gdn::mf128_stretch_tokens();
+        pl.nvs_max = std::max(1, (pl.C + vs - 1) / vs);
+        pl.off_wm = off;   // block matrices Bm, Te, Tb
+        off = align_up(off + (size_t)p->n_seqs * nblk * p->H_v * 3 * 256 * sizeof(float));
+        pl.off_wf = off;   // block flags
+        off = align_up(off + (size_t)p->n_seqs * nblk * p->H_v * sizeof(int32_t));
         pl.off_e = off;
         off = align_up(off + tok_rows * S * sizeof(float));
         pl.off_vs = off;
         if (pl.nvs_max > 1) off = align_up(off + (size_t)pl.units * NQ * pl.nvs_max * 32 * S * sizeof(float));
         pl.off_part = off;
-        off = align_up(off + tok_rows * NQ * (pl.G == 1 ? 2 : 3) * S * sizeof(float));
+        off = align_up(off + tok_rows * NQ * 3 * S * sizeof(float));
         pl.off_pb = off;
-        off = align_up(off + tok_rows * NQ * sizeof(float));
-        pl.off_pg = off;
-        off = align_up(off + tok_rows * NQ * 2 * sizeof(float));
+        off = align_up(off + tok_rows * 2 * NQ * sizeof(float));
         pl.off_hf = off;
-        off = align_up(off + (size_t)pl.units * NQ * pl.G * sizeof(float));
+        off = align_up(off + (size_t)pl.units * NQ * S * sizeof(float));
         pl.total = off;
         return pl;
     }
@@ -196,21 +194,42 @@ void fill_lens(const gdn_problem *p, int s0, int count, int32_t *dst) {
 
 int device_status(hipError_t e) { return e == hipSuccess ? GDN_OK : GDN_ERR_DEVICE; }
 
-// per-window gate factors and flags into the workspace for sequences s0 .. s0 + cnt - 1
-// (head size 128)
-hipError_t launch_gates(const gdn_problem *p, const Plan &pl, const float *g, void *ws, int s0,
-                        int cnt, hipStream_t st) {
-    gdn::GateArgs ga;
-    std::memset(&ga, 0, sizeof(ga));
-    ga.g = g;
-    ga.dtype = p->dtype;
-    ga.cbuf = (float *)((char *)ws + pl.off_a);
-    ga.dbuf = ga.cbuf + pl.gate_floats;
-    ga.wflag = (int32_t *)((char *)ws + pl.off_wf);
-    ga.sg = p->g;
-    ga.s_base = s0; ga.n_seqs_launch = cnt; ga.T = p->T; ga.H_v = p->H_v; ga.G = pl.G;
-    fill_lens(p, s0, cnt, ga.lens);
-    return gdn::launch_gate128(ga, st);
+// Argument block of the head-128 matrix-core kernels for sequences s0 .. s0 + cnt - 1.
+gdn::Mf128Args mf_args(const gdn_problem *p, const Plan &pl, void *ws, int s0, int cnt) {
+    gdn::Mf128Args a;
+    std::memset(&a, 0, sizeof(a));
+    char *w = (char *)ws;
+    a.snap = (float *)(w + pl.off_snap);
+    a.wmat = (float *)(w + pl.off_wm);
+    a.wflag = (int32_t *)(w + pl.off_wf);
+    a.ebuf = (float *)(w + pl.off_e);
+    a.vsbuf = (float *)(w + pl.off_vs);
+    a.part = (float *)(w + pl.off_part);
+    a.pbuf = (float *)(w + pl.off_pb);
+    a.hfin = (float *)(w + pl.off_hf);
+    a.sq = p->q; a.sk = p->k; a.sv = p->v; a.sg = p->g; a.sb = p->beta; a.sgy = p->gy; a.sy = p->y;
+    a.s_base = s0; a.n_seqs_launch = cnt;
+    a.T = p->T; a.H_k = p->H_k; a.H_v = p->H_v; a.C = pl.C; a.n_ck_max = pl.n_ck_max;
+    a.nvs_max = pl.nvs_max; a.kda = p->gate == GDN_GATE_KDA ? 1 : 0; a.dtype = p->dtype;
+    a.scale = p->scale;
+    fill_lens(p, s0, cnt, a.lens);
+    return a;
+}
+
+// Block preparation and forward scan of the head-128 kernels (y null: snapshots and errors only).
+int mf_forward(const gdn_problem *p, const Plan &pl, void *ws, const void *q, const void *k,
+               const void *v, const void *g, const void *beta, const float *state0, float *y,
+               float *state_out, hipStream_t st) {
+    for (int s0 = 0; s0 < p->n_seqs; s0 += gdn::kMaxSeqsPerLaunch) {
+        const int cnt = std::min(gdn::kMaxSeqsPerLaunch, p->n_seqs - s0);
+        gdn::Mf128Args a = mf_args(p, pl, ws, s0, cnt);
+        a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.state0 = state0;
+        a.y = y; a.state_out = state_out;
+        int rc = device_status(gdn::launch_prep128(a, st));
+        if (rc == GDN_OK) rc = device_status(gdn::launch_fwd_mf(a, st));
+        if (rc != GDN_OK) return rc;
+    }
+    return GDN_OK;
 }
 
 // Widen the given half-precision inputs into the workspace (a null source is skipped but
@@ -319,11 +338,15 @@ int gdn_fwd(const gdn_problem *p, const void *q_in, const void *k_in, const void
         for (int j = i + 1; j < 3; ++j)
             if (overlap(out[i], out[j])) return GDN_ERR_ARG;
 
+    if (pl.s128)   // head size 128: the matrix-core kernels read every input type directly
+        return mf_forward(p, pl, ws, q_in, k_in, v_in, g_in, beta_in, state0, y, state_out,
+                          (hipStream_t)stream);
+
     // half-precision inputs: widened into the workspace, then the fp32 path on the copies
     gdn_problem pc = *p;
     const float *q = (const float *)q_in, *k = (const float *)k_in, *v = (const float *)v_in;
     const float *g = (const float *)g_in, *beta = (const float *)beta_in;
-    if (p->dtype != GDN_DTYPE_F32 && !pl.s128) {
+    if (p->dtype != GDN_DTYPE_F32) {
         rc = widen_inputs(p, pl, ws, q_in, k_in, v_in, g_in, beta_in, nullptr, (hipStream_t)stream, pc,
                           q, k, v, g, beta, nullptr);
         if (rc != GDN_OK) return rc;
@@ -335,10 +358,6 @@ int gdn_fwd(const gdn_problem *p, const void *q_in, const void *k_in, const void
     a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.state0 = state0;
     a.y = y; a.state_out = state_out;
     a.snap = (float *)((char *)ws + pl.off_snap);
-    a.cbuf = (float *)((char *)ws + pl.off_a);
-    a.dbuf = a.cbuf + pl.gate_floats;
-    a.wflag = (const int32_t *)((char *)ws + pl.off_wf);
-    a.ebuf = (float *)((char *)ws + pl.off_e);
     a.sq = p->q; a.sk = p->k; a.sv = p->v; a.sg = p->g; a.sb = p->beta; a.sy = p->y;
     a.T = p->T; a.H_k = p->H_k; a.H_v = p->H_v; a.C = pl.C; a.n_ck_max = pl.n_ck_max;
     a.scale = p->scale;
@@ -348,12 +367,7 @@ int gdn_fwd(const gdn_problem *p, const void *q_in, const void *k_in, const void
         a.s_base = s0;
         fill_lens(p, s0, cnt, a.lens);
         const bool kda = p->gate == GDN_GATE_KDA;
-        if (pl.s128) {
-            rc = device_status(launch_gates(p, pl, g, ws, s0, cnt, (hipStream_t)stream));
-            if (rc != GDN_OK) return rc;
-        }
-        rc = device_status(pl.s128 ? gdn::launch_fwd128(a, kda, cnt, (hipStream_t)stream)
-                                   : gdn::launch_fwd(a, (int)SK, (int)SV, kda, cnt, (hipStream_t)stream));
+        rc = device_status(gdn::launch_fwd(a, (int)SK, (int)SV, kda, cnt, (hipStream_t)stream));
         if (rc != GDN_OK) return rc;
     }
     return GDN_OK;
@@ -392,13 +406,35 @@ int gdn_bwd(const gdn_problem *p, const void *q_in, const void *k_in, const void
         if (overlap(outg, i) || overlap(wsr, i)) return GDN_ERR_ARG;
     if (overlap(outg, wsr)) return GDN_ERR_ARG;
 
+    float *dq = grad_packed + off[0], *dk = grad_packed + off[1], *dv = grad_packed + off[2];
+    float *dg = grad_packed + off[3], *dbeta = grad_packed + off[4], *dstate = grad_packed + off[5];
+
+    if (pl.s128) {   // head size 128: matrix-core kernels, every input type read directly
+        if (!(flags & GDN_BWD_REUSE_SNAPSHOTS)) {
+            rc = mf_forward(p, pl, ws, q_in, k_in, v_in, g_in, beta_in, state0, nullptr, nullptr,
+                            (hipStream_t)stream);
+            if (rc != GDN_OK) return rc;
+        }
+        for (int s0 = 0; s0 < p->n_seqs; s0 += gdn::kMaxSeqsPerLaunch) {
+            const int cnt = std::min(gdn::kMaxSeqsPerLaunch, p->n_seqs - s0);
+            gdn::Mf128Args a = mf_args(p, pl, ws, s0, cnt);
+            a.q = q_in; a.k = k_in; a.v = v_in; a.g = g_in; a.beta = beta_in; a.gy = gy_in;
+            a.state0 = state0; a.dstate_out = dstate_out;
+            a.dq = dq; a.dk = dk; a.dv = dv; a.dg = dg; a.dbeta = dbeta; a.dstate = dstate;
+            rc = device_status(gdn::launch_bwd_mf(a, (hipStream_t)stream));
+            if (rc == GDN_OK) rc = device_status(gdn::launch_combine_mf(a, (hipStream_t)stream));
+            if (rc != GDN_OK) return rc;
+        }
+        return GDN_OK;
+    }
+
     // half-precision inputs of the small-head kernels: gy widened into the workspace, and q, k,
     // v, g, beta too unless the forward on the same inputs left their copies there
-    // (GDN_BWD_REUSE_SNAPSHOTS); the head-128 kernels read the half values directly
+    // (GDN_BWD_REUSE_SNAPSHOTS)
     gdn_problem pc = *p;
     const float *q = (const float *)q_in, *k = (const float *)k_in, *v = (const float *)v_in;
     const float *g = (const float *)g_in, *beta = (const float *)beta_in, *gy = (const float *)gy_in;
-    if (p->dtype != GDN_DTYPE_F32 && !pl.s128) {
+    if (p->dtype != GDN_DTYPE_F32) {
         const bool reuse = flags & GDN_BWD_REUSE_SNAPSHOTS;
         rc = widen_inputs(p, pl, ws, reuse ? nullptr : q_in, reuse ? nullptr : k_in,
                           reuse ? nullptr : v_in, reuse ? nullptr : g_in, reuse ? nullptr : beta_in,
@@ -407,8 +443,6 @@ int gdn_bwd(const gdn_problem *p, const void *q_in, const void *k_in, const void
     }
     p = &pc;
 
-    float *dq = grad_packed + off[0], *dk = grad_packed + off[1], *dv = grad_packed + off[2];
-    float *dg = grad_packed + off[3], *dbeta = grad_packed + off[4], *dstate = grad_packed + off[5];
     float *snap = (float *)((char *)ws + pl.off_snap);
     const bool kda = p->gate == GDN_GATE_KDA;
 
@@ -419,43 +453,21 @@ int gdn_bwd(const gdn_problem *p, const void *q_in, const void *k_in, const void
             std::memset(&f, 0, sizeof(f));
             f.q = q; f.k = k; f.v = v; f.g = g; f.beta = beta; f.state0 = state0;
             f.snap = snap;
-            f.cbuf = (float *)((char *)ws + pl.off_a);
-            f.dbuf = f.cbuf + pl.gate_floats;
-            f.wflag = (const int32_t *)((char *)ws + pl.off_wf);
-            f.ebuf = (float *)((char *)ws + pl.off_e);
             f.sq = p->q; f.sk = p->k; f.sv = p->v; f.sg = p->g; f.sb = p->beta; f.sy = p->y;
             f.s_base = s0;
             f.T = p->T; f.H_k = p->H_k; f.H_v = p->H_v; f.C = pl.C; f.n_ck_max = pl.n_ck_max;
             f.scale = p->scale;
             f.dtype = p->dtype;
             fill_lens(p, s0, cnt, f.lens);
-            if (pl.s128) {
-                rc = device_status(launch_gates(p, pl, g, ws, s0, cnt, (hipStream_t)stream));
-                if (rc != GDN_OK) return rc;
-            }
-            rc = device_status(pl.s128 ? gdn::launch_fwd128(f, kda, cnt, (hipStream_t)stream)
-                                       : gdn::launch_fwd(f, (int)SK, (int)SV, kda, cnt, (hipStream_t)stream));
+            rc = device_status(gdn::launch_fwd(f, (int)SK, (int)SV, kda, cnt, (hipStream_t)stream));
             if (rc != GDN_OK) return rc;
         }
         gdn::BwdArgs b;
         std::memset(&b, 0, sizeof(b));
         b.q = q; b.k = k; b.v = v; b.g = g; b.beta = beta; b.gy = gy; b.dstate_out = dstate_out;
         b.snap = snap;
-        if (pl.s128) {
-            b.cbuf = (const float *)((char *)ws + pl.off_a);
-            b.dbuf = b.cbuf + pl.gate_floats;
-            b.wflag = (const int32_t *)((char *)ws + pl.off_wf);
-            b.ebuf = (const float *)((char *)ws + pl.off_e);
-            b.vsbuf = (float *)((char *)ws + pl.off_vs);
-            b.part = (float *)((char *)ws + pl.off_part);
-            b.pbuf = (float *)((char *)ws + pl.off_pb);
-            b.pgbuf = (float *)((char *)ws + pl.off_pg);
-            b.hfin = (float *)((char *)ws + pl.off_hf);
-            b.nvs_max = pl.nvs_max;
-        } else {
-            b.segbuf = (float *)((char *)ws + pl.off_seg);
-            b.ebuf_seg = (float *)((char *)ws + pl.off_e);
-        }
+        b.segbuf = (float *)((char *)ws + pl.off_seg);
+        b.ebuf_seg = (float *)((char *)ws + pl.off_e);
         if (pl.parts) {
             b.dq = (float *)((char *)ws + pl.off_pq);
             b.dk = (float *)((char *)ws + pl.off_pk);
@@ -472,20 +484,7 @@ int gdn_bwd(const gdn_problem *p, const void *q_in, const void *k_in, const void
         b.scale = p->scale;
         b.dtype = p->dtype;
         fill_lens(p, s0, cnt, b.lens);
-        if (pl.s128) {
-            rc = device_status(gdn::launch_bwd128(b, kda, cnt, (hipStream_t)stream));
-            if (rc != GDN_OK) return rc;
-            gdn::Combine128Args c;
-            std::memset(&c, 0, sizeof(c));
-            c.part = b.part; c.pbuf = b.pbuf; c.pgbuf = b.pgbuf; c.hfin = b.hfin;
-            c.dq = dq; c.dk = dk; c.dg = dg; c.dbeta = dbeta;
-            c.s_base = s0; c.n_seqs_launch = cnt; c.T = p->T; c.H_k = p->H_k; c.H_v = p->H_v;
-            c.kda = kda ? 1 : 0;
-            fill_lens(p, s0, cnt, c.lens);
-            rc = device_status(gdn::launch_combine128(c, (hipStream_t)stream));
-        } else {
-            rc = device_status(gdn::launch_bwd(b, (int)SK, (int)SV, kda, cnt, (hipStream_t)stream));
-        }
+        rc = device_status(gdn::launch_bwd(b, (int)SK, (int)SV, kda, cnt, (hipStream_t)stream));
         if (rc != GDN_OK) return rc;
     }
     if (pl.parts) {

@@ -18,21 +18,11 @@ struct FwdArgs {
     float *y;          // nullptr: do not write y
     float *state_out;  // nullptr: do not write the final state
     float *snap;       // [unit][n_ck_max][S][S] snapshots (state before tokens 0, C, 2C, ...)
-    // S = 128 path, written by the gate kernel, each [n_seqs][T][H_v][G]: in a window
-    // processed column-scaled, cbuf holds the running product c of the gates a = exp(g)
-    // within the token's 8-token window (inclusive) and dbuf the product d of the window's
-    // later gates; in a window processed unscaled, cbuf holds a itself and dbuf 1.  wflag
-    // [n_seqs][ceil(T / 8)][H_v] is nonzero for a window processed unscaled
-    const float *cbuf, *dbuf;
-    const int32_t *wflag;
-    float *ebuf;       // S = 128 path: prediction errors e = v - u, [n_seqs][T][H_v][S]
     gdn_strides sq, sk, sv, sg, sb, sy;
     int32_t s_base;    // first sequence of this launch
     int32_t T, H_k, H_v, C, n_ck_max;
     float scale;
-    // element type (GDN_DTYPE_*) of q, k, v, g, beta, which the S = 128 kernels read as such
-    // (widened exactly at the load); the other kernels always receive fp32
-    int32_t dtype;
+    int32_t dtype;     // always fp32 here (half inputs are widened first)
     int32_t lens[kMaxSeqsPerLaunch];
 };
 
@@ -45,41 +35,11 @@ struct BwdArgs {
     float *dq, *dk;     // direct outputs (H_v == H_k) or per-value-head partials
     int64_t dqk_head;   // head count of the dq/dk arrays (H_k direct, H_v for partials)
     float *dv, *dg, *dbeta, *dstate;
-    // S = 128 path
-    const float *cbuf, *dbuf, *ebuf;  // gate kernel and forward outputs (see FwdArgs)
-    const int32_t *wflag;
-    float *vsbuf;              // [unit][4][nvs_max][32 x S] states at 64-token boundaries
-    float *part;               // [n_seqs][T][H_v][4][3][S] column sums of each row quarter
-    float *pbuf;               // [n_seqs][T][H_v][4] dbeta per quarter
-    float *pgbuf;              // [n_seqs][T][H_v][4][2] scalar-gate dg per quarter and column half
-    float *hfin;               // [n_seqs][H_v][4][G] column sums of dstate_out .* M_final per quarter
-    int32_t nvs_max;
     gdn_strides sq, sk, sv, sg, sb, sgy;
     int32_t s_base;
     int32_t T, H_k, H_v, C, n_ck_max;
     float scale;
-    int32_t dtype;      // element type of q, k, v, g, beta, gy (see FwdArgs)
-    int32_t lens[kMaxSeqsPerLaunch];
-};
-
-// Per-window gate factors and flags of every token t < len of the launch's sequences, as
-// described in FwdArgs (S = 128 path).
-struct GateArgs {
-    const float *g;
-    float *cbuf, *dbuf;          // [n_seqs][T][H_v][G]
-    int32_t *wflag;              // [n_seqs][ceil(T / 8)][H_v]
-    gdn_strides sg;
-    int32_t s_base, n_seqs_launch, T, H_v, G;
-    int32_t dtype;               // element type of g (see FwdArgs)
-    int32_t lens[kMaxSeqsPerLaunch];
-};
-
-// Sum of the row-quarter partials (and, for dq/dk, of the value heads of each key head) on
-// the S = 128 path; writes dq, dk, dg, dbeta including the zero rows of padded tokens.
-struct Combine128Args {
-    const float *part, *pbuf, *pgbuf, *hfin;
-    float *dq, *dk, *dg, *dbeta;
-    int32_t s_base, n_seqs_launch, T, H_k, H_v, kda;
+    int32_t dtype;      // always fp32 here
     int32_t lens[kMaxSeqsPerLaunch];
 };
 
@@ -139,9 +99,32 @@ hipError_t launch_ssm_combine(const SsmArgs &a, hipStream_t st);
 hipError_t launch_fwd(const FwdArgs &a, int SK, int SV, bool kda, int n_seqs_launch, hipStream_t st);
 hipError_t launch_bwd(const BwdArgs &a, int SK, int SV, bool kda, int n_seqs_launch, hipStream_t st);
 hipError_t launch_combine(const CombineArgs &a, hipStream_t st);
-hipError_t launch_gate128(const GateArgs &a, hipStream_t st);
-hipError_t launch_fwd128(const FwdArgs &a, bool kda, int n_seqs_launch, hipStream_t st);
-hipError_t launch_bwd128(const BwdArgs &a, bool kda, int n_seqs_launch, hipStream_t st);
-hipError_t launch_combine128(const Combine128Args &a, hipStream_t st);
+
+// Head size 128 on the matrix cores (gdn_mf.hip): one argument block for the block
+// preparation, forward, backward and combine kernels.  Blocks are the 16-token blocks of each
+// sequence; rows [s][t][h] index the per-token workspace arrays.
+struct Mf128Args {
+    const void *q, *k, *v, *g, *beta, *gy;   // element type dtype (GDN_DTYPE_*)
+    const float *state0, *dstate_out;
+    float *y, *state_out;   // forward outputs (y null: the backward's checkpoint pass)
+    float *snap;            // [unit][n_ck_max][S][S] state before tokens 0, C, 2C, ...
+    float *wmat;            // [n_seqs][nblk][H_v][3][16][16] block matrices Bm, Te, Tb
+    int32_t *wflag;         // [n_seqs][nblk][H_v] nonzero: block processed token by token
+    float *ebuf;            // [n_seqs][T][H_v][S] prediction errors e = v - u
+    float *vsbuf;           // [unit][4][nvs_max][32][S] states at stretch starts
+    float *part;            // [n_seqs][T][H_v][4][3][S] quarter partials dq | dk | dg
+    float *pbuf;            // [n_seqs][T][H_v][8] dbeta partials (quarter, 16-row block)
+    float *hfin;            // [unit][4][S] final-state dg column sums per quarter
+    float *dq, *dk, *dv, *dg, *dbeta, *dstate;
+    gdn_strides sq, sk, sv, sg, sb, sgy, sy;
+    int32_t s_base, n_seqs_launch, T, H_k, H_v, C, n_ck_max, nvs_max, kda, dtype;
+    float scale;
+    int32_t lens[kMaxSeqsPerLaunch];
+};
+int mf128_stretch_tokens();   // tokens per replayed stretch of the backward
+hipError_t launch_prep128(const Mf128Args &a, hipStream_t st);
+hipError_t launch_fwd_mf(const Mf128Args &a, hipStream_t st);
+hipError_t launch_bwd_mf(const Mf128Args &a, hipStream_t st);
+hipError_t launch_combine_mf(const Mf128Args &a, hipStream_t st);
 
 }  // namespace gdn

@@ -47,22 +47,22 @@ def problem(B, strides=None, **kw):
 def expected_ws(n, T, Hk, Hv, S, C, kda=True):
     al = lambda x: (x + 255) // 256 * 256  # noqa: E731
     units = n * Hv
-    if S == 128:                    # checkpoints on the 8-token window grid
-        C = -(-C // 8) * 8
+    if S == 128:                    # checkpoints on the 16-token block grid
+        C = -(-C // 16) * 16
     n_ck = max(1, -(-T // C))
     tot = al(units * n_ck * S * S * 4)
-    if S == 128:                    # row-quarter path
+    if S == 128:                    # matrix-core path, row quarters
         rows = n * T * Hv
-        nvs = max(1, -(-C // 64))
-        tot = al(tot + 2 * rows * (S if kda else 1) * 4)   # window gate factors c (or a), d
-        tot = al(tot + n * (-(-T // 8)) * Hv * 4)          # window flags
-        tot = al(tot + rows * S * 4)                       # prediction errors
+        nblk = -(-T // 16)
+        nvs = max(1, -(-C // 32))
+        tot = al(tot + n * nblk * Hv * 3 * 256 * 4)         # block matrices Bm, Te, Tb
+        tot = al(tot + n * nblk * Hv * 4)                   # block flags
+        tot = al(tot + rows * S * 4)                        # prediction errors
         if nvs > 1:
-            tot = al(tot + units * 4 * nvs * 32 * S * 4)   # stretch starts
-        tot = al(tot + rows * 4 * (3 if kda else 2) * S * 4)   # column partials
-        tot = al(tot + rows * 4 * 4)                       # dbeta partials
-        tot = al(tot + rows * 4 * 2 * 4)                   # scalar-gate dg partials
-        tot = al(tot + units * 4 * (S if kda else 1) * 4)  # final-state dg column sums
+            tot = al(tot + units * 4 * nvs * 32 * S * 4)    # stretch starts
+        tot = al(tot + rows * 4 * 3 * S * 4)                # column partials dq | dk | dg
+        tot = al(tot + rows * 8 * 4)                        # dbeta partials
+        tot = al(tot + units * 4 * S * 4)                   # final-state dg column sums
         return tot
     tot = al(tot + units * C * S * S * 4)
     tot = al(tot + units * C * S * 4)

@@ -257,47 +257,48 @@ def test_strided_views_equal_contiguous_bitwise(dev):
         assert np.array_equal(a[n], b[n]), n
 
 
-# Head size 128: row-quarter kernels with three storage levels (snapshots every C tokens,
-# register states every 8 tokens of a 64-token stretch, LDS states of the walked 8 tokens).
+# Head size 128: matrix-core kernels over 16-token blocks, with three storage levels
+# (snapshots every C tokens, stretch starts in the workspace, block starts in registers).
 S128_CASES = {
     # three segments (64, 64, 22 tokens), ragged second sequence, grouped heads
     "kda_c64": I.Workload("s128_kda_c64", 2, 150, 2, 4, 128, True, 64, -0.3,
                           seq_lens=(150, 77), seed=501),
-    # interval above the 64-token stretch: stretches saved to the workspace
+    # interval above the replayed stretch: stretch starts saved to the workspace
     "scalar_c200": I.Workload("s128_scalar_c200", 2, 300, 1, 3, 128, False, 200, -0.05,
                               seq_lens=(300, 133), seed=502),
-    # default interval ceil(sqrt(T)) = 10: partial sub-segments everywhere
+    # default interval ceil(sqrt(T)) = 10 (rounded up to 16): partial stretches everywhere
     "kda_default": I.Workload("s128_kda_default", 1, 100, 1, 2, 128, True, 0, -0.5, seed=503),
-    # every token its own segment
+    # every token its own segment (interval 1, rounded up to one block)
     "kda_c1": I.Workload("s128_kda_c1", 1, 19, 1, 1, 128, True, 1, -0.5, seed=504),
     # one segment longer than a stretch
     "scalar_cT": I.Workload("s128_scalar_cT", 1, 129, 1, 1, 128, False, 129, -1.0, seed=505),
-    # windows processed unscaled, mixed with column-scaled ones: some gates above one ...
+    # gates above one whose block products stay in range: column scaling with c > 1
     "kda_gate_above_one": I.Workload("s128_kda_up", 1, 150, 1, 2, 128, True, 64, -0.5,
-                                     seed=507, g_hi=0.00035),
+                                     seed=507, g_hi=0.5),
     "scalar_gate_above_one": I.Workload("s128_scalar_up", 1, 150, 1, 2, 128, False, 64, -1.0,
-                                        seed=508, g_hi=0.09),
-    # ... and window products below 2^-60
-    "kda_tiny_products": I.Workload("s128_kda_tiny", 1, 150, 1, 2, 128, True, 64, -7.0, seed=509),
-    "scalar_tiny_products": I.Workload("s128_scalar_tiny", 1, 150, 1, 2, 128, False, 200, -11.0,
-                                       seed=510),
+                                        seed=508, g_hi=1.0),
+    # blocks processed token by token, mixed with column-scaled ones: block products below
+    # 2^-60 ...
+    "kda_tiny_products": I.Workload("s128_kda_tiny", 1, 150, 1, 2, 128, True, 64, -3.8, seed=507),
+    "scalar_tiny_products": I.Workload("s128_scalar_tiny", 1, 150, 1, 2, 128, False, 200, -5.5,
+                                       seed=508),
 }
-UNSCALED = ("kda_gate_above_one", "scalar_gate_above_one", "kda_tiny_products",
-            "scalar_tiny_products")
+TOKENWISE = ("kda_tiny_products", "scalar_tiny_products")
 
 
-def unscaled_fraction(w, arrays):
-    """Share of the 8-token windows of each (sequence, value head) that hold a gate above
-    one or whose gate product falls below 2^-60 in some channel (float32, as the kernels)."""
+def tokenwise_fraction(w, arrays):
+    """Share of the 16-token blocks of each (sequence, value head) whose running gate product
+    (float32, token order, as the kernels take it) leaves [2^-60, 2^60] in some channel: those
+    blocks are processed token by token."""
     a = np.exp(arrays["g"].astype(np.float32)).reshape(w.n_seqs, w.T, w.H_v, w.G)
     hits = tot = 0
-    for s, L in enumerate(w.lens):
-        for t0 in range(0, L, 8):
-            win = a[s, t0:min(t0 + 8, L)]                      # [tokens, H_v, G]
-            prod = np.prod(win, axis=0, dtype=np.float32)      # [H_v, G]
-            bad = (win > 1).any(axis=(0, 2)) | (prod < np.float32(2.0 ** -60)).any(axis=1)
-            hits += int(bad.sum())
-            tot += bad.size
+    with np.errstate(over="ignore"):
+        for s, L in enumerate(w.lens):
+            for t0 in range(0, L, 16):
+                c = np.cumprod(a[s, t0:min(t0 + 16, L)], axis=0, dtype=np.float32)
+                bad = ((c < np.float32(2.0 ** -60)) | (c > np.float32(2.0 ** 60))).any(axis=(0, 2))
+                hits += int(bad.sum())
+                tot += bad.size
     return hits / tot
 
 
@@ -306,10 +307,30 @@ def test_parity_s128(dev, name):
     w = S128_CASES[name]
     log(f"[parity] {w.name} lens={w.lens} C={w.C}")
     arrays, _ = I.make_all(w)
-    if name in UNSCALED:   # the case must mix both kinds of window
-        f = unscaled_fraction(w, arrays)
-        log(f"[parity] {w.name}: unscaled windows {f:.2f}")
+    if name in TOKENWISE:   # the case must mix both kinds of block
+        f = tokenwise_fraction(w, arrays)
+        log(f"[parity] {w.name}: blocks processed token by token {f:.2f}")
         assert 0.1 < f < 0.9, f
+    _, got = run_case(dev, w, arrays, reuse=True)
+    rep = check(got, oracle_results(w, arrays))
+    log(f"[parity] {w.name}: " + ", ".join(f"{k} {v:.1e}" for k, v in rep.items()))
+
+
+@pytest.mark.parametrize("kda", [True, False])
+def test_parity_s128_products_above_range(dev, kda):
+    """Blocks whose running gate product rises past 2^60 and falls back inside the block
+    (eight tokens of log-gate +5.5, then eight of -5.5, in every channel of one head) are
+    processed token by token, mixed with column-scaled blocks; the values stay finite."""
+    w = I.Workload("s128_above_" + ("kda" if kda else "scalar"), 1, 96, 1, 2, 128, kda, 32,
+                   -0.3, seed=511)
+    arrays, _ = I.make_all(w)
+    g = arrays["g"]
+    for b in (1, 4):
+        g[0, 16 * b:16 * b + 8, 0, :] = 5.5
+        g[0, 16 * b + 8:16 * b + 16, 0, :] = -5.5
+    f = tokenwise_fraction(w, arrays)
+    log(f"[parity] {w.name}: blocks processed token by token {f:.2f}")
+    assert 0.1 < f < 0.9, f
     _, got = run_case(dev, w, arrays, reuse=True)
     rep = check(got, oracle_results(w, arrays))
     log(f"[parity] {w.name}: " + ", ".join(f"{k} {v:.1e}" for k, v in rep.items()))
@@ -323,13 +344,13 @@ def test_s128_bitwise_interval_reuse_and_strides(dev):
     _, a = run_case(dev, w, arrays, reuse=True)
     _, b = run_case(dev, w, arrays, reuse=True)
     _, c = run_case(dev, w, arrays, reuse=False, C=w.T)
-    _, d = run_case(dev, w, arrays, reuse=False, C=8)
+    _, d = run_case(dev, w, arrays, reuse=False, C=16)
     _, e = run_case(dev, w, arrays, reuse=True, C=100, packed=False, strided_gy=True)
     # a gradient buffer 4 bytes off a 16-byte boundary takes the one-column partial sums
     _, f = run_case(dev, w, arrays, reuse=True, grad_offset=1)
     for n in a:
         assert np.array_equal(a[n], b[n]), ("run-to-run", n)
         assert np.array_equal(a[n], c[n]), ("C=T", n)
-        assert np.array_equal(a[n], d[n]), ("C=8", n)
+        assert np.array_equal(a[n], d[n]), ("C=16", n)
         assert np.array_equal(a[n], e[n]), ("C=100, contiguous, strided gy", n)
         assert np.array_equal(a[n], f[n]), ("unaligned gradient buffer", n)
