@@ -130,6 +130,8 @@ class Problem:
         self.dtype = int(dtype)
         self.kda, self.C, self.scale = bool(kda), int(C), float(scale)
         self.seq_lens = None if seq_lens is None else [int(x) for x in seq_lens]
+        if self.seq_lens is not None and len(self.seq_lens) != n_seqs:
+            raise ValueError(f"seq_lens has {len(self.seq_lens)} entries for {n_seqs} sequences")
         self._lens = None
         self.strides = dict(strides or {})
         self._c = _Problem()
@@ -217,8 +219,27 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+def _check_view(p: Problem, t, name):
+    """t must have the (seq, tok, head) strides recorded in p for that tensor."""
+    if t is not None and _tok_strides(t, name) != tuple(p.strides.get(name, (0, 0, 0))):
+        raise ValueError(f"{name}: strides {tuple(t.stride())} differ from the problem's "
+                         f"{p.strides.get(name)}")
+
+
+def _check_state(p: Problem, t, name):
+    """A state tensor must be contiguous [n_seqs][H_v][S_v][S_k]."""
+    if t is None:
+        return
+    shape = (p.n_seqs, p.H_v, p.S_v, p.S_k)
+    if tuple(t.shape) != shape or not t.is_contiguous():
+        raise ValueError(f"{name}: expected a contiguous {shape} tensor, got {tuple(t.shape)}")
+
+
 def fwd(p: Problem, q, k, v, g, beta, state0, y, state_out, ws, stream=None):
     """gdn_fwd on device tensors (y must have the strides recorded in p for "y")."""
+    _check_view(p, y, "y")
+    _check_state(p, state0, "state0")
+    _check_state(p, state_out, "state_out")
     rc = lib.gdn_fwd(p.c, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state0),
                      _ptr(y), _ptr(state_out), _ptr(ws), ws.numel() * ws.element_size(),
                      _stream(stream))
@@ -229,6 +250,9 @@ def fwd(p: Problem, q, k, v, g, beta, state0, y, state_out, ws, stream=None):
 def bwd(p: Problem, q, k, v, g, beta, state0, gy, dstate_out, grad_packed, ws, flags=0,
         stream=None):
     """gdn_bwd on device tensors (gy must have the strides recorded in p for "gy")."""
+    _check_view(p, gy, "gy")
+    _check_state(p, state0, "state0")
+    _check_state(p, dstate_out, "dstate_out")
     rc = lib.gdn_bwd(p.c, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state0),
                      _ptr(gy), _ptr(dstate_out), _ptr(grad_packed), _ptr(ws),
                      ws.numel() * ws.element_size(), int(flags), _stream(stream))

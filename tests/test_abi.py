@@ -104,9 +104,14 @@ def test_grad_layout(B):
     assert total_s == total - n * T * Hv * (S - 1)
 
 
+def test_problem_rejects_length_count_mismatch(B):
+    with pytest.raises(ValueError):
+        problem(B, seq_lens=[64])
+
+
 @pytest.mark.parametrize("kw,code", [
     (dict(S=48), -2), (dict(S=8), -2), (dict(S_v=8), -2), (dict(S_v=256), -2),
-    (dict(H_k=3), -2), (dict(n_seqs=-1), -1),
+    (dict(H_k=3), -2), (dict(n_seqs=-1, seq_lens=None), -1),
     (dict(T=-1), -1), (dict(C=-1), -1), (dict(seq_lens=[65, 3]), -1),
     (dict(seq_lens=[-1, 3]), -1), (dict(scale=float("nan")), -1), (dict(H_k=0), -1),
     (dict(dtype=3), -1), (dict(dtype=-1), -1),
