@@ -8,7 +8,7 @@ the library; the first use of ``fwd``, ``bwd``, ``workspace_size`` or ``Problem`
 raises if the library has not been built (there is no fallback path).
 """
 
-_BINDING_NAMES = ("Problem", "workspace_size", "grad_layout", "unpack_grads", "fwd", "bwd",
+_BINDING_NAMES = ("Problem", "workspace_size", "grad_layout", "unpack_grads", "fwd", "bwd", "bwd_noalloc",
                   "lib", "GdnError", "STATUS", "EXPORTS", "BWD_REUSE_SNAPSHOTS",
                   # the short convolution and the q/k normalisation around the recurrence
                   "ssm_conv_fwd", "ssm_conv_bwd", "l2norm_fwd", "l2norm_bwd",

@@ -25,7 +25,7 @@ GATE_SCALAR, GATE_KDA = 0, 1
 DTYPE_F32, DTYPE_F16, DTYPE_BF16 = 0, 1, 2
 _DTYPES = {torch.float32: DTYPE_F32, torch.float16: DTYPE_F16, torch.bfloat16: DTYPE_BF16}
 BWD_REUSE_SNAPSHOTS = 1
-EXPORTS = ("gdn_workspace_size", "gdn_grad_packed_floats", "gdn_fwd", "gdn_bwd",
+EXPORTS = ("gdn_workspace_size", "gdn_grad_packed_floats", "gdn_fwd", "gdn_bwd", "gdn_bwd_noalloc",
            "gdn_ssm_conv_fwd", "gdn_ssm_conv_bwd", "gdn_l2norm_fwd", "gdn_l2norm_bwd",
            "gdn_ssm_workspace_size", "gdn_ssm_grad_packed_floats", "gdn_ssm_fwd", "gdn_ssm_bwd",
            "gdn_status_string")
@@ -61,6 +61,9 @@ lib.gdn_fwd.restype = ctypes.c_int
 lib.gdn_bwd.argtypes = [ctypes.POINTER(_Problem)] + [_VP] * 10 + [ctypes.c_size_t,
                                                                  ctypes.c_uint, _VP]
 lib.gdn_bwd.restype = ctypes.c_int
+lib.gdn_bwd_noalloc.argtypes = [ctypes.POINTER(_Problem)] + [_VP] * 9 + [_VP]
+lib.gdn_bwd_noalloc.restype = ctypes.c_int
+NOALLOC_SCRATCH_BYTES = 64 << 20   # GDN_NOALLOC_SCRATCH_BYTES
 class _ConvProblem(ctypes.Structure):
     _fields_ = [("n_seqs", ctypes.c_int32), ("T", ctypes.c_int32), ("d_inner", ctypes.c_int32),
                 ("d_conv", ctypes.c_int32), ("sx_seq", ctypes.c_int64), ("sx_tok", ctypes.c_int64),
@@ -258,6 +261,17 @@ def bwd(p: Problem, q, k, v, g, beta, state0, gy, dstate_out, grad_packed, ws, f
                      ws.numel() * ws.element_size(), int(flags), _stream(stream))
     if rc != 0:
         raise GdnError(rc, "gdn_bwd")
+
+
+def bwd_noalloc(p: Problem, q, k, v, g, beta, state0, gy, dstate_out, grad_packed, stream=None):
+    """gdn_bwd_noalloc: gdn_bwd on the library's own static workspace (no ws argument)."""
+    _check_view(p, gy, "gy")
+    _check_state(p, state0, "state0")
+    _check_state(p, dstate_out, "dstate_out")
+    rc = lib.gdn_bwd_noalloc(p.c, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state0),
+                             _ptr(gy), _ptr(dstate_out), _ptr(grad_packed), _stream(stream))
+    if rc != 0:
+        raise GdnError(rc, "gdn_bwd_noalloc")
 
 
 def conv_problem(n_seqs, T, d_inner, d_conv, sx_strides, y_strides) -> _ConvProblem:

@@ -6,6 +6,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 #include "gdn.h"
 #include "gdn_internal.h"
@@ -270,6 +271,34 @@ int widen_inputs(const gdn_problem *p, const Plan &pl, void *ws, const void *q, 
         *j.dst = base + j.off;
     }
     pc.dtype = GDN_DTYPE_F32;
+    return GDN_OK;
+}
+
+// Workspace of gdn_bwd_noalloc: one copy per GPU, held until the process ends.  Host code uses
+// it only through the device address looked up below, never through the array's name.
+static __device__ __align__(256) unsigned char scratch[GDN_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+
+// Device address of the scratch array on the device of stream st (looked up once per device,
+// with that device current).
+int scratch_address(hipStream_t st, void **out) {
+    int dev = -1, cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess) return GDN_ERR_DEVICE;
+    if (hipStreamGetDevice(st, &dev) != hipSuccess) dev = cur;
+    if (dev < 0 || dev >= kMaxDevices) return GDN_ERR_DEVICE;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        if (dev != cur && hipSetDevice(dev) != hipSuccess) return GDN_ERR_DEVICE;
+        void *ptr = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (dev != cur && hipSetDevice(cur) != hipSuccess) return GDN_ERR_DEVICE;
+        if (e != hipSuccess || !ptr) return GDN_ERR_DEVICE;
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
     return GDN_OK;
 }
 
@@ -728,6 +757,20 @@ int gdn_ssm_bwd(const gdn_ssm_problem *p, const float *s0, const float *x, const
     if (e == hipSuccess) e = gdn::launch_ssm(a, true, (hipStream_t)stream);
     if (e == hipSuccess) e = gdn::launch_ssm_combine(a, (hipStream_t)stream);
     return device_status(e);
+}
+
+int gdn_bwd_noalloc(const gdn_problem *p, const void *q, const void *k, const void *v,
+                    const void *g, const void *beta, const float *state0, const void *gy,
+                    const float *dstate_out, float *grad_packed, gdn_stream_t stream) {
+    const int rc = validate(p);
+    if (rc != GDN_OK) return rc;
+    const size_t need = make_plan(p).total;
+    if (need > GDN_NOALLOC_SCRATCH_BYTES) return GDN_ERR_WORKSPACE;
+    void *ws = nullptr;
+    const int rs = scratch_address((hipStream_t)stream, &ws);
+    if (rs != GDN_OK) return rs;
+    return gdn_bwd(p, q, k, v, g, beta, state0, gy, dstate_out, grad_packed, ws,
+                   GDN_NOALLOC_SCRATCH_BYTES, 0u, stream);
 }
 
 }  // extern "C"

@@ -161,6 +161,22 @@ int gdn_bwd(const gdn_problem *p, const void *q, const void *k, const void *v,
             const float *dstate_out, float *grad_packed, void *ws, size_t ws_bytes,
             unsigned flags, gdn_stream_t stream);
 
+/* Allocation-free backward, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc).  Same arguments,
+ * results and checks as gdn_bwd without the snapshot reuse, but no workspace argument: the
+ * workspace is a static device array of GDN_NOALLOC_SCRATCH_BYTES that the library holds on
+ * every GPU it runs on until the process ends (its address is looked up once per device, on
+ * that device's first call).  A problem whose gdn_workspace_size exceeds the array returns
+ * GDN_ERR_WORKSPACE before anything is enqueued.  The call allocates nothing.  Every call on
+ * one GPU shares that GPU's array and the array keeps the last call's contents (none of which
+ * a later call reads): calls that overlap in time on one GPU (other streams, other host
+ * threads) race on it and give wrong results, so the caller must serialise them.  The
+ * snapshots are always recomputed.  The stream's device selects the array. */
+#define GDN_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int gdn_bwd_noalloc(const gdn_problem *p, const void *q, const void *k, const void *v,
+                    const void *g, const void *beta, const float *state0, const void *gy,
+                    const float *dstate_out, float *grad_packed, gdn_stream_t stream);
+
 /* Short causal depthwise convolution upstream of the recurrence (the one that produces the
  * mixed q/k/v rows) and its gradient with respect to the input; the weights are frozen and
  * take no gradient (page "S1-24: chunked attention -- the kernel-free long-context path",
