@@ -68,8 +68,8 @@ _C = "gated_delta_rule_bwd_amd/csrc/"
 TRAFFIC = {
     ("gdn", "layer_kda_s128"): {
         "file": "traffic_layer_kda_s128.json",
-        "sources": [_C + "gdn_s128.hip", _C + "gdn_api.hip", _C + "gdn_internal.h"],
-        "kernels": ("bwd128_kernel<true, 0>", "combine128_kernel<4>")},
+        "sources": [_C + "gdn_mf.hip", _C + "gdn_kernels.hip", _C + "gdn_api.hip", _C + "gdn_internal.h"],
+        "kernels": ("gram1_kernel<0>", "bwd_mf_kernel<0>", "combine_kernel")},
     ("ssm_conv", "conv_layer_d10240_k4"): {
         "file": "traffic_conv_layer_d10240_k4.json",
         "sources": [_C + "ssm_conv.hip", _C + "gdn_internal.h"],
@@ -526,7 +526,7 @@ def main():
         "fwd_ms": fwd_ms,
         "bwd_ms": bwd_ms,
         "roofline": {"bound": "alu",
-                     "kernel": "gdn_bwd (bwd128_kernel + combine128_kernel)" if S2 == 128 * 128 else
+                     "kernel": "gdn_bwd (gram1_kernel + bwd_mf_kernel + combine_kernel)" if S2 == 128 * 128 else
                      "gdn_bwd (bwd_kernel" + (" + combine_kernel)" if w.H_v != w.H_k else ")"),
                      "achieved": achieved / 1e12, "peak": PEAK_FP32_VALU / 1e12,
                      "unit": "TFLOP/s", "frac": achieved / PEAK_FP32_VALU,

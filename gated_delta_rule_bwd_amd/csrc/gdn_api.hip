@@ -32,9 +32,9 @@ struct Plan {
     int64_t units = 0;
     bool s128 = false;   // head size 128: row-quarter kernels
     bool parts = false;  // small heads: dq/dk go through per-value-head partials
-    int nvs_max = 1;     // S_k = S_v = 128: replayed stretches per segment
+    int nbs = 1;         // S_k = S_v = 128: 16-token blocks per segment
     size_t off_snap = 0, off_seg = 0, off_e = 0, off_pq = 0, off_pk = 0;
-    size_t off_wm = 0, off_wf = 0, off_vs = 0, off_part = 0, off_pb = 0, off_hf = 0;
+    size_t off_wm = 0, off_wf = 0, off_c = 0, off_g1 = 0, off_vs = 0;
     // half-precision inputs: their fp32 copies, contiguous [n_seqs][T][heads][width] each
     size_t off_in = 0, in_q = 0, in_k = 0, in_v = 0, in_g = 0, in_b = 0, in_gy = 0;
     size_t total = 0;
@@ -93,23 +93,26 @@ Plan make_plan(const gdn_problem *p) {
     if (pl.s128) {
         const size_t tok_rows = (size_t)p->n_seqs * p->T * p->H_v;
         const size_t nblk = (size_t)(p->T + 15) / 16;
-        constexpr int NQ = 4;
-        const int vs = gdn::mf128_stretch_tokens();
-        pl.nvs_max = std::max(1, (pl.C + vs - 1) / vs);
+        pl.nbs = pl.C / 16;
         pl.off_wm = off;   // block matrices Bm, Te, Tb
         off = align_up(off + (size_t)p->n_seqs * nblk * p->H_v * 3 * 256 * sizeof(float));
         pl.off_wf = off;   // block flags
         off = align_up(off + (size_t)p->n_seqs * nblk * p->H_v * sizeof(int32_t));
+        pl.off_c = off;    // running gate products within blocks
+        off = align_up(off + tok_rows * pl.G * sizeof(float));
         pl.off_e = off;
         off = align_up(off + tok_rows * S * sizeof(float));
-        pl.off_vs = off;
-        if (pl.nvs_max > 1) off = align_up(off + (size_t)pl.units * NQ * pl.nvs_max * 32 * S * sizeof(float));
-        pl.off_part = off;
-        off = align_up(off + tok_rows * NQ * 3 * S * sizeof(float));
-        pl.off_pb = off;
-        off = align_up(off + tok_rows * 2 * NQ * sizeof(float));
-        pl.off_hf = off;
-        off = align_up(off + (size_t)pl.units * NQ * S * sizeof(float));
+        pl.off_g1 = off;   // Grams G1 of the blocks
+        off = align_up(off + (size_t)p->n_seqs * nblk * p->H_v * 256 * sizeof(float));
+        pl.off_vs = off;   // block starts of the segment being walked
+        if (pl.nbs > 1) off = align_up(off + (size_t)pl.units * pl.nbs * S * S * sizeof(float));
+        pl.parts = p->H_v != p->H_k;
+        if (pl.parts) {   // dq, dk per value head, summed over the heads of a key head afterwards
+            pl.off_pq = off;
+            off = align_up(off + tok_rows * S * sizeof(float));
+            pl.off_pk = off;
+            off = align_up(off + tok_rows * S * sizeof(float));
+        }
         pl.total = off;
         return pl;
     }
@@ -203,15 +206,16 @@ gdn::Mf128Args mf_args(const gdn_problem *p, const Plan &pl, void *ws, int s0, i
     a.snap = (float *)(w + pl.off_snap);
     a.wmat = (float *)(w + pl.off_wm);
     a.wflag = (int32_t *)(w + pl.off_wf);
+    a.cbuf = (float *)(w + pl.off_c);
     a.ebuf = (float *)(w + pl.off_e);
+    a.g1buf = (float *)(w + pl.off_g1);
     a.vsbuf = (float *)(w + pl.off_vs);
-    a.part = (float *)(w + pl.off_part);
-    a.pbuf = (float *)(w + pl.off_pb);
-    a.hfin = (float *)(w + pl.off_hf);
+    a.dq_part = pl.parts ? (float *)(w + pl.off_pq) : nullptr;
+    a.dk_part = pl.parts ? (float *)(w + pl.off_pk) : nullptr;
     a.sq = p->q; a.sk = p->k; a.sv = p->v; a.sg = p->g; a.sb = p->beta; a.sgy = p->gy; a.sy = p->y;
     a.s_base = s0; a.n_seqs_launch = cnt;
     a.T = p->T; a.H_k = p->H_k; a.H_v = p->H_v; a.C = pl.C; a.n_ck_max = pl.n_ck_max;
-    a.nvs_max = pl.nvs_max; a.kda = p->gate == GDN_GATE_KDA ? 1 : 0; a.dtype = p->dtype;
+    a.nbs = pl.nbs; a.kda = p->gate == GDN_GATE_KDA ? 1 : 0; a.dtype = p->dtype;
     a.scale = p->scale;
     fill_lens(p, s0, cnt, a.lens);
     return a;
@@ -451,10 +455,17 @@ int gdn_bwd(const gdn_problem *p, const void *q_in, const void *k_in, const void
             a.state0 = state0; a.dstate_out = dstate_out;
             a.dq = dq; a.dk = dk; a.dv = dv; a.dg = dg; a.dbeta = dbeta; a.dstate = dstate;
             rc = device_status(gdn::launch_bwd_mf(a, (hipStream_t)stream));
-            if (rc == GDN_OK) rc = device_status(gdn::launch_combine_mf(a, (hipStream_t)stream));
             if (rc != GDN_OK) return rc;
         }
-        return GDN_OK;
+        if (pl.parts) {   // dq, dk: the value heads of each key head in increasing order
+            gdn::CombineArgs c;
+            c.dq_part = (const float *)((char *)ws + pl.off_pq);
+            c.dk_part = (const float *)((char *)ws + pl.off_pk);
+            c.dq = dq; c.dk = dk;
+            c.n_seqs = p->n_seqs; c.T = p->T; c.H_k = p->H_k; c.H_v = p->H_v; c.S = (int)SK;
+            rc = device_status(gdn::launch_combine(c, (hipStream_t)stream));
+        }
+        return rc;
     }
 
     // half-precision inputs of the small-head kernels: gy widened into the workspace, and q, k,

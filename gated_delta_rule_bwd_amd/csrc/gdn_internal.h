@@ -101,8 +101,8 @@ hipError_t launch_bwd(const BwdArgs &a, int SK, int SV, bool kda, int n_seqs_lau
 hipError_t launch_combine(const CombineArgs &a, hipStream_t st);
 
 // Head size 128 on the matrix cores (gdn_mf.hip): one argument block for the block
-// preparation, forward, backward and combine kernels.  Blocks are the 16-token blocks of each
-// sequence; rows [s][t][h] index the per-token workspace arrays.
+// preparation, forward and backward kernels.  Blocks are the 16-token blocks of each sequence;
+// rows [s][t][h] index the per-token workspace arrays.
 struct Mf128Args {
     const void *q, *k, *v, *g, *beta, *gy;   // element type dtype (GDN_DTYPE_*)
     const float *state0, *dstate_out;
@@ -110,21 +110,20 @@ struct Mf128Args {
     float *snap;            // [unit][n_ck_max][S][S] state before tokens 0, C, 2C, ...
     float *wmat;            // [n_seqs][nblk][H_v][3][16][16] block matrices Bm, Te, Tb
     int32_t *wflag;         // [n_seqs][nblk][H_v] nonzero: block processed token by token
+    float *cbuf;            // [n_seqs][T][H_v][G] running gate product c within the token's
+                            // block (the gates a themselves in a token-by-token block)
     float *ebuf;            // [n_seqs][T][H_v][S] prediction errors e = v - u
-    float *vsbuf;           // [unit][4][nvs_max][32][S] states at stretch starts
-    float *part;            // [n_seqs][T][H_v][4][3][S] quarter partials dq | dk | dg
-    float *pbuf;            // [n_seqs][T][H_v][8] dbeta partials (quarter, 16-row block)
-    float *hfin;            // [unit][4][S] final-state dg column sums per quarter
+    float *g1buf;           // [n_seqs][nblk][H_v][16][16] Gram G1 = delta^T (scale gy)
+    float *vsbuf;           // [unit][nbs][S][S] block starts of the segment being walked
+    float *dq_part, *dk_part;   // [n_seqs][T][H_v][S] per value head (null: H_v == H_k, direct)
     float *dq, *dk, *dv, *dg, *dbeta, *dstate;
     gdn_strides sq, sk, sv, sg, sb, sgy, sy;
-    int32_t s_base, n_seqs_launch, T, H_k, H_v, C, n_ck_max, nvs_max, kda, dtype;
+    int32_t s_base, n_seqs_launch, T, H_k, H_v, C, n_ck_max, nbs, kda, dtype;
     float scale;
     int32_t lens[kMaxSeqsPerLaunch];
 };
-int mf128_stretch_tokens();   // tokens per replayed stretch of the backward
 hipError_t launch_prep128(const Mf128Args &a, hipStream_t st);
 hipError_t launch_fwd_mf(const Mf128Args &a, hipStream_t st);
-hipError_t launch_bwd_mf(const Mf128Args &a, hipStream_t st);
-hipError_t launch_combine_mf(const Mf128Args &a, hipStream_t st);
+hipError_t launch_bwd_mf(const Mf128Args &a, hipStream_t st);   // G1 pass, then the walk
 
 }  // namespace gdn

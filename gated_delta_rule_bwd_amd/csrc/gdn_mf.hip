@@ -23,11 +23,13 @@
 // token instead: each token is a one-token block whose state is first scaled by the token's
 // gates (c = 1 after that), so the arithmetic is the per-token recurrence itself.
 //
-// Rows of M evolve independently in both directions ("metal: GATED_DELTA_NET_BACK",
-// approval review: each row of the state is updated on its own), so a unit is split into
-// four row quarters of 32 rows, one workgroup each; the quarters of the backward meet only
-// in column sums, which each quarter writes as partials that the combine kernel adds in a
-// fixed order (and, for dq and dk, over the value heads of a key head in increasing order).
+// One workgroup owns a unit.  Rows of M evolve independently in both directions ("metal:
+// GATED_DELTA_NET_BACK", approval review: each row of the state is updated on its own), so the
+// forward gives each of its eight waves 16 rows, and the backward's chain (dd = dM k and the
+// update of dM) does the same; the backward's column sums (dq, dk, dg) take the columns of the
+// state and of the transposed gradient instead, 16 per wave, so they are complete inside the
+// workgroup.  Only dq and dk of key heads shared by several value heads are summed afterwards,
+// over those value heads in increasing order.
 //
 // MFMA lane layout (16x16x4 f32): lane l supplies A[l%16][kappa] and B[kappa][l%16], and
 // holds D[4(l/16) + r][l%16] in accumulator register r.  Every product below uses the
@@ -44,12 +46,9 @@ namespace {
 
 constexpr int S = 128;
 constexpr int W = 16;          // tokens per block
-constexpr int QR = 32;         // rows per quarter
-constexpr int NQ = S / QR;     // quarters per unit
 constexpr float kLo = 0x1p-60f, kHi = 0x1p60f;
 constexpr int SP = S + 4;      // [token][column] LDS rows
 constexpr int KP = W + 4;      // [column][token] LDS rows
-constexpr int RP = QR + 4;     // [token][row] LDS rows (backward row data)
 constexpr int MATF = 3 * W * W;   // floats of block matrices: Bm, Te, Tb
 
 typedef float f4 __attribute__((ext_vector_type(4)));
@@ -60,8 +59,6 @@ __device__ __forceinline__ f4 mfma(float a, float b, f4 c) {
 __device__ __forceinline__ f4 ld4(const float *p) { return *reinterpret_cast<const f4 *>(p); }
 __device__ __forceinline__ void st4(float *p, f4 v) { *reinterpret_cast<f4 *>(p) = v; }
 __device__ __forceinline__ f4 zero4() { return f4{0.f, 0.f, 0.f, 0.f}; }
-// compiler-only barrier: keeps memory accesses of one phase from being hoisted into another
-__device__ __forceinline__ void fence() { asm volatile("" ::: "memory"); }
 __device__ __forceinline__ float rcp(float x) { return __builtin_amdgcn_rcpf(x); }
 __device__ __forceinline__ float as_f(int x) { return __builtin_bit_cast(float, x); }
 __device__ __forceinline__ int as_i(float x) { return __builtin_bit_cast(int, x); }
@@ -129,22 +126,14 @@ __device__ __forceinline__ const In<DT> *tin(const void *p) {
     return reinterpret_cast<const In<DT> *>(p);
 }
 
-// Block index -> (unit of the launch, quarter); the four quarters of a unit go to one XCD
-// (workgroups are dealt to the eight XCDs round robin) so they share its L2.
-__device__ __forceinline__ void map_block(int b, int nb, int &unit, int &qb) {
-    int lin = b;
-    if (nb % (8 * NQ) == 0) lin = (b % 8) * (nb / 8) + b / 8;
-    unit = lin / NQ;
-    qb = lin % NQ;
-}
-
 // ------------------------------------------------------------------ block preparation
 
-// Per block of every (sequence, value head): the flag of a block processed token by token,
-// and the block matrices Bm (upper triangle of B with its diagonal), Te = (I + diag(beta) A)^-1
-// and Tb = (I + A diag(beta))^-1, A the strict upper triangle of the Gram A; a token-by-token
-// block gets Bm = diag(k_t . q_t) and Te = Tb = I.  One wave per block (lane: columns lane
-// and lane + 64 over the block's tokens).
+// Per block of every (sequence, value head): the running gate products c (written to cbuf for
+// every token of the block), the flag of a block processed token by token (its cbuf rows then
+// hold the gates a themselves), and the block matrices Bm (upper triangle of B with its
+// diagonal), Te = (I + diag(beta) A)^-1 and Tb = (I + A diag(beta))^-1, A the strict upper
+// triangle of the Gram A; a token-by-token block gets Bm = diag(k_t . q_t) and Te = Tb = I.
+// One wave per block (lane: columns lane and lane + 64 over the block's tokens).
 struct alignas(16) PrepLds {
     float kr[W][SP], kc[W][SP], qc[W][SP];
     float am[W][W + 1];
@@ -157,6 +146,7 @@ __global__ void __launch_bounds__(64) prep128_kernel(const Mf128Args a) {
     constexpr uint32_t ES = sizeof(In<DT>);
     const int lane = threadIdx.x, lm = lane & 15, g4 = lane >> 4;
     const int nblk = (a.T + W - 1) / W;
+    const int G = a.kda ? S : 1;
     const int64_t items = (int64_t)a.n_seqs_launch * nblk * a.H_v;
     const uint32_t gt = (uint32_t)a.sg.tok * ES, kt = (uint32_t)a.sk.tok * ES, qt = (uint32_t)a.sq.tok * ES;
     for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
@@ -192,6 +182,21 @@ __global__ void __launch_bounds__(64) prep128_kernel(const Mf128Args a) {
             }
         }
         const bool direct = __ballot(!ok) != 0;
+        {   // the running products (a token-by-token block: the gates) for the forward and backward
+            float *cb = a.cbuf + ((s * a.T + t0) * a.H_v + h) * (int64_t)G;
+            const int64_t ct = (int64_t)a.H_v * G;
+#pragma unroll
+            for (int n = 0; n < 2; ++n) {
+                const uint32_t i = lane + 64 * n;
+                if ((int)i < G) {
+#pragma unroll
+                    for (int tt = 0; tt < W; ++tt) {
+                        if (tt < cnt)
+                            cb[tt * ct + i] = direct ? expf(bld<DT>(rg, (a.kda ? i : 0u) * ES, tt * gt)) : c[n][tt];
+                    }
+                }
+            }
+        }
 #pragma unroll
         for (int n = 0; n < 2; ++n) {
             const int i = lane + 64 * n;
@@ -232,23 +237,24 @@ __global__ void __launch_bounds__(64) prep128_kernel(const Mf128Args a) {
             wm[sg * W + tt] = direct ? (sg == tt ? gB[r] : 0.f) : (sg <= tt ? gB[r] : 0.f);
         }
         __syncthreads();
-        // rows of the unit upper triangular inverses: lane sg < 16 of Te, 16 + sg of Tb; the
-        // matrix is read whole into registers first (broadcast LDS reads)
+        // rows of the unit upper triangular inverses (lane sg < 16: Te, 16 + sg: Tb), column by
+        // column: once entry rho of the row is final it is pushed into the later entries
         if (lane < 2 * W) {
             const int sg = lane & 15;
             const bool tb = lane >= W;
             float v[W];
 #pragma unroll
-            for (int tt = 0; tt < W; ++tt) {
-                float acc = 0.f;
+            for (int tt = 0; tt < W; ++tt) v[tt] = tt == sg ? 1.f : 0.f;
 #pragma unroll
-                for (int rho = 0; rho < tt; ++rho) {
-                    if (rho >= sg) {
+            for (int rho = 0; rho < W - 1; ++rho) {
+                if (rho >= sg) {
+                    const float vr = v[rho];
+#pragma unroll
+                    for (int tt = rho + 1; tt < W; ++tt) {
                         const float l = tb ? sm.am[rho][tt] * sm.bt[tt] : sm.bt[rho] * sm.am[rho][tt];
-                        acc = fmaf(v[rho], l, acc);
+                        v[tt] = fmaf(-vr, l, v[tt]);
                     }
                 }
-                v[tt] = tt < sg ? 0.f : (tt == sg ? 1.f : -acc);
             }
             float *dst = wm + (tb ? 2 : 1) * W * W + sg * W;
 #pragma unroll
@@ -261,42 +267,47 @@ __global__ void __launch_bounds__(64) prep128_kernel(const Mf128Args a) {
 
 // ------------------------------------------------------------------ forward scan
 
-// A workgroup owns a row quarter (32 rows) of a unit: two waves of 16 rows, each holding the
-// state transposed as eight 16 x 16 accumulator tiles, tile ib: lane l register r holds
-// M[j0 + l%16][16 ib + 4(l/16) + r].  Thread tid stages column tid of each block; the
-// block's inputs are loaded into registers one block ahead.
-struct alignas(16) FwdMfLds {
+constexpr int NW = 8;          // waves per workgroup, 16 rows each
+constexpr int NT = 64 * NW;    // threads per workgroup
+
+// A workgroup owns a unit (sequence, value head).  Wave w holds rows 16 w .. 16 w + 15 of the
+// state transposed as eight 16 x 16 tiles: tile ib, lane l, register r holds
+// M[16 w + l%16][16 ib + 4(l/16) + r].  Thread tid stages column tid % 128 of tokens
+// 4 (tid / 128) .. + 3 of a block; the next block's inputs are loaded into registers while the
+// current block is computed.
+struct alignas(16) FwdLds {
     float kc[W][SP], qc[W][SP];   // c.*k, c.*q   [token][column]
     float kr[S][KP];              // k./c         [column][token]
-    float pv[S];                  // block product (scaled block) or the token's gates
+    float pv[S];                  // block product per column (a token's gates)
 };
 
 template <int DT>
-__global__ void __launch_bounds__(128, 2) fwd_mf_kernel(const Mf128Args a) {
-    __shared__ FwdMfLds sm;
+__global__ void __launch_bounds__(NT) fwd_mf_kernel(const Mf128Args a) {
+    __shared__ FwdLds sm;
     constexpr uint32_t ES = sizeof(In<DT>);
-    int ul, qb;
-    map_block(blockIdx.x, gridDim.x, ul, qb);
+    const int ul = blockIdx.x;
     const int sl = ul / a.H_v, h = ul % a.H_v;
     const int64_t s = a.s_base + sl;
     const int hk = h % a.H_k;
     const int L = a.lens[sl];
     const int64_t unit = s * a.H_v + h;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, lm = lane & 15, g4 = lane >> 4;
-    const int j0 = qb * QR + wv * 16;
+    const int j0 = wv * 16;
+    const int ci = tid & (S - 1), tg = __builtin_amdgcn_readfirstlane(tid >> 7);   // staging: column ci, tokens 4 tg .. 4 tg + 3
     const int nblk = (a.T + W - 1) / W;
+    const int G = a.kda ? S : 1;
     const bool vec_state = (((uintptr_t)a.state0 | (uintptr_t)a.state_out) & 15) == 0;
-    const In<DT> *gin = tin<DT>(a.g) + s * a.sg.seq + h * a.sg.head;
+    const float *cin = a.cbuf + (s * a.T * a.H_v + h) * (int64_t)G;
     const In<DT> *kin = tin<DT>(a.k) + s * a.sk.seq + hk * a.sk.head;
     const In<DT> *qin = tin<DT>(a.q) + s * a.sq.seq + hk * a.sq.head;
     const In<DT> *vin = tin<DT>(a.v) + s * a.sv.seq + h * a.sv.head;
     const In<DT> *bin = tin<DT>(a.beta) + s * a.sb.seq + h * a.sb.head;
     float *yout = a.y ? a.y + s * a.sy.seq + h * a.sy.head : nullptr;
     float *eout = a.ebuf + (s * a.T * a.H_v + h) * S;
-    const uint32_t gt = (uint32_t)a.sg.tok * ES, kt = (uint32_t)a.sk.tok * ES, qt = (uint32_t)a.sq.tok * ES,
+    const uint32_t ct = (uint32_t)(a.H_v * G) * 4, kt = (uint32_t)a.sk.tok * ES, qt = (uint32_t)a.sq.tok * ES,
                    vt = (uint32_t)a.sv.tok * ES, bt = (uint32_t)a.sb.tok * ES, yt = (uint32_t)a.sy.tok * 4,
                    et = (uint32_t)(a.H_v * S) * 4;
-    const uint32_t gcol = (a.kda ? (uint32_t)tid : 0u) * ES;
+    const uint32_t ccol = (a.kda ? (uint32_t)ci : 0u) * 4;
 
     f4 M[S / 16];
     {
@@ -314,27 +325,27 @@ __global__ void __launch_bounds__(128, 2) fwd_mf_kernel(const Mf128Args a) {
     };
     float *snap = a.snap + unit * a.n_ck_max * S * S;
 
-    // inputs of one block, loaded a block ahead: column tid of g, k, q for its 16 tokens; per
-    // lane v and beta at (token 4(l/16) + r, row j0 + l%16) and the block matrices' operands
+    // inputs of one block: column ci of c, k, q at tokens 4 tg .. + 3; per lane v and beta at
+    // (token 4(l/16) + r, row 16 w + l%16) and the operands of Te^T and Bm^T
     struct Pre {
-        float g[W], k[W], q[W];
+        float c[4], k[4], q[4];
         float v[4], b[4], te[4], bm[4];
         int dir;
     };
     auto prefetch = [&](Pre &P, int t0) {
         const int cnt = min(W, L - t0);
         const int64_t bi = (s * nblk + t0 / W) * a.H_v + h;
-        const float *wm = a.wmat + bi * MATF;
         P.dir = a.wflag[bi];
-        const Rsrc rg = rsrc(gin + (int64_t)t0 * a.sg.tok), rk = rsrc(kin + (int64_t)t0 * a.sk.tok),
+        const Rsrc rc = rsrc(cin + (int64_t)t0 * (a.H_v * G)), rk = rsrc(kin + (int64_t)t0 * a.sk.tok),
                    rq = rsrc(qin + (int64_t)t0 * a.sq.tok), rv = rsrc(vin + (int64_t)t0 * a.sv.tok),
-                   rb = rsrc(bin + (int64_t)t0 * a.sb.tok), rw = rsrc(wm);
+                   rb = rsrc(bin + (int64_t)t0 * a.sb.tok), rw = rsrc(a.wmat + bi * MATF);
 #pragma unroll
-        for (int tt = 0; tt < W; ++tt) {
-            const bool ok = tt < cnt;
-            P.g[tt] = ok ? bld<DT>(rg, gcol, tt * gt) : 0.f;
-            P.k[tt] = ok ? bld<DT>(rk, tid * ES, tt * kt) : 0.f;
-            P.q[tt] = ok ? bld<DT>(rq, tid * ES, tt * qt) : 0.f;
+        for (int x = 0; x < 4; ++x) {
+            const uint32_t tt = 4 * tg + x;
+            const bool ok = (int)tt < cnt;
+            P.c[x] = ok ? bldf(rc, ccol, tt * ct) : 1.f;
+            P.k[x] = ok ? bld<DT>(rk, ci * ES, tt * kt) : 0.f;
+            P.q[x] = ok ? bld<DT>(rq, ci * ES, tt * qt) : 0.f;
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -401,26 +412,23 @@ __global__ void __launch_bounds__(128, 2) fwd_mf_kernel(const Mf128Args a) {
         for (int ib = 0; ib < S / 16; ++ib) M[ib] *= ld4(&sm.pv[16 * ib + 4 * g4]);
     };
 
-    const int i = tid;   // staged column
     Pre P;
     if (L > 0) prefetch(P, 0);
     for (int b = 0; b * W < L; ++b) {
         const int t0 = b * W, cnt = min(W, L - t0);
         if (t0 % a.C == 0) store_state(snap + (int64_t)(t0 / a.C) * S * S);
         if (!P.dir) {
-            float run = 1.f;
-            float krow[W];
+            float krow[4];
 #pragma unroll
-            for (int tt = 0; tt < W; ++tt) {
-                const float av = tt < cnt ? expf(P.g[tt]) : 1.f;
-                run = tt == 0 ? av : run * av;
-                krow[tt] = P.k[tt] * rcp(run);
-                sm.kc[tt][i] = P.k[tt] * run;
-                sm.qc[tt][i] = P.q[tt] * run;
+            for (int x = 0; x < 4; ++x) {
+                const int tt = 4 * tg + x;
+                const float c = P.c[x];
+                krow[x] = P.k[x] * rcp(c);
+                sm.kc[tt][ci] = P.k[x] * c;
+                sm.qc[tt][ci] = P.q[x] * c;
+                if (tt == cnt - 1) sm.pv[ci] = c;
             }
-#pragma unroll
-            for (int tt = 0; tt < W; tt += 4) st4(&sm.kr[i][tt], f4{krow[tt], krow[tt + 1], krow[tt + 2], krow[tt + 3]});
-            sm.pv[i] = run;
+            st4(&sm.kr[ci][4 * tg], f4{krow[0], krow[1], krow[2], krow[3]});
             const float vv[4] = {P.v[0], P.v[1], P.v[2], P.v[3]}, bb[4] = {P.b[0], P.b[1], P.b[2], P.b[3]};
             const float teA[4] = {P.te[0], P.te[1], P.te[2], P.te[3]}, bmA[4] = {P.bm[0], P.bm[1], P.bm[2], P.bm[3]};
             __syncthreads();
@@ -431,27 +439,27 @@ __global__ void __launch_bounds__(128, 2) fwd_mf_kernel(const Mf128Args a) {
         } else {   // token by token: each token a one-token block after its gates scale the state
             const int64_t bi = (s * nblk + b) * a.H_v + h;
             const float *wm = a.wmat + bi * MATF;
-            const Rsrc rg = rsrc(gin + (int64_t)t0 * a.sg.tok), rk = rsrc(kin + (int64_t)t0 * a.sk.tok),
+            const Rsrc rc = rsrc(cin + (int64_t)t0 * (a.H_v * G)), rk = rsrc(kin + (int64_t)t0 * a.sk.tok),
                        rq = rsrc(qin + (int64_t)t0 * a.sq.tok), rv = rsrc(vin + (int64_t)t0 * a.sv.tok),
                        rb = rsrc(bin + (int64_t)t0 * a.sb.tok);
             for (int tau = 0; tau < cnt; ++tau) {
-                const float av = expf(bld<DT>(rg, gcol, tau * gt));
-                const float kx = bld<DT>(rk, i * ES, tau * kt);
-                const float qx = bld<DT>(rq, i * ES, tau * qt);
+                const float av = bldf(rc, ccol + tau * ct, 0);
+                const float kx = bld<DT>(rk, ci * ES + tau * kt, 0);
+                const float qx = bld<DT>(rq, ci * ES + tau * qt, 0);
 #pragma unroll
-                for (int tt = 0; tt < W; ++tt) {
-                    sm.kc[tt][i] = tt == 0 ? kx : 0.f;
-                    sm.qc[tt][i] = tt == 0 ? qx : 0.f;
+                for (int x = 0; x < 4; ++x) {
+                    const int tt = 4 * tg + x;
+                    sm.kc[tt][ci] = tt == 0 ? kx : 0.f;
+                    sm.qc[tt][ci] = tt == 0 ? qx : 0.f;
                 }
-#pragma unroll
-                for (int tt = 0; tt < W; tt += 4) st4(&sm.kr[i][tt], f4{tt == 0 ? kx : 0.f, 0.f, 0.f, 0.f});
-                sm.pv[i] = av;
+                st4(&sm.kr[ci][4 * tg], f4{tg == 0 ? kx : 0.f, 0.f, 0.f, 0.f});
+                if (tg == 0) sm.pv[ci] = av;
                 float vv[4], bb[4], teA[4], bmA[4];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int tt = 4 * g4 + r;
-                    vv[r] = tt == 0 ? bld<DT>(rv, (j0 + lm) * ES, tau * vt) : 0.f;
-                    bb[r] = tt == 0 ? bld<DT>(rb, 0, tau * bt) : 0.f;
+                    vv[r] = tt == 0 ? bld<DT>(rv, (j0 + lm) * ES + tau * vt, 0) : 0.f;
+                    bb[r] = tt == 0 ? bld<DT>(rb, tau * bt, 0) : 0.f;
                     teA[r] = tt == lm ? 1.f : 0.f;
                     bmA[r] = (tt == 0 && lm == 0) ? wm[tau * (W + 1)] : 0.f;
                 }
@@ -464,9 +472,9 @@ __global__ void __launch_bounds__(128, 2) fwd_mf_kernel(const Mf128Args a) {
         }
     }
     if (yout) {
-        for (int64_t idx = tid; idx < (int64_t)(a.T - L) * QR; idx += 128) {
-            const int64_t t = L + idx / QR;
-            yout[t * a.sy.tok + qb * QR + (int)(idx % QR)] = 0.f;
+        for (int64_t idx = tid; idx < (int64_t)(a.T - L) * S; idx += NT) {
+            const int64_t t = L + idx / S;
+            yout[t * a.sy.tok + (int)(idx % S)] = 0.f;
         }
     }
     if (a.state_out) {
@@ -484,32 +492,91 @@ __global__ void __launch_bounds__(128, 2) fwd_mf_kernel(const Mf128Args a) {
 
 // ------------------------------------------------------------------ backward
 
-// A workgroup owns a row quarter (32 rows) of a unit; wave w owns its 32 rows at the 32
-// columns 32w .. 32w + 31: four 16 x 16 tiles (jb, ib), lane l register r holding element
-// [16 jb + 4(l/16) + r][16 ib + l%16] of the quarter's rows and the wave's columns.  The
-// start state of a block (M) and the gradient X = dM diag(c) (Xt) are held so.  Blocks are
-// walked from the last; a block's start state is the start of its 32-token stretch (a
-// snapshot, or a stretch start the segment's first pass left in the workspace) replayed over
-// at most one block.
-constexpr int VS = 2 * W;      // tokens per stretch
-constexpr int SCR_DD = 2 * W * (W + 4) - 512;   // dd0 partials at the scratch's end
+// The Gram G1[s][t] = delta_s . (scale gy_t) over the 128 rows of every block of every unit
+// (it needs only the forward's errors and the cotangent).  One wave per block; a block processed
+// token by token keeps its diagonal (the one-token Grams).
+template <int DT>
+__global__ void __launch_bounds__(64) gram1_kernel(const Mf128Args a) {
+    constexpr uint32_t ES = sizeof(In<DT>);
+    const int lane = threadIdx.x, lm = lane & 15, g4 = lane >> 4;
+    const int nblk = (a.T + W - 1) / W;
+    const int64_t items = (int64_t)a.n_seqs_launch * nblk * a.H_v;
+    const uint32_t gyt = (uint32_t)a.sgy.tok * ES;
+    for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
+        const int h = (int)(it % a.H_v);
+        const int64_t rest = it / a.H_v;
+        const int b = (int)(rest % nblk), sl = (int)(rest / nblk);
+        const int t0 = b * W, cnt = min(W, a.lens[sl] - t0);
+        if (cnt <= 0) continue;
+        const int64_t s = a.s_base + sl;
+        const bool ok = lm < cnt;
+        const float *er = a.ebuf + ((s * a.T + t0 + (ok ? lm : 0)) * a.H_v + h) * S;
+        const Rsrc rgy = rsrc(tin<DT>(a.gy) + s * a.sgy.seq + (int64_t)t0 * a.sgy.tok + h * a.sgy.head);
+        const Rsrc rb = rsrc(tin<DT>(a.beta) + s * a.sb.seq + (int64_t)t0 * a.sb.tok + h * a.sb.head);
+        const float bl = ok ? bld<DT>(rb, lm * (uint32_t)a.sb.tok * ES, 0) : 0.f;
+        // A = delta^T (row s = l%16, rows j along the contraction), B = scale gy (column t = l%16)
+        f4 g0 = zero4(), g1 = zero4();
+#pragma unroll
+        for (int kb = 0; kb < S / 16; ++kb) {
+            const int j = 16 * kb + 4 * g4;
+            const f4 e4 = ok ? ld4(er + j) : zero4();
+            f4 y4;
+#pragma unroll
+            for (int x = 0; x < 4; ++x) y4[x] = ok ? a.scale * bld<DT>(rgy, (j + x) * ES + lm * gyt, 0) : 0.f;
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                if (kb % 2 == 0) g0 = mfma(bl * e4[x], y4[x], g0);
+                else g1 = mfma(bl * e4[x], y4[x], g1);
+            }
+        }
+        const f4 gsum = g0 + g1;
+        float *dst = a.g1buf + ((s * nblk + b) * a.H_v + h) * (int64_t)(W * W);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dst[(4 * g4 + r) * W + lm] = gsum[r];
+    }
+}
 
-struct alignas(16) BwdMfLds {
-    float cc[4][32][KP], kk[4][32][KP], qq[4][32][KP];   // per wave: c, k, q [column][token]
-    float pw[4][32];                                     // per wave: a token's gates (token by token)
-    float sgy[W][RP], ee[W][RP], du[W][RP];              // scale gy, e, du of the quarter's rows
-    float bt[W];
-    float bm[W][W], tb[W][W];
-    float scr[4][2 * W * (W + 4)];                       // per wave: transposes, partial sums
+// A workgroup owns a unit.  Two layouts of the 128 x 128 matrices:
+//  - rows, for the chain dd = dM k and the update of dM: wave w holds rows 16 w .. 16 w + 15 of
+//    the gradient X = dM diag(c) transposed as eight tiles (tile ib, lane l, register r:
+//    X[16 w + l%16][16 ib + 4(l/16) + r]);
+//  - columns, for the column sums (dq, dk, dg) and the state replay: wave w holds columns
+//    16 w .. 16 w + 15 of the state M as eight tiles (tile jb, lane l, register r:
+//    M[16 jb + 4(l/16) + r][16 w + l%16]).
+// The gradient reaches the column layout through a transpose in LDS once per block.  Column
+// results are tiles P[i][t] (lane l, register r: column 16 w + 4(l/16) + r, token l%16).
+//
+// Per segment of C tokens the backward runs a fixed sequence of steps: replays of the segment's
+// blocks from its snapshot, each leaving the next block's start state in the workspace; for the
+// sequence's last segment, a replay of its last block (the final state, which starts the dg
+// recursion); then walks of the blocks from the last, each from its saved start state.  The
+// inputs of each step are loaded into registers during the previous step.
+constexpr int GP = W + 4;   // row pitch of the per-wave 16 x 16 partials
+
+struct alignas(16) BwdLds {
+    float krT[W][SP];          // k./c        [token][column]
+    float krI[S][KP];          // k./c        [column][token]
+    float qcI[S][KP];          // c.*q        [column][token]
+    float kcI[S][KP];          // c.*k        [column][token]
+    float sgy[W][SP];          // scale gy    [token][row]
+    float ee[W][SP];           // e           [token][row]
+    float du[W][SP];           // du          [token][row]
+    float xt[S][SP];           // X after the fold [column][row]; in a replay: delta [row][token]
+    float pv[S];               // fold factor per column (a token's gates)
+    float bt[W];               // beta
+    float bm[W][W], tb[W][W];  // Bm, Tb
+    float g1[W][GP];           // G1 = delta^T scale gy
+    float gp[NW][W][GP];       // per-wave partials of G2 = delta^T du, [s][t]
+    float gpt[NW][W][GP];      // the same, [t][s]
+    float pb[NW][W];           // per-wave partials of dbeta
+    float gs[NW][W];           // per-wave partial sums of the scalar gate's dg
 };
-static_assert(2 * W * (W + 4) >= 16 * RP && 2 * W * (W + 4) >= 512, "scratch size");
 
 template <int DT>
-__global__ void __launch_bounds__(256, 2) bwd_mf_kernel(const Mf128Args a) {
-    __shared__ BwdMfLds sm;
+__global__ void __launch_bounds__(NT) bwd_mf_kernel(const Mf128Args a) {
+    __shared__ BwdLds sm;
     constexpr uint32_t ES = sizeof(In<DT>);
-    int ul, qb;
-    map_block(blockIdx.x, gridDim.x, ul, qb);
+    const int ul = blockIdx.x;
     const int sl = ul / a.H_v, h = ul % a.H_v;
     const int64_t s = a.s_base + sl;
     const int hk = h % a.H_k;
@@ -517,606 +584,533 @@ __global__ void __launch_bounds__(256, 2) bwd_mf_kernel(const Mf128Args a) {
     const int C = a.C;
     const int64_t unit = s * a.H_v + h;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, lm = lane & 15, g4 = lane >> 4;
-    const int r0 = qb * QR;                 // first row of the quarter
-    const int c0 = wv * 32;                 // first column of the wave
+    const int j0 = 16 * wv, i0 = 16 * wv;   // rows (row layout) and columns (column layout) of the wave
+    const int ci = tid & (S - 1), tg = __builtin_amdgcn_readfirstlane(tid >> 7);   // staging: column/row ci, tokens 4 tg .. 4 tg + 3
     const int nblk = (a.T + W - 1) / W;
+    const int G = a.kda ? S : 1;
     const float scale = a.scale;
     const bool kda = a.kda != 0;
-    float *scr = sm.scr[wv];
-    float (*cc)[KP] = sm.cc[wv];
-    float (*kk)[KP] = sm.kk[wv];
-    float (*qq)[KP] = sm.qq[wv];
+    float (*dl)[KP] = reinterpret_cast<float (*)[KP]>(&sm.xt[0][0]);   // a replay's delta [row][token]
     // bases of this (sequence, head) and byte strides per token
-    const In<DT> *gin = tin<DT>(a.g) + s * a.sg.seq + h * a.sg.head;
+    const float *cin = a.cbuf + (s * a.T * a.H_v + h) * (int64_t)G;
     const In<DT> *kin = tin<DT>(a.k) + s * a.sk.seq + hk * a.sk.head;
     const In<DT> *qin = tin<DT>(a.q) + s * a.sq.seq + hk * a.sq.head;
-    const In<DT> *gyin = tin<DT>(a.gy) + s * a.sgy.seq + h * a.sgy.head + r0;
+    const In<DT> *gyin = tin<DT>(a.gy) + s * a.sgy.seq + h * a.sgy.head;
     const In<DT> *bin = tin<DT>(a.beta) + s * a.sb.seq + h * a.sb.head;
-    const int64_t row0 = s * a.T * a.H_v + h;   // workspace row of token 0; token stride H_v
-    const float *ein = a.ebuf + row0 * S + r0;
-    float *dvout = a.dv + row0 * S + r0;
-    float *pout = a.part + row0 * (NQ * 3 * S) + qb * (3 * S);
-    float *pbout = a.pbuf + row0 * (2 * NQ) + 2 * qb;
-    const uint32_t gt = (uint32_t)a.sg.tok * ES, kt = (uint32_t)a.sk.tok * ES, qt = (uint32_t)a.sq.tok * ES,
-                   gyt = (uint32_t)a.sgy.tok * ES, bt = (uint32_t)a.sb.tok * ES;
-    const uint32_t et = (uint32_t)a.H_v * S * 4, pt = (uint32_t)a.H_v * (NQ * 3 * S) * 4,
-                   pbt = (uint32_t)a.H_v * (2 * NQ) * 4;
+    const int64_t row0 = s * a.T * a.H_v + h;   // per-token workspace row of token 0; stride H_v
+    const float *ein = a.ebuf + row0 * S;
+    float *dvout = a.dv + row0 * S;
+    float *dqout = (a.dq_part ? a.dq_part : a.dq) + row0 * S;   // direct when H_v == H_k
+    float *dkout = (a.dk_part ? a.dk_part : a.dk) + row0 * S;
+    float *dgout = a.dg + row0 * G;
+    float *dbout = a.dbeta + row0;
+    const bool vec_out = (((uintptr_t)dqout | (uintptr_t)dkout | (uintptr_t)dgout) & 15) == 0;
+    const uint32_t ct = (uint32_t)(a.H_v * G) * 4, kt = (uint32_t)a.sk.tok * ES, qt = (uint32_t)a.sq.tok * ES,
+                   gyt = (uint32_t)a.sgy.tok * ES, bt = (uint32_t)a.sb.tok * ES, et = (uint32_t)a.H_v * S * 4;
+    const uint32_t ccol = (kda ? (uint32_t)ci : 0u) * 4;
 
-    auto load_state = [&](const float *base, f4 (&Mr)[2][2]) {
+    // the column layout in memory (row-major [S][S]): one vector offset per lane, the row block
+    // and register in the scalar offset
+    const uint32_t vcol = ((4 * g4) * S + i0 + lm) * 4;
+    auto load_cols = [&](const float *base, f4 (&Mc)[8]) {
+        const Rsrc rs = rsrc(base);
 #pragma unroll
-        for (int jb = 0; jb < 2; ++jb)
+        for (int jb = 0; jb < 8; ++jb)
 #pragma unroll
-            for (int ib = 0; ib < 2; ++ib)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) Mr[jb][ib][r] = base[(16 * jb + 4 * g4 + r) * S + c0 + 16 * ib + lm];
+            for (int r = 0; r < 4; ++r) Mc[jb][r] = bldf(rs, vcol, (16 * jb + r) * S * 4);
     };
-    auto save_state = [&](float *base, const f4 (&Mr)[2][2]) {
+    auto save_cols = [&](float *base, const f4 (&Mc)[8]) {
+        const Rsrc rs = rsrc(base);
 #pragma unroll
-        for (int jb = 0; jb < 2; ++jb)
+        for (int jb = 0; jb < 8; ++jb)
 #pragma unroll
-            for (int ib = 0; ib < 2; ++ib)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) base[(16 * jb + 4 * g4 + r) * S + c0 + 16 * ib + lm] = Mr[jb][ib][r];
+            for (int r = 0; r < 4; ++r) bst(rs, Mc[jb][r], vcol, (16 * jb + r) * S * 4);
     };
 
-    f4 Xt[2][2];
+    // the gradient in the row layout
+    f4 X[8];
     if (a.dstate_out) {
-        load_state(a.dstate_out + unit * S * S + (int64_t)r0 * S, Xt);
+        const float *p = a.dstate_out + unit * S * S + (int64_t)(j0 + lm) * S + 4 * g4;
+#pragma unroll
+        for (int ib = 0; ib < 8; ++ib) X[ib] = f4{p[16 * ib], p[16 * ib + 1], p[16 * ib + 2], p[16 * ib + 3]};
     } else {
 #pragma unroll
-        for (int jb = 0; jb < 2; ++jb)
-#pragma unroll
-            for (int ib = 0; ib < 2; ++ib) Xt[jb][ib] = zero4();
+        for (int ib = 0; ib < 8; ++ib) X[ib] = zero4();
     }
+    // the dg recursion's carry per column (tile layout: column i0 + 4(l/16) + r)
+    f4 carry = zero4();
 
-    // operands of the wave's columns at (column 16 ib + l%16, tokens 4(l/16) .. + 3), read from
-    // the staged block when used: k./c, c.*q, c.*k
-    auto KR = [&](int ib) {
-        const f4 cv = ld4(&cc[16 * ib + lm][4 * g4]), kv = ld4(&kk[16 * ib + lm][4 * g4]);
-        return f4{kv[0] * rcp(cv[0]), kv[1] * rcp(cv[1]), kv[2] * rcp(cv[2]), kv[3] * rcp(cv[3])};
+    // inputs of a block, loaded one step ahead: column (and row) ci at tokens 4 tg .. + 3 of c,
+    // k, q, gy, e and beta; one entry each of Bm, Tb and G1
+    struct Pre {
+        float c[4], k[4], q[4], gy[4], e[4], b[4];
+        float m0, m1, m2;
+        int dir;
     };
-    auto QC = [&](int ib) { return ld4(&qq[16 * ib + lm][4 * g4]) * ld4(&cc[16 * ib + lm][4 * g4]); };
-    auto KC = [&](int ib) { return ld4(&kk[16 * ib + lm][4 * g4]) * ld4(&cc[16 * ib + lm][4 * g4]); };
-
-    // ---- staging of a (sub)block: n tokens from tw; dir: one token, c = 1, its gates in pw
-    auto stage = [&](int tw, int n, bool dir, int tau0, const float *wm) {
-        {   // columns: lane holds column c0 + (lane & 31), tokens 8 (lane >> 5) .. + 7
-            const int ic = lane & 31, hf = lane >> 5;
-            const uint32_t i = c0 + ic;
-            const Rsrc rg = rsrc(gin + (int64_t)tw * a.sg.tok), rk = rsrc(kin + (int64_t)tw * a.sk.tok),
-                       rq = rsrc(qin + (int64_t)tw * a.sq.tok);
-            const uint32_t gcol = (kda ? i : 0u) * ES;
-            float av[8], kv[8], qv[8];
+    auto prefetch = [&](Pre &P, int t0) {
+        const int cnt = min(W, L - t0);
+        const int64_t bi = (s * nblk + t0 / W) * a.H_v + h;
+        P.dir = a.wflag[bi];
+        const Rsrc rc = rsrc(cin + (int64_t)t0 * (a.H_v * G)), rk = rsrc(kin + (int64_t)t0 * a.sk.tok),
+                   rq = rsrc(qin + (int64_t)t0 * a.sq.tok), rgy = rsrc(gyin + (int64_t)t0 * a.sgy.tok),
+                   re = rsrc(ein + (int64_t)t0 * (a.H_v * S)), rb = rsrc(bin + (int64_t)t0 * a.sb.tok),
+                   rw = rsrc(a.wmat + bi * MATF), rg1 = rsrc(a.g1buf + bi * (W * W));
 #pragma unroll
-            for (int x = 0; x < 8; ++x) {
-                const uint32_t tt = 8 * hf + x;
-                const bool valid = (int)tt < n;
-                av[x] = valid ? expf(bld<DT>(rg, gcol + tt * gt, 0)) : 1.f;
-                kv[x] = valid ? bld<DT>(rk, i * ES + tt * kt, 0) : 0.f;
-                qv[x] = valid ? bld<DT>(rq, i * ES + tt * qt, 0) : 0.f;
-            }
-            float c[8];
-            c[0] = av[0];
-#pragma unroll
-            for (int x = 1; x < 8; ++x) c[x] = c[x - 1] * av[x];
-            const float c7 = __shfl(c[7], ic, 64);
-            if (hf) {
-                c[0] = c7 * av[0];
-#pragma unroll
-                for (int x = 1; x < 8; ++x) c[x] = c[x - 1] * av[x];
-            }
-            if (dir) {
-                if (hf == 0) sm.pw[wv][ic] = av[0];
-#pragma unroll
-                for (int x = 0; x < 8; ++x) c[x] = 1.f;
-            }
-#pragma unroll
-            for (int x = 0; x < 8; x += 4) {
-                st4(&cc[ic][8 * hf + x], f4{c[x], c[x + 1], c[x + 2], c[x + 3]});
-                st4(&kk[ic][8 * hf + x], f4{kv[x], kv[x + 1], kv[x + 2], kv[x + 3]});
-                st4(&qq[ic][8 * hf + x], f4{qv[x], qv[x + 1], qv[x + 2], qv[x + 3]});
-            }
+        for (int x = 0; x < 4; ++x) {
+            const uint32_t tt = 4 * tg + x;
+            const bool ok = (int)tt < cnt;
+            P.c[x] = ok ? bldf(rc, ccol, tt * ct) : 1.f;
+            P.k[x] = ok ? bld<DT>(rk, ci * ES, tt * kt) : 0.f;
+            P.q[x] = ok ? bld<DT>(rq, ci * ES, tt * qt) : 0.f;
+            P.gy[x] = ok ? bld<DT>(rgy, ci * ES, tt * gyt) : 0.f;
+            P.e[x] = ok ? bldf(re, ci * 4, tt * et) : 0.f;
+            P.b[x] = ok ? bld<DT>(rb, 0, tt * bt) : 0.f;
         }
-        {   // rows of the quarter: scale gy, e; beta; the block matrices
-            const Rsrc rgy = rsrc(gyin + (int64_t)tw * a.sgy.tok), re = rsrc(ein + (int64_t)tw * (a.H_v * S));
+        const uint32_t m = tid & 255;
+        P.m0 = bldf(rw, m * 4, 0);                  // Bm
+        P.m1 = bldf(rw, (2 * W * W + m) * 4, 0);    // Tb
+        P.m2 = bldf(rg1, m * 4, 0);                 // G1
+    };
+    // staging of a column-scaled block for a walk
+    auto stage_walk = [&](const Pre &P, int cnt) {
+        float kr[4], qc[4], kc[4];
 #pragma unroll
-            for (int x = 0; x < 2; ++x) {
-                const int idx = tid + 256 * x;
-                const uint32_t tt = idx >> 5, j = idx & 31;
-                const bool valid = (int)tt < n;
-                sm.sgy[tt][j] = valid ? scale * bld<DT>(rgy, j * ES + tt * gyt, 0) : 0.f;
-                sm.ee[tt][j] = valid ? bldf(re, j * 4 + tt * et, 0) : 0.f;
+        for (int x = 0; x < 4; ++x) {
+            const int tt = 4 * tg + x;
+            const float c = P.c[x];
+            kr[x] = P.k[x] * rcp(c);
+            qc[x] = P.q[x] * c;
+            kc[x] = P.k[x] * c;
+            sm.krT[tt][ci] = kr[x];
+            sm.sgy[tt][ci] = scale * P.gy[x];
+            sm.ee[tt][ci] = P.e[x];
+            if (tt == cnt - 1) sm.pv[ci] = c;
+            if (ci == 0) sm.bt[tt] = P.b[x];
+        }
+        st4(&sm.krI[ci][4 * tg], f4{kr[0], kr[1], kr[2], kr[3]});
+        st4(&sm.qcI[ci][4 * tg], f4{qc[0], qc[1], qc[2], qc[3]});
+        st4(&sm.kcI[ci][4 * tg], f4{kc[0], kc[1], kc[2], kc[3]});
+        if (tid < 256) {
+            (&sm.bm[0][0])[tid] = P.m0;
+            (&sm.tb[0][0])[tid] = P.m1;
+            sm.g1[tid >> 4][tid & 15] = P.m2;
+        }
+        __syncthreads();
+    };
+    // staging of a column-scaled block for a replay: k./c and delta [row][token]
+    auto stage_replay = [&](const Pre &P, int cnt) {
+        float kr[4], d[4];
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+            const int tt = 4 * tg + x;
+            kr[x] = P.k[x] * rcp(P.c[x]);
+            d[x] = P.b[x] * P.e[x];
+            if (tt == cnt - 1) sm.pv[ci] = P.c[x];
+        }
+        st4(&sm.krI[ci][4 * tg], f4{kr[0], kr[1], kr[2], kr[3]});
+        st4(&dl[ci][4 * tg], f4{d[0], d[1], d[2], d[3]});
+        __syncthreads();
+    };
+    // staging of token t0 + tau of a token-by-token block (loaded directly) as a one-token block
+    // with c = 1, the token's gates in pv
+    auto stage_token = [&](int t0, int tau, bool walk) {
+        const int64_t bi = (s * nblk + t0 / W) * a.H_v + h;
+        const Rsrc rc = rsrc(cin + (int64_t)t0 * (a.H_v * G)), rk = rsrc(kin + (int64_t)t0 * a.sk.tok),
+                   rq = rsrc(qin + (int64_t)t0 * a.sq.tok), rgy = rsrc(gyin + (int64_t)t0 * a.sgy.tok),
+                   re = rsrc(ein + (int64_t)t0 * (a.H_v * S)), rb = rsrc(bin + (int64_t)t0 * a.sb.tok);
+        const float av = bldf(rc, ccol + tau * ct, 0);
+        const float kx = bld<DT>(rk, ci * ES + tau * kt, 0);
+        const float ex = bldf(re, ci * 4 + tau * et, 0);
+        const float bx = bld<DT>(rb, tau * bt, 0);
+        const f4 k4 = f4{tg == 0 ? kx : 0.f, 0.f, 0.f, 0.f};
+        st4(&sm.krI[ci][4 * tg], k4);
+        if (tg == 0) sm.pv[ci] = av;
+        if (!walk) {
+            st4(&dl[ci][4 * tg], f4{tg == 0 ? bx * ex : 0.f, 0.f, 0.f, 0.f});
+        } else {
+            const float qx = bld<DT>(rq, ci * ES + tau * qt, 0);
+            const float gx = scale * bld<DT>(rgy, ci * ES + tau * gyt, 0);
+            st4(&sm.qcI[ci][4 * tg], f4{tg == 0 ? qx : 0.f, 0.f, 0.f, 0.f});
+            st4(&sm.kcI[ci][4 * tg], k4);
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                const int tt = 4 * tg + x;
+                sm.krT[tt][ci] = tt == 0 ? kx : 0.f;
+                sm.sgy[tt][ci] = tt == 0 ? gx : 0.f;
+                sm.ee[tt][ci] = tt == 0 ? ex : 0.f;
+                if (ci == 0) sm.bt[tt] = tt == 0 ? bx : 0.f;
             }
-            if (tid < W) sm.bt[tid] = tid < n ? bld<DT>(rsrc(bin + (int64_t)tw * a.sb.tok), tid * bt, 0) : 0.f;
-            const Rsrc rw = rsrc(wm);
-#pragma unroll
-            for (int x = 0; x < 2; ++x) {
-                const int idx = tid + 256 * x, m = idx >> 8, e = idx & 255, sg = e >> 4, tt = e & 15;
-                float val;
-                if (!dir) val = bldf(rw, ((m == 0 ? 0 : 2 * W * W) + e) * 4, 0);
-                else if (m == 0) val = (sg == 0 && tt == 0) ? bldf(rw, tau0 * (W + 1) * 4, 0) : 0.f;
-                else val = sg == tt ? 1.f : 0.f;
-                if (m == 0) sm.bm[sg][tt] = val;
-                else sm.tb[sg][tt] = val;
+            if (tid < 256) {
+                const int sg = tid >> 4, t2 = tid & 15;
+                const float *wm = a.wmat + bi * MATF;
+                const float *g1b = a.g1buf + bi * (W * W);
+                sm.bm[sg][t2] = (sg == 0 && t2 == 0) ? wm[tau * (W + 1)] : 0.f;
+                sm.tb[sg][t2] = sg == t2 ? 1.f : 0.f;
+                sm.g1[sg][t2] = (sg == 0 && t2 == 0) ? g1b[tau * (W + 1)] : 0.f;
             }
         }
         __syncthreads();
     };
-    // per-column factor of the wave's columns (block product, or the token's gates)
-    auto col_factor = [&](int ib, bool dir) { return dir ? sm.pw[wv][16 * ib + lm] : cc[16 * ib + lm][W - 1]; };
-    auto scale_cols = [&](f4 (&Z)[2][2], bool dir) {
+
+    // ---- replay of a staged (sub)block in the column layout (dir: the token's gates scale the
+    // state first; otherwise the block product folds in at the end)
+    auto replay = [&](f4 (&Mr)[8], bool dir) {
+        const float p = sm.pv[i0 + lm];
+        if (dir) {
 #pragma unroll
-        for (int ib = 0; ib < 2; ++ib) {
-            const float p = col_factor(ib, dir);
+            for (int jb = 0; jb < 8; ++jb) Mr[jb] *= p;
+        }
+        const f4 kb = ld4(&sm.krI[i0 + lm][4 * g4]);
 #pragma unroll
-            for (int jb = 0; jb < 2; ++jb) Z[jb][ib] *= p;
+        for (int jb = 0; jb < 8; ++jb) {
+            const f4 d4 = ld4(&dl[16 * jb + lm][4 * g4]);
+#pragma unroll
+            for (int x = 0; x < 4; ++x) Mr[jb] = mfma(d4[x], kb[x], Mr[jb]);
+        }
+        if (!dir) {
+#pragma unroll
+            for (int jb = 0; jb < 8; ++jb) Mr[jb] *= p;
         }
     };
-
-    // ---- replay of a staged (sub)block: Mr from the block's start to its end
-    auto replay = [&](f4 (&Mr)[2][2], bool dir) {
-        if (dir) scale_cols(Mr, true);
-        const f4 kr0 = KR(0), kr1 = KR(1);
+    // the column sums of Z .* Mr over all rows for column i0 + l%16, Z in the column layout read
+    // from memory (row-major [S][S])
+    auto colsum_mem = [&](const float *Z, const f4 (&Mr)[8]) {
+        const Rsrc rz = rsrc(Z);
+        float v = 0.f;
 #pragma unroll
-        for (int jb = 0; jb < 2; ++jb)
+        for (int jb = 0; jb < 8; ++jb)
 #pragma unroll
-            for (int x = 0; x < 4; ++x) {
-                const int tt = 4 * g4 + x;
-                const float dl = sm.bt[tt] * sm.ee[tt][16 * jb + lm];
-                Mr[jb][0] = mfma(dl, kr0[x], Mr[jb][0]);
-                Mr[jb][1] = mfma(dl, kr1[x], Mr[jb][1]);
-            }
-        if (!dir) scale_cols(Mr, false);
+            for (int r = 0; r < 4; ++r) v = fmaf(bldf(rz, vcol, (16 * jb + r) * S * 4), Mr[jb][r], v);
+        return rows4_sum(v);
+    };
+    // a value per column i0 + l%16 into the tile layout (column i0 + 4(l/16) + r)
+    auto to_tile = [&](float v) {
+        f4 o;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) o[r] = __shfl(v, 4 * g4 + r);
+        return o;
     };
 
-    // column sum over the quarter's rows of X .* Mr, for the wave's columns 16 ib + l%16
-    auto colsum_xm = [&](const f4 (&Mr)[2][2], float (&out)[2]) {
-#pragma unroll
-        for (int ib = 0; ib < 2; ++ib) {
-            float v = 0.f;
-#pragma unroll
-            for (int jb = 0; jb < 2; ++jb)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) v = fmaf(Xt[jb][ib][r], Mr[jb][ib][r], v);
-            out[ib] = rows4_sum(v);
-        }
-    };
-
-    // ---- walk of a staged (sub)block with start state Mb; n tokens from tw.  Phases: the row
-    // Gram G1 = delta^T sgy; dd0 = X kr over the wave's columns (partials to the scratch); the
-    // column sums P1 = M^T sgy (finished into dq) and P3 = X^T delta; after the partials, waves
-    // 0 and 1 solve for dd of their 16 rows; after that, P2 = M^T du, G2 = delta^T du, the
-    // update of X, and the outputs.
-    auto walk = [&](const f4 (&Mb)[2][2], int tw, int n, bool dir) {
-        if (!dir) scale_cols(Xt, false);   // X = dM diag(c) at the block's last token
+    // ---- walk of a staged (sub)block with start state Mb (column layout); n tokens from tw.
+    auto walk = [&](const f4 (&Mb)[8], int tw, int n, bool dir) {
         const float btl = sm.bt[lm];
-        // G1[s][t] = delta_s . sgy_t (D layout s = 4(l/16) + r, t = l%16) and its transpose
-        f4 g1 = zero4();
+        // ---- phase A.  Chain: X' = X diag(P), its transpose for the column sums, dd0^T = KR X'^T,
+        // dd^T = Tb (dd0^T + Bm sgy^T), du = -beta dd, dv and the dbeta partials.
+        if (!dir) {
 #pragma unroll
-        for (int jb = 0; jb < 2; ++jb) {
-            const f4 sg4 = ld4(&sm.sgy[lm][16 * jb + 4 * g4]), e4 = ld4(&sm.ee[lm][16 * jb + 4 * g4]);
-#pragma unroll
-            for (int x = 0; x < 4; ++x) g1 = mfma(btl * e4[x], sg4[x], g1);
+            for (int ib = 0; ib < 8; ++ib) X[ib] *= ld4(&sm.pv[16 * ib + 4 * g4]);
         }
 #pragma unroll
-        for (int r = 0; r < 4; ++r) scr[(4 * g4 + r) * (W + 4) + lm] = g1[r];
-        const f4 g1t = ld4(&scr[lm * (W + 4) + 4 * g4]);
-        fence();
-        // dd0 = X kr (partial over the wave's columns), via X transposed through the scratch
-        f4 dd0[2] = {zero4(), zero4()};
+        for (int ib = 0; ib < 8; ++ib)
 #pragma unroll
-        for (int jb = 0; jb < 2; ++jb) {
+            for (int r = 0; r < 4; ++r) sm.xt[16 * ib + 4 * g4 + r][j0 + lm] = X[ib][r];
+        f4 d0 = zero4(), d1 = zero4();
 #pragma unroll
-            for (int ib = 0; ib < 2; ++ib)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) scr[(4 * g4 + r) * RP + 16 * ib + lm] = Xt[jb][ib][r];
-            const f4 xt0 = ld4(&scr[lm * RP + 4 * g4]), xt1 = ld4(&scr[lm * RP + 16 + 4 * g4]);
-#pragma unroll
-            for (int ib = 0; ib < 2; ++ib)
-#pragma unroll
-                for (int x = 0; x < 4; ++x) {
-                    const int il = 16 * ib + 4 * g4 + x;
-                    const float ar = kk[il][lm] * rcp(cc[il][lm]);
-                    dd0[jb] = mfma(ar, ib ? xt1[x] : xt0[x], dd0[jb]);
-                }
-            fence();
-        }
-        st4(&scr[SCR_DD + lane * 4], dd0[0]);
-        st4(&scr[SCR_DD + 256 + lane * 4], dd0[1]);
-        fence();
-        // P1 = M^T sgy + kr (G1 masked s <= t): dq = c P1, and the dg increment's first term
-        float inc[2][4];
-        float gsum[4] = {0.f, 0.f, 0.f, 0.f};
-        const Rsrc rpo = rsrc(pout + (int64_t)tw * (pt / 4));
-        {
-            f4 p1[2] = {zero4(), zero4()};
-#pragma unroll
-            for (int jb = 0; jb < 2; ++jb) {
-                const f4 sg4 = ld4(&sm.sgy[lm][16 * jb + 4 * g4]);
-#pragma unroll
-                for (int x = 0; x < 4; ++x)
-#pragma unroll
-                    for (int ib = 0; ib < 2; ++ib) p1[ib] = mfma(sg4[x], Mb[jb][ib][x], p1[ib]);
-            }
-            {
-                const f4 kr0 = KR(0), kr1 = KR(1);
-#pragma unroll
-                for (int x = 0; x < 4; ++x) {
-                    const float wq = 4 * g4 + x <= lm ? g1[x] : 0.f;
-                    p1[0] = mfma(wq, kr0[x], p1[0]);
-                    p1[1] = mfma(wq, kr1[x], p1[1]);
-                }
-            }
-#pragma unroll
-            for (int ib = 0; ib < 2; ++ib) {
-                const f4 cv = ld4(&cc[16 * ib + lm][4 * g4]), qc = QC(ib);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int tt = 4 * g4 + r;
-                    inc[ib][r] = qc[r] * p1[ib][r];
-                    if (tt < n) bst(rpo, cv[r] * p1[ib][r], (c0 + 16 * ib + lm) * 4 + tt * pt, 0);
-                }
-            }
-        }
-        fence();
-        // P3 = X^T delta + qc (G1^T masked s >= t), the rest after G2
-        f4 p3[2] = {zero4(), zero4()};
-#pragma unroll
-        for (int jb = 0; jb < 2; ++jb) {
-            const f4 e4 = ld4(&sm.ee[lm][16 * jb + 4 * g4]);
+        for (int ib = 0; ib < 8; ib += 2) {
+            const f4 a0 = ld4(&sm.krT[lm][16 * ib + 4 * g4]), a1 = ld4(&sm.krT[lm][16 * ib + 16 + 4 * g4]);
 #pragma unroll
             for (int x = 0; x < 4; ++x) {
-                const float dl = btl * e4[x];
-#pragma unroll
-                for (int ib = 0; ib < 2; ++ib) p3[ib] = mfma(dl, Xt[jb][ib][x], p3[ib]);
+                d0 = mfma(a0[x], X[ib][x], d0);
+                d1 = mfma(a1[x], X[ib + 1][x], d1);
             }
         }
+        f4 rhs = d0 + d1;
+        float sgB[4];   // sgy^T operand: scale gy at (token 4(l/16) + x, row 16 w + l%16)
+#pragma unroll
+        for (int x = 0; x < 4; ++x) sgB[x] = sm.sgy[4 * g4 + x][j0 + lm];
         {
-            const f4 qc0 = QC(0), qc1 = QC(1);
+            const f4 bm4 = ld4(&sm.bm[lm][4 * g4]);
 #pragma unroll
-            for (int x = 0; x < 4; ++x) {
-                const float wk1 = 4 * g4 + x >= lm ? g1t[x] : 0.f;
-                p3[0] = mfma(wk1, qc0[x], p3[0]);
-                p3[1] = mfma(wk1, qc1[x], p3[1]);
-            }
+            for (int x = 0; x < 4; ++x) rhs = mfma(bm4[x], sgB[x], rhs);
         }
-        __syncthreads();   // dd0 partials
-        if (wv < 2) {      // dd of row block jb = wv: Tb (dd0 + Bm sgy), then du, dv, dbeta
-            const int jb = wv;
-            f4 acc = ld4(&sm.scr[0][SCR_DD + jb * 256 + lane * 4]);
+        f4 dd = zero4();
+        {
+            const f4 tb4 = ld4(&sm.tb[lm][4 * g4]);
 #pragma unroll
-            for (int w2 = 1; w2 < 4; ++w2) acc += ld4(&sm.scr[w2][SCR_DD + jb * 256 + lane * 4]);
-            const f4 bm4 = ld4(&sm.bm[lm][4 * g4]), tb4 = ld4(&sm.tb[lm][4 * g4]);
-#pragma unroll
-            for (int x = 0; x < 4; ++x) acc = mfma(bm4[x], sm.sgy[4 * g4 + x][16 * jb + lm], acc);
-            f4 dd = zero4();
-#pragma unroll
-            for (int x = 0; x < 4; ++x) dd = mfma(tb4[x], acc[x], dd);
+            for (int x = 0; x < 4; ++x) dd = mfma(tb4[x], rhs[x], dd);
+        }
+        float duv[4];   // du^T (token 4(l/16) + r, row 16 w + l%16), the B operand of the update
+        {
+            const Rsrc rdv = rsrc(dvout + (int64_t)tw * (a.H_v * S));
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int tt = 4 * g4 + r;
                 const float bv = sm.bt[tt];
-                sm.du[tt][16 * jb + lm] = -bv * dd[r];
-                const float pb = row16_sum(dd[r] * sm.ee[tt][16 * jb + lm]);
-                if (tt < n) {
-                    bst(rsrc(dvout + (int64_t)tw * (et / 4)), bv * dd[r], (16 * jb + lm) * 4 + tt * et, 0);
-                    if (lm == 0) bst(rsrc(pbout + (int64_t)tw * (pbt / 4)), pb, jb * 4 + tt * pbt, 0);
+                duv[r] = -bv * dd[r];
+                sm.du[tt][j0 + lm] = duv[r];
+                const float pbv = row16_sum(dd[r] * sm.ee[tt][j0 + lm]);
+                if (lm == 0) sm.pb[wv][tt] = pbv;
+                if (tt < n) bst(rdv, bv * dd[r], (j0 + lm) * 4 + tt * et, 0);
+            }
+        }
+        // Column part: P1 = M^T sgy against the block start (dq's dense part); its share of dg at
+        // the block's first token; then P1 += KR^T (G1 masked s <= t).
+        f4 p1, dgacc;
+        {
+            f4 pa = zero4(), pb = zero4();
+#pragma unroll
+            for (int jb = 0; jb < 8; jb += 2) {
+                const f4 b0 = ld4(&sm.sgy[lm][16 * jb + 4 * g4]), b1 = ld4(&sm.sgy[lm][16 * jb + 16 + 4 * g4]);
+#pragma unroll
+                for (int x = 0; x < 4; ++x) {
+                    pa = mfma(Mb[jb][x], b0[x], pa);
+                    pb = mfma(Mb[jb + 1][x], b1[x], pb);
                 }
             }
-        }
-        __syncthreads();   // du
-        // P2 = M^T du + kr (G2 masked s < t); G2 = delta^T du; P3 += kc (G2^T masked s > t)
-        f4 p2[2] = {zero4(), zero4()}, g2 = zero4();
+            p1 = pa + pb;
 #pragma unroll
-        for (int jb = 0; jb < 2; ++jb) {
-            const f4 du4 = ld4(&sm.du[lm][16 * jb + 4 * g4]), e4 = ld4(&sm.ee[lm][16 * jb + 4 * g4]);
+            for (int r = 0; r < 4; ++r) dgacc[r] = sm.qcI[i0 + 4 * g4 + r][lm] * p1[r];
+            const f4 kr4 = ld4(&sm.krI[i0 + lm][4 * g4]);
 #pragma unroll
             for (int x = 0; x < 4; ++x) {
-#pragma unroll
-                for (int ib = 0; ib < 2; ++ib) p2[ib] = mfma(du4[x], Mb[jb][ib][x], p2[ib]);
-                g2 = mfma(btl * e4[x], du4[x], g2);
+                const float g = sm.g1[4 * g4 + x][lm];
+                p1 = mfma(kr4[x], 4 * g4 + x <= lm ? g : 0.f, p1);
             }
         }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) scr[(4 * g4 + r) * (W + 4) + lm] = g2[r];
-        const f4 g2t = ld4(&scr[lm * (W + 4) + 4 * g4]);
+        __syncthreads();   // X' transposed, du, dbeta partials
+        // ---- phase B.  Column part: P3 = X'^T delta, P2 = M^T du, the G2 partial over the wave's
+        // rows, the column sums of X' .* M.  Chain: X = X' + sgy qc^T + du kc^T.
+        f4 p3, p2, dg0;
         {
-            const f4 kr0 = KR(0), kr1 = KR(1), kc0 = KC(0), kc1 = KC(1);
+            f4 p3a = zero4(), p3b = zero4(), p2a = zero4(), p2b = zero4();
+            float xa = 0.f, xb = 0.f;
+#pragma unroll
+            for (int jb = 0; jb < 8; jb += 2) {
+                const f4 x0 = ld4(&sm.xt[i0 + lm][16 * jb + 4 * g4]), x1 = ld4(&sm.xt[i0 + lm][16 * jb + 16 + 4 * g4]);
+                const f4 e0 = ld4(&sm.ee[lm][16 * jb + 4 * g4]), e1 = ld4(&sm.ee[lm][16 * jb + 16 + 4 * g4]);
+                const f4 u0 = ld4(&sm.du[lm][16 * jb + 4 * g4]), u1 = ld4(&sm.du[lm][16 * jb + 16 + 4 * g4]);
+#pragma unroll
+                for (int x = 0; x < 4; ++x) {
+                    p3a = mfma(x0[x], btl * e0[x], p3a);
+                    p3b = mfma(x1[x], btl * e1[x], p3b);
+                    p2a = mfma(Mb[jb][x], u0[x], p2a);
+                    p2b = mfma(Mb[jb + 1][x], u1[x], p2b);
+                    xa = fmaf(x0[x], Mb[jb][x], xa);
+                    xb = fmaf(x1[x], Mb[jb + 1][x], xb);
+                }
+            }
+            p3 = p3a + p3b;
+            p2 = p2a + p2b;
+            // dg at the block's first token: the column sums of X .* M with X after the update,
+            // = sum(X' .* M) + sum_t (qc_t P1 + kc_t P2) over the dense parts
+            const f4 xm4 = to_tile(rows4_sum(xa + xb));
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                dg0[r] = xm4[r] + row16_sum(dgacc[r] + sm.kcI[i0 + 4 * g4 + r][lm] * p2[r]);
+            const f4 qc4 = ld4(&sm.qcI[i0 + lm][4 * g4]);
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {   // P3 += QC^T (G1^T masked s >= t)
+                const float g = sm.g1[lm][4 * g4 + x];
+                p3 = mfma(qc4[x], 4 * g4 + x >= lm ? g : 0.f, p3);
+            }
+        }
+        {   // G2 partial over rows 16 w ..: delta^T (row s = l%16) times du (column t = l%16)
+            const f4 e4 = ld4(&sm.ee[lm][j0 + 4 * g4]), u4 = ld4(&sm.du[lm][j0 + 4 * g4]);
+            f4 g2p = zero4();
+#pragma unroll
+            for (int x = 0; x < 4; ++x) g2p = mfma(btl * e4[x], u4[x], g2p);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sm.gp[wv][4 * g4 + r][lm] = g2p[r];
+            st4(&sm.gpt[wv][lm][4 * g4], g2p);
+        }
+#pragma unroll
+        for (int ib = 0; ib < 8; ++ib) {
+            const f4 qa = ld4(&sm.qcI[16 * ib + lm][4 * g4]), ka = ld4(&sm.kcI[16 * ib + lm][4 * g4]);
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                X[ib] = mfma(qa[x], sgB[x], X[ib]);
+                X[ib] = mfma(ka[x], duv[x], X[ib]);
+            }
+        }
+        if (wv == 0 && lane < W) {   // dbeta: the eight row-block partials in order
+            float b = 0.f;
+#pragma unroll
+            for (int w2 = 0; w2 < NW; ++w2) b += sm.pb[w2][lane];
+            if (lane < n) dbout[(int64_t)(tw + lane) * a.H_v] = b;
+        }
+        __syncthreads();   // G2 partials
+        // ---- phase C.  The G2 corrections, outputs, the dg recursion.
+        {
+            f4 g2v = zero4(), g2t = zero4();   // G2[4(l/16) + r][l%16] and G2[l%16][4(l/16) + r]
+#pragma unroll
+            for (int w2 = 0; w2 < NW; ++w2) {
+                g2v += ld4(&sm.gpt[w2][lm][4 * g4]);
+                g2t += ld4(&sm.gp[w2][lm][4 * g4]);
+            }
+            const f4 kr4 = ld4(&sm.krI[i0 + lm][4 * g4]), kc4 = ld4(&sm.kcI[i0 + lm][4 * g4]);
 #pragma unroll
             for (int x = 0; x < 4; ++x) {
                 const int sg = 4 * g4 + x;
-                const float wk3 = sg < lm ? g2[x] : 0.f, wk2 = sg > lm ? g2t[x] : 0.f;
-                p2[0] = mfma(wk3, kr0[x], p2[0]);
-                p2[1] = mfma(wk3, kr1[x], p2[1]);
-                p3[0] = mfma(wk2, kc0[x], p3[0]);
-                p3[1] = mfma(wk2, kc1[x], p3[1]);
+                p3 = mfma(kc4[x], sg > lm ? g2t[x] : 0.f, p3);    // KC^T (G2^T masked s > t)
+                p2 = mfma(kr4[x], sg < lm ? g2v[x] : 0.f, p2);    // KR^T (G2 masked s < t)
             }
         }
-        fence();
-        // X += sgy qc^T + du kc^T
+        // dq = c P1, dk = P3 / c + c P2, dg increments q.*dq - k.*(P3 / c) + k.*(c P2)
+        f4 cv = f4{1.f, 1.f, 1.f, 1.f};
+        if (!dir) {
+            const float *cp = cin + (int64_t)(tw + (lm < n ? lm : 0)) * (a.H_v * G);
 #pragma unroll
-        for (int ib = 0; ib < 2; ++ib) {
-            const f4 qc = QC(ib), kc = KC(ib);
-#pragma unroll
-            for (int jb = 0; jb < 2; ++jb)
-#pragma unroll
-                for (int x = 0; x < 4; ++x) {
-                    const int tt = 4 * g4 + x;
-                    Xt[jb][ib] = mfma(sm.sgy[tt][16 * jb + lm], qc[x], Xt[jb][ib]);
-                    Xt[jb][ib] = mfma(sm.du[tt][16 * jb + lm], kc[x], Xt[jb][ib]);
-                }
+            for (int r = 0; r < 4; ++r) cv[r] = cp[kda ? i0 + 4 * g4 + r : 0];
         }
-        // dg at the block's first token: column sums of X .* Mb (X now the gradient before it)
-        float dg0[2];
-        colsum_xm(Mb, dg0);
-        // dk = P3 / c + c P2; dg increments q.*dq - k.*(G^T delta - Mp^T du)
+        f4 dq4, dk4, inc;
 #pragma unroll
-        for (int ib = 0; ib < 2; ++ib) {
-            const int i = c0 + 16 * ib + lm;
-            const f4 cv = ld4(&cc[16 * ib + lm][4 * g4]), kr = KR(ib), kc = KC(ib);
+        for (int r = 0; r < 4; ++r) {
+            const int i = i0 + 4 * g4 + r;
+            const float c = cv[r], rc = rcp(c);
+            dq4[r] = c * p1[r];
+            dk4[r] = fmaf(rc, p3[r], c * p2[r]);
+            inc[r] = sm.qcI[i][lm] * p1[r] - sm.krI[i][lm] * p3[r] + sm.kcI[i][lm] * p2[r];
+        }
+        // suffix sums of the increments over the block's tokens (lanes l%16 upwards)
+#pragma unroll
+        for (int d = 1; d < W; d <<= 1) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int tt = 4 * g4 + r;
-                const float c = cv[r], rc = rcp(c);
-                const float dk = fmaf(rc, p3[ib][r], c * p2[ib][r]);
-                float g = inc[ib][r] + fmaf(-kr[r], p3[ib][r], kc[r] * p2[ib][r]);
-                if (tt == 0) g = dg0[ib];
-                if (tt < n) {
-                    bst(rpo, dk, (S + i) * 4 + tt * pt, 0);
-                    if (kda) bst(rpo, g, (2 * S + i) * 4 + tt * pt, 0);
+                const float o = __shfl_down(inc[r], d, W);
+                inc[r] += (lm + d < W) ? o : 0.f;
+            }
+        }
+        f4 dgv;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dgv[r] = lm == 0 ? dg0[r] : carry[r] + inc[r];
+        carry = dg0;
+        if (lm < n) {
+            const int64_t o = (int64_t)(tw + lm) * (a.H_v * S) + i0 + 4 * g4;
+            if (vec_out) {
+                st4(dqout + o, dq4);
+                st4(dkout + o, dk4);
+                if (kda) st4(dgout + o, dgv);
+            } else {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    dqout[o + r] = dq4[r];
+                    dkout[o + r] = dk4[r];
+                    if (kda) dgout[o + r] = dgv[r];
                 }
-                gsum[r] += g;
             }
         }
         if (!kda) {   // scalar gate: the wave's column sum per token
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float gs = row16_sum(gsum[r]);
-                const int tt = 4 * g4 + r;
-                if (lm == 0 && tt < n) bst(rpo, gs, (2 * S + wv) * 4 + tt * pt, 0);
-            }
+            const float gsv = rows4_sum(dgv[0] + dgv[1] + dgv[2] + dgv[3]);
+            if (g4 == 0) sm.gs[wv][lm] = gsv;
         }
-        if (dir) scale_cols(Xt, true);   // the gradient before the token's gates
+        if (dir) {   // the gradient before the token's gates
+#pragma unroll
+            for (int ib = 0; ib < 8; ++ib) X[ib] *= ld4(&sm.pv[16 * ib + 4 * g4]);
+        }
         __syncthreads();   // row data and scratch are free for the next staging
+        if (!kda && wv == 0 && lane < n) {
+            float g = 0.f;
+#pragma unroll
+            for (int w2 = 0; w2 < NW; ++w2) g += sm.gs[w2][lane];
+            dgout[(int64_t)(tw + lane) * a.H_v] = g;
+        }
     };
 
-    // a whole block from Mr at its start to its end (token by token if flagged)
-    auto replay_block = [&](f4 (&Mr)[2][2], int t0) {
-        const int cnt = min(W, L - t0);
-        const int64_t bi = (s * nblk + t0 / W) * a.H_v + h;
-        const float *wm = a.wmat + bi * MATF;
-        const bool dir = a.wflag[bi] != 0;
-        const int steps = dir ? cnt : 1;
-        for (int k = 0; k < steps; ++k) {
-            stage(dir ? t0 + k : t0, dir ? 1 : cnt, dir, k, wm);
-            replay(Mr, dir);
-            __syncthreads();
+    // ---- the step sequence
+    const float *snapu = a.snap + unit * a.n_ck_max * S * S;
+    float *bsb = a.vsbuf + unit * (int64_t)a.nbs * (S * S);   // block starts of the segment
+    const int n_ck = (L + C - 1) / C;
+    auto seg_nb = [&](int sg) { return (min(sg * C + C, L) - sg * C + W - 1) / W; };
+    auto n_steps = [&](int sg) { return 2 * seg_nb(sg) - 1 + (sg == n_ck - 1 ? 1 : 0); };
+    // step k of segment sg: 0 replay block bb (saving the next block's start), 1 replay the last
+    // block (final state), 2 walk block bb
+    auto step_info = [&](int sg, int k, int &kind, int &bb) {
+        const int nb = seg_nb(sg), fin = sg == n_ck - 1 ? 1 : 0;
+        if (k < nb - 1) {
+            kind = 0;
+            bb = k;
+        } else if (fin && k == nb - 1) {
+            kind = 1;
+            bb = nb - 1;
+        } else {
+            kind = 2;
+            bb = nb - 1 - (k - (nb - 1) - fin);
         }
     };
-    // walk a whole block with start state M (token by token if flagged: each token's start
-    // replayed from M)
-    auto walk_block = [&](f4 (&M)[2][2], int t0) {
-        const int cnt = min(W, L - t0);
-        const int64_t bi = (s * nblk + t0 / W) * a.H_v + h;
-        const float *wm = a.wmat + bi * MATF;
-        if (a.wflag[bi] == 0) {
-            stage(t0, cnt, false, 0, wm);
-            walk(M, t0, cnt, false);
-            return;
+    auto block_start = [&](int sg, int bb) -> const float * {
+        return bb == 0 ? snapu + (int64_t)sg * S * S : bsb + (int64_t)bb * (S * S);
+    };
+    auto final_sums = [&](const f4 (&Mf)[8]) {   // the dg recursion's start after the last token
+        if (a.dstate_out) carry = to_tile(colsum_mem(a.dstate_out + unit * S * S, Mf));
+    };
+
+    Pre P;
+    f4 M[8];
+    int sg = n_ck - 1, k = 0;
+    if (L > 0) prefetch(P, sg * C);   // the segment's first step handles its block 0
+    while (sg >= 0) {
+        int kind, bb;
+        step_info(sg, k, kind, bb);
+        const int t0 = sg * C + bb * W, cnt = min(W, L - t0);
+        int nsg = sg, nk = k + 1;
+        if (nk == n_steps(sg)) {
+            nsg = sg - 1;
+            nk = 0;
         }
-        for (int k = cnt - 1; k >= 0; --k) {
-            f4 Mr[2][2];
-#pragma unroll
-            for (int jb = 0; jb < 2; ++jb)
-#pragma unroll
-                for (int ib = 0; ib < 2; ++ib) Mr[jb][ib] = M[jb][ib];
-            for (int sx = 0; sx < k; ++sx) {
-                stage(t0 + sx, 1, true, sx, wm);
-                replay(Mr, true);
+        int nt0 = -1;
+        if (nsg >= 0) {
+            int nkind, nbb;
+            step_info(nsg, nk, nkind, nbb);
+            nt0 = nsg * C + nbb * W;
+        }
+        const bool dir = P.dir != 0;
+        if (kind != 2) {
+            // replay: the block as one column-scaled block, or token by token
+            load_cols(block_start(sg, bb), M);   // saved by the previous step when bb > 0
+            const int nsub = dir ? cnt : 1;
+            for (int u = 0; u < nsub; ++u) {
+                if (dir) stage_token(t0, u, false);
+                else stage_replay(P, cnt);
+                if (!dir && nt0 >= 0) prefetch(P, nt0);   // the registers are free again
+                replay(M, dir);
                 __syncthreads();
             }
-            stage(t0 + k, 1, true, k, wm);
-            scale_cols(Mr, true);
-            walk(Mr, t0 + k, 1, true);
-        }
-    };
-
-    const float *snapu = a.snap + unit * a.n_ck_max * S * S + (int64_t)r0 * S;
-    float *vsb = a.vsbuf + ((unit * NQ + qb) * (int64_t)a.nvs_max) * (QR * S);
-    const int nbk = (L + W - 1) / W;
-    for (int b = nbk - 1; b >= 0; --b) {
-        const int t0 = b * W, sg = t0 / C, ts = sg * C, te = min(ts + C, L);
-        const int nvs = (te - ts + VS - 1) / VS;
-        if (nvs > 1 && t0 + W >= te) {   // the segment's last block: its stretch starts first
-            f4 M[2][2];
-            load_state(snapu + (int64_t)sg * S * S, M);
-            for (int t = ts; t < ts + (nvs - 1) * VS; t += W) {
-                replay_block(M, t);
-                if ((t + W - ts) % VS == 0) save_state(vsb + (int64_t)((t + W - ts) / VS) * (QR * S), M);
-            }
-        }
-        const int vi = (t0 - ts) / VS, va = ts + vi * VS;
-        f4 M[2][2];
-        load_state(vi == 0 ? snapu + (int64_t)sg * S * S : vsb + (int64_t)vi * (QR * S), M);
-        if (t0 != va) replay_block(M, va);
-        if (b == nbk - 1) {   // final state: the start of the dg recursion after the last token
-            f4 Mf[2][2];
-#pragma unroll
-            for (int jb = 0; jb < 2; ++jb)
-#pragma unroll
-                for (int ib = 0; ib < 2; ++ib) Mf[jb][ib] = M[jb][ib];
-            replay_block(Mf, t0);
-            float hf[2];
-            colsum_xm(Mf, hf);
-            float *hp = a.hfin + (unit * NQ + qb) * (int64_t)S;
-            if (kda) {
-                if (g4 == 0) {
-                    hp[c0 + lm] = hf[0];
-                    hp[c0 + 16 + lm] = hf[1];
-                }
-            } else {
-                const float hs = row16_sum(hf[0] + hf[1]);
-                if (lane == 0) hp[wv] = hs;
-            }
-        }
-        walk_block(M, t0);
-    }
-    save_state(a.dstate + unit * S * S + (int64_t)r0 * S, Xt);   // the gradient before token 0
-    for (int64_t idx = tid; idx < (int64_t)(a.T - L) * QR; idx += 256) {
-        const int64_t t = L + idx / QR;
-        dvout[t * (a.H_v * S) + idx % QR] = 0.f;
-    }
-}
-
-// ------------------------------------------------------------------ quarter / head sums
-
-// dq, dk: sums over the quarters and the value heads of each key head (increasing order);
-// dbeta: sum of the eight row-block partials; dg: per block, from its last token down, the
-// next block's first-token value (after the sequence's last token: the final column sums)
-// plus the quarters' increments, and at the block's first token the quarters' direct
-// values.  A block processed token by token has every token as a first token.  The scalar
-// gate sums the columns (the backward left per-wave sums in the first four slots).
-template <int V>
-__global__ void __launch_bounds__(256) combine_mf_kernel(const Mf128Args a) {
-    const int64_t T = a.T, n = a.n_seqs_launch, Hk = a.H_k, Hv = a.H_v;
-    const bool kda = a.kda != 0;
-    const int64_t G = kda ? S : 1;
-    const int64_t VG = kda ? V : 1;
-    const int64_t nblk = (T + W - 1) / W;
-    const int64_t n_qk = n * T * Hk * (S / V);
-    const int64_t n_g = n * nblk * Hv * (G / VG);
-    const int64_t n_b = n * T * Hv;
-    const int64_t total = n_qk + n_g + n_b;
-    const int64_t seq0 = a.s_base;
-    auto ldv = [](const float *p, float (&x)[V]) {
-        if constexpr (V == 4) {
-            const f4 t = ld4(p);
-            x[0] = t[0]; x[1] = t[1]; x[2] = t[2]; x[3] = t[3];
+            if (kind == 0) save_cols(bsb + (int64_t)(bb + 1) * (S * S), M);
+            else final_sums(M);
         } else {
-            x[0] = *p;
-        }
-    };
-    auto stv = [](float *p, const float (&x)[V]) {
-        if constexpr (V == 4) st4(p, f4{x[0], x[1], x[2], x[3]});
-        else *p = x[0];
-    };
-    for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
-         idx += (int64_t)gridDim.x * blockDim.x) {
-        if (idx < n_qk) {
-            const int i = (int)(idx % (S / V)) * V;
-            int64_t rest = idx / (S / V);
-            const int kh = (int)(rest % Hk);
-            rest /= Hk;
-            const int t = (int)(rest % T);
-            const int sl = (int)(rest / T);
-            float q[V], k[V];
-#pragma unroll
-            for (int c = 0; c < V; ++c) q[c] = k[c] = 0.f;
-            if (t < a.lens[sl]) {
-                for (int h = kh; h < Hv; h += (int)Hk) {
-                    const float *pp = a.part + ((((seq0 + sl) * T + t) * Hv + h) * NQ) * (3 * S) + i;
-#pragma unroll
-                    for (int qb = 0; qb < NQ; ++qb) {
-                        float x[V], y[V];
-                        ldv(pp + (qb * 3 + 0) * S, x);
-                        ldv(pp + (qb * 3 + 1) * S, y);
-#pragma unroll
-                        for (int c = 0; c < V; ++c) q[c] += x[c], k[c] += y[c];
+            // walk: the block as one column-scaled block, or its tokens from the last, each from
+            // its own start state replayed from the block start
+            const int nsub = dir ? cnt : 1;
+            for (int u = 0; u < nsub; ++u) {
+                const int tau = cnt - 1 - u;
+                load_cols(block_start(sg, bb), M);
+                if (dir) {
+                    for (int sx = 0; sx < tau; ++sx) {
+                        stage_token(t0, sx, false);
+                        replay(M, true);
+                        __syncthreads();
                     }
-                }
-            }
-            const int64_t o = (((seq0 + sl) * T + t) * Hk + kh) * S + i;
-            stv(a.dq + o, q);
-            stv(a.dk + o, k);
-        } else if (idx < n_qk + n_g) {
-            const int64_t j = idx - n_qk;
-            const int i = (int)(j % (G / VG)) * (int)VG;
-            int64_t rest = j / (G / VG);
-            const int h = (int)(rest % Hv);
-            rest /= Hv;
-            const int m = (int)(rest % nblk);
-            const int sl = (int)(rest / nblk);
-            const int t0 = m * W, L = a.lens[sl];
-            const int cnt = max(0, min(W, L - t0));
-            const bool dir = cnt > 0 && a.wflag[(((seq0 + sl) * nblk + m) * Hv + h)] != 0;
-            auto part_sum = [&](int t, float (&g)[V]) {
-                const int64_t rt = (((seq0 + sl) * T + t) * Hv + h) * NQ;
+                    stage_token(t0, tau, true);
+                    const float p = sm.pv[i0 + lm];
 #pragma unroll
-                for (int c = 0; c < V; ++c) g[c] = 0.f;
-#pragma unroll
-                for (int qb = 0; qb < NQ; ++qb) {
-                    const float *pp = a.part + (rt + qb) * (3 * S) + 2 * S;
-                    if (kda) {
-                        float x[V];
-                        ldv(pp + i, x);
-#pragma unroll
-                        for (int c = 0; c < V; ++c) g[c] += x[c];
-                    } else {
-#pragma unroll
-                        for (int w2 = 0; w2 < 4; ++w2) g[0] += pp[w2];
-                    }
-                }
-            };
-            float carry[V];
-#pragma unroll
-            for (int c = 0; c < V; ++c) carry[c] = 0.f;
-            if (cnt > 0) {
-                if (t0 + W < L) {
-                    part_sum(t0 + W, carry);
+                    for (int jb = 0; jb < 8; ++jb) M[jb] *= p;
                 } else {
-                    const float *hf = a.hfin + ((seq0 + sl) * Hv + h) * NQ * S;
-#pragma unroll
-                    for (int qb = 0; qb < NQ; ++qb) {
-                        if (kda) {
-                            float x[V];
-                            ldv(hf + qb * S + i, x);
-#pragma unroll
-                            for (int c = 0; c < V; ++c) carry[c] += x[c];
-                        } else {
-#pragma unroll
-                            for (int w2 = 0; w2 < 4; ++w2) carry[0] += hf[qb * S + w2];
-                        }
-                    }
+                    stage_walk(P, cnt);
+                    if (nt0 >= 0) prefetch(P, nt0);   // the registers are free again
                 }
+                walk(M, dir ? t0 + tau : t0, dir ? 1 : cnt, dir);
             }
-            for (int tt = W - 1; tt >= 0; --tt) {
-                const int t = t0 + tt;
-                if (t >= T) continue;
-                float g[V];
-#pragma unroll
-                for (int c = 0; c < V; ++c) g[c] = 0.f;
-                if (tt < cnt) {
-                    float p[V];
-                    part_sum(t, p);
-#pragma unroll
-                    for (int c = 0; c < V; ++c) {
-                        if (tt == 0 || dir) {
-                            g[c] = p[c];
-                            carry[c] = p[c];
-                        } else {
-                            carry[c] += p[c];
-                            g[c] = carry[c];
-                        }
-                    }
-                }
-                float *dst = a.dg + (((seq0 + sl) * T + t) * Hv + h) * G + i;
-                if (kda) stv(dst, g);
-                else dst[0] = g[0];
-            }
-        } else {
-            const int64_t j = idx - n_qk - n_g;
-            const int h = (int)(j % Hv);
-            const int64_t rest = j / Hv;
-            const int t = (int)(rest % T);
-            const int sl = (int)(rest / T);
-            float b = 0.f;
-            if (t < a.lens[sl]) {
-                const float *pp = a.pbuf + (((seq0 + sl) * T + t) * Hv + h) * (2 * NQ);
-#pragma unroll
-                for (int x = 0; x < 2 * NQ; ++x) b += pp[x];
-            }
-            a.dbeta[((seq0 + sl) * T + t) * Hv + h] = b;
         }
+        if (dir && nt0 >= 0) prefetch(P, nt0);
+        sg = nsg;
+        k = nk;
+    }
+    {   // the gradient before token 0
+        float *p = a.dstate + unit * S * S + (int64_t)(j0 + lm) * S + 4 * g4;
+#pragma unroll
+        for (int ib = 0; ib < 8; ++ib)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) p[16 * ib + r] = X[ib][r];
+    }
+    for (int64_t idx = tid; idx < (int64_t)(a.T - L) * S; idx += NT) {   // padded tokens
+        const int64_t row = (int64_t)(L + idx / S) * a.H_v;
+        const int i = (int)(idx % S);
+        dvout[row * S + i] = 0.f;
+        dqout[row * S + i] = 0.f;
+        dkout[row * S + i] = 0.f;
+        if (kda) dgout[row * S + i] = 0.f;
+        else if (i == 0) dgout[row] = 0.f;
+        if (i == 0) dbout[row] = 0.f;
     }
 }
 
@@ -1142,39 +1136,33 @@ struct FwdK {
     static constexpr auto fn = fwd_mf_kernel<DT>;
 };
 template <int DT>
+struct Gram1K {
+    static constexpr auto fn = gram1_kernel<DT>;
+};
+template <int DT>
 struct BwdK {
     static constexpr auto fn = bwd_mf_kernel<DT>;
 };
 
+int block_items(const Mf128Args &a) {
+    const int64_t items = (int64_t)a.n_seqs_launch * ((a.T + W - 1) / W) * a.H_v;
+    return (int)std::min<int64_t>(items, 16384);
+}
+
 }  // namespace
 
-int mf128_stretch_tokens() { return VS; }
-
 hipError_t launch_prep128(const Mf128Args &a, hipStream_t st) {
-    const int64_t items = (int64_t)a.n_seqs_launch * ((a.T + W - 1) / W) * a.H_v;
-    if (items <= 0) return hipSuccess;
-    const int blocks = (int)std::min<int64_t>(items, 16384);
-    return launch(pick<PrepK>(a.dtype), a, blocks, 64, st);
+    return launch(pick<PrepK>(a.dtype), a, block_items(a), 64, st);
 }
 
 hipError_t launch_fwd_mf(const Mf128Args &a, hipStream_t st) {
-    return launch(pick<FwdK>(a.dtype), a, a.n_seqs_launch * a.H_v * NQ, 128, st);
+    return launch(pick<FwdK>(a.dtype), a, a.n_seqs_launch * a.H_v, NT, st);
 }
 
 hipError_t launch_bwd_mf(const Mf128Args &a, hipStream_t st) {
-    return launch(pick<BwdK>(a.dtype), a, a.n_seqs_launch * a.H_v * NQ, 256, st);
-}
-
-hipError_t launch_combine_mf(const Mf128Args &a, hipStream_t st) {
-    auto a16 = [](const void *p) { return p == nullptr || ((uintptr_t)p & 15) == 0; };
-    const bool vec = a16(a.part) && a16(a.hfin) && a16(a.dq) && a16(a.dk) && a16(a.dg);
-    const int64_t V = vec ? 4 : 1, VG = a.kda ? V : 1, G = a.kda ? S : 1;
-    const int64_t total = (int64_t)a.n_seqs_launch *
-                          (a.T * (a.H_k * (S / V) + a.H_v) + (int64_t)((a.T + W - 1) / W) * a.H_v * (G / VG));
-    if (total <= 0) return hipSuccess;
-    const int blocks = (int)std::min<int64_t>((total + 255) / 256, 16384);
-    return vec ? launch((const void *)combine_mf_kernel<4>, a, blocks, 256, st)
-               : launch((const void *)combine_mf_kernel<1>, a, blocks, 256, st);
+    hipError_t e = launch(pick<Gram1K>(a.dtype), a, block_items(a), 64, st);
+    if (e != hipSuccess) return e;
+    return launch(pick<BwdK>(a.dtype), a, a.n_seqs_launch * a.H_v, NT, st);
 }
 
 }  // namespace gdn

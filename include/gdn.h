@@ -103,8 +103,8 @@ typedef struct gdn_strides {
  *               GDN_GATE_KDA (g is [.., H_v, S_k])
  *   C           checkpoint interval in tokens; 0 selects ceil(sqrt(T)); values above T
  *               act as T (one segment).  For S = 128 the interval is rounded up to a
- *               multiple of 8 (the kernels carry the state column-scaled over 8-token
- *               windows that checkpoints must not split); results are then bitwise the
+ *               multiple of 16 (the kernels carry the state column-scaled over 16-token
+ *               blocks that checkpoints must not split); results are then bitwise the
  *               same for every interval
  *   scale       output scale (commonly 1/sqrt(S_k))
  *   seq_lens    HOST pointer to n_seqs lengths in [0, T], or NULL for all T

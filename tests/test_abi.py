@@ -51,18 +51,20 @@ def expected_ws(n, T, Hk, Hv, S, C, kda=True):
         C = -(-C // 16) * 16
     n_ck = max(1, -(-T // C))
     tot = al(units * n_ck * S * S * 4)
-    if S == 128:                    # matrix-core path, row quarters
+    if S == 128:                    # matrix-core path, one workgroup per (sequence, head)
         rows = n * T * Hv
         nblk = -(-T // 16)
-        nvs = max(1, -(-C // 32))
+        nbs = C // 16
         tot = al(tot + n * nblk * Hv * 3 * 256 * 4)         # block matrices Bm, Te, Tb
         tot = al(tot + n * nblk * Hv * 4)                   # block flags
+        tot = al(tot + rows * (S if kda else 1) * 4)        # running gate products
         tot = al(tot + rows * S * 4)                        # prediction errors
-        if nvs > 1:
-            tot = al(tot + units * 4 * nvs * 32 * S * 4)    # stretch starts
-        tot = al(tot + rows * 4 * 3 * S * 4)                # column partials dq | dk | dg
-        tot = al(tot + rows * 8 * 4)                        # dbeta partials
-        tot = al(tot + units * 4 * S * 4)                   # final-state dg column sums
+        tot = al(tot + n * nblk * Hv * 256 * 4)             # Grams G1
+        if nbs > 1:
+            tot = al(tot + units * nbs * S * S * 4)         # block starts of a segment
+        if Hv != Hk:
+            tot = al(tot + rows * S * 4)                    # dq per value head
+            tot = al(tot + rows * S * 4)                    # dk per value head
         return tot
     tot = al(tot + units * C * S * S * 4)
     tot = al(tot + units * C * S * 4)
