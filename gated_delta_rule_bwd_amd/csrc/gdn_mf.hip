@@ -67,6 +67,11 @@ template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
     return as_f(__builtin_amdgcn_mov_dpp(as_i(v), CTRL, 0xF, 0xF, true));
 }
+// the value of lane l - D in the same 16-lane row, 1 for the first D lanes of the row
+template <int D>
+__device__ __forceinline__ float row_shr(float v) {
+    return as_f(__builtin_amdgcn_update_dpp(as_i(1.f), as_i(v), 0x110 + D, 0xF, 0xF, false));
+}
 // sum over the 16 lanes of a DPP row (every lane receives it)
 __device__ __forceinline__ float row16_sum(float v) {
     v += dpp<0xB1>(v);
@@ -121,6 +126,24 @@ __device__ __forceinline__ float bldf(Rsrc r, uint32_t vbytes, uint32_t sbytes) 
 __device__ __forceinline__ void bst(Rsrc r, float v, uint32_t vbytes, uint32_t sbytes) {
     __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, vbytes, sbytes, 0);
 }
+// four consecutive elements (16 bytes of fp32 or 8 of a half type, aligned to that size)
+template <int DT>
+__device__ __forceinline__ f4 bld4(Rsrc r, uint32_t vbytes) {
+    if constexpr (DT == GDN_DTYPE_F32) {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, vbytes, 0, 0);
+        return f4{as_f((int)v[0]), as_f((int)v[1]), as_f((int)v[2]), as_f((int)v[3])};
+    } else {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, vbytes, 0, 0);
+        f4 o;
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+            const unsigned short hb = (unsigned short)((x & 1) ? (v[x >> 1] >> 16) : (v[x >> 1] & 0xffffu));
+            if constexpr (DT == GDN_DTYPE_BF16) o[x] = __builtin_bit_cast(float, (uint32_t)hb << 16);
+            else o[x] = (float)__builtin_bit_cast(_Float16, hb);
+        }
+        return o;
+    }
+}
 template <int DT>
 __device__ __forceinline__ const In<DT> *tin(const void *p) {
     return reinterpret_cast<const In<DT> *>(p);
@@ -133,23 +156,67 @@ __device__ __forceinline__ const In<DT> *tin(const void *p) {
 // hold the gates a themselves), and the block matrices Bm (upper triangle of B with its
 // diagonal), Te = (I + diag(beta) A)^-1 and Tb = (I + A diag(beta))^-1, A the strict upper
 // triangle of the Gram A; a token-by-token block gets Bm = diag(k_t . q_t) and Te = Tb = I.
-// One wave per block (lane: columns lane and lane + 64 over the block's tokens).
-struct alignas(16) PrepLds {
-    float kr[W][SP], kc[W][SP], qc[W][SP];
-    float am[W][W + 1];
-    float bt[W];
-};
+//
+// One wave per block: lane l takes token l%16 and the columns 16 kb + 4(l/16) + x (kb < 8,
+// x < 4).  c is a product scan over the 16 lanes of a row (the tokens of the block); the Grams
+// are dense products of the lanes' own values (lane l supplies row l%16 of the left operand and
+// column l%16 of the right one); the inverses of the unit triangular matrices use the
+// nilpotent product form (I + N)^-1 = (I - N)(I + N^2)(I + N^4)(I + N^8), N^16 = 0.
+constexpr int PW = 4;   // waves (blocks) per workgroup of the preparation
+
+// Z = X Y for 16 x 16 matrices held in the D layout, given X^T and Y
+__device__ __forceinline__ f4 mm16(const f4 &xt, const f4 &y) {
+    f4 z = zero4();
+#pragma unroll
+    for (int x = 0; x < 4; ++x) z = mfma(xt[x], y[x], z);
+    return z;
+}
 
 template <int DT>
-__global__ void __launch_bounds__(64) prep128_kernel(const Mf128Args a) {
-    __shared__ PrepLds sm;
+__global__ void __launch_bounds__(64 * PW) prep128_kernel(const Mf128Args a) {
+    __shared__ float trs[PW][W][W + 1];   // per-wave transposes
     constexpr uint32_t ES = sizeof(In<DT>);
-    const int lane = threadIdx.x, lm = lane & 15, g4 = lane >> 4;
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, lm = lane & 15, g4 = lane >> 4;
+    float (*tr)[W + 1] = trs[wv];
     const int nblk = (a.T + W - 1) / W;
     const int G = a.kda ? S : 1;
+    const bool kda = a.kda != 0;
     const int64_t items = (int64_t)a.n_seqs_launch * nblk * a.H_v;
-    const uint32_t gt = (uint32_t)a.sg.tok * ES, kt = (uint32_t)a.sk.tok * ES, qt = (uint32_t)a.sq.tok * ES;
-    for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
+    // rows whose starts are all aligned to four elements take vector loads
+    auto aligned_rows = [&](const void *p, const gdn_strides &st) {
+        return (((uintptr_t)p & (4 * ES - 1)) == 0) && st.seq % 4 == 0 && st.tok % 4 == 0 && st.head % 4 == 0;
+    };
+    const bool vec_g = aligned_rows(a.g, a.sg), vec_k = aligned_rows(a.k, a.sk), vec_q = aligned_rows(a.q, a.sq);
+    // the transpose of a D-layout matrix, in the D layout: every lane's writes reach the LDS
+    // before any lane reads (the wave barrier keeps the compiler from interleaving them; one
+    // wave's LDS accesses complete in order)
+    auto transpose = [&](const f4 &z) {
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int r = 0; r < 4; ++r) tr[4 * g4 + r][lm] = z[r];
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        f4 o;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) o[r] = tr[lm][4 * g4 + r];
+        __builtin_amdgcn_wave_barrier();
+        return o;
+    };
+    f4 eye;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) eye[r] = 4 * g4 + r == lm ? 1.f : 0.f;
+    // (I + N)^-1 for a strictly upper triangular N (D layout) and its transpose NT
+    auto inverse = [&](const f4 &N, const f4 &NT) {
+        const f4 n2 = mm16(NT, N), n2t = mm16(N, NT);
+        const f4 n4 = mm16(n2t, n2), n4t = mm16(n2, n2t);
+        const f4 n8 = mm16(n4t, n4);
+        const f4 r1 = (eye - N) + mm16(eye - NT, n2), r1t = (eye - NT) + mm16(n2, eye - NT);
+        const f4 r2 = r1 + mm16(r1t, n4), r2t = r1t + mm16(n4, r1t);
+        return r2 + mm16(r2t, n8);
+    };
+
+    for (int64_t it = (int64_t)blockIdx.x * PW + wv; it < items; it += (int64_t)gridDim.x * PW) {
         const int h = (int)(it % a.H_v);
         const int64_t rest = it / a.H_v;
         const int b = (int)(rest % nblk), sl = (int)(rest / nblk);
@@ -157,111 +224,113 @@ __global__ void __launch_bounds__(64) prep128_kernel(const Mf128Args a) {
         if (cnt <= 0) continue;
         const int64_t s = a.s_base + sl;
         const int hk = h % a.H_k;
+        const bool ok = lm < cnt;
+        const uint32_t tok = ok ? (uint32_t)lm : 0u;
         const Rsrc rg = rsrc(tin<DT>(a.g) + s * a.sg.seq + (int64_t)t0 * a.sg.tok + h * a.sg.head);
         const Rsrc rk = rsrc(tin<DT>(a.k) + s * a.sk.seq + (int64_t)t0 * a.sk.tok + hk * a.sk.head);
         const Rsrc rq = rsrc(tin<DT>(a.q) + s * a.sq.seq + (int64_t)t0 * a.sq.tok + hk * a.sq.head);
-        float c[2][W], kv[2][W], qv[2][W];
-        bool ok = true;
+        const Rsrc rb = rsrc(tin<DT>(a.beta) + s * a.sb.seq + (int64_t)t0 * a.sb.tok + h * a.sb.head);
+        const uint32_t gto = tok * (uint32_t)a.sg.tok * ES, kto = tok * (uint32_t)a.sk.tok * ES,
+                       qto = tok * (uint32_t)a.sq.tok * ES;
+        // the gates of token l%16 (column 16 (n / 4) + 4(l/16) + n % 4), and their running products
+        // over the block's tokens
+        auto column = [&](int n) { return (uint32_t)(16 * (n >> 2) + 4 * g4 + (n & 3)); };
+        // four consecutive columns 16 kb + 4(l/16) .. of a row (vector loads when aligned)
+        auto row4 = [&](Rsrc r, uint32_t rowb, bool vec, int kb) {
+            const uint32_t o = rowb + (uint32_t)(16 * kb + 4 * g4) * ES;
+            if (vec) return bld4<DT>(r, o);
+            return f4{bld<DT>(r, o, 0), bld<DT>(r, o + ES, 0), bld<DT>(r, o + 2 * ES, 0), bld<DT>(r, o + 3 * ES, 0)};
+        };
+        auto gate = [&](int n) { return ok ? expf(bld<DT>(rg, gto + (kda ? column(n) : 0u) * ES, 0)) : 1.f; };
+        float c[32];
+        if (kda) {
 #pragma unroll
-        for (int n = 0; n < 2; ++n) {
-            const uint32_t i = lane + 64 * n;
-            float run = 1.f;
+            for (int kb = 0; kb < 8; ++kb) {
+                const f4 gv = ok ? row4(rg, gto, vec_g, kb) : zero4();
 #pragma unroll
-            for (int tt = 0; tt < W; ++tt) {
-                float av = 1.f, kx = 0.f, qx = 0.f;
-                if (tt < cnt) {
-                    av = expf(bld<DT>(rg, (a.kda ? i : 0u) * ES, tt * gt));
-                    kx = bld<DT>(rk, i * ES, tt * kt);
-                    qx = bld<DT>(rq, i * ES, tt * qt);
-                }
-                run = tt == 0 ? av : run * av;
-                c[n][tt] = run;
-                kv[n][tt] = kx;
-                qv[n][tt] = qx;
-                ok = ok && run >= kLo && run <= kHi;
+                for (int x = 0; x < 4; ++x) c[4 * kb + x] = ok ? expf(gv[x]) : 1.f;
+            }
+        } else {
+            c[0] = gate(0);
+        }
+        const int nsc = kda ? 32 : 1;   // distinct columns of the scan
+#pragma unroll
+        for (int n = 0; n < 32; ++n) {   // lane l%16 takes the products with lanes l%16 - 1, - 2, - 4, - 8
+            if (n < nsc) {
+                c[n] *= row_shr<1>(c[n]);
+                c[n] *= row_shr<2>(c[n]);
+                c[n] *= row_shr<4>(c[n]);
+                c[n] *= row_shr<8>(c[n]);
             }
         }
-        const bool direct = __ballot(!ok) != 0;
+        if (!kda) {
+#pragma unroll
+            for (int n = 1; n < 32; ++n) c[n] = c[0];
+        }
+        bool bad = false;
+#pragma unroll
+        for (int n = 0; n < 32; ++n) bad = bad || (ok && !(c[n] >= kLo && c[n] <= kHi));
+        const bool direct = __ballot(bad) != 0;
         {   // the running products (a token-by-token block: the gates) for the forward and backward
-            float *cb = a.cbuf + ((s * a.T + t0) * a.H_v + h) * (int64_t)G;
-            const int64_t ct = (int64_t)a.H_v * G;
+            float *cb = a.cbuf + ((s * a.T + t0 + tok) * a.H_v + h) * (int64_t)G;
+            if (ok) {
+                if (kda) {
 #pragma unroll
-            for (int n = 0; n < 2; ++n) {
-                const uint32_t i = lane + 64 * n;
-                if ((int)i < G) {
-#pragma unroll
-                    for (int tt = 0; tt < W; ++tt) {
-                        if (tt < cnt)
-                            cb[tt * ct + i] = direct ? expf(bld<DT>(rg, (a.kda ? i : 0u) * ES, tt * gt)) : c[n][tt];
+                    for (int kb = 0; kb < 8; ++kb) {
+                        const int n = 4 * kb;
+                        st4(cb + 16 * kb + 4 * g4, direct ? f4{gate(n), gate(n + 1), gate(n + 2), gate(n + 3)}
+                                                          : f4{c[n], c[n + 1], c[n + 2], c[n + 3]});
                     }
+                } else if (g4 == 0) {
+                    cb[0] = direct ? gate(0) : c[0];
                 }
             }
         }
-#pragma unroll
-        for (int n = 0; n < 2; ++n) {
-            const int i = lane + 64 * n;
-#pragma unroll
-            for (int tt = 0; tt < W; ++tt) {
-                const float cv = direct ? 1.f : c[n][tt];
-                sm.kr[tt][i] = kv[n][tt] * rcp(cv);
-                sm.kc[tt][i] = kv[n][tt] * cv;
-                sm.qc[tt][i] = qv[n][tt] * cv;
-            }
-        }
-        if (lane < W) {
-            const Rsrc rb = rsrc(tin<DT>(a.beta) + s * a.sb.seq + (int64_t)t0 * a.sb.tok + h * a.sb.head);
-            sm.bt[lane] = lane < cnt ? bld<DT>(rb, 0, lane * (uint32_t)a.sb.tok * ES) : 0.f;
-        }
-        __syncthreads();
-        // Grams G[s][t] = kr_s . kc_t and kr_s . qc_t (D layout: s = 4 g4 + r, t = lm)
+        // Grams GA[s][t] = kr_s . kc_t and GB[s][t] = kr_s . qc_t (D layout: s = 4(l/16) + r, t = l%16)
         f4 ga0 = zero4(), ga1 = zero4(), gb0 = zero4(), gb1 = zero4();
 #pragma unroll
-        for (int kb = 0; kb < S / 16; kb += 2) {
-            const f4 ar0 = ld4(&sm.kr[lm][16 * kb + 4 * g4]), ar1 = ld4(&sm.kr[lm][16 * kb + 16 + 4 * g4]);
-            const f4 bc0 = ld4(&sm.kc[lm][16 * kb + 4 * g4]), bc1 = ld4(&sm.kc[lm][16 * kb + 16 + 4 * g4]);
-            const f4 bq0 = ld4(&sm.qc[lm][16 * kb + 4 * g4]), bq1 = ld4(&sm.qc[lm][16 * kb + 16 + 4 * g4]);
+        for (int kb = 0; kb < 8; ++kb) {
+            const f4 k4 = ok ? row4(rk, kto, vec_k, kb) : zero4(), q4 = ok ? row4(rq, qto, vec_q, kb) : zero4();
 #pragma unroll
             for (int x = 0; x < 4; ++x) {
-                ga0 = mfma(ar0[x], bc0[x], ga0);
-                gb0 = mfma(ar0[x], bq0[x], gb0);
-                ga1 = mfma(ar1[x], bc1[x], ga1);
-                gb1 = mfma(ar1[x], bq1[x], gb1);
+                const float cv = direct ? 1.f : c[4 * kb + x];
+                const float kr = k4[x] * rcp(cv), kc = k4[x] * cv, qc = q4[x] * cv;
+                if (kb & 1) {
+                    ga1 = mfma(kr, kc, ga1);
+                    gb1 = mfma(kr, qc, gb1);
+                } else {
+                    ga0 = mfma(kr, kc, ga0);
+                    gb0 = mfma(kr, qc, gb0);
+                }
             }
         }
         const f4 gA = ga0 + ga1, gB = gb0 + gb1;
+        float bs[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int tt = 4 * g4 + r;
+            bs[r] = tt < cnt ? bld<DT>(rb, tt * (uint32_t)a.sb.tok * ES, 0) : 0.f;
+        }
+        const float bl = ok ? bld<DT>(rb, lm * (uint32_t)a.sb.tok * ES, 0) : 0.f;
+        f4 bm, ne, nb;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int sg = 4 * g4 + r;
+            const float as = (!direct && sg < lm) ? gA[r] : 0.f;
+            bm[r] = direct ? (sg == lm ? gB[r] : 0.f) : (sg <= lm ? gB[r] : 0.f);
+            ne[r] = bs[r] * as;   // diag(beta) A
+            nb[r] = as * bl;      // A diag(beta)
+        }
+        const f4 te = inverse(ne, transpose(ne)), tb = inverse(nb, transpose(nb));
         float *wm = a.wmat + ((s * nblk + b) * a.H_v + h) * (int64_t)MATF;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int sg = 4 * g4 + r, tt = lm;
-            sm.am[sg][tt] = (!direct && sg < tt) ? gA[r] : 0.f;
-            wm[sg * W + tt] = direct ? (sg == tt ? gB[r] : 0.f) : (sg <= tt ? gB[r] : 0.f);
-        }
-        __syncthreads();
-        // rows of the unit upper triangular inverses (lane sg < 16: Te, 16 + sg: Tb), column by
-        // column: once entry rho of the row is final it is pushed into the later entries
-        if (lane < 2 * W) {
-            const int sg = lane & 15;
-            const bool tb = lane >= W;
-            float v[W];
-#pragma unroll
-            for (int tt = 0; tt < W; ++tt) v[tt] = tt == sg ? 1.f : 0.f;
-#pragma unroll
-            for (int rho = 0; rho < W - 1; ++rho) {
-                if (rho >= sg) {
-                    const float vr = v[rho];
-#pragma unroll
-                    for (int tt = rho + 1; tt < W; ++tt) {
-                        const float l = tb ? sm.am[rho][tt] * sm.bt[tt] : sm.bt[rho] * sm.am[rho][tt];
-                        v[tt] = fmaf(-vr, l, v[tt]);
-                    }
-                }
-            }
-            float *dst = wm + (tb ? 2 : 1) * W * W + sg * W;
-#pragma unroll
-            for (int tt = 0; tt < W; ++tt) dst[tt] = direct ? (tt == sg ? 1.f : 0.f) : v[tt];
+            const int o = (4 * g4 + r) * W + lm;
+            wm[o] = bm[r];
+            wm[W * W + o] = direct ? eye[r] : te[r];
+            wm[2 * W * W + o] = direct ? eye[r] : tb[r];
         }
         if (lane == 0) a.wflag[(s * nblk + b) * a.H_v + h] = direct ? 1 : 0;
-        __syncthreads();
     }
 }
 
@@ -502,6 +571,8 @@ __global__ void __launch_bounds__(64) gram1_kernel(const Mf128Args a) {
     const int nblk = (a.T + W - 1) / W;
     const int64_t items = (int64_t)a.n_seqs_launch * nblk * a.H_v;
     const uint32_t gyt = (uint32_t)a.sgy.tok * ES;
+    const bool vec_gy = (((uintptr_t)a.gy & (4 * ES - 1)) == 0) && a.sgy.seq % 4 == 0 && a.sgy.tok % 4 == 0 &&
+                        a.sgy.head % 4 == 0;
     for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
         const int h = (int)(it % a.H_v);
         const int64_t rest = it / a.H_v;
@@ -520,9 +591,14 @@ __global__ void __launch_bounds__(64) gram1_kernel(const Mf128Args a) {
         for (int kb = 0; kb < S / 16; ++kb) {
             const int j = 16 * kb + 4 * g4;
             const f4 e4 = ok ? ld4(er + j) : zero4();
-            f4 y4;
-#pragma unroll
-            for (int x = 0; x < 4; ++x) y4[x] = ok ? a.scale * bld<DT>(rgy, (j + x) * ES + lm * gyt, 0) : 0.f;
+            f4 y4 = zero4();
+            if (ok) {
+                const uint32_t o = j * ES + lm * gyt;
+                y4 = vec_gy ? bld4<DT>(rgy, o)
+                            : f4{bld<DT>(rgy, o, 0), bld<DT>(rgy, o + ES, 0), bld<DT>(rgy, o + 2 * ES, 0),
+                                 bld<DT>(rgy, o + 3 * ES, 0)};
+                y4 *= a.scale;
+            }
 #pragma unroll
             for (int x = 0; x < 4; ++x) {
                 if (kb % 2 == 0) g0 = mfma(bl * e4[x], y4[x], g0);
@@ -559,14 +635,14 @@ struct alignas(16) BwdLds {
     float qcI[S][KP];          // c.*q        [column][token]
     float kcI[S][KP];          // c.*k        [column][token]
     float sgy[W][SP];          // scale gy    [token][row]
-    float ee[W][SP];           // e           [token][row]
-    float du[W][SP];           // du          [token][row]
+    float ee[W][SP];           // delta = beta e  [token][row]
+    float du[W][SP];           // e, then du  [token][row]
     float xt[S][SP];           // X after the fold [column][row]; in a replay: delta [row][token]
     float pv[S];               // fold factor per column (a token's gates)
     float bt[W];               // beta
     float bm[W][W], tb[W][W];  // Bm, Tb
-    float g1[W][GP];           // G1 = delta^T scale gy
-    float gp[NW][W][GP];       // per-wave partials of G2 = delta^T du, [s][t]
+    float g1[W][GP];           // G1 = delta^T scale gy, upper triangle with the diagonal
+    float gp[NW][W][GP];       // per-wave partials of G2 = delta^T du, strict upper triangle, [s][t]
     float gpt[NW][W][GP];      // the same, [t][s]
     float pb[NW][W];           // per-wave partials of dbeta
     float gs[NW][W];           // per-wave partial sums of the scalar gate's dg
@@ -617,14 +693,14 @@ __global__ void __launch_bounds__(NT) bwd_mf_kernel(const Mf128Args a) {
 #pragma unroll
         for (int jb = 0; jb < 8; ++jb)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) Mc[jb][r] = bldf(rs, vcol, (16 * jb + r) * S * 4);
+            for (int r = 0; r < 4; ++r) Mc[jb][r] = bldf(rs, vcol + r * S * 4, 16 * jb * S * 4);
     };
     auto save_cols = [&](float *base, const f4 (&Mc)[8]) {
         const Rsrc rs = rsrc(base);
 #pragma unroll
         for (int jb = 0; jb < 8; ++jb)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) bst(rs, Mc[jb][r], vcol, (16 * jb + r) * S * 4);
+            for (int r = 0; r < 4; ++r) bst(rs, Mc[jb][r], vcol + r * S * 4, 16 * jb * S * 4);
     };
 
     // the gradient in the row layout
@@ -683,7 +759,8 @@ __global__ void __launch_bounds__(NT) bwd_mf_kernel(const Mf128Args a) {
             kc[x] = P.k[x] * c;
             sm.krT[tt][ci] = kr[x];
             sm.sgy[tt][ci] = scale * P.gy[x];
-            sm.ee[tt][ci] = P.e[x];
+            sm.ee[tt][ci] = P.b[x] * P.e[x];   // delta
+            sm.du[tt][ci] = P.e[x];            // e, until the walk replaces it by du
             if (tt == cnt - 1) sm.pv[ci] = c;
             if (ci == 0) sm.bt[tt] = P.b[x];
         }
@@ -693,7 +770,7 @@ __global__ void __launch_bounds__(NT) bwd_mf_kernel(const Mf128Args a) {
         if (tid < 256) {
             (&sm.bm[0][0])[tid] = P.m0;
             (&sm.tb[0][0])[tid] = P.m1;
-            sm.g1[tid >> 4][tid & 15] = P.m2;
+            sm.g1[tid >> 4][tid & 15] = (tid >> 4) <= (tid & 15) ? P.m2 : 0.f;   // s <= t
         }
         __syncthreads();
     };
@@ -737,7 +814,8 @@ __global__ void __launch_bounds__(NT) bwd_mf_kernel(const Mf128Args a) {
                 const int tt = 4 * tg + x;
                 sm.krT[tt][ci] = tt == 0 ? kx : 0.f;
                 sm.sgy[tt][ci] = tt == 0 ? gx : 0.f;
-                sm.ee[tt][ci] = tt == 0 ? ex : 0.f;
+                sm.ee[tt][ci] = tt == 0 ? bx * ex : 0.f;
+                sm.du[tt][ci] = tt == 0 ? ex : 0.f;
                 if (ci == 0) sm.bt[tt] = tt == 0 ? bx : 0.f;
             }
             if (tid < 256) {
@@ -780,7 +858,7 @@ __global__ void __launch_bounds__(NT) bwd_mf_kernel(const Mf128Args a) {
 #pragma unroll
         for (int jb = 0; jb < 8; ++jb)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) v = fmaf(bldf(rz, vcol, (16 * jb + r) * S * 4), Mr[jb][r], v);
+            for (int r = 0; r < 4; ++r) v = fmaf(bldf(rz, vcol + r * S * 4, 16 * jb * S * 4), Mr[jb][r], v);
         return rows4_sum(v);
     };
     // a value per column i0 + l%16 into the tile layout (column i0 + 4(l/16) + r)
@@ -793,7 +871,6 @@ __global__ void __launch_bounds__(NT) bwd_mf_kernel(const Mf128Args a) {
 
     // ---- walk of a staged (sub)block with start state Mb (column layout); n tokens from tw.
     auto walk = [&](const f4 (&Mb)[8], int tw, int n, bool dir) {
-        const float btl = sm.bt[lm];
         // ---- phase A.  Chain: X' = X diag(P), its transpose for the column sums, dd0^T = KR X'^T,
         // dd^T = Tb (dd0^T + Bm sgy^T), du = -beta dd, dv and the dbeta partials.
         if (!dir) {
@@ -837,8 +914,8 @@ __global__ void __launch_bounds__(NT) bwd_mf_kernel(const Mf128Args a) {
                 const int tt = 4 * g4 + r;
                 const float bv = sm.bt[tt];
                 duv[r] = -bv * dd[r];
+                const float pbv = row16_sum(dd[r] * sm.du[tt][j0 + lm]);   // e, read before du replaces it
                 sm.du[tt][j0 + lm] = duv[r];
-                const float pbv = row16_sum(dd[r] * sm.ee[tt][j0 + lm]);
                 if (lm == 0) sm.pb[wv][tt] = pbv;
                 if (tt < n) bst(rdv, bv * dd[r], (j0 + lm) * 4 + tt * et, 0);
             }
@@ -862,10 +939,7 @@ __global__ void __launch_bounds__(NT) bwd_mf_kernel(const Mf128Args a) {
             for (int r = 0; r < 4; ++r) dgacc[r] = sm.qcI[i0 + 4 * g4 + r][lm] * p1[r];
             const f4 kr4 = ld4(&sm.krI[i0 + lm][4 * g4]);
 #pragma unroll
-            for (int x = 0; x < 4; ++x) {
-                const float g = sm.g1[4 * g4 + x][lm];
-                p1 = mfma(kr4[x], 4 * g4 + x <= lm ? g : 0.f, p1);
-            }
+            for (int x = 0; x < 4; ++x) p1 = mfma(kr4[x], sm.g1[4 * g4 + x][lm], p1);
         }
         __syncthreads();   // X' transposed, du, dbeta partials
         // ---- phase B.  Column part: P3 = X'^T delta, P2 = M^T du, the G2 partial over the wave's
@@ -881,8 +955,8 @@ __global__ void __launch_bounds__(NT) bwd_mf_kernel(const Mf128Args a) {
                 const f4 u0 = ld4(&sm.du[lm][16 * jb + 4 * g4]), u1 = ld4(&sm.du[lm][16 * jb + 16 + 4 * g4]);
 #pragma unroll
                 for (int x = 0; x < 4; ++x) {
-                    p3a = mfma(x0[x], btl * e0[x], p3a);
-                    p3b = mfma(x1[x], btl * e1[x], p3b);
+                    p3a = mfma(x0[x], e0[x], p3a);
+                    p3b = mfma(x1[x], e1[x], p3b);
                     p2a = mfma(Mb[jb][x], u0[x], p2a);
                     p2b = mfma(Mb[jb + 1][x], u1[x], p2b);
                     xa = fmaf(x0[x], Mb[jb][x], xa);
@@ -899,28 +973,18 @@ __global__ void __launch_bounds__(NT) bwd_mf_kernel(const Mf128Args a) {
                 dg0[r] = xm4[r] + row16_sum(dgacc[r] + sm.kcI[i0 + 4 * g4 + r][lm] * p2[r]);
             const f4 qc4 = ld4(&sm.qcI[i0 + lm][4 * g4]);
 #pragma unroll
-            for (int x = 0; x < 4; ++x) {   // P3 += QC^T (G1^T masked s >= t)
-                const float g = sm.g1[lm][4 * g4 + x];
-                p3 = mfma(qc4[x], 4 * g4 + x >= lm ? g : 0.f, p3);
-            }
+            for (int x = 0; x < 4; ++x) p3 = mfma(qc4[x], sm.g1[lm][4 * g4 + x], p3);   // QC^T (G1^T, s >= t)
         }
         {   // G2 partial over rows 16 w ..: delta^T (row s = l%16) times du (column t = l%16)
             const f4 e4 = ld4(&sm.ee[lm][j0 + 4 * g4]), u4 = ld4(&sm.du[lm][j0 + 4 * g4]);
             f4 g2p = zero4();
 #pragma unroll
-            for (int x = 0; x < 4; ++x) g2p = mfma(btl * e4[x], u4[x], g2p);
+            for (int x = 0; x < 4; ++x) g2p = mfma(e4[x], u4[x], g2p);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) g2p[r] = 4 * g4 + r < lm ? g2p[r] : 0.f;   // s < t
 #pragma unroll
             for (int r = 0; r < 4; ++r) sm.gp[wv][4 * g4 + r][lm] = g2p[r];
             st4(&sm.gpt[wv][lm][4 * g4], g2p);
-        }
-#pragma unroll
-        for (int ib = 0; ib < 8; ++ib) {
-            const f4 qa = ld4(&sm.qcI[16 * ib + lm][4 * g4]), ka = ld4(&sm.kcI[16 * ib + lm][4 * g4]);
-#pragma unroll
-            for (int x = 0; x < 4; ++x) {
-                X[ib] = mfma(qa[x], sgB[x], X[ib]);
-                X[ib] = mfma(ka[x], duv[x], X[ib]);
-            }
         }
         if (wv == 0 && lane < W) {   // dbeta: the eight row-block partials in order
             float b = 0.f;
@@ -940,9 +1004,18 @@ __global__ void __launch_bounds__(NT) bwd_mf_kernel(const Mf128Args a) {
             const f4 kr4 = ld4(&sm.krI[i0 + lm][4 * g4]), kc4 = ld4(&sm.kcI[i0 + lm][4 * g4]);
 #pragma unroll
             for (int x = 0; x < 4; ++x) {
-                const int sg = 4 * g4 + x;
-                p3 = mfma(kc4[x], sg > lm ? g2t[x] : 0.f, p3);    // KC^T (G2^T masked s > t)
-                p2 = mfma(kr4[x], sg < lm ? g2v[x] : 0.f, p2);    // KR^T (G2 masked s < t)
+                p3 = mfma(kc4[x], g2t[x], p3);    // KC^T (G2^T, s > t)
+                p2 = mfma(kr4[x], g2v[x], p2);    // KR^T (G2, s < t)
+            }
+        }
+        // the chain: X = X' + sgy qc^T + du kc^T
+#pragma unroll
+        for (int ib = 0; ib < 8; ++ib) {
+            const f4 qa = ld4(&sm.qcI[16 * ib + lm][4 * g4]), ka = ld4(&sm.kcI[16 * ib + lm][4 * g4]);
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                X[ib] = mfma(qa[x], sgB[x], X[ib]);
+                X[ib] = mfma(ka[x], duv[x], X[ib]);
             }
         }
         // dq = c P1, dk = P3 / c + c P2, dg increments q.*dq - k.*(P3 / c) + k.*(c P2)
@@ -1054,14 +1127,19 @@ __global__ void __launch_bounds__(NT) bwd_mf_kernel(const Mf128Args a) {
             nt0 = nsg * C + nbb * W;
         }
         const bool dir = P.dir != 0;
+        // a column-scaled block is staged from the registers loaded during the previous step,
+        // which then take the next step's inputs
+        if (!dir) {
+            if (kind == 2) stage_walk(P, cnt);
+            else stage_replay(P, cnt);
+        }
+        if (nt0 >= 0) prefetch(P, nt0);
         if (kind != 2) {
             // replay: the block as one column-scaled block, or token by token
             load_cols(block_start(sg, bb), M);   // saved by the previous step when bb > 0
             const int nsub = dir ? cnt : 1;
             for (int u = 0; u < nsub; ++u) {
                 if (dir) stage_token(t0, u, false);
-                else stage_replay(P, cnt);
-                if (!dir && nt0 >= 0) prefetch(P, nt0);   // the registers are free again
                 replay(M, dir);
                 __syncthreads();
             }
@@ -1084,14 +1162,10 @@ __global__ void __launch_bounds__(NT) bwd_mf_kernel(const Mf128Args a) {
                     const float p = sm.pv[i0 + lm];
 #pragma unroll
                     for (int jb = 0; jb < 8; ++jb) M[jb] *= p;
-                } else {
-                    stage_walk(P, cnt);
-                    if (nt0 >= 0) prefetch(P, nt0);   // the registers are free again
                 }
                 walk(M, dir ? t0 + tau : t0, dir ? 1 : cnt, dir);
             }
         }
-        if (dir && nt0 >= 0) prefetch(P, nt0);
         sg = nsg;
         k = nk;
     }
@@ -1152,7 +1226,9 @@ int block_items(const Mf128Args &a) {
 }  // namespace
 
 hipError_t launch_prep128(const Mf128Args &a, hipStream_t st) {
-    return launch(pick<PrepK>(a.dtype), a, block_items(a), 64, st);
+    const int64_t items = (int64_t)a.n_seqs_launch * ((a.T + W - 1) / W) * a.H_v;
+    const int blocks = (int)std::min<int64_t>((items + PW - 1) / PW, 16384);
+    return launch(pick<PrepK>(a.dtype), a, blocks, 64 * PW, st);
 }
 
 hipError_t launch_fwd_mf(const Mf128Args &a, hipStream_t st) {
