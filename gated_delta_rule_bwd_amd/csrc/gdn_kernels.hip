@@ -4,7 +4,8 @@
 // Work decomposition.  One workgroup owns one (sequence, value head) unit and its S x S
 // fp32 state M = S^T (row j = value index, column i = key index).  Rows of M evolve
 // independently in both directions of the recurrence ("metal: GATED_DELTA_NET_BACK",
-// approval review: thread j owns row j), so the state is spread over the workgroup by rows:
+// approval review: one worker per row of the state), so the state is spread over the
+// workgroup by rows:
 // a row lives on LPR = 16 lanes (one DPP row), each lane holding NC = S/16 of its columns
 // (interleaved, column c = lane%16 + 16 n, so that a token vector load is coalesced), and
 // each lane holds R = 4 rows.  A wave therefore holds 4 row groups x 4 rows = 16 rows and

@@ -127,7 +127,12 @@ typedef struct gdn_problem {
 } gdn_problem;
 
 /* Bytes of device workspace that gdn_fwd and gdn_bwd need for this problem (0 on an
- * invalid problem).  The same workspace serves both calls. */
+ * invalid problem).  The same workspace serves both calls.  It holds what the scratch of the
+ * approval review's sizing note on "metal: GATED_DELTA_NET_BACK" holds -- the state snapshots
+ * every C tokens and the state recomputed inside a segment -- plus per-token arrays of the
+ * head-128 kernels: the running gate products, the prediction errors, the block matrices and
+ * Grams, the block starts of one segment and, when H_v > H_k, dq and dk per value head.  The
+ * caller allocates it once; nothing else is allocated. */
 size_t gdn_workspace_size(const gdn_problem *p);
 
 /* Layout of the packed gradient buffer (PR description of "metal: GATED_DELTA_NET_BACK":
@@ -140,8 +145,10 @@ size_t gdn_workspace_size(const gdn_problem *p);
  * Rows with t >= len_s are written as zeros. */
 size_t gdn_grad_packed_floats(const gdn_problem *p, size_t offsets[6]);
 
-/* Forward scan: writes y (strided as p->y) and state_out, and the state snapshots into the
- * workspace.  All pointers are device pointers; q, k, v, g, beta (and gy) hold p->dtype
+/* Forward scan (meTile, "Training kernels and gradients", section "Recurrent delta
+ * attention": per token the state decays by the gates, corrects by delta k^T with
+ * delta = beta (v - u), and reads out y = scale M q): writes y (strided as p->y) and
+ * state_out, and the state snapshots into the workspace.  All pointers are device pointers; q, k, v, g, beta (and gy) hold p->dtype
  * elements and are aligned to that element size, every other buffer is 4-byte aligned, ws
  * 16-byte aligned (GDN_ERR_UNSUPPORTED / GDN_ERR_ARG otherwise).  Returns GDN_OK or an error
  * code (nothing enqueued on error). */
@@ -149,8 +156,11 @@ int gdn_fwd(const gdn_problem *p, const void *q, const void *k, const void *v,
             const void *g, const void *beta, const float *state0, float *y,
             float *state_out, void *ws, size_t ws_bytes, gdn_stream_t stream);
 
-/* Backward: given the forward's inputs, the output cotangent gy (strided as p->gy) and
- * the final-state cotangent dstate_out (NULL means zero), writes the six input gradients
+/* Backward (the term-by-term gradients of the first review of "metal:
+ * GATED_DELTA_NET_BACK", restated at the top of this header; states recomputed from the
+ * snapshots every C tokens, the PR description's checkpointed recompute): given the forward's
+ * inputs, the output cotangent gy (strided as p->gy) and the final-state cotangent
+ * dstate_out (NULL means zero), writes the six input gradients
  * into grad_packed (layout: gdn_grad_packed_floats).  With GDN_BWD_REUSE_SNAPSHOTS the
  * snapshots already in ws from gdn_fwd are used; otherwise they are recomputed first.
  * dq and dk of one key head sum its value heads in increasing h, so results are bitwise

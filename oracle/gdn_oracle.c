@@ -8,8 +8,8 @@
  *
  *   Notation per (sequence s, value head h), key head hk = h mod H_k.  The state is held as
  *   M = S^T with rows j = value index (S_v of them) and columns i = key index (S_k of them),
- *   as the CPU-reference author describes the row-owner form ("metal: GATED_DELTA_NET_BACK",
- *   approval review: thread j owns row j of M = S^T).
+ *   the row-owner form of the CPU-reference author ("metal: GATED_DELTA_NET_BACK", approval
+ *   review: each row of M = S^T is handled on its own by one worker).
  *
  *   Forward, per token t (decay before correction; meTile "Training kernels and gradients",
  *   section "Recurrent delta attention"; the row-owner form in the same review):

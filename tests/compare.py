@@ -55,3 +55,30 @@ def check(results: dict, ref: dict, names=None, tol=TOL):
         report[name] = worst
         assert worst <= tol, f"{name}: max relative error {worst:.3e} at {at} > {tol:g} (diag {diag:.2e})"
     return report
+
+
+def slice_rel(x, r, axes=(0,), group=None):
+    """Worst relative error over slices: every index combination of `axes` (and, with `group`,
+    groups of that many entries along the last axis) is one slice, compared as
+    max|x - r| / max|r|; a slice whose reference is all zero must be exactly zero in x."""
+    x = np.asarray(x, dtype=np.float64)
+    r = np.asarray(r, dtype=np.float64)
+    assert x.shape == r.shape, (x.shape, r.shape)
+    if r.size == 0:
+        return 0.0
+    if group:
+        assert r.shape[-1] % group == 0, (r.shape, group)
+        x = x.reshape(*x.shape[:-1], -1, group)
+        r = r.reshape(*r.shape[:-1], -1, group)
+        axes = tuple(axes) + (r.ndim - 2,)
+    rest = tuple(a for a in range(r.ndim) if a not in axes)
+    xs = np.moveaxis(x, axes, range(len(axes))).reshape(*[r.shape[a] for a in axes], -1)
+    rs = np.moveaxis(r, axes, range(len(axes))).reshape(*[r.shape[a] for a in axes], -1)
+    del rest
+    if not np.all(np.isfinite(xs)):
+        return float("inf")
+    m = np.max(np.abs(rs), axis=-1)
+    d = np.max(np.abs(xs - rs), axis=-1)
+    if np.any((m == 0) & (d != 0)):
+        return float("inf")
+    return float(np.max(np.where(m > 0, d / np.where(m > 0, m, 1.0), 0.0)))

@@ -26,9 +26,14 @@ def dev():
     return binding
 
 
-def _rel(x, r):
-    m = float(np.max(np.abs(r)))
-    return float(np.max(np.abs(x - r))) / (m if m > 0 else 1.0)
+def _rel(x, r, name):
+    """Worst error over (sequence, head) slices: per-token regions [n][T][H][..] slice on axes
+    0 and 2, states [n][H][..] on 0 and 1, the input gradient [n][rows][D] per sequence and
+    128-channel group."""
+    from compare import slice_rel
+    if name == "dsx":
+        return slice_rel(x, r, (0,), 128 if r.shape[-1] % 128 == 0 else None)
+    return slice_rel(x, r, (0, 1) if name in ("state_out", "dstate") else (0, 2))
 
 
 def _inputs(seed, n, T, Hk, Hv, S, K):
@@ -108,12 +113,12 @@ def oracle_chain(a, n, T, Hk, Hv, S, C):
 
 @pytest.mark.parametrize("n,T,Hk,Hv,S,C", [
     (2, 40, 2, 4, 32, 0),      # small heads, two value heads per key head, ragged window
-    (1, 24, 1, 2, 128, 8),     # the head size of the layer shape (row-quarter kernels)
+    (1, 24, 1, 2, 128, 8),     # the head size of the layer shape (matrix-core kernels)
 ])
 def test_layer_chain(dev, n, T, Hk, Hv, S, C):
     a = _inputs(1700 + S + T, n, T, Hk, Hv, S, 4)
     got = gpu_chain(dev, a, n, T, Hk, Hv, S, C)
     ref = oracle_chain(a, n, T, Hk, Hv, S, C)
-    errs = {k: _rel(got[k], ref[k].reshape(got[k].shape)) for k in ref}
+    errs = {k: _rel(got[k], ref[k].reshape(got[k].shape), k) for k in ref}
     log(f"[chain] n={n} T={T} Hk={Hk} Hv={Hv} S={S}: " + " ".join(f"{k} {v:.1e}" for k, v in errs.items()))
     assert all(v <= TOL for v in errs.values()), errs

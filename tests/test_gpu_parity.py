@@ -44,27 +44,39 @@ def test_parity_full(dev, name, reuse):
     log(f"[parity] {name}: " + ", ".join(f"{k} {v:.1e}" for k, v in rep.items()))
 
 
-def test_parity_layer_shape_sampled(dev):
-    """Full-size layer shape in the benchmark's launch configuration; the oracle checks
-    two (sequence, key head) groups, each with its three value heads."""
+def test_parity_layer_shape_full(dev):
+    """Full-size layer shape in the benchmark's launch configuration, every unit against the
+    oracle: the oracle runs one sequence at a time (its 16 key heads with their 48 value heads,
+    each value head a problem of its own on the host cores)."""
     w = I.WORKLOADS["layer_kda_s128"]
-    log(f"[parity] {w.name} full size, sampled")
+    log(f"[parity] {w.name} full size, every (sequence, key head) group")
     arrays, _ = I.make_all(w)
     _, got = run_case(dev, w, arrays, reuse=True)
     del arrays
-    for seqs, khs in (([0], [0]), ([3], [15])):
-        ref, vh = oracle_sampled(w, seqs, khs)
-        sub = gpu_subset(got, w, seqs, khs, vh)
-        rep = check(sub, ref, REGIONS_FWD + REGIONS_BWD)
-        log(f"[parity] {w.name} seq {seqs} key heads {khs}: " +
-            ", ".join(f"{k} {v:.1e}" for k, v in rep.items()))
+    khs = list(range(w.H_k))
+    for s in range(w.n_seqs):
+        ref, vh = oracle_sampled(w, [s], khs)
+        rep = check(gpu_subset(got, w, [s], khs, vh), ref, REGIONS_FWD + REGIONS_BWD)
+        log(f"[parity] {w.name} seq {s}, all key heads: " + ", ".join(f"{k} {v:.1e}" for k, v in rep.items()))
+
+
+def test_parity_s128_many_units(dev):
+    """512 units (four sequences of 128 value heads over 32 key heads, ragged, KDA), so 512
+    workgroups run at once; every unit against the oracle."""
+    w = I.Workload("s128_many_units", 4, 40, 32, 128, 128, True, 16, -0.3, seq_lens=(40, 33, 17, 40),
+                   seed=521)
+    log(f"[parity] {w.name} lens={w.lens}")
+    arrays, _ = I.make_all(w)
+    _, got = run_case(dev, w, arrays, reuse=True)
+    rep = check(got, oracle_results(w, arrays), REGIONS_FWD + REGIONS_BWD)
+    log(f"[parity] {w.name}: " + ", ".join(f"{k} {v:.1e}" for k, v in rep.items()))
 
 
 def test_layer_shape_bf16_inputs_bitwise(dev):
     """Full-size layer shape with bf16 inputs, as the benchmark's bf16 mode launches it: every
     output is bitwise equal to the fp32-input run on the same (rounded) values, which holds at
     any size because the kernels widen each input exactly at the load; the fp32 kernels' own
-    parity at this shape is sampled against the oracle above."""
+    parity at this shape is checked in full against the oracle above."""
     w = I.WORKLOADS["layer_kda_s128"]
     log(f"[parity] {w.name} full size, bf16 inputs against fp32 inputs holding the same values")
     arrays = I.round_inputs(I.make_all(w)[0], "bf16")
@@ -81,19 +93,20 @@ def test_layer_shape_bf16_inputs_bitwise(dev):
     assert bool(torch.isfinite(outs[0][2]).all())
 
 
-def test_parity_long_context_sampled(dev):
+def test_parity_long_context_full(dev):
     """Full-size long-context workload (one 65536-token sequence, 48 value heads, interval
-    256, scalar gate); the oracle checks one key head with its three value heads over the
-    whole sequence."""
+    256, scalar gate), every unit against the oracle, four key heads (twelve value heads) at a
+    time."""
     w = I.WORKLOADS["long_scalar_s128"]
-    log(f"[parity] {w.name} full size, sampled")
+    log(f"[parity] {w.name} full size, every key head")
     arrays, _ = I.make_all(w)
     _, got = run_case(dev, w, arrays, reuse=True)
     del arrays
-    ref, vh = oracle_sampled(w, [0], [5])
-    sub = gpu_subset(got, w, [0], [5], vh)
-    rep = check(sub, ref, REGIONS_FWD + REGIONS_BWD)
-    log(f"[parity] {w.name} seq [0] key head [5]: " + ", ".join(f"{k} {v:.1e}" for k, v in rep.items()))
+    for k0 in range(0, w.H_k, 4):
+        khs = list(range(k0, min(w.H_k, k0 + 4)))
+        ref, vh = oracle_sampled(w, [0], khs)
+        rep = check(gpu_subset(got, w, [0], khs, vh), ref, REGIONS_FWD + REGIONS_BWD)
+        log(f"[parity] {w.name} key heads {khs}: " + ", ".join(f"{k} {v:.1e}" for k, v in rep.items()))
 
 
 # Head size 16: one wave per unit (16 rows, one column per lane).

@@ -6,6 +6,7 @@ torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
 from gpu_cases import log  # noqa: E402
+from compare import slice_rel  # noqa: E402
 
 TOL = 2e-4   # max |gpu - oracle| / max |oracle| per output region (fp32 recurrences vs fp64)
 
@@ -18,11 +19,15 @@ def dev():
     return binding
 
 
-def _rel(x, r):
-    if r.size == 0:
-        return 0.0
-    m = float(np.max(np.abs(r)))
-    return float(np.max(np.abs(x - r))) / (m if m > 0 else 1.0)
+# the (sequence, head) axes of each region: x, y, dx, dt, ddt [n][T][H][..], B, C, dB, dC
+# [n][T][G][N], states [n][H][P][N]
+AXES = {"y": (0, 2), "dx": (0, 2), "ddt": (0, 2), "dB": (0, 2), "dC": (0, 2),
+        "s_out": (0, 1), "ds": (0, 1)}
+
+
+def _rel(x, r, name="y"):
+    """Worst error over the (sequence, head) slices of a region."""
+    return slice_rel(x, r, AXES[name])
 
 
 def run(B, arr, softplus=True, with_gs=True, flags=1, recompute_too=False):
@@ -84,8 +89,8 @@ def test_ssm_parity(dev, n, T, H, P, N, G, aps, softplus, with_gs):
     arr = _arrays(n, T, H, P, N, G, aps, softplus, 1500 + T + H + N)
     y, sT, grads, grads2 = run(dev, arr, softplus, with_gs, recompute_too=True)
     ry, rsT, rg = oracle(arr, softplus, with_gs)
-    errs = {"y": _rel(y, ry), "s_out": _rel(sT, rsT)}
-    errs.update({k: _rel(grads[k], rg[k]) for k in rg})
+    errs = {"y": _rel(y, ry, "y"), "s_out": _rel(sT, rsT, "s_out")}
+    errs.update({k: _rel(grads[k], rg[k], k) for k in rg})
     log(f"[ssm] n={n} T={T} H={H} P={P} N={N} G={G} aps={aps} softplus={softplus}: "
         + " ".join(f"{k} {v:.1e}" for k, v in errs.items()))
     assert all(v <= TOL for v in errs.values()), errs
@@ -122,9 +127,10 @@ def test_ssm_layer_sampled(dev, name):
                "A": arr["A"][h:h + 1], "B": arr["B"][:1], "C": arr["C"][:1],
                "gy": arr["gy"][:1, :, h:h + 1], "gs": arr["gs"][:1, h:h + 1]}
         ry, rsT, rg = oracle(sub)
-        errs = {"y": _rel(y[:1, :, h:h + 1], ry), "s_out": _rel(sT[:1, h:h + 1], rsT),
-                "ds": _rel(gr["ds"][:1, h:h + 1], rg["ds"]), "dx": _rel(gr["dx"][:1, :, h:h + 1], rg["dx"]),
-                "ddt": _rel(gr["ddt"][:1, :, h:h + 1], rg["ddt"])}
+        errs = {"y": _rel(y[:1, :, h:h + 1], ry, "y"), "s_out": _rel(sT[:1, h:h + 1], rsT, "s_out"),
+                "ds": _rel(gr["ds"][:1, h:h + 1], rg["ds"], "ds"),
+                "dx": _rel(gr["dx"][:1, :, h:h + 1], rg["dx"], "dx"),
+                "ddt": _rel(gr["ddt"][:1, :, h:h + 1], rg["ddt"], "ddt")}
         log(f"[ssm] {name} head {h}: " + " ".join(f"{k} {v:.1e}" for k, v in errs.items()))
         assert all(v <= TOL for v in errs.values()), errs
     f64 = np.float64
@@ -132,6 +138,23 @@ def test_ssm_layer_sampled(dev, name):
     rhs_b = np.einsum("nthp,nthp->nt", arr["x"].astype(f64), gr["dx"].astype(f64))[..., None]
     lhs_c = np.einsum("ntgk,ntgk->ntg", gr["dC"].astype(f64), arr["C"].astype(f64))
     rhs_c = np.einsum("nthp,nthp->nt", arr["gy"].astype(f64), y.astype(f64))[..., None]
-    eb, ec = _rel(lhs_b, rhs_b), _rel(lhs_c, rhs_c)
+    eb, ec = slice_rel(lhs_b, rhs_b, (0, 2)), slice_rel(lhs_c, rhs_c, (0, 2))
     log(f"[ssm] {name} fold identities: dB.B {eb:.1e}, dC.C {ec:.1e}")
     assert eb <= TOL and ec <= TOL
+
+
+@pytest.mark.parametrize("name", ["ssm2_layer_h80_p64_n128", "ssm1_layer_d5120_n16"])
+def test_ssm_layer_heads_elementwise(dev, name):
+    """The layer's head and state shape (all heads, so dB and dC fold every head of the group)
+    over 256 tokens of one sequence: every output, dB and dC included, elementwise per
+    (sequence, head) slice against the oracle."""
+    from gated_delta_rule_bwd_amd import inputs as I
+    cfg = dict(I.SSM_WORKLOADS[name])
+    cfg["n_seqs"], cfg["T"] = 1, 256
+    arr = I.make_ssm(cfg)
+    y, sT, gr = run(dev, arr)
+    ry, rsT, rg = oracle(arr)
+    errs = {"y": _rel(y, ry, "y"), "s_out": _rel(sT, rsT, "s_out")}
+    errs.update({k: _rel(gr[k], rg[k], k) for k in rg})
+    log(f"[ssm] {name} heads x 256 tokens: " + " ".join(f"{k} {v:.1e}" for k, v in errs.items()))
+    assert all(v <= TOL for v in errs.values()), errs
