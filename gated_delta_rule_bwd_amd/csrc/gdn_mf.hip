@@ -144,6 +144,13 @@ __device__ __forceinline__ f4 bld4(Rsrc r, uint32_t vbytes) {
         return o;
     }
 }
+// A wave-uniform 32-bit value read through the constant address space, so it takes a scalar
+// load (its wait does not drain the vector memory counter).  Only for data no kernel of the
+// same launch writes.
+__device__ __forceinline__ int32_t sload(const int32_t *p, int64_t i) {
+    typedef const __attribute__((address_space(4))) int32_t *cptr;
+    return ((cptr)(uintptr_t)p)[i];
+}
 template <int DT>
 __device__ __forceinline__ const In<DT> *tin(const void *p) {
     return reinterpret_cast<const In<DT> *>(p);
@@ -404,7 +411,7 @@ __global__ void __launch_bounds__(NT) fwd_mf_kernel(const Mf128Args a) {
     auto prefetch = [&](Pre &P, int t0) {
         const int cnt = min(W, L - t0);
         const int64_t bi = (s * nblk + t0 / W) * a.H_v + h;
-        P.dir = a.wflag[bi];
+        P.dir = sload(a.wflag, bi);
         const Rsrc rc = rsrc(cin + (int64_t)t0 * (a.H_v * G)), rk = rsrc(kin + (int64_t)t0 * a.sk.tok),
                    rq = rsrc(qin + (int64_t)t0 * a.sq.tok), rv = rsrc(vin + (int64_t)t0 * a.sv.tok),
                    rb = rsrc(bin + (int64_t)t0 * a.sb.tok), rw = rsrc(a.wmat + bi * MATF);
@@ -726,7 +733,7 @@ __global__ void __launch_bounds__(NT) bwd_mf_kernel(const Mf128Args a) {
     auto prefetch = [&](Pre &P, int t0) {
         const int cnt = min(W, L - t0);
         const int64_t bi = (s * nblk + t0 / W) * a.H_v + h;
-        P.dir = a.wflag[bi];
+        P.dir = sload(a.wflag, bi);
         const Rsrc rc = rsrc(cin + (int64_t)t0 * (a.H_v * G)), rk = rsrc(kin + (int64_t)t0 * a.sk.tok),
                    rq = rsrc(qin + (int64_t)t0 * a.sq.tok), rgy = rsrc(gyin + (int64_t)t0 * a.sgy.tok),
                    re = rsrc(ein + (int64_t)t0 * (a.H_v * S)), rb = rsrc(bin + (int64_t)t0 * a.sb.tok),
