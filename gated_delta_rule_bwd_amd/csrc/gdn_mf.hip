@@ -359,7 +359,7 @@ struct alignas(16) FwdLds {
 
 template <int DT>
 __global__ void __launch_bounds__(NT) fwd_mf_kernel(const Mf128Args a) {
-    __shared__ FwdLds sm;
+    __shared__ FwdLds smb[2];   // staged blocks, alternately (one barrier per block)
     constexpr uint32_t ES = sizeof(In<DT>);
     const int ul = blockIdx.x;
     const int sl = ul / a.H_v, h = ul % a.H_v;
@@ -436,8 +436,8 @@ __global__ void __launch_bounds__(NT) fwd_mf_kernel(const Mf128Args a) {
 
     // one (sub)block of n tokens from token tw, its column data staged; vv, bb: v and beta,
     // teA, bmA: operands of Te^T and Bm^T
-    auto block = [&](int tw, int n, const float (&vv)[4], const float (&bb)[4], const float (&teA)[4],
-                     const float (&bmA)[4]) {
+    auto block = [&](const FwdLds &sm, int tw, int n, const float (&vv)[4], const float (&bb)[4],
+                     const float (&teA)[4], const float (&bmA)[4]) {
         // u and y against the start state: D[token][row]
         f4 u0 = zero4(), u1 = zero4(), y0 = zero4(), y1 = zero4();
 #pragma unroll
@@ -483,17 +483,22 @@ __global__ void __launch_bounds__(NT) fwd_mf_kernel(const Mf128Args a) {
             for (int x = 0; x < 4; ++x) M[ib] = mfma(ar[x], D[x], M[ib]);
         }
     };
-    auto scale_state = [&]() {
+    auto scale_state = [&](const FwdLds &sm) {
 #pragma unroll
         for (int ib = 0; ib < S / 16; ++ib) M[ib] *= ld4(&sm.pv[16 * ib + 4 * g4]);
     };
 
+    // Each staging fills the buffer the previous block did not use; every wave left that buffer
+    // before the barrier that followed the previous staging, so one barrier per block (per token
+    // of a token-by-token block) orders the writes and the reads.
     Pre P;
+    int cur = 0;
     if (L > 0) prefetch(P, 0);
     for (int b = 0; b * W < L; ++b) {
         const int t0 = b * W, cnt = min(W, L - t0);
         if (t0 % a.C == 0) store_state(snap + (int64_t)(t0 / a.C) * S * S);
         if (!P.dir) {
+            FwdLds &sm = smb[cur];
             float krow[4];
 #pragma unroll
             for (int x = 0; x < 4; ++x) {
@@ -509,9 +514,9 @@ __global__ void __launch_bounds__(NT) fwd_mf_kernel(const Mf128Args a) {
             const float teA[4] = {P.te[0], P.te[1], P.te[2], P.te[3]}, bmA[4] = {P.bm[0], P.bm[1], P.bm[2], P.bm[3]};
             __syncthreads();
             if (t0 + W < L) prefetch(P, t0 + W);   // the registers are free again
-            block(t0, cnt, vv, bb, teA, bmA);
-            scale_state();
-            __syncthreads();
+            block(sm, t0, cnt, vv, bb, teA, bmA);
+            scale_state(sm);
+            cur ^= 1;
         } else {   // token by token: each token a one-token block after its gates scale the state
             const int64_t bi = (s * nblk + b) * a.H_v + h;
             const float *wm = a.wmat + bi * MATF;
@@ -519,6 +524,7 @@ __global__ void __launch_bounds__(NT) fwd_mf_kernel(const Mf128Args a) {
                        rq = rsrc(qin + (int64_t)t0 * a.sq.tok), rv = rsrc(vin + (int64_t)t0 * a.sv.tok),
                        rb = rsrc(bin + (int64_t)t0 * a.sb.tok);
             for (int tau = 0; tau < cnt; ++tau) {
+                FwdLds &sm = smb[cur];
                 const float av = bldf(rc, ccol + tau * ct, 0);
                 const float kx = bld<DT>(rk, ci * ES + tau * kt, 0);
                 const float qx = bld<DT>(rq, ci * ES + tau * qt, 0);
@@ -540,9 +546,9 @@ __global__ void __launch_bounds__(NT) fwd_mf_kernel(const Mf128Args a) {
                     bmA[r] = (tt == 0 && lm == 0) ? wm[tau * (W + 1)] : 0.f;
                 }
                 __syncthreads();
-                scale_state();
-                block(t0 + tau, 1, vv, bb, teA, bmA);
-                __syncthreads();
+                scale_state(sm);
+                block(sm, t0 + tau, 1, vv, bb, teA, bmA);
+                cur ^= 1;
             }
             if (t0 + W < L) prefetch(P, t0 + W);
         }
