@@ -38,6 +38,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cstddef>
 
 #include "gdn_internal.h"
 
@@ -647,10 +648,10 @@ struct alignas(16) BwdLds {
     float krI[S][KP];          // k./c        [column][token]
     float qcI[S][KP];          // c.*q        [column][token]
     float kcI[S][KP];          // c.*k        [column][token]
-    float sgy[W][SP];          // scale gy    [token][row]
+    float sgy[W][SP];          // scale gy    [token][row]; with ee, in replays: delta
     float ee[W][SP];           // delta = beta e  [token][row]
     float du[W][SP];           // e, then du  [token][row]
-    float xt[S][SP];           // X after the fold [column][row]; in a replay: delta [row][token]
+    float xt[S][SP];           // X after the fold [column][row]; in replays: the state
     float pv[S];               // fold factor per column (a token's gates)
     float bt[W];               // beta
     float bm[W][W], tb[W][W];  // Bm, Tb
@@ -660,6 +661,10 @@ struct alignas(16) BwdLds {
     float pb[NW][W];           // per-wave partials of dbeta
     float gs[NW][W];           // per-wave partial sums of the scalar gate's dg
 };
+
+static_assert(2 * W * SP >= S * KP, "a replay's delta fits in sgy and ee");
+static_assert(offsetof(BwdLds, ee) == offsetof(BwdLds, sgy) + sizeof(float) * W * SP, "sgy and ee adjacent");
+static_assert(S * SP >= 32 * NT, "a replay's state fits in xt");
 
 template <int DT>
 __global__ void __launch_bounds__(NT) bwd_mf_kernel(const Mf128Args a) {
@@ -679,7 +684,10 @@ __global__ void __launch_bounds__(NT) bwd_mf_kernel(const Mf128Args a) {
     const int G = a.kda ? S : 1;
     const float scale = a.scale;
     const bool kda = a.kda != 0;
-    float (*dl)[KP] = reinterpret_cast<float (*)[KP]>(&sm.xt[0][0]);   // a replay's delta [row][token]
+    // during replays: the delta [row][token] in the space of sgy and ee, and the state handed from
+    // one replay step to the next in the space of xt (each lane reads back only what it wrote)
+    float (*dl)[KP] = reinterpret_cast<float (*)[KP]>(&sm.sgy[0][0]);
+    float *lst = &sm.xt[0][0];
     // bases of this (sequence, head) and byte strides per token
     const float *cin = a.cbuf + (s * a.T * a.H_v + h) * (int64_t)G;
     const In<DT> *kin = tin<DT>(a.k) + s * a.sk.seq + hk * a.sk.head;
@@ -714,6 +722,19 @@ __global__ void __launch_bounds__(NT) bwd_mf_kernel(const Mf128Args a) {
         for (int jb = 0; jb < 8; ++jb)
 #pragma unroll
             for (int r = 0; r < 4; ++r) bst(rs, Mc[jb][r], vcol + r * S * 4, 16 * jb * S * 4);
+    };
+
+    auto save_lds = [&](const f4 (&Mc)[8]) {
+#pragma unroll
+        for (int jb = 0; jb < 8; ++jb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) lst[(4 * jb + r) * NT + tid] = Mc[jb][r];
+    };
+    auto load_lds = [&](f4 (&Mc)[8]) {
+#pragma unroll
+        for (int jb = 0; jb < 8; ++jb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) Mc[jb][r] = lst[(4 * jb + r) * NT + tid];
     };
 
     // the gradient in the row layout
@@ -1148,16 +1169,22 @@ __global__ void __launch_bounds__(NT) bwd_mf_kernel(const Mf128Args a) {
         }
         if (nt0 >= 0) prefetch(P, nt0);
         if (kind != 2) {
-            // replay: the block as one column-scaled block, or token by token
-            load_cols(block_start(sg, bb), M);   // saved by the previous step when bb > 0
+            // replay: the block as one column-scaled block, or token by token, from the snapshot or
+            // from the state the previous replay step left in LDS
+            if (bb == 0) load_cols(block_start(sg, 0), M);
+            else load_lds(M);
             const int nsub = dir ? cnt : 1;
             for (int u = 0; u < nsub; ++u) {
                 if (dir) stage_token(t0, u, false);
                 replay(M, dir);
                 __syncthreads();
             }
-            if (kind == 0) save_cols(bsb + (int64_t)(bb + 1) * (S * S), M);
-            else final_sums(M);
+            if (kind == 0) {
+                save_cols(bsb + (int64_t)(bb + 1) * (S * S), M);   // for the walk of block bb + 1
+                save_lds(M);                                        // for the next replay step
+            } else {
+                final_sums(M);
+            }
         } else {
             // walk: the block as one column-scaled block, or its tokens from the last, each from
             // its own start state replayed from the block start
