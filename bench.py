@@ -525,7 +525,9 @@ def main():
         "pct_fp32_valu_peak": 100.0 * credited / (ms / 1e3) / PEAK_FP32_VALU,
         "fwd_ms": fwd_ms,
         "bwd_ms": bwd_ms,
-        "roofline": {"bound": "alu",
+        # head size 128 runs on the fp32 matrix cores (dense fp32 MFMA peak, the same figure as
+        # the fp32 vector peak); the small heads on the vector ALUs
+        "roofline": {"bound": "mfma" if S2 == 128 * 128 else "alu",
                      "kernel": "gdn_bwd (gram1_kernel + bwd_mf_kernel + combine_kernel)" if S2 == 128 * 128 else
                      "gdn_bwd (bwd_kernel" + (" + combine_kernel)" if w.H_v != w.H_k else ")"),
                      "achieved": achieved / 1e12, "peak": PEAK_FP32_VALU / 1e12,
