@@ -30,11 +30,10 @@ struct Plan {
     int n_ck_max = 1;  // snapshots per unit
     int G = 1;         // gate width
     int64_t units = 0;
-    bool s128 = false;   // head size 128: row-quarter kernels
+    bool s128 = false;   // head size 128: matrix-core kernels
     bool parts = false;  // small heads: dq/dk go through per-value-head partials
-    int nbs = 1;         // S_k = S_v = 128: 16-token blocks per segment
     size_t off_snap = 0, off_seg = 0, off_e = 0, off_pq = 0, off_pk = 0;
-    size_t off_wm = 0, off_wf = 0, off_c = 0, off_g1 = 0, off_vs = 0;
+    size_t off_wm = 0, off_wf = 0, off_c = 0, off_g1 = 0, off_g2 = 0, off_xs = 0;
     // half-precision inputs: their fp32 copies, contiguous [n_seqs][T][heads][width] each
     size_t off_in = 0, in_q = 0, in_k = 0, in_v = 0, in_g = 0, in_b = 0, in_gy = 0;
     size_t total = 0;
@@ -93,7 +92,6 @@ Plan make_plan(const gdn_problem *p) {
     if (pl.s128) {
         const size_t tok_rows = (size_t)p->n_seqs * p->T * p->H_v;
         const size_t nblk = (size_t)(p->T + 15) / 16;
-        pl.nbs = pl.C / 16;
         pl.off_wm = off;   // block matrices Bm, Te, Tb
         off = align_up(off + (size_t)p->n_seqs * nblk * p->H_v * 3 * 256 * sizeof(float));
         pl.off_wf = off;   // block flags
@@ -102,10 +100,12 @@ Plan make_plan(const gdn_problem *p) {
         off = align_up(off + tok_rows * pl.G * sizeof(float));
         pl.off_e = off;
         off = align_up(off + tok_rows * S * sizeof(float));
-        pl.off_g1 = off;   // Grams G1 of the blocks
+        pl.off_g1 = off;   // Grams G1 and G2 of the blocks
         off = align_up(off + (size_t)p->n_seqs * nblk * p->H_v * 256 * sizeof(float));
-        pl.off_vs = off;   // block starts of the segment being walked
-        if (pl.nbs > 1) off = align_up(off + (size_t)pl.units * pl.nbs * S * S * sizeof(float));
+        pl.off_g2 = off;
+        off = align_up(off + (size_t)p->n_seqs * nblk * p->H_v * 256 * sizeof(float));
+        pl.off_xs = off;   // the state gradient at each block's end
+        off = align_up(off + (size_t)pl.units * nblk * S * S * sizeof(float));
         pl.parts = p->H_v != p->H_k;
         if (pl.parts) {   // dq, dk per value head, summed over the heads of a key head afterwards
             pl.off_pq = off;
@@ -209,13 +209,14 @@ gdn::Mf128Args mf_args(const gdn_problem *p, const Plan &pl, void *ws, int s0, i
     a.cbuf = (float *)(w + pl.off_c);
     a.ebuf = (float *)(w + pl.off_e);
     a.g1buf = (float *)(w + pl.off_g1);
-    a.vsbuf = (float *)(w + pl.off_vs);
+    a.g2buf = (float *)(w + pl.off_g2);
+    a.xbuf = (float *)(w + pl.off_xs);
     a.dq_part = pl.parts ? (float *)(w + pl.off_pq) : nullptr;
     a.dk_part = pl.parts ? (float *)(w + pl.off_pk) : nullptr;
     a.sq = p->q; a.sk = p->k; a.sv = p->v; a.sg = p->g; a.sb = p->beta; a.sgy = p->gy; a.sy = p->y;
     a.s_base = s0; a.n_seqs_launch = cnt;
     a.T = p->T; a.H_k = p->H_k; a.H_v = p->H_v; a.C = pl.C; a.n_ck_max = pl.n_ck_max;
-    a.nbs = pl.nbs; a.kda = p->gate == GDN_GATE_KDA ? 1 : 0; a.dtype = p->dtype;
+    a.kda = p->gate == GDN_GATE_KDA ? 1 : 0; a.dtype = p->dtype;
     a.scale = p->scale;
     fill_lens(p, s0, cnt, a.lens);
     return a;

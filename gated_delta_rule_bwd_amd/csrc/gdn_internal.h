@@ -113,17 +113,19 @@ struct Mf128Args {
     float *cbuf;            // [n_seqs][T][H_v][G] running gate product c within the token's
                             // block (the gates a themselves in a token-by-token block)
     float *ebuf;            // [n_seqs][T][H_v][S] prediction errors e = v - u
-    float *g1buf;           // [n_seqs][nblk][H_v][16][16] Gram G1 = delta^T (scale gy)
-    float *vsbuf;           // [unit][nbs][S][S] block starts of the segment being walked
+    float *g1buf;           // [n_seqs][nblk][H_v][16][16] Grams G1 = delta^T (scale gy), s <= t,
+    float *g2buf;           // and G2 = delta^T du, s < t, over the rows of each block
+    float *xbuf;            // [unit][nblk][S][S] the state gradient at each block's end, folded
+                            // into the block's column scaling (tile-major 16 x 16 tiles)
     float *dq_part, *dk_part;   // [n_seqs][T][H_v][S] per value head (null: H_v == H_k, direct)
     float *dq, *dk, *dv, *dg, *dbeta, *dstate;
     gdn_strides sq, sk, sv, sg, sb, sgy, sy;
-    int32_t s_base, n_seqs_launch, T, H_k, H_v, C, n_ck_max, nbs, kda, dtype;
+    int32_t s_base, n_seqs_launch, T, H_k, H_v, C, n_ck_max, kda, dtype;
     float scale;
     int32_t lens[kMaxSeqsPerLaunch];
 };
 hipError_t launch_prep128(const Mf128Args &a, hipStream_t st);
 hipError_t launch_fwd_mf(const Mf128Args &a, hipStream_t st);
-hipError_t launch_bwd_mf(const Mf128Args &a, hipStream_t st);   // G1 pass, then the walk
+hipError_t launch_bwd_mf(const Mf128Args &a, hipStream_t st);   // the chain, then the column sums
 
 }  // namespace gdn

@@ -575,120 +575,64 @@ __global__ void __launch_bounds__(NT) fwd_mf_kernel(const Mf128Args a) {
 
 // ------------------------------------------------------------------ backward
 
-// The Gram G1[s][t] = delta_s . (scale gy_t) over the 128 rows of every block of every unit
-// (it needs only the forward's errors and the cotangent).  One wave per block; a block processed
-// token by token keeps its diagonal (the one-token Grams).
-template <int DT>
-__global__ void __launch_bounds__(64) gram1_kernel(const Mf128Args a) {
-    constexpr uint32_t ES = sizeof(In<DT>);
-    const int lane = threadIdx.x, lm = lane & 15, g4 = lane >> 4;
-    const int nblk = (a.T + W - 1) / W;
-    const int64_t items = (int64_t)a.n_seqs_launch * nblk * a.H_v;
-    const uint32_t gyt = (uint32_t)a.sgy.tok * ES;
-    const bool vec_gy = (((uintptr_t)a.gy & (4 * ES - 1)) == 0) && a.sgy.seq % 4 == 0 && a.sgy.tok % 4 == 0 &&
-                        a.sgy.head % 4 == 0;
-    for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
-        const int h = (int)(it % a.H_v);
-        const int64_t rest = it / a.H_v;
-        const int b = (int)(rest % nblk), sl = (int)(rest / nblk);
-        const int t0 = b * W, cnt = min(W, a.lens[sl] - t0);
-        if (cnt <= 0) continue;
-        const int64_t s = a.s_base + sl;
-        const bool ok = lm < cnt;
-        const float *er = a.ebuf + ((s * a.T + t0 + (ok ? lm : 0)) * a.H_v + h) * S;
-        const Rsrc rgy = rsrc(tin<DT>(a.gy) + s * a.sgy.seq + (int64_t)t0 * a.sgy.tok + h * a.sgy.head);
-        const Rsrc rb = rsrc(tin<DT>(a.beta) + s * a.sb.seq + (int64_t)t0 * a.sb.tok + h * a.sb.head);
-        const float bl = ok ? bld<DT>(rb, lm * (uint32_t)a.sb.tok * ES, 0) : 0.f;
-        // A = delta^T (row s = l%16, rows j along the contraction), B = scale gy (column t = l%16)
-        f4 g0 = zero4(), g1 = zero4();
-#pragma unroll
-        for (int kb = 0; kb < S / 16; ++kb) {
-            const int j = 16 * kb + 4 * g4;
-            const f4 e4 = ok ? ld4(er + j) : zero4();
-            f4 y4 = zero4();
-            if (ok) {
-                const uint32_t o = j * ES + lm * gyt;
-                y4 = vec_gy ? bld4<DT>(rgy, o)
-                            : f4{bld<DT>(rgy, o, 0), bld<DT>(rgy, o + ES, 0), bld<DT>(rgy, o + 2 * ES, 0),
-                                 bld<DT>(rgy, o + 3 * ES, 0)};
-                y4 *= a.scale;
-            }
-#pragma unroll
-            for (int x = 0; x < 4; ++x) {
-                if (kb % 2 == 0) g0 = mfma(bl * e4[x], y4[x], g0);
-                else g1 = mfma(bl * e4[x], y4[x], g1);
-            }
-        }
-        const f4 gsum = g0 + g1;
-        float *dst = a.g1buf + ((s * nblk + b) * a.H_v + h) * (int64_t)(W * W);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) dst[(4 * g4 + r) * W + lm] = gsum[r];
-    }
-}
-
-// A workgroup owns a unit.  Two layouts of the 128 x 128 matrices:
-//  - rows, for the chain dd = dM k and the update of dM: wave w holds rows 16 w .. 16 w + 15 of
-//    the gradient X = dM diag(c) transposed as eight tiles (tile ib, lane l, register r:
-//    X[16 w + l%16][16 ib + 4(l/16) + r]);
-//  - columns, for the column sums (dq, dk, dg) and the state replay: wave w holds columns
-//    16 w .. 16 w + 15 of the state M as eight tiles (tile jb, lane l, register r:
-//    M[16 jb + 4(l/16) + r][16 w + l%16]).
-// The gradient reaches the column layout through a transpose in LDS once per block.  Column
-// results are tiles P[i][t] (lane l, register r: column 16 w + 4(l/16) + r, token l%16).
+// The backward runs as two passes over the blocks.
 //
-// Per segment of C tokens the backward runs a fixed sequence of steps: replays of the segment's
-// blocks from its snapshot, each leaving the next block's start state in the workspace; for the
-// sequence's last segment, a replay of its last block (the final state, which starts the dg
-// recursion); then walks of the blocks from the last, each from its saved start state.  The
-// inputs of each step are loaded into registers during the previous step.
+// Pass 1, the chain (one workgroup per unit).  The rows of the state gradient evolve
+// independently, and its recurrence (dd = dM k, then the update of dM) reads no state, so this
+// pass walks the blocks of a sequence from the last in the row layout and never replays the
+// state.  Wave w holds rows 16 w .. 16 w + 15 of the gradient X = dM diag(c) transposed as eight
+// tiles (tile ib, lane l, register r: X[16 w + l%16][16 ib + 4(l/16) + r]).  Per block: the fold
+// X' = X diag(P) (P the block's gate product), saved for pass 2; dd^T = Tb (KR X'^T + Bm sgy^T);
+// dv = beta dd (which also hands du = -dv to pass 2); dbeta = dd . e; the block's Grams over the
+// rows G1 = delta^T sgy and G2 = delta^T du for pass 2; X = X' + sgy qc^T + du kc^T.
+//
+// Pass 2, the column sums (one workgroup per checkpoint segment of a unit, all in parallel).
+// Wave w holds columns 16 w .. 16 w + 15 of the state M as eight tiles (tile jb, lane l,
+// register r: M[16 jb + 4(l/16) + r][16 w + l%16]) and of the saved X' alike.  Starting from the
+// segment's snapshot, per block: the column sums against the block's start state and X' (dq, dk
+// and the increments of dg), then the replay to the next block's start.  Column results are
+// tiles P[i][t] (lane l, register r: column 16 w + 4(l/16) + r, token l%16).
+//
+// A saved gradient is tile-major: tile (R, Cb) of rows 16 R .., columns 16 Cb .. at float offset
+// 256 (8 R + Cb), element (rho, sigma) of the tile at 16 rho + sigma, so that both passes move
+// whole 1 KiB tiles.
+//
+// Both passes stage block b while block b - 1 (pass 1) or b + 1 (pass 2) may still be read, in
+// the other of two LDS buffers, so one barrier per block suffices; results the waves combine
+// (dbeta, the Grams, the scalar gate's dg) are summed after the next block's barrier.
 constexpr int GP = W + 4;   // row pitch of the per-wave 16 x 16 partials
 
-struct alignas(16) BwdLds {
+struct alignas(16) ChainLds {
     float krT[W][SP];          // k./c        [token][column]
-    float krI[S][KP];          // k./c        [column][token]
+    float sgy[W][SP];          // scale gy    [token][row]
+    float er[W][SP];           // e           [token][row]
     float qcI[S][KP];          // c.*q        [column][token]
     float kcI[S][KP];          // c.*k        [column][token]
-    float sgy[W][SP];          // scale gy    [token][row]; with ee, in replays: delta
-    float ee[W][SP];           // delta = beta e  [token][row]
-    float du[W][SP];           // e, then du  [token][row]
-    float xt[S][SP];           // X after the fold [column][row]; in replays: the state
     float pv[S];               // fold factor per column (a token's gates)
     float bt[W];               // beta
     float bm[W][W], tb[W][W];  // Bm, Tb
-    float g1[W][GP];           // G1 = delta^T scale gy, upper triangle with the diagonal
-    float gp[NW][W][GP];       // per-wave partials of G2 = delta^T du, strict upper triangle, [s][t]
-    float gpt[NW][W][GP];      // the same, [t][s]
     float pb[NW][W];           // per-wave partials of dbeta
-    float gs[NW][W];           // per-wave partial sums of the scalar gate's dg
+    float p1[NW][W][GP];       // per-wave partials of G1 [s][t]
+    float p2[NW][W][GP];       // per-wave partials of G2 [s][t]
 };
 
-static_assert(2 * W * SP >= S * KP, "a replay's delta fits in sgy and ee");
-static_assert(offsetof(BwdLds, ee) == offsetof(BwdLds, sgy) + sizeof(float) * W * SP, "sgy and ee adjacent");
-static_assert(S * SP >= 32 * NT, "a replay's state fits in xt");
-
 template <int DT>
-__global__ void __launch_bounds__(NT) bwd_mf_kernel(const Mf128Args a) {
-    __shared__ BwdLds sm;
+__global__ void __launch_bounds__(NT) chain_kernel(const Mf128Args a) {
+    __shared__ ChainLds smb[2];
+    __shared__ float dut[NW][W][GP];   // each wave's du, [token][row], for its Grams
     constexpr uint32_t ES = sizeof(In<DT>);
     const int ul = blockIdx.x;
     const int sl = ul / a.H_v, h = ul % a.H_v;
     const int64_t s = a.s_base + sl;
     const int hk = h % a.H_k;
     const int L = a.lens[sl];
-    const int C = a.C;
     const int64_t unit = s * a.H_v + h;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, lm = lane & 15, g4 = lane >> 4;
-    const int j0 = 16 * wv, i0 = 16 * wv;   // rows (row layout) and columns (column layout) of the wave
+    const int j0 = 16 * wv;
     const int ci = tid & (S - 1), tg = __builtin_amdgcn_readfirstlane(tid >> 7);   // staging: column/row ci, tokens 4 tg .. 4 tg + 3
     const int nblk = (a.T + W - 1) / W;
     const int G = a.kda ? S : 1;
     const float scale = a.scale;
-    const bool kda = a.kda != 0;
-    // during replays: the delta [row][token] in the space of sgy and ee, and the state handed from
-    // one replay step to the next in the space of xt (each lane reads back only what it wrote)
-    float (*dl)[KP] = reinterpret_cast<float (*)[KP]>(&sm.sgy[0][0]);
-    float *lst = &sm.xt[0][0];
-    // bases of this (sequence, head) and byte strides per token
     const float *cin = a.cbuf + (s * a.T * a.H_v + h) * (int64_t)G;
     const In<DT> *kin = tin<DT>(a.k) + s * a.sk.seq + hk * a.sk.head;
     const In<DT> *qin = tin<DT>(a.q) + s * a.sq.seq + hk * a.sq.head;
@@ -697,47 +641,14 @@ __global__ void __launch_bounds__(NT) bwd_mf_kernel(const Mf128Args a) {
     const int64_t row0 = s * a.T * a.H_v + h;   // per-token workspace row of token 0; stride H_v
     const float *ein = a.ebuf + row0 * S;
     float *dvout = a.dv + row0 * S;
-    float *dqout = (a.dq_part ? a.dq_part : a.dq) + row0 * S;   // direct when H_v == H_k
-    float *dkout = (a.dk_part ? a.dk_part : a.dk) + row0 * S;
-    float *dgout = a.dg + row0 * G;
     float *dbout = a.dbeta + row0;
-    const bool vec_out = (((uintptr_t)dqout | (uintptr_t)dkout | (uintptr_t)dgout) & 15) == 0;
+    float *xsave = a.xbuf + unit * (int64_t)nblk * (S * S);
+    float *g1u = a.g1buf + (s * nblk * a.H_v + h) * (int64_t)(W * W);   // block b at b H_v W^2
+    float *g2u = a.g2buf + (s * nblk * a.H_v + h) * (int64_t)(W * W);
     const uint32_t ct = (uint32_t)(a.H_v * G) * 4, kt = (uint32_t)a.sk.tok * ES, qt = (uint32_t)a.sq.tok * ES,
                    gyt = (uint32_t)a.sgy.tok * ES, bt = (uint32_t)a.sb.tok * ES, et = (uint32_t)a.H_v * S * 4;
-    const uint32_t ccol = (kda ? (uint32_t)ci : 0u) * 4;
+    const uint32_t ccol = (a.kda ? (uint32_t)ci : 0u) * 4;
 
-    // the column layout in memory (row-major [S][S]): one vector offset per lane, the row block
-    // and register in the scalar offset
-    const uint32_t vcol = ((4 * g4) * S + i0 + lm) * 4;
-    auto load_cols = [&](const float *base, f4 (&Mc)[8]) {
-        const Rsrc rs = rsrc(base);
-#pragma unroll
-        for (int jb = 0; jb < 8; ++jb)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) Mc[jb][r] = bldf(rs, vcol + r * S * 4, 16 * jb * S * 4);
-    };
-    auto save_cols = [&](float *base, const f4 (&Mc)[8]) {
-        const Rsrc rs = rsrc(base);
-#pragma unroll
-        for (int jb = 0; jb < 8; ++jb)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) bst(rs, Mc[jb][r], vcol + r * S * 4, 16 * jb * S * 4);
-    };
-
-    auto save_lds = [&](const f4 (&Mc)[8]) {
-#pragma unroll
-        for (int jb = 0; jb < 8; ++jb)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) lst[(4 * jb + r) * NT + tid] = Mc[jb][r];
-    };
-    auto load_lds = [&](f4 (&Mc)[8]) {
-#pragma unroll
-        for (int jb = 0; jb < 8; ++jb)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) Mc[jb][r] = lst[(4 * jb + r) * NT + tid];
-    };
-
-    // the gradient in the row layout
     f4 X[8];
     if (a.dstate_out) {
         const float *p = a.dstate_out + unit * S * S + (int64_t)(j0 + lm) * S + 4 * g4;
@@ -747,14 +658,13 @@ __global__ void __launch_bounds__(NT) bwd_mf_kernel(const Mf128Args a) {
 #pragma unroll
         for (int ib = 0; ib < 8; ++ib) X[ib] = zero4();
     }
-    // the dg recursion's carry per column (tile layout: column i0 + 4(l/16) + r)
-    f4 carry = zero4();
 
-    // inputs of a block, loaded one step ahead: column (and row) ci at tokens 4 tg .. + 3 of c,
-    // k, q, gy, e and beta; one entry each of Bm, Tb and G1
+    // inputs of a block, loaded one block ahead: column (and row) ci at tokens 4 tg .. + 3 of c,
+    // k, q, gy, e and beta (tokens past the end load the last one, replaced when staged); one
+    // entry each of Bm and Tb
     struct Pre {
         float c[4], k[4], q[4], gy[4], e[4], b[4];
-        float m0, m1, m2;
+        float m0, m1;
         int dir;
     };
     auto prefetch = [&](Pre &P, int t0) {
@@ -764,157 +674,85 @@ __global__ void __launch_bounds__(NT) bwd_mf_kernel(const Mf128Args a) {
         const Rsrc rc = rsrc(cin + (int64_t)t0 * (a.H_v * G)), rk = rsrc(kin + (int64_t)t0 * a.sk.tok),
                    rq = rsrc(qin + (int64_t)t0 * a.sq.tok), rgy = rsrc(gyin + (int64_t)t0 * a.sgy.tok),
                    re = rsrc(ein + (int64_t)t0 * (a.H_v * S)), rb = rsrc(bin + (int64_t)t0 * a.sb.tok),
-                   rw = rsrc(a.wmat + bi * MATF), rg1 = rsrc(a.g1buf + bi * (W * W));
+                   rw = rsrc(a.wmat + bi * MATF);
 #pragma unroll
         for (int x = 0; x < 4; ++x) {
-            const uint32_t tt = 4 * tg + x;
-            const bool ok = (int)tt < cnt;
-            P.c[x] = ok ? bldf(rc, ccol, tt * ct) : 1.f;
-            P.k[x] = ok ? bld<DT>(rk, ci * ES, tt * kt) : 0.f;
-            P.q[x] = ok ? bld<DT>(rq, ci * ES, tt * qt) : 0.f;
-            P.gy[x] = ok ? bld<DT>(rgy, ci * ES, tt * gyt) : 0.f;
-            P.e[x] = ok ? bldf(re, ci * 4, tt * et) : 0.f;
-            P.b[x] = ok ? bld<DT>(rb, 0, tt * bt) : 0.f;
+            const uint32_t tt = (uint32_t)min(4 * tg + x, cnt - 1);
+            P.c[x] = bldf(rc, ccol, tt * ct);
+            P.k[x] = bld<DT>(rk, ci * ES, tt * kt);
+            P.q[x] = bld<DT>(rq, ci * ES, tt * qt);
+            P.gy[x] = bld<DT>(rgy, ci * ES, tt * gyt);
+            P.e[x] = bldf(re, ci * 4, tt * et);
+            P.b[x] = bld<DT>(rb, 0, tt * bt);
         }
         const uint32_t m = tid & 255;
         P.m0 = bldf(rw, m * 4, 0);                  // Bm
         P.m1 = bldf(rw, (2 * W * W + m) * 4, 0);    // Tb
-        P.m2 = bldf(rg1, m * 4, 0);                 // G1
     };
-    // staging of a column-scaled block for a walk
-    auto stage_walk = [&](const Pre &P, int cnt) {
-        float kr[4], qc[4], kc[4];
+    // staging of a column-scaled block
+    auto stage = [&](ChainLds &sm, const Pre &P, int cnt) {
+        float qc[4], kc[4];
 #pragma unroll
         for (int x = 0; x < 4; ++x) {
             const int tt = 4 * tg + x;
-            const float c = P.c[x];
-            kr[x] = P.k[x] * rcp(c);
-            qc[x] = P.q[x] * c;
-            kc[x] = P.k[x] * c;
-            sm.krT[tt][ci] = kr[x];
-            sm.sgy[tt][ci] = scale * P.gy[x];
-            sm.ee[tt][ci] = P.b[x] * P.e[x];   // delta
-            sm.du[tt][ci] = P.e[x];            // e, until the walk replaces it by du
+            const bool ok = tt < cnt;   // tokens past the end: c = 1 and zeros
+            const float c = ok ? P.c[x] : 1.f, k = ok ? P.k[x] : 0.f;
+            qc[x] = ok ? P.q[x] * c : 0.f;
+            kc[x] = k * c;
+            sm.krT[tt][ci] = k * rcp(c);
+            sm.sgy[tt][ci] = ok ? scale * P.gy[x] : 0.f;
+            sm.er[tt][ci] = ok ? P.e[x] : 0.f;
             if (tt == cnt - 1) sm.pv[ci] = c;
-            if (ci == 0) sm.bt[tt] = P.b[x];
+            if (ci == 0) sm.bt[tt] = ok ? P.b[x] : 0.f;
         }
-        st4(&sm.krI[ci][4 * tg], f4{kr[0], kr[1], kr[2], kr[3]});
         st4(&sm.qcI[ci][4 * tg], f4{qc[0], qc[1], qc[2], qc[3]});
         st4(&sm.kcI[ci][4 * tg], f4{kc[0], kc[1], kc[2], kc[3]});
         if (tid < 256) {
             (&sm.bm[0][0])[tid] = P.m0;
             (&sm.tb[0][0])[tid] = P.m1;
-            sm.g1[tid >> 4][tid & 15] = (tid >> 4) <= (tid & 15) ? P.m2 : 0.f;   // s <= t
         }
-        __syncthreads();
-    };
-    // staging of a column-scaled block for a replay: k./c and delta [row][token]
-    auto stage_replay = [&](const Pre &P, int cnt) {
-        float kr[4], d[4];
-#pragma unroll
-        for (int x = 0; x < 4; ++x) {
-            const int tt = 4 * tg + x;
-            kr[x] = P.k[x] * rcp(P.c[x]);
-            d[x] = P.b[x] * P.e[x];
-            if (tt == cnt - 1) sm.pv[ci] = P.c[x];
-        }
-        st4(&sm.krI[ci][4 * tg], f4{kr[0], kr[1], kr[2], kr[3]});
-        st4(&dl[ci][4 * tg], f4{d[0], d[1], d[2], d[3]});
-        __syncthreads();
     };
     // staging of token t0 + tau of a token-by-token block (loaded directly) as a one-token block
     // with c = 1, the token's gates in pv
-    auto stage_token = [&](int t0, int tau, bool walk) {
+    auto stage_token = [&](ChainLds &sm, int t0, int tau) {
         const int64_t bi = (s * nblk + t0 / W) * a.H_v + h;
-        const Rsrc rc = rsrc(cin + (int64_t)t0 * (a.H_v * G)), rk = rsrc(kin + (int64_t)t0 * a.sk.tok),
-                   rq = rsrc(qin + (int64_t)t0 * a.sq.tok), rgy = rsrc(gyin + (int64_t)t0 * a.sgy.tok),
-                   re = rsrc(ein + (int64_t)t0 * (a.H_v * S)), rb = rsrc(bin + (int64_t)t0 * a.sb.tok);
-        const float av = bldf(rc, ccol + tau * ct, 0);
-        const float kx = bld<DT>(rk, ci * ES + tau * kt, 0);
-        const float ex = bldf(re, ci * 4 + tau * et, 0);
-        const float bx = bld<DT>(rb, tau * bt, 0);
+        const int64_t t = t0 + tau;
+        const float av = cin[t * (a.H_v * G) + (a.kda ? ci : 0)];
+        const float kx = (float)kin[t * a.sk.tok + ci];
+        const float qx = (float)qin[t * a.sq.tok + ci];
+        const float gx = scale * (float)gyin[t * a.sgy.tok + ci];
+        const float ex = ein[t * (a.H_v * S) + ci];
+        const float bx = (float)bin[t * a.sb.tok];
         const f4 k4 = f4{tg == 0 ? kx : 0.f, 0.f, 0.f, 0.f};
-        st4(&sm.krI[ci][4 * tg], k4);
+        st4(&sm.qcI[ci][4 * tg], f4{tg == 0 ? qx : 0.f, 0.f, 0.f, 0.f});
+        st4(&sm.kcI[ci][4 * tg], k4);
         if (tg == 0) sm.pv[ci] = av;
-        if (!walk) {
-            st4(&dl[ci][4 * tg], f4{tg == 0 ? bx * ex : 0.f, 0.f, 0.f, 0.f});
-        } else {
-            const float qx = bld<DT>(rq, ci * ES + tau * qt, 0);
-            const float gx = scale * bld<DT>(rgy, ci * ES + tau * gyt, 0);
-            st4(&sm.qcI[ci][4 * tg], f4{tg == 0 ? qx : 0.f, 0.f, 0.f, 0.f});
-            st4(&sm.kcI[ci][4 * tg], k4);
 #pragma unroll
-            for (int x = 0; x < 4; ++x) {
-                const int tt = 4 * tg + x;
-                sm.krT[tt][ci] = tt == 0 ? kx : 0.f;
-                sm.sgy[tt][ci] = tt == 0 ? gx : 0.f;
-                sm.ee[tt][ci] = tt == 0 ? bx * ex : 0.f;
-                sm.du[tt][ci] = tt == 0 ? ex : 0.f;
-                if (ci == 0) sm.bt[tt] = tt == 0 ? bx : 0.f;
-            }
-            if (tid < 256) {
-                const int sg = tid >> 4, t2 = tid & 15;
-                const float *wm = a.wmat + bi * MATF;
-                const float *g1b = a.g1buf + bi * (W * W);
-                sm.bm[sg][t2] = (sg == 0 && t2 == 0) ? wm[tau * (W + 1)] : 0.f;
-                sm.tb[sg][t2] = sg == t2 ? 1.f : 0.f;
-                sm.g1[sg][t2] = (sg == 0 && t2 == 0) ? g1b[tau * (W + 1)] : 0.f;
-            }
+        for (int x = 0; x < 4; ++x) {
+            const int tt = 4 * tg + x;
+            sm.krT[tt][ci] = tt == 0 ? kx : 0.f;
+            sm.sgy[tt][ci] = tt == 0 ? gx : 0.f;
+            sm.er[tt][ci] = tt == 0 ? ex : 0.f;
+            if (ci == 0) sm.bt[tt] = tt == 0 ? bx : 0.f;
         }
-        __syncthreads();
+        if (tid < 256) {
+            const int sg = tid >> 4, t2 = tid & 15;
+            sm.bm[sg][t2] = (sg == 0 && t2 == 0) ? a.wmat[bi * MATF + tau * (W + 1)] : 0.f;
+            sm.tb[sg][t2] = sg == t2 ? 1.f : 0.f;
+        }
     };
 
-    // ---- replay of a staged (sub)block in the column layout (dir: the token's gates scale the
-    // state first; otherwise the block product folds in at the end)
-    auto replay = [&](f4 (&Mr)[8], bool dir) {
-        const float p = sm.pv[i0 + lm];
-        if (dir) {
+    // ---- one step of the chain on a staged (sub)block of n tokens from tw: the fold and X'
+    // (saved to xs when given), then, once the next block's inputs are in flight, the rest
+    auto fold = [&](const ChainLds &sm, float *xs) {
 #pragma unroll
-            for (int jb = 0; jb < 8; ++jb) Mr[jb] *= p;
-        }
-        const f4 kb = ld4(&sm.krI[i0 + lm][4 * g4]);
+        for (int ib = 0; ib < 8; ++ib) X[ib] *= ld4(&sm.pv[16 * ib + 4 * g4]);
+        if (xs) {
 #pragma unroll
-        for (int jb = 0; jb < 8; ++jb) {
-            const f4 d4 = ld4(&dl[16 * jb + lm][4 * g4]);
-#pragma unroll
-            for (int x = 0; x < 4; ++x) Mr[jb] = mfma(d4[x], kb[x], Mr[jb]);
-        }
-        if (!dir) {
-#pragma unroll
-            for (int jb = 0; jb < 8; ++jb) Mr[jb] *= p;
+            for (int ib = 0; ib < 8; ++ib) st4(xs + (8 * wv + ib) * 256 + lm * 16 + 4 * g4, X[ib]);
         }
     };
-    // the column sums of Z .* Mr over all rows for column i0 + l%16, Z in the column layout read
-    // from memory (row-major [S][S])
-    auto colsum_mem = [&](const float *Z, const f4 (&Mr)[8]) {
-        const Rsrc rz = rsrc(Z);
-        float v = 0.f;
-#pragma unroll
-        for (int jb = 0; jb < 8; ++jb)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) v = fmaf(bldf(rz, vcol + r * S * 4, 16 * jb * S * 4), Mr[jb][r], v);
-        return rows4_sum(v);
-    };
-    // a value per column i0 + l%16 into the tile layout (column i0 + 4(l/16) + r)
-    auto to_tile = [&](float v) {
-        f4 o;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) o[r] = __shfl(v, 4 * g4 + r);
-        return o;
-    };
-
-    // ---- walk of a staged (sub)block with start state Mb (column layout); n tokens from tw.
-    auto walk = [&](const f4 (&Mb)[8], int tw, int n, bool dir) {
-        // ---- phase A.  Chain: X' = X diag(P), its transpose for the column sums, dd0^T = KR X'^T,
-        // dd^T = Tb (dd0^T + Bm sgy^T), du = -beta dd, dv and the dbeta partials.
-        if (!dir) {
-#pragma unroll
-            for (int ib = 0; ib < 8; ++ib) X[ib] *= ld4(&sm.pv[16 * ib + 4 * g4]);
-        }
-#pragma unroll
-        for (int ib = 0; ib < 8; ++ib)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) sm.xt[16 * ib + 4 * g4 + r][j0 + lm] = X[ib][r];
+    auto step = [&](ChainLds &sm, int tw, int n, bool dir) {
         f4 d0 = zero4(), d1 = zero4();
 #pragma unroll
         for (int ib = 0; ib < 8; ib += 2) {
@@ -948,101 +786,13 @@ __global__ void __launch_bounds__(NT) bwd_mf_kernel(const Mf128Args a) {
                 const int tt = 4 * g4 + r;
                 const float bv = sm.bt[tt];
                 duv[r] = -bv * dd[r];
-                const float pbv = row16_sum(dd[r] * sm.du[tt][j0 + lm]);   // e, read before du replaces it
-                sm.du[tt][j0 + lm] = duv[r];
+                const float pbv = row16_sum(dd[r] * sm.er[tt][j0 + lm]);
                 if (lm == 0) sm.pb[wv][tt] = pbv;
                 if (tt < n) bst(rdv, bv * dd[r], (j0 + lm) * 4 + tt * et, 0);
+                dut[wv][tt][lm] = duv[r];
             }
         }
-        // Column part: P1 = M^T sgy against the block start (dq's dense part); its share of dg at
-        // the block's first token; then P1 += KR^T (G1 masked s <= t).
-        f4 p1, dgacc;
-        {
-            f4 pa = zero4(), pb = zero4();
-#pragma unroll
-            for (int jb = 0; jb < 8; jb += 2) {
-                const f4 b0 = ld4(&sm.sgy[lm][16 * jb + 4 * g4]), b1 = ld4(&sm.sgy[lm][16 * jb + 16 + 4 * g4]);
-#pragma unroll
-                for (int x = 0; x < 4; ++x) {
-                    pa = mfma(Mb[jb][x], b0[x], pa);
-                    pb = mfma(Mb[jb + 1][x], b1[x], pb);
-                }
-            }
-            p1 = pa + pb;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) dgacc[r] = sm.qcI[i0 + 4 * g4 + r][lm] * p1[r];
-            const f4 kr4 = ld4(&sm.krI[i0 + lm][4 * g4]);
-#pragma unroll
-            for (int x = 0; x < 4; ++x) p1 = mfma(kr4[x], sm.g1[4 * g4 + x][lm], p1);
-        }
-        __syncthreads();   // X' transposed, du, dbeta partials
-        // ---- phase B.  Column part: P3 = X'^T delta, P2 = M^T du, the G2 partial over the wave's
-        // rows, the column sums of X' .* M.  Chain: X = X' + sgy qc^T + du kc^T.
-        f4 p3, p2, dg0;
-        {
-            f4 p3a = zero4(), p3b = zero4(), p2a = zero4(), p2b = zero4();
-            float xa = 0.f, xb = 0.f;
-#pragma unroll
-            for (int jb = 0; jb < 8; jb += 2) {
-                const f4 x0 = ld4(&sm.xt[i0 + lm][16 * jb + 4 * g4]), x1 = ld4(&sm.xt[i0 + lm][16 * jb + 16 + 4 * g4]);
-                const f4 e0 = ld4(&sm.ee[lm][16 * jb + 4 * g4]), e1 = ld4(&sm.ee[lm][16 * jb + 16 + 4 * g4]);
-                const f4 u0 = ld4(&sm.du[lm][16 * jb + 4 * g4]), u1 = ld4(&sm.du[lm][16 * jb + 16 + 4 * g4]);
-#pragma unroll
-                for (int x = 0; x < 4; ++x) {
-                    p3a = mfma(x0[x], e0[x], p3a);
-                    p3b = mfma(x1[x], e1[x], p3b);
-                    p2a = mfma(Mb[jb][x], u0[x], p2a);
-                    p2b = mfma(Mb[jb + 1][x], u1[x], p2b);
-                    xa = fmaf(x0[x], Mb[jb][x], xa);
-                    xb = fmaf(x1[x], Mb[jb + 1][x], xb);
-                }
-            }
-            p3 = p3a + p3b;
-            p2 = p2a + p2b;
-            // dg at the block's first token: the column sums of X .* M with X after the update,
-            // = sum(X' .* M) + sum_t (qc_t P1 + kc_t P2) over the dense parts
-            const f4 xm4 = to_tile(rows4_sum(xa + xb));
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                dg0[r] = xm4[r] + row16_sum(dgacc[r] + sm.kcI[i0 + 4 * g4 + r][lm] * p2[r]);
-            const f4 qc4 = ld4(&sm.qcI[i0 + lm][4 * g4]);
-#pragma unroll
-            for (int x = 0; x < 4; ++x) p3 = mfma(qc4[x], sm.g1[lm][4 * g4 + x], p3);   // QC^T (G1^T, s >= t)
-        }
-        {   // G2 partial over rows 16 w ..: delta^T (row s = l%16) times du (column t = l%16)
-            const f4 e4 = ld4(&sm.ee[lm][j0 + 4 * g4]), u4 = ld4(&sm.du[lm][j0 + 4 * g4]);
-            f4 g2p = zero4();
-#pragma unroll
-            for (int x = 0; x < 4; ++x) g2p = mfma(e4[x], u4[x], g2p);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) g2p[r] = 4 * g4 + r < lm ? g2p[r] : 0.f;   // s < t
-#pragma unroll
-            for (int r = 0; r < 4; ++r) sm.gp[wv][4 * g4 + r][lm] = g2p[r];
-            st4(&sm.gpt[wv][lm][4 * g4], g2p);
-        }
-        if (wv == 0 && lane < W) {   // dbeta: the eight row-block partials in order
-            float b = 0.f;
-#pragma unroll
-            for (int w2 = 0; w2 < NW; ++w2) b += sm.pb[w2][lane];
-            if (lane < n) dbout[(int64_t)(tw + lane) * a.H_v] = b;
-        }
-        __syncthreads();   // G2 partials
-        // ---- phase C.  The G2 corrections, outputs, the dg recursion.
-        {
-            f4 g2v = zero4(), g2t = zero4();   // G2[4(l/16) + r][l%16] and G2[l%16][4(l/16) + r]
-#pragma unroll
-            for (int w2 = 0; w2 < NW; ++w2) {
-                g2v += ld4(&sm.gpt[w2][lm][4 * g4]);
-                g2t += ld4(&sm.gp[w2][lm][4 * g4]);
-            }
-            const f4 kr4 = ld4(&sm.krI[i0 + lm][4 * g4]), kc4 = ld4(&sm.kcI[i0 + lm][4 * g4]);
-#pragma unroll
-            for (int x = 0; x < 4; ++x) {
-                p3 = mfma(kc4[x], g2t[x], p3);    // KC^T (G2^T, s > t)
-                p2 = mfma(kr4[x], g2v[x], p2);    // KR^T (G2, s < t)
-            }
-        }
-        // the chain: X = X' + sgy qc^T + du kc^T
+        // X = X' + sgy qc^T + du kc^T
 #pragma unroll
         for (int ib = 0; ib < 8; ++ib) {
             const f4 qa = ld4(&sm.qcI[16 * ib + lm][4 * g4]), ka = ld4(&sm.kcI[16 * ib + lm][4 * g4]);
@@ -1052,18 +802,415 @@ __global__ void __launch_bounds__(NT) bwd_mf_kernel(const Mf128Args a) {
                 X[ib] = mfma(ka[x], duv[x], X[ib]);
             }
         }
-        // dq = c P1, dk = P3 / c + c P2, dg increments q.*dq - k.*(P3 / c) + k.*(c P2)
-        f4 cv = f4{1.f, 1.f, 1.f, 1.f};
-        if (!dir) {
-            const float *cp = cin + (int64_t)(tw + (lm < n ? lm : 0)) * (a.H_v * G);
+        // the Grams over the wave's rows: delta^T (row s = l%16, the wave's rows along the
+        // contraction) times scale gy and du (column t = l%16)
+        {
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+            const f4 e4 = ld4(&sm.er[lm][j0 + 4 * g4]) * sm.bt[lm];
+            const f4 y4 = ld4(&sm.sgy[lm][j0 + 4 * g4]), u4 = ld4(&dut[wv][lm][4 * g4]);
+            f4 q1 = zero4(), q2 = zero4();
 #pragma unroll
-            for (int r = 0; r < 4; ++r) cv[r] = cp[kda ? i0 + 4 * g4 + r : 0];
+            for (int x = 0; x < 4; ++x) {
+                q1 = mfma(e4[x], y4[x], q1);
+                q2 = mfma(e4[x], u4[x], q2);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                sm.p1[wv][4 * g4 + r][lm] = q1[r];
+                sm.p2[wv][4 * g4 + r][lm] = q2[r];
+            }
         }
+        if (dir) {   // the gradient before the token's gates
+#pragma unroll
+            for (int ib = 0; ib < 8; ++ib) X[ib] *= ld4(&sm.pv[16 * ib + 4 * g4]);
+        }
+    };
+    // the previous step's dbeta and Grams: the eight per-wave partials in order, once every wave
+    // has passed the barrier after this step's staging
+    int pend_t0 = 0, pend_tau = -1, pend_n = 0;
+    auto flush = [&](const ChainLds &sp) {
+        if (pend_n == 0) return;
+        if (wv == 0 && lane < pend_n) {
+            float b = 0.f;
+#pragma unroll
+            for (int w2 = 0; w2 < NW; ++w2) b += sp.pb[w2][lane];
+            dbout[(int64_t)(pend_t0 + (pend_tau < 0 ? lane : pend_tau)) * a.H_v] = b;
+        }
+        const int e = tid & 255, sr = e >> 4, tc = e & 15;
+        const int64_t gb = (int64_t)(pend_t0 / W) * a.H_v * (W * W);
+        if (pend_tau < 0) {   // G1 keeps s <= t, G2 s < t
+            float g = 0.f;
+            if (tid < 256) {
+#pragma unroll
+                for (int w2 = 0; w2 < NW; ++w2) g += sp.p1[w2][sr][tc];
+                g1u[gb + e] = sr <= tc ? g : 0.f;
+            } else {
+#pragma unroll
+                for (int w2 = 0; w2 < NW; ++w2) g += sp.p2[w2][sr][tc];
+                g2u[gb + e] = sr < tc ? g : 0.f;
+            }
+        } else if (tid == 0) {   // a one-token block: its G1 on the diagonal
+            float g = 0.f;
+#pragma unroll
+            for (int w2 = 0; w2 < NW; ++w2) g += sp.p1[w2][0][0];
+            g1u[gb + pend_tau * (W + 1)] = g;
+        }
+    };
+
+    Pre P;
+    const int nb = (L + W - 1) / W;
+    int cur = 0;
+    if (nb > 0) prefetch(P, (nb - 1) * W);
+    for (int b = nb - 1; b >= 0; --b) {
+        const int t0 = b * W, cnt = min(W, L - t0);
+        const bool dir = P.dir != 0;
+        float *xs = xsave + (int64_t)b * (S * S);
+        if (!dir) {
+            stage(smb[cur], P, cnt);
+            __syncthreads();
+            flush(smb[cur ^ 1]);
+            fold(smb[cur], xs);
+            if (b > 0) prefetch(P, t0 - W);   // after the stores of X', which its wait then covers
+            step(smb[cur], t0, cnt, false);
+            pend_t0 = t0;
+            pend_tau = -1;
+            pend_n = cnt;
+            cur ^= 1;
+        } else {
+            if (b > 0) prefetch(P, t0 - W);
+            for (int u = 0; u < cnt; ++u) {
+                const int tau = cnt - 1 - u;
+                stage_token(smb[cur], t0, tau);
+                __syncthreads();
+                flush(smb[cur ^ 1]);
+                if (u == 0) {   // X' of the block: the gradient after its last token
+#pragma unroll
+                    for (int ib = 0; ib < 8; ++ib) st4(xs + (8 * wv + ib) * 256 + lm * 16 + 4 * g4, X[ib]);
+                }
+                step(smb[cur], t0 + tau, 1, true);
+                pend_t0 = t0;
+                pend_tau = tau;
+                pend_n = 1;
+                cur ^= 1;
+            }
+        }
+    }
+    __syncthreads();
+    flush(smb[cur ^ 1]);
+    {   // the gradient before token 0
+        float *p = a.dstate + unit * S * S + (int64_t)(j0 + lm) * S + 4 * g4;
+#pragma unroll
+        for (int ib = 0; ib < 8; ++ib)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) p[16 * ib + r] = X[ib][r];
+    }
+    for (int64_t idx = tid; idx < (int64_t)(a.T - L) * S; idx += NT) {   // padded tokens
+        const int64_t row = (int64_t)(L + idx / S) * a.H_v;
+        const int i = (int)(idx % S);
+        dvout[row * S + i] = 0.f;
+        if (i == 0) dbout[row] = 0.f;
+    }
+}
+
+struct alignas(16) ColLds {
+    float krI[S][KP];          // k./c        [column][token]; token by token: q and k of the gradient's update
+    float qcI[S][KP];          // c.*q        [column][token]
+    float kcI[S][KP];          // c.*k        [column][token]
+    float cI[S][KP];           // c           [column][token]
+    float dl[S][KP];           // delta       [row][token]; token by token: scale gy and du of the update
+    float sgy[W][SP];          // scale gy    [token][row]
+    float ee[W][SP];           // delta       [token][row]
+    float du[W][SP];           // du          [token][row]
+    float pv[S];               // fold factor per column (a token's gates)
+    float g1[W][GP];           // G1 = delta^T scale gy, [s][t], s <= t
+    float g2[W][GP];           // G2 = delta^T du, [s][t], s < t
+    float g2t[W][GP];          // G2 transposed
+    float gs[NW][W];           // per-wave partial sums of the scalar gate's dg
+};
+
+template <int DT>
+__global__ void __launch_bounds__(NT) colsum_kernel(const Mf128Args a) {
+    __shared__ ColLds smb[2];
+    constexpr uint32_t ES = sizeof(In<DT>);
+    const int units = a.n_seqs_launch * a.H_v;
+    const int ul = blockIdx.x % units, sg = blockIdx.x / units;
+    const int sl = ul / a.H_v, h = ul % a.H_v;
+    const int64_t s = a.s_base + sl;
+    const int hk = h % a.H_k;
+    const int L = a.lens[sl];
+    const int C = a.C;
+    const int64_t unit = s * a.H_v + h;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, lm = lane & 15, g4 = lane >> 4;
+    const int i0 = 16 * wv;   // the wave's columns
+    const int ci = tid & (S - 1), tg = __builtin_amdgcn_readfirstlane(tid >> 7);   // staging: column/row ci, tokens 4 tg .. 4 tg + 3
+    const int nblk = (a.T + W - 1) / W;
+    const int G = a.kda ? S : 1;
+    const float scale = a.scale;
+    const bool kda = a.kda != 0;
+    const float *cin = a.cbuf + (s * a.T * a.H_v + h) * (int64_t)G;
+    const In<DT> *kin = tin<DT>(a.k) + s * a.sk.seq + hk * a.sk.head;
+    const In<DT> *qin = tin<DT>(a.q) + s * a.sq.seq + hk * a.sq.head;
+    const In<DT> *gyin = tin<DT>(a.gy) + s * a.sgy.seq + h * a.sgy.head;
+    const In<DT> *bin = tin<DT>(a.beta) + s * a.sb.seq + h * a.sb.head;
+    const int64_t row0 = s * a.T * a.H_v + h;   // per-token workspace row of token 0; stride H_v
+    const float *ein = a.ebuf + row0 * S;
+    const float *dvin = a.dv + row0 * S;
+    float *dqout = (a.dq_part ? a.dq_part : a.dq) + row0 * S;   // direct when H_v == H_k
+    float *dkout = (a.dk_part ? a.dk_part : a.dk) + row0 * S;
+    float *dgout = a.dg + row0 * G;
+    const bool vec_out = (((uintptr_t)dqout | (uintptr_t)dkout | (uintptr_t)dgout) & 15) == 0;
+    const uint32_t ct = (uint32_t)(a.H_v * G) * 4, kt = (uint32_t)a.sk.tok * ES, qt = (uint32_t)a.sq.tok * ES,
+                   gyt = (uint32_t)a.sgy.tok * ES, bt = (uint32_t)a.sb.tok * ES, et = (uint32_t)a.H_v * S * 4;
+    const uint32_t ccol = (kda ? (uint32_t)ci : 0u) * 4;
+
+    {   // padded tokens of the segment's span
+        const int64_t p0 = max((int64_t)L, (int64_t)sg * C), p1 = min((int64_t)a.T, (int64_t)sg * C + C);
+        for (int64_t idx = tid; idx < (p1 - p0) * S; idx += NT) {
+            const int64_t row = (p0 + idx / S) * a.H_v;
+            const int i = (int)(idx % S);
+            dqout[row * S + i] = 0.f;
+            dkout[row * S + i] = 0.f;
+            if (kda) dgout[row * S + i] = 0.f;
+            else if (i == 0) dgout[row] = 0.f;
+        }
+    }
+    const int ts = sg * C;
+    if (ts >= L) return;
+    const int nb = (min(ts + C, L) - ts + W - 1) / W;
+
+    // a 128 x 128 matrix in the column layout: row-major [S][S] (the snapshots) or tile-major (X')
+    const uint32_t vcol = ((4 * g4) * S + i0 + lm) * 4;
+    auto load_cols = [&](const float *base, f4 (&Mc)[8]) {
+        const Rsrc rs = rsrc(base);
+#pragma unroll
+        for (int jb = 0; jb < 8; ++jb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) Mc[jb][r] = bldf(rs, vcol + r * S * 4, 16 * jb * S * 4);
+    };
+    const uint32_t vtile = (wv * 256 + 4 * g4 * 16 + lm) * 4;
+    auto load_tiles = [&](const float *base, f4 (&Xc)[8]) {
+        const Rsrc rs = rsrc(base);
+#pragma unroll
+        for (int jb = 0; jb < 8; ++jb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) Xc[jb][r] = bldf(rs, vtile + r * 16 * 4, jb * 8 * 256 * 4);
+    };
+    // a value per column i0 + l%16 into the tile layout (column i0 + 4(l/16) + r)
+    auto to_tile = [&](float v) {
+        f4 o;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) o[r] = __shfl(v, 4 * g4 + r);
+        return o;
+    };
+
+    // inputs of a block, loaded one block ahead: column (and row) ci at tokens 4 tg .. + 3 of c,
+    // k, q, gy, e, beta and dv (tokens past the end load the last one, replaced when staged);
+    // one entry each of G1 and G2
+    struct Pre {
+        float c[4], k[4], q[4], gy[4], e[4], b[4], dv[4];
+        float m1, m2;
+        int dir;
+    };
+    auto prefetch = [&](Pre &P, int t0) {
+        const int cnt = min(W, L - t0);
+        const int64_t bi = (s * nblk + t0 / W) * a.H_v + h;
+        P.dir = sload(a.wflag, bi);
+        const Rsrc rc = rsrc(cin + (int64_t)t0 * (a.H_v * G)), rk = rsrc(kin + (int64_t)t0 * a.sk.tok),
+                   rq = rsrc(qin + (int64_t)t0 * a.sq.tok), rgy = rsrc(gyin + (int64_t)t0 * a.sgy.tok),
+                   re = rsrc(ein + (int64_t)t0 * (a.H_v * S)), rb = rsrc(bin + (int64_t)t0 * a.sb.tok),
+                   rdv = rsrc(dvin + (int64_t)t0 * (a.H_v * S));
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+            const uint32_t tt = (uint32_t)min(4 * tg + x, cnt - 1);
+            P.c[x] = bldf(rc, ccol, tt * ct);
+            P.k[x] = bld<DT>(rk, ci * ES, tt * kt);
+            P.q[x] = bld<DT>(rq, ci * ES, tt * qt);
+            P.gy[x] = bld<DT>(rgy, ci * ES, tt * gyt);
+            P.e[x] = bldf(re, ci * 4, tt * et);
+            P.b[x] = bld<DT>(rb, 0, tt * bt);
+            P.dv[x] = bldf(rdv, ci * 4, tt * et);
+        }
+        const int64_t gb = bi * (W * W) + (tid & 255);
+        P.m1 = a.g1buf[gb];
+        P.m2 = a.g2buf[gb];
+    };
+    auto stage = [&](ColLds &sm, const Pre &P, int cnt) {
+        float kr[4], qc[4], kc[4], d[4], cc[4];
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+            const int tt = 4 * tg + x;
+            const bool ok = tt < cnt;   // tokens past the end: c = 1 and zeros
+            const float c = ok ? P.c[x] : 1.f, k = ok ? P.k[x] : 0.f;
+            cc[x] = c;
+            kr[x] = k * rcp(c);
+            qc[x] = ok ? P.q[x] * c : 0.f;
+            kc[x] = k * c;
+            d[x] = ok ? P.b[x] * P.e[x] : 0.f;
+            sm.sgy[tt][ci] = ok ? scale * P.gy[x] : 0.f;
+            sm.ee[tt][ci] = d[x];
+            sm.du[tt][ci] = ok ? -P.dv[x] : 0.f;
+            if (tt == cnt - 1) sm.pv[ci] = c;
+        }
+        st4(&sm.krI[ci][4 * tg], f4{kr[0], kr[1], kr[2], kr[3]});
+        st4(&sm.qcI[ci][4 * tg], f4{qc[0], qc[1], qc[2], qc[3]});
+        st4(&sm.kcI[ci][4 * tg], f4{kc[0], kc[1], kc[2], kc[3]});
+        st4(&sm.cI[ci][4 * tg], f4{cc[0], cc[1], cc[2], cc[3]});
+        st4(&sm.dl[ci][4 * tg], f4{d[0], d[1], d[2], d[3]});
+        if (tid < 256) {
+            sm.g1[tid >> 4][tid & 15] = P.m1;
+            sm.g2[tid >> 4][tid & 15] = P.m2;
+            sm.g2t[tid & 15][tid >> 4] = P.m2;
+        }
+    };
+    // token t0 + tau of a token-by-token block as a one-token block with c = 1 (loaded directly)
+    auto stage_token = [&](ColLds &sm, int t0, int tau) {
+        const int64_t bi = (s * nblk + t0 / W) * a.H_v + h;
+        const int64_t t = t0 + tau;
+        const float av = cin[t * (a.H_v * G) + (kda ? ci : 0)];
+        const float kx = (float)kin[t * a.sk.tok + ci];
+        const float qx = (float)qin[t * a.sq.tok + ci];
+        const float gx = scale * (float)gyin[t * a.sgy.tok + ci];
+        const float dx = (float)bin[t * a.sb.tok] * ein[t * (a.H_v * S) + ci];
+        const float ux = -dvin[t * (a.H_v * S) + ci];
+        const bool z = tg == 0;
+        st4(&sm.krI[ci][4 * tg], f4{z ? kx : 0.f, 0.f, 0.f, 0.f});
+        st4(&sm.qcI[ci][4 * tg], f4{z ? qx : 0.f, 0.f, 0.f, 0.f});
+        st4(&sm.kcI[ci][4 * tg], f4{z ? kx : 0.f, 0.f, 0.f, 0.f});
+        st4(&sm.cI[ci][4 * tg], f4{1.f, 1.f, 1.f, 1.f});
+        st4(&sm.dl[ci][4 * tg], f4{z ? dx : 0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+            const int tt = 4 * tg + x;
+            sm.sgy[tt][ci] = tt == 0 ? gx : 0.f;
+            sm.ee[tt][ci] = tt == 0 ? dx : 0.f;
+            sm.du[tt][ci] = tt == 0 ? ux : 0.f;
+        }
+        if (z) sm.pv[ci] = av;
+        if (tid < 256) {
+            const int sr = tid >> 4, t2 = tid & 15;
+            sm.g1[sr][t2] = (sr == 0 && t2 == 0) ? a.g1buf[bi * (W * W) + tau * (W + 1)] : 0.f;
+            sm.g2[sr][t2] = 0.f;
+            sm.g2t[sr][t2] = 0.f;
+        }
+    };
+    // token t0 + tau of a token-by-token block as the operands of the gradient's update: rows
+    // (scale gy, du) against columns (q, k), the token's gates in pv
+    auto stage_update = [&](ColLds &sm, int t0, int tau) {
+        const int64_t t = t0 + tau;
+        const float av = cin[t * (a.H_v * G) + (kda ? ci : 0)];
+        const bool z = tg == 0;
+        const float gx = z ? scale * (float)gyin[t * a.sgy.tok + ci] : 0.f;
+        const float ux = z ? -dvin[t * (a.H_v * S) + ci] : 0.f;
+        const float qx = z ? (float)qin[t * a.sq.tok + ci] : 0.f;
+        const float kx = z ? (float)kin[t * a.sk.tok + ci] : 0.f;
+        st4(&sm.dl[ci][4 * tg], f4{gx, ux, 0.f, 0.f});
+        st4(&sm.krI[ci][4 * tg], f4{qx, kx, 0.f, 0.f});
+        if (z) sm.pv[ci] = av;
+    };
+    // Z += A B^T over the staged token slots for the column layout: A = dl [row][slot], B = krI
+    // [column][slot]
+    auto rank_update = [&](const ColLds &sm, f4 (&Z)[8]) {
+        const f4 kb = ld4(&sm.krI[i0 + lm][4 * g4]);
+#pragma unroll
+        for (int jb = 0; jb < 8; ++jb) {
+            const f4 d4 = ld4(&sm.dl[16 * jb + lm][4 * g4]);
+#pragma unroll
+            for (int x = 0; x < 4; ++x) Z[jb] = mfma(d4[x], kb[x], Z[jb]);
+        }
+    };
+
+    // ---- the column sums of a staged (sub)block of n tokens from tw with start state M and
+    // gradient X' at its end (column layout); then the state's replay to the block's end (dir: the
+    // token's gates have scaled M already; otherwise the block product folds in at the end)
+    f4 M[8];
+    auto block = [&](ColLds &sm, const f4 (&Xc)[8], int tw, int n, bool dir) {
+        // P1 = M^T sgy (dq's dense part); its share of dg at the block's first token; P1 += KR^T G1
+        f4 p1, dgacc, p2, p3, dg0;
+        {
+            f4 pa = zero4(), pb = zero4();
+#pragma unroll
+            for (int jb = 0; jb < 8; jb += 2) {
+                const f4 b0 = ld4(&sm.sgy[lm][16 * jb + 4 * g4]), b1 = ld4(&sm.sgy[lm][16 * jb + 16 + 4 * g4]);
+#pragma unroll
+                for (int x = 0; x < 4; ++x) {
+                    pa = mfma(M[jb][x], b0[x], pa);
+                    pb = mfma(M[jb + 1][x], b1[x], pb);
+                }
+            }
+            p1 = pa + pb;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) dgacc[r] = sm.qcI[i0 + 4 * g4 + r][lm] * p1[r];
+            const f4 kr4 = ld4(&sm.krI[i0 + lm][4 * g4]);
+#pragma unroll
+            for (int x = 0; x < 4; ++x) p1 = mfma(kr4[x], sm.g1[4 * g4 + x][lm], p1);
+        }
+        // P2 = M^T du; then, with X' (loaded last), P3 = X'^T delta and the column sums of X' .* M
+        {
+            f4 p2a = zero4(), p2b = zero4();
+#pragma unroll
+            for (int jb = 0; jb < 8; jb += 2) {
+                const f4 u0 = ld4(&sm.du[lm][16 * jb + 4 * g4]), u1 = ld4(&sm.du[lm][16 * jb + 16 + 4 * g4]);
+#pragma unroll
+                for (int x = 0; x < 4; ++x) {
+                    p2a = mfma(M[jb][x], u0[x], p2a);
+                    p2b = mfma(M[jb + 1][x], u1[x], p2b);
+                }
+            }
+            p2 = p2a + p2b;
+            f4 p3a = zero4(), p3b = zero4();
+            float xa = 0.f, xb = 0.f;
+#pragma unroll
+            for (int jb = 0; jb < 8; jb += 2) {
+                const f4 e0 = ld4(&sm.ee[lm][16 * jb + 4 * g4]), e1 = ld4(&sm.ee[lm][16 * jb + 16 + 4 * g4]);
+#pragma unroll
+                for (int x = 0; x < 4; ++x) {
+                    p3a = mfma(Xc[jb][x], e0[x], p3a);
+                    p3b = mfma(Xc[jb + 1][x], e1[x], p3b);
+                    xa = fmaf(Xc[jb][x], M[jb][x], xa);
+                    xb = fmaf(Xc[jb + 1][x], M[jb + 1][x], xb);
+                }
+            }
+            p3 = p3a + p3b;
+            // dg at the block's first token: the column sums of X .* M with X after the update,
+            // = sum(X' .* M) + sum_t (qc_t P1 + kc_t P2) over the dense parts
+            const f4 xm4 = to_tile(rows4_sum(xa + xb));
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                dg0[r] = xm4[r] + row16_sum(dgacc[r] + sm.kcI[i0 + 4 * g4 + r][lm] * p2[r]);
+            const f4 qc4 = ld4(&sm.qcI[i0 + lm][4 * g4]), kr4 = ld4(&sm.krI[i0 + lm][4 * g4]),
+                     kc4 = ld4(&sm.kcI[i0 + lm][4 * g4]);
+            const f4 g1t = f4{sm.g1[lm][4 * g4], sm.g1[lm][4 * g4 + 1], sm.g1[lm][4 * g4 + 2], sm.g1[lm][4 * g4 + 3]};
+            const f4 g2v = ld4(&sm.g2t[lm][4 * g4]), g2t = ld4(&sm.g2[lm][4 * g4]);
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                p3 = mfma(qc4[x], g1t[x], p3);    // QC^T (G1^T, s >= t)
+                p3 = mfma(kc4[x], g2t[x], p3);    // KC^T (G2^T, s > t)
+                p2 = mfma(kr4[x], g2v[x], p2);    // KR^T (G2, s < t)
+            }
+        }
+        // the replay: M += delta kr^T; dg after the block = the column sums of X' .* M before the
+        // fold (X' and M carry the block's product inversely)
+        rank_update(sm, M);
+        f4 carry = zero4();
+        if (!dir) {
+            float v = 0.f;
+#pragma unroll
+            for (int jb = 0; jb < 8; ++jb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) v = fmaf(Xc[jb][r], M[jb][r], v);
+            carry = to_tile(rows4_sum(v));
+            const float p = sm.pv[i0 + lm];
+#pragma unroll
+            for (int jb = 0; jb < 8; ++jb) M[jb] *= p;
+        }
+        // dq = c P1, dk = P3 / c + c P2, dg increments q.*dq - k.*(P3 / c) + k.*(c P2)
         f4 dq4, dk4, inc;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int i = i0 + 4 * g4 + r;
-            const float c = cv[r], rc = rcp(c);
+            const float c = sm.cI[i][lm], rc = rcp(c);
             dq4[r] = c * p1[r];
             dk4[r] = fmaf(rc, p3[r], c * p2[r]);
             inc[r] = sm.qcI[i][lm] * p1[r] - sm.krI[i][lm] * p3[r] + sm.kcI[i][lm] * p2[r];
@@ -1080,7 +1227,6 @@ __global__ void __launch_bounds__(NT) bwd_mf_kernel(const Mf128Args a) {
         f4 dgv;
 #pragma unroll
         for (int r = 0; r < 4; ++r) dgv[r] = lm == 0 ? dg0[r] : carry[r] + inc[r];
-        carry = dg0;
         if (lm < n) {
             const int64_t o = (int64_t)(tw + lm) * (a.H_v * S) + i0 + 4 * g4;
             if (vec_out) {
@@ -1100,132 +1246,65 @@ __global__ void __launch_bounds__(NT) bwd_mf_kernel(const Mf128Args a) {
             const float gsv = rows4_sum(dgv[0] + dgv[1] + dgv[2] + dgv[3]);
             if (g4 == 0) sm.gs[wv][lm] = gsv;
         }
-        if (dir) {   // the gradient before the token's gates
-#pragma unroll
-            for (int ib = 0; ib < 8; ++ib) X[ib] *= ld4(&sm.pv[16 * ib + 4 * g4]);
-        }
-        __syncthreads();   // row data and scratch are free for the next staging
-        if (!kda && wv == 0 && lane < n) {
+    };
+    // the scalar gate's dg of the previous step: the eight per-wave sums in order, once every
+    // wave has passed the barrier after this step's staging
+    int pend_tw = 0, pend_n = 0;
+    auto flush = [&](const ColLds &sp) {
+        if (!kda && wv == 0 && lane < pend_n) {
             float g = 0.f;
 #pragma unroll
-            for (int w2 = 0; w2 < NW; ++w2) g += sm.gs[w2][lane];
-            dgout[(int64_t)(tw + lane) * a.H_v] = g;
+            for (int w2 = 0; w2 < NW; ++w2) g += sp.gs[w2][lane];
+            dgout[(int64_t)(pend_tw + lane) * a.H_v] = g;
         }
     };
 
-    // ---- the step sequence
-    const float *snapu = a.snap + unit * a.n_ck_max * S * S;
-    float *bsb = a.vsbuf + unit * (int64_t)a.nbs * (S * S);   // block starts of the segment
-    const int n_ck = (L + C - 1) / C;
-    auto seg_nb = [&](int sg) { return (min(sg * C + C, L) - sg * C + W - 1) / W; };
-    auto n_steps = [&](int sg) { return 2 * seg_nb(sg) - 1 + (sg == n_ck - 1 ? 1 : 0); };
-    // step k of segment sg: 0 replay block bb (saving the next block's start), 1 replay the last
-    // block (final state), 2 walk block bb
-    auto step_info = [&](int sg, int k, int &kind, int &bb) {
-        const int nb = seg_nb(sg), fin = sg == n_ck - 1 ? 1 : 0;
-        if (k < nb - 1) {
-            kind = 0;
-            bb = k;
-        } else if (fin && k == nb - 1) {
-            kind = 1;
-            bb = nb - 1;
-        } else {
-            kind = 2;
-            bb = nb - 1 - (k - (nb - 1) - fin);
-        }
-    };
-    auto block_start = [&](int sg, int bb) -> const float * {
-        return bb == 0 ? snapu + (int64_t)sg * S * S : bsb + (int64_t)bb * (S * S);
-    };
-    auto final_sums = [&](const f4 (&Mf)[8]) {   // the dg recursion's start after the last token
-        if (a.dstate_out) carry = to_tile(colsum_mem(a.dstate_out + unit * S * S, Mf));
-    };
-
+    load_cols(a.snap + (unit * a.n_ck_max + sg) * (int64_t)(S * S), M);
     Pre P;
-    f4 M[8];
-    int sg = n_ck - 1, k = 0;
-    if (L > 0) prefetch(P, sg * C);   // the segment's first step handles its block 0
-    while (sg >= 0) {
-        int kind, bb;
-        step_info(sg, k, kind, bb);
-        const int t0 = sg * C + bb * W, cnt = min(W, L - t0);
-        int nsg = sg, nk = k + 1;
-        if (nk == n_steps(sg)) {
-            nsg = sg - 1;
-            nk = 0;
-        }
-        int nt0 = -1;
-        if (nsg >= 0) {
-            int nkind, nbb;
-            step_info(nsg, nk, nkind, nbb);
-            nt0 = nsg * C + nbb * W;
-        }
+    prefetch(P, ts);
+    int cur = 0;
+    for (int bb = 0; bb < nb; ++bb) {
+        const int t0 = ts + bb * W, cnt = min(W, L - t0);
+        const float *xs = a.xbuf + (unit * nblk + t0 / W) * (int64_t)(S * S);
         const bool dir = P.dir != 0;
-        // a column-scaled block is staged from the registers loaded during the previous step,
-        // which then take the next step's inputs
-        if (!dir) {
-            if (kind == 2) stage_walk(P, cnt);
-            else stage_replay(P, cnt);
-        }
-        if (nt0 >= 0) prefetch(P, nt0);
-        if (kind != 2) {
-            // replay: the block as one column-scaled block, or token by token, from the snapshot or
-            // from the state the previous replay step left in LDS
-            if (bb == 0) load_cols(block_start(sg, 0), M);
-            else load_lds(M);
-            const int nsub = dir ? cnt : 1;
-            for (int u = 0; u < nsub; ++u) {
-                if (dir) stage_token(t0, u, false);
-                replay(M, dir);
-                __syncthreads();
-            }
-            if (kind == 0) {
-                save_cols(bsb + (int64_t)(bb + 1) * (S * S), M);   // for the walk of block bb + 1
-                save_lds(M);                                        // for the next replay step
-            } else {
-                final_sums(M);
-            }
-        } else {
-            // walk: the block as one column-scaled block, or its tokens from the last, each from
-            // its own start state replayed from the block start
-            const int nsub = dir ? cnt : 1;
-            for (int u = 0; u < nsub; ++u) {
-                const int tau = cnt - 1 - u;
-                load_cols(block_start(sg, bb), M);
-                if (dir) {
-                    for (int sx = 0; sx < tau; ++sx) {
-                        stage_token(t0, sx, false);
-                        replay(M, true);
-                        __syncthreads();
-                    }
-                    stage_token(t0, tau, true);
+        // a column-scaled block in one step; a token-by-token block one token per step from the
+        // first, the gradient after token tau being X' of the block stepped back over the block's
+        // later tokens
+        const int nsub = dir ? cnt : 1;
+        for (int tau = 0; tau < nsub; ++tau) {
+            ColLds &sm = smb[cur];
+            f4 Xc[8];
+            if (!dir) stage(sm, P, cnt);
+            load_tiles(xs, Xc);   // before the next block's inputs, so its wait leaves them in flight
+            if (tau == 0 && bb + 1 < nb) prefetch(P, t0 + W);
+            if (dir) {
+                for (int u = cnt - 1; u > tau; --u) {
+                    __syncthreads();
+                    stage_update(sm, t0, u);
+                    __syncthreads();
+                    rank_update(sm, Xc);
                     const float p = sm.pv[i0 + lm];
 #pragma unroll
-                    for (int jb = 0; jb < 8; ++jb) M[jb] *= p;
+                    for (int jb = 0; jb < 8; ++jb) Xc[jb] *= p;
                 }
-                walk(M, dir ? t0 + tau : t0, dir ? 1 : cnt, dir);
+                __syncthreads();
+                stage_token(sm, t0, tau);
             }
+            __syncthreads();
+            flush(smb[cur ^ 1]);
+            if (dir) {
+                const float p = sm.pv[i0 + lm];
+#pragma unroll
+                for (int jb = 0; jb < 8; ++jb) M[jb] *= p;
+            }
+            block(sm, Xc, dir ? t0 + tau : t0, dir ? 1 : cnt, dir);
+            pend_tw = dir ? t0 + tau : t0;
+            pend_n = dir ? 1 : cnt;
+            cur ^= 1;
         }
-        sg = nsg;
-        k = nk;
     }
-    {   // the gradient before token 0
-        float *p = a.dstate + unit * S * S + (int64_t)(j0 + lm) * S + 4 * g4;
-#pragma unroll
-        for (int ib = 0; ib < 8; ++ib)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) p[16 * ib + r] = X[ib][r];
-    }
-    for (int64_t idx = tid; idx < (int64_t)(a.T - L) * S; idx += NT) {   // padded tokens
-        const int64_t row = (int64_t)(L + idx / S) * a.H_v;
-        const int i = (int)(idx % S);
-        dvout[row * S + i] = 0.f;
-        dqout[row * S + i] = 0.f;
-        dkout[row * S + i] = 0.f;
-        if (kda) dgout[row * S + i] = 0.f;
-        else if (i == 0) dgout[row] = 0.f;
-        if (i == 0) dbout[row] = 0.f;
-    }
+    __syncthreads();
+    flush(smb[cur ^ 1]);
 }
 
 template <typename Args>
@@ -1250,18 +1329,13 @@ struct FwdK {
     static constexpr auto fn = fwd_mf_kernel<DT>;
 };
 template <int DT>
-struct Gram1K {
-    static constexpr auto fn = gram1_kernel<DT>;
+struct ChainK {
+    static constexpr auto fn = chain_kernel<DT>;
 };
 template <int DT>
-struct BwdK {
-    static constexpr auto fn = bwd_mf_kernel<DT>;
+struct ColK {
+    static constexpr auto fn = colsum_kernel<DT>;
 };
-
-int block_items(const Mf128Args &a) {
-    const int64_t items = (int64_t)a.n_seqs_launch * ((a.T + W - 1) / W) * a.H_v;
-    return (int)std::min<int64_t>(items, 16384);
-}
 
 }  // namespace
 
@@ -1276,9 +1350,9 @@ hipError_t launch_fwd_mf(const Mf128Args &a, hipStream_t st) {
 }
 
 hipError_t launch_bwd_mf(const Mf128Args &a, hipStream_t st) {
-    hipError_t e = launch(pick<Gram1K>(a.dtype), a, block_items(a), 64, st);
-    if (e != hipSuccess) return e;
-    return launch(pick<BwdK>(a.dtype), a, a.n_seqs_launch * a.H_v, NT, st);
+    hipError_t e = launch(pick<ChainK>(a.dtype), a, a.n_seqs_launch * a.H_v, NT, st);
+    if (e == hipSuccess) e = launch(pick<ColK>(a.dtype), a, a.n_seqs_launch * a.H_v * a.n_ck_max, NT, st);
+    return e;
 }
 
 }  // namespace gdn

@@ -54,14 +54,13 @@ def expected_ws(n, T, Hk, Hv, S, C, kda=True):
     if S == 128:                    # matrix-core path, one workgroup per (sequence, head)
         rows = n * T * Hv
         nblk = -(-T // 16)
-        nbs = C // 16
         tot = al(tot + n * nblk * Hv * 3 * 256 * 4)         # block matrices Bm, Te, Tb
         tot = al(tot + n * nblk * Hv * 4)                   # block flags
         tot = al(tot + rows * (S if kda else 1) * 4)        # running gate products
         tot = al(tot + rows * S * 4)                        # prediction errors
         tot = al(tot + n * nblk * Hv * 256 * 4)             # Grams G1
-        if nbs > 1:
-            tot = al(tot + units * nbs * S * S * 4)         # block starts of a segment
+        tot = al(tot + n * nblk * Hv * 256 * 4)             # Grams G2
+        tot = al(tot + units * nblk * S * S * 4)            # state gradient per block
         if Hv != Hk:
             tot = al(tot + rows * S * 4)                    # dq per value head
             tot = al(tot + rows * S * 4)                    # dk per value head
