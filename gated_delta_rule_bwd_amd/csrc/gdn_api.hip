@@ -33,7 +33,8 @@ struct Plan {
     bool s128 = false;   // head size 128: matrix-core kernels
     bool parts = false;  // small heads: dq/dk go through per-value-head partials
     size_t off_snap = 0, off_seg = 0, off_e = 0, off_pq = 0, off_pk = 0;
-    size_t off_wm = 0, off_wf = 0, off_c = 0, off_g1 = 0, off_g2 = 0, off_xs = 0;
+    size_t off_wm = 0, off_wf = 0, off_c = 0, off_g1 = 0, off_g2 = 0, off_dbp = 0, off_xs = 0;
+    int nslab = 1;       // head size 128: row slabs per unit of the forward and the chain
     // half-precision inputs: their fp32 copies, contiguous [n_seqs][T][heads][width] each
     size_t off_in = 0, in_q = 0, in_k = 0, in_v = 0, in_g = 0, in_b = 0, in_gy = 0;
     size_t total = 0;
@@ -100,10 +101,15 @@ Plan make_plan(const gdn_problem *p) {
         off = align_up(off + tok_rows * pl.G * sizeof(float));
         pl.off_e = off;
         off = align_up(off + tok_rows * S * sizeof(float));
-        pl.off_g1 = off;   // Grams G1 and G2 of the blocks
-        off = align_up(off + (size_t)p->n_seqs * nblk * p->H_v * 256 * sizeof(float));
+        // too few units to fill the chip with one workgroup each: the forward and the chain split
+        // every unit's rows into two slabs, whose sums over rows are kept apart
+        pl.nslab = pl.units <= 128 ? 2 : 1;
+        pl.off_g1 = off;   // Grams G1 and G2 of the blocks, per slab
+        off = align_up(off + (size_t)p->n_seqs * nblk * p->H_v * pl.nslab * 256 * sizeof(float));
         pl.off_g2 = off;
-        off = align_up(off + (size_t)p->n_seqs * nblk * p->H_v * 256 * sizeof(float));
+        off = align_up(off + (size_t)p->n_seqs * nblk * p->H_v * pl.nslab * 256 * sizeof(float));
+        pl.off_dbp = off;  // dbeta per slab
+        if (pl.nslab > 1) off = align_up(off + tok_rows * pl.nslab * sizeof(float));
         pl.off_xs = off;   // the state gradient at each block's end
         off = align_up(off + (size_t)pl.units * nblk * S * S * sizeof(float));
         pl.parts = p->H_v != p->H_k;
@@ -210,6 +216,8 @@ gdn::Mf128Args mf_args(const gdn_problem *p, const Plan &pl, void *ws, int s0, i
     a.ebuf = (float *)(w + pl.off_e);
     a.g1buf = (float *)(w + pl.off_g1);
     a.g2buf = (float *)(w + pl.off_g2);
+    a.dbp = (float *)(w + pl.off_dbp);
+    a.nslab = pl.nslab;
     a.xbuf = (float *)(w + pl.off_xs);
     a.dq_part = pl.parts ? (float *)(w + pl.off_pq) : nullptr;
     a.dk_part = pl.parts ? (float *)(w + pl.off_pk) : nullptr;

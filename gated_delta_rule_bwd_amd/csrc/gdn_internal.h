@@ -113,14 +113,16 @@ struct Mf128Args {
     float *cbuf;            // [n_seqs][T][H_v][G] running gate product c within the token's
                             // block (the gates a themselves in a token-by-token block)
     float *ebuf;            // [n_seqs][T][H_v][S] prediction errors e = v - u
-    float *g1buf;           // [n_seqs][nblk][H_v][16][16] Grams G1 = delta^T (scale gy), s <= t,
-    float *g2buf;           // and G2 = delta^T du, s < t, over the rows of each block
+    float *g1buf;           // [n_seqs][nblk][H_v][nslab][16][16] Grams G1 = delta^T (scale gy),
+    float *g2buf;           // s <= t, and G2 = delta^T du, s < t, over each slab's rows of a block
+    float *dbp;             // [n_seqs][T][H_v][nslab] dbeta per slab (nslab > 1)
     float *xbuf;            // [unit][nblk][S][S] the state gradient at each block's end, folded
                             // into the block's column scaling (tile-major 16 x 16 tiles)
     float *dq_part, *dk_part;   // [n_seqs][T][H_v][S] per value head (null: H_v == H_k, direct)
     float *dq, *dk, *dv, *dg, *dbeta, *dstate;
     gdn_strides sq, sk, sv, sg, sb, sgy, sy;
     int32_t s_base, n_seqs_launch, T, H_k, H_v, C, n_ck_max, kda, dtype;
+    int32_t nslab;          // row slabs per unit of the forward and the chain: 1 or 2
     float scale;
     int32_t lens[kMaxSeqsPerLaunch];
 };

@@ -51,6 +51,10 @@ constexpr float kLo = 0x1p-60f, kHi = 0x1p60f;
 constexpr int SP = S + 4;      // [token][column] LDS rows
 constexpr int KP = W + 4;      // [column][token] LDS rows
 constexpr int MATF = 3 * W * W;   // floats of block matrices: Bm, Te, Tb
+// [column][token] LDS arrays with the token quads of a column rotated by bits 4-5 of the column,
+// so that writes of four columns of one token spread over the banks; a quad stays contiguous
+__device__ __forceinline__ int cti(int col, int t) { return col * KP + 4 * ((t >> 2) ^ ((col >> 4) & 3)) + (t & 3); }
+__device__ __forceinline__ int ctq(int col, int q) { return col * KP + 4 * (q ^ ((col >> 4) & 3)); }
 
 typedef float f4 __attribute__((ext_vector_type(4)));
 
@@ -145,6 +149,18 @@ __device__ __forceinline__ f4 bld4(Rsrc r, uint32_t vbytes) {
         return o;
     }
 }
+// four consecutive elements at byte offset o: one vector load when every row start is aligned
+// to four elements, else four loads
+template <int DT>
+__device__ __forceinline__ f4 ld4v(Rsrc r, uint32_t o, bool vec) {
+    constexpr uint32_t ES = sizeof(In<DT>);
+    if (vec) return bld4<DT>(r, o);
+    return f4{bld<DT>(r, o, 0), bld<DT>(r, o + ES, 0), bld<DT>(r, o + 2 * ES, 0), bld<DT>(r, o + 3 * ES, 0)};
+}
+__device__ __forceinline__ bool rows_aligned(const void *p, const gdn_strides &st, uint32_t es) {
+    return (((uintptr_t)p & (4 * es - 1)) == 0) && st.seq % 4 == 0 && st.tok % 4 == 0 && st.head % 4 == 0;
+}
+
 // A wave-uniform 32-bit value read through the constant address space, so it takes a scalar
 // load (its wait does not drain the vector memory counter).  Only for data no kernel of the
 // same launch writes.
@@ -184,7 +200,7 @@ template <int DT>
 __global__ void __launch_bounds__(64 * PW) prep128_kernel(const Mf128Args a) {
     __shared__ float trs[PW][W][W + 1];   // per-wave transposes
     constexpr uint32_t ES = sizeof(In<DT>);
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, lm = lane & 15, g4 = lane >> 4;
+    const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lm = lane & 15, g4 = lane >> 4;
     float (*tr)[W + 1] = trs[wv];
     const int nblk = (a.T + W - 1) / W;
     const int G = a.kda ? S : 1;
@@ -344,33 +360,36 @@ __global__ void __launch_bounds__(64 * PW) prep128_kernel(const Mf128Args a) {
 
 // ------------------------------------------------------------------ forward scan
 
-constexpr int NW = 8;          // waves per workgroup, 16 rows each
-constexpr int NT = 64 * NW;    // threads per workgroup
+constexpr int NW = 8;          // waves per workgroup of the column pass, 16 rows (columns) each
+constexpr int NT = 64 * NW;    // its threads
 
-// A workgroup owns a unit (sequence, value head).  Wave w holds rows 16 w .. 16 w + 15 of the
-// state transposed as eight 16 x 16 tiles: tile ib, lane l, register r holds
-// M[16 w + l%16][16 ib + 4(l/16) + r].  Thread tid stages column tid % 128 of tokens
-// 4 (tid / 128) .. + 3 of a block; the next block's inputs are loaded into registers while the
-// current block is computed.
+// A workgroup owns R = 16 NWC rows of a unit (sequence, value head): all 128 (NWC = 8), or one of
+// two halves when the launch has too few units to fill the chip with whole units (the rows of
+// the state evolve independently).  Wave w holds rows j0 = R slab + 16 w .. + 15 of the state
+// transposed as eight 16 x 16 tiles: tile ib, lane l, register r holds
+// M[j0 + l%16][16 ib + 4(l/16) + r].  Thread tid stages column tid % 128 of tokens
+// TPT (tid / 128) .. + TPT - 1 of a block; the next block's inputs are loaded into registers while
+// the current block is computed.
 struct alignas(16) FwdLds {
     float kc[W][SP], qc[W][SP];   // c.*k, c.*q   [token][column]
     float kr[S][KP];              // k./c         [column][token]
     float pv[S];                  // block product per column (a token's gates)
 };
 
-template <int DT>
-__global__ void __launch_bounds__(NT) fwd_mf_kernel(const Mf128Args a) {
+template <int DT, int NWC>
+__global__ void __launch_bounds__(64 * NWC) fwd_mf_kernel(const Mf128Args a) {
+    constexpr int NTC = 64 * NWC, NSL = NW / NWC, TPT = W * S / NTC;
     __shared__ FwdLds smb[2];   // staged blocks, alternately (one barrier per block)
     constexpr uint32_t ES = sizeof(In<DT>);
-    const int ul = blockIdx.x;
+    const int ul = blockIdx.x / NSL, slab = blockIdx.x % NSL;
     const int sl = ul / a.H_v, h = ul % a.H_v;
     const int64_t s = a.s_base + sl;
     const int hk = h % a.H_k;
     const int L = a.lens[sl];
     const int64_t unit = s * a.H_v + h;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, lm = lane & 15, g4 = lane >> 4;
-    const int j0 = wv * 16;
-    const int ci = tid & (S - 1), tg = __builtin_amdgcn_readfirstlane(tid >> 7);   // staging: column ci, tokens 4 tg .. 4 tg + 3
+    const int j0 = 16 * (NWC * slab + wv);
+    const int ci = tid & (S - 1), tg = __builtin_amdgcn_readfirstlane(tid >> 7);   // staging: column ci, tokens TPT tg ..
     const int nblk = (a.T + W - 1) / W;
     const int G = a.kda ? S : 1;
     const bool vec_state = (((uintptr_t)a.state0 | (uintptr_t)a.state_out) & 15) == 0;
@@ -402,10 +421,11 @@ __global__ void __launch_bounds__(NT) fwd_mf_kernel(const Mf128Args a) {
     };
     float *snap = a.snap + unit * a.n_ck_max * S * S;
 
-    // inputs of one block: column ci of c, k, q at tokens 4 tg .. + 3; per lane v and beta at
-    // (token 4(l/16) + r, row 16 w + l%16) and the operands of Te^T and Bm^T
+    // inputs of one block: column ci of c, k, q at tokens TPT tg .. (tokens past the end load the
+    // last one, replaced when staged); per lane v and beta at (token 4(l/16) + r, row j0 + l%16)
+    // and the operands of Te^T and Bm^T
     struct Pre {
-        float c[4], k[4], q[4];
+        float c[TPT], k[TPT], q[TPT];
         float v[4], b[4], te[4], bm[4];
         int dir;
     };
@@ -417,21 +437,19 @@ __global__ void __launch_bounds__(NT) fwd_mf_kernel(const Mf128Args a) {
                    rq = rsrc(qin + (int64_t)t0 * a.sq.tok), rv = rsrc(vin + (int64_t)t0 * a.sv.tok),
                    rb = rsrc(bin + (int64_t)t0 * a.sb.tok), rw = rsrc(a.wmat + bi * MATF);
 #pragma unroll
-        for (int x = 0; x < 4; ++x) {
-            const uint32_t tt = 4 * tg + x;
-            const bool ok = (int)tt < cnt;
-            P.c[x] = ok ? bldf(rc, ccol, tt * ct) : 1.f;
-            P.k[x] = ok ? bld<DT>(rk, ci * ES, tt * kt) : 0.f;
-            P.q[x] = ok ? bld<DT>(rq, ci * ES, tt * qt) : 0.f;
+        for (int x = 0; x < TPT; ++x) {
+            const uint32_t tt = (uint32_t)min(TPT * tg + x, cnt - 1);
+            P.c[x] = bldf(rc, ccol, tt * ct);
+            P.k[x] = bld<DT>(rk, ci * ES, tt * kt);
+            P.q[x] = bld<DT>(rq, ci * ES, tt * qt);
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const uint32_t tt = 4 * g4 + r;
-            const bool ok = (int)tt < cnt;
-            P.v[r] = ok ? bld<DT>(rv, (j0 + lm) * ES + tt * vt, 0) : 0.f;
-            P.b[r] = ok ? bld<DT>(rb, tt * bt, 0) : 0.f;
-            P.te[r] = bldf(rw, (W * W + tt * W + lm) * 4, 0);
-            P.bm[r] = bldf(rw, (tt * W + lm) * 4, 0);
+            const uint32_t tt = (uint32_t)min(4 * g4 + r, cnt - 1);
+            P.v[r] = bld<DT>(rv, (j0 + lm) * ES + tt * vt, 0);
+            P.b[r] = bld<DT>(rb, tt * bt, 0);
+            P.te[r] = bldf(rw, (W * W + (4 * g4 + r) * W + lm) * 4, 0);
+            P.bm[r] = bldf(rw, ((4 * g4 + r) * W + lm) * 4, 0);
         }
     };
 
@@ -500,18 +518,27 @@ __global__ void __launch_bounds__(NT) fwd_mf_kernel(const Mf128Args a) {
         if (t0 % a.C == 0) store_state(snap + (int64_t)(t0 / a.C) * S * S);
         if (!P.dir) {
             FwdLds &sm = smb[cur];
-            float krow[4];
+            float krow[TPT];
 #pragma unroll
-            for (int x = 0; x < 4; ++x) {
-                const int tt = 4 * tg + x;
-                const float c = P.c[x];
-                krow[x] = P.k[x] * rcp(c);
-                sm.kc[tt][ci] = P.k[x] * c;
-                sm.qc[tt][ci] = P.q[x] * c;
+            for (int x = 0; x < TPT; ++x) {
+                const int tt = TPT * tg + x;
+                const bool ok = tt < cnt;   // tokens past the end: c = 1 and zeros
+                const float c = ok ? P.c[x] : 1.f, k = ok ? P.k[x] : 0.f;
+                krow[x] = k * rcp(c);
+                sm.kc[tt][ci] = k * c;
+                sm.qc[tt][ci] = ok ? P.q[x] * c : 0.f;
                 if (tt == cnt - 1) sm.pv[ci] = c;
             }
-            st4(&sm.kr[ci][4 * tg], f4{krow[0], krow[1], krow[2], krow[3]});
-            const float vv[4] = {P.v[0], P.v[1], P.v[2], P.v[3]}, bb[4] = {P.b[0], P.b[1], P.b[2], P.b[3]};
+#pragma unroll
+            for (int x = 0; x < TPT; x += 4)
+                st4(&sm.kr[ci][TPT * tg + x], f4{krow[x], krow[x + 1], krow[x + 2], krow[x + 3]});
+            float vv[4], bb[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const bool ok = 4 * g4 + r < cnt;
+                vv[r] = ok ? P.v[r] : 0.f;
+                bb[r] = ok ? P.b[r] : 0.f;
+            }
             const float teA[4] = {P.te[0], P.te[1], P.te[2], P.te[3]}, bmA[4] = {P.bm[0], P.bm[1], P.bm[2], P.bm[3]};
             __syncthreads();
             if (t0 + W < L) prefetch(P, t0 + W);   // the registers are free again
@@ -530,12 +557,13 @@ __global__ void __launch_bounds__(NT) fwd_mf_kernel(const Mf128Args a) {
                 const float kx = bld<DT>(rk, ci * ES + tau * kt, 0);
                 const float qx = bld<DT>(rq, ci * ES + tau * qt, 0);
 #pragma unroll
-                for (int x = 0; x < 4; ++x) {
-                    const int tt = 4 * tg + x;
+                for (int x = 0; x < TPT; ++x) {
+                    const int tt = TPT * tg + x;
                     sm.kc[tt][ci] = tt == 0 ? kx : 0.f;
                     sm.qc[tt][ci] = tt == 0 ? qx : 0.f;
                 }
-                st4(&sm.kr[ci][4 * tg], f4{tg == 0 ? kx : 0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+                for (int x = 0; x < TPT; x += 4) st4(&sm.kr[ci][TPT * tg + x], f4{tg == 0 && x == 0 ? kx : 0.f, 0.f, 0.f, 0.f});
                 if (tg == 0) sm.pv[ci] = av;
                 float vv[4], bb[4], teA[4], bmA[4];
 #pragma unroll
@@ -554,10 +582,11 @@ __global__ void __launch_bounds__(NT) fwd_mf_kernel(const Mf128Args a) {
             if (t0 + W < L) prefetch(P, t0 + W);
         }
     }
-    if (yout) {
-        for (int64_t idx = tid; idx < (int64_t)(a.T - L) * S; idx += NT) {
-            const int64_t t = L + idx / S;
-            yout[t * a.sy.tok + (int)(idx % S)] = 0.f;
+    if (yout) {   // padded tokens: the workgroup's rows
+        constexpr int R = 16 * NWC;
+        for (int64_t idx = tid; idx < (int64_t)(a.T - L) * R; idx += NTC) {
+            const int64_t t = L + idx / R;
+            yout[t * a.sy.tok + 16 * NWC * slab + (int)(idx % R)] = 0.f;
         }
     }
     if (a.state_out) {
@@ -602,52 +631,59 @@ __global__ void __launch_bounds__(NT) fwd_mf_kernel(const Mf128Args a) {
 // (dbeta, the Grams, the scalar gate's dg) are summed after the next block's barrier.
 constexpr int GP = W + 4;   // row pitch of the per-wave 16 x 16 partials
 
+template <int NWC>
 struct alignas(16) ChainLds {
+    static constexpr int RP = 16 * NWC + 4;   // row pitch of the workgroup's rows
     float krT[W][SP];          // k./c        [token][column]
-    float sgy[W][SP];          // scale gy    [token][row]
-    float er[W][SP];           // e           [token][row]
+    float sgy[W][RP];          // scale gy    [token][row of the workgroup]
+    float er[W][RP];           // e           [token][row of the workgroup]
     float qcI[S][KP];          // c.*q        [column][token]
     float kcI[S][KP];          // c.*k        [column][token]
     float pv[S];               // fold factor per column (a token's gates)
     float bt[W];               // beta
     float bm[W][W], tb[W][W];  // Bm, Tb
-    float pb[NW][W];           // per-wave partials of dbeta
-    float p1[NW][W][GP];       // per-wave partials of G1 [s][t]
-    float p2[NW][W][GP];       // per-wave partials of G2 [s][t]
+    float pb[NWC][W];          // per-wave partials of dbeta
+    float p1[NWC][W][GP];      // per-wave partials of G1 [s][t]
+    float p2[NWC][W][GP];      // per-wave partials of G2 [s][t]
 };
 
-template <int DT>
-__global__ void __launch_bounds__(NT) chain_kernel(const Mf128Args a) {
-    __shared__ ChainLds smb[2];
-    __shared__ float dut[NW][W][GP];   // each wave's du, [token][row], for its Grams
+// The chain's workgroup owns 16 NWC rows of a unit (all, or one of NSL = 8 / NWC slabs: the rows
+// are independent); its sums over rows (dbeta, G1, G2) are written per slab, and the column pass
+// adds the slabs in order.
+template <int DT, int NWC>
+__global__ void __launch_bounds__(64 * NWC) chain_kernel(const Mf128Args a) {
+    constexpr int NTC = 64 * NWC, NSL = NW / NWC, R = 16 * NWC;
+    __shared__ ChainLds<NWC> smb[2];
+    __shared__ float dut[NWC][W][GP];   // each wave's du, [token][row], for its Grams
     constexpr uint32_t ES = sizeof(In<DT>);
-    const int ul = blockIdx.x;
+    const int ul = blockIdx.x / NSL, slab = blockIdx.x % NSL;
     const int sl = ul / a.H_v, h = ul % a.H_v;
     const int64_t s = a.s_base + sl;
     const int hk = h % a.H_k;
     const int L = a.lens[sl];
     const int64_t unit = s * a.H_v + h;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, lm = lane & 15, g4 = lane >> 4;
-    const int j0 = 16 * wv;
-    const int ci = tid & (S - 1), tg = __builtin_amdgcn_readfirstlane(tid >> 7);   // staging: column/row ci, tokens 4 tg .. 4 tg + 3
+    const int jl = 16 * wv, r0 = R * slab, j0 = r0 + jl;   // the wave's rows: local and in the state
     const int nblk = (a.T + W - 1) / W;
     const int G = a.kda ? S : 1;
+    const int nsl = a.nslab;
     const float scale = a.scale;
     const float *cin = a.cbuf + (s * a.T * a.H_v + h) * (int64_t)G;
     const In<DT> *kin = tin<DT>(a.k) + s * a.sk.seq + hk * a.sk.head;
     const In<DT> *qin = tin<DT>(a.q) + s * a.sq.seq + hk * a.sq.head;
-    const In<DT> *gyin = tin<DT>(a.gy) + s * a.sgy.seq + h * a.sgy.head;
+    const In<DT> *gyin = tin<DT>(a.gy) + s * a.sgy.seq + h * a.sgy.head + r0;
     const In<DT> *bin = tin<DT>(a.beta) + s * a.sb.seq + h * a.sb.head;
     const int64_t row0 = s * a.T * a.H_v + h;   // per-token workspace row of token 0; stride H_v
-    const float *ein = a.ebuf + row0 * S;
+    const float *ein = a.ebuf + row0 * S + r0;
     float *dvout = a.dv + row0 * S;
-    float *dbout = a.dbeta + row0;
+    const bool vec_dv = ((uintptr_t)a.dv & 15) == 0;
+    float *dbout = NSL > 1 ? a.dbp + row0 * nsl + slab : a.dbeta + row0;   // stride H_v nsl per token
+    const int64_t dbt = NSL > 1 ? (int64_t)a.H_v * nsl : a.H_v;
     float *xsave = a.xbuf + unit * (int64_t)nblk * (S * S);
-    float *g1u = a.g1buf + (s * nblk * a.H_v + h) * (int64_t)(W * W);   // block b at b H_v W^2
-    float *g2u = a.g2buf + (s * nblk * a.H_v + h) * (int64_t)(W * W);
+    float *g1u = a.g1buf + ((s * nblk * a.H_v + h) * nsl + slab) * (int64_t)(W * W);   // block b at b H_v nsl W^2
+    float *g2u = a.g2buf + ((s * nblk * a.H_v + h) * nsl + slab) * (int64_t)(W * W);
     const uint32_t ct = (uint32_t)(a.H_v * G) * 4, kt = (uint32_t)a.sk.tok * ES, qt = (uint32_t)a.sq.tok * ES,
                    gyt = (uint32_t)a.sgy.tok * ES, bt = (uint32_t)a.sb.tok * ES, et = (uint32_t)a.H_v * S * 4;
-    const uint32_t ccol = (a.kda ? (uint32_t)ci : 0u) * 4;
 
     f4 X[8];
     if (a.dstate_out) {
@@ -659,11 +695,18 @@ __global__ void __launch_bounds__(NT) chain_kernel(const Mf128Args a) {
         for (int ib = 0; ib < 8; ++ib) X[ib] = zero4();
     }
 
-    // inputs of a block, loaded one block ahead: column (and row) ci at tokens 4 tg .. + 3 of c,
-    // k, q, gy, e and beta (tokens past the end load the last one, replaced when staged); one
-    // entry each of Bm and Tb
+    // inputs of a block, loaded one block ahead (tokens past the end load the last one, replaced
+    // when staged): thread (tk = tid / 32 + v NTC / 32, cg = tid % 32) takes columns 4 cg .. + 3
+    // of token tk of c, k and q and that token's beta; thread (tr, rq) rows 4 rq .. + 3 of the
+    // workgroup at token tr of gy and e; entries of Bm and Tb
+    constexpr int TPV = S * W / (4 * NTC);
+    const int cg = tid & 31, tk0 = tid >> 5;
+    const int rq = tid % (R / 4), tr = tid / (R / 4);
+    const bool vk = rows_aligned(a.k, a.sk, ES), vq = rows_aligned(a.q, a.sq, ES), vgy = rows_aligned(a.gy, a.sgy, ES);
     struct Pre {
-        float c[4], k[4], q[4], gy[4], e[4], b[4];
+        f4 c[TPV], k[TPV], q[TPV];
+        float b[TPV];
+        f4 gy, e;
         float m0, m1;
         int dir;
     };
@@ -672,41 +715,50 @@ __global__ void __launch_bounds__(NT) chain_kernel(const Mf128Args a) {
         const int64_t bi = (s * nblk + t0 / W) * a.H_v + h;
         P.dir = sload(a.wflag, bi);
         const Rsrc rc = rsrc(cin + (int64_t)t0 * (a.H_v * G)), rk = rsrc(kin + (int64_t)t0 * a.sk.tok),
-                   rq = rsrc(qin + (int64_t)t0 * a.sq.tok), rgy = rsrc(gyin + (int64_t)t0 * a.sgy.tok),
+                   rq_ = rsrc(qin + (int64_t)t0 * a.sq.tok), rgy = rsrc(gyin + (int64_t)t0 * a.sgy.tok),
                    re = rsrc(ein + (int64_t)t0 * (a.H_v * S)), rb = rsrc(bin + (int64_t)t0 * a.sb.tok),
                    rw = rsrc(a.wmat + bi * MATF);
 #pragma unroll
-        for (int x = 0; x < 4; ++x) {
-            const uint32_t tt = (uint32_t)min(4 * tg + x, cnt - 1);
-            P.c[x] = bldf(rc, ccol, tt * ct);
-            P.k[x] = bld<DT>(rk, ci * ES, tt * kt);
-            P.q[x] = bld<DT>(rq, ci * ES, tt * qt);
-            P.gy[x] = bld<DT>(rgy, ci * ES, tt * gyt);
-            P.e[x] = bldf(re, ci * 4, tt * et);
-            P.b[x] = bld<DT>(rb, 0, tt * bt);
+        for (int v = 0; v < TPV; ++v) {
+            const uint32_t tt = (uint32_t)min(tk0 + v * (NTC / 32), cnt - 1);
+            if (a.kda) P.c[v] = ld4v<GDN_DTYPE_F32>(rc, tt * ct + 16 * cg, true);
+            else P.c[v] = f4{1.f, 1.f, 1.f, 1.f} * bldf(rc, tt * ct, 0);
+            P.k[v] = ld4v<DT>(rk, tt * kt + 4 * cg * ES, vk);
+            P.q[v] = ld4v<DT>(rq_, tt * qt + 4 * cg * ES, vq);
+            P.b[v] = bld<DT>(rb, tt * bt, 0);
+        }
+        {
+            const uint32_t tt = (uint32_t)min(tr, cnt - 1);
+            P.gy = ld4v<DT>(rgy, tt * gyt + 4 * rq * ES, vgy);
+            P.e = ld4v<GDN_DTYPE_F32>(re, tt * et + 16 * rq, true);
         }
         const uint32_t m = tid & 255;
         P.m0 = bldf(rw, m * 4, 0);                  // Bm
         P.m1 = bldf(rw, (2 * W * W + m) * 4, 0);    // Tb
     };
     // staging of a column-scaled block
-    auto stage = [&](ChainLds &sm, const Pre &P, int cnt) {
-        float qc[4], kc[4];
+    auto stage = [&](ChainLds<NWC> &sm, const Pre &P, int cnt) {
+        float *qcI = &sm.qcI[0][0], *kcI = &sm.kcI[0][0];
 #pragma unroll
-        for (int x = 0; x < 4; ++x) {
-            const int tt = 4 * tg + x;
+        for (int v = 0; v < TPV; ++v) {
+            const int tt = tk0 + v * (NTC / 32);
             const bool ok = tt < cnt;   // tokens past the end: c = 1 and zeros
-            const float c = ok ? P.c[x] : 1.f, k = ok ? P.k[x] : 0.f;
-            qc[x] = ok ? P.q[x] * c : 0.f;
-            kc[x] = k * c;
-            sm.krT[tt][ci] = k * rcp(c);
-            sm.sgy[tt][ci] = ok ? scale * P.gy[x] : 0.f;
-            sm.er[tt][ci] = ok ? P.e[x] : 0.f;
-            if (tt == cnt - 1) sm.pv[ci] = c;
-            if (ci == 0) sm.bt[tt] = ok ? P.b[x] : 0.f;
+            const f4 c = ok ? P.c[v] : f4{1.f, 1.f, 1.f, 1.f}, k = ok ? P.k[v] : zero4();
+            const f4 qc = ok ? P.q[v] * c : zero4(), kc = k * c;
+            st4(&sm.krT[tt][4 * cg], f4{k[0] * rcp(c[0]), k[1] * rcp(c[1]), k[2] * rcp(c[2]), k[3] * rcp(c[3])});
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                qcI[cti(4 * cg + x, tt)] = qc[x];
+                kcI[cti(4 * cg + x, tt)] = kc[x];
+            }
+            if (tt == cnt - 1) st4(&sm.pv[4 * cg], c);
+            if (cg == 0) sm.bt[tt] = ok ? P.b[v] : 0.f;
         }
-        st4(&sm.qcI[ci][4 * tg], f4{qc[0], qc[1], qc[2], qc[3]});
-        st4(&sm.kcI[ci][4 * tg], f4{kc[0], kc[1], kc[2], kc[3]});
+        {
+            const bool ok = tr < cnt;
+            st4(&sm.sgy[tr][4 * rq], ok ? P.gy * scale : zero4());
+            st4(&sm.er[tr][4 * rq], ok ? P.e : zero4());
+        }
         if (tid < 256) {
             (&sm.bm[0][0])[tid] = P.m0;
             (&sm.tb[0][0])[tid] = P.m1;
@@ -714,26 +766,45 @@ __global__ void __launch_bounds__(NT) chain_kernel(const Mf128Args a) {
     };
     // staging of token t0 + tau of a token-by-token block (loaded directly) as a one-token block
     // with c = 1, the token's gates in pv
-    auto stage_token = [&](ChainLds &sm, int t0, int tau) {
+    auto stage_token = [&](ChainLds<NWC> &sm, int t0, int tau) {
         const int64_t bi = (s * nblk + t0 / W) * a.H_v + h;
         const int64_t t = t0 + tau;
-        const float av = cin[t * (a.H_v * G) + (a.kda ? ci : 0)];
-        const float kx = (float)kin[t * a.sk.tok + ci];
-        const float qx = (float)qin[t * a.sq.tok + ci];
-        const float gx = scale * (float)gyin[t * a.sgy.tok + ci];
-        const float ex = ein[t * (a.H_v * S) + ci];
-        const float bx = (float)bin[t * a.sb.tok];
-        const f4 k4 = f4{tg == 0 ? kx : 0.f, 0.f, 0.f, 0.f};
-        st4(&sm.qcI[ci][4 * tg], f4{tg == 0 ? qx : 0.f, 0.f, 0.f, 0.f});
-        st4(&sm.kcI[ci][4 * tg], k4);
-        if (tg == 0) sm.pv[ci] = av;
+        float *qcI = &sm.qcI[0][0], *kcI = &sm.kcI[0][0];
+        const bool z = tk0 == 0;   // threads of token slot 0 load the token; the others zero
 #pragma unroll
-        for (int x = 0; x < 4; ++x) {
-            const int tt = 4 * tg + x;
-            sm.krT[tt][ci] = tt == 0 ? kx : 0.f;
-            sm.sgy[tt][ci] = tt == 0 ? gx : 0.f;
-            sm.er[tt][ci] = tt == 0 ? ex : 0.f;
-            if (ci == 0) sm.bt[tt] = tt == 0 ? bx : 0.f;
+        for (int v = 0; v < TPV; ++v) {
+            const int tt = tk0 + v * (NTC / 32);
+            f4 k = zero4(), q = zero4();
+            if (z && v == 0) {
+#pragma unroll
+                for (int x = 0; x < 4; ++x) {
+                    k[x] = (float)kin[t * a.sk.tok + 4 * cg + x];
+                    q[x] = (float)qin[t * a.sq.tok + 4 * cg + x];
+                }
+                f4 av;
+#pragma unroll
+                for (int x = 0; x < 4; ++x) av[x] = cin[t * (a.H_v * G) + (a.kda ? 4 * cg + x : 0)];
+                st4(&sm.pv[4 * cg], av);
+            }
+            st4(&sm.krT[tt][4 * cg], k);
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                qcI[cti(4 * cg + x, tt)] = q[x];
+                kcI[cti(4 * cg + x, tt)] = k[x];
+            }
+            if (cg == 0) sm.bt[tt] = (z && v == 0) ? (float)bin[t * a.sb.tok] : 0.f;
+        }
+        {
+            f4 gy = zero4(), e = zero4();
+            if (tr == 0) {
+#pragma unroll
+                for (int x = 0; x < 4; ++x) {
+                    gy[x] = scale * (float)gyin[t * a.sgy.tok + 4 * rq + x];
+                    e[x] = ein[t * (a.H_v * S) + 4 * rq + x];
+                }
+            }
+            st4(&sm.sgy[tr][4 * rq], gy);
+            st4(&sm.er[tr][4 * rq], e);
         }
         if (tid < 256) {
             const int sg = tid >> 4, t2 = tid & 15;
@@ -744,15 +815,16 @@ __global__ void __launch_bounds__(NT) chain_kernel(const Mf128Args a) {
 
     // ---- one step of the chain on a staged (sub)block of n tokens from tw: the fold and X'
     // (saved to xs when given), then, once the next block's inputs are in flight, the rest
-    auto fold = [&](const ChainLds &sm, float *xs) {
+    auto save_x = [&](float *xs) {
+#pragma unroll
+        for (int ib = 0; ib < 8; ++ib) st4(xs + ((j0 >> 4) * 8 + ib) * 256 + lm * 16 + 4 * g4, X[ib]);
+    };
+    auto fold = [&](const ChainLds<NWC> &sm, float *xs) {
 #pragma unroll
         for (int ib = 0; ib < 8; ++ib) X[ib] *= ld4(&sm.pv[16 * ib + 4 * g4]);
-        if (xs) {
-#pragma unroll
-            for (int ib = 0; ib < 8; ++ib) st4(xs + (8 * wv + ib) * 256 + lm * 16 + 4 * g4, X[ib]);
-        }
+        save_x(xs);
     };
-    auto step = [&](ChainLds &sm, int tw, int n, bool dir) {
+    auto step = [&](ChainLds<NWC> &sm, int tw, int n, bool dir) {
         f4 d0 = zero4(), d1 = zero4();
 #pragma unroll
         for (int ib = 0; ib < 8; ib += 2) {
@@ -764,9 +836,9 @@ __global__ void __launch_bounds__(NT) chain_kernel(const Mf128Args a) {
             }
         }
         f4 rhs = d0 + d1;
-        float sgB[4];   // sgy^T operand: scale gy at (token 4(l/16) + x, row 16 w + l%16)
+        float sgB[4];   // sgy^T operand: scale gy at (token 4(l/16) + x, row j0 + l%16)
 #pragma unroll
-        for (int x = 0; x < 4; ++x) sgB[x] = sm.sgy[4 * g4 + x][j0 + lm];
+        for (int x = 0; x < 4; ++x) sgB[x] = sm.sgy[4 * g4 + x][jl + lm];
         {
             const f4 bm4 = ld4(&sm.bm[lm][4 * g4]);
 #pragma unroll
@@ -778,24 +850,20 @@ __global__ void __launch_bounds__(NT) chain_kernel(const Mf128Args a) {
 #pragma unroll
             for (int x = 0; x < 4; ++x) dd = mfma(tb4[x], rhs[x], dd);
         }
-        float duv[4];   // du^T (token 4(l/16) + r, row 16 w + l%16), the B operand of the update
-        {
-            const Rsrc rdv = rsrc(dvout + (int64_t)tw * (a.H_v * S));
+        float duv[4];   // du^T (token 4(l/16) + r, row j0 + l%16), the B operand of the update
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int tt = 4 * g4 + r;
-                const float bv = sm.bt[tt];
-                duv[r] = -bv * dd[r];
-                const float pbv = row16_sum(dd[r] * sm.er[tt][j0 + lm]);
-                if (lm == 0) sm.pb[wv][tt] = pbv;
-                if (tt < n) bst(rdv, bv * dd[r], (j0 + lm) * 4 + tt * et, 0);
-                dut[wv][tt][lm] = duv[r];
-            }
+        for (int r = 0; r < 4; ++r) {
+            const int tt = 4 * g4 + r;
+            duv[r] = -sm.bt[tt] * dd[r];
+            const float pbv = row16_sum(dd[r] * sm.er[tt][jl + lm]);
+            if (lm == 0) sm.pb[wv][tt] = pbv;
+            dut[wv][tt][lm] = duv[r];
         }
         // X = X' + sgy qc^T + du kc^T
+        const float *qcI = &sm.qcI[0][0], *kcI = &sm.kcI[0][0];
 #pragma unroll
         for (int ib = 0; ib < 8; ++ib) {
-            const f4 qa = ld4(&sm.qcI[16 * ib + lm][4 * g4]), ka = ld4(&sm.kcI[16 * ib + lm][4 * g4]);
+            const f4 qa = ld4(qcI + ctq(16 * ib + lm, g4)), ka = ld4(kcI + ctq(16 * ib + lm, g4));
 #pragma unroll
             for (int x = 0; x < 4; ++x) {
                 X[ib] = mfma(qa[x], sgB[x], X[ib]);
@@ -808,8 +876,18 @@ __global__ void __launch_bounds__(NT) chain_kernel(const Mf128Args a) {
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-            const f4 e4 = ld4(&sm.er[lm][j0 + 4 * g4]) * sm.bt[lm];
-            const f4 y4 = ld4(&sm.sgy[lm][j0 + 4 * g4]), u4 = ld4(&dut[wv][lm][4 * g4]);
+            const f4 e4 = ld4(&sm.er[lm][jl + 4 * g4]) * sm.bt[lm];
+            const f4 y4 = ld4(&sm.sgy[lm][jl + 4 * g4]), u4 = ld4(&dut[wv][lm][4 * g4]);
+            // dv = beta dd = -du: token l%16, rows j0 + 4(l/16) ..
+            if (lm < n) {
+                float *o = dvout + (int64_t)(tw + lm) * (a.H_v * S) + j0 + 4 * g4;
+                if (vec_dv) {
+                    st4(o, -u4);
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) o[r] = -u4[r];
+                }
+            }
             f4 q1 = zero4(), q2 = zero4();
 #pragma unroll
             for (int x = 0; x < 4; ++x) {
@@ -827,34 +905,36 @@ __global__ void __launch_bounds__(NT) chain_kernel(const Mf128Args a) {
             for (int ib = 0; ib < 8; ++ib) X[ib] *= ld4(&sm.pv[16 * ib + 4 * g4]);
         }
     };
-    // the previous step's dbeta and Grams: the eight per-wave partials in order, once every wave
-    // has passed the barrier after this step's staging
+    // the previous step's dbeta and Grams over the workgroup's rows: the per-wave partials in
+    // order, once every wave has passed the barrier after this step's staging
     int pend_t0 = 0, pend_tau = -1, pend_n = 0;
-    auto flush = [&](const ChainLds &sp) {
+    auto flush = [&](const ChainLds<NWC> &sp) {
         if (pend_n == 0) return;
         if (wv == 0 && lane < pend_n) {
             float b = 0.f;
 #pragma unroll
-            for (int w2 = 0; w2 < NW; ++w2) b += sp.pb[w2][lane];
-            dbout[(int64_t)(pend_t0 + (pend_tau < 0 ? lane : pend_tau)) * a.H_v] = b;
+            for (int w2 = 0; w2 < NWC; ++w2) b += sp.pb[w2][lane];
+            dbout[(int64_t)(pend_t0 + (pend_tau < 0 ? lane : pend_tau)) * dbt] = b;
         }
-        const int e = tid & 255, sr = e >> 4, tc = e & 15;
-        const int64_t gb = (int64_t)(pend_t0 / W) * a.H_v * (W * W);
+        const int64_t gb = (int64_t)(pend_t0 / W) * a.H_v * nsl * (W * W);
         if (pend_tau < 0) {   // G1 keeps s <= t, G2 s < t
-            float g = 0.f;
-            if (tid < 256) {
+            for (int e = tid; e < 2 * W * W; e += NTC) {
+                const int m = e & 255, sr = m >> 4, tc = m & 15;
+                float g = 0.f;
+                if (e < 256) {
 #pragma unroll
-                for (int w2 = 0; w2 < NW; ++w2) g += sp.p1[w2][sr][tc];
-                g1u[gb + e] = sr <= tc ? g : 0.f;
-            } else {
+                    for (int w2 = 0; w2 < NWC; ++w2) g += sp.p1[w2][sr][tc];
+                    g1u[gb + m] = sr <= tc ? g : 0.f;
+                } else {
 #pragma unroll
-                for (int w2 = 0; w2 < NW; ++w2) g += sp.p2[w2][sr][tc];
-                g2u[gb + e] = sr < tc ? g : 0.f;
+                    for (int w2 = 0; w2 < NWC; ++w2) g += sp.p2[w2][sr][tc];
+                    g2u[gb + m] = sr < tc ? g : 0.f;
+                }
             }
         } else if (tid == 0) {   // a one-token block: its G1 on the diagonal
             float g = 0.f;
 #pragma unroll
-            for (int w2 = 0; w2 < NW; ++w2) g += sp.p1[w2][0][0];
+            for (int w2 = 0; w2 < NWC; ++w2) g += sp.p1[w2][0][0];
             g1u[gb + pend_tau * (W + 1)] = g;
         }
     };
@@ -885,10 +965,7 @@ __global__ void __launch_bounds__(NT) chain_kernel(const Mf128Args a) {
                 stage_token(smb[cur], t0, tau);
                 __syncthreads();
                 flush(smb[cur ^ 1]);
-                if (u == 0) {   // X' of the block: the gradient after its last token
-#pragma unroll
-                    for (int ib = 0; ib < 8; ++ib) st4(xs + (8 * wv + ib) * 256 + lm * 16 + 4 * g4, X[ib]);
-                }
+                if (u == 0) save_x(xs);   // X' of the block: the gradient after its last token
                 step(smb[cur], t0 + tau, 1, true);
                 pend_t0 = t0;
                 pend_tau = tau;
@@ -906,11 +983,11 @@ __global__ void __launch_bounds__(NT) chain_kernel(const Mf128Args a) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) p[16 * ib + r] = X[ib][r];
     }
-    for (int64_t idx = tid; idx < (int64_t)(a.T - L) * S; idx += NT) {   // padded tokens
-        const int64_t row = (int64_t)(L + idx / S) * a.H_v;
-        const int i = (int)(idx % S);
-        dvout[row * S + i] = 0.f;
-        if (i == 0) dbout[row] = 0.f;
+    for (int64_t idx = tid; idx < (int64_t)(a.T - L) * R; idx += NTC) {   // padded tokens
+        const int64_t row = (int64_t)(L + idx / R) * a.H_v;
+        const int i = (int)(idx % R);
+        dvout[row * S + r0 + i] = 0.f;
+        if (slab == 0 && i == 0) a.dbeta[row0 + row] = 0.f;
     }
 }
 
@@ -961,9 +1038,10 @@ __global__ void __launch_bounds__(NT) colsum_kernel(const Mf128Args a) {
     float *dkout = (a.dk_part ? a.dk_part : a.dk) + row0 * S;
     float *dgout = a.dg + row0 * G;
     const bool vec_out = (((uintptr_t)dqout | (uintptr_t)dkout | (uintptr_t)dgout) & 15) == 0;
+    const bool vec_dv = ((uintptr_t)a.dv & 15) == 0;
     const uint32_t ct = (uint32_t)(a.H_v * G) * 4, kt = (uint32_t)a.sk.tok * ES, qt = (uint32_t)a.sq.tok * ES,
                    gyt = (uint32_t)a.sgy.tok * ES, bt = (uint32_t)a.sb.tok * ES, et = (uint32_t)a.H_v * S * 4;
-    const uint32_t ccol = (kda ? (uint32_t)ci : 0u) * 4;
+    const int nsl = a.nslab;
 
     {   // padded tokens of the segment's span
         const int64_t p0 = max((int64_t)L, (int64_t)sg * C), p1 = min((int64_t)a.T, (int64_t)sg * C + C);
@@ -979,6 +1057,14 @@ __global__ void __launch_bounds__(NT) colsum_kernel(const Mf128Args a) {
     const int ts = sg * C;
     if (ts >= L) return;
     const int nb = (min(ts + C, L) - ts + W - 1) / W;
+    if (nsl > 1) {   // dbeta of the segment's tokens: the chain's slabs in order
+        for (int t = ts + tid; t < min(ts + C, L); t += NT) {
+            const int64_t r = row0 + (int64_t)t * a.H_v;
+            float b = 0.f;
+            for (int k = 0; k < nsl; ++k) b += a.dbp[r * nsl + k];
+            a.dbeta[r] = b;
+        }
+    }
 
     // a 128 x 128 matrix in the column layout: row-major [S][S] (the snapshots) or tile-major (X')
     const uint32_t vcol = ((4 * g4) * S + i0 + lm) * 4;
@@ -1005,12 +1091,15 @@ __global__ void __launch_bounds__(NT) colsum_kernel(const Mf128Args a) {
         return o;
     };
 
-    // inputs of a block, loaded one block ahead: column (and row) ci at tokens 4 tg .. + 3 of c,
-    // k, q, gy, e, beta and dv (tokens past the end load the last one, replaced when staged);
-    // one entry each of G1 and G2
+    // inputs of a block, loaded one block ahead (tokens past the end load the last one, replaced
+    // when staged): thread (tk = tid / 32, cg = tid % 32) takes columns (rows) 4 cg .. + 3 of token
+    // tk of c, k, q, gy, e and dv and that token's beta; one entry of each slab's G1 and G2
+    const int cg = tid & 31, tk = tid >> 5;
+    const bool vk = rows_aligned(a.k, a.sk, ES), vq = rows_aligned(a.q, a.sq, ES), vgy = rows_aligned(a.gy, a.sgy, ES);
     struct Pre {
-        float c[4], k[4], q[4], gy[4], e[4], b[4], dv[4];
-        float m1, m2;
+        f4 c, k, q, gy, e, dv;
+        float b;
+        float m1[2], m2[2];   // the chain's slabs (at most two)
         int dir;
     };
     auto prefetch = [&](Pre &P, int t0) {
@@ -1021,47 +1110,46 @@ __global__ void __launch_bounds__(NT) colsum_kernel(const Mf128Args a) {
                    rq = rsrc(qin + (int64_t)t0 * a.sq.tok), rgy = rsrc(gyin + (int64_t)t0 * a.sgy.tok),
                    re = rsrc(ein + (int64_t)t0 * (a.H_v * S)), rb = rsrc(bin + (int64_t)t0 * a.sb.tok),
                    rdv = rsrc(dvin + (int64_t)t0 * (a.H_v * S));
+        const uint32_t tt = (uint32_t)min(tk, cnt - 1);
+        if (kda) P.c = ld4v<GDN_DTYPE_F32>(rc, tt * ct + 16 * cg, true);
+        else P.c = f4{1.f, 1.f, 1.f, 1.f} * bldf(rc, tt * ct, 0);
+        P.k = ld4v<DT>(rk, tt * kt + 4 * cg * ES, vk);
+        P.q = ld4v<DT>(rq, tt * qt + 4 * cg * ES, vq);
+        P.gy = ld4v<DT>(rgy, tt * gyt + 4 * cg * ES, vgy);
+        P.e = ld4v<GDN_DTYPE_F32>(re, tt * et + 16 * cg, true);
+        P.dv = ld4v<GDN_DTYPE_F32>(rdv, tt * et + 16 * cg, vec_dv);
+        P.b = bld<DT>(rb, tt * bt, 0);
+        const int64_t gb = bi * nsl * (W * W) + (tid & 255);
 #pragma unroll
-        for (int x = 0; x < 4; ++x) {
-            const uint32_t tt = (uint32_t)min(4 * tg + x, cnt - 1);
-            P.c[x] = bldf(rc, ccol, tt * ct);
-            P.k[x] = bld<DT>(rk, ci * ES, tt * kt);
-            P.q[x] = bld<DT>(rq, ci * ES, tt * qt);
-            P.gy[x] = bld<DT>(rgy, ci * ES, tt * gyt);
-            P.e[x] = bldf(re, ci * 4, tt * et);
-            P.b[x] = bld<DT>(rb, 0, tt * bt);
-            P.dv[x] = bldf(rdv, ci * 4, tt * et);
+        for (int k = 0; k < 2; ++k) {
+            const int64_t o = gb + min(k, nsl - 1) * (W * W);
+            P.m1[k] = a.g1buf[o];
+            P.m2[k] = a.g2buf[o];
         }
-        const int64_t gb = bi * (W * W) + (tid & 255);
-        P.m1 = a.g1buf[gb];
-        P.m2 = a.g2buf[gb];
     };
     auto stage = [&](ColLds &sm, const Pre &P, int cnt) {
-        float kr[4], qc[4], kc[4], d[4], cc[4];
+        const bool ok = tk < cnt;   // tokens past the end: c = 1 and zeros
+        const f4 c = ok ? P.c : f4{1.f, 1.f, 1.f, 1.f}, k = ok ? P.k : zero4();
+        const f4 qc = ok ? P.q * c : zero4(), kc = k * c, d = ok ? P.e * P.b : zero4();
+        float *krI = &sm.krI[0][0], *qcI = &sm.qcI[0][0], *kcI = &sm.kcI[0][0], *cI = &sm.cI[0][0], *dl = &sm.dl[0][0];
 #pragma unroll
         for (int x = 0; x < 4; ++x) {
-            const int tt = 4 * tg + x;
-            const bool ok = tt < cnt;   // tokens past the end: c = 1 and zeros
-            const float c = ok ? P.c[x] : 1.f, k = ok ? P.k[x] : 0.f;
-            cc[x] = c;
-            kr[x] = k * rcp(c);
-            qc[x] = ok ? P.q[x] * c : 0.f;
-            kc[x] = k * c;
-            d[x] = ok ? P.b[x] * P.e[x] : 0.f;
-            sm.sgy[tt][ci] = ok ? scale * P.gy[x] : 0.f;
-            sm.ee[tt][ci] = d[x];
-            sm.du[tt][ci] = ok ? -P.dv[x] : 0.f;
-            if (tt == cnt - 1) sm.pv[ci] = c;
+            const int o = cti(4 * cg + x, tk);
+            krI[o] = k[x] * rcp(c[x]);
+            qcI[o] = qc[x];
+            kcI[o] = kc[x];
+            cI[o] = c[x];
+            dl[o] = d[x];
         }
-        st4(&sm.krI[ci][4 * tg], f4{kr[0], kr[1], kr[2], kr[3]});
-        st4(&sm.qcI[ci][4 * tg], f4{qc[0], qc[1], qc[2], qc[3]});
-        st4(&sm.kcI[ci][4 * tg], f4{kc[0], kc[1], kc[2], kc[3]});
-        st4(&sm.cI[ci][4 * tg], f4{cc[0], cc[1], cc[2], cc[3]});
-        st4(&sm.dl[ci][4 * tg], f4{d[0], d[1], d[2], d[3]});
-        if (tid < 256) {
-            sm.g1[tid >> 4][tid & 15] = P.m1;
-            sm.g2[tid >> 4][tid & 15] = P.m2;
-            sm.g2t[tid & 15][tid >> 4] = P.m2;
+        st4(&sm.sgy[tk][4 * cg], ok ? P.gy * scale : zero4());
+        st4(&sm.ee[tk][4 * cg], d);
+        st4(&sm.du[tk][4 * cg], ok ? -P.dv : zero4());
+        if (tk == cnt - 1) st4(&sm.pv[4 * cg], c);
+        if (tid < 256) {   // the slabs' partials in order
+            const float g1 = nsl > 1 ? P.m1[0] + P.m1[1] : P.m1[0], g2 = nsl > 1 ? P.m2[0] + P.m2[1] : P.m2[0];
+            sm.g1[tid >> 4][tid & 15] = g1;
+            sm.g2[tid >> 4][tid & 15] = g2;
+            sm.g2t[tid & 15][tid >> 4] = g2;
         }
     };
     // token t0 + tau of a token-by-token block as a one-token block with c = 1 (loaded directly)
@@ -1075,11 +1163,11 @@ __global__ void __launch_bounds__(NT) colsum_kernel(const Mf128Args a) {
         const float dx = (float)bin[t * a.sb.tok] * ein[t * (a.H_v * S) + ci];
         const float ux = -dvin[t * (a.H_v * S) + ci];
         const bool z = tg == 0;
-        st4(&sm.krI[ci][4 * tg], f4{z ? kx : 0.f, 0.f, 0.f, 0.f});
-        st4(&sm.qcI[ci][4 * tg], f4{z ? qx : 0.f, 0.f, 0.f, 0.f});
-        st4(&sm.kcI[ci][4 * tg], f4{z ? kx : 0.f, 0.f, 0.f, 0.f});
-        st4(&sm.cI[ci][4 * tg], f4{1.f, 1.f, 1.f, 1.f});
-        st4(&sm.dl[ci][4 * tg], f4{z ? dx : 0.f, 0.f, 0.f, 0.f});
+        st4(&sm.krI[0][0] + ctq(ci, tg), f4{z ? kx : 0.f, 0.f, 0.f, 0.f});
+        st4(&sm.qcI[0][0] + ctq(ci, tg), f4{z ? qx : 0.f, 0.f, 0.f, 0.f});
+        st4(&sm.kcI[0][0] + ctq(ci, tg), f4{z ? kx : 0.f, 0.f, 0.f, 0.f});
+        st4(&sm.cI[0][0] + ctq(ci, tg), f4{1.f, 1.f, 1.f, 1.f});
+        st4(&sm.dl[0][0] + ctq(ci, tg), f4{z ? dx : 0.f, 0.f, 0.f, 0.f});
 #pragma unroll
         for (int x = 0; x < 4; ++x) {
             const int tt = 4 * tg + x;
@@ -1090,7 +1178,10 @@ __global__ void __launch_bounds__(NT) colsum_kernel(const Mf128Args a) {
         if (z) sm.pv[ci] = av;
         if (tid < 256) {
             const int sr = tid >> 4, t2 = tid & 15;
-            sm.g1[sr][t2] = (sr == 0 && t2 == 0) ? a.g1buf[bi * (W * W) + tau * (W + 1)] : 0.f;
+            float g = 0.f;
+            if (sr == 0 && t2 == 0)
+                for (int k = 0; k < nsl; ++k) g += a.g1buf[(bi * nsl + k) * (W * W) + tau * (W + 1)];
+            sm.g1[sr][t2] = g;
             sm.g2[sr][t2] = 0.f;
             sm.g2t[sr][t2] = 0.f;
         }
@@ -1105,17 +1196,17 @@ __global__ void __launch_bounds__(NT) colsum_kernel(const Mf128Args a) {
         const float ux = z ? -dvin[t * (a.H_v * S) + ci] : 0.f;
         const float qx = z ? (float)qin[t * a.sq.tok + ci] : 0.f;
         const float kx = z ? (float)kin[t * a.sk.tok + ci] : 0.f;
-        st4(&sm.dl[ci][4 * tg], f4{gx, ux, 0.f, 0.f});
-        st4(&sm.krI[ci][4 * tg], f4{qx, kx, 0.f, 0.f});
+        st4(&sm.dl[0][0] + ctq(ci, tg), f4{gx, ux, 0.f, 0.f});
+        st4(&sm.krI[0][0] + ctq(ci, tg), f4{qx, kx, 0.f, 0.f});
         if (z) sm.pv[ci] = av;
     };
     // Z += A B^T over the staged token slots for the column layout: A = dl [row][slot], B = krI
     // [column][slot]
     auto rank_update = [&](const ColLds &sm, f4 (&Z)[8]) {
-        const f4 kb = ld4(&sm.krI[i0 + lm][4 * g4]);
+        const f4 kb = ld4(&sm.krI[0][0] + ctq(i0 + lm, g4));
 #pragma unroll
         for (int jb = 0; jb < 8; ++jb) {
-            const f4 d4 = ld4(&sm.dl[16 * jb + lm][4 * g4]);
+            const f4 d4 = ld4(&sm.dl[0][0] + ctq(16 * jb + lm, g4));
 #pragma unroll
             for (int x = 0; x < 4; ++x) Z[jb] = mfma(d4[x], kb[x], Z[jb]);
         }
@@ -1141,8 +1232,8 @@ __global__ void __launch_bounds__(NT) colsum_kernel(const Mf128Args a) {
             }
             p1 = pa + pb;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) dgacc[r] = sm.qcI[i0 + 4 * g4 + r][lm] * p1[r];
-            const f4 kr4 = ld4(&sm.krI[i0 + lm][4 * g4]);
+            for (int r = 0; r < 4; ++r) dgacc[r] = (&sm.qcI[0][0])[cti(i0 + 4 * g4 + r, lm)] * p1[r];
+            const f4 kr4 = ld4(&sm.krI[0][0] + ctq(i0 + lm, g4));
 #pragma unroll
             for (int x = 0; x < 4; ++x) p1 = mfma(kr4[x], sm.g1[4 * g4 + x][lm], p1);
         }
@@ -1178,9 +1269,9 @@ __global__ void __launch_bounds__(NT) colsum_kernel(const Mf128Args a) {
             const f4 xm4 = to_tile(rows4_sum(xa + xb));
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                dg0[r] = xm4[r] + row16_sum(dgacc[r] + sm.kcI[i0 + 4 * g4 + r][lm] * p2[r]);
-            const f4 qc4 = ld4(&sm.qcI[i0 + lm][4 * g4]), kr4 = ld4(&sm.krI[i0 + lm][4 * g4]),
-                     kc4 = ld4(&sm.kcI[i0 + lm][4 * g4]);
+                dg0[r] = xm4[r] + row16_sum(dgacc[r] + (&sm.kcI[0][0])[cti(i0 + 4 * g4 + r, lm)] * p2[r]);
+            const f4 qc4 = ld4(&sm.qcI[0][0] + ctq(i0 + lm, g4)), kr4 = ld4(&sm.krI[0][0] + ctq(i0 + lm, g4)),
+                     kc4 = ld4(&sm.kcI[0][0] + ctq(i0 + lm, g4));
             const f4 g1t = f4{sm.g1[lm][4 * g4], sm.g1[lm][4 * g4 + 1], sm.g1[lm][4 * g4 + 2], sm.g1[lm][4 * g4 + 3]};
             const f4 g2v = ld4(&sm.g2t[lm][4 * g4]), g2t = ld4(&sm.g2[lm][4 * g4]);
 #pragma unroll
@@ -1210,10 +1301,10 @@ __global__ void __launch_bounds__(NT) colsum_kernel(const Mf128Args a) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int i = i0 + 4 * g4 + r;
-            const float c = sm.cI[i][lm], rc = rcp(c);
+            const float c = (&sm.cI[0][0])[cti(i, lm)], rc = rcp(c);
             dq4[r] = c * p1[r];
             dk4[r] = fmaf(rc, p3[r], c * p2[r]);
-            inc[r] = sm.qcI[i][lm] * p1[r] - sm.krI[i][lm] * p3[r] + sm.kcI[i][lm] * p2[r];
+            inc[r] = (&sm.qcI[0][0])[cti(i, lm)] * p1[r] - (&sm.krI[0][0])[cti(i, lm)] * p3[r] + (&sm.kcI[0][0])[cti(i, lm)] * p2[r];
         }
         // suffix sums of the increments over the block's tokens (lanes l%16 upwards)
 #pragma unroll
@@ -1326,11 +1417,19 @@ struct PrepK {
 };
 template <int DT>
 struct FwdK {
-    static constexpr auto fn = fwd_mf_kernel<DT>;
+    static constexpr auto fn = fwd_mf_kernel<DT, NW>;
+};
+template <int DT>
+struct FwdK2 {
+    static constexpr auto fn = fwd_mf_kernel<DT, NW / 2>;
 };
 template <int DT>
 struct ChainK {
-    static constexpr auto fn = chain_kernel<DT>;
+    static constexpr auto fn = chain_kernel<DT, NW>;
+};
+template <int DT>
+struct ChainK2 {
+    static constexpr auto fn = chain_kernel<DT, NW / 2>;
 };
 template <int DT>
 struct ColK {
@@ -1346,11 +1445,15 @@ hipError_t launch_prep128(const Mf128Args &a, hipStream_t st) {
 }
 
 hipError_t launch_fwd_mf(const Mf128Args &a, hipStream_t st) {
-    return launch(pick<FwdK>(a.dtype), a, a.n_seqs_launch * a.H_v, NT, st);
+    const int units = a.n_seqs_launch * a.H_v;
+    if (a.nslab == 2) return launch(pick<FwdK2>(a.dtype), a, 2 * units, NT / 2, st);
+    return launch(pick<FwdK>(a.dtype), a, units, NT, st);
 }
 
 hipError_t launch_bwd_mf(const Mf128Args &a, hipStream_t st) {
-    hipError_t e = launch(pick<ChainK>(a.dtype), a, a.n_seqs_launch * a.H_v, NT, st);
+    const int units = a.n_seqs_launch * a.H_v;
+    hipError_t e = a.nslab == 2 ? launch(pick<ChainK2>(a.dtype), a, 2 * units, NT / 2, st)
+                                : launch(pick<ChainK>(a.dtype), a, units, NT, st);
     if (e == hipSuccess) e = launch(pick<ColK>(a.dtype), a, a.n_seqs_launch * a.H_v * a.n_ck_max, NT, st);
     return e;
 }

@@ -58,8 +58,11 @@ def expected_ws(n, T, Hk, Hv, S, C, kda=True):
         tot = al(tot + n * nblk * Hv * 4)                   # block flags
         tot = al(tot + rows * (S if kda else 1) * 4)        # running gate products
         tot = al(tot + rows * S * 4)                        # prediction errors
-        tot = al(tot + n * nblk * Hv * 256 * 4)             # Grams G1
-        tot = al(tot + n * nblk * Hv * 256 * 4)             # Grams G2
+        nsl = 2 if units <= 128 else 1                      # row slabs of small launches
+        tot = al(tot + n * nblk * Hv * nsl * 256 * 4)       # Grams G1
+        tot = al(tot + n * nblk * Hv * nsl * 256 * 4)       # Grams G2
+        if nsl > 1:
+            tot = al(tot + rows * nsl * 4)                  # dbeta per slab
         tot = al(tot + units * nblk * S * S * 4)            # state gradient per block
         if Hv != Hk:
             tot = al(tot + rows * S * 4)                    # dq per value head
