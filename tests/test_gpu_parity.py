@@ -270,20 +270,20 @@ def test_strided_views_equal_contiguous_bitwise(dev):
         assert np.array_equal(a[n], b[n]), n
 
 
-# Head size 128: matrix-core kernels over 16-token blocks, with three storage levels
-# (snapshots every C tokens, stretch starts in the workspace, block starts in registers).
+# Head size 128: matrix-core kernels over 16-token blocks; the backward's column pass replays
+# each checkpoint segment (C tokens, a multiple of 16) from its snapshot.
 S128_CASES = {
     # three segments (64, 64, 22 tokens), ragged second sequence, grouped heads
     "kda_c64": I.Workload("s128_kda_c64", 2, 150, 2, 4, 128, True, 64, -0.3,
                           seq_lens=(150, 77), seed=501),
-    # interval above the replayed stretch: stretch starts saved to the workspace
+    # long segments (200 rounded up to 208 tokens: 13 blocks), a ragged last one
     "scalar_c200": I.Workload("s128_scalar_c200", 2, 300, 1, 3, 128, False, 200, -0.05,
                               seq_lens=(300, 133), seed=502),
-    # default interval ceil(sqrt(T)) = 10 (rounded up to 16): partial stretches everywhere
+    # default interval ceil(sqrt(T)) = 10, rounded up to 16: one block per segment
     "kda_default": I.Workload("s128_kda_default", 1, 100, 1, 2, 128, True, 0, -0.5, seed=503),
-    # every token its own segment (interval 1, rounded up to one block)
+    # interval 1, rounded up to one block; a partial last block
     "kda_c1": I.Workload("s128_kda_c1", 1, 19, 1, 1, 128, True, 1, -0.5, seed=504),
-    # one segment longer than a stretch
+    # one segment over the whole sequence, its last block a single token
     "scalar_cT": I.Workload("s128_scalar_cT", 1, 129, 1, 1, 128, False, 129, -1.0, seed=505),
     # gates above one whose block products stay in range: column scaling with c > 1
     "kda_gate_above_one": I.Workload("s128_kda_up", 1, 150, 1, 2, 128, True, 64, -0.5,
