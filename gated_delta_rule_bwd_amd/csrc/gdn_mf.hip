@@ -77,6 +77,11 @@ template <int D>
 __device__ __forceinline__ float row_shr(float v) {
     return as_f(__builtin_amdgcn_update_dpp(as_i(1.f), as_i(v), 0x110 + D, 0xF, 0xF, false));
 }
+// the value of lane l + D in the same 16-lane row, 0 for the last D lanes of the row
+template <int D>
+__device__ __forceinline__ float row_shl0(float v) {
+    return as_f(__builtin_amdgcn_update_dpp(0, as_i(v), 0x100 + D, 0xF, 0xF, false));
+}
 // sum over the 16 lanes of a DPP row (every lane receives it)
 __device__ __forceinline__ float row16_sum(float v) {
     v += dpp<0xB1>(v);
@@ -1218,7 +1223,7 @@ __global__ void __launch_bounds__(NT) colsum_kernel(const Mf128Args a) {
     f4 M[8];
     auto block = [&](ColLds &sm, const f4 (&Xc)[8], int tw, int n, bool dir) {
         // P1 = M^T sgy (dq's dense part); its share of dg at the block's first token; P1 += KR^T G1
-        f4 p1, dgacc, p2, p3, dg0;
+        f4 p1, dgacc, p2, p3, dg0, carry, krv;
         {
             f4 pa = zero4(), pb = zero4();
 #pragma unroll
@@ -1265,11 +1270,17 @@ __global__ void __launch_bounds__(NT) colsum_kernel(const Mf128Args a) {
             }
             p3 = p3a + p3b;
             // dg at the block's first token: the column sums of X .* M with X after the update,
-            // = sum(X' .* M) + sum_t (qc_t P1 + kc_t P2) over the dense parts
+            // = sum(X' .* M) + sum_t (qc_t P1 + kc_t P2) over the dense parts; dg after the block:
+            // the column sums of X' .* (M + delta kr^T) (X' and the replayed state carry the
+            // block's product inversely) = sum(X' .* M) + sum_t kr_t P3 over the dense part
             const f4 xm4 = to_tile(rows4_sum(xa + xb));
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                dg0[r] = xm4[r] + row16_sum(dgacc[r] + (&sm.kcI[0][0])[cti(i0 + 4 * g4 + r, lm)] * p2[r]);
+            for (int r = 0; r < 4; ++r) {
+                const int o = cti(i0 + 4 * g4 + r, lm);
+                krv[r] = (&sm.krI[0][0])[o];
+                dg0[r] = xm4[r] + row16_sum(dgacc[r] + (&sm.kcI[0][0])[o] * p2[r]);
+                carry[r] = xm4[r] + row16_sum(krv[r] * p3[r]);
+            }
             const f4 qc4 = ld4(&sm.qcI[0][0] + ctq(i0 + lm, g4)), kr4 = ld4(&sm.krI[0][0] + ctq(i0 + lm, g4)),
                      kc4 = ld4(&sm.kcI[0][0] + ctq(i0 + lm, g4));
             const f4 g1t = f4{sm.g1[lm][4 * g4], sm.g1[lm][4 * g4 + 1], sm.g1[lm][4 * g4 + 2], sm.g1[lm][4 * g4 + 3]};
@@ -1281,17 +1292,9 @@ __global__ void __launch_bounds__(NT) colsum_kernel(const Mf128Args a) {
                 p2 = mfma(kr4[x], g2v[x], p2);    // KR^T (G2, s < t)
             }
         }
-        // the replay: M += delta kr^T; dg after the block = the column sums of X' .* M before the
-        // fold (X' and M carry the block's product inversely)
+        // the replay: M += delta kr^T, then the block product
         rank_update(sm, M);
-        f4 carry = zero4();
         if (!dir) {
-            float v = 0.f;
-#pragma unroll
-            for (int jb = 0; jb < 8; ++jb)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) v = fmaf(Xc[jb][r], M[jb][r], v);
-            carry = to_tile(rows4_sum(v));
             const float p = sm.pv[i0 + lm];
 #pragma unroll
             for (int jb = 0; jb < 8; ++jb) M[jb] *= p;
@@ -1304,16 +1307,15 @@ __global__ void __launch_bounds__(NT) colsum_kernel(const Mf128Args a) {
             const float c = (&sm.cI[0][0])[cti(i, lm)], rc = rcp(c);
             dq4[r] = c * p1[r];
             dk4[r] = fmaf(rc, p3[r], c * p2[r]);
-            inc[r] = (&sm.qcI[0][0])[cti(i, lm)] * p1[r] - (&sm.krI[0][0])[cti(i, lm)] * p3[r] + (&sm.kcI[0][0])[cti(i, lm)] * p2[r];
+            inc[r] = (&sm.qcI[0][0])[cti(i, lm)] * p1[r] - krv[r] * p3[r] + (&sm.kcI[0][0])[cti(i, lm)] * p2[r];
         }
         // suffix sums of the increments over the block's tokens (lanes l%16 upwards)
 #pragma unroll
-        for (int d = 1; d < W; d <<= 1) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float o = __shfl_down(inc[r], d, W);
-                inc[r] += (lm + d < W) ? o : 0.f;
-            }
+        for (int r = 0; r < 4; ++r) {
+            inc[r] += row_shl0<1>(inc[r]);
+            inc[r] += row_shl0<2>(inc[r]);
+            inc[r] += row_shl0<4>(inc[r]);
+            inc[r] += row_shl0<8>(inc[r]);
         }
         f4 dgv;
 #pragma unroll
