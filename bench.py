@@ -69,7 +69,7 @@ TRAFFIC = {
     ("gdn", "layer_kda_s128"): {
         "file": "traffic_layer_kda_s128.json",
         "sources": [_C + "gdn_mf.hip", _C + "gdn_kernels.hip", _C + "gdn_api.hip", _C + "gdn_internal.h"],
-        "kernels": ("chain_kernel<0>", "colsum_kernel<0>", "combine_kernel")},
+        "kernels": ("chain_kernel<0, 8>", "colsum_kernel<0>")},
     ("ssm_conv", "conv_layer_d10240_k4"): {
         "file": "traffic_conv_layer_d10240_k4.json",
         "sources": [_C + "ssm_conv.hip", _C + "gdn_internal.h"],
@@ -528,7 +528,7 @@ def main():
         # head size 128 runs on the fp32 matrix cores (dense fp32 MFMA peak, the same figure as
         # the fp32 vector peak); the small heads on the vector ALUs
         "roofline": {"bound": "mfma" if S2 == 128 * 128 else "alu",
-                     "kernel": "gdn_bwd (chain_kernel + colsum_kernel + combine_kernel)" if S2 == 128 * 128 else
+                     "kernel": "gdn_bwd (chain_kernel + colsum_kernel)" if S2 == 128 * 128 else
                      "gdn_bwd (bwd_kernel" + (" + combine_kernel)" if w.H_v != w.H_k else ")"),
                      "achieved": achieved / 1e12, "peak": PEAK_FP32_VALU / 1e12,
                      "unit": "TFLOP/s", "frac": achieved / PEAK_FP32_VALU,

@@ -112,13 +112,9 @@ Plan make_plan(const gdn_problem *p) {
         if (pl.nslab > 1) off = align_up(off + tok_rows * pl.nslab * sizeof(float));
         pl.off_xs = off;   // the state gradient at each block's end
         off = align_up(off + (size_t)pl.units * nblk * S * S * sizeof(float));
-        pl.parts = p->H_v != p->H_k;
-        if (pl.parts) {   // dq, dk per value head, summed over the heads of a key head afterwards
-            pl.off_pq = off;
-            off = align_up(off + tok_rows * S * sizeof(float));
-            pl.off_pk = off;
-            off = align_up(off + tok_rows * S * sizeof(float));
-        }
+        // dq and dk go straight to the outputs: the column pass sums the value heads of a key
+        // head in one workgroup
+        pl.parts = false;
         pl.total = off;
         return pl;
     }
@@ -219,8 +215,6 @@ gdn::Mf128Args mf_args(const gdn_problem *p, const Plan &pl, void *ws, int s0, i
     a.dbp = (float *)(w + pl.off_dbp);
     a.nslab = pl.nslab;
     a.xbuf = (float *)(w + pl.off_xs);
-    a.dq_part = pl.parts ? (float *)(w + pl.off_pq) : nullptr;
-    a.dk_part = pl.parts ? (float *)(w + pl.off_pk) : nullptr;
     a.sq = p->q; a.sk = p->k; a.sv = p->v; a.sg = p->g; a.sb = p->beta; a.sgy = p->gy; a.sy = p->y;
     a.s_base = s0; a.n_seqs_launch = cnt;
     a.T = p->T; a.H_k = p->H_k; a.H_v = p->H_v; a.C = pl.C; a.n_ck_max = pl.n_ck_max;
@@ -465,14 +459,6 @@ int gdn_bwd(const gdn_problem *p, const void *q_in, const void *k_in, const void
             a.dq = dq; a.dk = dk; a.dv = dv; a.dg = dg; a.dbeta = dbeta; a.dstate = dstate;
             rc = device_status(gdn::launch_bwd_mf(a, (hipStream_t)stream));
             if (rc != GDN_OK) return rc;
-        }
-        if (pl.parts) {   // dq, dk: the value heads of each key head in increasing order
-            gdn::CombineArgs c;
-            c.dq_part = (const float *)((char *)ws + pl.off_pq);
-            c.dk_part = (const float *)((char *)ws + pl.off_pk);
-            c.dq = dq; c.dk = dk;
-            c.n_seqs = p->n_seqs; c.T = p->T; c.H_k = p->H_k; c.H_v = p->H_v; c.S = (int)SK;
-            rc = device_status(gdn::launch_combine(c, (hipStream_t)stream));
         }
         return rc;
     }

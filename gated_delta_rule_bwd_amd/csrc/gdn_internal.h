@@ -118,8 +118,7 @@ struct Mf128Args {
     float *dbp;             // [n_seqs][T][H_v][nslab] dbeta per slab (nslab > 1)
     float *xbuf;            // [unit][nblk][S][S] the state gradient at each block's end, folded
                             // into the block's column scaling (tile-major 16 x 16 tiles)
-    float *dq_part, *dk_part;   // [n_seqs][T][H_v][S] per value head (null: H_v == H_k, direct)
-    float *dq, *dk, *dv, *dg, *dbeta, *dstate;
+    float *dq, *dk, *dv, *dg, *dbeta, *dstate;   // dq, dk per key head, summed over its value heads
     gdn_strides sq, sk, sv, sg, sb, sgy, sy;
     int32_t s_base, n_seqs_launch, T, H_k, H_v, C, n_ck_max, kda, dtype;
     int32_t nslab;          // row slabs per unit of the forward and the chain: 1 or 2

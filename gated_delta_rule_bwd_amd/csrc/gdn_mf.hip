@@ -28,8 +28,8 @@
 // forward gives each of its eight waves 16 rows, and the backward's chain (dd = dM k and the
 // update of dM) does the same; the backward's column sums (dq, dk, dg) take the columns of the
 // state and of the transposed gradient instead, 16 per wave, so they are complete inside the
-// workgroup.  Only dq and dk of key heads shared by several value heads are summed afterwards,
-// over those value heads in increasing order.
+// workgroup.  dq and dk of a key head shared by several value heads are summed by the column
+// pass itself: one workgroup takes the value heads of the key head in increasing order.
 //
 // MFMA lane layout (16x16x4 f32): lane l supplies A[l%16][kappa] and B[kappa][l%16], and
 // holds D[4(l/16) + r][l%16] in accumulator register r.  Every product below uses the
@@ -620,7 +620,8 @@ __global__ void __launch_bounds__(64 * NWC) fwd_mf_kernel(const Mf128Args a) {
 // dv = beta dd (which also hands du = -dv to pass 2); dbeta = dd . e; the block's Grams over the
 // rows G1 = delta^T sgy and G2 = delta^T du for pass 2; X = X' + sgy qc^T + du kc^T.
 //
-// Pass 2, the column sums (one workgroup per checkpoint segment of a unit, all in parallel).
+// Pass 2, the column sums (one workgroup per checkpoint segment of a (sequence, key head), all in
+// parallel; inside it the value heads of the key head one after the other, adding dq and dk).
 // Wave w holds columns 16 w .. 16 w + 15 of the state M as eight tiles (tile jb, lane l,
 // register r: M[16 jb + 4(l/16) + r][16 w + l%16]) and of the saved X' alike.  Starting from the
 // segment's snapshot, per block: the column sums against the block's start state and X' (dq, dk
@@ -1016,14 +1017,15 @@ template <int DT>
 __global__ void __launch_bounds__(NT) colsum_kernel(const Mf128Args a) {
     __shared__ ColLds smb[2];
     constexpr uint32_t ES = sizeof(In<DT>);
-    const int units = a.n_seqs_launch * a.H_v;
-    const int ul = blockIdx.x % units, sg = blockIdx.x / units;
-    const int sl = ul / a.H_v, h = ul % a.H_v;
+    // one workgroup per (sequence, key head, segment): the value heads hk, hk + H_k, .. of the
+    // key head one after the other, each adding its dq and dk to the key head's sums
+    const int groups = a.n_seqs_launch * a.H_k;
+    const int gl = blockIdx.x % groups, sg = blockIdx.x / groups;
+    const int sl = gl / a.H_k, hk = gl % a.H_k;
     const int64_t s = a.s_base + sl;
-    const int hk = h % a.H_k;
     const int L = a.lens[sl];
     const int C = a.C;
-    const int64_t unit = s * a.H_v + h;
+    const int nrep = a.H_v / a.H_k;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, lm = lane & 15, g4 = lane >> 4;
     const int i0 = 16 * wv;   // the wave's columns
     const int ci = tid & (S - 1), tg = __builtin_amdgcn_readfirstlane(tid >> 7);   // staging: column/row ci, tokens 4 tg .. 4 tg + 3
@@ -1031,45 +1033,53 @@ __global__ void __launch_bounds__(NT) colsum_kernel(const Mf128Args a) {
     const int G = a.kda ? S : 1;
     const float scale = a.scale;
     const bool kda = a.kda != 0;
-    const float *cin = a.cbuf + (s * a.T * a.H_v + h) * (int64_t)G;
     const In<DT> *kin = tin<DT>(a.k) + s * a.sk.seq + hk * a.sk.head;
     const In<DT> *qin = tin<DT>(a.q) + s * a.sq.seq + hk * a.sq.head;
-    const In<DT> *gyin = tin<DT>(a.gy) + s * a.sgy.seq + h * a.sgy.head;
-    const In<DT> *bin = tin<DT>(a.beta) + s * a.sb.seq + h * a.sb.head;
-    const int64_t row0 = s * a.T * a.H_v + h;   // per-token workspace row of token 0; stride H_v
-    const float *ein = a.ebuf + row0 * S;
-    const float *dvin = a.dv + row0 * S;
-    float *dqout = (a.dq_part ? a.dq_part : a.dq) + row0 * S;   // direct when H_v == H_k
-    float *dkout = (a.dk_part ? a.dk_part : a.dk) + row0 * S;
-    float *dgout = a.dg + row0 * G;
-    const bool vec_out = (((uintptr_t)dqout | (uintptr_t)dkout | (uintptr_t)dgout) & 15) == 0;
+    const int64_t qkt = (int64_t)a.H_k * S;     // token stride of dq and dk
+    float *dqout = a.dq + (s * a.T * a.H_k + hk) * S;
+    float *dkout = a.dk + (s * a.T * a.H_k + hk) * S;
+    const bool vec_out = (((uintptr_t)a.dq | (uintptr_t)a.dk | (uintptr_t)a.dg) & 15) == 0;
     const bool vec_dv = ((uintptr_t)a.dv & 15) == 0;
     const uint32_t ct = (uint32_t)(a.H_v * G) * 4, kt = (uint32_t)a.sk.tok * ES, qt = (uint32_t)a.sq.tok * ES,
                    gyt = (uint32_t)a.sgy.tok * ES, bt = (uint32_t)a.sb.tok * ES, et = (uint32_t)a.H_v * S * 4;
     const int nsl = a.nslab;
+    const int ts = sg * C;
 
-    {   // padded tokens of the segment's span
-        const int64_t p0 = max((int64_t)L, (int64_t)sg * C), p1 = min((int64_t)a.T, (int64_t)sg * C + C);
+    // the value head in progress (set at the top of each head's pass)
+    int rep = 0, h = hk;
+    int64_t unit = 0, row0 = 0;   // row0: per-token workspace row of token 0; stride H_v
+    const float *cin = nullptr, *ein = nullptr, *dvin = nullptr;
+    const In<DT> *gyin = nullptr, *bin = nullptr;
+    float *dgout = nullptr;
+    auto set_head = [&](int r) {
+        rep = r;
+        h = hk + r * a.H_k;
+        unit = s * a.H_v + h;
+        row0 = s * a.T * a.H_v + h;
+        cin = a.cbuf + row0 * (int64_t)G;
+        gyin = tin<DT>(a.gy) + s * a.sgy.seq + h * a.sgy.head;
+        bin = tin<DT>(a.beta) + s * a.sb.seq + h * a.sb.head;
+        ein = a.ebuf + row0 * S;
+        dvin = a.dv + row0 * S;
+        dgout = a.dg + row0 * G;
+    };
+    // padded tokens of the segment's span: dg of every value head, dq and dk of the key head
+    {
+        const int64_t p0 = max((int64_t)L, (int64_t)ts), p1 = min((int64_t)a.T, (int64_t)ts + C);
         for (int64_t idx = tid; idx < (p1 - p0) * S; idx += NT) {
-            const int64_t row = (p0 + idx / S) * a.H_v;
+            const int64_t t = p0 + idx / S;
             const int i = (int)(idx % S);
-            dqout[row * S + i] = 0.f;
-            dkout[row * S + i] = 0.f;
-            if (kda) dgout[row * S + i] = 0.f;
-            else if (i == 0) dgout[row] = 0.f;
+            dqout[t * qkt + i] = 0.f;
+            dkout[t * qkt + i] = 0.f;
+            for (int r = 0; r < nrep; ++r) {
+                const int64_t row = (s * a.T + t) * a.H_v + hk + r * a.H_k;
+                if (kda) a.dg[row * S + i] = 0.f;
+                else if (i == 0) a.dg[row] = 0.f;
+            }
         }
     }
-    const int ts = sg * C;
     if (ts >= L) return;
     const int nb = (min(ts + C, L) - ts + W - 1) / W;
-    if (nsl > 1) {   // dbeta of the segment's tokens: the chain's slabs in order
-        for (int t = ts + tid; t < min(ts + C, L); t += NT) {
-            const int64_t r = row0 + (int64_t)t * a.H_v;
-            float b = 0.f;
-            for (int k = 0; k < nsl; ++k) b += a.dbp[r * nsl + k];
-            a.dbeta[r] = b;
-        }
-    }
 
     // a 128 x 128 matrix in the column layout: row-major [S][S] (the snapshots) or tile-major (X')
     const uint32_t vcol = ((4 * g4) * S + i0 + lm) * 4;
@@ -1222,6 +1232,22 @@ __global__ void __launch_bounds__(NT) colsum_kernel(const Mf128Args a) {
     // token's gates have scaled M already; otherwise the block product folds in at the end)
     f4 M[8];
     auto block = [&](ColLds &sm, const f4 (&Xc)[8], int tw, int n, bool dir) {
+        // the earlier value heads' dq and dk of the block's tokens (zero for the first head),
+        // loaded first so that the products below cover their latency
+        f4 pq = zero4(), pk = zero4();
+        if (rep > 0 && lm < n) {
+            const int64_t oq = (int64_t)(tw + lm) * qkt + i0 + 4 * g4;
+            if (vec_out) {
+                pq = ld4(dqout + oq);
+                pk = ld4(dkout + oq);
+            } else {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    pq[r] = dqout[oq + r];
+                    pk[r] = dkout[oq + r];
+                }
+            }
+        }
         // P1 = M^T sgy (dq's dense part); its share of dg at the block's first token; P1 += KR^T G1
         f4 p1, dgacc, p2, p3, dg0, carry, krv;
         {
@@ -1322,15 +1348,16 @@ __global__ void __launch_bounds__(NT) colsum_kernel(const Mf128Args a) {
         for (int r = 0; r < 4; ++r) dgv[r] = lm == 0 ? dg0[r] : carry[r] + inc[r];
         if (lm < n) {
             const int64_t o = (int64_t)(tw + lm) * (a.H_v * S) + i0 + 4 * g4;
+            const int64_t oq = (int64_t)(tw + lm) * qkt + i0 + 4 * g4;
             if (vec_out) {
-                st4(dqout + o, dq4);
-                st4(dkout + o, dk4);
+                st4(dqout + oq, pq + dq4);
+                st4(dkout + oq, pk + dk4);
                 if (kda) st4(dgout + o, dgv);
             } else {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    dqout[o + r] = dq4[r];
-                    dkout[o + r] = dk4[r];
+                    dqout[oq + r] = pq[r] + dq4[r];
+                    dkout[oq + r] = pk[r] + dk4[r];
                     if (kda) dgout[o + r] = dgv[r];
                 }
             }
@@ -1352,52 +1379,64 @@ __global__ void __launch_bounds__(NT) colsum_kernel(const Mf128Args a) {
         }
     };
 
-    load_cols(a.snap + (unit * a.n_ck_max + sg) * (int64_t)(S * S), M);
-    Pre P;
-    prefetch(P, ts);
     int cur = 0;
-    for (int bb = 0; bb < nb; ++bb) {
-        const int t0 = ts + bb * W, cnt = min(W, L - t0);
-        const float *xs = a.xbuf + (unit * nblk + t0 / W) * (int64_t)(S * S);
-        const bool dir = P.dir != 0;
-        // a column-scaled block in one step; a token-by-token block one token per step from the
-        // first, the gradient after token tau being X' of the block stepped back over the block's
-        // later tokens
-        const int nsub = dir ? cnt : 1;
-        for (int tau = 0; tau < nsub; ++tau) {
-            ColLds &sm = smb[cur];
-            f4 Xc[8];
-            if (!dir) stage(sm, P, cnt);
-            load_tiles(xs, Xc);   // before the next block's inputs, so its wait leaves them in flight
-            if (tau == 0 && bb + 1 < nb) prefetch(P, t0 + W);
-            if (dir) {
-                for (int u = cnt - 1; u > tau; --u) {
-                    __syncthreads();
-                    stage_update(sm, t0, u);
-                    __syncthreads();
-                    rank_update(sm, Xc);
-                    const float p = sm.pv[i0 + lm];
+    for (int r = 0; r < nrep; ++r) {
+        set_head(r);
+        if (nsl > 1) {   // dbeta of the segment's tokens: the chain's slabs in order
+            for (int t = ts + tid; t < min(ts + C, L); t += NT) {
+                const int64_t rw = row0 + (int64_t)t * a.H_v;
+                float b = 0.f;
+                for (int k = 0; k < nsl; ++k) b += a.dbp[rw * nsl + k];
+                a.dbeta[rw] = b;
+            }
+        }
+        load_cols(a.snap + (unit * a.n_ck_max + sg) * (int64_t)(S * S), M);
+        Pre P;
+        prefetch(P, ts);
+        pend_n = 0;
+        for (int bb = 0; bb < nb; ++bb) {
+            const int t0 = ts + bb * W, cnt = min(W, L - t0);
+            const float *xs = a.xbuf + (unit * nblk + t0 / W) * (int64_t)(S * S);
+            const bool dir = P.dir != 0;
+            // a column-scaled block in one step; a token-by-token block one token per step from
+            // the first, the gradient after token tau being X' of the block stepped back over the
+            // block's later tokens
+            const int nsub = dir ? cnt : 1;
+            for (int tau = 0; tau < nsub; ++tau) {
+                ColLds &sm = smb[cur];
+                f4 Xc[8];
+                if (!dir) stage(sm, P, cnt);
+                load_tiles(xs, Xc);   // before the next block's inputs, so its wait leaves them in flight
+                if (tau == 0 && bb + 1 < nb) prefetch(P, t0 + W);
+                if (dir) {
+                    for (int u = cnt - 1; u > tau; --u) {
+                        __syncthreads();
+                        stage_update(sm, t0, u);
+                        __syncthreads();
+                        rank_update(sm, Xc);
+                        const float p = sm.pv[i0 + lm];
 #pragma unroll
-                    for (int jb = 0; jb < 8; ++jb) Xc[jb] *= p;
+                        for (int jb = 0; jb < 8; ++jb) Xc[jb] *= p;
+                    }
+                    __syncthreads();
+                    stage_token(sm, t0, tau);
                 }
                 __syncthreads();
-                stage_token(sm, t0, tau);
-            }
-            __syncthreads();
-            flush(smb[cur ^ 1]);
-            if (dir) {
-                const float p = sm.pv[i0 + lm];
+                flush(smb[cur ^ 1]);
+                if (dir) {
+                    const float p = sm.pv[i0 + lm];
 #pragma unroll
-                for (int jb = 0; jb < 8; ++jb) M[jb] *= p;
+                    for (int jb = 0; jb < 8; ++jb) M[jb] *= p;
+                }
+                block(sm, Xc, dir ? t0 + tau : t0, dir ? 1 : cnt, dir);
+                pend_tw = dir ? t0 + tau : t0;
+                pend_n = dir ? 1 : cnt;
+                cur ^= 1;
             }
-            block(sm, Xc, dir ? t0 + tau : t0, dir ? 1 : cnt, dir);
-            pend_tw = dir ? t0 + tau : t0;
-            pend_n = dir ? 1 : cnt;
-            cur ^= 1;
         }
+        __syncthreads();
+        flush(smb[cur ^ 1]);
     }
-    __syncthreads();
-    flush(smb[cur ^ 1]);
 }
 
 template <typename Args>
@@ -1456,7 +1495,7 @@ hipError_t launch_bwd_mf(const Mf128Args &a, hipStream_t st) {
     const int units = a.n_seqs_launch * a.H_v;
     hipError_t e = a.nslab == 2 ? launch(pick<ChainK2>(a.dtype), a, 2 * units, NT / 2, st)
                                 : launch(pick<ChainK>(a.dtype), a, units, NT, st);
-    if (e == hipSuccess) e = launch(pick<ColK>(a.dtype), a, a.n_seqs_launch * a.H_v * a.n_ck_max, NT, st);
+    if (e == hipSuccess) e = launch(pick<ColK>(a.dtype), a, a.n_seqs_launch * a.H_k * a.n_ck_max, NT, st);
     return e;
 }
 

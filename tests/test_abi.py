@@ -64,10 +64,7 @@ def expected_ws(n, T, Hk, Hv, S, C, kda=True):
         if nsl > 1:
             tot = al(tot + rows * nsl * 4)                  # dbeta per slab
         tot = al(tot + units * nblk * S * S * 4)            # state gradient per block
-        if Hv != Hk:
-            tot = al(tot + rows * S * 4)                    # dq per value head
-            tot = al(tot + rows * S * 4)                    # dk per value head
-        return tot
+        return tot                                          # dq, dk summed in the column pass
     tot = al(tot + units * C * S * S * 4)
     tot = al(tot + units * C * S * 4)
     if Hv != Hk:
