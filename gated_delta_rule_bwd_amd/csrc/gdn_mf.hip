@@ -82,6 +82,15 @@ template <int D>
 __device__ __forceinline__ float row_shl0(float v) {
     return as_f(__builtin_amdgcn_update_dpp(0, as_i(v), 0x100 + D, 0xF, 0xF, false));
 }
+// the value of lane l - D in the same 16-lane row, 0 for the first D lanes of the row
+template <int D>
+__device__ __forceinline__ float row_shr0(float v) {
+    return as_f(__builtin_amdgcn_update_dpp(0, as_i(v), 0x110 + D, 0xF, 0xF, false));
+}
+// the value of the last lane of the 16-lane row, in every lane of the row (row_newbcast:15)
+__device__ __forceinline__ float row_bcast15(float v) {
+    return as_f(__builtin_amdgcn_mov_dpp(as_i(v), 0x15F, 0xF, 0xF, false));
+}
 // sum over the 16 lanes of a DPP row (every lane receives it)
 __device__ __forceinline__ float row16_sum(float v) {
     v += dpp<0xB1>(v);
@@ -651,6 +660,7 @@ struct alignas(16) ChainLds {
     float pb[NWC][W];          // per-wave partials of dbeta
     float p1[NWC][W][GP];      // per-wave partials of G1 [s][t]
     float p2[NWC][W][GP];      // per-wave partials of G2 [s][t]
+    float anp[NWC][S];         // per-wave partials of dg at a segment's first token
 };
 
 // The chain's workgroup owns 16 NWC rows of a unit (all, or one of NSL = 8 / NWC slabs: the rows
@@ -685,7 +695,9 @@ __global__ void __launch_bounds__(64 * NWC) chain_kernel(const Mf128Args a) {
     const bool vec_dv = ((uintptr_t)a.dv & 15) == 0;
     float *dbout = NSL > 1 ? a.dbp + row0 * nsl + slab : a.dbeta + row0;   // stride H_v nsl per token
     const int64_t dbt = NSL > 1 ? (int64_t)a.H_v * nsl : a.H_v;
-    float *xsave = a.xbuf + unit * (int64_t)nblk * (S * S);
+    float *ringw = a.ring + (int64_t)blockIdx.x * (2 * R * S);   // this workgroup's two gradients
+    float *p3out = a.p3buf + row0 * S;                               // token stride H_v S
+    float *ancu = a.anc + unit * (int64_t)a.n_ck_max * S;
     float *g1u = a.g1buf + ((s * nblk * a.H_v + h) * nsl + slab) * (int64_t)(W * W);   // block b at b H_v nsl W^2
     float *g2u = a.g2buf + ((s * nblk * a.H_v + h) * nsl + slab) * (int64_t)(W * W);
     const uint32_t ct = (uint32_t)(a.H_v * G) * 4, kt = (uint32_t)a.sk.tok * ES, qt = (uint32_t)a.sq.tok * ES,
@@ -821,16 +833,78 @@ __global__ void __launch_bounds__(64 * NWC) chain_kernel(const Mf128Args a) {
 
     // ---- one step of the chain on a staged (sub)block of n tokens from tw: the fold and X'
     // (saved to xs when given), then, once the next block's inputs are in flight, the rest
-    auto save_x = [&](float *xs) {
+    // The gradient entering a step goes to a ring slot at the end of the step before (tile
+    // (wave, ib) column-major: element (row, column) of a tile at 16 column + row), so that after
+    // the staging barrier every wave reads its columns of it with 16-byte loads.
+    auto save_ring = [&](int slot) {
+        float *base = ringw + slot * (R * S) + 256 * 8 * wv + 16 * (4 * g4) + lm;
 #pragma unroll
-        for (int ib = 0; ib < 8; ++ib) st4(xs + ((j0 >> 4) * 8 + ib) * 256 + lm * 16 + 4 * g4, X[ib]);
+        for (int ib = 0; ib < 8; ++ib)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) base[256 * ib + 16 * r] = X[ib][r];
     };
-    auto fold = [&](const ChainLds<NWC> &sm, float *xs) {
+    auto fold = [&](const ChainLds<NWC> &sm) {
 #pragma unroll
         for (int ib = 0; ib < 8; ++ib) X[ib] *= ld4(&sm.pv[16 * ib + 4 * g4]);
-        save_x(xs);
     };
-    auto step = [&](ChainLds<NWC> &sm, int tw, int n, bool dir) {
+    // P3 = X'^T delta of a step over the workgroup's rows, X' = X diag(pv) the folded gradient
+    // (pv = 1 for a token-by-token step): diag(pv) (X^T delta) with X from the ring.  Wave w takes
+    // the column tiles CT w .. CT w + CT - 1, each a contraction over the workgroup's NWC row tiles;
+    // lane l, register r: column 16 ct + 4(l/16) + r, token l%16.  Two row slabs add their halves
+    // into a zeroed buffer (two terms: the order does not change the sum).
+    constexpr int CT = 8 / NWC;
+    f4 xa[CT][NWC];
+    auto p3_load = [&](int slot) {
+        const float *base = ringw + slot * (R * S) + 16 * lm + 4 * g4;
+#pragma unroll
+        for (int c = 0; c < CT; ++c)
+#pragma unroll
+            for (int rt = 0; rt < NWC; ++rt) xa[c][rt] = ld4(base + 256 * (8 * rt + CT * wv + c));
+    };
+    auto p3_finish = [&](const ChainLds<NWC> &sm, int tw, int n, bool fold_pv) {
+        f4 dP[NWC];
+#pragma unroll
+        for (int rt = 0; rt < NWC; ++rt) dP[rt] = ld4(&sm.er[lm][16 * rt + 4 * g4]) * sm.bt[lm];
+#pragma unroll
+        for (int c = 0; c < CT; ++c) {
+            const int ct = CT * wv + c;
+            f4 acc = zero4();
+#pragma unroll
+            for (int rt = 0; rt < NWC; ++rt)
+#pragma unroll
+                for (int x = 0; x < 4; ++x) acc = mfma(xa[c][rt][x], dP[rt][x], acc);
+            if (fold_pv) acc *= ld4(&sm.pv[16 * ct + 4 * g4]);
+            if (lm < n) {
+                float *o = p3out + (int64_t)(tw + lm) * (a.H_v * S) + 16 * ct + 4 * g4;
+                if constexpr (NSL == 1) {
+                    st4(o, acc);
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) unsafeAtomicAdd(o + r, acc[r]);
+                }
+            }
+        }
+    };
+    // dg at a segment's first token: the column sums of the gradient there times the segment's
+    // snapshot, over the wave's rows (summed over the waves after the next barrier)
+    bool anc_pend = false;
+    int anc_sg = 0;
+    auto anchor_part = [&](ChainLds<NWC> &sm, int sgi) {
+        const float *ms = a.snap + (unit * a.n_ck_max + sgi) * (int64_t)(S * S) + (int64_t)(j0 + lm) * S + 4 * g4;
+#pragma unroll
+        for (int ib = 0; ib < 8; ++ib) {
+            f4 v = X[ib] * ld4(ms + 16 * ib);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) v[r] = row16_sum(v[r]);
+            if (lm == 0) st4(&sm.anp[wv][16 * ib + 4 * g4], v);
+        }
+        anc_pend = true;
+        anc_sg = sgi;
+    };
+    int wslot = 1;   // ring slot of the gradient entering the next step
+    // mid(): work that needs no result of the step (the step's P3), placed after dd so that the
+    // ring loads it waits for have had the dd products' time to arrive
+    auto step = [&](ChainLds<NWC> &sm, int tw, int n, bool dir, auto &&mid) {
         f4 d0 = zero4(), d1 = zero4();
 #pragma unroll
         for (int ib = 0; ib < 8; ib += 2) {
@@ -865,6 +939,7 @@ __global__ void __launch_bounds__(64 * NWC) chain_kernel(const Mf128Args a) {
             if (lm == 0) sm.pb[wv][tt] = pbv;
             dut[wv][tt][lm] = duv[r];
         }
+        mid();
         // X = X' + sgy qc^T + du kc^T
         const float *qcI = &sm.qcI[0][0], *kcI = &sm.kcI[0][0];
 #pragma unroll
@@ -876,6 +951,11 @@ __global__ void __launch_bounds__(64 * NWC) chain_kernel(const Mf128Args a) {
                 X[ib] = mfma(ka[x], duv[x], X[ib]);
             }
         }
+        if (dir) {   // the gradient before the token's gates
+#pragma unroll
+            for (int ib = 0; ib < 8; ++ib) X[ib] *= ld4(&sm.pv[16 * ib + 4 * g4]);
+        }
+        save_ring(wslot);   // the gradient entering the next step, early for the next barrier
         // the Grams over the wave's rows: delta^T (row s = l%16, the wave's rows along the
         // contraction) times scale gy and du (column t = l%16)
         {
@@ -906,15 +986,21 @@ __global__ void __launch_bounds__(64 * NWC) chain_kernel(const Mf128Args a) {
                 sm.p2[wv][4 * g4 + r][lm] = q2[r];
             }
         }
-        if (dir) {   // the gradient before the token's gates
-#pragma unroll
-            for (int ib = 0; ib < 8; ++ib) X[ib] *= ld4(&sm.pv[16 * ib + 4 * g4]);
-        }
     };
     // the previous step's dbeta and Grams over the workgroup's rows: the per-wave partials in
     // order, once every wave has passed the barrier after this step's staging
     int pend_t0 = 0, pend_tau = -1, pend_n = 0;
     auto flush = [&](const ChainLds<NWC> &sp) {
+        if (anc_pend) {
+            for (int col = tid; col < S; col += NTC) {
+                float g = 0.f;
+#pragma unroll
+                for (int w2 = 0; w2 < NWC; ++w2) g += sp.anp[w2][col];
+                if constexpr (NSL == 1) ancu[(int64_t)anc_sg * S + col] = g;
+                else unsafeAtomicAdd(&ancu[(int64_t)anc_sg * S + col], g);
+            }
+            anc_pend = false;
+        }
         if (pend_n == 0) return;
         if (wv == 0 && lane < pend_n) {
             float b = 0.f;
@@ -948,18 +1034,21 @@ __global__ void __launch_bounds__(64 * NWC) chain_kernel(const Mf128Args a) {
     Pre P;
     const int nb = (L + W - 1) / W;
     int cur = 0;
+    save_ring(0);   // the gradient entering the last block
     if (nb > 0) prefetch(P, (nb - 1) * W);
     for (int b = nb - 1; b >= 0; --b) {
         const int t0 = b * W, cnt = min(W, L - t0);
         const bool dir = P.dir != 0;
-        float *xs = xsave + (int64_t)b * (S * S);
         if (!dir) {
             stage(smb[cur], P, cnt);
             __syncthreads();
             flush(smb[cur ^ 1]);
-            fold(smb[cur], xs);
-            if (b > 0) prefetch(P, t0 - W);   // after the stores of X', which its wait then covers
-            step(smb[cur], t0, cnt, false);
+            p3_load(wslot ^ 1);
+            fold(smb[cur]);
+            if (b > 0) prefetch(P, t0 - W);
+            step(smb[cur], t0, cnt, false, [&] { p3_finish(smb[cur], t0, cnt, true); });
+            wslot ^= 1;
+            if (t0 % a.C == 0) anchor_part(smb[cur], t0 / a.C);
             pend_t0 = t0;
             pend_tau = -1;
             pend_n = cnt;
@@ -971,8 +1060,10 @@ __global__ void __launch_bounds__(64 * NWC) chain_kernel(const Mf128Args a) {
                 stage_token(smb[cur], t0, tau);
                 __syncthreads();
                 flush(smb[cur ^ 1]);
-                if (u == 0) save_x(xs);   // X' of the block: the gradient after its last token
-                step(smb[cur], t0 + tau, 1, true);
+                p3_load(wslot ^ 1);
+                step(smb[cur], t0 + tau, 1, true, [&] { p3_finish(smb[cur], t0 + tau, 1, false); });
+                wslot ^= 1;
+                if (tau == 0 && t0 % a.C == 0) anchor_part(smb[cur], t0 / a.C);
                 pend_t0 = t0;
                 pend_tau = tau;
                 pend_n = 1;
@@ -1004,7 +1095,6 @@ struct alignas(16) ColLds {
     float cI[S][KP];           // c           [column][token]
     float dl[S][KP];           // delta       [row][token]; token by token: scale gy and du of the update
     float sgy[W][SP];          // scale gy    [token][row]
-    float ee[W][SP];           // delta       [token][row]
     float du[W][SP];           // du          [token][row]
     float pv[S];               // fold factor per column (a token's gates)
     float g1[W][GP];           // G1 = delta^T scale gy, [s][t], s <= t
@@ -1090,21 +1180,6 @@ __global__ void __launch_bounds__(NT) colsum_kernel(const Mf128Args a) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) Mc[jb][r] = bldf(rs, vcol + r * S * 4, 16 * jb * S * 4);
     };
-    const uint32_t vtile = (wv * 256 + 4 * g4 * 16 + lm) * 4;
-    auto load_tiles = [&](const float *base, f4 (&Xc)[8]) {
-        const Rsrc rs = rsrc(base);
-#pragma unroll
-        for (int jb = 0; jb < 8; ++jb)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) Xc[jb][r] = bldf(rs, vtile + r * 16 * 4, jb * 8 * 256 * 4);
-    };
-    // a value per column i0 + l%16 into the tile layout (column i0 + 4(l/16) + r)
-    auto to_tile = [&](float v) {
-        f4 o;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) o[r] = __shfl(v, 4 * g4 + r);
-        return o;
-    };
 
     // inputs of a block, loaded one block ahead (tokens past the end load the last one, replaced
     // when staged): thread (tk = tid / 32, cg = tid % 32) takes columns (rows) 4 cg .. + 3 of token
@@ -1157,7 +1232,6 @@ __global__ void __launch_bounds__(NT) colsum_kernel(const Mf128Args a) {
             dl[o] = d[x];
         }
         st4(&sm.sgy[tk][4 * cg], ok ? P.gy * scale : zero4());
-        st4(&sm.ee[tk][4 * cg], d);
         st4(&sm.du[tk][4 * cg], ok ? -P.dv : zero4());
         if (tk == cnt - 1) st4(&sm.pv[4 * cg], c);
         if (tid < 256) {   // the slabs' partials in order
@@ -1187,7 +1261,6 @@ __global__ void __launch_bounds__(NT) colsum_kernel(const Mf128Args a) {
         for (int x = 0; x < 4; ++x) {
             const int tt = 4 * tg + x;
             sm.sgy[tt][ci] = tt == 0 ? gx : 0.f;
-            sm.ee[tt][ci] = tt == 0 ? dx : 0.f;
             sm.du[tt][ci] = tt == 0 ? ux : 0.f;
         }
         if (z) sm.pv[ci] = av;
@@ -1200,20 +1273,6 @@ __global__ void __launch_bounds__(NT) colsum_kernel(const Mf128Args a) {
             sm.g2[sr][t2] = 0.f;
             sm.g2t[sr][t2] = 0.f;
         }
-    };
-    // token t0 + tau of a token-by-token block as the operands of the gradient's update: rows
-    // (scale gy, du) against columns (q, k), the token's gates in pv
-    auto stage_update = [&](ColLds &sm, int t0, int tau) {
-        const int64_t t = t0 + tau;
-        const float av = cin[t * (a.H_v * G) + (kda ? ci : 0)];
-        const bool z = tg == 0;
-        const float gx = z ? scale * (float)gyin[t * a.sgy.tok + ci] : 0.f;
-        const float ux = z ? -dvin[t * (a.H_v * S) + ci] : 0.f;
-        const float qx = z ? (float)qin[t * a.sq.tok + ci] : 0.f;
-        const float kx = z ? (float)kin[t * a.sk.tok + ci] : 0.f;
-        st4(&sm.dl[0][0] + ctq(ci, tg), f4{gx, ux, 0.f, 0.f});
-        st4(&sm.krI[0][0] + ctq(ci, tg), f4{qx, kx, 0.f, 0.f});
-        if (z) sm.pv[ci] = av;
     };
     // Z += A B^T over the staged token slots for the column layout: A = dl [row][slot], B = krI
     // [column][slot]
@@ -1231,25 +1290,30 @@ __global__ void __launch_bounds__(NT) colsum_kernel(const Mf128Args a) {
     // gradient X' at its end (column layout); then the state's replay to the block's end (dir: the
     // token's gates have scaled M already; otherwise the block product folds in at the end)
     f4 M[8];
-    auto block = [&](ColLds &sm, const f4 (&Xc)[8], int tw, int n, bool dir) {
-        // the earlier value heads' dq and dk of the block's tokens (zero for the first head),
-        // loaded first so that the products below cover their latency
-        f4 pq = zero4(), pk = zero4();
-        if (rep > 0 && lm < n) {
+    f4 dgrun;                     // dg at the next token, per column (i0 + 4(l/16) + r)
+    const float *p3in = nullptr;   // the chain's P3 of the value head
+    auto block = [&](ColLds &sm, int tw, int n, bool dir) {
+        // the earlier value heads' dq and dk of the block's tokens (zero for the first head) and
+        // the chain's P3 = X'^T delta, loaded first so that the products below cover their latency
+        f4 pq = zero4(), pk = zero4(), p3 = zero4();
+        if (lm < n) {
             const int64_t oq = (int64_t)(tw + lm) * qkt + i0 + 4 * g4;
-            if (vec_out) {
-                pq = ld4(dqout + oq);
-                pk = ld4(dkout + oq);
-            } else {
+            p3 = ld4(p3in + (int64_t)(tw + lm) * (a.H_v * S) + i0 + 4 * g4);
+            if (rep > 0) {
+                if (vec_out) {
+                    pq = ld4(dqout + oq);
+                    pk = ld4(dkout + oq);
+                } else {
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    pq[r] = dqout[oq + r];
-                    pk[r] = dkout[oq + r];
+                    for (int r = 0; r < 4; ++r) {
+                        pq[r] = dqout[oq + r];
+                        pk[r] = dkout[oq + r];
+                    }
                 }
             }
         }
-        // P1 = M^T sgy (dq's dense part); its share of dg at the block's first token; P1 += KR^T G1
-        f4 p1, dgacc, p2, p3, dg0, carry, krv;
+        // P1 = M^T sgy (dq's dense part), then P1 += KR^T G1
+        f4 p1, p2, krv;
         {
             f4 pa = zero4(), pb = zero4();
 #pragma unroll
@@ -1262,13 +1326,11 @@ __global__ void __launch_bounds__(NT) colsum_kernel(const Mf128Args a) {
                 }
             }
             p1 = pa + pb;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) dgacc[r] = (&sm.qcI[0][0])[cti(i0 + 4 * g4 + r, lm)] * p1[r];
             const f4 kr4 = ld4(&sm.krI[0][0] + ctq(i0 + lm, g4));
 #pragma unroll
             for (int x = 0; x < 4; ++x) p1 = mfma(kr4[x], sm.g1[4 * g4 + x][lm], p1);
         }
-        // P2 = M^T du; then, with X' (loaded last), P3 = X'^T delta and the column sums of X' .* M
+        // P2 = M^T du; the rank-16 corrections of P2 and P3 through the block's Grams
         {
             f4 p2a = zero4(), p2b = zero4();
 #pragma unroll
@@ -1281,32 +1343,8 @@ __global__ void __launch_bounds__(NT) colsum_kernel(const Mf128Args a) {
                 }
             }
             p2 = p2a + p2b;
-            f4 p3a = zero4(), p3b = zero4();
-            float xa = 0.f, xb = 0.f;
 #pragma unroll
-            for (int jb = 0; jb < 8; jb += 2) {
-                const f4 e0 = ld4(&sm.ee[lm][16 * jb + 4 * g4]), e1 = ld4(&sm.ee[lm][16 * jb + 16 + 4 * g4]);
-#pragma unroll
-                for (int x = 0; x < 4; ++x) {
-                    p3a = mfma(Xc[jb][x], e0[x], p3a);
-                    p3b = mfma(Xc[jb + 1][x], e1[x], p3b);
-                    xa = fmaf(Xc[jb][x], M[jb][x], xa);
-                    xb = fmaf(Xc[jb + 1][x], M[jb + 1][x], xb);
-                }
-            }
-            p3 = p3a + p3b;
-            // dg at the block's first token: the column sums of X .* M with X after the update,
-            // = sum(X' .* M) + sum_t (qc_t P1 + kc_t P2) over the dense parts; dg after the block:
-            // the column sums of X' .* (M + delta kr^T) (X' and the replayed state carry the
-            // block's product inversely) = sum(X' .* M) + sum_t kr_t P3 over the dense part
-            const f4 xm4 = to_tile(rows4_sum(xa + xb));
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int o = cti(i0 + 4 * g4 + r, lm);
-                krv[r] = (&sm.krI[0][0])[o];
-                dg0[r] = xm4[r] + row16_sum(dgacc[r] + (&sm.kcI[0][0])[o] * p2[r]);
-                carry[r] = xm4[r] + row16_sum(krv[r] * p3[r]);
-            }
+            for (int r = 0; r < 4; ++r) krv[r] = (&sm.krI[0][0])[cti(i0 + 4 * g4 + r, lm)];
             const f4 qc4 = ld4(&sm.qcI[0][0] + ctq(i0 + lm, g4)), kr4 = ld4(&sm.krI[0][0] + ctq(i0 + lm, g4)),
                      kc4 = ld4(&sm.kcI[0][0] + ctq(i0 + lm, g4));
             const f4 g1t = f4{sm.g1[lm][4 * g4], sm.g1[lm][4 * g4 + 1], sm.g1[lm][4 * g4 + 2], sm.g1[lm][4 * g4 + 3]};
@@ -1335,17 +1373,19 @@ __global__ void __launch_bounds__(NT) colsum_kernel(const Mf128Args a) {
             dk4[r] = fmaf(rc, p3[r], c * p2[r]);
             inc[r] = (&sm.qcI[0][0])[cti(i, lm)] * p1[r] - krv[r] * p3[r] + (&sm.kcI[0][0])[cti(i, lm)] * p2[r];
         }
-        // suffix sums of the increments over the block's tokens (lanes l%16 upwards)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            inc[r] += row_shl0<1>(inc[r]);
-            inc[r] += row_shl0<2>(inc[r]);
-            inc[r] += row_shl0<4>(inc[r]);
-            inc[r] += row_shl0<8>(inc[r]);
-        }
+        // dg_t = dg at the segment's first token - the increments of the earlier tokens: an
+        // exclusive prefix sum over the block's tokens (lanes l%16 upwards) from the running value
         f4 dgv;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) dgv[r] = lm == 0 ? dg0[r] : carry[r] + inc[r];
+        for (int r = 0; r < 4; ++r) {
+            float v = inc[r];
+            v += row_shr0<1>(v);
+            v += row_shr0<2>(v);
+            v += row_shr0<4>(v);
+            v += row_shr0<8>(v);
+            dgv[r] = dgrun[r] - (v - inc[r]);
+            dgrun[r] -= row_bcast15(v);
+        }
         if (lm < n) {
             const int64_t o = (int64_t)(tw + lm) * (a.H_v * S) + i0 + 4 * g4;
             const int64_t oq = (int64_t)(tw + lm) * qkt + i0 + 4 * g4;
@@ -1391,36 +1431,21 @@ __global__ void __launch_bounds__(NT) colsum_kernel(const Mf128Args a) {
             }
         }
         load_cols(a.snap + (unit * a.n_ck_max + sg) * (int64_t)(S * S), M);
+        dgrun = ld4(a.anc + (unit * a.n_ck_max + sg) * (int64_t)S + i0 + 4 * g4);
+        p3in = a.p3buf + row0 * S;
         Pre P;
         prefetch(P, ts);
         pend_n = 0;
         for (int bb = 0; bb < nb; ++bb) {
             const int t0 = ts + bb * W, cnt = min(W, L - t0);
-            const float *xs = a.xbuf + (unit * nblk + t0 / W) * (int64_t)(S * S);
             const bool dir = P.dir != 0;
-            // a column-scaled block in one step; a token-by-token block one token per step from
-            // the first, the gradient after token tau being X' of the block stepped back over the
-            // block's later tokens
+            // a column-scaled block in one step; a token-by-token block one token per step
             const int nsub = dir ? cnt : 1;
             for (int tau = 0; tau < nsub; ++tau) {
                 ColLds &sm = smb[cur];
-                f4 Xc[8];
                 if (!dir) stage(sm, P, cnt);
-                load_tiles(xs, Xc);   // before the next block's inputs, so its wait leaves them in flight
+                else stage_token(sm, t0, tau);
                 if (tau == 0 && bb + 1 < nb) prefetch(P, t0 + W);
-                if (dir) {
-                    for (int u = cnt - 1; u > tau; --u) {
-                        __syncthreads();
-                        stage_update(sm, t0, u);
-                        __syncthreads();
-                        rank_update(sm, Xc);
-                        const float p = sm.pv[i0 + lm];
-#pragma unroll
-                        for (int jb = 0; jb < 8; ++jb) Xc[jb] *= p;
-                    }
-                    __syncthreads();
-                    stage_token(sm, t0, tau);
-                }
                 __syncthreads();
                 flush(smb[cur ^ 1]);
                 if (dir) {
@@ -1428,7 +1453,7 @@ __global__ void __launch_bounds__(NT) colsum_kernel(const Mf128Args a) {
 #pragma unroll
                     for (int jb = 0; jb < 8; ++jb) M[jb] *= p;
                 }
-                block(sm, Xc, dir ? t0 + tau : t0, dir ? 1 : cnt, dir);
+                block(sm, dir ? t0 + tau : t0, dir ? 1 : cnt, dir);
                 pend_tw = dir ? t0 + tau : t0;
                 pend_n = dir ? 1 : cnt;
                 cur ^= 1;
@@ -1437,6 +1462,19 @@ __global__ void __launch_bounds__(NT) colsum_kernel(const Mf128Args a) {
         __syncthreads();
         flush(smb[cur ^ 1]);
     }
+}
+
+// p[0 .. n) = 0 (n a multiple of 4, p 16-byte aligned); a kernel rather than a memset, so that a
+// captured graph records no memset node
+__global__ void __launch_bounds__(256) zero_kernel(float *p, int64_t n) {
+    for (int64_t i = 4 * ((int64_t)blockIdx.x * 256 + threadIdx.x); i < n; i += 4 * (int64_t)gridDim.x * 256)
+        st4(p + i, zero4());
+}
+hipError_t launch_zero(float *p, int64_t n, hipStream_t st) {
+    if (n <= 0) return hipSuccess;
+    const int blocks = (int)std::min<int64_t>((n / 4 + 255) / 256, 4096);
+    hipLaunchKernelGGL(zero_kernel, dim3(blocks), dim3(256), 0, st, p, n);
+    return hipGetLastError();
 }
 
 template <typename Args>
@@ -1493,8 +1531,15 @@ hipError_t launch_fwd_mf(const Mf128Args &a, hipStream_t st) {
 
 hipError_t launch_bwd_mf(const Mf128Args &a, hipStream_t st) {
     const int units = a.n_seqs_launch * a.H_v;
-    hipError_t e = a.nslab == 2 ? launch(pick<ChainK2>(a.dtype), a, 2 * units, NT / 2, st)
-                                : launch(pick<ChainK>(a.dtype), a, units, NT, st);
+    hipError_t e = hipSuccess;
+    if (a.nslab == 2) {   // the two slabs of a unit add their P3 and dg anchors into zeros
+        e = launch_zero(a.p3buf + (int64_t)a.s_base * a.T * a.H_v * S, (int64_t)units * a.T * S, st);
+        if (e == hipSuccess)
+            e = launch_zero(a.anc + (int64_t)a.s_base * a.H_v * a.n_ck_max * S, (int64_t)units * a.n_ck_max * S, st);
+        if (e == hipSuccess) e = launch(pick<ChainK2>(a.dtype), a, 2 * units, NT / 2, st);
+    } else {
+        e = launch(pick<ChainK>(a.dtype), a, units, NT, st);
+    }
     if (e == hipSuccess) e = launch(pick<ColK>(a.dtype), a, a.n_seqs_launch * a.H_k * a.n_ck_max, NT, st);
     return e;
 }

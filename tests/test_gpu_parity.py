@@ -350,7 +350,9 @@ def test_parity_s128_products_above_range(dev, kda):
 
 
 def test_s128_bitwise_interval_reuse_and_strides(dev):
-    """S = 128: checkpoint interval, snapshot reuse and strided views change no bit."""
+    """S = 128: snapshot reuse, strided views and run-to-run repetition change no bit; the
+    checkpoint interval changes no bit outside dg (dg is summed within each checkpoint segment
+    from its value at the segment's first token, so other intervals round differently)."""
     w = I.Workload("s128_bits", 2, 140, 2, 4, 128, True, 64, -0.3, seq_lens=(140, 70),
                    packed=True, seed=506)
     arrays, _ = I.make_all(w)
@@ -363,7 +365,9 @@ def test_s128_bitwise_interval_reuse_and_strides(dev):
     _, f = run_case(dev, w, arrays, reuse=True, grad_offset=1)
     for n in a:
         assert np.array_equal(a[n], b[n]), ("run-to-run", n)
-        assert np.array_equal(a[n], c[n]), ("C=T", n)
-        assert np.array_equal(a[n], d[n]), ("C=16", n)
-        assert np.array_equal(a[n], e[n]), ("C=100, contiguous, strided gy", n)
         assert np.array_equal(a[n], f[n]), ("unaligned gradient buffer", n)
+        for other, what in ((c, "C=T"), (d, "C=16"), (e, "C=100, contiguous, strided gy")):
+            if n == "dg":
+                check({n: other[n]}, {n: a[n]}, tol=1e-5)
+            else:
+                assert np.array_equal(a[n], other[n]), (what, n)
