@@ -34,7 +34,7 @@ struct Plan {
     bool parts = false;  // small heads: dq/dk go through per-value-head partials
     size_t off_snap = 0, off_seg = 0, off_e = 0, off_pq = 0, off_pk = 0;
     size_t off_wm = 0, off_wf = 0, off_c = 0, off_g1 = 0, off_g2 = 0, off_dbp = 0, off_p3 = 0,
-           off_anc = 0, off_ring = 0;
+           off_anc = 0;
     int nslab = 1;       // head size 128: row slabs per unit of the forward and the chain
     // half-precision inputs: their fp32 copies, contiguous [n_seqs][T][heads][width] each
     size_t off_in = 0, in_q = 0, in_k = 0, in_v = 0, in_g = 0, in_b = 0, in_gy = 0;
@@ -115,8 +115,6 @@ Plan make_plan(const gdn_problem *p) {
         off = align_up(off + tok_rows * S * sizeof(float));
         pl.off_anc = off;  // dg at the first token of every checkpoint segment
         off = align_up(off + (size_t)pl.units * pl.n_ck_max * S * sizeof(float));
-        pl.off_ring = off; // two gradients per chain workgroup, transposed through memory
-        off = align_up(off + (size_t)pl.units * 2 * S * S * sizeof(float));
         // dq and dk go straight to the outputs: the column pass sums the value heads of a key
         // head in one workgroup
         pl.parts = false;
@@ -221,7 +219,6 @@ gdn::Mf128Args mf_args(const gdn_problem *p, const Plan &pl, void *ws, int s0, i
     a.nslab = pl.nslab;
     a.p3buf = (float *)(w + pl.off_p3);
     a.anc = (float *)(w + pl.off_anc);
-    a.ring = (float *)(w + pl.off_ring);
     a.sq = p->q; a.sk = p->k; a.sv = p->v; a.sg = p->g; a.sb = p->beta; a.sgy = p->gy; a.sy = p->y;
     a.s_base = s0; a.n_seqs_launch = cnt;
     a.T = p->T; a.H_k = p->H_k; a.H_v = p->H_v; a.C = pl.C; a.n_ck_max = pl.n_ck_max;

@@ -119,8 +119,6 @@ struct Mf128Args {
     float *p3buf;           // [n_seqs][T][H_v][S] P3 = X'^T delta per token (the chain's column
                             // sums of the state gradient against the token's delta)
     float *anc;             // [unit][n_ck_max][S] dg at each checkpoint segment's first token
-    float *ring;            // [chain workgroup][2][16 NWC][S] the gradient X' of the last two
-                            // steps, transposed through memory (16 x 16 tiles, column-major)
     float *dq, *dk, *dv, *dg, *dbeta, *dstate;   // dq, dk per key head, summed over its value heads
     gdn_strides sq, sk, sv, sg, sb, sgy, sy;
     int32_t s_base, n_seqs_launch, T, H_k, H_v, C, n_ck_max, kda, dtype;

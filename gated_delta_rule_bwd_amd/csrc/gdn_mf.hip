@@ -669,8 +669,9 @@ struct alignas(16) ChainLds {
 template <int DT, int NWC>
 __global__ void __launch_bounds__(64 * NWC) chain_kernel(const Mf128Args a) {
     constexpr int NTC = 64 * NWC, NSL = NW / NWC, R = 16 * NWC;
-    __shared__ ChainLds<NWC> smb[2];
+    __shared__ ChainLds<NWC> sm;       // the staged block (two barriers per block)
     __shared__ float dut[NWC][W][GP];   // each wave's du, [token][row], for its Grams
+    __shared__ f4 tT[R * S / 4];        // the gradient entering the step, for P3 (transposed reads)
     constexpr uint32_t ES = sizeof(In<DT>);
     const int ul = blockIdx.x / NSL, slab = blockIdx.x % NSL;
     const int sl = ul / a.H_v, h = ul % a.H_v;
@@ -695,7 +696,6 @@ __global__ void __launch_bounds__(64 * NWC) chain_kernel(const Mf128Args a) {
     const bool vec_dv = ((uintptr_t)a.dv & 15) == 0;
     float *dbout = NSL > 1 ? a.dbp + row0 * nsl + slab : a.dbeta + row0;   // stride H_v nsl per token
     const int64_t dbt = NSL > 1 ? (int64_t)a.H_v * nsl : a.H_v;
-    float *ringw = a.ring + (int64_t)blockIdx.x * (2 * R * S);   // this workgroup's two gradients
     float *p3out = a.p3buf + row0 * S;                               // token stride H_v S
     float *ancu = a.anc + unit * (int64_t)a.n_ck_max * S;
     float *g1u = a.g1buf + ((s * nblk * a.H_v + h) * nsl + slab) * (int64_t)(W * W);   // block b at b H_v nsl W^2
@@ -833,33 +833,36 @@ __global__ void __launch_bounds__(64 * NWC) chain_kernel(const Mf128Args a) {
 
     // ---- one step of the chain on a staged (sub)block of n tokens from tw: the fold and X'
     // (saved to xs when given), then, once the next block's inputs are in flight, the rest
-    // The gradient entering a step goes to a ring slot at the end of the step before (tile
-    // (wave, ib) column-major: element (row, column) of a tile at 16 column + row), so that after
-    // the staging barrier every wave reads its columns of it with 16-byte loads.
-    auto save_ring = [&](int slot) {
-        float *base = ringw + slot * (R * S) + 256 * 8 * wv + 16 * (4 * g4) + lm;
+    // The gradient entering a step is written to tT after the barrier that ends the step before:
+    // tile (row tile, column tile) at 256 (8 rt + ct), element (rho, sigma) of a tile at
+    // (16 rho + sigma) ^ (((rho >> 1) & 7) << 2), so that a lane's four columns of a row stay one
+    // 16-byte write and the column reads (one element per lane, four rows per lane) spread over
+    // the banks.
+    auto swz = [](int rho, int sigma) { return (16 * rho + sigma) ^ (((rho >> 1) & 7) << 2); };
+    auto save_T = [&]() {
+        float *base = reinterpret_cast<float *>(tT) + 256 * 8 * wv + swz(lm, 4 * g4);
 #pragma unroll
-        for (int ib = 0; ib < 8; ++ib)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) base[256 * ib + 16 * r] = X[ib][r];
+        for (int ib = 0; ib < 8; ++ib) st4(base + 256 * ib, X[ib]);
     };
     auto fold = [&](const ChainLds<NWC> &sm) {
 #pragma unroll
         for (int ib = 0; ib < 8; ++ib) X[ib] *= ld4(&sm.pv[16 * ib + 4 * g4]);
     };
     // P3 = X'^T delta of a step over the workgroup's rows, X' = X diag(pv) the folded gradient
-    // (pv = 1 for a token-by-token step): diag(pv) (X^T delta) with X from the ring.  Wave w takes
+    // (pv = 1 for a token-by-token step): diag(pv) (X^T delta) with X from tT.  Wave w takes
     // the column tiles CT w .. CT w + CT - 1, each a contraction over the workgroup's NWC row tiles;
     // lane l, register r: column 16 ct + 4(l/16) + r, token l%16.  Two row slabs add their halves
     // into a zeroed buffer (two terms: the order does not change the sum).
     constexpr int CT = 8 / NWC;
     f4 xa[CT][NWC];
-    auto p3_load = [&](int slot) {
-        const float *base = ringw + slot * (R * S) + 16 * lm + 4 * g4;
+    auto p3_load = [&]() {
+        const float *tf = reinterpret_cast<const float *>(tT);
 #pragma unroll
         for (int c = 0; c < CT; ++c)
 #pragma unroll
-            for (int rt = 0; rt < NWC; ++rt) xa[c][rt] = ld4(base + 256 * (8 * rt + CT * wv + c));
+            for (int rt = 0; rt < NWC; ++rt)
+#pragma unroll
+                for (int x = 0; x < 4; ++x) xa[c][rt][x] = tf[256 * (8 * rt + CT * wv + c) + swz(4 * g4 + x, lm)];
     };
     auto p3_finish = [&](const ChainLds<NWC> &sm, int tw, int n, bool fold_pv) {
         f4 dP[NWC];
@@ -901,9 +904,8 @@ __global__ void __launch_bounds__(64 * NWC) chain_kernel(const Mf128Args a) {
         anc_pend = true;
         anc_sg = sgi;
     };
-    int wslot = 1;   // ring slot of the gradient entering the next step
     // mid(): work that needs no result of the step (the step's P3), placed after dd so that the
-    // ring loads it waits for have had the dd products' time to arrive
+    // loads of tT it waits for have had the dd products' time to arrive
     auto step = [&](ChainLds<NWC> &sm, int tw, int n, bool dir, auto &&mid) {
         f4 d0 = zero4(), d1 = zero4();
 #pragma unroll
@@ -955,7 +957,6 @@ __global__ void __launch_bounds__(64 * NWC) chain_kernel(const Mf128Args a) {
 #pragma unroll
             for (int ib = 0; ib < 8; ++ib) X[ib] *= ld4(&sm.pv[16 * ib + 4 * g4]);
         }
-        save_ring(wslot);   // the gradient entering the next step, early for the next barrier
         // the Grams over the wave's rows: delta^T (row s = l%16, the wave's rows along the
         // contraction) times scale gy and du (column t = l%16)
         {
@@ -1031,48 +1032,47 @@ __global__ void __launch_bounds__(64 * NWC) chain_kernel(const Mf128Args a) {
         }
     };
 
+    // Per step: staging, barrier, P3 and the step (all waves read the staged block and tT), barrier,
+    // then the sums over the waves (flush) and the gradient entering the next step into tT.
     Pre P;
     const int nb = (L + W - 1) / W;
-    int cur = 0;
-    save_ring(0);   // the gradient entering the last block
+    save_T();   // the gradient entering the last block
     if (nb > 0) prefetch(P, (nb - 1) * W);
     for (int b = nb - 1; b >= 0; --b) {
         const int t0 = b * W, cnt = min(W, L - t0);
         const bool dir = P.dir != 0;
         if (!dir) {
-            stage(smb[cur], P, cnt);
+            stage(sm, P, cnt);
             __syncthreads();
-            flush(smb[cur ^ 1]);
-            p3_load(wslot ^ 1);
-            fold(smb[cur]);
+            p3_load();
+            fold(sm);
             if (b > 0) prefetch(P, t0 - W);
-            step(smb[cur], t0, cnt, false, [&] { p3_finish(smb[cur], t0, cnt, true); });
-            wslot ^= 1;
-            if (t0 % a.C == 0) anchor_part(smb[cur], t0 / a.C);
+            step(sm, t0, cnt, false, [&] { p3_finish(sm, t0, cnt, true); });
+            if (t0 % a.C == 0) anchor_part(sm, t0 / a.C);
             pend_t0 = t0;
             pend_tau = -1;
             pend_n = cnt;
-            cur ^= 1;
+            __syncthreads();
+            flush(sm);
+            save_T();
         } else {
             if (b > 0) prefetch(P, t0 - W);
             for (int u = 0; u < cnt; ++u) {
                 const int tau = cnt - 1 - u;
-                stage_token(smb[cur], t0, tau);
+                stage_token(sm, t0, tau);
                 __syncthreads();
-                flush(smb[cur ^ 1]);
-                p3_load(wslot ^ 1);
-                step(smb[cur], t0 + tau, 1, true, [&] { p3_finish(smb[cur], t0 + tau, 1, false); });
-                wslot ^= 1;
-                if (tau == 0 && t0 % a.C == 0) anchor_part(smb[cur], t0 / a.C);
+                p3_load();
+                step(sm, t0 + tau, 1, true, [&] { p3_finish(sm, t0 + tau, 1, false); });
+                if (tau == 0 && t0 % a.C == 0) anchor_part(sm, t0 / a.C);
                 pend_t0 = t0;
                 pend_tau = tau;
                 pend_n = 1;
-                cur ^= 1;
+                __syncthreads();
+                flush(sm);
+                save_T();
             }
         }
     }
-    __syncthreads();
-    flush(smb[cur ^ 1]);
     {   // the gradient before token 0
         float *p = a.dstate + unit * S * S + (int64_t)(j0 + lm) * S + 4 * g4;
 #pragma unroll
