@@ -34,8 +34,9 @@ struct Plan {
     bool parts = false;  // small heads: dq/dk go through per-value-head partials
     size_t off_snap = 0, off_seg = 0, off_e = 0, off_pq = 0, off_pk = 0;
     size_t off_wm = 0, off_wf = 0, off_c = 0, off_g1 = 0, off_g2 = 0, off_dbp = 0, off_p3 = 0,
-           off_anc = 0;
+           off_anc = 0, off_carry = 0;
     int nslab = 1;       // head size 128: row slabs per unit of the forward and the chain
+    int piece = 1;       // head size 128: tokens per piece of the pipelined passes (a multiple of C)
     // half-precision inputs: their fp32 copies, contiguous [n_seqs][T][heads][width] each
     size_t off_in = 0, in_q = 0, in_k = 0, in_v = 0, in_g = 0, in_b = 0, in_gy = 0;
     size_t total = 0;
@@ -115,6 +116,12 @@ Plan make_plan(const gdn_problem *p) {
         off = align_up(off + tok_rows * S * sizeof(float));
         pl.off_anc = off;  // dg at the first token of every checkpoint segment
         off = align_up(off + (size_t)pl.units * pl.n_ck_max * S * sizeof(float));
+        pl.off_carry = off;   // the state or gradient between the pieces of a pipelined pass
+        off = align_up(off + (size_t)pl.units * S * S * sizeof(float));
+        // pieces of about 1024 tokens, at most 16, each a whole number of checkpoint segments
+        const int64_t np = std::min<int64_t>(16, std::max<int64_t>(1, p->T / 1024));
+        const int64_t per = (p->T + np - 1) / np;
+        pl.piece = (int)std::max<int64_t>(pl.C, (per + pl.C - 1) / pl.C * pl.C);
         // dq and dk go straight to the outputs: the column pass sums the value heads of a key
         // head in one workgroup
         pl.parts = false;
@@ -219,6 +226,9 @@ gdn::Mf128Args mf_args(const gdn_problem *p, const Plan &pl, void *ws, int s0, i
     a.nslab = pl.nslab;
     a.p3buf = (float *)(w + pl.off_p3);
     a.anc = (float *)(w + pl.off_anc);
+    a.carry = (float *)(w + pl.off_carry);
+    a.t_lo = 0;
+    a.t_hi = p->T;
     a.sq = p->q; a.sk = p->k; a.sv = p->v; a.sg = p->g; a.sb = p->beta; a.sgy = p->gy; a.sy = p->y;
     a.s_base = s0; a.n_seqs_launch = cnt;
     a.T = p->T; a.H_k = p->H_k; a.H_v = p->H_v; a.C = pl.C; a.n_ck_max = pl.n_ck_max;
@@ -228,17 +238,117 @@ gdn::Mf128Args mf_args(const gdn_problem *p, const Plan &pl, void *ws, int s0, i
     return a;
 }
 
-// Block preparation and forward scan of the head-128 kernels (y null: snapshots and errors only).
+// Second stream and events of the pipelined head-128 passes, one set per device, created on
+// first use (default priority) and kept until the process ends.  A call holds its device's lock
+// while it enqueues, so calls from several host threads take turns.
+constexpr int kMaxSideDevices = 64, kSideEvents = 64;
+struct Side {
+    hipStream_t s = nullptr;
+    hipEvent_t ev[kSideEvents] = {};
+    int next = 0;
+    hipEvent_t take() {
+        hipEvent_t e = ev[next];
+        next = (next + 1) % kSideEvents;
+        return e;
+    }
+};
+std::mutex g_side_mu[kMaxSideDevices];
+Side g_side[kMaxSideDevices];
+
+int side_for(hipStream_t st, std::unique_lock<std::mutex> &lk, Side **out) {
+    int dev = -1, cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess) return GDN_ERR_DEVICE;
+    if (hipStreamGetDevice(st, &dev) != hipSuccess) dev = cur;
+    if (dev < 0 || dev >= kMaxSideDevices) return GDN_ERR_DEVICE;
+    lk = std::unique_lock<std::mutex>(g_side_mu[dev]);
+    Side &sd = g_side[dev];
+    if (!sd.s) {
+        if (dev != cur && hipSetDevice(dev) != hipSuccess) return GDN_ERR_DEVICE;
+        bool ok = hipStreamCreateWithFlags(&sd.s, hipStreamNonBlocking) == hipSuccess;
+        for (int i = 0; ok && i < kSideEvents; ++i)
+            ok = hipEventCreateWithFlags(&sd.ev[i], hipEventDisableTiming) == hipSuccess;
+        if (dev != cur && hipSetDevice(cur) != hipSuccess) ok = false;
+        if (!ok) return GDN_ERR_DEVICE;
+    }
+    *out = &sd;
+    return GDN_OK;
+}
+// work enqueued on `to` from now on waits for everything enqueued on `from` so far
+int order_after(Side &sd, hipStream_t from, hipStream_t to) {
+    hipEvent_t e = sd.take();
+    if (hipEventRecord(e, from) != hipSuccess || hipStreamWaitEvent(to, e, 0) != hipSuccess) return GDN_ERR_DEVICE;
+    return GDN_OK;
+}
+gdn::Mf128Args piece_of(gdn::Mf128Args a, int t_lo, int t_hi) {
+    a.t_lo = t_lo;
+    a.t_hi = t_hi;
+    return a;
+}
+
+// Block preparation and forward scan of the head-128 kernels (y null: snapshots and errors
+// only).  Pipelined: the token axis in pieces, the preparation of the next piece on the second
+// stream while the forward walks the current one on st.
 int mf_forward(const gdn_problem *p, const Plan &pl, void *ws, const void *q, const void *k,
                const void *v, const void *g, const void *beta, const float *state0, float *y,
-               float *state_out, hipStream_t st) {
+               float *state_out, hipStream_t st, bool pipelined) {
+    const int T = p->T, PT = pl.piece, np = (T + PT - 1) / PT;
     for (int s0 = 0; s0 < p->n_seqs; s0 += gdn::kMaxSeqsPerLaunch) {
         const int cnt = std::min(gdn::kMaxSeqsPerLaunch, p->n_seqs - s0);
         gdn::Mf128Args a = mf_args(p, pl, ws, s0, cnt);
         a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.state0 = state0;
         a.y = y; a.state_out = state_out;
-        int rc = device_status(gdn::launch_prep128(a, st));
-        if (rc == GDN_OK) rc = device_status(gdn::launch_fwd_mf(a, st));
+        if (!pipelined || np <= 1) {
+            int rc = device_status(gdn::launch_prep128(a, st));
+            if (rc == GDN_OK) rc = device_status(gdn::launch_fwd_mf(a, st));
+            if (rc != GDN_OK) return rc;
+            continue;
+        }
+        std::unique_lock<std::mutex> lk;
+        Side *sd = nullptr;
+        int rc = side_for(st, lk, &sd);
+        if (rc == GDN_OK) rc = order_after(*sd, st, sd->s);
+        if (rc == GDN_OK) rc = device_status(gdn::launch_prep128(piece_of(a, 0, PT), st));
+        for (int j = 0; rc == GDN_OK && j < np; ++j) {
+            if (j + 1 < np)
+                rc = device_status(gdn::launch_prep128(piece_of(a, (j + 1) * PT, std::min(T, (j + 2) * PT)), sd->s));
+            if (rc == GDN_OK && j > 0) rc = order_after(*sd, sd->s, st);   // piece j prepared
+            if (rc == GDN_OK) rc = device_status(gdn::launch_fwd_mf(piece_of(a, j * PT, std::min(T, (j + 1) * PT)), st));
+        }
+        if (rc != GDN_OK) return rc;
+    }
+    return GDN_OK;
+}
+
+// The chain and the column sums of the head-128 backward.  Pipelined: the chain walks the pieces
+// from the last on st, and the column sums of each piece run on the second stream as soon as the
+// chain has passed it.
+int mf_backward(const gdn_problem *p, const Plan &pl, void *ws, gdn::Mf128Args a, hipStream_t st,
+                bool pipelined) {
+    const int T = p->T, PT = pl.piece, np = (T + PT - 1) / PT;
+    for (int s0 = 0; s0 < p->n_seqs; s0 += gdn::kMaxSeqsPerLaunch) {
+        const int cnt = std::min(gdn::kMaxSeqsPerLaunch, p->n_seqs - s0);
+        gdn::Mf128Args b = mf_args(p, pl, ws, s0, cnt);
+        b.q = a.q; b.k = a.k; b.v = a.v; b.g = a.g; b.beta = a.beta; b.gy = a.gy;
+        b.state0 = a.state0; b.dstate_out = a.dstate_out;
+        b.dq = a.dq; b.dk = a.dk; b.dv = a.dv; b.dg = a.dg; b.dbeta = a.dbeta; b.dstate = a.dstate;
+        int rc = device_status(gdn::launch_zero_bwd(b, st));
+        if (rc != GDN_OK) return rc;
+        if (!pipelined || np <= 1) {
+            rc = device_status(gdn::launch_chain(b, st));
+            if (rc == GDN_OK) rc = device_status(gdn::launch_colsum(b, st));
+            if (rc != GDN_OK) return rc;
+            continue;
+        }
+        std::unique_lock<std::mutex> lk;
+        Side *sd = nullptr;
+        rc = side_for(st, lk, &sd);
+        for (int j = np - 1; rc == GDN_OK && j >= 0; --j) {
+            const gdn::Mf128Args bj = piece_of(b, j * PT, std::min(T, (j + 1) * PT));
+            rc = device_status(gdn::launch_chain(bj, st));
+            if (rc == GDN_OK) rc = order_after(*sd, st, sd->s);
+            if (rc == GDN_OK) rc = device_status(gdn::launch_colsum(bj, sd->s));
+        }
+        if (rc == GDN_OK) rc = order_after(*sd, sd->s, st);   // st waits for the last column sums
         if (rc != GDN_OK) return rc;
     }
     return GDN_OK;
@@ -380,7 +490,7 @@ int gdn_fwd(const gdn_problem *p, const void *q_in, const void *k_in, const void
 
     if (pl.s128)   // head size 128: the matrix-core kernels read every input type directly
         return mf_forward(p, pl, ws, q_in, k_in, v_in, g_in, beta_in, state0, y, state_out,
-                          (hipStream_t)stream);
+                          (hipStream_t)stream, true);
 
     // half-precision inputs: widened into the workspace, then the fp32 path on the copies
     gdn_problem pc = *p;
@@ -413,10 +523,15 @@ int gdn_fwd(const gdn_problem *p, const void *q_in, const void *k_in, const void
     return GDN_OK;
 }
 
-int gdn_bwd(const gdn_problem *p, const void *q_in, const void *k_in, const void *v_in,
-            const void *g_in, const void *beta_in, const float *state0, const void *gy_in,
-            const float *dstate_out, float *grad_packed, void *ws, size_t ws_bytes,
-            unsigned flags, gdn_stream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// gdn_bwd; pipelined: the head-128 passes may use the device's second stream
+int bwd_impl(const gdn_problem *p, const void *q_in, const void *k_in, const void *v_in,
+             const void *g_in, const void *beta_in, const float *state0, const void *gy_in,
+             const float *dstate_out, float *grad_packed, void *ws, size_t ws_bytes,
+             unsigned flags, gdn_stream_t stream, bool pipelined) {
     int rc = validate(p);
     if (rc != GDN_OK) return rc;
     if (flags & ~GDN_BWD_REUSE_SNAPSHOTS) return GDN_ERR_ARG;
@@ -452,19 +567,15 @@ int gdn_bwd(const gdn_problem *p, const void *q_in, const void *k_in, const void
     if (pl.s128) {   // head size 128: matrix-core kernels, every input type read directly
         if (!(flags & GDN_BWD_REUSE_SNAPSHOTS)) {
             rc = mf_forward(p, pl, ws, q_in, k_in, v_in, g_in, beta_in, state0, nullptr, nullptr,
-                            (hipStream_t)stream);
+                            (hipStream_t)stream, pipelined);
             if (rc != GDN_OK) return rc;
         }
-        for (int s0 = 0; s0 < p->n_seqs; s0 += gdn::kMaxSeqsPerLaunch) {
-            const int cnt = std::min(gdn::kMaxSeqsPerLaunch, p->n_seqs - s0);
-            gdn::Mf128Args a = mf_args(p, pl, ws, s0, cnt);
-            a.q = q_in; a.k = k_in; a.v = v_in; a.g = g_in; a.beta = beta_in; a.gy = gy_in;
-            a.state0 = state0; a.dstate_out = dstate_out;
-            a.dq = dq; a.dk = dk; a.dv = dv; a.dg = dg; a.dbeta = dbeta; a.dstate = dstate;
-            rc = device_status(gdn::launch_bwd_mf(a, (hipStream_t)stream));
-            if (rc != GDN_OK) return rc;
-        }
-        return rc;
+        gdn::Mf128Args a;
+        std::memset(&a, 0, sizeof(a));
+        a.q = q_in; a.k = k_in; a.v = v_in; a.g = g_in; a.beta = beta_in; a.gy = gy_in;
+        a.state0 = state0; a.dstate_out = dstate_out;
+        a.dq = dq; a.dk = dk; a.dv = dv; a.dg = dg; a.dbeta = dbeta; a.dstate = dstate;
+        return mf_backward(p, pl, ws, a, (hipStream_t)stream, pipelined);
     }
 
     // half-precision inputs of the small-head kernels: gy widened into the workspace, and q, k,
@@ -536,6 +647,18 @@ int gdn_bwd(const gdn_problem *p, const void *q_in, const void *k_in, const void
         if (rc != GDN_OK) return rc;
     }
     return GDN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gdn_bwd(const gdn_problem *p, const void *q_in, const void *k_in, const void *v_in,
+            const void *g_in, const void *beta_in, const float *state0, const void *gy_in,
+            const float *dstate_out, float *grad_packed, void *ws, size_t ws_bytes,
+            unsigned flags, gdn_stream_t stream) {
+    return bwd_impl(p, q_in, k_in, v_in, g_in, beta_in, state0, gy_in, dstate_out, grad_packed,
+                    ws, ws_bytes, flags, stream, true);
 }
 
 static int conv_check(const gdn_conv_problem *p, const void *in, const void *c, const void *out,
@@ -779,8 +902,9 @@ int gdn_bwd_noalloc(const gdn_problem *p, const void *q, const void *k, const vo
     void *ws = nullptr;
     const int rs = scratch_address((hipStream_t)stream, &ws);
     if (rs != GDN_OK) return rs;
-    return gdn_bwd(p, q, k, v, g, beta, state0, gy, dstate_out, grad_packed, ws,
-                   GDN_NOALLOC_SCRATCH_BYTES, 0u, stream);
+    // one stream: no second stream or events are created on this path
+    return bwd_impl(p, q, k, v, g, beta, state0, gy, dstate_out, grad_packed, ws,
+                    GDN_NOALLOC_SCRATCH_BYTES, 0u, stream, false);
 }
 
 }  // extern "C"

@@ -123,11 +123,16 @@ struct Mf128Args {
     gdn_strides sq, sk, sv, sg, sb, sgy, sy;
     int32_t s_base, n_seqs_launch, T, H_k, H_v, C, n_ck_max, kda, dtype;
     int32_t nslab;          // row slabs per unit of the forward and the chain: 1 or 2
+    int32_t t_lo, t_hi;     // tokens of this launch: [t_lo, t_hi), t_lo a multiple of 16 (of C
+                            // for the chain and the column pass); 0 and T for a whole pass
+    float *carry;           // [unit][S][S] state (forward) or gradient (chain) between launches
     float scale;
     int32_t lens[kMaxSeqsPerLaunch];
 };
 hipError_t launch_prep128(const Mf128Args &a, hipStream_t st);
 hipError_t launch_fwd_mf(const Mf128Args &a, hipStream_t st);
-hipError_t launch_bwd_mf(const Mf128Args &a, hipStream_t st);   // the chain, then the column sums
+hipError_t launch_zero_bwd(const Mf128Args &a, hipStream_t st);  // before the first chain launch
+hipError_t launch_chain(const Mf128Args &a, hipStream_t st);     // the chain over [t_lo, t_hi)
+hipError_t launch_colsum(const Mf128Args &a, hipStream_t st);    // the column sums of its segments
 
 }  // namespace gdn

@@ -219,7 +219,8 @@ __global__ void __launch_bounds__(64 * PW) prep128_kernel(const Mf128Args a) {
     const int nblk = (a.T + W - 1) / W;
     const int G = a.kda ? S : 1;
     const bool kda = a.kda != 0;
-    const int64_t items = (int64_t)a.n_seqs_launch * nblk * a.H_v;
+    const int b_lo = a.t_lo / W, nbp = min(nblk, (a.t_hi + W - 1) / W) - b_lo;   // the launch's blocks
+    const int64_t items = (int64_t)a.n_seqs_launch * nbp * a.H_v;
     // rows whose starts are all aligned to four elements take vector loads
     auto aligned_rows = [&](const void *p, const gdn_strides &st) {
         return (((uintptr_t)p & (4 * ES - 1)) == 0) && st.seq % 4 == 0 && st.tok % 4 == 0 && st.head % 4 == 0;
@@ -257,7 +258,7 @@ __global__ void __launch_bounds__(64 * PW) prep128_kernel(const Mf128Args a) {
     for (int64_t it = (int64_t)blockIdx.x * PW + wv; it < items; it += (int64_t)gridDim.x * PW) {
         const int h = (int)(it % a.H_v);
         const int64_t rest = it / a.H_v;
-        const int b = (int)(rest % nblk), sl = (int)(rest / nblk);
+        const int b = b_lo + (int)(rest % nbp), sl = (int)(rest / nbp);
         const int t0 = b * W, cnt = min(W, a.lens[sl] - t0);
         if (cnt <= 0) continue;
         const int64_t s = a.s_base + sl;
@@ -419,12 +420,15 @@ __global__ void __launch_bounds__(64 * NWC) fwd_mf_kernel(const Mf128Args a) {
                    et = (uint32_t)(a.H_v * S) * 4;
     const uint32_t ccol = (a.kda ? (uint32_t)ci : 0u) * 4;
 
+    // the state entering the launch's tokens: state0 at the sequence's start, else the carry
+    const bool from_carry = a.t_lo > 0;
+    const int t_end = min(L, a.t_hi);   // the launch's last token (exclusive) of this sequence
     f4 M[S / 16];
     {
-        const float *p = a.state0 + unit * S * S + (int64_t)(j0 + lm) * S + 4 * g4;
+        const float *p = (from_carry ? a.carry : a.state0) + unit * S * S + (int64_t)(j0 + lm) * S + 4 * g4;
 #pragma unroll
         for (int ib = 0; ib < S / 16; ++ib) {
-            if (vec_state) M[ib] = ld4(p + 16 * ib);
+            if (vec_state || from_carry) M[ib] = ld4(p + 16 * ib);
             else M[ib] = f4{p[16 * ib], p[16 * ib + 1], p[16 * ib + 2], p[16 * ib + 3]};
         }
     }
@@ -526,8 +530,8 @@ __global__ void __launch_bounds__(64 * NWC) fwd_mf_kernel(const Mf128Args a) {
     // of a token-by-token block) orders the writes and the reads.
     Pre P;
     int cur = 0;
-    if (L > 0) prefetch(P, 0);
-    for (int b = 0; b * W < L; ++b) {
+    if (a.t_lo < t_end) prefetch(P, a.t_lo);
+    for (int b = a.t_lo / W; b * W < t_end; ++b) {
         const int t0 = b * W, cnt = min(W, L - t0);
         if (t0 % a.C == 0) store_state(snap + (int64_t)(t0 / a.C) * S * S);
         if (!P.dir) {
@@ -555,7 +559,7 @@ __global__ void __launch_bounds__(64 * NWC) fwd_mf_kernel(const Mf128Args a) {
             }
             const float teA[4] = {P.te[0], P.te[1], P.te[2], P.te[3]}, bmA[4] = {P.bm[0], P.bm[1], P.bm[2], P.bm[3]};
             __syncthreads();
-            if (t0 + W < L) prefetch(P, t0 + W);   // the registers are free again
+            if (t0 + W < t_end) prefetch(P, t0 + W);   // the registers are free again
             block(sm, t0, cnt, vv, bb, teA, bmA);
             scale_state(sm);
             cur ^= 1;
@@ -593,17 +597,20 @@ __global__ void __launch_bounds__(64 * NWC) fwd_mf_kernel(const Mf128Args a) {
                 block(sm, t0 + tau, 1, vv, bb, teA, bmA);
                 cur ^= 1;
             }
-            if (t0 + W < L) prefetch(P, t0 + W);
+            if (t0 + W < t_end) prefetch(P, t0 + W);
         }
     }
-    if (yout) {   // padded tokens: the workgroup's rows
+    if (yout) {   // padded tokens of the launch: the workgroup's rows
         constexpr int R = 16 * NWC;
-        for (int64_t idx = tid; idx < (int64_t)(a.T - L) * R; idx += NTC) {
-            const int64_t t = L + idx / R;
+        const int p0 = max(L, a.t_lo), p1 = min(a.T, a.t_hi);
+        for (int64_t idx = tid; idx < (int64_t)max(0, p1 - p0) * R; idx += NTC) {
+            const int64_t t = p0 + idx / R;
             yout[t * a.sy.tok + 16 * NWC * slab + (int)(idx % R)] = 0.f;
         }
     }
-    if (a.state_out) {
+    if (a.t_hi < a.T) {   // the state after the launch's tokens, for the next launch
+        store_state(a.carry + unit * S * S);
+    } else if (a.state_out) {
         if (vec_state) {
             store_state(a.state_out + unit * S * S);
         } else {
@@ -703,8 +710,15 @@ __global__ void __launch_bounds__(64 * NWC) chain_kernel(const Mf128Args a) {
     const uint32_t ct = (uint32_t)(a.H_v * G) * 4, kt = (uint32_t)a.sk.tok * ES, qt = (uint32_t)a.sq.tok * ES,
                    gyt = (uint32_t)a.sgy.tok * ES, bt = (uint32_t)a.sb.tok * ES, et = (uint32_t)a.H_v * S * 4;
 
+    // the gradient entering the launch's tokens (walking backwards): dstate_out after the
+    // sequence's end, else the carry from the launch of the later tokens
+    const bool from_carry = a.t_hi < a.T;
     f4 X[8];
-    if (a.dstate_out) {
+    if (from_carry) {
+        const float *p = a.carry + unit * S * S + (int64_t)(j0 + lm) * S + 4 * g4;
+#pragma unroll
+        for (int ib = 0; ib < 8; ++ib) X[ib] = ld4(p + 16 * ib);
+    } else if (a.dstate_out) {
         const float *p = a.dstate_out + unit * S * S + (int64_t)(j0 + lm) * S + 4 * g4;
 #pragma unroll
         for (int ib = 0; ib < 8; ++ib) X[ib] = f4{p[16 * ib], p[16 * ib + 1], p[16 * ib + 2], p[16 * ib + 3]};
@@ -1035,10 +1049,10 @@ __global__ void __launch_bounds__(64 * NWC) chain_kernel(const Mf128Args a) {
     // Per step: staging, barrier, P3 and the step (all waves read the staged block and tT), barrier,
     // then the sums over the waves (flush) and the gradient entering the next step into tT.
     Pre P;
-    const int nb = (L + W - 1) / W;
+    const int nb = min((L + W - 1) / W, (a.t_hi + W - 1) / W), b_lo = a.t_lo / W;   // the launch's blocks
     save_T();   // the gradient entering the last block
-    if (nb > 0) prefetch(P, (nb - 1) * W);
-    for (int b = nb - 1; b >= 0; --b) {
+    if (nb > b_lo) prefetch(P, (nb - 1) * W);
+    for (int b = nb - 1; b >= b_lo; --b) {
         const int t0 = b * W, cnt = min(W, L - t0);
         const bool dir = P.dir != 0;
         if (!dir) {
@@ -1046,7 +1060,7 @@ __global__ void __launch_bounds__(64 * NWC) chain_kernel(const Mf128Args a) {
             __syncthreads();
             p3_load();
             fold(sm);
-            if (b > 0) prefetch(P, t0 - W);
+            if (b > b_lo) prefetch(P, t0 - W);
             step(sm, t0, cnt, false, [&] { p3_finish(sm, t0, cnt, true); });
             if (t0 % a.C == 0) anchor_part(sm, t0 / a.C);
             pend_t0 = t0;
@@ -1056,7 +1070,7 @@ __global__ void __launch_bounds__(64 * NWC) chain_kernel(const Mf128Args a) {
             flush(sm);
             save_T();
         } else {
-            if (b > 0) prefetch(P, t0 - W);
+            if (b > b_lo) prefetch(P, t0 - W);
             for (int u = 0; u < cnt; ++u) {
                 const int tau = cnt - 1 - u;
                 stage_token(sm, t0, tau);
@@ -1073,15 +1087,20 @@ __global__ void __launch_bounds__(64 * NWC) chain_kernel(const Mf128Args a) {
             }
         }
     }
-    {   // the gradient before token 0
+    if (a.t_lo > 0) {   // the gradient before the launch's tokens, for the next launch
+        float *p = a.carry + unit * S * S + (int64_t)(j0 + lm) * S + 4 * g4;
+#pragma unroll
+        for (int ib = 0; ib < 8; ++ib) st4(p + 16 * ib, X[ib]);
+    } else {   // the gradient before token 0
         float *p = a.dstate + unit * S * S + (int64_t)(j0 + lm) * S + 4 * g4;
 #pragma unroll
         for (int ib = 0; ib < 8; ++ib)
 #pragma unroll
             for (int r = 0; r < 4; ++r) p[16 * ib + r] = X[ib][r];
     }
-    for (int64_t idx = tid; idx < (int64_t)(a.T - L) * R; idx += NTC) {   // padded tokens
-        const int64_t row = (int64_t)(L + idx / R) * a.H_v;
+    const int pad0 = max(L, a.t_lo), pad1 = min(a.T, a.t_hi);   // padded tokens of the launch
+    for (int64_t idx = tid; idx < (int64_t)max(0, pad1 - pad0) * R; idx += NTC) {
+        const int64_t row = (int64_t)(pad0 + idx / R) * a.H_v;
         const int i = (int)(idx % R);
         dvout[row * S + r0 + i] = 0.f;
         if (slab == 0 && i == 0) a.dbeta[row0 + row] = 0.f;
@@ -1110,7 +1129,7 @@ __global__ void __launch_bounds__(NT) colsum_kernel(const Mf128Args a) {
     // one workgroup per (sequence, key head, segment): the value heads hk, hk + H_k, .. of the
     // key head one after the other, each adding its dq and dk to the key head's sums
     const int groups = a.n_seqs_launch * a.H_k;
-    const int gl = blockIdx.x % groups, sg = blockIdx.x / groups;
+    const int gl = blockIdx.x % groups, sg = a.t_lo / a.C + blockIdx.x / groups;
     const int sl = gl / a.H_k, hk = gl % a.H_k;
     const int64_t s = a.s_base + sl;
     const int L = a.lens[sl];
@@ -1518,7 +1537,8 @@ struct ColK {
 }  // namespace
 
 hipError_t launch_prep128(const Mf128Args &a, hipStream_t st) {
-    const int64_t items = (int64_t)a.n_seqs_launch * ((a.T + W - 1) / W) * a.H_v;
+    const int nblk = (a.T + W - 1) / W;
+    const int64_t items = (int64_t)a.n_seqs_launch * (std::min(nblk, (a.t_hi + W - 1) / W) - a.t_lo / W) * a.H_v;
     const int blocks = (int)std::min<int64_t>((items + PW - 1) / PW, 16384);
     return launch(pick<PrepK>(a.dtype), a, blocks, 64 * PW, st);
 }
@@ -1529,19 +1549,24 @@ hipError_t launch_fwd_mf(const Mf128Args &a, hipStream_t st) {
     return launch(pick<FwdK>(a.dtype), a, units, NT, st);
 }
 
-hipError_t launch_bwd_mf(const Mf128Args &a, hipStream_t st) {
-    const int units = a.n_seqs_launch * a.H_v;
-    hipError_t e = hipSuccess;
-    if (a.nslab == 2) {   // the two slabs of a unit add their P3 and dg anchors into zeros
-        e = launch_zero(a.p3buf + (int64_t)a.s_base * a.T * a.H_v * S, (int64_t)units * a.T * S, st);
-        if (e == hipSuccess)
-            e = launch_zero(a.anc + (int64_t)a.s_base * a.H_v * a.n_ck_max * S, (int64_t)units * a.n_ck_max * S, st);
-        if (e == hipSuccess) e = launch(pick<ChainK2>(a.dtype), a, 2 * units, NT / 2, st);
-    } else {
-        e = launch(pick<ChainK>(a.dtype), a, units, NT, st);
-    }
-    if (e == hipSuccess) e = launch(pick<ColK>(a.dtype), a, a.n_seqs_launch * a.H_k * a.n_ck_max, NT, st);
+hipError_t launch_zero_bwd(const Mf128Args &a, hipStream_t st) {
+    // the two slabs of a unit add their P3 and segment dg into zeros
+    if (a.nslab != 2) return hipSuccess;
+    const int64_t units = (int64_t)a.n_seqs_launch * a.H_v;
+    hipError_t e = launch_zero(a.p3buf + (int64_t)a.s_base * a.T * a.H_v * S, units * a.T * S, st);
+    if (e == hipSuccess) e = launch_zero(a.anc + (int64_t)a.s_base * a.H_v * a.n_ck_max * S, units * a.n_ck_max * S, st);
     return e;
+}
+
+hipError_t launch_chain(const Mf128Args &a, hipStream_t st) {
+    const int units = a.n_seqs_launch * a.H_v;
+    return a.nslab == 2 ? launch(pick<ChainK2>(a.dtype), a, 2 * units, NT / 2, st)
+                        : launch(pick<ChainK>(a.dtype), a, units, NT, st);
+}
+
+hipError_t launch_colsum(const Mf128Args &a, hipStream_t st) {
+    const int segs = (std::min(a.t_hi, a.T) + a.C - 1) / a.C - a.t_lo / a.C;
+    return launch(pick<ColK>(a.dtype), a, a.n_seqs_launch * a.H_k * segs, NT, st);
 }
 
 }  // namespace gdn

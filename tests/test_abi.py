@@ -65,6 +65,7 @@ def expected_ws(n, T, Hk, Hv, S, C, kda=True):
             tot = al(tot + rows * nsl * 4)                  # dbeta per slab
         tot = al(tot + rows * S * 4)                        # the chain's column sums X'^T delta
         tot = al(tot + units * n_ck * S * 4)                # dg at each segment's first token
+        tot = al(tot + units * S * S * 4)                   # state / gradient between pieces
         return tot                                          # dq, dk summed in the column pass
     tot = al(tot + units * C * S * S * 4)
     tot = al(tot + units * C * S * 4)

@@ -371,3 +371,25 @@ def test_s128_bitwise_interval_reuse_and_strides(dev):
                 check({n: other[n]}, {n: a[n]}, tol=1e-5)
             else:
                 assert np.array_equal(a[n], other[n]), (what, n)
+
+
+def test_s128_pipelined_pieces(dev):
+    """S = 128 over 2200 tokens: gdn_fwd and gdn_bwd split the token axis into two pieces
+    (1152 tokens each, the second sequence ending inside the first), the chain's pieces on the
+    caller's stream and their column sums on a second one; two row slabs per unit.  Against the
+    oracle, and bitwise against the single-stream allocation-free backward (one piece)."""
+    from gated_delta_rule_bwd_amd import binding as B
+    w = I.Workload("s128_pieces", 2, 2200, 1, 2, 128, True, 64, -0.3, seq_lens=(2200, 1000),
+                   seed=511)
+    log(f"[parity] {w.name} lens={w.lens}")
+    arrays, _ = I.make_all(w)
+    dc, got = run_case(dev, w, arrays, reuse=True)
+    rep = check(got, oracle_results(w, arrays), REGIONS_FWD + REGIONS_BWD)
+    log(f"[parity] {w.name}: " + ", ".join(f"{k} {v:.1e}" for k, v in rep.items()))
+    assert B.workspace_size(dc.p) <= B.NOALLOC_SCRATCH_BYTES
+    dc.grad.fill_(float("nan"))
+    B.bwd_noalloc(dc.p, dc.q, dc.k, dc.v, dc.g, dc.beta, dc.state0, dc.gy, dc.dstate_out, dc.grad)
+    torch.cuda.synchronize()
+    one = {k: v.detach().cpu().numpy() for k, v in dc.grads().items()}
+    for n in REGIONS_BWD:
+        assert np.array_equal(one[n], got[n]), ("pieces vs one piece", n)
