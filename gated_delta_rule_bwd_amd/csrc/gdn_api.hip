@@ -14,6 +14,7 @@
 namespace {
 
 constexpr size_t kAlign = 256;
+constexpr int kRingSlots = 4;   // piece slots of the head-128 chain's results on long sequences
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -37,6 +38,10 @@ struct Plan {
            off_anc = 0, off_carry = 0;
     int nslab = 1;       // head size 128: row slabs per unit of the forward and the chain
     int piece = 1;       // head size 128: tokens per piece of the pipelined passes (a multiple of C)
+    int np = 1;          // pieces
+    int ring = 0;        // piece slots of the chain's results (0: one buffer for every token)
+    int pb_T = 0;        // tokens per sequence of such a buffer
+    size_t sz_g = 0, sz_dbp = 0, sz_p3 = 0;   // floats per slot
     // half-precision inputs: their fp32 copies, contiguous [n_seqs][T][heads][width] each
     size_t off_in = 0, in_q = 0, in_k = 0, in_v = 0, in_g = 0, in_b = 0, in_gy = 0;
     size_t total = 0;
@@ -106,22 +111,31 @@ Plan make_plan(const gdn_problem *p) {
         // too few units to fill the chip with one workgroup each: the forward and the chain split
         // every unit's rows into two slabs, whose sums over rows are kept apart
         pl.nslab = pl.units <= 128 ? 2 : 1;
-        pl.off_g1 = off;   // Grams G1 and G2 of the blocks, per slab
-        off = align_up(off + (size_t)p->n_seqs * nblk * p->H_v * pl.nslab * 256 * sizeof(float));
-        pl.off_g2 = off;
-        off = align_up(off + (size_t)p->n_seqs * nblk * p->H_v * pl.nslab * 256 * sizeof(float));
-        pl.off_dbp = off;  // dbeta per slab
-        if (pl.nslab > 1) off = align_up(off + tok_rows * pl.nslab * sizeof(float));
-        pl.off_p3 = off;   // the chain's column sums X'^T delta per token
-        off = align_up(off + tok_rows * S * sizeof(float));
-        pl.off_anc = off;  // dg at the first token of every checkpoint segment
-        off = align_up(off + (size_t)pl.units * pl.n_ck_max * S * sizeof(float));
-        pl.off_carry = off;   // the state or gradient between the pieces of a pipelined pass
-        off = align_up(off + (size_t)pl.units * S * S * sizeof(float));
         // pieces of about 1024 tokens, at most 16, each a whole number of checkpoint segments
         const int64_t np = std::min<int64_t>(16, std::max<int64_t>(1, p->T / 1024));
         const int64_t per = (p->T + np - 1) / np;
         pl.piece = (int)std::max<int64_t>(pl.C, (per + pl.C - 1) / pl.C * pl.C);
+        pl.np = (p->T + pl.piece - 1) / pl.piece;
+        // the chain's results for the column pass (G1, G2, dbeta per slab, P3): for the whole
+        // sequence, or, beyond kRingSlots pieces, in a ring of that many piece slots
+        pl.ring = pl.np > kRingSlots ? kRingSlots : 0;
+        pl.pb_T = pl.ring ? pl.piece : (int)nblk * 16;
+        const size_t pb_rows = (size_t)p->n_seqs * pl.pb_T * p->H_v, slots = pl.ring ? pl.ring : 1;
+        pl.sz_g = pb_rows / 16 * pl.nslab * 256;
+        pl.sz_dbp = pl.nslab > 1 ? pb_rows * pl.nslab : 0;
+        pl.sz_p3 = pb_rows * S;
+        pl.off_g1 = off;   // Grams G1 and G2 of the blocks, per slab
+        off = align_up(off + slots * pl.sz_g * sizeof(float));
+        pl.off_g2 = off;
+        off = align_up(off + slots * pl.sz_g * sizeof(float));
+        pl.off_dbp = off;  // dbeta per slab
+        off = align_up(off + slots * pl.sz_dbp * sizeof(float));
+        pl.off_p3 = off;   // the chain's column sums X'^T delta per token
+        off = align_up(off + slots * pl.sz_p3 * sizeof(float));
+        pl.off_anc = off;  // dg at the first token of every checkpoint segment
+        off = align_up(off + (size_t)pl.units * pl.n_ck_max * S * sizeof(float));
+        pl.off_carry = off;   // the state or gradient between the pieces of a pipelined pass
+        off = align_up(off + (size_t)pl.units * S * S * sizeof(float));
         // dq and dk go straight to the outputs: the column pass sums the value heads of a key
         // head in one workgroup
         pl.parts = false;
@@ -225,6 +239,8 @@ gdn::Mf128Args mf_args(const gdn_problem *p, const Plan &pl, void *ws, int s0, i
     a.dbp = (float *)(w + pl.off_dbp);
     a.nslab = pl.nslab;
     a.p3buf = (float *)(w + pl.off_p3);
+    a.pb_T = pl.pb_T;
+    a.pb_t0 = 0;
     a.anc = (float *)(w + pl.off_anc);
     a.carry = (float *)(w + pl.off_carry);
     a.t_lo = 0;
@@ -321,19 +337,26 @@ int mf_forward(const gdn_problem *p, const Plan &pl, void *ws, const void *q, co
 
 // The chain and the column sums of the head-128 backward.  Pipelined: the chain walks the pieces
 // from the last on st, and the column sums of each piece run on the second stream as soon as the
-// chain has passed it.
+// chain has passed it.  With a ring of piece slots the chain's results for piece i (counted in
+// processing order) go to slot i % ring, and the chain of piece i waits for the column sums of
+// piece i - ring, which read that slot.
 int mf_backward(const gdn_problem *p, const Plan &pl, void *ws, gdn::Mf128Args a, hipStream_t st,
                 bool pipelined) {
-    const int T = p->T, PT = pl.piece, np = (T + PT - 1) / PT;
+    const int T = p->T, PT = pl.piece, np = pl.np;
     for (int s0 = 0; s0 < p->n_seqs; s0 += gdn::kMaxSeqsPerLaunch) {
         const int cnt = std::min(gdn::kMaxSeqsPerLaunch, p->n_seqs - s0);
         gdn::Mf128Args b = mf_args(p, pl, ws, s0, cnt);
         b.q = a.q; b.k = a.k; b.v = a.v; b.g = a.g; b.beta = a.beta; b.gy = a.gy;
         b.state0 = a.state0; b.dstate_out = a.dstate_out;
         b.dq = a.dq; b.dk = a.dk; b.dv = a.dv; b.dg = a.dg; b.dbeta = a.dbeta; b.dstate = a.dstate;
-        int rc = device_status(gdn::launch_zero_bwd(b, st));
+        int rc = device_status(gdn::launch_zero_anc(b, st));
+        for (int k = 0; rc == GDN_OK && k < (pl.ring ? pl.ring : 1); ++k) {   // P3 of every slot
+            gdn::Mf128Args bk = b;
+            bk.p3buf += k * pl.sz_p3;
+            rc = device_status(gdn::launch_zero_p3(bk, st));
+        }
         if (rc != GDN_OK) return rc;
-        if (!pipelined || np <= 1) {
+        if (np <= 1 || (!pipelined && !pl.ring)) {   // one launch of each over every token
             rc = device_status(gdn::launch_chain(b, st));
             if (rc == GDN_OK) rc = device_status(gdn::launch_colsum(b, st));
             if (rc != GDN_OK) return rc;
@@ -341,14 +364,44 @@ int mf_backward(const gdn_problem *p, const Plan &pl, void *ws, gdn::Mf128Args a
         }
         std::unique_lock<std::mutex> lk;
         Side *sd = nullptr;
-        rc = side_for(st, lk, &sd);
-        for (int j = np - 1; rc == GDN_OK && j >= 0; --j) {
-            const gdn::Mf128Args bj = piece_of(b, j * PT, std::min(T, (j + 1) * PT));
-            rc = device_status(gdn::launch_chain(bj, st));
+        if (pipelined) rc = side_for(st, lk, &sd);
+        hipEvent_t done[gdn::kMaxPieces] = {};   // column sums of piece i finished (ring reuse)
+        for (int i = 0; rc == GDN_OK && i < np; ++i) {
+            const int j = np - 1 - i;
+            gdn::Mf128Args bj = piece_of(b, j * PT, std::min(T, (j + 1) * PT));
+            if (pl.ring) {
+                const int slot = i % pl.ring;
+                bj.g1buf += slot * pl.sz_g;
+                bj.g2buf += slot * pl.sz_g;
+                bj.dbp += slot * pl.sz_dbp;
+                bj.p3buf += slot * pl.sz_p3;
+                bj.pb_t0 = j * PT;
+                if (pipelined && i >= pl.ring && hipStreamWaitEvent(st, done[i - pl.ring], 0) != hipSuccess)
+                    rc = GDN_ERR_DEVICE;
+            }
+            if (rc == GDN_OK) rc = device_status(gdn::launch_chain(bj, st));
+            if (!pipelined) {
+                if (rc == GDN_OK) rc = device_status(gdn::launch_colsum(bj, st));
+                // the slot's P3 back to zeros for the piece that reuses it (two slabs add into it)
+                if (rc == GDN_OK && pl.ring && i + pl.ring < np) rc = device_status(gdn::launch_zero_p3(bj, st));
+                continue;
+            }
             if (rc == GDN_OK) rc = order_after(*sd, st, sd->s);
+            // The slot of the previous piece, whose column sums have ended, back to zeros for the
+            // piece that reuses it (two slabs add their P3 into it).  Enqueued between the wait
+            // for this chain and the column sums (also where no piece reuses the slot), it lets
+            // the next chain launch (queued right behind this one on st) take the CUs this chain
+            // frees before the column sums do.
+            if (rc == GDN_OK && pl.ring && i >= 1) {
+                gdn::Mf128Args prev = bj;
+                prev.p3buf = b.p3buf + ((i - 1) % pl.ring) * pl.sz_p3;
+                rc = device_status(gdn::launch_zero_p3_all(prev, sd->s));
+                done[i - 1] = sd->take();
+                if (rc == GDN_OK && hipEventRecord(done[i - 1], sd->s) != hipSuccess) rc = GDN_ERR_DEVICE;
+            }
             if (rc == GDN_OK) rc = device_status(gdn::launch_colsum(bj, sd->s));
         }
-        if (rc == GDN_OK) rc = order_after(*sd, sd->s, st);   // st waits for the last column sums
+        if (rc == GDN_OK && pipelined) rc = order_after(*sd, sd->s, st);   // st waits for the last column sums
         if (rc != GDN_OK) return rc;
     }
     return GDN_OK;

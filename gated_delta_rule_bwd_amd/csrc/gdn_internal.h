@@ -10,6 +10,8 @@ namespace gdn {
 
 // Sequences handled by one launch; their lengths travel in the kernel argument block.
 constexpr int kMaxSeqsPerLaunch = 256;
+// Pieces of the token axis in the pipelined head-128 passes.
+constexpr int kMaxPieces = 16;
 
 // Arguments of the forward scan (also used, with y == nullptr, as the checkpoint pass
 // of the backward).
@@ -113,11 +115,14 @@ struct Mf128Args {
     float *cbuf;            // [n_seqs][T][H_v][G] running gate product c within the token's
                             // block (the gates a themselves in a token-by-token block)
     float *ebuf;            // [n_seqs][T][H_v][S] prediction errors e = v - u
-    float *g1buf;           // [n_seqs][nblk][H_v][nslab][16][16] Grams G1 = delta^T (scale gy),
+    // The chain's per-token results for the column pass, for tokens pb_t0 .. pb_t0 + pb_T - 1
+    // of every sequence (the whole sequence, or one piece of a pipelined pass):
+    float *g1buf;           // [n_seqs][pb_T/16][H_v][nslab][16][16] Grams G1 = delta^T (scale gy),
     float *g2buf;           // s <= t, and G2 = delta^T du, s < t, over each slab's rows of a block
-    float *dbp;             // [n_seqs][T][H_v][nslab] dbeta per slab (nslab > 1)
-    float *p3buf;           // [n_seqs][T][H_v][S] P3 = X'^T delta per token (the chain's column
+    float *dbp;             // [n_seqs][pb_T][H_v][nslab] dbeta per slab (nslab > 1)
+    float *p3buf;           // [n_seqs][pb_T][H_v][S] P3 = X'^T delta per token (the chain's column
                             // sums of the state gradient against the token's delta)
+    int32_t pb_T, pb_t0;
     float *anc;             // [unit][n_ck_max][S] dg at each checkpoint segment's first token
     float *dq, *dk, *dv, *dg, *dbeta, *dstate;   // dq, dk per key head, summed over its value heads
     gdn_strides sq, sk, sv, sg, sb, sgy, sy;
@@ -131,7 +136,9 @@ struct Mf128Args {
 };
 hipError_t launch_prep128(const Mf128Args &a, hipStream_t st);
 hipError_t launch_fwd_mf(const Mf128Args &a, hipStream_t st);
-hipError_t launch_zero_bwd(const Mf128Args &a, hipStream_t st);  // before the first chain launch
+hipError_t launch_zero_anc(const Mf128Args &a, hipStream_t st);  // before the first chain launch
+hipError_t launch_zero_p3(const Mf128Args &a, hipStream_t st);   // before a chain launch fills P3
+hipError_t launch_zero_p3_all(const Mf128Args &a, hipStream_t st);   // also with one slab
 hipError_t launch_chain(const Mf128Args &a, hipStream_t st);     // the chain over [t_lo, t_hi)
 hipError_t launch_colsum(const Mf128Args &a, hipStream_t st);    // the column sums of its segments
 

@@ -701,12 +701,14 @@ __global__ void __launch_bounds__(64 * NWC) chain_kernel(const Mf128Args a) {
     const float *ein = a.ebuf + row0 * S + r0;
     float *dvout = a.dv + row0 * S;
     const bool vec_dv = ((uintptr_t)a.dv & 15) == 0;
-    float *dbout = NSL > 1 ? a.dbp + row0 * nsl + slab : a.dbeta + row0;   // stride H_v nsl per token
+    const int64_t prow0 = (s * a.pb_T - a.pb_t0) * a.H_v + h;   // piece-buffer row of token 0; stride H_v
+    float *dbout = NSL > 1 ? a.dbp + prow0 * nsl + slab : a.dbeta + row0;   // stride H_v nsl per token
     const int64_t dbt = NSL > 1 ? (int64_t)a.H_v * nsl : a.H_v;
-    float *p3out = a.p3buf + row0 * S;                               // token stride H_v S
+    float *p3out = a.p3buf + prow0 * S;                              // token stride H_v S
     float *ancu = a.anc + unit * (int64_t)a.n_ck_max * S;
-    float *g1u = a.g1buf + ((s * nblk * a.H_v + h) * nsl + slab) * (int64_t)(W * W);   // block b at b H_v nsl W^2
-    float *g2u = a.g2buf + ((s * nblk * a.H_v + h) * nsl + slab) * (int64_t)(W * W);
+    const int64_t gbase = ((s * (a.pb_T / W) - a.pb_t0 / W) * a.H_v + h) * nsl + slab;   // block b at b H_v nsl W^2
+    float *g1u = a.g1buf + gbase * (W * W);
+    float *g2u = a.g2buf + gbase * (W * W);
     const uint32_t ct = (uint32_t)(a.H_v * G) * 4, kt = (uint32_t)a.sk.tok * ES, qt = (uint32_t)a.sq.tok * ES,
                    gyt = (uint32_t)a.sgy.tok * ES, bt = (uint32_t)a.sb.tok * ES, et = (uint32_t)a.H_v * S * 4;
 
@@ -1228,7 +1230,7 @@ __global__ void __launch_bounds__(NT) colsum_kernel(const Mf128Args a) {
         P.e = ld4v<GDN_DTYPE_F32>(re, tt * et + 16 * cg, true);
         P.dv = ld4v<GDN_DTYPE_F32>(rdv, tt * et + 16 * cg, vec_dv);
         P.b = bld<DT>(rb, tt * bt, 0);
-        const int64_t gb = bi * nsl * (W * W) + (tid & 255);
+        const int64_t gb = ((s * (a.pb_T / W) + (t0 - a.pb_t0) / W) * a.H_v + h) * nsl * (W * W) + (tid & 255);
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
             const int64_t o = gb + min(k, nsl - 1) * (W * W);
@@ -1287,7 +1289,8 @@ __global__ void __launch_bounds__(NT) colsum_kernel(const Mf128Args a) {
             const int sr = tid >> 4, t2 = tid & 15;
             float g = 0.f;
             if (sr == 0 && t2 == 0)
-                for (int k = 0; k < nsl; ++k) g += a.g1buf[(bi * nsl + k) * (W * W) + tau * (W + 1)];
+                for (int k = 0; k < nsl; ++k)
+                    g += a.g1buf[(((s * (a.pb_T / W) + (t0 - a.pb_t0) / W) * a.H_v + h) * nsl + k) * (W * W) + tau * (W + 1)];
             sm.g1[sr][t2] = g;
             sm.g2[sr][t2] = 0.f;
             sm.g2t[sr][t2] = 0.f;
@@ -1443,15 +1446,15 @@ __global__ void __launch_bounds__(NT) colsum_kernel(const Mf128Args a) {
         set_head(r);
         if (nsl > 1) {   // dbeta of the segment's tokens: the chain's slabs in order
             for (int t = ts + tid; t < min(ts + C, L); t += NT) {
-                const int64_t rw = row0 + (int64_t)t * a.H_v;
+                const int64_t rw = row0 + (int64_t)t * a.H_v, pr = (s * a.pb_T + t - a.pb_t0) * a.H_v + h;
                 float b = 0.f;
-                for (int k = 0; k < nsl; ++k) b += a.dbp[rw * nsl + k];
+                for (int k = 0; k < nsl; ++k) b += a.dbp[pr * nsl + k];
                 a.dbeta[rw] = b;
             }
         }
         load_cols(a.snap + (unit * a.n_ck_max + sg) * (int64_t)(S * S), M);
         dgrun = ld4(a.anc + (unit * a.n_ck_max + sg) * (int64_t)S + i0 + 4 * g4);
-        p3in = a.p3buf + row0 * S;
+        p3in = a.p3buf + ((s * a.pb_T - a.pb_t0) * a.H_v + h) * S;
         Pre P;
         prefetch(P, ts);
         pend_n = 0;
@@ -1549,13 +1552,22 @@ hipError_t launch_fwd_mf(const Mf128Args &a, hipStream_t st) {
     return launch(pick<FwdK>(a.dtype), a, units, NT, st);
 }
 
-hipError_t launch_zero_bwd(const Mf128Args &a, hipStream_t st) {
-    // the two slabs of a unit add their P3 and segment dg into zeros
+hipError_t launch_zero_anc(const Mf128Args &a, hipStream_t st) {
+    // the two slabs of a unit add their segment dg into zeros
     if (a.nslab != 2) return hipSuccess;
     const int64_t units = (int64_t)a.n_seqs_launch * a.H_v;
-    hipError_t e = launch_zero(a.p3buf + (int64_t)a.s_base * a.T * a.H_v * S, units * a.T * S, st);
-    if (e == hipSuccess) e = launch_zero(a.anc + (int64_t)a.s_base * a.H_v * a.n_ck_max * S, units * a.n_ck_max * S, st);
-    return e;
+    return launch_zero(a.anc + (int64_t)a.s_base * a.H_v * a.n_ck_max * S, units * a.n_ck_max * S, st);
+}
+
+hipError_t launch_zero_p3_all(const Mf128Args &a, hipStream_t st) {
+    // the launch's sequences of the piece buffer's P3
+    const int64_t units = (int64_t)a.n_seqs_launch * a.H_v;
+    return launch_zero(a.p3buf + (int64_t)a.s_base * a.pb_T * a.H_v * S, units * a.pb_T * S, st);
+}
+
+hipError_t launch_zero_p3(const Mf128Args &a, hipStream_t st) {
+    // the two slabs of a unit add their P3 into zeros
+    return a.nslab == 2 ? launch_zero_p3_all(a, st) : hipSuccess;
 }
 
 hipError_t launch_chain(const Mf128Args &a, hipStream_t st) {

@@ -59,11 +59,17 @@ def expected_ws(n, T, Hk, Hv, S, C, kda=True):
         tot = al(tot + rows * (S if kda else 1) * 4)        # running gate products
         tot = al(tot + rows * S * 4)                        # prediction errors
         nsl = 2 if units <= 128 else 1                      # row slabs of small launches
-        tot = al(tot + n * nblk * Hv * nsl * 256 * 4)       # Grams G1
-        tot = al(tot + n * nblk * Hv * nsl * 256 * 4)       # Grams G2
-        if nsl > 1:
-            tot = al(tot + rows * nsl * 4)                  # dbeta per slab
-        tot = al(tot + rows * S * 4)                        # the chain's column sums X'^T delta
+        # pieces of about 1024 tokens (at most 16, whole segments); beyond 4 pieces the chain's
+        # results for the column pass live in a ring of 4 piece slots
+        npt = min(16, max(1, T // 1024))
+        piece = max(C, -(-(-(-T // npt)) // C) * C)
+        npieces = -(-T // piece)
+        slots, pbT = (4, piece) if npieces > 4 else (1, nblk * 16)
+        pb_rows = n * pbT * Hv
+        tot = al(tot + slots * pb_rows // 16 * nsl * 256 * 4)   # Grams G1
+        tot = al(tot + slots * pb_rows // 16 * nsl * 256 * 4)   # Grams G2
+        tot = al(tot + slots * (pb_rows * nsl if nsl > 1 else 0) * 4)   # dbeta per slab
+        tot = al(tot + slots * pb_rows * S * 4)             # the chain's column sums X'^T delta
         tot = al(tot + units * n_ck * S * 4)                # dg at each segment's first token
         tot = al(tot + units * S * S * 4)                   # state / gradient between pieces
         return tot                                          # dq, dk summed in the column pass
@@ -86,6 +92,10 @@ def test_workspace_size(B):
     # layer shape, 4 x 4096 tokens, 48 value heads, S = 128, C = 64
     big = problem(B, n_seqs=4, T=4096, H_k=16, H_v=48, S=128, C=64, seq_lens=None)
     assert B.workspace_size(big) == expected_ws(4, 4096, 16, 48, 128, 64)
+    # 65536 tokens, 48 value heads, scalar gate, C = 256: 16 pieces, the ring of 4 slots
+    long = problem(B, n_seqs=1, T=65536, H_k=16, H_v=48, S=128, C=256, kda=False, seq_lens=None)
+    assert B.workspace_size(long) == expected_ws(1, 65536, 16, 48, 128, 256, kda=False)
+    assert B.workspace_size(long) < 4.0e9
     long = problem(B, n_seqs=1, T=65536, H_k=16, H_v=48, S=128, C=256, kda=False,
                    seq_lens=None)
     assert B.workspace_size(long) == expected_ws(1, 65536, 16, 48, 128, 256, kda=False)

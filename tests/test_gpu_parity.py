@@ -373,14 +373,25 @@ def test_s128_bitwise_interval_reuse_and_strides(dev):
                 assert np.array_equal(a[n], other[n]), (what, n)
 
 
-def test_s128_pipelined_pieces(dev):
-    """S = 128 over 2200 tokens: gdn_fwd and gdn_bwd split the token axis into two pieces
-    (1152 tokens each, the second sequence ending inside the first), the chain's pieces on the
-    caller's stream and their column sums on a second one; two row slabs per unit.  Against the
-    oracle, and bitwise against the single-stream allocation-free backward (one piece)."""
+PIECE_CASES = {
+    # two pieces of 1152 tokens, the second sequence ending inside the first
+    "two_pieces": I.Workload("s128_pieces", 2, 2200, 1, 2, 128, True, 64, -0.3,
+                             seq_lens=(2200, 1000), seed=511),
+    # five pieces of 1088 tokens: the chain's results go through the ring of four piece slots
+    "ring": I.Workload("s128_ring", 2, 5200, 1, 2, 128, False, 64, -0.2,
+                       seq_lens=(5200, 3000), seed=512),
+}
+
+
+@pytest.mark.parametrize("name", list(PIECE_CASES))
+def test_s128_pipelined_pieces(dev, name):
+    """S = 128 over several pieces of the token axis: gdn_fwd and gdn_bwd pipeline the pieces,
+    the chain's on the caller's stream and their column sums on a second one; two row slabs
+    per unit.  Against the oracle, and bitwise against the single-stream allocation-free
+    backward (one piece when the chain's results fit a buffer for every token, else the same
+    pieces in turn on one stream)."""
     from gated_delta_rule_bwd_amd import binding as B
-    w = I.Workload("s128_pieces", 2, 2200, 1, 2, 128, True, 64, -0.3, seq_lens=(2200, 1000),
-                   seed=511)
+    w = PIECE_CASES[name]
     log(f"[parity] {w.name} lens={w.lens}")
     arrays, _ = I.make_all(w)
     dc, got = run_case(dev, w, arrays, reuse=True)
