@@ -130,21 +130,28 @@ def pmc_summary(d, op, workload):
     n_copy = sum(ncf[k] for k in copy)
     fetch_scale = n_copy * cal["copy_calibration_bytes"] / (1024 * sum(cf[(k, "FETCH_SIZE")] for k in copy))
     write_scale = n_copy * cal["copy_calibration_bytes"] / (1024 * sum(cw[(k, "WRITE_SIZE")] for k in copy))
+    # the counter runs time PMC_CALLS calls of the op (one warm-up step, one timed step); a call
+    # may launch a kernel several times (the pieces of a pipelined pass)
     kernels = {}
     for k in nfe:
         if k not in nwr:
             continue
         kernels[k] = {"fetch_bytes": fe[(k, "FETCH_SIZE")] * 1024 * fetch_scale / nfe[k],
-                      "write_bytes": wr[(k, "WRITE_SIZE")] * 1024 * write_scale / nwr[k]}
+                      "write_bytes": wr[(k, "WRITE_SIZE")] * 1024 * write_scale / nwr[k],
+                      "dispatches_per_call": nfe[k] / PMC_CALLS}
     spec = TRAFFIC[(op, workload)]
     return {"op": op, "workload": workload, "source_sha256": sources_hash(spec["sources"]),
             "counter_scale": {"fetch": fetch_scale, "write": write_scale},
             "kernels": kernels}
 
 
+PMC_CALLS = 2   # calls of the op in a counter run (--steps 1 --warmup 1)
+
+
 def traffic_bytes(op, workload):
-    """HBM bytes of one timed call (the roofline kernels) from the committed counter summary,
-    or None when there is none or the kernels changed since it was taken."""
+    """HBM bytes of one timed call (every launch of the roofline kernels in it) from the
+    committed counter summary, or None when there is none or the kernels changed since it was
+    taken."""
     spec = TRAFFIC.get((op, workload))
     if spec is None:
         return None
@@ -158,7 +165,8 @@ def traffic_bytes(op, workload):
     ks = t["kernels"]
     if not all(k in ks for k in spec["kernels"]):
         return None
-    return sum(ks[k]["fetch_bytes"] + ks[k]["write_bytes"] for k in spec["kernels"])
+    return sum((ks[k]["fetch_bytes"] + ks[k]["write_bytes"]) * ks[k].get("dispatches_per_call", 1)
+               for k in spec["kernels"])
 
 
 def copy_calibration(mib):
