@@ -1264,7 +1264,6 @@ __global__ void __launch_bounds__(NT) colsum_kernel(const Mf128Args a) {
     };
     // token t0 + tau of a token-by-token block as a one-token block with c = 1 (loaded directly)
     auto stage_token = [&](ColLds &sm, int t0, int tau) {
-        const int64_t bi = (s * nblk + t0 / W) * a.H_v + h;
         const int64_t t = t0 + tau;
         const float av = cin[t * (a.H_v * G) + (kda ? ci : 0)];
         const float kx = (float)kin[t * a.sk.tok + ci];
