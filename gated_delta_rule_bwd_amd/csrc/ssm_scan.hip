@@ -103,8 +103,10 @@ __device__ __forceinline__ float step_of(float z, int softplus) {
 // The 16 rows of a workgroup share one (sequence, group), so a window's B and C rows are
 // common to all of them; x, the step (and gy) are per row.  Each window is staged in LDS once
 // and the next one is loaded into registers while the current one is computed.
+// (sized for NC = N states: the LDS a workgroup takes bounds how many fit on a CU)
+template <int NC>
 struct Stage {
-    float B[WIN][128], C[WIN][128];
+    float B[WIN][NC], C[WIN][NC];
     float x[WIN][ROWS], d[WIN][ROWS], gy[WIN][ROWS];
 };
 
@@ -143,7 +145,7 @@ struct Loader {
             if (tid < 128) s1v = a.gy[((seq * T + t) * H + lh) * P + li];
         }
     }
-    __device__ void put(const SsmArgs &a, Stage &st) const {
+    __device__ void put(const SsmArgs &a, Stage<16 * NPL> &st) const {
 #pragma unroll
         for (int m = 0; m < NQ; ++m) {
             const int qq = tid + 256 * m;
@@ -199,7 +201,7 @@ __device__ __forceinline__ void st_cols(float *row, int sub, const float (&v)[NP
 // ---- forward -------------------------------------------------------------------------------
 template <int NPL, bool APS>
 __global__ void __launch_bounds__(256) ssm_fwd_kernel(const SsmArgs a) {
-    __shared__ Stage stg[2];
+    __shared__ Stage<16 * NPL> stg[2];
     __shared__ float ys[2][WIN][ROWS];
     const int tid = threadIdx.x, sub = tid & 15, rho = tid >> 4;
     const int64_t r0 = (int64_t)blockIdx.x * ROWS;
@@ -231,7 +233,7 @@ __global__ void __launch_bounds__(256) ssm_fwd_kernel(const SsmArgs a) {
         const int t0 = win * WIN, cnt = wcnt(win);
         if (win + PD - 1 < nwin) ld[(U + PD - 1) % PD].load(a, (win + PD - 1) * WIN, wcnt(win + PD - 1));
         st_cols<NPL>(a.ck + (w.r * nwin + win) * N, sub, st);     // state before the window
-        const Stage &sg = stg[cur];
+        const Stage<16 * NPL> &sg = stg[cur];
 #pragma unroll
         for (int k = 0; k < WIN; ++k) {
             if (k < cnt) {                                           // uniform
@@ -268,8 +270,8 @@ __global__ void __launch_bounds__(256) ssm_fwd_kernel(const SsmArgs a) {
 // ---- backward ------------------------------------------------------------------------------
 template <int NPL, bool APS>
 __global__ void __launch_bounds__(256) ssm_bwd_kernel(const SsmArgs a) {
-    __shared__ Stage stg[2];
-    __shared__ float red[WIN][4][2][128];          // [token][wave][dC | dB][column]
+    __shared__ Stage<16 * NPL> stg[2];
+    __shared__ float red[WIN][4][2][16 * NPL];     // [token][wave][dC | dB][column]
     __shared__ float os[2][WIN][ROWS];             // dx, ddt term per (token, row)
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int sub = tid & 15, rho = tid >> 4, rg = lane >> 4;
@@ -301,7 +303,7 @@ __global__ void __launch_bounds__(256) ssm_bwd_kernel(const SsmArgs a) {
         const int win = nwin - 1 - it, cur = it & 1;
         const int t0 = win * WIN, cnt = min(WIN, a.T - t0);
         if (win > 0) ld.load(a, t0 - WIN, WIN);
-        const Stage &sg = stg[cur];
+        const Stage<16 * NPL> &sg = stg[cur];
         float sp[NPL], S[WIN][NPL];
         ld_cols<NPL>(a.ck + (w.r * nwin + win) * N, sub, sp);
         // replay the window: S[k] is the state after token t0 + k
