@@ -29,8 +29,14 @@
  * gdn_problem.dtype selects a half type.  Index arithmetic is 64-bit.
  *
  * Ownership and concurrency
- *   - The caller owns every buffer.  The library allocates nothing and keeps no state
- *     between calls.
+ *   - The caller owns every buffer.  The library allocates no device memory (apart from the
+ *     static array of gdn_bwd_noalloc) and keeps no data between calls.
+ *   - For head size 128, gdn_fwd and gdn_bwd split the token axis into pieces and enqueue part
+ *     of the work (the preparation of later pieces, the column sums of finished pieces) on a
+ *     second stream that the library creates for the device on first use, at the default
+ *     priority, with a pool of events; before returning, a call makes the caller's stream wait
+ *     for that work, so the caller sees stream order as if everything ran on its stream.
+ *     Calls from several host threads on one device take turns while enqueueing.
  *   - Calls are asynchronous on the given HIP stream (NULL = the legacy default stream);
  *     results are valid once the stream has passed the call.  Faults surface at the
  *     caller's synchronisation.
@@ -129,10 +135,13 @@ typedef struct gdn_problem {
 /* Bytes of device workspace that gdn_fwd and gdn_bwd need for this problem (0 on an
  * invalid problem).  The same workspace serves both calls.  It holds what the scratch of the
  * approval review's sizing note on "metal: GATED_DELTA_NET_BACK" holds -- the state snapshots
- * every C tokens and the state recomputed inside a segment -- plus per-token arrays of the
- * head-128 kernels: the running gate products, the prediction errors, the block matrices and
- * Grams, the block starts of one segment and, when H_v > H_k, dq and dk per value head.  The
- * caller allocates it once; nothing else is allocated. */
+ * every C tokens -- plus, for head size 128, per-token arrays of the matrix-core kernels (the
+ * running gate products, the prediction errors, the block matrices, and the chain's results
+ * for the column sums: its Grams, dbeta per row slab and P3, for every token or, on long
+ * sequences, for a ring of four pieces), dg at the first token of every segment and the state
+ * carried between pieces; for the other head sizes the states recomputed inside one segment
+ * and, when H_v > H_k, dq and dk per value head.  The caller allocates it once; nothing else
+ * is allocated. */
 size_t gdn_workspace_size(const gdn_problem *p);
 
 /* Layout of the packed gradient buffer (PR description of "metal: GATED_DELTA_NET_BACK":
