@@ -1313,7 +1313,8 @@ __global__ void __launch_bounds__(NT) colsum_kernel(const Mf128Args a) {
     f4 M[8];
     f4 dgrun;                     // dg at the next token, per column (i0 + 4(l/16) + r)
     const float *p3in = nullptr;   // the chain's P3 of the value head
-    auto block = [&](ColLds &sm, int tw, int n, bool dir) {
+    // (replay: the state after this (sub)block is needed; not after the segment's last token)
+    auto block = [&](ColLds &sm, int tw, int n, bool dir, bool replay) {
         // the earlier value heads' dq and dk of the block's tokens (zero for the first head) and
         // the chain's P3 = X'^T delta, loaded first so that the products below cover their latency
         f4 pq = zero4(), pk = zero4(), p3 = zero4();
@@ -1378,11 +1379,13 @@ __global__ void __launch_bounds__(NT) colsum_kernel(const Mf128Args a) {
             }
         }
         // the replay: M += delta kr^T, then the block product
-        rank_update(sm, M);
-        if (!dir) {
-            const float p = sm.pv[i0 + lm];
+        if (replay) {
+            rank_update(sm, M);
+            if (!dir) {
+                const float p = sm.pv[i0 + lm];
 #pragma unroll
-            for (int jb = 0; jb < 8; ++jb) M[jb] *= p;
+                for (int jb = 0; jb < 8; ++jb) M[jb] *= p;
+            }
         }
         // dq = c P1, dk = P3 / c + c P2, dg increments q.*dq - k.*(P3 / c) + k.*(c P2)
         f4 dq4, dk4, inc;
@@ -1474,7 +1477,7 @@ __global__ void __launch_bounds__(NT) colsum_kernel(const Mf128Args a) {
 #pragma unroll
                     for (int jb = 0; jb < 8; ++jb) M[jb] *= p;
                 }
-                block(sm, dir ? t0 + tau : t0, dir ? 1 : cnt, dir);
+                block(sm, dir ? t0 + tau : t0, dir ? 1 : cnt, dir, bb + 1 < nb || (dir && tau + 1 < nsub));
                 pend_tw = dir ? t0 + tau : t0;
                 pend_n = dir ? 1 : cnt;
                 cur ^= 1;
