@@ -16,8 +16,8 @@
 // triangular system (inverse Tb), and the column sums dq, dk are dense products against the
 // block's start state (M) and end gradient (X) plus rank-16 corrections from the block's
 // Gram matrices of the rows.  The per-channel gate gradient dg follows from the column sums
-// by an exact telescoping identity, with its value at each block's first token taken
-// directly as a column sum of the gradient times the start state.
+// by an exact telescoping identity, from its value at each checkpoint segment's first token,
+// taken directly as a column sum of the gradient times the segment's snapshot.
 //
 // A block whose running products leave [2^-60, 2^60] in some column is processed token by
 // token instead: each token is a one-token block whose state is first scaled by the token's
@@ -29,7 +29,10 @@
 // update of dM) does the same; the backward's column sums (dq, dk, dg) take the columns of the
 // state and of the transposed gradient instead, 16 per wave, so they are complete inside the
 // workgroup.  dq and dk of a key head shared by several value heads are summed by the column
-// pass itself: one workgroup takes the value heads of the key head in increasing order.
+// pass itself: one workgroup takes the value heads of the key head in increasing order.  The
+// host runs both directions over pieces of the token axis (the state or gradient carried
+// between launches), the column sums of a piece beside the chain of the next on a second
+// stream.
 //
 // MFMA lane layout (16x16x4 f32): lane l supplies A[l%16][kappa] and B[kappa][l%16], and
 // holds D[4(l/16) + r][l%16] in accumulator register r.  Every product below uses the
@@ -627,30 +630,30 @@ __global__ void __launch_bounds__(64 * NWC) fwd_mf_kernel(const Mf128Args a) {
 
 // The backward runs as two passes over the blocks.
 //
-// Pass 1, the chain (one workgroup per unit).  The rows of the state gradient evolve
-// independently, and its recurrence (dd = dM k, then the update of dM) reads no state, so this
-// pass walks the blocks of a sequence from the last in the row layout and never replays the
+// Pass 1, the chain (one workgroup per unit, or per row slab).  The rows of the state gradient
+// evolve independently, and its recurrence (dd = dM k, then the update of dM) reads no state, so
+// this pass walks the blocks of a sequence from the last in the row layout and never replays the
 // state.  Wave w holds rows 16 w .. 16 w + 15 of the gradient X = dM diag(c) transposed as eight
 // tiles (tile ib, lane l, register r: X[16 w + l%16][16 ib + 4(l/16) + r]).  Per block: the fold
-// X' = X diag(P) (P the block's gate product), saved for pass 2; dd^T = Tb (KR X'^T + Bm sgy^T);
-// dv = beta dd (which also hands du = -dv to pass 2); dbeta = dd . e; the block's Grams over the
-// rows G1 = delta^T sgy and G2 = delta^T du for pass 2; X = X' + sgy qc^T + du kc^T.
+// X' = X diag(P) (P the block's gate product); dd^T = Tb (KR X'^T + Bm sgy^T); dv = beta dd
+// (which also hands du = -dv to pass 2); dbeta = dd . e; the block's Grams over the rows
+// G1 = delta^T sgy and G2 = delta^T du for pass 2; X = X' + sgy qc^T + du kc^T; and
+// P3 = X'^T delta, the column sums of the gradient against the block's deltas, from the gradient
+// entering the block transposed through LDS.  At a checkpoint segment's first token: dg there.
 //
 // Pass 2, the column sums (one workgroup per checkpoint segment of a (sequence, key head), all in
 // parallel; inside it the value heads of the key head one after the other, adding dq and dk).
 // Wave w holds columns 16 w .. 16 w + 15 of the state M as eight tiles (tile jb, lane l,
-// register r: M[16 jb + 4(l/16) + r][16 w + l%16]) and of the saved X' alike.  Starting from the
-// segment's snapshot, per block: the column sums against the block's start state and X' (dq, dk
-// and the increments of dg), then the replay to the next block's start.  Column results are
-// tiles P[i][t] (lane l, register r: column 16 w + 4(l/16) + r, token l%16).
+// register r: M[16 jb + 4(l/16) + r][16 w + l%16]).  Starting from the segment's snapshot, per
+// block: the column sums against the block's start state (dq, the dense part of dk besides P3,
+// the increments of dg), then the replay to the next block's start.  Column results are tiles
+// P[i][t] (lane l, register r: column 16 w + 4(l/16) + r, token l%16).
 //
-// A saved gradient is tile-major: tile (R, Cb) of rows 16 R .., columns 16 Cb .. at float offset
-// 256 (8 R + Cb), element (rho, sigma) of the tile at 16 rho + sigma, so that both passes move
-// whole 1 KiB tiles.
-//
-// Both passes stage block b while block b - 1 (pass 1) or b + 1 (pass 2) may still be read, in
-// the other of two LDS buffers, so one barrier per block suffices; results the waves combine
-// (dbeta, the Grams, the scalar gate's dg) are summed after the next block's barrier.
+// The chain stages each block into one LDS buffer and takes two barriers per block (after the
+// staging; after the step, before the gradient entering the next step is written for P3); the
+// column pass stages block b + 1 while block b may still be read, in the other of two LDS
+// buffers, so one barrier per block suffices.  Results the waves combine (dbeta, the Grams, the
+// scalar gate's dg) are summed after a later barrier.
 constexpr int GP = W + 4;   // row pitch of the per-wave 16 x 16 partials
 
 template <int NWC>
@@ -1192,7 +1195,7 @@ __global__ void __launch_bounds__(NT) colsum_kernel(const Mf128Args a) {
     if (ts >= L) return;
     const int nb = (min(ts + C, L) - ts + W - 1) / W;
 
-    // a 128 x 128 matrix in the column layout: row-major [S][S] (the snapshots) or tile-major (X')
+    // a 128 x 128 row-major [S][S] matrix (a snapshot) in the column layout
     const uint32_t vcol = ((4 * g4) * S + i0 + lm) * 4;
     auto load_cols = [&](const float *base, f4 (&Mc)[8]) {
         const Rsrc rs = rsrc(base);
