@@ -80,11 +80,12 @@ TRAFFIC = {
         "kernels": ("l2norm_kernel<4, 16, true>",)},
     ("ssm_scan", "ssm2_layer_h80_p64_n128"): {
         "file": "traffic_ssm2_layer_h80_p64_n128.json",
-        "sources": [_C + "ssm_scan.hip", _C + "gdn_api.hip", _C + "gdn_internal.h"],
-        "kernels": ("ssm_bwd_kernel<8, false>", "ssm_combine_kernel")},
+        "sources": [_C + "ssm_chunk.hip", _C + "ssm_scan.hip", _C + "ssm_common.h", _C + "gdn_api.hip",
+                    _C + "gdn_internal.h"],
+        "kernels": ("ssm_dsq_kernel<64, 128>", "ssm_chunk_kernel<64, 128>", "ssm_chunk_combine_kernel")},
     ("ssm_scan", "ssm1_layer_d5120_n16"): {
         "file": "traffic_ssm1_layer_d5120_n16.json",
-        "sources": [_C + "ssm_scan.hip", _C + "gdn_api.hip", _C + "gdn_internal.h"],
+        "sources": [_C + "ssm_scan.hip", _C + "ssm_common.h", _C + "gdn_api.hip", _C + "gdn_internal.h"],
         "kernels": ("ssm_bwd_kernel<1, true>", "ssm_combine_kernel")},
 }
 
@@ -355,7 +356,9 @@ def bench_l2norm(args):
 def bench_ssm(args):
     """The selective scan forward + backward (gdn_ssm_fwd, then gdn_ssm_bwd reusing its window
     states) on a layer-sized workload.  Credited work per token x state element: forward 5
-    flops (decay, input, readout), backward 12 (window replay 3, reverse walk 9)."""
+    flops (decay, input, readout), backward 12 (window replay 3, reverse walk 9) -- the
+    per-token recurrence's count, also for the Mamba-2 shape, whose backward runs in 32-token
+    chunks on the fp32 matrix cores (the same 157.3 TFLOP/s peak as the vector ALUs)."""
     import torch
     from gated_delta_rule_bwd_amd import binding as B
     from gated_delta_rule_bwd_amd import inputs as I
@@ -401,6 +404,7 @@ def bench_ssm(args):
     n, T, H, P, N = (cfg[k] for k in ("n_seqs", "T", "H", "P", "N"))
     elems = n * T * H * P * N                     # token x state-element steps
     bwd_flops = 12 * elems
+    chunked = not cfg["a_per_state"] and P == 64 and N == 128
     out = {
         "metric": "SSM_SCAN fwd+bwd token·state-element steps/s; % FP32 VALU peak",
         "value": elems / (ms / 1e3), "unit": "token·state-elements/s", "n_gpus": 1,
@@ -410,7 +414,8 @@ def bench_ssm(args):
                                                              "a_per_state")}},
         "fwd_ms": fwd_ms, "bwd_ms": bwd_ms,
         "pct_fp32_valu_peak": 100.0 * 17 * elems / (ms / 1e3) / PEAK_FP32_VALU,
-        "roofline": {"bound": "alu", "kernel": "gdn_ssm_bwd (ssm_bwd_kernel + ssm_combine_kernel)",
+        "roofline": {"bound": "mfma" if chunked else "alu",
+                     "kernel": "gdn_ssm_bwd (" + " + ".join(TRAFFIC[("ssm_scan", name)]["kernels"]) + ")",
                      "achieved": bwd_flops / (bwd_ms / 1e3) / 1e12, "peak": PEAK_FP32_VALU / 1e12,
                      "unit": "TFLOP/s", "frac": bwd_flops / (bwd_ms / 1e3) / PEAK_FP32_VALU,
                      "traffic": traffic_bytes("ssm_scan", name)},

@@ -14,7 +14,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libgdn.so")
 SOURCES = ["gdn_api.hip", "gdn_kernels.hip", "gdn_mf.hip", "ssm_conv.hip", "l2norm.hip",
-           "ssm_scan.hip"]
+           "ssm_scan.hip", "ssm_chunk.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

@@ -809,8 +809,10 @@ int gdn_l2norm_bwd(const gdn_l2norm_problem *p, const float *x, const float *dy,
 // ---- selective scan ----------------------------------------------------------------------
 
 struct SsmPlan {
-    size_t off_ck, off_part, off_dd, total;
+    size_t off_ck, off_part, off_dd, off_dsq, off_cpart, total;
     int64_t rows, nwin;
+    int32_t ckw, nck, hgs;
+    bool chunked;   // backward in 32-token chunks on the matrix cores (see ssm_chunk.hip)
 };
 
 static int ssm_validate(const gdn_ssm_problem *p) {
@@ -828,13 +830,31 @@ static int ssm_validate(const gdn_ssm_problem *p) {
 
 static SsmPlan ssm_plan(const gdn_ssm_problem *p) {
     SsmPlan pl;
-    const size_t n = p->n_seqs, T = p->T, H = p->H, P = p->P, N = p->N;
+    const size_t n = p->n_seqs, T = p->T, H = p->H, P = p->P, N = p->N, G = p->G;
     pl.rows = (int64_t)(n * H * P);
     pl.nwin = (p->T + 7) / 8;
+    pl.chunked = gdn::ssm_chunked(p->P, p->N, p->a_per_state);
     size_t off = 0;
-    pl.off_ck = off;   off += align_up((size_t)pl.rows * pl.nwin * N * 4);
-    pl.off_part = off; off += align_up((size_t)pl.rows / 16 * T * 2 * N * 4);
-    pl.off_dd = off;   off += align_up(n * T * H * P * 4);
+    pl.off_part = pl.off_dd = pl.off_dsq = pl.off_cpart = 0;
+    pl.hgs = 1;
+    if (pl.chunked) {
+        // the state before every 32-token chunk; the state gradient after each chunk; dB, dC
+        // per head slice, enough slices for about 2048 workgroups
+        const int64_t nc = (p->T + 31) / 32, Hg = p->H / p->G;
+        const int64_t wgs = std::max<int64_t>(1, (int64_t)n * nc * p->G);
+        pl.hgs = (int32_t)std::max<int64_t>(1, std::min<int64_t>({(2048 + wgs - 1) / wgs, Hg, 16}));
+        pl.ckw = 4;
+        pl.nck = (int32_t)nc;
+        pl.off_ck = off;    off += align_up((size_t)pl.rows * nc * N * 4);
+        pl.off_dsq = off;   off += align_up(n * H * nc * P * N * 4);
+        pl.off_cpart = off; off += align_up((size_t)pl.hgs * 2 * n * T * G * N * 4);
+    } else {
+        pl.ckw = 1;
+        pl.nck = (int32_t)pl.nwin;
+        pl.off_ck = off;   off += align_up((size_t)pl.rows * pl.nwin * N * 4);
+        pl.off_part = off; off += align_up((size_t)pl.rows / 16 * T * 2 * N * 4);
+        pl.off_dd = off;   off += align_up(n * T * H * P * 4);
+    }
     pl.total = off;
     return pl;
 }
@@ -891,6 +911,9 @@ static gdn::SsmArgs ssm_args(const gdn_ssm_problem *p, const SsmPlan &pl, void *
     a.ck = (float *)(w + pl.off_ck);
     a.part = (float *)(w + pl.off_part);
     a.ddrow = (float *)(w + pl.off_dd);
+    a.dsq = (float *)(w + pl.off_dsq);
+    a.cpart = (float *)(w + pl.off_cpart);
+    a.ckw = pl.ckw; a.nck = pl.nck; a.hgs = pl.hgs;
     a.n_seqs = p->n_seqs; a.T = p->T; a.H = p->H; a.P = p->P; a.N = p->N; a.G = p->G;
     a.aps = p->a_per_state; a.softplus = p->dt_softplus;
     return a;
@@ -940,8 +963,12 @@ int gdn_ssm_bwd(const gdn_ssm_problem *p, const float *s0, const float *x, const
     hipError_t e = hipSuccess;
     if (!(flags & GDN_BWD_REUSE_SNAPSHOTS))     // window states first (no y, s_out)
         e = gdn::launch_ssm(a, false, (hipStream_t)stream);
-    if (e == hipSuccess) e = gdn::launch_ssm(a, true, (hipStream_t)stream);
-    if (e == hipSuccess) e = gdn::launch_ssm_combine(a, (hipStream_t)stream);
+    if (pl.chunked) {
+        if (e == hipSuccess) e = gdn::launch_ssm_chunk_bwd(a, (hipStream_t)stream);
+    } else {
+        if (e == hipSuccess) e = gdn::launch_ssm(a, true, (hipStream_t)stream);
+        if (e == hipSuccess) e = gdn::launch_ssm_combine(a, (hipStream_t)stream);
+    }
     return device_status(e);
 }
 

@@ -17,6 +17,7 @@
 #include <hip/hip_runtime.h>
 
 #include "gdn_internal.h"
+#include "ssm_common.h"
 
 namespace gdn {
 namespace {
@@ -86,19 +87,6 @@ __device__ __forceinline__ Row row_of(const SsmArgs &a, int64_t r) {
     return o;
 }
 
-// The step of a token and head: softplus(dt) = log(1 + e^dt), or the raw dt.  Computed with
-// the hardware exp and log: below dt = -4 (e^dt < 0.019) as the series e - e^2/2 + e^3/3 -
-// e^4/4 (truncation below 2e-8 relative), elsewhere as log(1 + e^dt), whose argument is then
-// at least 1.018 so the rounding of 1 + e^dt costs at most ~3e-6 relative; above 20 it is dt.
-// Both directions use this one function, so the backward's replay gives the forward's bits.
-__device__ __forceinline__ float step_of(float z, int softplus) {
-    if (!softplus) return z;
-    const float e = __expf(z);
-    const float series = e * (1.f - e * (0.5f - e * (1.f / 3.f - e * 0.25f)));
-    const float direct = __logf(1.f + e);
-    return z > 20.f ? z : (z < -4.f ? series : direct);
-}
-
 // ---- window staging --------------------------------------------------------------------
 // The 16 rows of a workgroup share one (sequence, group), so a window's B and C rows are
 // common to all of them; x, the step (and gy) are per row.  Each window is staged in LDS once
@@ -158,7 +146,7 @@ struct Loader {
         }
         const int tok = (tid & 127) >> 4, rr = tid & 15;
         if (tid < 128) st.x[tok][rr] = s0v;
-        else st.d[tok][rr] = step_of(s0v, a.softplus);
+        else st.d[tok][rr] = ssm_step(s0v, a.softplus);
         if constexpr (GY) {
             if (tid < 128) st.gy[tok][rr] = s1v;
         }
@@ -232,7 +220,8 @@ __global__ void __launch_bounds__(256) ssm_fwd_kernel(const SsmArgs a) {
         const int cur = win & 1;
         const int t0 = win * WIN, cnt = wcnt(win);
         if (win + PD - 1 < nwin) ld[(U + PD - 1) % PD].load(a, (win + PD - 1) * WIN, wcnt(win + PD - 1));
-        st_cols<NPL>(a.ck + (w.r * nwin + win) * N, sub, st);     // state before the window
+        if (win % a.ckw == 0)                                       // state before the window
+            st_cols<NPL>(a.ck + (w.r * a.nck + win / a.ckw) * N, sub, st);
         const Stage<16 * NPL> &sg = stg[cur];
 #pragma unroll
         for (int k = 0; k < WIN; ++k) {
@@ -305,7 +294,7 @@ __global__ void __launch_bounds__(256) ssm_bwd_kernel(const SsmArgs a) {
         if (win > 0) ld.load(a, t0 - WIN, WIN);
         const Stage<16 * NPL> &sg = stg[cur];
         float sp[NPL], S[WIN][NPL];
-        ld_cols<NPL>(a.ck + (w.r * nwin + win) * N, sub, sp);
+        ld_cols<NPL>(a.ck + (w.r * a.nck + win) * N, sub, sp);   // every window saved
         // replay the window: S[k] is the state after token t0 + k
 #pragma unroll
         for (int k = 0; k < WIN; ++k) {

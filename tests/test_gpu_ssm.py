@@ -73,6 +73,12 @@ CASES = [
     (2, 8, 4, 16, 32, 4, False, True, True),      # exactly one window; one head per group
     (1, 1, 2, 16, 16, 1, False, True, True),      # one token
     (2, 0, 4, 16, 32, 2, False, True, True),      # no tokens: d_s0 is the cotangent itself
+    # head size 64 with 128 states and one decay per head: the backward in 32-token chunks
+    (2, 100, 4, 64, 128, 2, False, True, True),   # two groups of two heads, ragged last chunk
+    (1, 64, 3, 64, 128, 1, False, False, False),  # raw steps, no final-state cotangent, 2 chunks
+    (1, 40, 40, 64, 128, 1, False, True, True),   # 16 head slices of 3 heads, two of them empty
+    (1, 1, 2, 64, 128, 2, False, True, True),     # one token
+    (2, 0, 2, 64, 128, 1, False, True, True),     # no tokens
 ]
 
 
@@ -98,6 +104,29 @@ def test_ssm_parity(dev, n, T, H, P, N, G, aps, softplus, with_gs):
         assert np.array_equal(grads[k], grads2[k]), k
     if T == 0:
         assert np.array_equal(grads["ds"], arr["gs"] if with_gs else np.zeros_like(arr["gs"]))
+
+
+def test_ssm_chunked_unaligned_rows(dev):
+    """x and gy one float past a 16-byte boundary (the API asks 4-byte alignment of them): the
+    chunked backward reads their rows with scalar loads and gives the aligned run's bits."""
+    arr = _arrays(1, 70, 2, 64, 128, 1, False, True, 1700)
+    y, sT, ga = run(dev, arr)
+    g = {k: torch.from_numpy(np.ascontiguousarray(v)).cuda() for k, v in arr.items()}
+    for k in ("x", "gy"):
+        buf = torch.empty(g[k].numel() + 1, device="cuda")
+        buf[1:] = g[k].reshape(-1)
+        g[k] = buf[1:].view(g[k].shape)
+        assert g[k].data_ptr() % 16 == 4
+    p = dev.ssm_problem_from(g["x"], g["B"], g["A"], True)
+    ws = torch.empty(max(dev.ssm_workspace_size(p), 16) // 4, dtype=torch.float32, device="cuda")
+    y2, s2 = torch.empty(g["x"].shape, device="cuda"), torch.empty_like(g["s0"])
+    dev.ssm_fwd(p, g["s0"], g["x"], g["dt"], g["A"], g["B"], g["C"], y2, s2, ws)
+    total, lay = dev.ssm_grad_layout(p)
+    gp = torch.full((total,), float("nan"), device="cuda")
+    dev.ssm_bwd(p, g["s0"], g["x"], g["dt"], g["A"], g["B"], g["C"], g["gy"], g["gs"], gp, ws, flags=1)
+    torch.cuda.synchronize()
+    for k, (o, shp) in lay.items():
+        assert np.array_equal(gp[o:o + int(np.prod(shp))].view(shp).cpu().numpy(), ga[k]), k
 
 
 def test_ssm_deterministic(dev):
