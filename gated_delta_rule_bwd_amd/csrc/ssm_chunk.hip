@@ -91,7 +91,10 @@ __device__ __forceinline__ f4 ld4u(const float *p, bool vec) {
 // ---- pass 1: the state gradient after every chunk ---------------------------------------
 // One wave per (sequence, head, 16 rows of P, 64 columns of N) walks the chunks backwards and
 // keeps its 16 x 64 slice of dS in four accumulator tiles: dsq[c] is the gradient of the state
-// after chunk c, and after chunk 0 the gradient of the initial state is d_s0.
+// after chunk c, and after chunk 0 the gradient of the initial state is d_s0.  Column l % 16 of
+// tile j is state 64 nh + 4 (l % 16) + j, so a lane reads the four states of its C operand, and
+// writes its four tiles' values of a row, as one float4.  The chunks' inputs are loaded two
+// chunks ahead.
 template <int P, int N>
 __global__ void __launch_bounds__(64) ssm_dsq_kernel(const SsmArgs a) {
     const int lane = threadIdx.x, ar = lane & 15, kg = lane >> 4;
@@ -105,15 +108,17 @@ __global__ void __launch_bounds__(64) ssm_dsq_kernel(const SsmArgs a) {
     const int nc = (a.T + Q - 1) / Q;
     const float Ah = a.A[h];
     const int prow = 16 * pt + 4 * kg;   // rows of the lane's accumulator registers
-    const int ncol = 64 * nh + ar;       // its column in tile j is ncol + 16 j
+    const int ncol = 64 * nh + 4 * ar;   // its four states (one per tile)
     f4 acc[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int r = 0; r < 4; ++r) {
+        const f4 v = a.gs ? ld4(a.gs + (unit * P + prow + r) * N + ncol) : zero4();
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-            acc[j][r] = a.gs ? a.gs[(unit * P + prow + r) * N + ncol + 16 * j] : 0.f;
+        for (int j = 0; j < 4; ++j) acc[j][r] = v[j];
+    }
     struct Ld {
-        float gy[8], c[4][8], dt;
+        f4 c[8];
+        float gy[8], dt;
     };
     auto load = [&](int c, Ld &L) {
         const int t0 = c * Q;
@@ -121,49 +126,49 @@ __global__ void __launch_bounds__(64) ssm_dsq_kernel(const SsmArgs a) {
         for (int q = 0; q < 2; ++q)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int t = t0 + 16 * q + 4 * kg + i;
-                const bool ok = t < a.T;
-                const int64_t tc = ok ? t : T - 1;
-                const float gv = a.gy[((s * T + tc) * H + h) * P + 16 * pt + ar];
-                L.gy[4 * q + i] = ok ? gv : 0.f;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const float cv = a.C[((s * T + tc) * G + g) * N + ncol + 16 * j];
-                    L.c[j][4 * q + i] = ok ? cv : 0.f;
-                }
+                const int64_t tc = std::min(t0 + 16 * q + 4 * kg + i, a.T - 1);   // masked at use
+                L.gy[4 * q + i] = a.gy[((s * T + tc) * H + h) * P + 16 * pt + ar];
+                L.c[4 * q + i] = ld4(a.C + ((s * T + tc) * G + g) * N + ncol);
             }
         L.dt = a.dt[(s * T + std::min(t0 + (lane & 31), a.T - 1)) * H + h];
     };
     float *dsq = a.dsq + unit * nc * (int64_t)(P * N);
-    Ld cur, nxt;
-    if (nc > 0) load(nc - 1, cur);
-    for (int c = nc - 1; c >= 0; --c) {
-        if (c > 0) load(c - 1, nxt);
+    auto step = [&](int c, const Ld &L) {
         float *o = dsq + (int64_t)c * P * N;
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) o[(prow + r) * N + ncol + 16 * j] = acc[j][r];
+        for (int r = 0; r < 4; ++r) st4(o + (prow + r) * N + ncol, f4{acc[0][r], acc[1][r], acc[2][r], acc[3][r]});
         const bool ok = lane < Q && c * Q + lane < a.T;
-        const float l = ok ? ssm_step(cur.dt, a.softplus) * Ah : 0.f;
+        const float l = ok ? ssm_step(L.dt, a.softplus) * Ah : 0.f;
         const float e = __expf(scan32(l, lane));
         const float elast = __shfl(e, Q - 1, 64);
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[j] *= elast;
 #pragma unroll
-        for (int q = 0; q < 2; ++q)
+        for (int k = 0; k < 8; ++k) {
+            const int kt = 16 * (k >> 2) + 4 * kg + (k & 3);
+            const float ek = __shfl(e, kt, 64);   // every lane takes part in the shuffle
+            // a token past the end adds nothing (its C is finite: a clamped in-range row)
+            const float av = c * Q + kt < a.T ? L.gy[k] * ek : 0.f;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float av = cur.gy[4 * q + i] * __shfl(e, 16 * q + 4 * kg + i, 64);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) acc[j] = mfma(av, cur.c[j][4 * q + i], acc[j]);
-            }
-        if (c > 0) cur = nxt;
+            for (int j = 0; j < 4; ++j) acc[j] = mfma(av, L.c[k][j], acc[j]);
+        }
+    };
+    Ld L0, L1, L2;
+    if (nc > 0) load(nc - 1, L0);
+    if (nc > 1) load(nc - 2, L1);
+    for (int c = nc - 1; c >= 0; c -= 3) {
+        if (c >= 2) load(c - 2, L2);
+        step(c, L0);
+        if (c < 1) break;
+        if (c >= 3) load(c - 3, L0);
+        step(c - 1, L1);
+        if (c < 2) break;
+        if (c >= 4) load(c - 4, L1);
+        step(c - 2, L2);
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) a.ds0[(unit * P + prow + r) * N + ncol + 16 * j] = acc[j][r];
+    for (int r = 0; r < 4; ++r)
+        st4(a.ds0 + (unit * P + prow + r) * N + ncol, f4{acc[0][r], acc[1][r], acc[2][r], acc[3][r]});
 }
 
 // ---- pass 2: the chunks' gradients ------------------------------------------------------
@@ -232,12 +237,9 @@ __global__ void __launch_bounds__(512) ssm_chunk_kernel(const SsmArgs a) {
     auto fetch = [&](int64_t h, Pf &F) {
         {
             const int row = tid >> 4, c4 = tid & 15;
-            const int t = t0 + row;
-            const bool ok = t < a.T;
-            const int64_t off = ((s * T + (ok ? t : T - 1)) * H + h) * P + 4 * c4;
-            const f4 xv = ld4u(a.x + off, vec), gv = ld4u(a.gy + off, vec);
-            F.x = ok ? xv : zero4();
-            F.gy = ok ? gv : zero4();
+            const int64_t off = ((s * T + std::min(t0 + row, a.T - 1)) * H + h) * P + 4 * c4;
+            F.x = ld4u(a.x + off, vec);    // rows past the end are zeroed when staged
+            F.gy = ld4u(a.gy + off, vec);
         }
         const float *dsp = a.dsq + ((s * H + h) * nc + c) * (int64_t)(P * N);
         const float *sip = a.ck + (s * H + h) * P * (int64_t)a.nck * N + (int64_t)(c * QW / a.ckw) * N;
@@ -252,8 +254,9 @@ __global__ void __launch_bounds__(512) ssm_chunk_kernel(const SsmArgs a) {
     auto put = [&](const Pf &F, int par, float Ah) {
         {
             const int row = tid >> 4, c4 = tid & 15;
-            st4(&sm.xs[row][4 * c4], F.x);
-            st4(&sm.gys[row][4 * c4], F.gy);
+            const bool ok = t0 + row < a.T;
+            st4(&sm.xs[row][4 * c4], ok ? F.x : zero4());
+            st4(&sm.gys[row][4 * c4], ok ? F.gy : zero4());
         }
         float k0 = 0.f;
 #pragma unroll
