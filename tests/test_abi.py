@@ -361,6 +361,19 @@ def test_ssm_sizes_and_layout(B):
     assert [lay[k][0] for k in ("ds", "dx", "ddt", "dB", "dC")] == [sum(sizes[:i]) for i in range(5)]
 
 
+def test_ssm_chunked_workspace(B):
+    """One decay per head with P = 64, N = 128: the chunked backward's workspace (the state before
+    each 32-token chunk, the state gradient after each chunk, dB and dC per head slice; here two
+    slices, one per head of a group), much smaller than the per-token form's."""
+    up = lambda b: (b + 255) // 256 * 256
+    n, T, H, P, N, G = 2, 100, 4, 64, 128, 2
+    nc, rows = 4, n * H * P
+    ws = B.ssm_workspace_size(_ssm(B, n_seqs=n, T=T, H=H, P=P, N=N, G=G))
+    assert ws == up(4 * rows * nc * N) + up(4 * n * H * nc * P * N) + up(4 * 2 * 2 * n * T * G * N)
+    per_token = B.ssm_workspace_size(_ssm(B, n_seqs=n, T=T, H=H, P=P, N=N, G=G, a_per_state=1))
+    assert per_token >= 4 * (rows * 13 * N + rows // 16 * T * 2 * N + n * T * H * P) > ws
+
+
 @pytest.mark.parametrize("kw,code", [
     (dict(H=4, G=3), -1), (dict(N=24), -2), (dict(N=256), -2), (dict(P=3, H=4, G=2), -2),
     (dict(a_per_state=2), -1), (dict(dt_softplus=-1), -1), (dict(T=-1), -1), (dict(P=0), -1),
