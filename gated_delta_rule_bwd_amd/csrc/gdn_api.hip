@@ -809,10 +809,11 @@ int gdn_l2norm_bwd(const gdn_l2norm_problem *p, const float *x, const float *dy,
 // ---- selective scan ----------------------------------------------------------------------
 
 struct SsmPlan {
-    size_t off_ck, off_part, off_dd, off_dsq, off_cpart, total;
+    size_t off_ck, off_part, off_dd, off_dsq, off_cpart, off_gsw, total;
     int64_t rows, nwin;
-    int32_t ckw, nck, hgs;
+    int32_t ckw, nck, hgs, seg_rows;
     bool chunked;   // backward in 32-token chunks on the matrix cores (see ssm_chunk.hip)
+    bool rowwise;   // 16 states: backward in two passes, one lane per row (see ssm_scan.hip)
 };
 
 static int ssm_validate(const gdn_ssm_problem *p) {
@@ -834,9 +835,11 @@ static SsmPlan ssm_plan(const gdn_ssm_problem *p) {
     pl.rows = (int64_t)(n * H * P);
     pl.nwin = (p->T + 7) / 8;
     pl.chunked = gdn::ssm_chunked(p->P, p->N, p->a_per_state);
+    pl.rowwise = !pl.chunked && gdn::ssm_rowwise(p->P, p->H, p->G, p->N);
     size_t off = 0;
-    pl.off_part = pl.off_dd = pl.off_dsq = pl.off_cpart = 0;
+    pl.off_part = pl.off_dd = pl.off_dsq = pl.off_cpart = pl.off_gsw = 0;
     pl.hgs = 1;
+    pl.seg_rows = pl.rowwise ? 256 : 16;
     if (pl.chunked) {
         // the state before every 32-token chunk; the state gradient after each chunk; dB, dC
         // per head slice, enough slices for about 2048 workgroups
@@ -852,8 +855,11 @@ static SsmPlan ssm_plan(const gdn_ssm_problem *p) {
         pl.ckw = 1;
         pl.nck = (int32_t)pl.nwin;
         pl.off_ck = off;   off += align_up((size_t)pl.rows * pl.nwin * N * 4);
-        pl.off_part = off; off += align_up((size_t)pl.rows / 16 * T * 2 * N * 4);
+        pl.off_part = off; off += align_up((size_t)pl.rows / pl.seg_rows * T * 2 * N * 4);
         pl.off_dd = off;   off += align_up(n * T * H * P * 4);
+        if (pl.rowwise) {  // the state gradient entering every window
+            pl.off_gsw = off; off += align_up((size_t)pl.rows * pl.nwin * N * 4);
+        }
     }
     pl.total = off;
     return pl;
@@ -913,7 +919,8 @@ static gdn::SsmArgs ssm_args(const gdn_ssm_problem *p, const SsmPlan &pl, void *
     a.ddrow = (float *)(w + pl.off_dd);
     a.dsq = (float *)(w + pl.off_dsq);
     a.cpart = (float *)(w + pl.off_cpart);
-    a.ckw = pl.ckw; a.nck = pl.nck; a.hgs = pl.hgs;
+    a.gsw = (float *)(w + pl.off_gsw);
+    a.ckw = pl.ckw; a.nck = pl.nck; a.hgs = pl.hgs; a.seg_rows = pl.seg_rows;
     a.n_seqs = p->n_seqs; a.T = p->T; a.H = p->H; a.P = p->P; a.N = p->N; a.G = p->G;
     a.aps = p->a_per_state; a.softplus = p->dt_softplus;
     return a;
@@ -965,6 +972,8 @@ int gdn_ssm_bwd(const gdn_ssm_problem *p, const float *s0, const float *x, const
         e = gdn::launch_ssm(a, false, (hipStream_t)stream);
     if (pl.chunked) {
         if (e == hipSuccess) e = gdn::launch_ssm_chunk_bwd(a, (hipStream_t)stream);
+    } else if (pl.rowwise) {
+        if (e == hipSuccess) e = gdn::launch_ssm_rowwise_bwd(a, (hipStream_t)stream);
     } else {
         if (e == hipSuccess) e = gdn::launch_ssm(a, true, (hipStream_t)stream);
         if (e == hipSuccess) e = gdn::launch_ssm_combine(a, (hipStream_t)stream);

@@ -88,22 +88,29 @@ hipError_t launch_l2norm(const NormArgs &a, bool bwd, hipStream_t st);
 // Selective state-space scan and its reverse recurrence (see ssm_scan.hip, ssm_chunk.hip).
 // Contiguous tensors: s0/s_out/ds0 [n][H][P][N], x/y/gy/dx/ddrow [n][T][H][P], dt/ddt [n][T][H],
 // A [H][N] (aps) or [H], B/C/dB/dC [n][T][G][N]; workspace: ck [rows][nck][N] (the state before
-// every ckw-th 8-token window), and for the per-token backward part [rows/16][T][2][N] and
-// ddrow, for the chunked backward dsq [n][H][ceil(T/32)][P][N] (the state gradient after each
-// 32-token chunk) and cpart [hgs][2][n][T][G][N] (dB, dC summed over each head slice).
+// every ckw-th 8-token window); for the per-token backward part [rows/seg_rows][T][2][N] and
+// ddrow, the row-wise one also gsw [rows][ceil(T/8)][N] (the state gradient entering each
+// window from the right); for the chunked backward dsq [n][H][ceil(T/32)][P][N] (the state
+// gradient after each 32-token chunk) and cpart [hgs][2][n][T][G][N] (dB, dC per head slice).
 struct SsmArgs {
     const float *s0, *x, *dt, *A, *B, *C, *gy, *gs;
-    float *ck, *part, *ddrow, *dsq, *cpart;
+    float *ck, *part, *ddrow, *dsq, *cpart, *gsw;
     float *y, *s_out, *ds0, *dx, *ddt, *dB, *dC;
     int32_t n_seqs, T, H, P, N, G, aps, softplus;
     int32_t ckw, nck;   // windows per saved state (1, or 4 for the chunked backward); states per row
     int32_t hgs;        // head slices per group in the chunked backward
+    int32_t seg_rows;   // rows per column-sum segment of part (16, or 256 in the row-wise backward)
 };
 hipError_t launch_ssm(const SsmArgs &a, bool bwd, hipStream_t st);   // forward or walk
 hipError_t launch_ssm_combine(const SsmArgs &a, hipStream_t st);
 // Chunked backward (one decay per head, P = 64, N = 128): the chunk-end state gradients, the
 // chunks' gradients on the matrix cores, then the head slices' dB and dC summed in order.
 bool ssm_chunked(int P, int N, int aps);
+// Row-wise backward for 16 states (rows of a group a multiple of 256): the state gradient
+// entering every 8-token window, then the windows in parallel with one lane per row, then the
+// combine over 256-row segments.
+bool ssm_rowwise(int P, int H, int G, int N);
+hipError_t launch_ssm_rowwise_bwd(const SsmArgs &a, hipStream_t st);
 hipError_t launch_ssm_chunk_bwd(const SsmArgs &a, hipStream_t st);
 // head sizes: key width SK and value width SV, each in {16, 32, 64, 128}, not both 128
 hipError_t launch_fwd(const FwdArgs &a, int SK, int SV, bool kda, int n_seqs_launch, hipStream_t st);

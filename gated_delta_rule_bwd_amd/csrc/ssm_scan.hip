@@ -397,6 +397,207 @@ __global__ void __launch_bounds__(256) ssm_bwd_kernel(const SsmArgs a) {
     st_cols<NPL>(a.ds0 + w.r * N, sub, gs);
 }
 
+// ---- row-wise backward for 16 states ---------------------------------------------------
+// With 16 states a lane of the per-token walk above owns one state element, so most of its
+// instructions are the per-token sums across lanes.  Here the walk is split in two passes:
+// pass 1 runs the state gradient's own recurrence (gs += gy C, gs *= a from the last token) in
+// the forward's layout and stores the gradient entering every window from the right (and
+// d_s0); pass 2 then takes every window independently, one lane per row with its 16 states in
+// registers, so a row's sums (dx, the ddt term) are in-lane, and only the column sums of a token
+// (dC, dB over rows) cross lanes: a reduce-scatter over the wave after which each lane holds one
+// (quantity, state) sum over the wave's 64 rows, then a sum over the four waves in LDS.  The
+// gradient chain runs the walk's own operations in the walk's order, so pass 2 starts each
+// window from the gradient the single-pass walk would have there.
+constexpr int GB = 32;   // tokens per staging block of pass 1
+
+template <bool APS>
+__global__ void __launch_bounds__(256) ssm_gsw_kernel(const SsmArgs a) {
+    // per block of GB tokens: the rows' gy and step, the group's C (16 states)
+    __shared__ float sgy[2][GB][ROWS], sd[2][GB][ROWS], sC[2][GB][16];
+    const int tid = threadIdx.x, sub = tid & 15, rho = tid >> 4;
+    const int64_t r0 = (int64_t)blockIdx.x * ROWS;
+    const Row w = row_of(a, r0 + rho);
+    const int64_t N = a.N, T = a.T, H = a.H, P = a.P, G = a.G;
+    const int nwin = (a.T + WIN - 1) / WIN;
+    const int nblk = (a.T + GB - 1) / GB;
+    float gs = a.gs ? a.gs[w.r * N + sub] : 0.f;
+    const float Aj = APS ? a.A[w.h * N + sub] : a.A[w.h];
+    // thread tid stages token pairs (tokens 2 (tid >> 4) + {0, 1}) of row tid & 15: gy, dt; and
+    // C of those tokens, state tid & 15
+    const Row lw = row_of(a, r0 + sub);
+    const int tk = 2 * rho;
+    float pg[2], pd[2], pc[2];
+    auto load = [&](int blk) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int64_t t = min(blk * GB + tk + u, a.T - 1);
+            pg[u] = a.gy[((lw.s * T + t) * H + lw.h) * P + lw.i];
+            pd[u] = a.dt[(lw.s * T + t) * H + lw.h];
+            pc[u] = a.C[((lw.s * T + t) * G + lw.g) * N + sub];
+        }
+    };
+    // a token past the end gets gy = 0 and step 0 (decay 1): it leaves gs as it is, so the
+    // token loop below needs no branch and its LDS reads can run ahead
+    auto put = [&](int blk, int buf) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const bool ok = blk * GB + tk + u < a.T;
+            sgy[buf][tk + u][sub] = ok ? pg[u] : 0.f;
+            sd[buf][tk + u][sub] = ok ? ssm_step(pd[u], a.softplus) : 0.f;
+            sC[buf][tk + u][sub] = pc[u];
+        }
+    };
+    if (nblk > 0) {
+        load(nblk - 1);
+        put(nblk - 1, 0);
+    }
+    __syncthreads();
+    for (int it = 0; it < nblk; ++it) {
+        const int blk = nblk - 1 - it, cur = it & 1;
+        const int t0 = blk * GB;
+        if (blk > 0) load(blk - 1);
+#pragma unroll
+        for (int k = GB - 1; k >= 0; --k) {
+            if ((k & (WIN - 1)) == WIN - 1)   // the gradient entering the window (a window past
+                // the end stores the unchanged value into the last window's slot, which that
+                // window then writes again with the same bits)
+                a.gsw[(w.r * nwin + min((t0 + k) / WIN, nwin - 1)) * N + sub] = gs;
+            gs = fmaf(sgy[cur][k][rho], sC[cur][k][sub], gs);
+            gs = dexp(sd[cur][k][rho] * Aj) * gs;
+        }
+        if (blk > 0) put(blk - 1, cur ^ 1);
+        __syncthreads();
+    }
+    a.ds0[w.r * N + sub] = gs;
+}
+
+constexpr int RB = 256;   // rows per block of pass 2 (and per column-sum segment)
+
+__device__ __forceinline__ void ld16(const float *p, float (&v)[16]) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const float4 t = reinterpret_cast<const float4 *>(p)[q];
+        v[4 * q] = t.x; v[4 * q + 1] = t.y; v[4 * q + 2] = t.z; v[4 * q + 3] = t.w;
+    }
+}
+
+template <bool APS>
+__global__ void __launch_bounds__(256) ssm_win16_kernel(const SsmArgs a) {
+    constexpr int N = 16;
+    __shared__ float bc[2][WIN][N];          // B, C rows of the window's tokens
+    __shared__ float red[WIN][4][2 * N];     // [token][wave][dC | dB state]
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int nwin = (a.T + WIN - 1) / WIN;
+    const int win = (int)(blockIdx.x % nwin);
+    const int64_t rb = blockIdx.x / nwin;
+    const Row w = row_of(a, rb * RB + tid);   // the block's rows share (sequence, group)
+    const int64_t T = a.T, H = a.H, P = a.P, G = a.G;
+    const int t0 = win * WIN, cnt = min(WIN, a.T - t0);
+    {
+        const int k = tid >> 5, q = (tid >> 4) & 1, n = tid & 15;
+        const Row w0 = row_of(a, rb * RB);
+        const int64_t t = min(t0 + k, a.T - 1);
+        bc[q][k][n] = (q ? a.C : a.B)[((w0.s * T + t) * G + w0.g) * N + n];
+    }
+    float sp[N], gs[N], Av[N];
+    ld16(a.ck + (w.r * a.nck + win) * N, sp);
+    ld16(a.gsw + (w.r * nwin + win) * N, gs);
+    float Ah = 0.f;
+    if constexpr (APS) ld16(a.A + w.h * N, Av);
+    else Ah = a.A[w.h];
+    float xv[WIN], gv[WIN], dv[WIN], sg[WIN];
+#pragma unroll
+    for (int k = 0; k < WIN; ++k) {
+        const int64_t t = min(t0 + k, a.T - 1);   // tokens past the end are skipped below
+        const int64_t at = ((w.s * T + t) * H + w.h) * P + w.i;
+        // a token past the end gets x = gy = 0 and step 0: the replay leaves the state as it
+        // is, so it needs no branch per token
+        const bool ok = t0 + k < a.T;
+        const float xr = a.x[at], gr = a.gy[at], z = a.dt[(w.s * T + t) * H + w.h];
+        xv[k] = ok ? xr : 0.f;
+        gv[k] = ok ? gr : 0.f;
+        dv[k] = ok ? ssm_step(z, a.softplus) : 0.f;
+        sg[k] = (P == 1 && a.softplus) ? 1.f / (1.f + expf(-z)) : 1.f;   // a head of one row: ddt
+    }
+    __syncthreads();
+    // replay: S[k] is the state after token t0 + k
+    float S[WIN][N];
+#pragma unroll
+    for (int k = 0; k < WIN; ++k) {
+        const float b = dv[k] * xv[k];
+        const float ah = APS ? 0.f : dexp(dv[k] * Ah);
+#pragma unroll
+        for (int n = 0; n < N; ++n) {
+            const float aj = APS ? dexp(dv[k] * Av[n]) : ah;
+            S[k][n] = fmaf(aj, k ? S[k - 1][n] : sp[n], b * bc[0][k][n]);
+        }
+    }
+    const bool b3 = lane & 8, b2 = lane & 4, b1 = lane & 2;
+    // the walk recomputes the decays rather than keeping the replay's 8 x 16 (registers): an
+    // empty asm statement hides the steps' identity from the compiler, which would keep them
+#pragma unroll
+    for (int k = 0; k < WIN; ++k) asm volatile("" : "+v"(dv[k]));
+#pragma unroll
+    for (int k = WIN - 1; k >= 0; --k) {
+        // a uniform branch per token: it also keeps the compiler from overlapping the tokens'
+        // walks, whose live values would not fit the registers
+        if (k < cnt) {
+            const float d = dv[k], xk = xv[k], gyk = gv[k], dxv = d * xk;
+            const float ah = APS ? 0.f : dexp(d * Ah);
+            float v[2 * N];   // this row's column terms: dC then dB
+            float gB = 0.f, dec = 0.f;
+#pragma unroll
+            for (int n = 0; n < N; ++n) {
+                const float aj = APS ? dexp(d * Av[n]) : ah;
+                const float prev = k ? S[k - 1][n] : sp[n];
+                gs[n] = fmaf(gyk, bc[1][k][n], gs[n]);
+                v[n] = gyk * S[k][n];
+                v[N + n] = gs[n] * dxv;
+                gB = fmaf(gs[n], bc[0][k][n], gB);
+                dec = APS ? fmaf(gs[n] * (Av[n] * aj), prev, dec) : fmaf(gs[n], prev, dec);
+                gs[n] = aj * gs[n];
+            }
+            const int64_t at = ((w.s * T + t0 + k) * H + w.h) * P + w.i;
+            a.dx[at] = d * gB;
+            (P == 1 ? a.ddt : a.ddrow)[at] = ((APS ? dec : Ah * ah * dec) + xk * gB) * sg[k];
+            // reduce-scatter over the wave: lanes 0-31 keep dC, 32-63 dB (permlane32); then
+            // states 8 bit4 (permlane16), 4 bit3 (row_ror:8), 2 bit2 (row_half_mirror), bit1
+            // (quad lane^2); lane^1 holds the same sum: lane l ends with state (l >> 1) & 15
+            float u[16], w8[8], x4[4], y2[2];
+#pragma unroll
+            for (int m = 0; m < 16; ++m) {
+                auto pr = __builtin_amdgcn_permlane32_swap(as_i(v[m]), as_i(v[16 + m]), false, false);
+                u[m] = as_f(pr[0]) + as_f(pr[1]);
+            }
+#pragma unroll
+            for (int m = 0; m < 8; ++m) {
+                auto pr = __builtin_amdgcn_permlane16_swap(as_i(u[m]), as_i(u[8 + m]), false, false);
+                w8[m] = as_f(pr[0]) + as_f(pr[1]);
+            }
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const float keep = b3 ? w8[4 + m] : w8[m], send = b3 ? w8[m] : w8[4 + m];
+                x4[m] = keep + dpp<0x128>(send);
+            }
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+                const float keep = b2 ? x4[2 + m] : x4[m], send = b2 ? x4[m] : x4[2 + m];
+                y2[m] = keep + dpp<0x141>(send);
+            }
+            float z = (b1 ? y2[1] : y2[0]) + dpp<0x4E>(b1 ? y2[0] : y2[1]);
+            z += dpp<0xB1>(z);
+            if ((lane & 1) == 0) red[k][wave][lane >> 1] = z;
+        }
+    }
+    __syncthreads();
+    {   // the block's partial: [segment][token][dC | dB][state], waves summed in order
+        const int k = tid >> 5, idx = tid & 31;
+        if (k < cnt)
+            a.part[(rb * T + t0 + k) * 2 * N + idx] =
+                ((red[k][0][idx] + red[k][1][idx]) + red[k][2][idx]) + red[k][3][idx];
+    }
+}
+
 // ---- combine: dB, dC over the segments of each group; ddt over the rows of each head ------
 // One thread per (sequence, token, group, 4 columns) of dB / dC, summing the group's segments
 // in increasing order with eight loads in flight; one per (sequence, token, head) of ddt.
@@ -404,14 +605,16 @@ __global__ void __launch_bounds__(256) ssm_combine_kernel(const SsmArgs a) {
     const int64_t T = a.T, H = a.H, G = a.G, N = a.N, P = a.P;
     const int64_t N4 = N / 4;
     const int64_t nbc = (int64_t)a.n_seqs * T * G * N4;    // float4 groups of dB / dC
-    const int64_t ndt = (int64_t)a.n_seqs * T * H;
-    const int64_t K = P * (H / G) / ROWS;                    // segments per group
+    // the row-wise backward writes ddt itself when a head is one row
+    const int64_t ndt = (a.seg_rows != ROWS && P == 1) ? 0 : (int64_t)a.n_seqs * T * H;
+    const int64_t SR = a.seg_rows;                           // rows per segment
+    const int64_t K = P * (H / G) / SR;                      // segments per group
     const int64_t kstride = T * 2 * N;                       // floats between segments
     for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < nbc + ndt;
          idx += (int64_t)gridDim.x * blockDim.x) {
         if (idx < nbc) {
             const int64_t n4 = idx % N4, g = (idx / N4) % G, t = (idx / (N4 * G)) % T, s = idx / (N4 * G * T);
-            const int64_t seg0 = (s * H * P + g * P * (H / G)) / ROWS;
+            const int64_t seg0 = (s * H * P + g * P * (H / G)) / SR;
             const float *pp = a.part + (seg0 * T + t) * 2 * N + 4 * n4;
             float4 dc = make_float4(0.f, 0.f, 0.f, 0.f), db = dc;
             int64_t k = 0;
@@ -476,8 +679,28 @@ hipError_t launch_ssm(const SsmArgs &a, bool bwd, hipStream_t st) {
     }
 }
 
+bool ssm_rowwise(int P, int H, int G, int N) {
+    return N == 16 && G >= 1 && H % G == 0 && (int64_t)P * (H / G) % RB == 0;
+}
+
+hipError_t launch_ssm_rowwise_bwd(const SsmArgs &a, hipStream_t st) {
+    const int64_t rows = (int64_t)a.n_seqs * a.H * a.P;
+    if (rows <= 0) return hipSuccess;
+    if (!ssm_rowwise(a.P, a.H, a.G, a.N) || a.ckw != 1 || a.seg_rows != RB) return hipErrorInvalidValue;
+    void *params[] = {const_cast<SsmArgs *>(&a)};
+    hipError_t e = hipLaunchKernel(a.aps ? (const void *)ssm_gsw_kernel<true> : (const void *)ssm_gsw_kernel<false>,
+                                   dim3((unsigned)(rows / ROWS)), dim3(256), params, 0, st);
+    const int64_t nwin = (a.T + WIN - 1) / WIN;
+    if (e == hipSuccess && nwin > 0)
+        e = hipLaunchKernel(a.aps ? (const void *)ssm_win16_kernel<true> : (const void *)ssm_win16_kernel<false>,
+                            dim3((unsigned)(rows / RB * nwin)), dim3(256), params, 0, st);
+    if (e == hipSuccess) e = launch_ssm_combine(a, st);
+    return e;
+}
+
 hipError_t launch_ssm_combine(const SsmArgs &a, hipStream_t st) {
-    const int64_t n = (int64_t)a.n_seqs * a.T * ((int64_t)a.G * a.N / 4 + a.H);
+    const bool ddt = !(a.seg_rows != ROWS && a.P == 1);
+    const int64_t n = (int64_t)a.n_seqs * a.T * ((int64_t)a.G * a.N / 4 + (ddt ? a.H : 0));
     if (n <= 0) return hipSuccess;
     void *params[] = {const_cast<SsmArgs *>(&a)};
     return hipLaunchKernel((const void *)ssm_combine_kernel, dim3(grid_for(n)), dim3(256), params, 0, st);
