@@ -86,7 +86,7 @@ TRAFFIC = {
     ("ssm_scan", "ssm1_layer_d5120_n16"): {
         "file": "traffic_ssm1_layer_d5120_n16.json",
         "sources": [_C + "ssm_scan.hip", _C + "ssm_common.h", _C + "gdn_api.hip", _C + "gdn_internal.h"],
-        "kernels": ("ssm_bwd_kernel<1, true>", "ssm_combine_kernel")},
+        "kernels": ("ssm_gsw_kernel<true>", "ssm_win16_kernel<true>", "ssm_combine_kernel")},
 }
 
 
