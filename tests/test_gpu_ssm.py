@@ -179,6 +179,33 @@ def test_ssm_layer_sampled(dev, name):
 
 
 @pytest.mark.parametrize("name", ["ssm2_layer_h80_p64_n128", "ssm1_layer_d5120_n16"])
+def test_ssm_layer_tail_elementwise(dev, name):
+    """Full layer size in the benchmark's launch configuration, every head: dB and dC (which fold
+    every head of the group), dx and ddt of the last 512 tokens of sequence 0, elementwise per
+    slice.  The oracle takes the state before those tokens from its own forward over the
+    sequence, then runs forward and backward over the tail from it with the final-state
+    cotangent: the tail's gradients depend on nothing else."""
+    from gated_delta_rule_bwd_amd import inputs as I
+    from oracle import ssm_scan as S
+    cfg = I.SSM_WORKLOADS[name]
+    arr = I.make_ssm(cfg)
+    y, sT, gr = run(dev, arr)
+    T, K = cfg["T"], 512
+    t0 = T - K
+    head = {k: arr[k][:1] for k in ("s0", "x", "dt", "B", "C")}
+    _, s_mid = S.ssm_fwd(head["s0"], head["x"][:, :t0], head["dt"][:, :t0], arr["A"],
+                         head["B"][:, :t0], head["C"][:, :t0])
+    tail = lambda v: v[:1, t0:]
+    _, dx, ddt, dB, dC = S.ssm_bwd(s_mid, tail(arr["x"]), tail(arr["dt"]), arr["A"], tail(arr["B"]),
+                                   tail(arr["C"]), tail(arr["gy"]), arr["gs"][:1])
+    errs = {"dx": _rel(gr["dx"][:1, t0:], dx, "dx"), "ddt": _rel(gr["ddt"][:1, t0:], ddt, "ddt"),
+            "dB": _rel(gr["dB"][:1, t0:], dB, "dB"), "dC": _rel(gr["dC"][:1, t0:], dC, "dC")}
+    log(f"[ssm] {name} last {K} tokens of sequence 0, every head: "
+        + " ".join(f"{k} {v:.1e}" for k, v in errs.items()))
+    assert all(v <= TOL for v in errs.values()), errs
+
+
+@pytest.mark.parametrize("name", ["ssm2_layer_h80_p64_n128", "ssm1_layer_d5120_n16"])
 def test_ssm_layer_heads_elementwise(dev, name):
     """The layer's head and state shape (all heads, so dB and dC fold every head of the group)
     over 256 tokens of one sequence: every output, dB and dC included, elementwise per
