@@ -826,6 +826,14 @@ static int ssm_validate(const gdn_ssm_problem *p) {
     if ((int64_t)p->P * (p->H / p->G) % 16 != 0) return GDN_ERR_UNSUPPORTED;
     // one workgroup per 16 rows: the grid must fit a launch dimension
     if ((int64_t)p->n_seqs * p->H * p->P / 16 > INT32_MAX) return GDN_ERR_UNSUPPORTED;
+    // the chunked backward: at most one workgroup per (sequence, head, 32-token chunk); the
+    // row-wise one: one per (256 rows, 8-token window)
+    if (gdn::ssm_chunked(p->P, p->N, p->a_per_state) &&
+        (int64_t)p->n_seqs * p->H * (((int64_t)p->T + 31) / 32) > INT32_MAX)
+        return GDN_ERR_UNSUPPORTED;
+    if (gdn::ssm_rowwise(p->P, p->H, p->G, p->N) &&
+        (int64_t)p->n_seqs * p->H * p->P / 256 * (((int64_t)p->T + 7) / 8) > INT32_MAX)
+        return GDN_ERR_UNSUPPORTED;
     return GDN_OK;
 }
 
