@@ -949,6 +949,7 @@ int gdn_ssm_fwd(const gdn_ssm_problem *p, const float *s0, const float *x, const
     if (rc != GDN_OK) return rc;
     gdn::SsmArgs a = ssm_args(p, pl, ws, s0, x, dt, A, B, C);
     a.y = y; a.s_out = s_out;
+    if (pl.chunked) return device_status(gdn::launch_ssm_chunk_fwd(a, (hipStream_t)stream));
     return device_status(gdn::launch_ssm(a, false, (hipStream_t)stream));
 }
 
@@ -977,7 +978,7 @@ int gdn_ssm_bwd(const gdn_ssm_problem *p, const float *s0, const float *x, const
     a.dB = grad_packed + off[3]; a.dC = grad_packed + off[4];
     hipError_t e = hipSuccess;
     if (!(flags & GDN_BWD_REUSE_SNAPSHOTS))     // window states first (no y, s_out)
-        e = gdn::launch_ssm(a, false, (hipStream_t)stream);
+        e = pl.chunked ? gdn::launch_ssm_chunk_fwd(a, (hipStream_t)stream) : gdn::launch_ssm(a, false, (hipStream_t)stream);
     if (pl.chunked) {
         if (e == hipSuccess) e = gdn::launch_ssm_chunk_bwd(a, (hipStream_t)stream);
     } else if (pl.rowwise) {

@@ -112,6 +112,8 @@ bool ssm_chunked(int P, int N, int aps);
 bool ssm_rowwise(int P, int H, int G, int N);
 hipError_t launch_ssm_rowwise_bwd(const SsmArgs &a, hipStream_t st);
 hipError_t launch_ssm_chunk_bwd(const SsmArgs &a, hipStream_t st);
+// Its forward: the state before every chunk (and s_out), then y per chunk (y null: states only).
+hipError_t launch_ssm_chunk_fwd(const SsmArgs &a, hipStream_t st);
 // head sizes: key width SK and value width SV, each in {16, 32, 64, 128}, not both 128
 hipError_t launch_fwd(const FwdArgs &a, int SK, int SV, bool kda, int n_seqs_launch, hipStream_t st);
 hipError_t launch_bwd(const BwdArgs &a, int SK, int SV, bool kda, int n_seqs_launch, hipStream_t st);

@@ -485,9 +485,247 @@ __global__ void __launch_bounds__(256) ssm_chunk_combine_kernel(const SsmArgs a)
     }
 }
 
+// ---- forward: the state before every chunk, then the chunks' outputs --------------------
+// Pass 1: one wave per (sequence, head, 16 rows of P, 64 states) walks the chunks in order with
+// its slice of the state in four accumulator tiles, saves the state before every chunk (for the
+// output pass and the backward) and updates s <- e^{L_31} s + (diag(d w) x)^T B over the chunk
+// (w_u = e^{L_31 - L_u}); after the last chunk it is the final state.  Tokens past the end have
+// step 0, so they add nothing.  The lane layout is that of the chunk-end gradient pass.
+template <int P, int N>
+__global__ void __launch_bounds__(64) ssm_fst_kernel(const SsmArgs a) {
+    const int lane = threadIdx.x, ar = lane & 15, kg = lane >> 4;
+    int64_t b = blockIdx.x;
+    const int nh = (int)(b % (N / 64));
+    b /= N / 64;
+    const int pt = (int)(b % (P / 16));
+    b /= P / 16;
+    const int64_t T = a.T, H = a.H, G = a.G;
+    const int64_t h = b % H, s = b / H, g = h / (H / G), unit = s * H + h;
+    const int nc = (a.T + Q - 1) / Q;
+    const float Ah = a.A[h];
+    const int prow = 16 * pt + 4 * kg;
+    const int ncol = 64 * nh + 4 * ar;
+    f4 acc[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const f4 v = ld4(a.s0 + (unit * P + prow + r) * N + ncol);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[j][r] = v[j];
+    }
+    struct Ld {
+        f4 b[8];
+        float x[8], dt;
+    };
+    auto load = [&](int c, Ld &L) {
+        const int t0 = c * Q;
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int64_t tc = std::min(t0 + 16 * q + 4 * kg + i, a.T - 1);   // step 0 past the end
+                L.x[4 * q + i] = a.x[((s * T + tc) * H + h) * P + 16 * pt + ar];
+                L.b[4 * q + i] = ld4(a.B + ((s * T + tc) * G + g) * N + ncol);
+            }
+        L.dt = a.dt[(s * T + std::min(t0 + (lane & 31), a.T - 1)) * H + h];
+    };
+    float *ckp = a.ck + unit * P * (int64_t)a.nck * N;
+    auto step = [&](int c, const Ld &L) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            st4(ckp + ((int64_t)(prow + r) * a.nck + c * QW / a.ckw) * N + ncol,
+                f4{acc[0][r], acc[1][r], acc[2][r], acc[3][r]});
+        const bool ok = lane < Q && c * Q + lane < a.T;
+        const float d = ok ? ssm_step(L.dt, a.softplus) : 0.f;
+        const float lam = scan32(d * Ah, lane);
+        const float last = __shfl(lam, Q - 1, 64);
+        const float dw = d * __expf(last - lam);
+        const float elast = __expf(last);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[j] *= elast;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const float av = L.x[k] * __shfl(dw, 16 * (k >> 2) + 4 * kg + (k & 3), 64);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[j] = mfma(av, L.b[k][j], acc[j]);
+        }
+    };
+    Ld L0, L1, L2;
+    if (nc > 0) load(0, L0);
+    if (nc > 1) load(1, L1);
+    for (int c = 0; c < nc; c += 3) {
+        if (c + 2 < nc) load(c + 2, L2);
+        step(c, L0);
+        if (c + 1 >= nc) break;
+        if (c + 3 < nc) load(c + 3, L0);
+        step(c + 1, L1);
+        if (c + 2 >= nc) break;
+        if (c + 4 < nc) load(c + 4, L1);
+        step(c + 2, L2);
+    }
+    if (a.s_out) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            st4(a.s_out + (unit * P + prow + r) * N + ncol, f4{acc[0][r], acc[1][r], acc[2][r], acc[3][r]});
+    }
+}
+
+// Pass 2: one 512-thread workgroup per (sequence, chunk, group, head slice); per head
+//   y = (D.CB) diag(d) x + diag(e^L) C s_in^T,
+// wave w owning the 16 x 16 tile (tokens 16 (w & 1), elements 16 (w >> 1)) of y; CB is formed
+// once per chunk on waves 0-2 (its B rows' LDS then holds the head's d x and D.CB).
+struct FwdLds {
+    float Cc[Q][132];
+    float sin[64][132];
+    union {
+        float Bc[Q][132];
+        struct {
+            float xs[Q][68];       // d_u x_u
+            float M1[Q][36];       // (D.CB)[t][u]
+        } hd;
+    } u;
+    float L[Q], eL[Q];
+};
+
+template <int P, int N>
+__global__ void __launch_bounds__(512) ssm_chunk_fwd_kernel(const SsmArgs a) {
+    static_assert(P == 64 && N == 128, "tile assignment of this kernel");
+    __shared__ FwdLds sm;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, ar = lane & 15, kg = lane >> 4;
+    const int64_t T = a.T, H = a.H, G = a.G;
+    const int nc = (a.T + Q - 1) / Q;
+    int64_t b = blockIdx.x;
+    const int hsl = (int)(b % a.hgs);
+    b /= a.hgs;
+    const int64_t g = b % G;
+    b /= G;
+    const int c = (int)(b % nc);
+    const int64_t s = b / nc;
+    const int t0 = c * Q;
+    const int Hg = a.H / a.G, hper = (Hg + a.hgs - 1) / a.hgs;
+    const int h_lo = (int)g * Hg + std::min(Hg, hsl * hper);
+    const int h_hi = (int)g * Hg + std::min(Hg, (hsl + 1) * hper);
+    if (h_lo >= h_hi) return;
+    const int ti = wv & 1, pj = wv >> 1;
+    const bool vec = ((uintptr_t)a.x & 15) == 0;
+
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+        const int e = tid + 512 * m, row = e >> 5, c4 = e & 31;
+        const bool ok = t0 + row < a.T;
+        const int64_t off = ((s * T + std::min(t0 + row, a.T - 1)) * G + g) * N + 4 * c4;
+        const f4 bv = ld4(a.B + off), cv = ld4(a.C + off);
+        st4(&sm.u.Bc[row][4 * c4], ok ? bv : zero4());
+        st4(&sm.Cc[row][4 * c4], ok ? cv : zero4());
+    }
+    __syncthreads();
+    const int gi = wv > 0 ? 1 : 0, gj = wv > 1 ? 1 : 0;   // CB tile of waves 0-2
+    f4 cb = zero4();
+    if (wv < 3) {
+#pragma unroll
+        for (int q = 0; q < N / 16; ++q) {
+            const f4 af = ld4(&sm.Cc[16 * gi + ar][16 * q + 4 * kg]);
+            const f4 bf = ld4(&sm.u.Bc[16 * gj + ar][16 * q + 4 * kg]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) cb = mfma(af[i], bf[i], cb);
+        }
+    }
+    __syncthreads();   // the B rows' LDS is the heads' from here on
+
+    struct Pf {
+        f4 x, si[4];
+        float dt, dtl;
+    };
+    auto fetch = [&](int64_t h, Pf &F) {
+        const int row = tid >> 4, c4 = tid & 15;
+        const int64_t tc = std::min(t0 + row, a.T - 1);
+        F.x = ld4u(a.x + ((s * T + tc) * H + h) * P + 4 * c4, vec);
+        F.dt = a.dt[(s * T + tc) * H + h];
+        F.dtl = a.dt[(s * T + std::min(t0 + (lane & 31), a.T - 1)) * H + h];
+        const float *sip = a.ck + (s * H + h) * P * (int64_t)a.nck * N + (int64_t)(c * QW / a.ckw) * N;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const int e = tid + 512 * m, p = e >> 5, c4b = e & 31;
+            F.si[m] = ld4(sip + (int64_t)p * a.nck * N + 4 * c4b);
+        }
+    };
+    Pf F;
+    fetch(h_lo, F);
+    for (int h = h_lo; h < h_hi; ++h) {
+        const float Ah = a.A[h];
+        {
+            const int row = tid >> 4, c4 = tid & 15;
+            const bool ok = t0 + row < a.T;
+            const float d = ok ? ssm_step(F.dt, a.softplus) : 0.f;
+            st4(&sm.u.hd.xs[row][4 * c4], F.x * d);
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const int e = tid + 512 * m, p = e >> 5, c4b = e & 31;
+                st4(&sm.sin[p][4 * c4b], F.si[m]);
+            }
+            if (wv == 0) {
+                const bool okl = lane < Q && t0 + lane < a.T;
+                const float dl = okl ? ssm_step(F.dtl, a.softplus) : 0.f;
+                const float L = scan32(dl * Ah, lane);
+                if (lane < Q) {
+                    sm.L[lane] = L;
+                    sm.eL[lane] = __expf(L);
+                }
+            }
+        }
+        __syncthreads();
+        if (h + 1 < h_hi) fetch(h + 1, F);
+        if (wv < 3) {   // D.CB on the three nonzero tiles
+            const int u = 16 * gj + ar;
+            const float lu = sm.L[u];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = 16 * gi + 4 * kg + r;
+                sm.u.hd.M1[t][u] = u <= t ? __expf(sm.L[t] - lu) * cb[r] : 0.f;
+            }
+        }
+        __syncthreads();
+        f4 yi = zero4(), ye = zero4();
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {   // (D.CB) (d x): u below the tile's last token
+            if (q > ti) continue;
+            const f4 af = ld4(&sm.u.hd.M1[16 * ti + ar][16 * q + 4 * kg]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) yi = mfma(af[i], sm.u.hd.xs[16 * q + 4 * kg + i][16 * pj + ar], yi);
+        }
+#pragma unroll
+        for (int q = 0; q < N / 16; ++q) {   // C s_in^T
+            const f4 af = ld4(&sm.Cc[16 * ti + ar][16 * q + 4 * kg]);
+            const f4 bf = ld4(&sm.sin[16 * pj + ar][16 * q + 4 * kg]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) ye = mfma(af[i], bf[i], ye);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int t = 16 * ti + 4 * kg + r;
+            if (t0 + t < a.T) a.y[((s * T + t0 + t) * H + h) * P + 16 * pj + ar] = fmaf(sm.eL[t], ye[r], yi[r]);
+        }
+        __syncthreads();
+    }
+}
+
 }  // namespace
 
 bool ssm_chunked(int P, int N, int aps) { return aps == 0 && P == 64 && N == 128; }
+
+hipError_t launch_ssm_chunk_fwd(const SsmArgs &a, hipStream_t st) {
+    const int64_t units = (int64_t)a.n_seqs * a.H;
+    if (units <= 0) return hipSuccess;
+    if (!ssm_chunked(a.P, a.N, a.aps) || a.hgs < 1 || a.H % a.G != 0 || QW % a.ckw != 0)
+        return hipErrorInvalidValue;
+    void *params[] = {const_cast<SsmArgs *>(&a)};
+    hipError_t e = hipLaunchKernel((const void *)ssm_fst_kernel<64, 128>, dim3((unsigned)(units * (64 / 16) * (128 / 64))),
+                                   dim3(64), params, 0, st);
+    const int64_t nc = (a.T + Q - 1) / Q;
+    const int64_t nwg = (int64_t)a.n_seqs * nc * a.G * a.hgs;
+    if (e == hipSuccess && a.y && nwg > 0)
+        e = hipLaunchKernel((const void *)ssm_chunk_fwd_kernel<64, 128>, dim3((unsigned)nwg), dim3(512), params, 0, st);
+    return e;
+}
 
 hipError_t launch_ssm_chunk_bwd(const SsmArgs &a, hipStream_t st) {
     const int64_t units = (int64_t)a.n_seqs * a.H;
