@@ -1,6 +1,6 @@
-// ssm_chunk.hip -- gfx950 backward of the selective scan with one decay per head (the Mamba-2
-// branch; page "S1-24: chunked attention", the SSM_SCAN_BACK commit notes and the n_group fold)
-// in 32-token chunks on the fp32 matrix cores (v_mfma_f32_16x16x4f32).
+// ssm_chunk.hip -- gfx950 forward and backward of the selective scan with one decay per head
+// (the Mamba-2 branch; page "S1-24: chunked attention", the SSM_SCAN_BACK commit notes and the
+// n_group fold) in 32-token chunks on the fp32 matrix cores (v_mfma_f32_16x16x4f32).
 //
 // Per (sequence, head) and chunk of tokens t = 0..31 with steps d_t, log-decays l_t = d_t A and
 // partial sums L_t = l_0 + ... + l_t, the state after token t is
@@ -20,6 +20,9 @@
 // where Y_t = e^{L_t} C_t . (gy s_in)_t, Z = (D.GX) diag(d) . CB and R_v = d_v w_v x_v . (dS B_v):
 // the terms of <G_u, s_u> in which token u's own decay takes part.  The chunk-end gradients come
 // from a first pass that walks each head's chunks backwards, dS <- e^{L_31} dS + gy^T diag(e^L) C.
+// The forward reads the closed form the other way: a pass walks the chunks forwards,
+// s <- e^{L_31} s + (diag(d w) x)^T B, saving the state before each chunk, and then per chunk
+// y = (D.CB) diag(d) x + diag(e^L) C s_in^T.
 //
 // Matrix-core operands: for a product over K = 16 q + 4 g + i (q: a 16-wide slice, g = lane / 16,
 // i < 4), lane l supplies A[l % 16][K] and B[K][l % 16] in the i-th of four products, so an
