@@ -13,7 +13,11 @@
 // sums; the column sums of a token (dC = sum_i gy s, dB = sum_i gs d x over the 16 rows) are
 // reduce-scattered over the four row groups of a wave with permlane swaps, summed over the four
 // waves in LDS at the window's end and written as the segment's partial; a combine kernel adds
-// the segments of each group (and the rows of each head for ddt) in a fixed order.
+// the segments of each group (and the rows of each head for ddt) in a fixed order.  With 16
+// states and whole 256-row blocks per group the backward instead runs in two passes (the state
+// gradient entering every window, then the windows in parallel with one lane per row: see
+// ssm_gsw_kernel and ssm_win16_kernel); one decay per head with head size 64 and 128 states
+// runs in chunks on the matrix cores (ssm_chunk.hip).
 #include <hip/hip_runtime.h>
 
 #include "gdn_internal.h"
