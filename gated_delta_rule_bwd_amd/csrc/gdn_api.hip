@@ -827,12 +827,12 @@ static int ssm_validate(const gdn_ssm_problem *p) {
     // one workgroup per 16 rows: the grid must fit a launch dimension
     if ((int64_t)p->n_seqs * p->H * p->P / 16 > INT32_MAX) return GDN_ERR_UNSUPPORTED;
     // the chunked backward: at most one workgroup per (sequence, head, 32-token chunk); the
-    // row-wise one: one per (256 rows, 8-token window)
+    // row-wise one: one per (128 rows, 8-token window)
     if (gdn::ssm_chunked(p->P, p->N, p->a_per_state) &&
         (int64_t)p->n_seqs * p->H * (((int64_t)p->T + 31) / 32) > INT32_MAX)
         return GDN_ERR_UNSUPPORTED;
     if (gdn::ssm_rowwise(p->P, p->H, p->G, p->N) &&
-        (int64_t)p->n_seqs * p->H * p->P / 256 * (((int64_t)p->T + 7) / 8) > INT32_MAX)
+        (int64_t)p->n_seqs * p->H * p->P / 128 * (((int64_t)p->T + 7) / 8) > INT32_MAX)
         return GDN_ERR_UNSUPPORTED;
     return GDN_OK;
 }
@@ -847,7 +847,7 @@ static SsmPlan ssm_plan(const gdn_ssm_problem *p) {
     size_t off = 0;
     pl.off_part = pl.off_dd = pl.off_dsq = pl.off_cpart = pl.off_gsw = 0;
     pl.hgs = 1;
-    pl.seg_rows = pl.rowwise ? 256 : 16;
+    pl.seg_rows = pl.rowwise ? 128 : 16;   // rows per column-sum partial
     if (pl.chunked) {
         // the state before every 32-token chunk; the state gradient after each chunk; dB, dC
         // per head slice, enough slices for about 2048 workgroups

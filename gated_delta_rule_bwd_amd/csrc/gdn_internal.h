@@ -106,9 +106,9 @@ hipError_t launch_ssm_combine(const SsmArgs &a, hipStream_t st);
 // Chunked backward (one decay per head, P = 64, N = 128): the chunk-end state gradients, the
 // chunks' gradients on the matrix cores, then the head slices' dB and dC summed in order.
 bool ssm_chunked(int P, int N, int aps);
-// Row-wise backward for 16 states (rows of a group a multiple of 256): the state gradient
-// entering every 8-token window, then the windows in parallel with one lane per row, then the
-// combine over 256-row segments.
+// Row-wise backward for 16 states (rows of a group a multiple of 128): the state gradient
+// entering every 8-token window, then the windows in parallel with two lanes per row, then the
+// combine over 128-row segments.
 bool ssm_rowwise(int P, int H, int G, int N);
 hipError_t launch_ssm_rowwise_bwd(const SsmArgs &a, hipStream_t st);
 hipError_t launch_ssm_chunk_bwd(const SsmArgs &a, hipStream_t st);

@@ -14,8 +14,8 @@
 // reduce-scattered over the four row groups of a wave with permlane swaps, summed over the four
 // waves in LDS at the window's end and written as the segment's partial; a combine kernel adds
 // the segments of each group (and the rows of each head for ddt) in a fixed order.  With 16
-// states and whole 256-row blocks per group the backward instead runs in two passes (the state
-// gradient entering every window, then the windows in parallel with one lane per row: see
+// states and whole 128-row blocks per group the backward instead runs in two passes (the state
+// gradient entering every window, then the windows in parallel with two lanes per row: see
 // ssm_gsw_kernel and ssm_win16_kernel); one decay per head with head size 64 and 128 states
 // runs in chunks on the matrix cores (ssm_chunk.hip).
 #include <hip/hip_runtime.h>
@@ -406,12 +406,14 @@ __global__ void __launch_bounds__(256) ssm_bwd_kernel(const SsmArgs a) {
 // instructions are the per-token sums across lanes.  Here the walk is split in two passes:
 // pass 1 runs the state gradient's own recurrence (gs += gy C, gs *= a from the last token) in
 // the forward's layout and stores the gradient entering every window from the right (and
-// d_s0); pass 2 then takes every window independently, one lane per row with its 16 states in
-// registers, so a row's sums (dx, the ddt term) are in-lane, and only the column sums of a token
-// (dC, dB over rows) cross lanes: a reduce-scatter over the wave after which each lane holds one
-// (quantity, state) sum over the wave's 64 rows, then a sum over the four waves in LDS.  The
-// gradient chain runs the walk's own operations in the walk's order, so pass 2 starts each
-// window from the gradient the single-pass walk would have there.
+// d_s0); pass 2 then takes every window independently, two lanes per row with eight states
+// each in registers, so a row's sums (dx, the ddt term) are one pair sum, and only the column
+// sums of a token (dC, dB over rows) cross more lanes: a reduce-scatter over the wave after which
+// each lane holds one (quantity, state) sum over the wave's 32 rows, then a sum over the four
+// waves in LDS.  (One lane per row, all 16 states in registers, needed 238 registers, two waves
+// per SIMD, and was 8 % slower.)  The gradient chain runs the walk's own operations in the
+// walk's order, so pass 2 starts each window from the gradient the single-pass walk would have
+// there.
 constexpr int GB = 32;   // tokens per staging block of pass 1
 
 template <bool APS>
@@ -475,26 +477,32 @@ __global__ void __launch_bounds__(256) ssm_gsw_kernel(const SsmArgs a) {
     a.ds0[w.r * N + sub] = gs;
 }
 
-constexpr int RB = 256;   // rows per block of pass 2 (and per column-sum segment)
+constexpr int RB = 128;   // rows per block of pass 2 (and per column-sum segment): two lanes per
+                          // row, eight states each
 
-__device__ __forceinline__ void ld16(const float *p, float (&v)[16]) {
+__device__ __forceinline__ void ld8(const float *p, float (&v)[8]) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < 2; ++q) {
         const float4 t = reinterpret_cast<const float4 *>(p)[q];
         v[4 * q] = t.x; v[4 * q + 1] = t.y; v[4 * q + 2] = t.z; v[4 * q + 3] = t.w;
     }
 }
 
+// One workgroup per (128 rows, 8-token window); lane l owns states 8 (l & 1) .. + 7 of row l / 2.
+// Replay the window from its saved state, walk it back from the window's gradient; the token's
+// dC and dB are reduce-scattered over the wave's 32 rows (permlane32: dC or dB, permlane16: 4
+// states, row_ror:8: 2, lane^4: 1, then lane^2 added), so lane l ends with state
+// 8 (l & 1) + 4 bit4 + 2 bit3 + bit2 of dC (l < 32) or dB.
 template <bool APS>
 __global__ void __launch_bounds__(256) ssm_win16_kernel(const SsmArgs a) {
-    constexpr int N = 16;
+    constexpr int N = 16, NH = 8;
     __shared__ float bc[2][WIN][N];          // B, C rows of the window's tokens
     __shared__ float red[WIN][4][2 * N];     // [token][wave][dC | dB state]
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hb = lane & 1;
     const int nwin = (a.T + WIN - 1) / WIN;
     const int win = (int)(blockIdx.x % nwin);
     const int64_t rb = blockIdx.x / nwin;
-    const Row w = row_of(a, rb * RB + tid);   // the block's rows share (sequence, group)
+    const Row w = row_of(a, rb * RB + (tid >> 1));   // the block's rows share (sequence, group)
     const int64_t T = a.T, H = a.H, P = a.P, G = a.G;
     const int t0 = win * WIN, cnt = min(WIN, a.T - t0);
     {
@@ -503,98 +511,107 @@ __global__ void __launch_bounds__(256) ssm_win16_kernel(const SsmArgs a) {
         const int64_t t = min(t0 + k, a.T - 1);
         bc[q][k][n] = (q ? a.C : a.B)[((w0.s * T + t) * G + w0.g) * N + n];
     }
-    float sp[N], gs[N], Av[N];
-    ld16(a.ck + (w.r * a.nck + win) * N, sp);
-    ld16(a.gsw + (w.r * nwin + win) * N, gs);
+    float sp[NH], gs[NH], Av[NH];
+    ld8(a.ck + (w.r * a.nck + win) * N + NH * hb, sp);
+    ld8(a.gsw + (w.r * nwin + win) * N + NH * hb, gs);
     float Ah = 0.f;
-    if constexpr (APS) ld16(a.A + w.h * N, Av);
+    if constexpr (APS) ld8(a.A + w.h * N + NH * hb, Av);
     else Ah = a.A[w.h];
     float xv[WIN], gv[WIN], dv[WIN], sg[WIN];
+    {
+        // the pair's lanes each take the step (and softplus') of four tokens and swap them
+        float m4[4], s4[4];
 #pragma unroll
-    for (int k = 0; k < WIN; ++k) {
-        const int64_t t = min(t0 + k, a.T - 1);   // tokens past the end are skipped below
-        const int64_t at = ((w.s * T + t) * H + w.h) * P + w.i;
-        // a token past the end gets x = gy = 0 and step 0: the replay leaves the state as it
-        // is, so it needs no branch per token
-        const bool ok = t0 + k < a.T;
-        const float xr = a.x[at], gr = a.gy[at], z = a.dt[(w.s * T + t) * H + w.h];
-        xv[k] = ok ? xr : 0.f;
-        gv[k] = ok ? gr : 0.f;
-        dv[k] = ok ? ssm_step(z, a.softplus) : 0.f;
-        sg[k] = (P == 1 && a.softplus) ? 1.f / (1.f + expf(-z)) : 1.f;   // a head of one row: ddt
+        for (int k = 0; k < WIN; ++k) {
+            const int64_t t = min(t0 + k, a.T - 1);   // tokens past the end are skipped below
+            const int64_t at = ((w.s * T + t) * H + w.h) * P + w.i;
+            const bool ok = t0 + k < a.T;
+            const float xr = a.x[at], gr = a.gy[at];
+            xv[k] = ok ? xr : 0.f;
+            gv[k] = ok ? gr : 0.f;
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int k = 4 * hb + j;
+            const float z = a.dt[(w.s * T + min(t0 + k, a.T - 1)) * H + w.h];
+            m4[j] = t0 + k < a.T ? ssm_step(z, a.softplus) : 0.f;
+            s4[j] = (P == 1 && a.softplus) ? 1.f / (1.f + expf(-z)) : 1.f;
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float mo = dpp<0xB1>(m4[j]), so = dpp<0xB1>(s4[j]);   // the other lane's tokens
+            dv[j] = hb ? mo : m4[j];
+            dv[4 + j] = hb ? m4[j] : mo;
+            sg[j] = hb ? so : s4[j];
+            sg[4 + j] = hb ? s4[j] : so;
+        }
     }
     __syncthreads();
-    // replay: S[k] is the state after token t0 + k
-    float S[WIN][N];
+    float S[WIN][NH];
 #pragma unroll
     for (int k = 0; k < WIN; ++k) {
         const float b = dv[k] * xv[k];
         const float ah = APS ? 0.f : dexp(dv[k] * Ah);
 #pragma unroll
-        for (int n = 0; n < N; ++n) {
-            const float aj = APS ? dexp(dv[k] * Av[n]) : ah;
-            S[k][n] = fmaf(aj, k ? S[k - 1][n] : sp[n], b * bc[0][k][n]);
+        for (int m = 0; m < NH; ++m) {
+            const float aj = APS ? dexp(dv[k] * Av[m]) : ah;
+            S[k][m] = fmaf(aj, k ? S[k - 1][m] : sp[m], b * bc[0][k][NH * hb + m]);
         }
     }
-    const bool b3 = lane & 8, b2 = lane & 4, b1 = lane & 2;
-    // the walk recomputes the decays rather than keeping the replay's 8 x 16 (registers): an
-    // empty asm statement hides the steps' identity from the compiler, which would keep them
+    const bool b3 = lane & 8, b2 = lane & 4;
 #pragma unroll
     for (int k = 0; k < WIN; ++k) asm volatile("" : "+v"(dv[k]));
 #pragma unroll
     for (int k = WIN - 1; k >= 0; --k) {
-        // a uniform branch per token: it also keeps the compiler from overlapping the tokens'
-        // walks, whose live values would not fit the registers
         if (k < cnt) {
             const float d = dv[k], xk = xv[k], gyk = gv[k], dxv = d * xk;
             const float ah = APS ? 0.f : dexp(d * Ah);
-            float v[2 * N];   // this row's column terms: dC then dB
+            float v[2 * NH];
             float gB = 0.f, dec = 0.f;
 #pragma unroll
-            for (int n = 0; n < N; ++n) {
-                const float aj = APS ? dexp(d * Av[n]) : ah;
-                const float prev = k ? S[k - 1][n] : sp[n];
-                gs[n] = fmaf(gyk, bc[1][k][n], gs[n]);
-                v[n] = gyk * S[k][n];
-                v[N + n] = gs[n] * dxv;
-                gB = fmaf(gs[n], bc[0][k][n], gB);
-                dec = APS ? fmaf(gs[n] * (Av[n] * aj), prev, dec) : fmaf(gs[n], prev, dec);
-                gs[n] = aj * gs[n];
+            for (int m = 0; m < NH; ++m) {
+                const float aj = APS ? dexp(d * Av[m]) : ah;
+                const float prev = k ? S[k - 1][m] : sp[m];
+                gs[m] = fmaf(gyk, bc[1][k][NH * hb + m], gs[m]);
+                v[m] = gyk * S[k][m];
+                v[NH + m] = gs[m] * dxv;
+                gB = fmaf(gs[m], bc[0][k][NH * hb + m], gB);
+                dec = APS ? fmaf(gs[m] * (Av[m] * aj), prev, dec) : fmaf(gs[m], prev, dec);
+                gs[m] = aj * gs[m];
             }
-            const int64_t at = ((w.s * T + t0 + k) * H + w.h) * P + w.i;
-            a.dx[at] = d * gB;
-            (P == 1 ? a.ddt : a.ddrow)[at] = ((APS ? dec : Ah * ah * dec) + xk * gB) * sg[k];
-            // reduce-scatter over the wave: lanes 0-31 keep dC, 32-63 dB (permlane32); then
-            // states 8 bit4 (permlane16), 4 bit3 (row_ror:8), 2 bit2 (row_half_mirror), bit1
-            // (quad lane^2); lane^1 holds the same sum: lane l ends with state (l >> 1) & 15
-            float u[16], w8[8], x4[4], y2[2];
+            gB += dpp<0xB1>(gB);    // the pair's halves
+            dec += dpp<0xB1>(dec);
+            if (hb == 0) {
+                const int64_t at = ((w.s * T + t0 + k) * H + w.h) * P + w.i;
+                a.dx[at] = d * gB;
+                (P == 1 ? a.ddt : a.ddrow)[at] = ((APS ? dec : Ah * ah * dec) + xk * gB) * sg[k];
+            }
+            float u[8], w4[4], x2[2];
 #pragma unroll
-            for (int m = 0; m < 16; ++m) {
-                auto pr = __builtin_amdgcn_permlane32_swap(as_i(v[m]), as_i(v[16 + m]), false, false);
+            for (int m = 0; m < 8; ++m) {
+                auto pr = __builtin_amdgcn_permlane32_swap(as_i(v[m]), as_i(v[8 + m]), false, false);
                 u[m] = as_f(pr[0]) + as_f(pr[1]);
             }
 #pragma unroll
-            for (int m = 0; m < 8; ++m) {
-                auto pr = __builtin_amdgcn_permlane16_swap(as_i(u[m]), as_i(u[8 + m]), false, false);
-                w8[m] = as_f(pr[0]) + as_f(pr[1]);
-            }
-#pragma unroll
             for (int m = 0; m < 4; ++m) {
-                const float keep = b3 ? w8[4 + m] : w8[m], send = b3 ? w8[m] : w8[4 + m];
-                x4[m] = keep + dpp<0x128>(send);
+                auto pr = __builtin_amdgcn_permlane16_swap(as_i(u[m]), as_i(u[4 + m]), false, false);
+                w4[m] = as_f(pr[0]) + as_f(pr[1]);
             }
 #pragma unroll
             for (int m = 0; m < 2; ++m) {
-                const float keep = b2 ? x4[2 + m] : x4[m], send = b2 ? x4[m] : x4[2 + m];
-                y2[m] = keep + dpp<0x141>(send);
+                const float keep = b3 ? w4[2 + m] : w4[m], send = b3 ? w4[m] : w4[2 + m];
+                x2[m] = keep + dpp<0x128>(send);
             }
-            float z = (b1 ? y2[1] : y2[0]) + dpp<0x4E>(b1 ? y2[0] : y2[1]);
-            z += dpp<0xB1>(z);
-            if ((lane & 1) == 0) red[k][wave][lane >> 1] = z;
+            const float keep = b2 ? x2[1] : x2[0], send = b2 ? x2[0] : x2[1];
+            float z = keep + __shfl_xor(send, 4, 64);
+            z += dpp<0x4E>(z);
+            // lane l: dC (l < 32) or dB of state 8 (l & 1) + 4 bit4 + 2 bit3 + bit2
+            if ((lane & 2) == 0)
+                red[k][wave][(lane >> 5) * N + NH * hb + 4 * ((lane >> 4) & 1) + 2 * ((lane >> 3) & 1) + ((lane >> 2) & 1)] = z;
         }
     }
     __syncthreads();
-    {   // the block's partial: [segment][token][dC | dB][state], waves summed in order
+    {
         const int k = tid >> 5, idx = tid & 31;
         if (k < cnt)
             a.part[(rb * T + t0 + k) * 2 * N + idx] =

@@ -267,7 +267,7 @@ typedef struct gdn_ssm_problem {
 
 /* Bytes of device workspace gdn_ssm_fwd and gdn_ssm_bwd need (0 on an invalid problem): the
  * state before every 8-token window, per-16-row column partials and per-row ddt terms (with
- * N = 16 and a multiple of 256 rows per group: per-256-row partials and the state gradient
+ * N = 16 and a multiple of 128 rows per group: per-128-row partials and the state gradient
  * entering every window); for one decay per head with P = 64 and N = 128, whose backward runs
  * in 32-token chunks on the matrix cores, the state before every chunk, the state gradient
  * after every chunk and dB/dC per head slice instead.  The same workspace serves both calls. */

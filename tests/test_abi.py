@@ -379,7 +379,7 @@ def test_ssm_chunked_workspace(B):
     (dict(a_per_state=2), -1), (dict(dt_softplus=-1), -1), (dict(T=-1), -1), (dict(P=0), -1),
     (dict(n_seqs=1 << 20, H=1 << 10, P=1 << 7, G=1), -2),    # 2^33 rows: beyond one launch
     (dict(n_seqs=1 << 12, T=1 << 20, H=1 << 4, P=64, N=128, G=1), -2),   # 2^31 chunks x heads
-    (dict(n_seqs=1 << 14, T=1 << 20, H=1 << 8, P=1, N=16, G=1), -2),     # 2^31 windows x row blocks
+    (dict(n_seqs=1 << 14, T=1 << 20, H=1 << 8, P=1, N=16, G=1), -2),     # 2^32 windows x row blocks
 ])
 def test_ssm_invalid_problems(B, kw, code):
     p = _ssm(B, **kw)

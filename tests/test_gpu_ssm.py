@@ -79,8 +79,9 @@ CASES = [
     (1, 40, 40, 64, 128, 1, False, True, True),   # 16 head slices of 3 heads, two of them empty
     (1, 1, 2, 64, 128, 2, False, True, True),     # one token
     (2, 0, 2, 64, 128, 1, False, True, True),     # no tokens
-    # 16 states with 256 rows per group: the backward in two passes, one lane per row
+    # 16 states with a multiple of 128 rows per group: the backward in two passes, two lanes per row
     (2, 45, 256, 1, 16, 1, True, True, True),     # Mamba-1 channels, ragged last window
+    (1, 30, 256, 1, 16, 2, True, True, True),     # 128 channels per group, two groups
     (1, 20, 64, 8, 16, 2, True, False, False),    # head size 8 (ddt sums 8 rows), two groups
     (2, 8, 128, 4, 16, 1, False, True, True),     # one decay per head, two row blocks
     (1, 1, 256, 1, 16, 1, True, True, True),      # one token
