@@ -67,7 +67,9 @@ CASES = [
     # n, T, H, P, N, G, a_per_state, softplus, with_gs
     (2, 37, 4, 16, 32, 2, False, True, True),     # Mamba-2 branch, two heads per group, ragged window
     (2, 45, 32, 1, 16, 2, True, True, True),      # Mamba-1 branch, 16 channels per group
-    (1, 20, 2, 64, 128, 1, False, True, True),    # the widest state
+    (1, 20, 2, 64, 128, 1, False, True, True),    # the widest state (the chunked backward)
+    (1, 20, 2, 32, 128, 1, False, True, True),    # the widest state, head size 32: per token
+    (1, 17, 2, 64, 128, 1, True, True, True),     # the widest state with per-state decay: per token
     (2, 24, 4, 8, 64, 1, False, False, False),    # raw steps, no final-state cotangent
     (1, 9, 16, 1, 64, 1, True, True, True),       # per-state decay over 64 states
     (2, 8, 4, 16, 32, 4, False, True, True),      # exactly one window; one head per group
