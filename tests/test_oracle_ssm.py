@@ -2,8 +2,10 @@
 central differences of a weighted objective that includes the final state (both branches,
 grouped heads, with and without softplus), the forward written in its materialised form (each
 output a sum over earlier tokens with explicit decay products from cumulative sums), closed
-forms, linearity, and the group fold against explicit repetition of B and C.  Five planted
-mistakes must each fail a pin."""
+forms, linearity, the group fold against explicit repetition of B and C, and, with one decay per
+head, the backward in the chunked closed form (the gradients of a chunk as dense products of
+its Grams, given the state before it and the gradient after it).  Five planted mistakes must
+each fail a pin."""
 import numpy as np
 import pytest
 
@@ -161,3 +163,78 @@ def test_planted_mistakes_are_caught(mutation):
     finally:
         S._MUTATION = 0
     assert caught, mutation
+
+
+def chunked_bwd(s0, x, dt, A, B, C, gy, gs, softplus_dt=True, Q=4):
+    """The backward with one decay per head in chunks of Q tokens, from the closed form of the
+    state inside a chunk, s_t = e^{L_t} s_in + sum_{u <= t} e^{L_t - L_u} d_u x_u B_u^T (L the
+    running sum of d A): per chunk the gradient of the state after it (dS, walked backwards over
+    the chunks), then every gradient as a product of the chunk's Grams CB = C B^T and
+    GX = gy x^T masked by D[t][u] = e^{L_t - L_u} (u <= t)."""
+    n, T, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    d = np.logaddexp(0.0, dt) if softplus_dt else np.array(dt, dtype=np.float64)
+    grp = np.arange(H) // (H // G)
+    nc = (T + Q - 1) // Q
+    _, _, states = S.ssm_fwd(s0, x, dt, A, B, C, softplus_dt, keep_states=True)
+    dx, ddt = np.zeros((n, T, H, P)), np.zeros((n, T, H))
+    dB, dC = np.zeros((n, T, G, N)), np.zeros((n, T, G, N))
+    ds0 = np.zeros((n, H, P, N))
+    sig = 1.0 / (1.0 + np.exp(-dt)) if softplus_dt else np.ones_like(dt)
+
+    def chunk(s, h, c):
+        t0 = c * Q
+        cnt = min(Q, T - t0)
+        g = grp[h]
+        pad = lambda v, w: np.concatenate([v, np.zeros((Q - cnt, w))]) if cnt < Q else v
+        dd = np.concatenate([d[s, t0:t0 + cnt, h], np.zeros(Q - cnt)])
+        L = np.cumsum(dd * A[h])
+        return (t0, cnt, dd, L, pad(x[s, t0:t0 + cnt, h], P), pad(gy[s, t0:t0 + cnt, h], P),
+                pad(B[s, t0:t0 + cnt, g], N), pad(C[s, t0:t0 + cnt, g], N))
+
+    for s in range(n):
+        for h in range(H):
+            dS = np.zeros((nc, P, N))
+            cur = np.zeros((P, N)) if gs is None else np.array(gs[s, h], dtype=np.float64)
+            for c in range(nc - 1, -1, -1):
+                _, _, _, L, _, gyc, _, Cc = chunk(s, h, c)
+                dS[c] = cur
+                cur = np.exp(L[-1]) * cur + (gyc * np.exp(L)[:, None]).T @ Cc
+            ds0[s, h] = cur
+            for c in range(nc):
+                t0, cnt, dd, L, xc, gyc, Bc, Cc = chunk(s, h, c)
+                s_in, dSQ = states[t0][s, h], dS[c]
+                D = np.tril(np.exp(L[:, None] - L[None, :]))
+                CB, GX = Cc @ Bc.T, gyc @ xc.T
+                w, eL = np.exp(L[-1] - L), np.exp(L)
+                Wd = D * GX * dd[None, :]
+                GBi, GBe = (D * CB).T @ gyc, (w[:, None] * Bc) @ dSQ.T
+                dCi = (eL[:, None] * gyc) @ s_in
+                Z = Wd * CB
+                row = np.array([Z[t, :t].sum() for t in range(Q)])
+                col = np.array([Z[t + 1:, t].sum() for t in range(Q)])
+                excl = lambda v: np.concatenate([[0.0], np.cumsum(v)[:-1]])
+                R = dd * np.einsum("up,up->u", xc, GBe)
+                Y = np.einsum("tn,tn->t", Cc, dCi)
+                dl = (np.cumsum(Y[::-1])[::-1] + np.exp(L[-1]) * np.sum(dSQ * s_in)
+                      + excl(col - row) + excl(R))
+                GB = GBi + GBe
+                dx[s, t0:t0 + cnt, h] = (dd[:, None] * GB)[:cnt]
+                ddt[s, t0:t0 + cnt, h] = ((A[h] * dl + np.einsum("up,up->u", xc, GB))[:cnt]
+                                           * sig[s, t0:t0 + cnt, h])
+                dB[s, t0:t0 + cnt, grp[h]] += (Wd.T @ Cc + ((dd * w)[:, None] * xc) @ dSQ)[:cnt]
+                dC[s, t0:t0 + cnt, grp[h]] += (Wd @ Bc + dCi)[:cnt]
+    return ds0, dx, ddt, dB, dC
+
+
+@pytest.mark.parametrize("T,softplus_dt,with_gs", [(11, True, True), (8, False, True), (3, True, False)])
+def test_backward_equals_chunked_closed_form(T, softplus_dt, with_gs):
+    """With one decay per head: ragged and whole chunks, raw steps, no final-state cotangent."""
+    s0, x, dt, A, B, C = case(31 + T, T=T, H=4, P=3, N=5, G=2, positive_dt=not softplus_dt)
+    rng = np.random.default_rng(T)
+    gy = rng.standard_normal(x.shape)
+    gs = rng.standard_normal(s0.shape) if with_gs else None
+    ref = S.ssm_bwd(s0, x, dt, A, B, C, gy, gs, softplus_dt)
+    got = chunked_bwd(s0, x, dt, A, B, C, gy, gs, softplus_dt)
+    for r, g in zip(ref, got):
+        assert np.allclose(g, r, rtol=1e-10, atol=1e-12)
