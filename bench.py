@@ -509,6 +509,9 @@ def main():
     fwd_ms = sum(a.elapsed_time(b) for a, b, _ in ev) / args.steps
     bwd_ms = sum(b.elapsed_time(c) for _, b, c in ev) / args.steps
     ms = total_ms / args.steps
+    step_ms = sorted(a.elapsed_time(c) for a, _, c in ev)   # each step's fwd + bwd alone
+    median_ms = step_ms[len(step_ms) // 2] if len(step_ms) % 2 else 0.5 * (
+        step_ms[len(step_ms) // 2 - 1] + step_ms[len(step_ms) // 2])
 
     S = w.S
     S2 = w.S_k * w.S_v                 # state elements (S^2 for square heads)
@@ -538,6 +541,7 @@ def main():
         "pct_fp32_valu_peak": 100.0 * credited / (ms / 1e3) / PEAK_FP32_VALU,
         "fwd_ms": fwd_ms,
         "bwd_ms": bwd_ms,
+        "median_step_ms": median_ms,        # the median over the timed steps (value uses the mean)
         # head size 128 runs on the fp32 matrix cores (dense fp32 MFMA peak, the same figure as
         # the fp32 vector peak); the small heads on the vector ALUs
         "roofline": {"bound": "mfma" if S2 == 128 * 128 else "alu",
