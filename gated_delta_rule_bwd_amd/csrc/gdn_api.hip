@@ -861,8 +861,8 @@ static SsmPlan ssm_plan(const gdn_ssm_problem *p) {
         pl.off_cpart = off; off += align_up((size_t)pl.hgs * 2 * n * T * G * N * 4);
     } else {
         pl.ckw = 1;
-        pl.nck = (int32_t)pl.nwin;
-        pl.off_ck = off;   off += align_up((size_t)pl.rows * pl.nwin * N * 4);
+        pl.nck = (int32_t)pl.nwin + (pl.rowwise ? 1 : 0);   // row-wise: one spare slot per row
+        pl.off_ck = off;   off += align_up((size_t)pl.rows * pl.nck * N * 4);
         pl.off_part = off; off += align_up((size_t)pl.rows / pl.seg_rows * T * 2 * N * 4);
         pl.off_dd = off;   off += align_up(n * T * H * P * 4);
         if (pl.rowwise) {  // the state gradient entering every window
@@ -950,6 +950,7 @@ int gdn_ssm_fwd(const gdn_ssm_problem *p, const float *s0, const float *x, const
     gdn::SsmArgs a = ssm_args(p, pl, ws, s0, x, dt, A, B, C);
     a.y = y; a.s_out = s_out;
     if (pl.chunked) return device_status(gdn::launch_ssm_chunk_fwd(a, (hipStream_t)stream));
+    if (pl.rowwise) return device_status(gdn::launch_ssm_rowwise_fwd(a, (hipStream_t)stream));
     return device_status(gdn::launch_ssm(a, false, (hipStream_t)stream));
 }
 
@@ -978,7 +979,9 @@ int gdn_ssm_bwd(const gdn_ssm_problem *p, const float *s0, const float *x, const
     a.dB = grad_packed + off[3]; a.dC = grad_packed + off[4];
     hipError_t e = hipSuccess;
     if (!(flags & GDN_BWD_REUSE_SNAPSHOTS))     // window states first (no y, s_out)
-        e = pl.chunked ? gdn::launch_ssm_chunk_fwd(a, (hipStream_t)stream) : gdn::launch_ssm(a, false, (hipStream_t)stream);
+        e = pl.chunked ? gdn::launch_ssm_chunk_fwd(a, (hipStream_t)stream)
+            : pl.rowwise ? gdn::launch_ssm_rowwise_fwd(a, (hipStream_t)stream)
+                         : gdn::launch_ssm(a, false, (hipStream_t)stream);
     if (pl.chunked) {
         if (e == hipSuccess) e = gdn::launch_ssm_chunk_bwd(a, (hipStream_t)stream);
     } else if (pl.rowwise) {

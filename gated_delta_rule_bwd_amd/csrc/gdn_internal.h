@@ -111,6 +111,9 @@ bool ssm_chunked(int P, int N, int aps);
 // combine over 128-row segments.
 bool ssm_rowwise(int P, int H, int G, int N);
 hipError_t launch_ssm_rowwise_bwd(const SsmArgs &a, hipStream_t st);
+// Its forward: the state before every window (and s_out), then y per window (y null: states
+// only).  The saved states take nck = ceil(T / 8) + 1 slots per row (the last one spare).
+hipError_t launch_ssm_rowwise_fwd(const SsmArgs &a, hipStream_t st);
 hipError_t launch_ssm_chunk_bwd(const SsmArgs &a, hipStream_t st);
 // Its forward: the state before every chunk (and s_out), then y per chunk (y null: states only).
 hipError_t launch_ssm_chunk_fwd(const SsmArgs &a, hipStream_t st);

@@ -619,6 +619,134 @@ __global__ void __launch_bounds__(256) ssm_win16_kernel(const SsmArgs a) {
     }
 }
 
+// ---- row-wise forward for 16 states -----------------------------------------------------
+// The same shapes' forward in two passes: the state's own recurrence (s = a s + d x B from the
+// first token) in the per-token layout, saving the state before every window (a window past the
+// end saves into one spare slot per row, so the token loop needs no branch) and s_out; then every
+// window on its own, two lanes per row, replaying from the saved state for y (a pair sum per
+// token instead of the per-token kernel's 16-lane sum).  Both replay with the walk's formula, so
+// the backward's replay gives the same states.
+template <bool APS>
+__global__ void __launch_bounds__(256) ssm_sst_kernel(const SsmArgs a) {
+    // per block of GB tokens: the rows' d x and step, the group's B (16 states)
+    __shared__ float sb[2][GB][ROWS], sd[2][GB][ROWS], sB[2][GB][16];
+    const int tid = threadIdx.x, sub = tid & 15, rho = tid >> 4;
+    const int64_t r0 = (int64_t)blockIdx.x * ROWS;
+    const Row w = row_of(a, r0 + rho);
+    const int64_t N = a.N, T = a.T, H = a.H, P = a.P, G = a.G;
+    const int nwin = (a.T + WIN - 1) / WIN;
+    const int nblk = (a.T + GB - 1) / GB;
+    float st = a.s0[w.r * N + sub];
+    const float Aj = APS ? a.A[w.h * N + sub] : a.A[w.h];
+    const Row lw = row_of(a, r0 + sub);
+    const int tk = 2 * rho;
+    float px[2], pd[2], pb[2];
+    auto load = [&](int blk) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int64_t t = min(blk * GB + tk + u, a.T - 1);
+            px[u] = a.x[((lw.s * T + t) * H + lw.h) * P + lw.i];
+            pd[u] = a.dt[(lw.s * T + t) * H + lw.h];
+            pb[u] = a.B[((lw.s * T + t) * G + lw.g) * N + sub];
+        }
+    };
+    // a token past the end gets step 0 (decay 1) and d x = 0: it leaves the state as it is
+    auto put = [&](int blk, int buf) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const bool ok = blk * GB + tk + u < a.T;
+            const float d = ok ? ssm_step(pd[u], a.softplus) : 0.f;
+            sd[buf][tk + u][sub] = d;
+            sb[buf][tk + u][sub] = d * (ok ? px[u] : 0.f);
+            sB[buf][tk + u][sub] = pb[u];
+        }
+    };
+    if (nblk > 0) {
+        load(0);
+        put(0, 0);
+    }
+    __syncthreads();
+    for (int blk = 0; blk < nblk; ++blk) {
+        const int cur = blk & 1, t0 = blk * GB;
+        if (blk + 1 < nblk) load(blk + 1);
+#pragma unroll
+        for (int k = 0; k < GB; ++k) {
+            if ((k & (WIN - 1)) == 0)   // the state before the window (slot nwin: past the end)
+                a.ck[(w.r * a.nck + min((t0 + k) / WIN, nwin)) * N + sub] = st;
+            st = fmaf(dexp(sd[cur][k][rho] * Aj), st, sb[cur][k][rho] * sB[cur][k][sub]);
+        }
+        if (blk + 1 < nblk) put(blk + 1, cur ^ 1);
+        __syncthreads();
+    }
+    if (a.s_out) a.s_out[w.r * N + sub] = st;
+}
+
+template <bool APS>
+__global__ void __launch_bounds__(256) ssm_y16_kernel(const SsmArgs a) {
+    constexpr int N = 16, NH = 8;
+    __shared__ float bc[2][WIN][N];          // B, C rows of the window's tokens
+    const int tid = threadIdx.x, lane = tid & 63, hb = lane & 1;
+    const int nwin = (a.T + WIN - 1) / WIN;
+    const int win = (int)(blockIdx.x % nwin);
+    const int64_t rb = blockIdx.x / nwin;
+    const Row w = row_of(a, rb * RB + (tid >> 1));
+    const int64_t T = a.T, H = a.H, P = a.P, G = a.G;
+    const int t0 = win * WIN, cnt = min(WIN, a.T - t0);
+    {
+        const int k = tid >> 5, q = (tid >> 4) & 1, n = tid & 15;
+        const Row w0 = row_of(a, rb * RB);
+        const int64_t t = min(t0 + k, a.T - 1);
+        bc[q][k][n] = (q ? a.C : a.B)[((w0.s * T + t) * G + w0.g) * N + n];
+    }
+    float sv[NH], Av[NH];
+    ld8(a.ck + (w.r * a.nck + win) * N + NH * hb, sv);
+    float Ah = 0.f;
+    if constexpr (APS) ld8(a.A + w.h * N + NH * hb, Av);
+    else Ah = a.A[w.h];
+    float xv[WIN], dv[WIN];
+    {
+        float m4[4];
+#pragma unroll
+        for (int k = 0; k < WIN; ++k) {
+            const int64_t t = min(t0 + k, a.T - 1);
+            const float xr = a.x[((w.s * T + t) * H + w.h) * P + w.i];
+            xv[k] = t0 + k < a.T ? xr : 0.f;
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int k = 4 * hb + j;
+            const float z = a.dt[(w.s * T + min(t0 + k, a.T - 1)) * H + w.h];
+            m4[j] = t0 + k < a.T ? ssm_step(z, a.softplus) : 0.f;
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float mo = dpp<0xB1>(m4[j]);
+            dv[j] = hb ? mo : m4[j];
+            dv[4 + j] = hb ? m4[j] : mo;
+        }
+    }
+    __syncthreads();
+    float yk[WIN];
+#pragma unroll
+    for (int k = 0; k < WIN; ++k) {
+        const float b = dv[k] * xv[k];
+        const float ah = APS ? 0.f : dexp(dv[k] * Ah);
+        float y = 0.f;
+#pragma unroll
+        for (int m = 0; m < NH; ++m) {
+            const float aj = APS ? dexp(dv[k] * Av[m]) : ah;
+            sv[m] = fmaf(aj, sv[m], b * bc[0][k][NH * hb + m]);
+            y = fmaf(sv[m], bc[1][k][NH * hb + m], y);
+        }
+        yk[k] = y + dpp<0xB1>(y);
+    }
+    if (hb == 0) {
+#pragma unroll
+        for (int k = 0; k < WIN; ++k)
+            if (k < cnt) a.y[((w.s * T + t0 + k) * H + w.h) * P + w.i] = yk[k];
+    }
+}
+
 // ---- combine: dB, dC over the segments of each group; ddt over the rows of each head ------
 // One thread per (sequence, token, group, 4 columns) of dB / dC, summing the group's segments
 // in increasing order with eight loads in flight; one per (sequence, token, head) of ddt.
@@ -702,6 +830,20 @@ hipError_t launch_ssm(const SsmArgs &a, bool bwd, hipStream_t st) {
 
 bool ssm_rowwise(int P, int H, int G, int N) {
     return N == 16 && G >= 1 && H % G == 0 && (int64_t)P * (H / G) % RB == 0;
+}
+
+hipError_t launch_ssm_rowwise_fwd(const SsmArgs &a, hipStream_t st) {
+    const int64_t rows = (int64_t)a.n_seqs * a.H * a.P;
+    if (rows <= 0) return hipSuccess;
+    const int64_t nwin = (a.T + WIN - 1) / WIN;
+    if (!ssm_rowwise(a.P, a.H, a.G, a.N) || a.ckw != 1 || a.nck != nwin + 1) return hipErrorInvalidValue;
+    void *params[] = {const_cast<SsmArgs *>(&a)};
+    hipError_t e = hipLaunchKernel(a.aps ? (const void *)ssm_sst_kernel<true> : (const void *)ssm_sst_kernel<false>,
+                                   dim3((unsigned)(rows / ROWS)), dim3(256), params, 0, st);
+    if (e == hipSuccess && a.y && nwin > 0)
+        e = hipLaunchKernel(a.aps ? (const void *)ssm_y16_kernel<true> : (const void *)ssm_y16_kernel<false>,
+                            dim3((unsigned)(rows / RB * nwin)), dim3(256), params, 0, st);
+    return e;
 }
 
 hipError_t launch_ssm_rowwise_bwd(const SsmArgs &a, hipStream_t st) {
