@@ -174,6 +174,65 @@ __device__ __forceinline__ f4 ld4v(Rsrc r, uint32_t o, bool vec) {
     if (vec) return bld4<DT>(r, o);
     return f4{bld<DT>(r, o, 0), bld<DT>(r, o + ES, 0), bld<DT>(r, o + 2 * ES, 0), bld<DT>(r, o + 3 * ES, 0)};
 }
+
+// Loads issued one block ahead keep the input's own bits and are widened where they are staged:
+// a widening right at the load would make the wave wait for that load there.
+typedef unsigned int u2 __attribute__((ext_vector_type(2)));
+template <int DT>
+struct RawT {
+    using one = float;
+    using four = f4;
+};
+template <>
+struct RawT<GDN_DTYPE_F16> {
+    using one = unsigned short;
+    using four = u2;
+};
+template <>
+struct RawT<GDN_DTYPE_BF16> {
+    using one = unsigned short;
+    using four = u2;
+};
+template <int DT>
+using Raw = typename RawT<DT>::one;
+template <int DT>
+using Raw4 = typename RawT<DT>::four;
+template <int DT>
+__device__ __forceinline__ Raw<DT> rld(Rsrc r, uint32_t vbytes, uint32_t sbytes) {
+    if constexpr (DT == GDN_DTYPE_F32) return bld<DT>(r, vbytes, sbytes);
+    else return __builtin_amdgcn_raw_buffer_load_b16(r, vbytes, sbytes, 0);
+}
+template <int DT>
+__device__ __forceinline__ float widen(Raw<DT> x) {
+    if constexpr (DT == GDN_DTYPE_F32) return x;
+    else if constexpr (DT == GDN_DTYPE_BF16) return __builtin_bit_cast(float, (uint32_t)x << 16);
+    else return (float)__builtin_bit_cast(_Float16, x);
+}
+// four elements as ld4v; the unaligned form packs four loads (it waits for them)
+template <int DT>
+__device__ __forceinline__ Raw4<DT> rld4v(Rsrc r, uint32_t o, bool vec) {
+    if constexpr (DT == GDN_DTYPE_F32) {
+        return ld4v<DT>(r, o, vec);
+    } else {
+        if (vec) return __builtin_amdgcn_raw_buffer_load_b64(r, o, 0, 0);
+        uint32_t h[4];
+#pragma unroll
+        for (int x = 0; x < 4; ++x) h[x] = __builtin_amdgcn_raw_buffer_load_b16(r, o + 2 * x, 0, 0);
+        return u2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+    }
+}
+template <int DT>
+__device__ __forceinline__ f4 widen4(Raw4<DT> v) {
+    if constexpr (DT == GDN_DTYPE_F32) {
+        return v;
+    } else {
+        f4 o;
+#pragma unroll
+        for (int x = 0; x < 4; ++x)
+            o[x] = widen<DT>((unsigned short)((x & 1) ? (v[x >> 1] >> 16) : (v[x >> 1] & 0xffffu)));
+        return o;
+    }
+}
 __device__ __forceinline__ bool rows_aligned(const void *p, const gdn_strides &st, uint32_t es) {
     return (((uintptr_t)p & (4 * es - 1)) == 0) && st.seq % 4 == 0 && st.tok % 4 == 0 && st.head % 4 == 0;
 }
@@ -446,8 +505,10 @@ __global__ void __launch_bounds__(64 * NWC) fwd_mf_kernel(const Mf128Args a) {
     // last one, replaced when staged); per lane v and beta at (token 4(l/16) + r, row j0 + l%16)
     // and the operands of Te^T and Bm^T
     struct Pre {
-        float c[TPT], k[TPT], q[TPT];
-        float v[4], b[4], te[4], bm[4];
+        float c[TPT];
+        Raw<DT> k[TPT], q[TPT];
+        Raw<DT> v[4], b[4];
+        float te[4], bm[4];
         int dir;
     };
     auto prefetch = [&](Pre &P, int t0) {
@@ -461,14 +522,14 @@ __global__ void __launch_bounds__(64 * NWC) fwd_mf_kernel(const Mf128Args a) {
         for (int x = 0; x < TPT; ++x) {
             const uint32_t tt = (uint32_t)min(TPT * tg + x, cnt - 1);
             P.c[x] = bldf(rc, ccol, tt * ct);
-            P.k[x] = bld<DT>(rk, ci * ES, tt * kt);
-            P.q[x] = bld<DT>(rq, ci * ES, tt * qt);
+            P.k[x] = rld<DT>(rk, ci * ES, tt * kt);
+            P.q[x] = rld<DT>(rq, ci * ES, tt * qt);
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const uint32_t tt = (uint32_t)min(4 * g4 + r, cnt - 1);
-            P.v[r] = bld<DT>(rv, (j0 + lm) * ES + tt * vt, 0);
-            P.b[r] = bld<DT>(rb, tt * bt, 0);
+            P.v[r] = rld<DT>(rv, (j0 + lm) * ES + tt * vt, 0);
+            P.b[r] = rld<DT>(rb, tt * bt, 0);
             P.te[r] = bldf(rw, (W * W + (4 * g4 + r) * W + lm) * 4, 0);
             P.bm[r] = bldf(rw, ((4 * g4 + r) * W + lm) * 4, 0);
         }
@@ -544,10 +605,10 @@ __global__ void __launch_bounds__(64 * NWC) fwd_mf_kernel(const Mf128Args a) {
             for (int x = 0; x < TPT; ++x) {
                 const int tt = TPT * tg + x;
                 const bool ok = tt < cnt;   // tokens past the end: c = 1 and zeros
-                const float c = ok ? P.c[x] : 1.f, k = ok ? P.k[x] : 0.f;
+                const float c = ok ? P.c[x] : 1.f, k = ok ? widen<DT>(P.k[x]) : 0.f;
                 krow[x] = k * rcp(c);
                 sm.kc[tt][ci] = k * c;
-                sm.qc[tt][ci] = ok ? P.q[x] * c : 0.f;
+                sm.qc[tt][ci] = ok ? widen<DT>(P.q[x]) * c : 0.f;
                 if (tt == cnt - 1) sm.pv[ci] = c;
             }
 #pragma unroll
@@ -557,8 +618,8 @@ __global__ void __launch_bounds__(64 * NWC) fwd_mf_kernel(const Mf128Args a) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const bool ok = 4 * g4 + r < cnt;
-                vv[r] = ok ? P.v[r] : 0.f;
-                bb[r] = ok ? P.b[r] : 0.f;
+                vv[r] = ok ? widen<DT>(P.v[r]) : 0.f;
+                bb[r] = ok ? widen<DT>(P.b[r]) : 0.f;
             }
             const float teA[4] = {P.te[0], P.te[1], P.te[2], P.te[3]}, bmA[4] = {P.bm[0], P.bm[1], P.bm[2], P.bm[3]};
             __syncthreads();
@@ -741,9 +802,11 @@ __global__ void __launch_bounds__(64 * NWC) chain_kernel(const Mf128Args a) {
     const int rq = tid % (R / 4), tr = tid / (R / 4);
     const bool vk = rows_aligned(a.k, a.sk, ES), vq = rows_aligned(a.q, a.sq, ES), vgy = rows_aligned(a.gy, a.sgy, ES);
     struct Pre {
-        f4 c[TPV], k[TPV], q[TPV];
-        float b[TPV];
-        f4 gy, e;
+        f4 c[TPV];
+        Raw4<DT> k[TPV], q[TPV];
+        Raw<DT> b[TPV];
+        Raw4<DT> gy;
+        f4 e;
         float m0, m1;
         int dir;
     };
@@ -760,13 +823,13 @@ __global__ void __launch_bounds__(64 * NWC) chain_kernel(const Mf128Args a) {
             const uint32_t tt = (uint32_t)min(tk0 + v * (NTC / 32), cnt - 1);
             if (a.kda) P.c[v] = ld4v<GDN_DTYPE_F32>(rc, tt * ct + 16 * cg, true);
             else P.c[v] = f4{1.f, 1.f, 1.f, 1.f} * bldf(rc, tt * ct, 0);
-            P.k[v] = ld4v<DT>(rk, tt * kt + 4 * cg * ES, vk);
-            P.q[v] = ld4v<DT>(rq_, tt * qt + 4 * cg * ES, vq);
-            P.b[v] = bld<DT>(rb, tt * bt, 0);
+            P.k[v] = rld4v<DT>(rk, tt * kt + 4 * cg * ES, vk);
+            P.q[v] = rld4v<DT>(rq_, tt * qt + 4 * cg * ES, vq);
+            P.b[v] = rld<DT>(rb, tt * bt, 0);
         }
         {
             const uint32_t tt = (uint32_t)min(tr, cnt - 1);
-            P.gy = ld4v<DT>(rgy, tt * gyt + 4 * rq * ES, vgy);
+            P.gy = rld4v<DT>(rgy, tt * gyt + 4 * rq * ES, vgy);
             P.e = ld4v<GDN_DTYPE_F32>(re, tt * et + 16 * rq, true);
         }
         const uint32_t m = tid & 255;
@@ -780,8 +843,8 @@ __global__ void __launch_bounds__(64 * NWC) chain_kernel(const Mf128Args a) {
         for (int v = 0; v < TPV; ++v) {
             const int tt = tk0 + v * (NTC / 32);
             const bool ok = tt < cnt;   // tokens past the end: c = 1 and zeros
-            const f4 c = ok ? P.c[v] : f4{1.f, 1.f, 1.f, 1.f}, k = ok ? P.k[v] : zero4();
-            const f4 qc = ok ? P.q[v] * c : zero4(), kc = k * c;
+            const f4 c = ok ? P.c[v] : f4{1.f, 1.f, 1.f, 1.f}, k = ok ? widen4<DT>(P.k[v]) : zero4();
+            const f4 qc = ok ? widen4<DT>(P.q[v]) * c : zero4(), kc = k * c;
             st4(&sm.krT[tt][4 * cg], f4{k[0] * rcp(c[0]), k[1] * rcp(c[1]), k[2] * rcp(c[2]), k[3] * rcp(c[3])});
 #pragma unroll
             for (int x = 0; x < 4; ++x) {
@@ -789,11 +852,11 @@ __global__ void __launch_bounds__(64 * NWC) chain_kernel(const Mf128Args a) {
                 kcI[cti(4 * cg + x, tt)] = kc[x];
             }
             if (tt == cnt - 1) st4(&sm.pv[4 * cg], c);
-            if (cg == 0) sm.bt[tt] = ok ? P.b[v] : 0.f;
+            if (cg == 0) sm.bt[tt] = ok ? widen<DT>(P.b[v]) : 0.f;
         }
         {
             const bool ok = tr < cnt;
-            st4(&sm.sgy[tr][4 * rq], ok ? P.gy * scale : zero4());
+            st4(&sm.sgy[tr][4 * rq], ok ? widen4<DT>(P.gy) * scale : zero4());
             st4(&sm.er[tr][4 * rq], ok ? P.e : zero4());
         }
         if (tid < 256) {
@@ -1211,8 +1274,9 @@ __global__ void __launch_bounds__(NT) colsum_kernel(const Mf128Args a) {
     const int cg = tid & 31, tk = tid >> 5;
     const bool vk = rows_aligned(a.k, a.sk, ES), vq = rows_aligned(a.q, a.sq, ES), vgy = rows_aligned(a.gy, a.sgy, ES);
     struct Pre {
-        f4 c, k, q, gy, e, dv;
-        float b;
+        f4 c, e, dv;
+        Raw4<DT> k, q, gy;
+        Raw<DT> b;
         float m1[2], m2[2];   // the chain's slabs (at most two)
         int dir;
     };
@@ -1227,12 +1291,12 @@ __global__ void __launch_bounds__(NT) colsum_kernel(const Mf128Args a) {
         const uint32_t tt = (uint32_t)min(tk, cnt - 1);
         if (kda) P.c = ld4v<GDN_DTYPE_F32>(rc, tt * ct + 16 * cg, true);
         else P.c = f4{1.f, 1.f, 1.f, 1.f} * bldf(rc, tt * ct, 0);
-        P.k = ld4v<DT>(rk, tt * kt + 4 * cg * ES, vk);
-        P.q = ld4v<DT>(rq, tt * qt + 4 * cg * ES, vq);
-        P.gy = ld4v<DT>(rgy, tt * gyt + 4 * cg * ES, vgy);
+        P.k = rld4v<DT>(rk, tt * kt + 4 * cg * ES, vk);
+        P.q = rld4v<DT>(rq, tt * qt + 4 * cg * ES, vq);
+        P.gy = rld4v<DT>(rgy, tt * gyt + 4 * cg * ES, vgy);
         P.e = ld4v<GDN_DTYPE_F32>(re, tt * et + 16 * cg, true);
         P.dv = ld4v<GDN_DTYPE_F32>(rdv, tt * et + 16 * cg, vec_dv);
-        P.b = bld<DT>(rb, tt * bt, 0);
+        P.b = rld<DT>(rb, tt * bt, 0);
         const int64_t gb = ((s * (a.pb_T / W) + (t0 - a.pb_t0) / W) * a.H_v + h) * nsl * (W * W) + (tid & 255);
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
@@ -1243,8 +1307,8 @@ __global__ void __launch_bounds__(NT) colsum_kernel(const Mf128Args a) {
     };
     auto stage = [&](ColLds &sm, const Pre &P, int cnt) {
         const bool ok = tk < cnt;   // tokens past the end: c = 1 and zeros
-        const f4 c = ok ? P.c : f4{1.f, 1.f, 1.f, 1.f}, k = ok ? P.k : zero4();
-        const f4 qc = ok ? P.q * c : zero4(), kc = k * c, d = ok ? P.e * P.b : zero4();
+        const f4 c = ok ? P.c : f4{1.f, 1.f, 1.f, 1.f}, k = ok ? widen4<DT>(P.k) : zero4();
+        const f4 qc = ok ? widen4<DT>(P.q) * c : zero4(), kc = k * c, d = ok ? P.e * widen<DT>(P.b) : zero4();
         float *krI = &sm.krI[0][0], *qcI = &sm.qcI[0][0], *kcI = &sm.kcI[0][0], *cI = &sm.cI[0][0], *dl = &sm.dl[0][0];
 #pragma unroll
         for (int x = 0; x < 4; ++x) {
@@ -1255,7 +1319,7 @@ __global__ void __launch_bounds__(NT) colsum_kernel(const Mf128Args a) {
             cI[o] = c[x];
             dl[o] = d[x];
         }
-        st4(&sm.sgy[tk][4 * cg], ok ? P.gy * scale : zero4());
+        st4(&sm.sgy[tk][4 * cg], ok ? widen4<DT>(P.gy) * scale : zero4());
         st4(&sm.du[tk][4 * cg], ok ? -P.dv : zero4());
         if (tk == cnt - 1) st4(&sm.pv[4 * cg], c);
         if (tid < 256) {   // the slabs' partials in order

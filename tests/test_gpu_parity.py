@@ -373,6 +373,37 @@ def test_s128_bitwise_interval_reuse_and_strides(dev):
                 assert np.array_equal(a[n], other[n]), (what, n)
 
 
+
+@pytest.mark.parametrize("kind", ["f32", "bf16", "f16"])
+def test_s128_rows_off_four_element_boundary(dev, kind):
+    """S = 128 with q, k, v, g, beta and gy one element past an allocation's start, so no row
+    starts on a four-element boundary: the kernels take their one-element loads (for 16-bit
+    inputs: four loads packed before the widening) and every output is bitwise equal to the
+    aligned run on the same values."""
+    w = I.Workload("s128_offrows", 2, 90, 2, 4, 128, True, 64, -0.3, seq_lens=(90, 37), seed=509)
+    arrays, _ = I.make_all(w)
+    dt = torch.float32
+    if kind != "f32":
+        arrays = I.round_inputs(arrays, kind)
+        dt = TORCH_HALF[kind]
+    log(f"[parity] {w.name} {kind}: inputs one element off")
+    _, a = run_case(dev, w, arrays, in_dtype=dt)
+    dc = dev(w, arrays, in_dtype=dt)
+    for name in ("q", "k", "v", "g", "beta", "gy"):
+        t = getattr(dc, name)
+        assert t.is_contiguous()
+        buf = torch.empty(t.numel() + 1, dtype=t.dtype, device=t.device)
+        off = buf[1:].view(t.shape)
+        off.copy_(t)
+        assert off.data_ptr() % 8 != 0
+        setattr(dc, name, off)
+    dc.fwd()
+    dc.bwd(reuse=True)
+    torch.cuda.synchronize()
+    b = dc.results_numpy()
+    for n in a:
+        assert np.array_equal(a[n], b[n]), n
+
 PIECE_CASES = {
     # two pieces of 1152 tokens, the second sequence ending inside the first
     "two_pieces": I.Workload("s128_pieces", 2, 2200, 1, 2, 128, True, 64, -0.3,
