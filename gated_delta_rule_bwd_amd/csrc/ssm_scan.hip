@@ -77,6 +77,10 @@ __device__ __forceinline__ void stv(float *p, const float (&v)[NPL]) {
 // exp for the per-token decay: the hardware exp2 of x log2(e).  Its relative error is about
 // |x| 2^-24 from rounding x log2(e), the same order as the rounding of the product d A itself.
 __device__ __forceinline__ float dexp(float x) { return __expf(x); }
+// The row-wise kernels for 16 states keep A scaled by log2(e) and take their decays as
+// 2^(step A log2 e): one multiply and the hardware base-2 exponential per decay.
+constexpr float kLog2e = 1.4426950408889634f, kLn2 = 0.6931471805599453f;
+__device__ __forceinline__ float dexp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 struct Row {
     int64_t r, s, h, i, g;
@@ -427,7 +431,7 @@ __global__ void __launch_bounds__(256) ssm_gsw_kernel(const SsmArgs a) {
     const int nwin = (a.T + WIN - 1) / WIN;
     const int nblk = (a.T + GB - 1) / GB;
     float gs = a.gs ? a.gs[w.r * N + sub] : 0.f;
-    const float Aj = APS ? a.A[w.h * N + sub] : a.A[w.h];
+    const float Aj = (APS ? a.A[w.h * N + sub] : a.A[w.h]) * kLog2e;
     // thread tid stages token pairs (tokens 2 (tid >> 4) + {0, 1}) of row tid & 15: gy, dt; and
     // C of those tokens, state tid & 15
     const Row lw = row_of(a, r0 + sub);
@@ -469,7 +473,7 @@ __global__ void __launch_bounds__(256) ssm_gsw_kernel(const SsmArgs a) {
                 // window then writes again with the same bits)
                 a.gsw[(w.r * nwin + min((t0 + k) / WIN, nwin - 1)) * N + sub] = gs;
             gs = fmaf(sgy[cur][k][rho], sC[cur][k][sub], gs);
-            gs = dexp(sd[cur][k][rho] * Aj) * gs;
+            gs = dexp2(sd[cur][k][rho] * Aj) * gs;
         }
         if (blk > 0) put(blk - 1, cur ^ 1);
         __syncthreads();
@@ -514,9 +518,15 @@ __global__ void __launch_bounds__(256) ssm_win16_kernel(const SsmArgs a) {
     float sp[NH], gs[NH], Av[NH];
     ld8(a.ck + (w.r * a.nck + win) * N + NH * hb, sp);
     ld8(a.gsw + (w.r * nwin + win) * N + NH * hb, gs);
-    float Ah = 0.f;
-    if constexpr (APS) ld8(a.A + w.h * N + NH * hb, Av);
-    else Ah = a.A[w.h];
+    float Ah = 0.f, Ah2 = 0.f;   // A (one per head), and scaled by log2(e)
+    if constexpr (APS) {
+        ld8(a.A + w.h * N + NH * hb, Av);
+#pragma unroll
+        for (int m = 0; m < NH; ++m) Av[m] *= kLog2e;
+    } else {
+        Ah = a.A[w.h];
+        Ah2 = Ah * kLog2e;
+    }
     float xv[WIN], gv[WIN], dv[WIN], sg[WIN];
     {
         // the pair's lanes each take the step (and softplus') of four tokens and swap them
@@ -551,40 +561,50 @@ __global__ void __launch_bounds__(256) ssm_win16_kernel(const SsmArgs a) {
 #pragma unroll
     for (int k = 0; k < WIN; ++k) {
         const float b = dv[k] * xv[k];
-        const float ah = APS ? 0.f : dexp(dv[k] * Ah);
+        const float ah = APS ? 0.f : dexp2(dv[k] * Ah2);
 #pragma unroll
         for (int m = 0; m < NH; ++m) {
-            const float aj = APS ? dexp(dv[k] * Av[m]) : ah;
+            const float aj = APS ? dexp2(dv[k] * Av[m]) : ah;
             S[k][m] = fmaf(aj, k ? S[k - 1][m] : sp[m], b * bc[0][k][NH * hb + m]);
         }
     }
     const bool b3 = lane & 8, b2 = lane & 4;
+    const int x4 = (lane ^ 4) << 2;   // byte address of lane ^ 4 for ds_bpermute
+    // the window's dx and ddt (or ddrow) entries of this row, one token apart
+    const int64_t at0 = ((w.s * T + t0) * H + w.h) * P + w.i, tstr = H * P;
+    float *const dxw = a.dx + at0, *const ddw = (P == 1 ? a.ddt : a.ddrow) + at0;
 #pragma unroll
     for (int k = 0; k < WIN; ++k) asm volatile("" : "+v"(dv[k]));
+    // a full window walks without a test per token (the last, partial one with it)
+    auto walk = [&](auto full) {
 #pragma unroll
     for (int k = WIN - 1; k >= 0; --k) {
-        if (k < cnt) {
+        if (decltype(full)::value || k < cnt) {
             const float d = dv[k], xk = xv[k], gyk = gv[k], dxv = d * xk;
-            const float ah = APS ? 0.f : dexp(d * Ah);
+            const float ah = APS ? 0.f : dexp2(d * Ah2);
             float v[2 * NH];
-            float gB = 0.f, dec = 0.f;
+            float gB = 0.f, dec = 0.f;   // dec: sum of gs a A s_prev (A log2(e) with APS)
 #pragma unroll
             for (int m = 0; m < NH; ++m) {
-                const float aj = APS ? dexp(d * Av[m]) : ah;
+                const float aj = APS ? dexp2(d * Av[m]) : ah;
                 const float prev = k ? S[k - 1][m] : sp[m];
                 gs[m] = fmaf(gyk, bc[1][k][NH * hb + m], gs[m]);
                 v[m] = gyk * S[k][m];
                 v[NH + m] = gs[m] * dxv;
                 gB = fmaf(gs[m], bc[0][k][NH * hb + m], gB);
-                dec = APS ? fmaf(gs[m] * (Av[m] * aj), prev, dec) : fmaf(gs[m], prev, dec);
-                gs[m] = aj * gs[m];
+                if constexpr (APS) {
+                    gs[m] = aj * gs[m];
+                    dec = fmaf(gs[m] * prev, Av[m], dec);
+                } else {
+                    dec = fmaf(gs[m], prev, dec);
+                    gs[m] = aj * gs[m];
+                }
             }
             gB += dpp<0xB1>(gB);    // the pair's halves
             dec += dpp<0xB1>(dec);
             if (hb == 0) {
-                const int64_t at = ((w.s * T + t0 + k) * H + w.h) * P + w.i;
-                a.dx[at] = d * gB;
-                (P == 1 ? a.ddt : a.ddrow)[at] = ((APS ? dec : Ah * ah * dec) + xk * gB) * sg[k];
+                dxw[k * tstr] = d * gB;
+                ddw[k * tstr] = ((APS ? dec * kLn2 : Ah * ah * dec) + xk * gB) * sg[k];
             }
             float u[8], w4[4], x2[2];
 #pragma unroll
@@ -603,13 +623,16 @@ __global__ void __launch_bounds__(256) ssm_win16_kernel(const SsmArgs a) {
                 x2[m] = keep + dpp<0x128>(send);
             }
             const float keep = b2 ? x2[1] : x2[0], send = b2 ? x2[0] : x2[1];
-            float z = keep + __shfl_xor(send, 4, 64);
+            float z = keep + as_f(__builtin_amdgcn_ds_bpermute(x4, as_i(send)));
             z += dpp<0x4E>(z);
             // lane l: dC (l < 32) or dB of state 8 (l & 1) + 4 bit4 + 2 bit3 + bit2
             if ((lane & 2) == 0)
                 red[k][wave][(lane >> 5) * N + NH * hb + 4 * ((lane >> 4) & 1) + 2 * ((lane >> 3) & 1) + ((lane >> 2) & 1)] = z;
         }
     }
+    };
+    if (cnt == WIN) walk(std::true_type{});
+    else walk(std::false_type{});
     __syncthreads();
     {
         const int k = tid >> 5, idx = tid & 31;
@@ -637,7 +660,7 @@ __global__ void __launch_bounds__(256) ssm_sst_kernel(const SsmArgs a) {
     const int nwin = (a.T + WIN - 1) / WIN;
     const int nblk = (a.T + GB - 1) / GB;
     float st = a.s0[w.r * N + sub];
-    const float Aj = APS ? a.A[w.h * N + sub] : a.A[w.h];
+    const float Aj = (APS ? a.A[w.h * N + sub] : a.A[w.h]) * kLog2e;
     const Row lw = row_of(a, r0 + sub);
     const int tk = 2 * rho;
     float px[2], pd[2], pb[2];
@@ -673,7 +696,7 @@ __global__ void __launch_bounds__(256) ssm_sst_kernel(const SsmArgs a) {
         for (int k = 0; k < GB; ++k) {
             if ((k & (WIN - 1)) == 0)   // the state before the window (slot nwin: past the end)
                 a.ck[(w.r * a.nck + min((t0 + k) / WIN, nwin)) * N + sub] = st;
-            st = fmaf(dexp(sd[cur][k][rho] * Aj), st, sb[cur][k][rho] * sB[cur][k][sub]);
+            st = fmaf(dexp2(sd[cur][k][rho] * Aj), st, sb[cur][k][rho] * sB[cur][k][sub]);
         }
         if (blk + 1 < nblk) put(blk + 1, cur ^ 1);
         __syncthreads();
@@ -701,8 +724,13 @@ __global__ void __launch_bounds__(256) ssm_y16_kernel(const SsmArgs a) {
     float sv[NH], Av[NH];
     ld8(a.ck + (w.r * a.nck + win) * N + NH * hb, sv);
     float Ah = 0.f;
-    if constexpr (APS) ld8(a.A + w.h * N + NH * hb, Av);
-    else Ah = a.A[w.h];
+    if constexpr (APS) {
+        ld8(a.A + w.h * N + NH * hb, Av);
+#pragma unroll
+        for (int m = 0; m < NH; ++m) Av[m] *= kLog2e;
+    } else {
+        Ah = a.A[w.h] * kLog2e;
+    }
     float xv[WIN], dv[WIN];
     {
         float m4[4];
@@ -730,11 +758,11 @@ __global__ void __launch_bounds__(256) ssm_y16_kernel(const SsmArgs a) {
 #pragma unroll
     for (int k = 0; k < WIN; ++k) {
         const float b = dv[k] * xv[k];
-        const float ah = APS ? 0.f : dexp(dv[k] * Ah);
+        const float ah = APS ? 0.f : dexp2(dv[k] * Ah);
         float y = 0.f;
 #pragma unroll
         for (int m = 0; m < NH; ++m) {
-            const float aj = APS ? dexp(dv[k] * Av[m]) : ah;
+            const float aj = APS ? dexp2(dv[k] * Av[m]) : ah;
             sv[m] = fmaf(aj, sv[m], b * bc[0][k][NH * hb + m]);
             y = fmaf(sv[m], bc[1][k][NH * hb + m], y);
         }
