@@ -494,14 +494,15 @@ __device__ __forceinline__ void ld8(const float *p, float (&v)[8]) {
 
 // One workgroup per (128 rows, 8-token window); lane l owns states 8 (l & 1) .. + 7 of row l / 2.
 // Replay the window from its saved state, walk it back from the window's gradient; the token's
-// dC and dB are reduce-scattered over the wave's 32 rows (permlane32: dC or dB, permlane16: 4
-// states, row_ror:8: 2, lane^4: 1, then lane^2 added), so lane l ends with state
-// 8 (l & 1) + 4 bit4 + 2 bit3 + bit2 of dC (l < 32) or dB.
+// dC and dB are reduce-scattered over the wave's 32 rows in three steps (permlane32: dC or dB,
+// permlane16: 4 states, row_ror:8: 2), so lane l ends with states 8 (l & 1) + 4 bit4 + 2 bit3
+// + {0, 1} of dC (l < 32) or dB over 8 of the rows; the window's end sums the four lanes (bits
+// 1, 2) of each of the four waves from LDS in a fixed order.
 template <bool APS>
 __global__ void __launch_bounds__(256) ssm_win16_kernel(const SsmArgs a) {
     constexpr int N = 16, NH = 8;
     __shared__ float bc[2][WIN][N];          // B, C rows of the window's tokens
-    __shared__ float red[WIN][4][2 * N];     // [token][wave][dC | dB state]
+    __shared__ float red[WIN][4][4][2 * N];  // [token][wave][lane bits 1, 2][dC | dB state]
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hb = lane & 1;
     const int nwin = (a.T + WIN - 1) / WIN;
     const int win = (int)(blockIdx.x % nwin);
@@ -568,8 +569,9 @@ __global__ void __launch_bounds__(256) ssm_win16_kernel(const SsmArgs a) {
             S[k][m] = fmaf(aj, k ? S[k - 1][m] : sp[m], b * bc[0][k][NH * hb + m]);
         }
     }
-    const bool b3 = lane & 8, b2 = lane & 4;
-    const int x4 = (lane ^ 4) << 2;   // byte address of lane ^ 4 for ds_bpermute
+    const bool b3 = lane & 8;
+    // this lane's pair of sums in red[k][wave]: row (lane bits 1, 2), column of its first state
+    const int rcol = ((lane >> 1) & 3) * 2 * N + (lane >> 5) * N + NH * hb + 4 * ((lane >> 4) & 1) + 2 * ((lane >> 3) & 1);
     // the window's dx and ddt (or ddrow) entries of this row, one token apart
     const int64_t at0 = ((w.s * T + t0) * H + w.h) * P + w.i, tstr = H * P;
     float *const dxw = a.dx + at0, *const ddw = (P == 1 ? a.ddt : a.ddrow) + at0;
@@ -622,12 +624,7 @@ __global__ void __launch_bounds__(256) ssm_win16_kernel(const SsmArgs a) {
                 const float keep = b3 ? w4[2 + m] : w4[m], send = b3 ? w4[m] : w4[2 + m];
                 x2[m] = keep + dpp<0x128>(send);
             }
-            const float keep = b2 ? x2[1] : x2[0], send = b2 ? x2[0] : x2[1];
-            float z = keep + as_f(__builtin_amdgcn_ds_bpermute(x4, as_i(send)));
-            z += dpp<0x4E>(z);
-            // lane l: dC (l < 32) or dB of state 8 (l & 1) + 4 bit4 + 2 bit3 + bit2
-            if ((lane & 2) == 0)
-                red[k][wave][(lane >> 5) * N + NH * hb + 4 * ((lane >> 4) & 1) + 2 * ((lane >> 3) & 1) + ((lane >> 2) & 1)] = z;
+            *reinterpret_cast<float2 *>(&red[k][wave][0][0] + rcol) = make_float2(x2[0], x2[1]);
         }
     }
     };
@@ -636,9 +633,14 @@ __global__ void __launch_bounds__(256) ssm_win16_kernel(const SsmArgs a) {
     __syncthreads();
     {
         const int k = tid >> 5, idx = tid & 31;
-        if (k < cnt)
-            a.part[(rb * T + t0 + k) * 2 * N + idx] =
-                ((red[k][0][idx] + red[k][1][idx]) + red[k][2][idx]) + red[k][3][idx];
+        if (k < cnt) {
+            float sum = 0.f;
+#pragma unroll
+            for (int wv = 0; wv < 4; ++wv)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) sum += red[k][wv][q][idx];
+            a.part[(rb * T + t0 + k) * 2 * N + idx] = sum;
+        }
     }
 }
 
