@@ -484,6 +484,35 @@ __global__ void __launch_bounds__(256) ssm_gsw_kernel(const SsmArgs a) {
 constexpr int RB = 128;   // rows per block of pass 2 (and per column-sum segment): two lanes per
                           // row, eight states each
 
+// row_of for a wave-uniform row, with 32-bit divisions when the row and the rows of a sequence
+// fit in 32 bits
+__device__ __forceinline__ Row row_of_uniform(const SsmArgs &a, int64_t r) {
+    const int64_t rows_seq = (int64_t)a.P * a.H;
+    if (r > 0xffffffffll || rows_seq > 0xffffffffll) return row_of(a, r);
+    const uint32_t ru = (uint32_t)r, P = (uint32_t)a.P, H = (uint32_t)a.H;
+    const uint32_t q = ru / P, s = q / H, h = q - s * H;
+    Row o;
+    o.r = r;
+    o.i = ru - q * P;
+    o.h = h;
+    o.s = s;
+    o.g = h / (H / (uint32_t)a.G);
+    return o;
+}
+
+// Row j of the RB-row block starting at row r0 (a multiple of RB): the block lies in one
+// (sequence, group), since a group's rows are a multiple of RB, so only the head and position
+// differ from the block's first row (found once, with scalar arithmetic).
+__device__ __forceinline__ Row block_row(const SsmArgs &a, const Row &w0, int j) {
+    Row w = w0;
+    const int q = (int)w0.i + j;
+    const int dh = a.P == 1 ? q : q / a.P;
+    w.r = w0.r + j;
+    w.i = q - dh * a.P;
+    w.h = w0.h + dh;
+    return w;
+}
+
 __device__ __forceinline__ void ld8(const float *p, float (&v)[8]) {
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
@@ -507,15 +536,17 @@ __global__ void __launch_bounds__(256) ssm_win16_kernel(const SsmArgs a) {
     const int nwin = (a.T + WIN - 1) / WIN;
     const int win = (int)(blockIdx.x % nwin);
     const int64_t rb = blockIdx.x / nwin;
-    const Row w = row_of(a, rb * RB + (tid >> 1));   // the block's rows share (sequence, group)
+    const Row w0 = row_of_uniform(a, rb * RB), w = block_row(a, w0, tid >> 1);
     const int64_t T = a.T, H = a.H, P = a.P, G = a.G;
     const int t0 = win * WIN, cnt = min(WIN, a.T - t0);
     {
         const int k = tid >> 5, q = (tid >> 4) & 1, n = tid & 15;
-        const Row w0 = row_of(a, rb * RB);
         const int64_t t = min(t0 + k, a.T - 1);
         bc[q][k][n] = (q ? a.C : a.B)[((w0.s * T + t) * G + w0.g) * N + n];
     }
+    // this row's x, gy (one token apart: tstr) and step (H apart) from the window's first token
+    const int64_t at0 = ((w.s * T + t0) * H + w.h) * P + w.i, tstr = H * P;
+    const float *const xw = a.x + at0, *const gw = a.gy + at0, *const dtw = a.dt + (w.s * T + t0) * H + w.h;
     float sp[NH], gs[NH], Av[NH];
     ld8(a.ck + (w.r * a.nck + win) * N + NH * hb, sp);
     ld8(a.gsw + (w.r * nwin + win) * N + NH * hb, gs);
@@ -534,19 +565,18 @@ __global__ void __launch_bounds__(256) ssm_win16_kernel(const SsmArgs a) {
         float m4[4], s4[4];
 #pragma unroll
         for (int k = 0; k < WIN; ++k) {
-            const int64_t t = min(t0 + k, a.T - 1);   // tokens past the end are skipped below
-            const int64_t at = ((w.s * T + t) * H + w.h) * P + w.i;
-            const bool ok = t0 + k < a.T;
-            const float xr = a.x[at], gr = a.gy[at];
+            const int kk = min(k, cnt - 1);   // tokens past the end are skipped below
+            const bool ok = k < cnt;
+            const float xr = xw[kk * tstr], gr = gw[kk * tstr];
             xv[k] = ok ? xr : 0.f;
             gv[k] = ok ? gr : 0.f;
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int k = 4 * hb + j;
-            const float z = a.dt[(w.s * T + min(t0 + k, a.T - 1)) * H + w.h];
-            m4[j] = t0 + k < a.T ? ssm_step(z, a.softplus) : 0.f;
-            s4[j] = (P == 1 && a.softplus) ? 1.f / (1.f + expf(-z)) : 1.f;
+            const float z = dtw[min(k, cnt - 1) * H];
+            m4[j] = k < cnt ? ssm_step(z, a.softplus) : 0.f;
+            s4[j] = (P == 1 && a.softplus) ? __builtin_amdgcn_rcpf(1.f + expf(-z)) : 1.f;
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -573,7 +603,6 @@ __global__ void __launch_bounds__(256) ssm_win16_kernel(const SsmArgs a) {
     // this lane's pair of sums in red[k][wave]: row (lane bits 1, 2), column of its first state
     const int rcol = ((lane >> 1) & 3) * 2 * N + (lane >> 5) * N + NH * hb + 4 * ((lane >> 4) & 1) + 2 * ((lane >> 3) & 1);
     // the window's dx and ddt (or ddrow) entries of this row, one token apart
-    const int64_t at0 = ((w.s * T + t0) * H + w.h) * P + w.i, tstr = H * P;
     float *const dxw = a.dx + at0, *const ddw = (P == 1 ? a.ddt : a.ddrow) + at0;
 #pragma unroll
     for (int k = 0; k < WIN; ++k) asm volatile("" : "+v"(dv[k]));
@@ -714,15 +743,16 @@ __global__ void __launch_bounds__(256) ssm_y16_kernel(const SsmArgs a) {
     const int nwin = (a.T + WIN - 1) / WIN;
     const int win = (int)(blockIdx.x % nwin);
     const int64_t rb = blockIdx.x / nwin;
-    const Row w = row_of(a, rb * RB + (tid >> 1));
+    const Row w0 = row_of_uniform(a, rb * RB), w = block_row(a, w0, tid >> 1);
     const int64_t T = a.T, H = a.H, P = a.P, G = a.G;
     const int t0 = win * WIN, cnt = min(WIN, a.T - t0);
     {
         const int k = tid >> 5, q = (tid >> 4) & 1, n = tid & 15;
-        const Row w0 = row_of(a, rb * RB);
         const int64_t t = min(t0 + k, a.T - 1);
         bc[q][k][n] = (q ? a.C : a.B)[((w0.s * T + t) * G + w0.g) * N + n];
     }
+    const int64_t at0 = ((w.s * T + t0) * H + w.h) * P + w.i, tstr = H * P;
+    const float *const dtw = a.dt + (w.s * T + t0) * H + w.h;
     float sv[NH], Av[NH];
     ld8(a.ck + (w.r * a.nck + win) * N + NH * hb, sv);
     float Ah = 0.f;
@@ -738,15 +768,14 @@ __global__ void __launch_bounds__(256) ssm_y16_kernel(const SsmArgs a) {
         float m4[4];
 #pragma unroll
         for (int k = 0; k < WIN; ++k) {
-            const int64_t t = min(t0 + k, a.T - 1);
-            const float xr = a.x[((w.s * T + t) * H + w.h) * P + w.i];
-            xv[k] = t0 + k < a.T ? xr : 0.f;
+            const float xr = a.x[at0 + min(k, cnt - 1) * tstr];
+            xv[k] = k < cnt ? xr : 0.f;
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int k = 4 * hb + j;
-            const float z = a.dt[(w.s * T + min(t0 + k, a.T - 1)) * H + w.h];
-            m4[j] = t0 + k < a.T ? ssm_step(z, a.softplus) : 0.f;
+            const float z = dtw[min(k, cnt - 1) * H];
+            m4[j] = k < cnt ? ssm_step(z, a.softplus) : 0.f;
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -773,7 +802,7 @@ __global__ void __launch_bounds__(256) ssm_y16_kernel(const SsmArgs a) {
     if (hb == 0) {
 #pragma unroll
         for (int k = 0; k < WIN; ++k)
-            if (k < cnt) a.y[((w.s * T + t0 + k) * H + w.h) * P + w.i] = yk[k];
+            if (k < cnt) a.y[at0 + k * tstr] = yk[k];
     }
 }
 
