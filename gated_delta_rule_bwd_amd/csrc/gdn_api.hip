@@ -828,7 +828,7 @@ static int ssm_validate(const gdn_ssm_problem *p) {
     if ((int64_t)p->n_seqs * p->H * p->P / 16 > INT32_MAX) return GDN_ERR_UNSUPPORTED;
     // the chunked backward: at most one workgroup per (sequence, head, 32-token chunk); the
     // row-wise one: one per (128 rows, 8-token window)
-    if (gdn::ssm_chunked(p->P, p->N, p->a_per_state) &&
+    if (gdn::ssm_chunked(p->P, p->N, p->a_per_state, p->H, p->G) &&
         (int64_t)p->n_seqs * p->H * (((int64_t)p->T + 31) / 32) > INT32_MAX)
         return GDN_ERR_UNSUPPORTED;
     if (gdn::ssm_rowwise(p->P, p->H, p->G, p->N) &&
@@ -842,7 +842,7 @@ static SsmPlan ssm_plan(const gdn_ssm_problem *p) {
     const size_t n = p->n_seqs, T = p->T, H = p->H, P = p->P, N = p->N, G = p->G;
     pl.rows = (int64_t)(n * H * P);
     pl.nwin = (p->T + 7) / 8;
-    pl.chunked = gdn::ssm_chunked(p->P, p->N, p->a_per_state);
+    pl.chunked = gdn::ssm_chunked(p->P, p->N, p->a_per_state, p->H, p->G);
     pl.rowwise = !pl.chunked && gdn::ssm_rowwise(p->P, p->H, p->G, p->N);
     size_t off = 0;
     pl.off_part = pl.off_dd = pl.off_dsq = pl.off_cpart = pl.off_gsw = 0;

@@ -103,9 +103,10 @@ struct SsmArgs {
 };
 hipError_t launch_ssm(const SsmArgs &a, bool bwd, hipStream_t st);   // forward or walk
 hipError_t launch_ssm_combine(const SsmArgs &a, hipStream_t st);
-// Chunked backward (one decay per head, P = 64, N = 128): the chunk-end state gradients, the
-// chunks' gradients on the matrix cores, then the head slices' dB and dC summed in order.
-bool ssm_chunked(int P, int N, int aps);
+// Chunked backward (one decay per head, P = 64, N = 128, H P and G N at most 2^24): the chunk-end
+// state gradients, the chunks' gradients on the matrix cores, then the head slices' dB and dC
+// summed in order.
+bool ssm_chunked(int P, int N, int aps, int64_t H, int64_t G);
 // Row-wise backward for 16 states (rows of a group a multiple of 128): the state gradient
 // entering every 8-token window, then the windows in parallel with two lanes per row, then the
 // combine over 128-row segments.

@@ -86,6 +86,22 @@ __device__ __forceinline__ float scan32_suffix(float v, int lane) {
     }
     return v;
 }
+// Buffer loads: a wave-uniform base (scalar registers), a per-lane byte offset fixed for the
+// kernel and a scalar byte offset for the token, so a chunk's loads need no vector address
+// arithmetic.  Bases are taken at the chunk's first token; offsets stay far below 2^31.
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+__device__ __forceinline__ Rsrc rsrc(const float *p) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(p), (short)0, 0x7fffffff, 0x00020000);
+}
+__device__ __forceinline__ float bld(Rsrc r, uint32_t vbytes, uint32_t sbytes) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, vbytes, sbytes, 0));
+}
+// (the whole vector is bit-cast: bit-casting its elements one by one made this compiler load
+// only the first dword)
+__device__ __forceinline__ f4 bld4(Rsrc r, uint32_t vbytes, uint32_t sbytes) {
+    return __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(r, vbytes, sbytes, 0));
+}
+
 // Four consecutive floats; one 16-byte load when the address allows it.
 __device__ __forceinline__ f4 ld4u(const float *p, bool vec) {
     return vec ? ld4(p) : f4{p[0], p[1], p[2], p[3]};
@@ -123,17 +139,25 @@ __global__ void __launch_bounds__(64) ssm_dsq_kernel(const SsmArgs a) {
         f4 c[8];
         float gy[8], dt;
     };
+    // a chunk inside the sequence loads from wave-uniform token bases with fixed lane offsets
+    // (lane rows 4 kg tokens down); the last one clamps its tokens to the sequence (masked at use)
+    const int64_t HP = H * P, GN = G * N;
+    const float *const gyb = a.gy + s * T * HP + h * P + 16 * pt, *const cb = a.C + s * T * GN + g * N + 64 * nh;
+    const float *const dtb = a.dt + s * T * H + h;
+    const uint32_t HP4 = (uint32_t)HP * 4, GN4 = (uint32_t)GN * 4, H4 = (uint32_t)H * 4;
     auto load = [&](int c, Ld &L) {
-        const int t0 = c * Q;
+        // tokens past the end read the last one (masked at use)
+        const int t0 = c * Q, last = a.T - 1 - t0;
+        const Rsrc rg = rsrc(gyb + t0 * HP), rc = rsrc(cb + t0 * GN), rd = rsrc(dtb + t0 * H);
 #pragma unroll
         for (int q = 0; q < 2; ++q)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int64_t tc = std::min(t0 + 16 * q + 4 * kg + i, a.T - 1);   // masked at use
-                L.gy[4 * q + i] = a.gy[((s * T + tc) * H + h) * P + 16 * pt + ar];
-                L.c[4 * q + i] = ld4(a.C + ((s * T + tc) * G + g) * N + ncol);
+                const uint32_t tl = (uint32_t)min(16 * q + 4 * kg + i, last);
+                L.gy[4 * q + i] = bld(rg, tl * HP4 + 4 * ar, 0);
+                L.c[4 * q + i] = bld4(rc, tl * GN4 + 16 * ar, 0);
             }
-        L.dt = a.dt[(s * T + std::min(t0 + (lane & 31), a.T - 1)) * H + h];
+        L.dt = bld(rd, (uint32_t)min(lane & 31, last) * H4, 0);
     };
     float *dsq = a.dsq + unit * nc * (int64_t)(P * N);
     auto step = [&](int c, const Ld &L) {
@@ -519,17 +543,25 @@ __global__ void __launch_bounds__(64) ssm_fst_kernel(const SsmArgs a) {
         f4 b[8];
         float x[8], dt;
     };
+    // as in the chunk-end pass: uniform token bases with fixed lane offsets inside the sequence,
+    // clamped tokens (step 0 past the end) in its last chunk
+    const int64_t HP = H * P, GN = G * N;
+    const float *const xb = a.x + s * T * HP + h * P + 16 * pt, *const bb = a.B + s * T * GN + g * N + 64 * nh;
+    const float *const dtb = a.dt + s * T * H + h;
+    const uint32_t HP4 = (uint32_t)HP * 4, GN4 = (uint32_t)GN * 4, H4 = (uint32_t)H * 4;
     auto load = [&](int c, Ld &L) {
-        const int t0 = c * Q;
+        // tokens past the end read the last one (their step is 0)
+        const int t0 = c * Q, last = a.T - 1 - t0;
+        const Rsrc rx = rsrc(xb + t0 * HP), rb = rsrc(bb + t0 * GN), rd = rsrc(dtb + t0 * H);
 #pragma unroll
         for (int q = 0; q < 2; ++q)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int64_t tc = std::min(t0 + 16 * q + 4 * kg + i, a.T - 1);   // step 0 past the end
-                L.x[4 * q + i] = a.x[((s * T + tc) * H + h) * P + 16 * pt + ar];
-                L.b[4 * q + i] = ld4(a.B + ((s * T + tc) * G + g) * N + ncol);
+                const uint32_t tl = (uint32_t)min(16 * q + 4 * kg + i, last);
+                L.x[4 * q + i] = bld(rx, tl * HP4 + 4 * ar, 0);
+                L.b[4 * q + i] = bld4(rb, tl * GN4 + 16 * ar, 0);
             }
-        L.dt = a.dt[(s * T + std::min(t0 + (lane & 31), a.T - 1)) * H + h];
+        L.dt = bld(rd, (uint32_t)min(lane & 31, last) * H4, 0);
     };
     float *ckp = a.ck + unit * P * (int64_t)a.nck * N;
     auto step = [&](int c, const Ld &L) {
@@ -713,12 +745,16 @@ __global__ void __launch_bounds__(512) ssm_chunk_fwd_kernel(const SsmArgs a) {
 
 }  // namespace
 
-bool ssm_chunked(int P, int N, int aps) { return aps == 0 && P == 64 && N == 128; }
+// The chunk walks address 32 tokens of a head's rows and of a group's B/C rows with 32-bit byte
+// offsets from the chunk's first token, so a token's stride stays at most 2^24 floats.
+bool ssm_chunked(int P, int N, int aps, int64_t H, int64_t G) {
+    return aps == 0 && P == 64 && N == 128 && H * P <= (int64_t(1) << 24) && G * N <= (int64_t(1) << 24);
+}
 
 hipError_t launch_ssm_chunk_fwd(const SsmArgs &a, hipStream_t st) {
     const int64_t units = (int64_t)a.n_seqs * a.H;
     if (units <= 0) return hipSuccess;
-    if (!ssm_chunked(a.P, a.N, a.aps) || a.hgs < 1 || a.H % a.G != 0 || QW % a.ckw != 0)
+    if (!ssm_chunked(a.P, a.N, a.aps, a.H, a.G) || a.hgs < 1 || a.H % a.G != 0 || QW % a.ckw != 0)
         return hipErrorInvalidValue;
     void *params[] = {const_cast<SsmArgs *>(&a)};
     hipError_t e = hipLaunchKernel((const void *)ssm_fst_kernel<64, 128>, dim3((unsigned)(units * (64 / 16) * (128 / 64))),
@@ -733,7 +769,7 @@ hipError_t launch_ssm_chunk_fwd(const SsmArgs &a, hipStream_t st) {
 hipError_t launch_ssm_chunk_bwd(const SsmArgs &a, hipStream_t st) {
     const int64_t units = (int64_t)a.n_seqs * a.H;
     if (units <= 0) return hipSuccess;
-    if (!ssm_chunked(a.P, a.N, a.aps) || a.hgs < 1 || a.H % a.G != 0 || QW % a.ckw != 0)
+    if (!ssm_chunked(a.P, a.N, a.aps, a.H, a.G) || a.hgs < 1 || a.H % a.G != 0 || QW % a.ckw != 0)
         return hipErrorInvalidValue;
     void *params[] = {const_cast<SsmArgs *>(&a)};
     hipError_t e = hipLaunchKernel((const void *)ssm_dsq_kernel<64, 128>, dim3((unsigned)(units * (64 / 16) * (128 / 64))),
