@@ -107,9 +107,9 @@ hipError_t launch_ssm_combine(const SsmArgs &a, hipStream_t st);
 // state gradients, the chunks' gradients on the matrix cores, then the head slices' dB and dC
 // summed in order.
 bool ssm_chunked(int P, int N, int aps, int64_t H, int64_t G);
-// Row-wise backward for 16 states (rows of a group a multiple of 128): the state gradient
-// entering every 8-token window, then the windows in parallel with two lanes per row, then the
-// combine over 128-row segments.
+// Row-wise backward for 16 states (rows of a group a multiple of 128, H P and G N at most 2^24):
+// the state gradient entering every 8-token window, then the windows in parallel with two lanes
+// per row, then the combine over 128-row segments.
 bool ssm_rowwise(int P, int H, int G, int N);
 hipError_t launch_ssm_rowwise_bwd(const SsmArgs &a, hipStream_t st);
 // Its forward: the state before every window (and s_out), then y per window (y null: states

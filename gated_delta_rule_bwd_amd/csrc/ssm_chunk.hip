@@ -86,16 +86,6 @@ __device__ __forceinline__ float scan32_suffix(float v, int lane) {
     }
     return v;
 }
-// Buffer loads: a wave-uniform base (scalar registers), a per-lane byte offset fixed for the
-// kernel and a scalar byte offset for the token, so a chunk's loads need no vector address
-// arithmetic.  Bases are taken at the chunk's first token; offsets stay far below 2^31.
-typedef __amdgpu_buffer_rsrc_t Rsrc;
-__device__ __forceinline__ Rsrc rsrc(const float *p) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(p), (short)0, 0x7fffffff, 0x00020000);
-}
-__device__ __forceinline__ float bld(Rsrc r, uint32_t vbytes, uint32_t sbytes) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, vbytes, sbytes, 0));
-}
 // (the whole vector is bit-cast: bit-casting its elements one by one made this compiler load
 // only the first dword)
 __device__ __forceinline__ f4 bld4(Rsrc r, uint32_t vbytes, uint32_t sbytes) {

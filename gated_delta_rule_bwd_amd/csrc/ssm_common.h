@@ -19,4 +19,15 @@ __device__ __forceinline__ float ssm_step(float z, int softplus) {
     return z > 20.f ? z : (z < -4.f ? series : direct);
 }
 
+// Buffer loads: a wave-uniform base (scalar registers), a per-lane byte offset and a scalar byte
+// offset, so a block's or chunk's loads need no 64-bit vector address arithmetic.  Bases are
+// taken at the block's or chunk's first token; the offsets used stay below 2^31.
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+__device__ __forceinline__ Rsrc rsrc(const float *p) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(p), (short)0, 0x7fffffff, 0x00020000);
+}
+__device__ __forceinline__ float bld(Rsrc r, uint32_t vbytes, uint32_t sbytes) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, vbytes, sbytes, 0));
+}
+
 }  // namespace gdn

@@ -95,6 +95,22 @@ __device__ __forceinline__ Row row_of(const SsmArgs &a, int64_t r) {
     return o;
 }
 
+// row_of for a wave-uniform row, with 32-bit divisions when the row and the rows of a sequence
+// fit in 32 bits
+__device__ __forceinline__ Row row_of_uniform(const SsmArgs &a, int64_t r) {
+    const int64_t rows_seq = (int64_t)a.P * a.H;
+    if (r > 0xffffffffll || rows_seq > 0xffffffffll) return row_of(a, r);
+    const uint32_t ru = (uint32_t)r, P = (uint32_t)a.P, H = (uint32_t)a.H;
+    const uint32_t q = ru / P, s = q / H, h = q - s * H;
+    Row o;
+    o.r = r;
+    o.i = ru - q * P;
+    o.h = h;
+    o.s = s;
+    o.g = h / (H / (uint32_t)a.G);
+    return o;
+}
+
 // ---- window staging --------------------------------------------------------------------
 // The 16 rows of a workgroup share one (sequence, group), so a window's B and C rows are
 // common to all of them; x, the step (and gy) are per row.  Each window is staged in LDS once
@@ -436,14 +452,21 @@ __global__ void __launch_bounds__(256) ssm_gsw_kernel(const SsmArgs a) {
     // C of those tokens, state tid & 15
     const Row lw = row_of(a, r0 + sub);
     const int tk = 2 * rho;
+    // the block's 16 rows share a sequence: its first token's entries are the loads' base, the
+    // row's own entries a lane offset (tokens past the end read the last one)
+    const int64_t s0 = row_of_uniform(a, r0).s, HP = H * P, GN = G * N;
+    const float *const gyq = a.gy + s0 * T * HP, *const dtq = a.dt + s0 * T * H, *const cq = a.C + s0 * T * GN;
+    const uint32_t og = (uint32_t)(lw.h * P + lw.i) * 4, od = (uint32_t)lw.h * 4, oc = (uint32_t)(lw.g * N + sub) * 4;
     float pg[2], pd[2], pc[2];
     auto load = [&](int blk) {
+        const int tb = blk * GB, last = a.T - 1 - tb;
+        const Rsrc rg = rsrc(gyq + tb * HP), rd = rsrc(dtq + (int64_t)tb * H), rc = rsrc(cq + tb * GN);
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-            const int64_t t = min(blk * GB + tk + u, a.T - 1);
-            pg[u] = a.gy[((lw.s * T + t) * H + lw.h) * P + lw.i];
-            pd[u] = a.dt[(lw.s * T + t) * H + lw.h];
-            pc[u] = a.C[((lw.s * T + t) * G + lw.g) * N + sub];
+            const uint32_t tl = (uint32_t)min(tk + u, last);
+            pg[u] = bld(rg, tl * (uint32_t)HP * 4 + og, 0);
+            pd[u] = bld(rd, tl * (uint32_t)H * 4 + od, 0);
+            pc[u] = bld(rc, tl * (uint32_t)GN * 4 + oc, 0);
         }
     };
     // a token past the end gets gy = 0 and step 0 (decay 1): it leaves gs as it is, so the
@@ -483,22 +506,6 @@ __global__ void __launch_bounds__(256) ssm_gsw_kernel(const SsmArgs a) {
 
 constexpr int RB = 128;   // rows per block of pass 2 (and per column-sum segment): two lanes per
                           // row, eight states each
-
-// row_of for a wave-uniform row, with 32-bit divisions when the row and the rows of a sequence
-// fit in 32 bits
-__device__ __forceinline__ Row row_of_uniform(const SsmArgs &a, int64_t r) {
-    const int64_t rows_seq = (int64_t)a.P * a.H;
-    if (r > 0xffffffffll || rows_seq > 0xffffffffll) return row_of(a, r);
-    const uint32_t ru = (uint32_t)r, P = (uint32_t)a.P, H = (uint32_t)a.H;
-    const uint32_t q = ru / P, s = q / H, h = q - s * H;
-    Row o;
-    o.r = r;
-    o.i = ru - q * P;
-    o.h = h;
-    o.s = s;
-    o.g = h / (H / (uint32_t)a.G);
-    return o;
-}
 
 // Row j of the RB-row block starting at row r0 (a multiple of RB): the block lies in one
 // (sequence, group), since a group's rows are a multiple of RB, so only the head and position
@@ -694,14 +701,20 @@ __global__ void __launch_bounds__(256) ssm_sst_kernel(const SsmArgs a) {
     const float Aj = (APS ? a.A[w.h * N + sub] : a.A[w.h]) * kLog2e;
     const Row lw = row_of(a, r0 + sub);
     const int tk = 2 * rho;
+    // loads as in the gradient pass: the sequence's first token as base, the row as lane offset
+    const int64_t s0 = row_of_uniform(a, r0).s, HP = H * P, GN = G * N;
+    const float *const xq = a.x + s0 * T * HP, *const dtq = a.dt + s0 * T * H, *const bq = a.B + s0 * T * GN;
+    const uint32_t ox = (uint32_t)(lw.h * P + lw.i) * 4, od = (uint32_t)lw.h * 4, ob = (uint32_t)(lw.g * N + sub) * 4;
     float px[2], pd[2], pb[2];
     auto load = [&](int blk) {
+        const int tb = blk * GB, last = a.T - 1 - tb;
+        const Rsrc rx = rsrc(xq + tb * HP), rd = rsrc(dtq + (int64_t)tb * H), rb = rsrc(bq + tb * GN);
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-            const int64_t t = min(blk * GB + tk + u, a.T - 1);
-            px[u] = a.x[((lw.s * T + t) * H + lw.h) * P + lw.i];
-            pd[u] = a.dt[(lw.s * T + t) * H + lw.h];
-            pb[u] = a.B[((lw.s * T + t) * G + lw.g) * N + sub];
+            const uint32_t tl = (uint32_t)min(tk + u, last);
+            px[u] = bld(rx, tl * (uint32_t)HP * 4 + ox, 0);
+            pd[u] = bld(rd, tl * (uint32_t)H * 4 + od, 0);
+            pb[u] = bld(rb, tl * (uint32_t)GN * 4 + ob, 0);
         }
     };
     // a token past the end gets step 0 (decay 1) and d x = 0: it leaves the state as it is
@@ -887,8 +900,11 @@ hipError_t launch_ssm(const SsmArgs &a, bool bwd, hipStream_t st) {
     }
 }
 
+// (the chain passes address 32 tokens of a row's entries with 32-bit byte offsets from a block's
+// first token, so H P and G N stay at most 2^24 floats)
 bool ssm_rowwise(int P, int H, int G, int N) {
-    return N == 16 && G >= 1 && H % G == 0 && (int64_t)P * (H / G) % RB == 0;
+    return N == 16 && G >= 1 && H % G == 0 && (int64_t)P * (H / G) % RB == 0 &&
+           (int64_t)H * P <= (int64_t(1) << 24) && (int64_t)G * N <= (int64_t(1) << 24);
 }
 
 hipError_t launch_ssm_rowwise_fwd(const SsmArgs &a, hipStream_t st) {
