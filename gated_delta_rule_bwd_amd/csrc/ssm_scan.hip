@@ -20,6 +20,8 @@
 // runs in chunks on the matrix cores (ssm_chunk.hip).
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "gdn_internal.h"
 #include "ssm_common.h"
 
@@ -538,7 +540,7 @@ template <bool APS>
 __global__ void __launch_bounds__(256) ssm_win16_kernel(const SsmArgs a) {
     constexpr int N = 16, NH = 8;
     __shared__ float bc[2][WIN][N];          // B, C rows of the window's tokens
-    __shared__ float red[WIN][4][4][2 * N];  // [token][wave][lane bits 1, 2][dC | dB state]
+    __shared__ __align__(16) float red[WIN][4][4][2 * N];  // [token][wave][lane bits 1, 2][dC | dB state]
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hb = lane & 1;
     const int nwin = (a.T + WIN - 1) / WIN;
     const int win = (int)(blockIdx.x % nwin);
